@@ -1,0 +1,44 @@
+"""Plain, slow, fp64 CPU oracle for the orthonormalized optimizer step.
+
+THIS PACKAGE IS TEST INFRASTRUCTURE.  Only the test-suite, the smoke check and
+the CPU-baseline leg of the benchmark may import it.  The product path (the HIP
+library and its Python binding) never imports, links or calls anything here, and
+nothing here imports the product package.
+
+What it computes, and where each step comes from (page titles and sections of the
+public pages about microsoft/dion):
+
+* ``newton_schulz`` -- Muon's orthogonalization: repeated matrix products that
+  push the singular values of the normalised gradient towards one, approximating
+  the U V^T factor of the SVD.  MSR talk "Dion: The distributed orthonormal
+  update revolution is here", passage contrasting SGD with orthonormal updates
+  and the passage on Muon's dense Newton-Schulz matrix products.
+* ``dion_step`` -- Dion's amortised power iteration (one power-iteration step
+  per optimizer step, warm-started from the previous right factor), the low-rank
+  fraction, error feedback, and the SGD-form weight update.  Same talk, passages
+  on amortised power iteration and on low-rank fraction with error feedback;
+  agentlenshq "microsoft/dion", section "How it works"; paper page "Dion:
+  Distributed Orthonormalized Updates", abstract.
+
+Every reading that the pages leave open (where mu enters, the QR sign
+convention, column normalisation of the new right factor, the Newton-Schulz
+coefficients) is listed in the design doc together with the reason for it.
+
+Pins: ``tests/test_oracle_pins.py`` checks these functions against closed forms
+(SVD), invariants of the definitions, and an independent brute-force
+implementation (``oracle.brute``) on tiny inputs.  The fidelity of the readings
+themselves to the real method is "parity unpinned": the pages print no update
+equation and no worked example.
+"""
+
+from .dion_ref import (  # noqa: F401
+    MUON_ABC,
+    NS_EPS,
+    round_bf16,
+    round_to_dtype,
+    qr_positive,
+    dion_step,
+    dion_step_batched,
+    newton_schulz,
+    newton_schulz_batched,
+)

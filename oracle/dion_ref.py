@@ -1,0 +1,192 @@
+"""fp64 reference for the Dion step and for Newton-Schulz.  TEST INFRASTRUCTURE.
+
+Inputs are numpy arrays holding the exact values the GPU receives (fp32 values,
+or fp32 arrays whose values are bf16-representable).  Everything is widened to
+fp64 and computed in fp64 with plain numpy routines; no blocking, fusion or
+reordering beyond what the steps themselves state.
+
+Each step is a small module-level function so that the pin tests can replace
+one of them with a deliberately wrong variant and show that a pin catches it.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+# Muon's published quintic Newton-Schulz coefficients (a, b, c).  The pages name
+# Muon (hysenlabs "Microsoft Dion: orthonormal optimizers that assume DTensor
+# parallelism", section "What an orthonormal optimizer changes about the update
+# rule") but print no coefficients; this is the plain reading, and both sides
+# take (a, b, c) as an explicit argument.
+MUON_ABC = (3.4445, -4.7750, 2.0315)
+
+# Added to the Frobenius norm before the Newton-Schulz normalisation, so that a
+# zero gradient gives a zero output instead of 0/0.
+NS_EPS = 1e-7
+
+
+# ----------------------------------------------------------------------------
+# Rounding to the storage dtype (round to nearest, ties to even)
+# ----------------------------------------------------------------------------
+
+_BF16_MANT_BITS = 8          # significant bits including the implicit one
+_BF16_EMIN = -126            # smallest normal exponent (shared with fp32)
+_BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round fp64 values to the nearest bfloat16 value, ties to even.
+
+    Written from the number format: a bfloat16 normal number is f * 2**e with
+    8 significant bits, so its spacing in the binade [2**e, 2**(e+1)) is
+    2**(e-7); below 2**-126 the spacing stays 2**-133 (subnormals).  Scaling by a
+    power of two is exact in fp64 and ``np.rint`` rounds half to even.
+    Returns fp64 values.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array(x, copy=True)
+    finite = np.isfinite(x) & (x != 0)
+    xf = x[finite]
+    _, e = np.frexp(xf)                      # xf = f * 2**e, 0.5 <= |f| < 1
+    e = np.maximum(e - 1, _BF16_EMIN)        # exponent of the leading bit
+    quantum = np.ldexp(1.0, e - (_BF16_MANT_BITS - 1))
+    y = np.rint(xf / quantum) * quantum
+    y = np.where(np.abs(y) > _BF16_MAX, np.copysign(np.inf, y), y)
+    out[finite] = y
+    return out
+
+
+def round_to_dtype(x, dtype: str) -> np.ndarray:
+    """Round fp64 values to the storage dtype ('bf16' or 'f32'), returned as fp64."""
+    if dtype == "bf16":
+        return round_bf16(x)
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------
+# Dion: amortised power iteration with error feedback
+# ----------------------------------------------------------------------------
+
+def qr_positive(A: np.ndarray):
+    """Thin QR factorisation A = P R with diag(R) >= 0.
+
+    Householder QR from LAPACK, then the columns whose R-diagonal is negative
+    are flipped, which makes the factor unique for full-column-rank A (it is
+    then the Gram-Schmidt basis of A's columns, in order).
+    """
+    P, R = np.linalg.qr(_f64(A), mode="reduced")
+    s = np.sign(np.diag(R))
+    s[s == 0] = 1.0
+    return P * s[None, :], R * s[:, None]
+
+
+def _momentum_accumulate(M, G):
+    # The gradient is added to the decoupled momentum buffer; mu is not applied
+    # here (it acts as the error-feedback decay below).
+    return M + G
+
+
+def _power_left(B, Q):
+    # One power-iteration product, warm-started from the previous right factor.
+    return B @ Q
+
+
+def _orthonormalize(P_tilde):
+    return qr_positive(P_tilde)[0]
+
+
+def _power_right(B, P):
+    return B.T @ P
+
+
+def _error_feedback(B, P, R, mu):
+    # The rank-r part P R^T is what the step applies; the buffer keeps all of the
+    # rest and a fraction mu of the applied part.
+    return B - (1.0 - mu) * (P @ R.T)
+
+
+def _column_normalize(R):
+    norms = np.linalg.norm(R, axis=0)
+    safe = np.where(norms > 0, norms, 1.0)
+    Qn = R / safe[None, :]
+    Qn[:, norms == 0] = 0.0
+    return Qn, norms
+
+
+def _weight_update(X, P, Q_new, lr, scale):
+    # SGD form: step along minus the orthonormalised direction, scaled by lr.
+    dX = -lr * scale * (P @ Q_new.T)
+    return X + dX, dX
+
+
+def dion_step(X, G, M, Q, mu: float, lr: float, scale: float = 1.0,
+              x_dtype: str = "bf16") -> dict:
+    """One Dion step on one matrix, in fp64.
+
+    X (m x n) weight, G (m x n) gradient, M (m x n) momentum, Q (n x r) right
+    factor.  Returns a dict with the new state and the intermediates:
+    ``X`` (rounded to ``x_dtype``), ``X_exact`` (before rounding), ``dX``,
+    ``M``, ``Q``, ``P``, ``R``, ``B``, ``P_tilde``, ``col_norms``.
+    """
+    X, G, M, Q = _f64(X), _f64(G), _f64(M), _f64(Q)
+    m, n = X.shape
+    if G.shape != (m, n) or M.shape != (m, n) or Q.shape[0] != n:
+        raise ValueError("shape mismatch")
+    B = _momentum_accumulate(M, G)
+    P_tilde = _power_left(B, Q)
+    P = _orthonormalize(P_tilde)
+    R = _power_right(B, P)
+    M_new = _error_feedback(B, P, R, mu)
+    Q_new, norms = _column_normalize(R)
+    X_exact, dX = _weight_update(X, P, Q_new, lr, scale)
+    return dict(X=round_to_dtype(X_exact, x_dtype), X_exact=X_exact, dX=dX,
+                M=M_new, Q=Q_new, P=P, R=R, B=B, P_tilde=P_tilde, col_norms=norms)
+
+
+def dion_step_batched(Xs, Gs, Ms, Qs, mu, lr, scale=1.0, x_dtype="bf16"):
+    """A group of independent same-shape matrices: one ``dion_step`` each."""
+    return [dion_step(X, G, M, Q, mu, lr, scale, x_dtype)
+            for X, G, M, Q in zip(Xs, Gs, Ms, Qs)]
+
+
+# ----------------------------------------------------------------------------
+# Newton-Schulz (Muon)
+# ----------------------------------------------------------------------------
+
+def newton_schulz(G, steps: int = 5, abc=MUON_ABC, eps: float = NS_EPS) -> np.ndarray:
+    """Newton-Schulz orthogonalisation of one matrix, in fp64.
+
+    Works on the wide orientation (rows <= cols) so that the Gram matrix is the
+    small one, normalises by the Frobenius norm, then repeats
+    A = X X^T,  Bp = b A + c A A,  X = a X + Bp X   ``steps`` times.
+    For the quintic f(s) = a s + b s^3 + c s^5 this maps G = U S V^T to
+    U f(...f(S / (|G|_F + eps))...) V^T.
+    """
+    a, b, c = (float(v) for v in abc)
+    G = _f64(G)
+    tall = G.shape[0] > G.shape[1]
+    Xk = _ns_normalize(G.T if tall else G, eps)
+    for _ in range(steps):
+        Xk = _ns_step(Xk, a, b, c)
+    return Xk.T if tall else Xk
+
+
+def _ns_normalize(G, eps):
+    return G / (np.linalg.norm(G) + eps)
+
+
+def _ns_step(Xk, a, b, c):
+    A = Xk @ Xk.T
+    Bp = b * A + c * (A @ A)
+    return a * Xk + Bp @ Xk
+
+
+def newton_schulz_batched(Gs, steps=5, abc=MUON_ABC, eps=NS_EPS):
+    """Independent Newton-Schulz on each matrix of a group (e.g. per-head blocks)."""
+    return [newton_schulz(G, steps, abc, eps) for G in Gs]

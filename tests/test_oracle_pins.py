@@ -1,0 +1,328 @@
+"""Pins for the fp64 oracle, on the CPU.
+
+The pages print no worked example and no numbers, so the oracle is pinned by
+closed forms (the SVD), invariants that follow from the definitions, and an
+independent loop/modified-Gram-Schmidt formulation on tiny inputs.  The
+``test_mutant_*`` cases plant a plausible mistake in the oracle (a wrong sign, a
+dropped term, a transposed operand, a missing normalisation) and show that at
+least one pin rejects it.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import brute, dion_ref
+from orthonormal_optimizer_update_amd import synth
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+# ----------------------------------------------------------------------------
+# pin helpers: each returns a max error, so mutants can be shown to fail them
+# ----------------------------------------------------------------------------
+
+def quintic_spectral(G, steps=5, abc=oracle.MUON_ABC, eps=oracle.NS_EPS):
+    """Closed form of the iteration: apply f(s) = a s + b s^3 + c s^5 to the
+    normalised singular values and rebuild U f(S) V^T."""
+    a, b, c = abc
+    U, s, Vt = np.linalg.svd(np.asarray(G, np.float64), full_matrices=False)
+    s = s / (np.linalg.norm(G) + eps)
+    for _ in range(steps):
+        s = a * s + b * s ** 3 + c * s ** 5
+    return (U * s) @ Vt
+
+
+def ns_closed_form_err(G, **kw):
+    return np.abs(oracle.newton_schulz(G, **kw) - quintic_spectral(G, **kw)).max()
+
+
+def ef_invariant_err(out, mu):
+    P, B, Mn = out["P"], out["B"], out["M"]
+    e1 = np.abs(P.T @ Mn - mu * (P.T @ B)).max()
+    proj = np.eye(P.shape[0]) - P @ P.T
+    e2 = np.abs(proj @ Mn - proj @ B).max()
+    return max(e1, e2) / np.abs(B).max()
+
+
+def singular_warm_start_err(B, r, mu, lr, scale=1.0):
+    """With Q = the top-r right singular vectors, one step must give P = U_r,
+    new Q = V_r, dX = -lr*scale*U_r V_r^T, M = B - (1-mu) U_r S_r V_r^T."""
+    U, s, Vt = np.linalg.svd(B, full_matrices=False)
+    Ur, Vr, Sr = U[:, :r], Vt[:r].T, s[:r]
+    X = np.zeros_like(B)
+    # B reaches the step as momentum + gradient, split unevenly
+    N = np.cos(np.arange(B.size, dtype=np.float64)).reshape(B.shape)
+    out = oracle.dion_step(X, 0.3 * B + N, 0.7 * B - N, Vr, mu, lr, scale, x_dtype="f32")
+    errs = [
+        np.abs(out["P"] - Ur).max(),
+        np.abs(out["Q"] - Vr).max(),
+        np.abs(out["dX"] - (-lr * scale) * (Ur @ Vr.T)).max() / (lr * scale),
+        np.abs(out["M"] - (B - (1 - mu) * (Ur * Sr) @ Vr.T)).max() / np.abs(B).max(),
+    ]
+    return max(errs)
+
+
+def descent_err(out, lr, scale):
+    """<dX, B> = -lr*scale*sum_k |R_k| and every row of P^T dX has norm lr*scale."""
+    inner = np.sum(out["dX"] * out["B"])
+    want = -lr * scale * np.sum(np.linalg.norm(out["R"], axis=0))
+    e1 = abs(inner - want) / abs(want)
+    rows = np.linalg.norm(out["P"].T @ out["dX"], axis=1)
+    e2 = np.abs(rows - lr * scale).max() / (lr * scale)
+    return max(e1, e2)
+
+
+def mgs_err(out):
+    P_mgs = np.array(brute.mgs_qr(out["P_tilde"].tolist()))
+    return np.abs(out["P"] - P_mgs).max()
+
+
+def unit_col_err(out):
+    return np.abs(np.linalg.norm(out["Q"], axis=0) - 1.0).max()
+
+
+def _generic_case(rng, m=30, n=22, r=5):
+    X = rng.standard_normal((m, n)) * 0.02
+    G = rng.standard_normal((m, n))
+    M = rng.standard_normal((m, n)) * 0.5
+    Q = rng.standard_normal((n, r))
+    Q /= np.linalg.norm(Q, axis=0)
+    return X, G, M, Q
+
+
+# ----------------------------------------------------------------------------
+# Newton-Schulz
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(48, 80), (80, 48), (33, 33), (1, 7)])
+def test_ns_matches_spectral_closed_form(rng, shape):
+    G = rng.standard_normal(shape)
+    assert ns_closed_form_err(G) <= 1e-12
+
+
+def test_ns_cubic_converges_to_polar_factor(rng):
+    """Textbook cubic (1.5, -0.5, 0) converges to the polar factor U V^T of the
+    SVD, the direction the talk says orthonormal updates take."""
+    U, _ = np.linalg.qr(rng.standard_normal((40, 25)))
+    V, _ = np.linalg.qr(rng.standard_normal((25, 25)))
+    s = np.linspace(1.0, 0.3, 25)
+    G = (U * s) @ V.T
+    Y = oracle.newton_schulz(G, steps=60, abc=(1.5, -0.5, 0.0), eps=0.0)
+    assert np.abs(Y - U @ V.T).max() <= 1e-10
+
+
+def test_ns_singular_values_cluster_near_one(rng):
+    G = rng.standard_normal((48, 80))
+    Y = oracle.newton_schulz(G)
+    U, s, Vt = np.linalg.svd(G, full_matrices=False)
+    core = U.T @ Y @ Vt.T                         # diagonal if singular vectors match
+    off = core - np.diag(np.diag(core))
+    assert np.abs(off).max() <= 1e-12
+    sv = np.diag(core)
+    assert sv.min() >= 0.6 and sv.max() <= 1.2
+
+
+def test_ns_transpose_zero_and_scale(rng):
+    G = rng.standard_normal((20, 31))
+    assert np.abs(oracle.newton_schulz(G.T) - oracle.newton_schulz(G).T).max() <= 1e-14
+    assert np.all(oracle.newton_schulz(np.zeros((6, 9))) == 0)
+    Y1 = oracle.newton_schulz(G, eps=0.0)
+    Y2 = oracle.newton_schulz(37.5 * G, eps=0.0)
+    assert np.abs(Y1 - Y2).max() <= 1e-13
+
+
+def test_ns_brute_force_agrees(rng):
+    for shape in [(5, 8), (8, 5), (6, 6)]:
+        G = rng.standard_normal(shape)
+        got = np.array(brute.newton_schulz(G.tolist(), 5, oracle.MUON_ABC, oracle.NS_EPS))
+        assert np.abs(got - oracle.newton_schulz(G)).max() <= 1e-13
+
+
+# ----------------------------------------------------------------------------
+# Dion
+# ----------------------------------------------------------------------------
+
+def test_dion_singular_warm_start_closed_form(rng):
+    B = rng.standard_normal((30, 22))
+    assert singular_warm_start_err(B, 6, mu=0.95, lr=0.01, scale=1.7) <= 1e-12
+
+
+def test_dion_p_orthonormal_and_is_gram_schmidt_basis(rng):
+    out = oracle.dion_step(*_generic_case(rng), mu=0.9, lr=0.1)
+    P, Pt = out["P"], out["P_tilde"]
+    assert np.abs(P.T @ P - np.eye(P.shape[1])).max() <= 1e-13
+    # span(P) = span(B Q): the residual of P_tilde outside span(P) vanishes
+    assert np.abs(Pt - P @ (P.T @ Pt)).max() <= 1e-12 * np.abs(Pt).max()
+    assert mgs_err(out) <= 1e-13
+    # Cholesky QR: P = P_tilde L^{-T} with L L^T = P_tilde^T P_tilde
+    L = np.linalg.cholesky(Pt.T @ Pt)
+    assert np.abs(P - np.linalg.solve(L, Pt.T).T).max() <= 1e-11
+
+
+def test_dion_error_feedback_invariants(rng):
+    for mu in (0.0, 0.5, 0.95):
+        out = oracle.dion_step(*_generic_case(rng), mu=mu, lr=0.1)
+        assert ef_invariant_err(out, mu) <= 1e-13
+
+
+def test_dion_rank_r_recovery(rng):
+    m, n, r = 40, 28, 4
+    U, _ = np.linalg.qr(rng.standard_normal((m, r)))
+    V, _ = np.linalg.qr(rng.standard_normal((n, r)))
+    B = (U * np.array([5.0, 3.0, 2.0, 1.0])) @ V.T
+    Q = rng.standard_normal((n, r))
+    mu = 0.8
+    out = oracle.dion_step(np.zeros((m, n)), B, np.zeros((m, n)), Q, mu, 0.1, x_dtype="f32")
+    P, R = out["P"], out["R"]
+    assert np.abs(P @ P.T - U @ U.T).max() <= 1e-12
+    assert np.abs(P @ R.T - B).max() <= 1e-12
+    assert np.abs(out["M"] - mu * B).max() <= 1e-12
+
+
+def test_dion_special_cases(rng):
+    X, G, M, Q = _generic_case(rng)
+    out = oracle.dion_step(X, G, M, Q, mu=1.0, lr=0.1)
+    assert np.abs(out["M"] - (M + G)).max() <= 1e-13
+    out = oracle.dion_step(X, G, M, Q, mu=0.9, lr=0.0, x_dtype="f32")
+    assert np.array_equal(out["X_exact"], X)
+    assert unit_col_err(out) <= 1e-14
+    # full rank r = n <= m: the rank-r part is all of B
+    m, n = 12, 7
+    B = rng.standard_normal((m, n))
+    out = oracle.dion_step(np.zeros((m, n)), B, np.zeros((m, n)), rng.standard_normal((n, n)), 0.3, 0.1)
+    assert np.abs(out["P"] @ out["R"].T - B).max() <= 1e-12
+
+
+def test_dion_zero_column_gives_zero_q(rng):
+    m, n, r = 10, 8, 3
+    B = np.zeros((m, n))
+    B[:, 0] = rng.standard_normal(m)          # rank 1, so two columns of R vanish
+    Q = rng.standard_normal((n, r))
+    out = oracle.dion_step(np.zeros((m, n)), B, np.zeros((m, n)), Q, 0.9, 0.1)
+    assert np.all(np.isfinite(out["Q"]))
+
+
+def test_dion_update_is_descent(rng):
+    out = oracle.dion_step(*_generic_case(rng), mu=0.9, lr=0.05, scale=2.0)
+    assert descent_err(out, 0.05, 2.0) <= 1e-12
+
+
+def test_dion_amortised_power_iteration_converges(rng):
+    """Feeding Q back with a fixed momentum-free B is subspace iteration: span(Q)
+    approaches the top-r right singular subspace at rate sigma_{r+1}/sigma_r."""
+    m, n, r = 30, 20, 3
+    U, _ = np.linalg.qr(rng.standard_normal((m, n)))
+    V, _ = np.linalg.qr(rng.standard_normal((n, n)))
+    s = np.concatenate([[8.0, 6.0, 4.0], 2.0 * 0.9 ** np.arange(n - 3)])
+    B = (U * s) @ V.T
+    Q = rng.standard_normal((n, r))
+    Vr = V[:, :r]
+    gaps = []
+    for _ in range(40):
+        out = oracle.dion_step(np.zeros((m, n)), B, np.zeros((m, n)), Q, 0.9, 0.1)
+        Q = out["Q"]
+        Qo, _ = np.linalg.qr(Q)
+        gaps.append(np.linalg.norm(Qo - Vr @ (Vr.T @ Qo)))
+    assert gaps[-1] <= 1e-10
+    assert all(b <= a * 0.75 + 1e-14 for a, b in zip(gaps[:-1], gaps[1:]))
+
+
+def test_dion_brute_force_multistep(rng):
+    m, n, r, mu, lr = 12, 9, 3, 0.95, 0.01
+    X = rng.standard_normal((m, n)) * 0.02
+    Q = rng.standard_normal((n, r))
+    Q /= np.linalg.norm(Q, axis=0)
+    M = np.zeros((m, n))
+    Xb, Mb, Qb = X.copy(), M.copy(), Q.copy()
+    for _ in range(10):
+        G = rng.standard_normal((m, n))
+        out = oracle.dion_step(X, G, M, Q, mu, lr, x_dtype="f32")
+        Xn, Mn, Qn, P, R = (np.array(v) for v in brute.dion_step(Xb, G, Mb, Qb, mu, lr))
+        assert np.abs(out["X_exact"] - Xn).max() <= 1e-12
+        assert np.abs(out["M"] - Mn).max() <= 1e-12
+        assert np.abs(out["Q"] - Qn).max() <= 1e-12
+        assert np.abs(out["P"] - P).max() <= 1e-12
+        assert np.abs(out["R"] - R).max() <= 1e-11
+        X, M, Q = out["X_exact"], out["M"], out["Q"]
+        Xb, Mb, Qb = Xn, Mn, Qn
+
+
+# ----------------------------------------------------------------------------
+# Rounding
+# ----------------------------------------------------------------------------
+
+def test_round_bf16_known_values():
+    vals = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -9, 1 + 2 ** -7 + 2 ** -8, 2 ** -133 * 1.5,
+                     2 ** -134, (2 - 2 ** -8) * 2.0 ** 127, (2 - 2 ** -7) * 2.0 ** 127, -0.0, 65504.0])
+    want = np.array([1.0, 1 + 2 ** -7, 1 + 2 ** -6, 2 ** -132, 0.0, np.inf, (2 - 2 ** -7) * 2.0 ** 127, -0.0, 65536.0])
+    got = oracle.round_bf16(vals)
+    assert np.array_equal(got, want)
+
+
+def test_round_bf16_matches_bit_pattern_rounding(rng):
+    """Two independent roundings of fp32 values to bf16 agree bit for bit: the
+    oracle's (from the number format) and the input generator's (bit pattern)."""
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-30, 30, 200000))).astype(np.float32)
+    a = oracle.round_bf16(x.astype(np.float64))
+    b = synth.to_bf16_values(x).astype(np.float64)
+    assert np.array_equal(a, b)
+
+
+# ----------------------------------------------------------------------------
+# Mutants: a planted mistake in the oracle must fail a pin
+# ----------------------------------------------------------------------------
+
+MUTANTS = {
+    "ef_sign": ("_error_feedback", lambda B, P, R, mu: B + (1.0 - mu) * (P @ R.T)),
+    "ef_mu_swapped": ("_error_feedback", lambda B, P, R, mu: B - mu * (P @ R.T)),
+    "ef_dropped": ("_error_feedback", lambda B, P, R, mu: B),
+    "right_not_transposed": ("_power_right", lambda B, P: B @ P),
+    "left_transposed": ("_power_left", lambda B, Q: B.T @ Q),
+    "momentum_dropped": ("_momentum_accumulate", lambda M, G: G),
+    "no_sign_fix": ("_orthonormalize", lambda Pt: np.linalg.qr(Pt)[0]),
+    "no_colnorm": ("_column_normalize", lambda R: (R.copy(), np.linalg.norm(R, axis=0))),
+    "update_sign": ("_weight_update", lambda X, P, Qn, lr, s: (X + lr * s * (P @ Qn.T), lr * s * (P @ Qn.T))),
+}
+
+
+def _all_dion_pins(rng):
+    errs = []
+    B = rng.standard_normal((30, 30))
+    errs.append(singular_warm_start_err(B, 6, 0.9, 0.01, 1.3))
+    X, G, M, Q = _generic_case(rng, 30, 30, 5)
+    out = oracle.dion_step(X, G, M, Q, mu=0.9, lr=0.05, scale=1.0)
+    errs += [ef_invariant_err(out, 0.9), descent_err(out, 0.05, 1.0), mgs_err(out), unit_col_err(out)]
+    return max(errs)
+
+
+@pytest.mark.parametrize("name", [k for k in MUTANTS if MUTANTS[k] is not None])
+def test_mutant_dion_caught(monkeypatch, rng, name):
+    assert _all_dion_pins(np.random.default_rng(7)) <= 1e-10     # the real oracle passes
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(dion_ref, attr, fn)
+    assert not (_all_dion_pins(np.random.default_rng(7)) <= 1e-6)   # NaN counts as caught
+
+
+NS_MUTANTS = {
+    "b_sign": lambda X, a, b, c: dion_ref.__dict__["_orig_ns_step"](X, a, -b, c),
+    "apply_right": lambda X, a, b, c: a * X + X @ (b * (X @ X.T) + c * (X @ X.T) @ (X @ X.T)),
+    "dropped_square": lambda X, a, b, c: a * X + (b * (X @ X.T)) @ X,
+    "gram_transposed": lambda X, a, b, c: a * X + (b * (X.T @ X) + c * (X.T @ X) @ (X.T @ X)) @ X.T.T
+    if X.shape[0] == X.shape[1] else None,
+}
+
+
+@pytest.mark.parametrize("name", list(NS_MUTANTS))
+def test_mutant_ns_caught(monkeypatch, rng, name):
+    G = rng.standard_normal((24, 24))
+    assert ns_closed_form_err(G) <= 1e-12
+    monkeypatch.setitem(dion_ref.__dict__, "_orig_ns_step", dion_ref._ns_step)
+    monkeypatch.setattr(dion_ref, "_ns_step", NS_MUTANTS[name])
+    assert not (ns_closed_form_err(G) <= 1e-6)
+
+
+def test_mutant_ns_normalization_caught(monkeypatch, rng):
+    G = 3.0 * rng.standard_normal((16, 24))
+    monkeypatch.setattr(dion_ref, "_ns_normalize", lambda X, eps: X / (np.abs(X).max() + eps))
+    assert not (ns_closed_form_err(G) <= 1e-6)
