@@ -1,0 +1,194 @@
+#!/usr/bin/env python3
+"""Throughput of the orthonormalized optimizer step on one MI355X.
+
+One bench step on the 4096 x 4096 bf16 workload (fp32 momentum, gradient with a
+planted rank-32 part of 10x norm) is the whole hot path once:
+    dion_step at r = 1024 (rank fraction 1/4)
+    dion_step at r = 256  (rank fraction 1/16)
+    newton_schulz, 5 iterations, on the same matrix.
+Inputs are synthetic, seeded and resident in HBM before timing starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|3|4|5]
+
+Prints ONE JSON line.  The oracle is timed on the host cores on a bounded
+sample (one step of the same workload) as the reported CPU baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "optimizer steps/sec & ms/step vs matrix size, rank frac 1/4,1/16; % HBM/MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", type=int, default=2)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+class Timer:
+    """HIP events on the stream the library launches on (torch's current stream)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.s = torch.cuda.Event(enable_timing=True)
+        self.e = torch.cuda.Event(enable_timing=True)
+
+    def __enter__(self):
+        self.s.record(self.torch.cuda.current_stream())
+        return self
+
+    def __exit__(self, *a):
+        self.e.record(self.torch.cuda.current_stream())
+        self.e.synchronize()
+        self.ms = self.s.elapsed_time(self.e)
+
+
+def workload2(torch, api, synth):
+    """State and closures for the 4096 x 4096 workload."""
+    wl = synth.WORKLOADS[2]
+    m = n = 4096
+    dev = "cuda"
+    S = synth.planted(2, m, n, 32, wl["planted_ratio"])
+    Gs = [torch.from_numpy(synth.gradient(2, m, n, t, "bf16", planted_part=S)).to(dev).to(torch.bfloat16)
+          for t in (1, 2, 3)]
+    X0 = torch.from_numpy(synth.weight(2, m, n, "bf16")).to(dev).to(torch.bfloat16)
+    paths = {}
+    for r in wl["ranks"]:
+        st = dict(X=X0.clone(), M=torch.zeros(m, n, device=dev),
+                  Q=torch.from_numpy(synth.right_factor0(2, n, r)).to(dev),
+                  ws=api.workspace(api.dion_workspace_size(m, n, r), dev))
+        paths[f"dion_r{r}"] = st
+    ns_ws = api.workspace(api.ns_workspace_size(m, n), dev)
+    ns_out = torch.empty(m, n, device=dev, dtype=torch.bfloat16)
+    mu, lr = wl["mu"], wl["lr"]
+
+    def run_path(name, i):
+        G = Gs[i % len(Gs)]
+        if name == "ns5":
+            api.newton_schulz(G, out=ns_out, steps=5, ws=ns_ws)
+        else:
+            st = paths[name]
+            api.dion_step(st["X"], G, st["M"], st["Q"], mu, lr, ws=st["ws"])
+
+    names = [f"dion_r{r}" for r in wl["ranks"]] + ["ns5"]
+
+    def ns_steps(k):
+        api.newton_schulz(Gs[0], out=ns_out, steps=k, ws=ns_ws)
+
+    info = dict(workload=wl["name"], m=m, n=n, ranks=wl["ranks"], ns_iterations=5,
+                mu=mu, lr=lr, x_dtype="bf16", momentum_dtype="f32")
+    return names, run_path, ns_steps, info, (m, n)
+
+
+def cpu_baseline(synth, oracle):
+    """One oracle step of the same workload on the host (bounded sample)."""
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    wl = synth.WORKLOADS[2]
+    m = n = 4096
+    S = synth.planted(2, m, n, 32, wl["planted_ratio"])
+    G = synth.gradient(2, m, n, 1, "bf16", planted_part=S)
+    X = synth.weight(2, m, n, "bf16")
+    t0 = time.perf_counter()
+    for r in wl["ranks"]:
+        oracle.dion_step(X, G, np.zeros((m, n)), synth.right_factor0(2, n, r), wl["mu"], wl["lr"])
+    oracle.newton_schulz(G, 5)
+    dt = time.perf_counter() - t0
+    return {"value": 1.0 / dt, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": "one full step (Dion r=1024, Dion r=256, Newton-Schulz x5) of the "
+                      "4096x4096 workload, fp64 numpy, first step's inputs",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU sharding "
+              "is not part of this build.", file=sys.stderr)
+        sys.exit(2)
+    if args.workload != 2:
+        print("only --workload 2 is a bench line; the other workloads are parity cases",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from orthonormal_optimizer_update_amd import api, synth
+    api.lib()
+    torch.cuda.set_device(0)
+    names, run_path, ns_steps, info, (m, n) = workload2(torch, api, synth)
+
+    for i in range(args.warmup):
+        for nm in names:
+            run_path(nm, i)
+    torch.cuda.synchronize()
+
+    # Timed region: exactly K whole steps.
+    with Timer(torch) as t:
+        for i in range(args.steps):
+            for nm in names:
+                run_path(nm, i)
+    torch.cuda.synchronize()
+    ms_step = t.ms / args.steps
+
+    # Per-path breakdown (not part of the headline number).
+    per_path = {}
+    for nm in names:
+        with Timer(torch) as tp:
+            for i in range(args.steps):
+                run_path(nm, i)
+        per_path[nm] = {"ms": tp.ms / args.steps, "steps_per_s": 1000.0 * args.steps / tp.ms}
+
+    # Dominant kernel: the Newton-Schulz MFMA GEMM (three launches per
+    # iteration, each 2*m*m*n flops at m = n).  Its average launch time is
+    # (time of 5 iterations - time of 0 iterations) / 15, on the same stream.
+    reps = max(3, args.steps // 2)
+    with Timer(torch) as t5:
+        for _ in range(reps):
+            ns_steps(5)
+    with Timer(torch) as t0:
+        for _ in range(reps):
+            ns_steps(0)
+    gemm_ms = (t5.ms - t0.ms) / reps / 15.0
+    flops = 2.0 * m * m * n
+    achieved = flops / (gemm_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "kernel": "gemm_kernel (Newton-Schulz products, bf16 MFMA 32x32x16, 256x256 tiles)",
+                "avg_launch_ms": gemm_ms, "flops_per_launch": flops}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import dion_ref as oracle  # reported CPU baseline only
+        cpu = cpu_baseline(synth, oracle)
+
+    line = {
+        "metric": METRIC, "value": 1000.0 / ms_step, "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic", "config": info, "paths": per_path, "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,288 @@
+// C-ABI entry points of libortho.so: argument checks, workspace carving and the
+// stream-ordered kernel sequence of each operation.  No allocation, no host
+// synchronisation.
+#include <string.h>
+
+#include "../../include/ortho.h"
+#include "launch.h"
+#include "plan.h"
+
+using namespace ortho;
+
+namespace {
+
+constexpr float kMuonA = 3.4445f, kMuonB = -4.7750f, kMuonC = 2.0315f;
+constexpr float kNsEps = 1e-7f;
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+// Pointer table over caller matrices [b0, b0 + nb).  `vec_bytes` is the width
+// of the vector accesses the consuming kernel makes.
+MatArg user_table(const ortho_mat* mats, int b0, int nb, size_t vec_bytes) {
+  MatArg t;
+  memset(&t, 0, sizeof(t));
+  const size_t esz = mats[b0].dtype == ORTHO_BF16 ? 2 : 4;
+  t.ld = mats[b0].ld;
+  t.rows = static_cast<int>(mats[b0].rows);
+  t.cols = static_cast<int>(mats[b0].cols);
+  bool vec = (static_cast<size_t>(t.ld) * esz) % vec_bytes == 0;
+  for (int i = 0; i < nb; ++i) {
+    t.p[i] = mats[b0 + i].data;
+    vec = vec && aligned(t.p[i], vec_bytes);
+  }
+  t.vec = vec;
+  return t;
+}
+
+// Pointer table over one workspace region of members [0, nb).
+MatArg ws_table(char* base, size_t member_bytes, size_t off, int nb, int64_t ld, int rows,
+                int cols, size_t esz, size_t vec_bytes) {
+  MatArg t;
+  memset(&t, 0, sizeof(t));
+  t.ld = ld;
+  t.rows = rows;
+  t.cols = cols;
+  for (int i = 0; i < nb; ++i) t.p[i] = base + i * member_bytes + off;
+  t.vec = (static_cast<size_t>(ld) * esz) % vec_bytes == 0;
+  return t;
+}
+
+#define ORTHO_TRY(expr)                               \
+  do {                                                \
+    if ((expr) != hipSuccess) return ORTHO_E_HIP;     \
+  } while (0)
+
+ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, const ortho_mat* M,
+                      const ortho_mat* Q, int32_t r, float mu, float lr, float scale,
+                      const ortho_mat* P_out, const ortho_mat* R_out, int32_t* status, void* ws,
+                      void* stream) {
+  const int64_t m = X[0].rows, n = X[0].cols;
+  DionPlan pl;
+  if (!plan_dion(m, n, r, batch, &pl)) return ORTHO_E_SHAPE;
+  const bool bf = X[0].dtype == ORTHO_BF16;
+  const hipStream_t s = as_stream(stream);
+  char* base = static_cast<char*>(ws);
+  const size_t mb = pl.member_bytes;
+  const int mi = static_cast<int>(m), ni = static_cast<int>(n);
+  const int64_t rp = pl.rp;
+  const size_t gvec = bf ? 8 : 16;
+
+  for (int b0 = 0; b0 < batch; b0 += pl.chunk) {
+    const int nb = batch - b0 < pl.chunk ? batch - b0 : pl.chunk;
+    const MatArg tX = user_table(X, b0, nb, gvec);
+    const MatArg tG = user_table(G, b0, nb, gvec);
+    const MatArg tM = user_table(M, b0, nb, 16);
+    const MatArg tQ = user_table(Q, b0, nb, 16);
+    const MatArg tPt = ws_table(base, mb, pl.off_pt, nb, rp, mi, r, 4, 16);
+    const MatArg tP1 = ws_table(base, mb, pl.off_p1, nb, rp, mi, r, 4, 16);
+    const MatArg tPart = ws_table(base, mb, pl.off_part, nb, r, 0, r, 4, 16);
+    const MatArg tR = ws_table(base, mb, pl.off_r, nb, rp, ni, r, 4, 16);
+    const MatArg tTt = ws_table(base, mb, pl.off_tt, nb, r, r, r, 4, 16);
+    float* part_f = reinterpret_cast<float*>(base + pl.off_part);
+    double* part_d = reinterpret_cast<double*>(base + pl.off_part);
+
+    // Sweep 1: P_tilde = (M + G) Q.
+    DionLeftArgs la;
+    la.m = tM; la.g = tG; la.q = tQ;
+    la.out = pl.split_left > 1 ? tPart : tPt;
+    la.split_stride = m * r;
+    la.M = mi; la.N = ni; la.r = r;
+    la.splits = pl.split_left; la.kchunk = pl.kchunk_left;
+    ORTHO_TRY(launch_dion_left(la, bf, nb, s));
+    if (pl.split_left > 1) {
+      RedArgs ra;
+      ra.part = part_f; ra.part_member_stride = static_cast<int64_t>(mb / 4);
+      ra.slice = m * r; ra.splits = pl.split_left; ra.rows = mi; ra.cols = r;
+      ra.out = tPt; ra.colsq = nullptr; ra.colsq_member_stride = 0;
+      ORTHO_TRY(launch_reduce_splits(ra, nb, s));
+    }
+
+    // Orthonormalisation: two Cholesky-QR passes with an fp64 Gram.
+    for (int pass = 0; pass < 2; ++pass) {
+      const MatArg& src = pass == 0 ? tPt : tP1;
+      const MatArg& dst = pass == 0 ? tP1 : tPt;
+      Gram64Args ga;
+      ga.p = src; ga.part = part_d; ga.part_member_stride = static_cast<int64_t>(mb / 8);
+      ga.slice = static_cast<int64_t>(r) * r; ga.m = mi; ga.r = r; ga.kchunk = pl.kchunk_gram;
+      ORTHO_TRY(launch_gram64(ga, pl.split_gram, nb, s));
+      CholArgs ca;
+      ca.part = part_d; ca.part_member_stride = static_cast<int64_t>(mb / 8);
+      ca.slice = static_cast<int64_t>(r) * r; ca.splits = pl.split_gram;
+      ca.s = reinterpret_cast<double*>(base + pl.off_s);
+      ca.x = reinterpret_cast<double*>(base + pl.off_x);
+      ca.d = reinterpret_cast<double*>(base + pl.off_d);
+      ca.mat_stride = static_cast<int64_t>(mb / 8); ca.vec_stride = static_cast<int64_t>(mb / 8);
+      ca.r = r; ca.status = status;
+      ORTHO_TRY(launch_cholesky_inverse(ca, reinterpret_cast<float*>(base + pl.off_tt),
+                                        static_cast<int64_t>(mb / 4), nb, s));
+      ApplyArgs aa;
+      aa.pt = src; aa.tt = tTt; aa.out = dst; aa.M = mi; aa.r = r;
+      ORTHO_TRY(launch_apply_t(aa, nb, s));
+    }
+
+    // Sweep 2: R = (M + G)^T P, then Q' = column-normalised R.
+    DionRightArgs rb;
+    rb.m = tM; rb.g = tG; rb.p = tPt; rb.out = tPart;
+    rb.split_stride = n * r;
+    rb.M = mi; rb.N = ni; rb.r = r;
+    rb.splits = pl.split_right; rb.kchunk = pl.kchunk_right;
+    ORTHO_TRY(launch_dion_right(rb, bf, nb, s));
+    RedArgs rr;
+    rr.part = part_f; rr.part_member_stride = static_cast<int64_t>(mb / 4);
+    rr.slice = n * r; rr.splits = pl.split_right; rr.rows = ni; rr.cols = r;
+    rr.out = tR;
+    rr.colsq = reinterpret_cast<float*>(base + pl.off_colsq);
+    rr.colsq_member_stride = static_cast<int64_t>(mb / 4);
+    ORTHO_TRY(launch_reduce_splits(rr, nb, s));
+    ColnormArgs cn;
+    cn.r = tR; cn.q = tQ; cn.colsq = rr.colsq; cn.colsq_member_stride = rr.colsq_member_stride;
+    cn.nrb = pl.nrb; cn.rows = ni; cn.cols = r; cn.status = status;
+    ORTHO_TRY(launch_colnorm(cn, nb, s));
+
+    if (P_out)
+      ORTHO_TRY(hipMemcpy2DAsync(P_out->data, P_out->ld * 4, base + pl.off_pt, rp * 4, r * 4, m,
+                                 hipMemcpyDeviceToDevice, s));
+    if (R_out)
+      ORTHO_TRY(hipMemcpy2DAsync(R_out->data, R_out->ld * 4, base + pl.off_r, rp * 4, r * 4, n,
+                                 hipMemcpyDeviceToDevice, s));
+
+    // Sweep 3: error feedback into M and the weight update into X.
+    DionUpdateArgs ua;
+    ua.p = tPt; ua.r = tR; ua.q = tQ; ua.m = tM; ua.g = tG; ua.x = tX;
+    ua.c1 = 1.0f - mu; ua.c2 = lr * scale;
+    ua.M = mi; ua.N = ni; ua.rank = r;
+    ORTHO_TRY(launch_dion_update(ua, bf, nb, s));
+  }
+  return ORTHO_OK;
+}
+
+ortho_status run_ns(int32_t batch, const ortho_mat* G, const ortho_mat* Out, int32_t steps,
+                    const float* abc, void* ws, void* stream) {
+  NsPlan pl;
+  if (!plan_ns(G[0].rows, G[0].cols, batch, &pl)) return ORTHO_E_SHAPE;
+  const bool bf = G[0].dtype == ORTHO_BF16;
+  const float a = abc ? abc[0] : kMuonA, b = abc ? abc[1] : kMuonB, c = abc ? abc[2] : kMuonC;
+  const hipStream_t s = as_stream(stream);
+  char* base = static_cast<char*>(ws);
+  const size_t mb = pl.member_bytes;
+  const int M = static_cast<int>(pl.M), N = static_cast<int>(pl.N);
+  const size_t gvec = bf ? 8 : 16;
+
+  for (int b0 = 0; b0 < batch; b0 += pl.chunk) {
+    const int nb = batch - b0 < pl.chunk ? batch - b0 : pl.chunk;
+    const MatArg tG = user_table(G, b0, nb, gvec);
+    const MatArg tOut = user_table(Out, b0, nb, gvec);
+    const MatArg x32 = ws_table(base, mb, pl.off_x32, nb, pl.ld_x, M, N, 4, 16);
+    const MatArg xb[2] = {ws_table(base, mb, pl.off_xb0, nb, pl.ld_x, M, N, 2, 16),
+                          ws_table(base, mb, pl.off_xb1, nb, pl.ld_x, M, N, 2, 16)};
+    const MatArg xbt[2] = {ws_table(base, mb, pl.off_xbt0, nb, pl.ld_xt, N, M, 2, 16),
+                           ws_table(base, mb, pl.off_xbt1, nb, pl.ld_xt, N, M, 2, 16)};
+    const MatArg ta = ws_table(base, mb, pl.off_a, nb, pl.ld_xt, M, M, 2, 16);
+    const MatArg tbp = ws_table(base, mb, pl.off_bp, nb, pl.ld_xt, M, M, 2, 16);
+    const MatArg tbp32 = ws_table(base, mb, pl.off_bp32, nb, pl.ld_xt, M, M, 4, 16);
+    float* partial = reinterpret_cast<float*>(base + pl.off_partial);
+    float* scl = reinterpret_cast<float*>(base + pl.off_scale);
+
+    SumsqArgs sa;
+    sa.g = tG; sa.partial = partial; sa.partial_stride = static_cast<int64_t>(mb / 4);
+    sa.chunk = pl.part_chunk;
+    ORTHO_TRY(launch_sumsq(sa, pl.nparts, nb, bf, s));
+    ORTHO_TRY(launch_ns_scale(partial, static_cast<int64_t>(mb / 4), pl.nparts, scl,
+                              static_cast<int64_t>(mb / 4), kNsEps, nb, s));
+    NsInitArgs ia;
+    ia.g = tG; ia.x32 = x32; ia.xb = xb[0]; ia.xbt = xbt[0];
+    ia.scale = scl; ia.scale_stride = static_cast<int64_t>(mb / 4);
+    ia.M = M; ia.N = N; ia.transposed = pl.transposed;
+    ORTHO_TRY(launch_ns_init(ia, nb, bf, s));
+    if (steps == 0) ORTHO_TRY(launch_ns_store(ia, tOut, nb, bf, s));
+    for (int it = 0; it < steps; ++it) {
+      const int cur = it & 1;
+      NsGramArgs g1;
+      g1.x = xb[cur]; g1.a = ta; g1.M = M; g1.K = N;
+      ORTHO_TRY(launch_ns_gram(g1, nb, s));
+      NsPolyArgs g2;
+      g2.a = ta; g2.bp = tbp; g2.bp32 = tbp32; g2.b = b; g2.c = c; g2.M = M;
+      ORTHO_TRY(launch_ns_poly(g2, nb, s));
+      NsApplyArgs g3;
+      g3.bp = tbp; g3.xbt = xbt[cur]; g3.x32 = x32; g3.xb_next = xb[cur ^ 1];
+      g3.xbt_next = xbt[cur ^ 1]; g3.out = tOut; g3.bp32 = tbp32; g3.a = a;
+      g3.M = M; g3.N = N; g3.last = it == steps - 1; g3.out_transposed = pl.transposed;
+      ORTHO_TRY(launch_ns_apply(g3, bf, nb, s));
+    }
+  }
+  return ORTHO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ortho_dion_workspace_size(int64_t m, int64_t n, int32_t r, int32_t batch) {
+  DionPlan p;
+  return plan_dion(m, n, r, batch, &p) ? p.total_bytes : 0;
+}
+
+size_t ortho_ns_workspace_size(int64_t m, int64_t n, int32_t batch) {
+  NsPlan p;
+  return plan_ns(m, n, batch, &p) ? p.total_bytes : 0;
+}
+
+ortho_status dion_step_ex(ortho_mat X, ortho_mat G, ortho_mat M, ortho_mat Q, int32_t r, float mu,
+                          float lr, float scale, const ortho_mat* P_out, const ortho_mat* R_out,
+                          int32_t* dev_status, void* ws, size_t ws_bytes, void* stream) {
+  const ortho_status st =
+      validate_dion(1, &X, &G, &M, &Q, r, mu, lr, scale, P_out, R_out, ws, ws_bytes);
+  if (st != ORTHO_OK) return st;
+  return run_dion(1, &X, &G, &M, &Q, r, mu, lr, scale, P_out, R_out, dev_status, ws, stream);
+}
+
+ortho_status dion_step(ortho_mat X, ortho_mat G, ortho_mat M, ortho_mat Q, int32_t r, float mu,
+                       float lr, void* ws, size_t ws_bytes, void* stream) {
+  return dion_step_ex(X, G, M, Q, r, mu, lr, 1.0f, nullptr, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+ortho_status dion_step_batched(int32_t batch, const ortho_mat* X, const ortho_mat* G,
+                               const ortho_mat* M, const ortho_mat* Q, int32_t r, float mu, float lr,
+                               float scale, int32_t* dev_status, void* ws, size_t ws_bytes,
+                               void* stream) {
+  const ortho_status st =
+      validate_dion(batch, X, G, M, Q, r, mu, lr, scale, nullptr, nullptr, ws, ws_bytes);
+  if (st != ORTHO_OK) return st;
+  return run_dion(batch, X, G, M, Q, r, mu, lr, scale, nullptr, nullptr, dev_status, ws, stream);
+}
+
+ortho_status newton_schulz(ortho_mat G, ortho_mat Out, int32_t steps, const float* abc, void* ws,
+                           size_t ws_bytes, void* stream) {
+  const ortho_status st = validate_ns(1, &G, &Out, steps, abc, ws, ws_bytes);
+  if (st != ORTHO_OK) return st;
+  return run_ns(1, &G, &Out, steps, abc, ws, stream);
+}
+
+ortho_status newton_schulz_batched(int32_t batch, const ortho_mat* G, const ortho_mat* Out,
+                                   int32_t steps, const float* abc, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  const ortho_status st = validate_ns(batch, G, Out, steps, abc, ws, ws_bytes);
+  if (st != ORTHO_OK) return st;
+  return run_ns(batch, G, Out, steps, abc, ws, stream);
+}
+
+const char* ortho_status_str(int32_t status) {
+  switch (status) {
+    case ORTHO_OK: return "ok";
+    case ORTHO_E_NULL: return "a required pointer is NULL";
+    case ORTHO_E_SHAPE: return "matrix shapes disagree or a dimension is out of range";
+    case ORTHO_E_DTYPE: return "unsupported or mismatched dtype";
+    case ORTHO_E_RANK: return "rank r outside [1, min(m, n)] or different from Q.cols";
+    case ORTHO_E_LAYOUT: return "leading dimension smaller than cols, or differs within a group";
+    case ORTHO_E_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case ORTHO_E_PARAM: return "invalid scalar parameter (mu, lr, scale, abc, steps or batch)";
+    case ORTHO_E_HIP: return "a HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t ortho_abi_version(void) { return ORTHO_ABI_VERSION; }
+
+}  // extern "C"

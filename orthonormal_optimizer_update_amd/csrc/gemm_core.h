@@ -1,0 +1,355 @@
+// Generic LDS-staged MFMA GEMM for gfx950:  C[i, j] = sum_k A[i, k] * Bop[j, k]
+// ("NT" form: both operands are consumed with the reduction index k contiguous
+// in LDS).  Loaders bring a tile of each operand from HBM into registers, turn
+// it into one or two bf16 pieces (x = hi + lo) and store it to LDS in the
+// k-contiguous layout the MFMA fragments want; transposing loaders do the
+// transpose in registers, so every global access stays row-coalesced.
+//
+// Products: PRODS = 1 uses hi*hi; PRODS = 3 adds lo*hi and hi*lo, which gives
+// products close to fp32 accuracy from bf16 matrix cores.  NBOP = 2 runs two
+// right operands against the same left tile with two accumulator sets.
+//
+// Matrix core: v_mfma_f32_32x32x16_bf16.  Each lane supplies eight consecutive
+// k values of one row (lanes 0-31: k 0-7, lanes 32-63: k 8-15) for both A and
+// Bop, so the pairing of k slots is identical for the two operands.  The fp32
+// result of lane l, element e is row 8*(e/4) + 4*(l/32) + e%4, column l%32.
+#pragma once
+
+#include "common.h"
+
+namespace ortho {
+
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int NA_, int NB_, int PRODS_,
+          int NBOP_>
+struct GemmCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int NT = WAVES_M * WAVES_N * 64;
+  static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  static constexpr int MI = WTM / 32, NI = WTN / 32;
+  static constexpr int NA = NA_, NB = NB_, PRODS = PRODS_, NBOP = NBOP_;
+  static constexpr int LDS_LD = BK + 8;  // bf16 elements per LDS row; +16 B breaks bank aliasing
+  static constexpr int A_ELEMS = BM * LDS_LD;
+  static constexpr int B_ELEMS = BN * LDS_LD;
+  static constexpr int STAGE = NA * A_ELEMS + NBOP * NB * B_ELEMS;
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(BK % 16 == 0, "BK must be a multiple of 16");
+  static_assert(PRODS == 1 || (PRODS == 3 && NA == 2 && NB == 2), "bad product set");
+};
+
+// ---------------------------------------------------------------------------
+// Loaders.  A loader instance owns one ROWS x BK tile of one operand.
+// load(row0, k0, kend) issues the global loads for rows [row0, row0+ROWS) and
+// k in [k0, k0+BK) (zero outside the matrix and for k >= kend); store() writes
+// the NP bf16 pieces to LDS (piece p at s + p*pstride, row stride LDS_LD).
+// ---------------------------------------------------------------------------
+
+template <int NP>
+__device__ __forceinline__ void put4(bf16* s, int pstride, float a, float b, float c, float d) {
+  if constexpr (NP == 1) {
+    bf16x4 h = {to_bf16(a), to_bf16(b), to_bf16(c), to_bf16(d)};
+    *reinterpret_cast<bf16x4*>(s) = h;
+  } else {
+    bf16 h0, h1, h2, h3, l0, l1, l2, l3;
+    split_bf16(a, h0, l0);
+    split_bf16(b, h1, l1);
+    split_bf16(c, h2, l2);
+    split_bf16(d, h3, l3);
+    bf16x4 h = {h0, h1, h2, h3};
+    bf16x4 l = {l0, l1, l2, l3};
+    *reinterpret_cast<bf16x4*>(s) = h;
+    *reinterpret_cast<bf16x4*>(s + pstride) = l;
+  }
+}
+
+// Row-major source, k contiguous: element (i, k) = S[i*ld + k].  The source
+// is SRC_T (float or bf16 bits); with ADD = true the element is
+// S[i*ld+k] + S2[i*ld2+k] (momentum plus gradient).
+template <int ROWS, int BK, int NT, int NP, typename SRC_T, bool ADD, typename SRC2_T>
+struct LdRow {
+  static constexpr int CPR = BK / 4;
+  static constexpr int NCH = ROWS * CPR / NT;
+  static_assert(ROWS * CPR % NT == 0, "tile does not divide among threads");
+  const SRC_T* p;
+  const SRC2_T* p2;
+  int64_t ld, ld2;
+  int rows;
+  bool vec;
+  float4 v[NCH];
+
+  __device__ LdRow(const MatArg& a, const MatArg& a2, int bi)
+      : p(static_cast<const SRC_T*>(a.p[bi])),
+        p2(ADD ? static_cast<const SRC2_T*>(a2.p[bi]) : nullptr),
+        ld(a.ld), ld2(a2.ld), rows(a.rows), vec(a.vec && (!ADD || a2.vec)) {}
+
+  __device__ __forceinline__ void load(int row0, int k0, int kend) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int idx = threadIdx.x + c * NT;
+      const int r = idx / CPR, kc = (idx % CPR) * 4;
+      const int gr = row0 + r;
+      if (gr < rows) {
+        v[c] = load4<SRC_T>(p + gr * ld, k0 + kc, kend, vec);
+        if constexpr (ADD) {
+          float4 g = load4<SRC2_T>(p2 + gr * ld2, k0 + kc, kend, vec);
+          v[c].x += g.x; v[c].y += g.y; v[c].z += g.z; v[c].w += g.w;
+        }
+      } else {
+        v[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  }
+
+  template <int LDS_LD>
+  __device__ __forceinline__ void store(bf16* s, int pstride) const {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int idx = threadIdx.x + c * NT;
+      const int r = idx / CPR, kc = (idx % CPR) * 4;
+      put4<NP>(s + r * LDS_LD + kc, pstride, v[c].x, v[c].y, v[c].z, v[c].w);
+    }
+  }
+};
+
+// Row-major bf16 source used as-is (one piece), 8 elements per access.
+template <int ROWS, int BK, int NT>
+struct LdRowBf16 {
+  static constexpr int CPR = BK / 8;
+  static constexpr int NCH = ROWS * CPR / NT;
+  static_assert(ROWS * CPR % NT == 0, "tile does not divide among threads");
+  const uint16_t* p;
+  int64_t ld;
+  int rows;
+  bool vec;
+  uint4 v[NCH];
+
+  __device__ LdRowBf16(const MatArg& a, const MatArg&, int bi)
+      : p(static_cast<const uint16_t*>(a.p[bi])), ld(a.ld), rows(a.rows), vec(a.vec) {}
+
+  __device__ __forceinline__ void load(int row0, int k0, int kend) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int idx = threadIdx.x + c * NT;
+      const int r = idx / CPR, kc = (idx % CPR) * 8;
+      const int gr = row0 + r, gk = k0 + kc;
+      if (gr < rows && vec && gk + 8 <= kend) {
+        v[c] = *reinterpret_cast<const uint4*>(p + gr * ld + gk);
+      } else {
+        uint16_t t[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t[j] = (gr < rows && gk + j < kend) ? p[gr * ld + gk + j] : 0;
+        v[c] = make_uint4(t[0] | (uint32_t(t[1]) << 16), t[2] | (uint32_t(t[3]) << 16),
+                          t[4] | (uint32_t(t[5]) << 16), t[6] | (uint32_t(t[7]) << 16));
+      }
+    }
+  }
+
+  template <int LDS_LD>
+  __device__ __forceinline__ void store(bf16* s, int) const {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int idx = threadIdx.x + c * NT;
+      const int r = idx / CPR, kc = (idx % CPR) * 8;
+      *reinterpret_cast<uint4*>(s + r * LDS_LD + kc) = v[c];
+    }
+  }
+};
+
+// Transposing loader: element (j, k) of the operand is S[k*ld + j] (the source
+// is stored with j contiguous).  Each thread reads a 4(k) x 4(j) block with
+// row-coalesced loads and writes it transposed to LDS.  `rows` is the j extent.
+template <int ROWS, int BK, int NT, int NP, typename SRC_T, bool ADD, typename SRC2_T>
+struct LdCol {
+  static constexpr int JC = ROWS / 4, KC = BK / 4;
+  static constexpr int NCH = JC * KC / NT;
+  static_assert(JC * KC % NT == 0, "tile does not divide among threads");
+  const SRC_T* p;
+  const SRC2_T* p2;
+  int64_t ld, ld2;
+  int rows;
+  bool vec;
+  float4 v[NCH][4];
+
+  __device__ LdCol(const MatArg& a, const MatArg& a2, int bi)
+      : p(static_cast<const SRC_T*>(a.p[bi])),
+        p2(ADD ? static_cast<const SRC2_T*>(a2.p[bi]) : nullptr),
+        ld(a.ld), ld2(a2.ld), rows(a.rows), vec(a.vec && (!ADD || a2.vec)) {}
+
+  __device__ __forceinline__ void load(int row0, int k0, int kend) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int idx = threadIdx.x + c * NT;
+      const int jc = (idx % JC) * 4, kc = (idx / JC) * 4;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int gk = k0 + kc + t;
+        if (gk < kend) {
+          v[c][t] = load4<SRC_T>(p + gk * ld, row0 + jc, rows, vec);
+          if constexpr (ADD) {
+            float4 g = load4<SRC2_T>(p2 + gk * ld2, row0 + jc, rows, vec);
+            v[c][t].x += g.x; v[c][t].y += g.y; v[c][t].z += g.z; v[c][t].w += g.w;
+          }
+        } else {
+          v[c][t] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+    }
+  }
+
+  template <int LDS_LD>
+  __device__ __forceinline__ void store(bf16* s, int pstride) const {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int idx = threadIdx.x + c * NT;
+      const int jc = (idx % JC) * 4, kc = (idx / JC) * 4;
+      put4<NP>(s + (jc + 0) * LDS_LD + kc, pstride, v[c][0].x, v[c][1].x, v[c][2].x, v[c][3].x);
+      put4<NP>(s + (jc + 1) * LDS_LD + kc, pstride, v[c][0].y, v[c][1].y, v[c][2].y, v[c][3].y);
+      put4<NP>(s + (jc + 2) * LDS_LD + kc, pstride, v[c][0].z, v[c][1].z, v[c][2].z, v[c][3].z);
+      put4<NP>(s + (jc + 3) * LDS_LD + kc, pstride, v[c][0].w, v[c][1].w, v[c][2].w, v[c][3].w);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Kernel parameters and body
+// ---------------------------------------------------------------------------
+
+template <typename EpiArgs>
+struct GemmParams {
+  MatArg a, a2;      // left operand (a2: second source when the loader adds two)
+  MatArg b0, b0s;    // right operand 0 (b0s: second source)
+  MatArg b1, b1s;    // right operand 1 (NBOP = 2 only)
+  EpiArgs e;
+  int M, N, K;       // C is M x N, reduction length K
+  int tiles_n;       // column tiles
+  int splits;        // split-K factor (blockIdx.y = member * splits + split)
+  int kchunk;        // k range per split, a multiple of BK
+  int tri;           // right operand is zero for k > j (triangular factor)
+};
+
+template <class Cfg, class LA, class LB, class Epi>
+__global__ __launch_bounds__(Cfg::NT) void gemm_kernel(GemmParams<typename Epi::Args> p) {
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * Cfg::STAGE];
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, LDS_LD = Cfg::LDS_LD;
+  constexpr int MI = Cfg::MI, NI = Cfg::NI, NBOP = Cfg::NBOP;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
+
+  // Consecutive workgroup ids go round-robin over the 8 XCDs; give each XCD a
+  // contiguous run of tiles so that neighbouring tiles share its L2.
+  int bid = blockIdx.x;
+  const int nwg = gridDim.x;
+  if ((nwg & 7) == 0) bid = (bid & 7) * (nwg >> 3) + (bid >> 3);
+  const int tm = bid / p.tiles_n, tn = bid % p.tiles_n;
+  const int bi = blockIdx.y / p.splits, split = blockIdx.y % p.splits;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kbeg = split * p.kchunk;
+  int kend = min(p.K, kbeg + p.kchunk);
+  if (p.tri) kend = min(kend, n0 + BN);
+  const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+
+  floatx16 acc[NBOP][MI][NI];
+#pragma unroll
+  for (int q = 0; q < NBOP; ++q)
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[q][i][j][e] = 0.f;
+
+  LA la(p.a, p.a2, bi);
+  LB lb0(p.b0, p.b0s, bi);
+  LB lb1(NBOP == 2 ? p.b1 : p.b0, NBOP == 2 ? p.b1s : p.b0s, bi);
+
+  auto stage_a = [&](int s) { return smem + s * Cfg::STAGE; };
+  auto stage_b = [&](int s, int q) {
+    return smem + s * Cfg::STAGE + Cfg::NA * Cfg::A_ELEMS + q * Cfg::NB * Cfg::B_ELEMS;
+  };
+
+  if (nk > 0) {
+    la.load(m0, kbeg, kend);
+    lb0.load(n0, kbeg, kend);
+    if constexpr (NBOP == 2) lb1.load(n0, kbeg, kend);
+    la.template store<LDS_LD>(stage_a(0), Cfg::A_ELEMS);
+    lb0.template store<LDS_LD>(stage_b(0, 0), Cfg::B_ELEMS);
+    if constexpr (NBOP == 2) lb1.template store<LDS_LD>(stage_b(0, 1), Cfg::B_ELEMS);
+  }
+
+  const int frag_row = lane & 31;
+  const int frag_k = (lane >> 5) * 8;
+
+  for (int kt = 0; kt < nk; ++kt) {
+    __syncthreads();
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      const int kn = kbeg + (kt + 1) * BK;
+      la.load(m0, kn, kend);
+      lb0.load(n0, kn, kend);
+      if constexpr (NBOP == 2) lb1.load(n0, kn, kend);
+    }
+    const bf16* sa = stage_a(cur);
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 16) {
+      bf16x8 af[Cfg::NA][MI];
+#pragma unroll
+      for (int pa = 0; pa < Cfg::NA; ++pa)
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+          af[pa][i] = *reinterpret_cast<const bf16x8*>(
+              sa + pa * Cfg::A_ELEMS + (wm * Cfg::WTM + i * 32 + frag_row) * LDS_LD + kk + frag_k);
+#pragma unroll
+      for (int q = 0; q < NBOP; ++q) {
+        const bf16* sb = stage_b(cur, q);
+        bf16x8 bfr[Cfg::NB][NI];
+#pragma unroll
+        for (int pb = 0; pb < Cfg::NB; ++pb)
+#pragma unroll
+          for (int j = 0; j < NI; ++j)
+            bfr[pb][j] = *reinterpret_cast<const bf16x8*>(
+                sb + pb * Cfg::B_ELEMS + (wn * Cfg::WTN + j * 32 + frag_row) * LDS_LD + kk + frag_k);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NI; ++j) {
+            if constexpr (Cfg::PRODS == 3) {
+              acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], bfr[0][j], acc[q][i][j], 0, 0, 0);
+              acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bfr[1][j], acc[q][i][j], 0, 0, 0);
+            }
+            acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bfr[0][j], acc[q][i][j], 0, 0, 0);
+          }
+      }
+    }
+    if (more) {
+      const int nxt = cur ^ 1;
+      la.template store<LDS_LD>(stage_a(nxt), Cfg::A_ELEMS);
+      lb0.template store<LDS_LD>(stage_b(nxt, 0), Cfg::B_ELEMS);
+      if constexpr (NBOP == 2) lb1.template store<LDS_LD>(stage_b(nxt, 1), Cfg::B_ELEMS);
+    }
+  }
+
+  // Epilogue: hand each lane's four consecutive rows of one column to the
+  // policy, which applies bounds and writes.
+  Epi epi(p.e, bi, split);
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int row0 = m0 + wm * Cfg::WTM + i * 32 + g * 8 + (lane >> 5) * 4;
+        const int col = n0 + wn * Cfg::WTN + j * 32 + (lane & 31);
+        if constexpr (NBOP == 1) {
+          epi.apply(row0, col, p.M, p.N, acc[0][i][j][g * 4 + 0], acc[0][i][j][g * 4 + 1],
+                    acc[0][i][j][g * 4 + 2], acc[0][i][j][g * 4 + 3]);
+        } else {
+          epi.apply2(row0, col, p.M, p.N, acc[0][i][j][g * 4 + 0], acc[0][i][j][g * 4 + 1],
+                     acc[0][i][j][g * 4 + 2], acc[0][i][j][g * 4 + 3], acc[1][i][j][g * 4 + 0],
+                     acc[1][i][j][g * 4 + 1], acc[1][i][j][g * 4 + 2], acc[1][i][j][g * 4 + 3]);
+        }
+      }
+}
+
+}  // namespace ortho

@@ -1,0 +1,504 @@
+// Reductions, normalisations and the small dense r x r linear algebra of the
+// Dion orthonormalisation, for gfx950.
+#include "common.h"
+#include "launch.h"
+
+namespace ortho {
+
+// ---------------------------------------------------------------------------
+// Split-K reduction:  out[i][j] = sum_s part[s][i][j], summed in slice order
+// (deterministic).  With colsq != nullptr the kernel also writes, per 64-row
+// block, the sum of squares of each output column (for the column norms).
+// grid (ceil(cols/64), ceil(rows/64), members); 256 threads = 64 cols x 4.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void reduce_splits_kernel(RedArgs a) {
+  __shared__ float red[4][64];
+  const int bi = blockIdx.z;
+  const float* part = a.part + bi * a.part_member_stride;
+  float* out = static_cast<float*>(const_cast<void*>(a.out.p[bi]));
+  const int c = blockIdx.x * 64 + (threadIdx.x & 63);
+  const int rg = threadIdx.x >> 6;
+  const int rbase = blockIdx.y * 64;
+  float sq = 0.f;
+  if (c < a.cols) {
+    for (int rr = rg; rr < 64; rr += 4) {
+      const int r = rbase + rr;
+      if (r >= a.rows) break;
+      float s = 0.f;
+      for (int k = 0; k < a.splits; ++k) s += part[k * a.slice + (int64_t)r * a.cols + c];
+      out[(int64_t)r * a.out.ld + c] = s;
+      sq += s * s;
+    }
+  }
+  if (a.colsq) {
+    red[rg][threadIdx.x & 63] = sq;
+    __syncthreads();
+    if (rg == 0 && c < a.cols) {
+      const float t = red[0][threadIdx.x] + red[1][threadIdx.x] + red[2][threadIdx.x] + red[3][threadIdx.x];
+      a.colsq[bi * a.colsq_member_stride + (int64_t)blockIdx.y * a.cols + c] = t;
+    }
+  }
+}
+
+// Column normalisation Q'[:, j] = R[:, j] / |R[:, j]|, from the per-row-block
+// column sums of squares (summed in block order).  A zero column gives a zero
+// column and sets ORTHO_DEV_ZERO_COLUMN.
+__global__ __launch_bounds__(256) void colnorm_kernel(ColnormArgs a) {
+  __shared__ float inv[64];
+  const int bi = blockIdx.z;
+  const int c0 = blockIdx.x * 64;
+  if (threadIdx.x < 64) {
+    const int c = c0 + threadIdx.x;
+    float v = 0.f;
+    if (c < a.cols) {
+      const float* cs = a.colsq + bi * a.colsq_member_stride;
+      float s = 0.f;
+      for (int b = 0; b < a.nrb; ++b) s += cs[(int64_t)b * a.cols + c];
+      if (s > 0.f) {
+        v = 1.0f / sqrtf(s);
+      } else if (!(s != s)) {
+        v = 0.f;
+        if (a.status && blockIdx.y == 0) atomicOr(a.status, 2);
+      } else {
+        v = s;  // NaN propagates
+      }
+    }
+    inv[threadIdx.x] = v;
+  }
+  __syncthreads();
+  const float* r = static_cast<const float*>(a.r.p[bi]);
+  float* q = static_cast<float*>(const_cast<void*>(a.q.p[bi]));
+  const int cc = threadIdx.x & 63;
+  const int c = c0 + cc;
+  if (c >= a.cols) return;
+  for (int rr = threadIdx.x >> 6; rr < 64; rr += 4) {
+    const int row = blockIdx.y * 64 + rr;
+    if (row >= a.rows) break;
+    q[(int64_t)row * a.q.ld + c] = r[(int64_t)row * a.r.ld + c] * inv[cc];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Newton-Schulz normalisation
+// ---------------------------------------------------------------------------
+
+// Partial sums of squares of G: block b of member bi covers elements
+// [b*chunk, (b+1)*chunk) in row-major order of the logical m x n matrix.
+template <typename T>
+__global__ __launch_bounds__(256) void sumsq_kernel(SumsqArgs a) {
+  __shared__ float red[256];
+  const int bi = blockIdx.y;
+  const T* g = static_cast<const T*>(a.g.p[bi]);
+  const int64_t total = (int64_t)a.g.rows * a.g.cols;
+  const int64_t beg = (int64_t)blockIdx.x * a.chunk;
+  const int64_t end = beg + a.chunk < total ? beg + a.chunk : total;
+  float s = 0.f;
+  for (int64_t e = beg + threadIdx.x; e < end; e += 256) {
+    const int64_t r = e / a.g.cols, c = e % a.g.cols;
+    const float v = load_as_f32<T>(g, r * a.g.ld + c);
+    s += v * v;
+  }
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) a.partial[bi * a.partial_stride + blockIdx.x] = red[0];
+}
+
+// scale = 1 / (sqrt(sum of partials) + eps), summed in fp64 in block order.
+__global__ __launch_bounds__(64) void ns_scale_kernel(const float* partial, int64_t partial_stride,
+                                                      int nparts, float* scale, int64_t scale_stride,
+                                                      float eps) {
+  if (threadIdx.x != 0) return;
+  const int bi = blockIdx.x;
+  double s = 0.0;
+  for (int i = 0; i < nparts; ++i) s += partial[bi * partial_stride + i];
+  scale[bi * scale_stride] = static_cast<float>(1.0 / (sqrt(s) + (double)eps));
+}
+
+// X0 = scale * G (wide orientation: rows <= cols, transposing a tall G), into
+// the fp32 iterate and its two bf16 copies.  64 x 64 tiles through LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void ns_init_kernel(NsInitArgs a) {
+  __shared__ float tile[64][65];
+  const int bi = blockIdx.z;
+  const T* g = static_cast<const T*>(a.g.p[bi]);
+  float* x32 = static_cast<float*>(const_cast<void*>(a.x32.p[bi]));
+  uint16_t* xb = static_cast<uint16_t*>(const_cast<void*>(a.xb.p[bi]));
+  uint16_t* xbt = static_cast<uint16_t*>(const_cast<void*>(a.xbt.p[bi]));
+  const float sc = a.scale[bi * a.scale_stride];
+  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;  // tile of X (M x N)
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  // Load tile[ii][jj] = X[i0+ii][j0+jj], reading G row-coalesced.
+  for (int k = ty; k < 64; k += 4) {
+    if (!a.transposed) {
+      const int i = i0 + k, j = j0 + tx;
+      tile[k][tx] = (i < a.M && j < a.N) ? load_as_f32<T>(g, (int64_t)i * a.g.ld + j) * sc : 0.f;
+    } else {
+      const int j = j0 + k, i = i0 + tx;  // X[i][j] = G[j][i]
+      tile[tx][k] = (i < a.M && j < a.N) ? load_as_f32<T>(g, (int64_t)j * a.g.ld + i) * sc : 0.f;
+    }
+  }
+  __syncthreads();
+  for (int k = ty; k < 64; k += 4) {
+    const int i = i0 + k, j = j0 + tx;
+    if (i < a.M && j < a.N) {
+      const float v = tile[k][tx];
+      x32[(int64_t)i * a.x32.ld + j] = v;
+      xb[(int64_t)i * a.xb.ld + j] = to_bf16_bits(v);
+    }
+    const int jt = j0 + k, it = i0 + tx;  // X^T[jt][it]
+    if (it < a.M && jt < a.N) xbt[(int64_t)jt * a.xbt.ld + it] = to_bf16_bits(tile[tx][k]);
+  }
+}
+
+// Out = X (the normalised input) when no iteration is requested, in the
+// caller's dtype and orientation.
+template <typename T>
+__global__ __launch_bounds__(256) void ns_store_kernel(NsInitArgs a, MatArg out) {
+  const int bi = blockIdx.z;
+  const float* x32 = static_cast<const float*>(a.x32.p[bi]);
+  T* o = static_cast<T*>(const_cast<void*>(out.p[bi]));
+  const int i = blockIdx.y * 16 + (threadIdx.x >> 4);
+  const int j = blockIdx.x * 16 + (threadIdx.x & 15);
+  if (i >= a.M || j >= a.N) return;
+  const float v = x32[(int64_t)i * a.x32.ld + j];
+  if (a.transposed) store_from_f32<T>(o, (int64_t)j * out.ld + i, v);
+  else store_from_f32<T>(o, (int64_t)i * out.ld + j, v);
+}
+
+// ---------------------------------------------------------------------------
+// fp64 Gram  W = P^T P  over rows [kbeg, kend) of P (m x r, fp32), lower
+// 64 x 64 tiles only, one split-K slice per blockIdx.y.  v_mfma_f64_16x16x4_f64:
+// lane l supplies row (l%16) and k = l/16 of each operand; result element e of
+// lane l is row l/16 + 4*e, column l%16 of the 16 x 16 tile (rows interleave
+// across the four result registers, unlike the fp32-result instructions).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gram64_kernel(Gram64Args a) {
+  __shared__ double sa[32][66];
+  __shared__ double sb[32][66];
+  const int member = blockIdx.z;
+  const float* P = static_cast<const float*>(a.p.p[member]);
+  double* part = a.part + member * a.part_member_stride + blockIdx.y * a.slice;
+  // lower-triangular tile decode: t -> (ta, tb), tb <= ta
+  const int t = blockIdx.x;
+  int ta = static_cast<int>((sqrt(8.0 * t + 1.0) - 1.0) * 0.5);
+  while ((ta + 1) * (ta + 2) / 2 <= t) ++ta;
+  while (ta * (ta + 1) / 2 > t) --ta;
+  const int tb = t - ta * (ta + 1) / 2;
+  const int a0 = ta * 64, b0 = tb * 64;
+  const int r = a.r;
+  const int kbeg = blockIdx.y * a.kchunk;
+  const int kend = min(a.m, kbeg + a.kchunk);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wa = wave >> 1, wb = wave & 1;
+  doublex4 acc[2][2];
+  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 2; ++j) acc[i][j] = doublex4{0.0, 0.0, 0.0, 0.0};
+  for (int k0 = kbeg; k0 < kend; k0 += 32) {
+    // 32 rows x 64 cols of each operand; 256 threads x 8 elements
+    for (int e = threadIdx.x; e < 32 * 64; e += 256) {
+      const int kr = e >> 6, cc = e & 63;
+      const int gk = k0 + kr;
+      const bool okk = gk < kend;
+      sa[kr][cc] = (okk && a0 + cc < r) ? (double)P[(int64_t)gk * a.p.ld + a0 + cc] : 0.0;
+      sb[kr][cc] = (okk && b0 + cc < r) ? (double)P[(int64_t)gk * a.p.ld + b0 + cc] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 32; kk += 4) {
+      double af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) af[i] = sa[kk + (lane >> 4)][wa * 32 + i * 16 + (lane & 15)];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bf[j] = sb[kk + (lane >> 4)][wb * 32 + j * 16 + (lane & 15)];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = a0 + wa * 32 + i * 16 + (lane >> 4) + 4 * e;
+        const int col = b0 + wb * 32 + j * 16 + (lane & 15);
+        if (row < r && col < r) part[(int64_t)row * r + col] = acc[i][j][e];
+      }
+}
+
+// Sum the Gram slices and scale to unit diagonal: S = D W D with
+// d_i = 1 / sqrt(W_ii) (lower triangle), zero the inverse buffer, write d.
+__global__ __launch_bounds__(256) void chol_prep_kernel(CholArgs a) {
+  const int member = blockIdx.z;
+  const double* part = a.part + member * a.part_member_stride;
+  double* S = a.s + member * a.mat_stride;
+  double* X = a.x + member * a.mat_stride;
+  double* d = a.d + member * a.vec_stride;
+  const int r = a.r;
+  const int i = blockIdx.y * 16 + (threadIdx.x >> 4);
+  const int j = blockIdx.x * 16 + (threadIdx.x & 15);
+  if (i >= r || j >= r) return;
+  X[(int64_t)i * r + j] = 0.0;
+  if (j > i) return;
+  auto sum = [&](int u, int v) {
+    double s = 0.0;
+    for (int k = 0; k < a.splits; ++k) s += part[k * a.slice + (int64_t)u * r + v];
+    return s;
+  };
+  const double wii = sum(i, i), wjj = sum(j, j);
+  const double di = wii > 0.0 ? 1.0 / sqrt(wii) : 1.0;
+  const double dj = wjj > 0.0 ? 1.0 / sqrt(wjj) : 1.0;
+  S[(int64_t)i * r + j] = sum(i, j) * di * dj;
+  if (i == j) d[i] = di;
+}
+
+// Factor the nb x nb diagonal block k of S in LDS (S_kk = L_kk L_kk^T), write
+// L_kk back, and write its inverse as block (k, k) of X.  A pivot that is not
+// positive is replaced by a tiny positive shift and flagged.
+__global__ __launch_bounds__(256) void chol_diag_kernel(CholArgs a, int kb) {
+  __shared__ double L[64][65];
+  __shared__ double Xi[64][65];
+  const int member = blockIdx.x;
+  double* S = a.s + member * a.mat_stride;
+  double* X = a.x + member * a.mat_stride;
+  const int r = a.r;
+  const int o = kb * 64;
+  const int nb = min(64, r - o);
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int i = e >> 6, j = e & 63;
+    L[i][j] = (i < nb && j <= i) ? S[(int64_t)(o + i) * r + o + j] : 0.0;
+    Xi[i][j] = 0.0;
+  }
+  __syncthreads();
+  for (int j = 0; j < nb; ++j) {
+    if (threadIdx.x == 0) {
+      double piv = L[j][j];
+      if (!(piv > 1e-14) && piv == piv) {
+        piv = 1e-14;
+        if (a.status) atomicOr(a.status, 1);
+      }
+      L[j][j] = sqrt(piv);
+    }
+    __syncthreads();
+    const double ljj = L[j][j];
+    for (int i = j + 1 + threadIdx.x; i < nb; i += 256) L[i][j] /= ljj;
+    __syncthreads();
+    const int T = nb - j - 1;
+    for (int e = threadIdx.x; e < T * T; e += 256) {
+      const int ii = j + 1 + e / T, cc = j + 1 + e % T;
+      if (cc <= ii) L[ii][cc] -= L[ii][j] * L[cc][j];
+    }
+    __syncthreads();  // the next pivot and column read the updated trailing block
+  }
+  __syncthreads();
+  // Inverse of the lower-triangular L: one column per thread.
+  if (threadIdx.x < nb) {
+    const int c = threadIdx.x;
+    Xi[c][c] = 1.0 / L[c][c];
+    for (int i = c + 1; i < nb; ++i) {
+      double s = 0.0;
+      for (int t = c; t < i; ++t) s += L[i][t] * Xi[t][c];
+      Xi[i][c] = -s / L[i][i];
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int i = e >> 6, j = e & 63;
+    if (i < nb && j <= i) {
+      S[(int64_t)(o + i) * r + o + j] = L[i][j];
+      X[(int64_t)(o + i) * r + o + j] = Xi[i][j];
+    }
+  }
+}
+
+// C (64 x 64 tile) = A * B^T (TRANS_B) or A * B, fp64, K = 64, A and B tiles
+// read from row-major r x r matrices.  Each thread owns a 4 x 4 block.
+template <bool TRANS_B>
+__device__ void tile_gemm64(const double* A, const double* B, int r, int ar, int ac, int br,
+                            int bc, double (*sA)[65], double (*sB)[65], double acc[4][4]) {
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int i = e >> 6, j = e & 63;
+    sA[i][j] = (ar + i < r && ac + j < r) ? A[(int64_t)(ar + i) * r + ac + j] : 0.0;
+    sB[i][j] = (br + i < r && bc + j < r) ? B[(int64_t)(br + i) * r + bc + j] : 0.0;
+  }
+  __syncthreads();
+  const int ti = (threadIdx.x >> 4) * 4, tj = (threadIdx.x & 15) * 4;
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+  for (int t = 0; t < 64; ++t) {
+    double av[4], bv[4];
+    for (int i = 0; i < 4; ++i) av[i] = sA[ti + i][t];
+    for (int j = 0; j < 4; ++j) bv[j] = TRANS_B ? sB[tj + j][t] : sB[t][tj + j];
+    for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 4; ++j) acc[i][j] += av[i] * bv[j];
+  }
+  __syncthreads();
+}
+
+// Panel step for block column kb (tile index t):
+//   t <  T:  L_ik = S_ik * Linv_kk^T        for i = kb + 1 + t
+//   t >= T:  X_kj = Linv_kk * Y_kj           for j = t - T  (j < kb)
+__global__ __launch_bounds__(256) void chol_panel_kernel(CholArgs a, int kb) {
+  __shared__ double sA[64][65];
+  __shared__ double sB[64][65];
+  const int member = blockIdx.y;
+  double* S = a.s + member * a.mat_stride;
+  double* X = a.x + member * a.mat_stride;
+  const int r = a.r, nblk = (r + 63) / 64;
+  const int T = nblk - kb - 1;
+  const int t = blockIdx.x;
+  double acc[4][4];
+  int orow, ocol;
+  double* out;
+  if (t < T) {
+    const int ib = kb + 1 + t;
+    tile_gemm64<true>(S, X, r, ib * 64, kb * 64, kb * 64, kb * 64, sA, sB, acc);
+    out = S; orow = ib * 64; ocol = kb * 64;
+  } else {
+    const int jb = t - T;
+    tile_gemm64<false>(X, X, r, kb * 64, kb * 64, kb * 64, jb * 64, sA, sB, acc);
+    out = X; orow = kb * 64; ocol = jb * 64;
+  }
+  const int ti = (threadIdx.x >> 4) * 4, tj = (threadIdx.x & 15) * 4;
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j)
+      if (orow + ti + i < r && ocol + tj + j < r) out[(int64_t)(orow + ti + i) * r + ocol + tj + j] = acc[i][j];
+}
+
+// Trailing update after block column kb (tile index t):
+//   t <  T(T+1)/2:  S_ij -= L_ik L_jk^T   for kb < j <= i
+//   otherwise:      Y_ij -= L_ik X_kj     for i > kb, j <= kb
+__global__ __launch_bounds__(256) void chol_update_kernel(CholArgs a, int kb) {
+  __shared__ double sA[64][65];
+  __shared__ double sB[64][65];
+  const int member = blockIdx.y;
+  double* S = a.s + member * a.mat_stride;
+  double* X = a.x + member * a.mat_stride;
+  const int r = a.r, nblk = (r + 63) / 64;
+  const int T = nblk - kb - 1;
+  const int ntri = T * (T + 1) / 2;
+  int t = blockIdx.x;
+  double acc[4][4];
+  int ib, jb;
+  double* out;
+  if (t < ntri) {
+    int ti = static_cast<int>((sqrt(8.0 * t + 1.0) - 1.0) * 0.5);
+    while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
+    while (ti * (ti + 1) / 2 > t) --ti;
+    const int tj = t - ti * (ti + 1) / 2;
+    ib = kb + 1 + ti;
+    jb = kb + 1 + tj;
+    tile_gemm64<true>(S, S, r, ib * 64, kb * 64, jb * 64, kb * 64, sA, sB, acc);
+    out = S;
+  } else {
+    t -= ntri;
+    ib = kb + 1 + t / (kb + 1);
+    jb = t % (kb + 1);
+    tile_gemm64<false>(S, X, r, ib * 64, kb * 64, kb * 64, jb * 64, sA, sB, acc);
+    out = X;
+  }
+  const int ti = (threadIdx.x >> 4) * 4, tj = (threadIdx.x & 15) * 4;
+  const int orow = ib * 64, ocol = jb * 64;
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j) {
+      const int rr = orow + ti + i, cc = ocol + tj + j;
+      if (rr < r && cc < r && (out == X || cc <= rr)) out[(int64_t)rr * r + cc] -= acc[i][j];
+    }
+}
+
+// T^T[j][k] = Linv[j][k] * d[k] for k <= j, else 0, as fp32: the right factor
+// of P1 = P_tilde * T with T = D L^{-T} upper triangular.
+__global__ __launch_bounds__(256) void make_t_kernel(CholArgs a, float* tt, int64_t tt_stride) {
+  const int member = blockIdx.z;
+  const double* X = a.x + member * a.mat_stride;
+  const double* d = a.d + member * a.vec_stride;
+  float* out = tt + member * tt_stride;
+  const int r = a.r;
+  const int j = blockIdx.y * 16 + (threadIdx.x >> 4);
+  const int k = blockIdx.x * 16 + (threadIdx.x & 15);
+  if (j >= r || k >= r) return;
+  out[(int64_t)j * r + k] = k <= j ? static_cast<float>(X[(int64_t)j * r + k] * d[k]) : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+static inline int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
+
+hipError_t launch_reduce_splits(const RedArgs& a, int members, hipStream_t s) {
+  dim3 grid(cdiv(a.cols, 64), cdiv(a.rows, 64), members);
+  hipLaunchKernelGGL(reduce_splits_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_colnorm(const ColnormArgs& a, int members, hipStream_t s) {
+  dim3 grid(cdiv(a.cols, 64), cdiv(a.rows, 64), members);
+  hipLaunchKernelGGL(colnorm_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sumsq(const SumsqArgs& a, int nblocks, int members, bool bf16, hipStream_t s) {
+  dim3 grid(nblocks, members);
+  if (bf16) hipLaunchKernelGGL(sumsq_kernel<uint16_t>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(sumsq_kernel<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ns_scale(const float* partial, int64_t partial_stride, int nparts, float* scale,
+                           int64_t scale_stride, float eps, int members, hipStream_t s) {
+  hipLaunchKernelGGL(ns_scale_kernel, dim3(members), dim3(64), 0, s, partial, partial_stride, nparts,
+                     scale, scale_stride, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_ns_init(const NsInitArgs& a, int members, bool bf16, hipStream_t s) {
+  dim3 grid(cdiv(a.N, 64), cdiv(a.M, 64), members);
+  if (bf16) hipLaunchKernelGGL(ns_init_kernel<uint16_t>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(ns_init_kernel<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ns_store(const NsInitArgs& a, const MatArg& out, int members, bool bf16,
+                           hipStream_t s) {
+  dim3 grid(cdiv(a.N, 16), cdiv(a.M, 16), members);
+  if (bf16) hipLaunchKernelGGL(ns_store_kernel<uint16_t>, grid, dim3(256), 0, s, a, out);
+  else hipLaunchKernelGGL(ns_store_kernel<float>, grid, dim3(256), 0, s, a, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_gram64(const Gram64Args& a, int splits, int members, hipStream_t s) {
+  const int tb = cdiv(a.r, 64);
+  dim3 grid(tb * (tb + 1) / 2, splits, members);
+  hipLaunchKernelGGL(gram64_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// Cholesky of the scaled Gram, its inverse, and T^T, for every member.
+hipError_t launch_cholesky_inverse(const CholArgs& a, float* tt, int64_t tt_stride, int members,
+                                   hipStream_t s) {
+  const int r = a.r, nblk = cdiv(r, 64);
+  hipLaunchKernelGGL(chol_prep_kernel, dim3(cdiv(r, 16), cdiv(r, 16), members), dim3(256), 0, s, a);
+  for (int kb = 0; kb < nblk; ++kb) {
+    hipLaunchKernelGGL(chol_diag_kernel, dim3(members), dim3(256), 0, s, a, kb);
+    const int T = nblk - kb - 1;
+    const int npanel = T + kb;
+    if (npanel > 0)
+      hipLaunchKernelGGL(chol_panel_kernel, dim3(npanel, members), dim3(256), 0, s, a, kb);
+    const int nupd = T * (T + 1) / 2 + T * (kb + 1);
+    if (nupd > 0)
+      hipLaunchKernelGGL(chol_update_kernel, dim3(nupd, members), dim3(256), 0, s, a, kb);
+  }
+  hipLaunchKernelGGL(make_t_kernel, dim3(cdiv(r, 16), cdiv(r, 16), members), dim3(256), 0, s, a, tt,
+                     tt_stride);
+  return hipGetLastError();
+}
+
+}  // namespace ortho

@@ -1,0 +1,189 @@
+// Instantiations of the MFMA GEMM core for every contraction of the Dion and
+// Newton-Schulz paths, and their host launchers.
+#include "epilogues.h"
+#include "gemm_core.h"
+#include "launch.h"
+
+namespace ortho {
+
+namespace {
+
+inline int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
+
+template <class Cfg, class LA, class LB, class Epi>
+hipError_t run(GemmParams<typename Epi::Args>& p, int members, hipStream_t s) {
+  if (p.M <= 0 || p.N <= 0 || members <= 0) return hipSuccess;
+  const int tm = cdiv(p.M, Cfg::BM), tn = cdiv(p.N, Cfg::BN);
+  p.tiles_n = tn;
+  if (p.splits < 1) p.splits = 1;
+  if (p.kchunk <= 0) p.kchunk = cdiv(p.K, Cfg::BK) * Cfg::BK;
+  dim3 grid(tm * tn, members * p.splits);
+  hipLaunchKernelGGL((gemm_kernel<Cfg, LA, LB, Epi>), grid, dim3(Cfg::NT), 0, s, p);
+  return hipGetLastError();
+}
+
+MatArg with_rows(MatArg a, int rows) {
+  a.rows = rows;
+  return a;
+}
+
+// Tall-skinny Dion contractions: 128 x 128 tiles, 4 waves, two bf16 pieces per
+// operand and three products (hi*hi + lo*hi + hi*lo).
+using CfgSplit = GemmCfg<128, 128, 32, 2, 2, 2, 2, 3, 1>;
+// Dion sweep 3 with bf16 weights: one product, two right operands.
+using CfgUpdBf = GemmCfg<128, 128, 32, 2, 2, 1, 1, 1, 2>;
+// Dion sweep 3 with fp32 weights: split products, two right operands.
+using CfgUpdF32 = GemmCfg<128, 128, 32, 2, 2, 2, 2, 3, 2>;
+// Newton-Schulz: 256 x 256 tiles with 8 waves for large matrices, 128 x 128
+// with 4 waves when the Gram side is small.
+using CfgNsBig = GemmCfg<256, 256, 32, 2, 4, 1, 1, 1, 1>;
+using CfgNsSmall = GemmCfg<128, 128, 32, 2, 2, 1, 1, 1, 1>;
+
+template <int ROWS, int NT, int NP>
+using RowF32 = LdRow<ROWS, 32, NT, NP, float, false, float>;
+template <int ROWS, int NT, int NP, typename GT>
+using RowMG = LdRow<ROWS, 32, NT, NP, float, true, GT>;
+template <int ROWS, int NT, int NP>
+using ColF32 = LdCol<ROWS, 32, NT, NP, float, false, float>;
+template <int ROWS, int NT, int NP, typename GT>
+using ColMG = LdCol<ROWS, 32, NT, NP, float, true, GT>;
+
+template <typename GT>
+hipError_t dion_left_t(const DionLeftArgs& a, int members, hipStream_t s) {
+  GemmParams<EpiStoreF32::Args> p{};
+  p.a = with_rows(a.m, a.M);
+  p.a2 = with_rows(a.g, a.M);
+  p.b0 = with_rows(a.q, a.r);  // element (j, k) = Q[k][j]
+  p.e.c = a.out;
+  p.e.split_stride = a.splits > 1 ? a.split_stride : 0;
+  p.e.has_t = 0;
+  p.M = a.M; p.N = a.r; p.K = a.N;
+  p.splits = a.splits; p.kchunk = a.kchunk; p.tri = 0;
+  return run<CfgSplit, RowMG<128, 256, 2, GT>, ColF32<128, 256, 2>, EpiStoreF32>(p, members, s);
+}
+
+template <typename GT>
+hipError_t dion_right_t(const DionRightArgs& a, int members, hipStream_t s) {
+  GemmParams<EpiStoreF32::Args> p{};
+  p.a = with_rows(a.m, a.N);   // element (j, i) = M[i][j] + G[i][j]
+  p.a2 = with_rows(a.g, a.N);
+  p.b0 = with_rows(a.p, a.r);  // element (k, i) = P[i][k]
+  p.e.c = a.out;
+  p.e.split_stride = a.splits > 1 ? a.split_stride : 0;
+  p.e.has_t = 0;
+  p.M = a.N; p.N = a.r; p.K = a.M;
+  p.splits = a.splits; p.kchunk = a.kchunk; p.tri = 0;
+  return run<CfgSplit, ColMG<128, 256, 2, GT>, ColF32<128, 256, 2>, EpiStoreF32>(p, members, s);
+}
+
+template <typename XT, class Cfg, int NP>
+hipError_t dion_update_t(const DionUpdateArgs& a, int members, hipStream_t s) {
+  GemmParams<typename EpiDion<XT>::Args> p{};
+  p.a = with_rows(a.p, a.M);
+  p.b0 = with_rows(a.r, a.N);
+  p.b1 = with_rows(a.q, a.N);
+  p.e.m = a.m; p.e.g = a.g; p.e.x = a.x;
+  p.e.c1 = a.c1; p.e.c2 = a.c2;
+  p.M = a.M; p.N = a.N; p.K = a.rank;
+  p.splits = 1; p.kchunk = 0; p.tri = 0;
+  return run<Cfg, RowF32<128, 256, NP>, RowF32<128, 256, NP>, EpiDion<XT>>(p, members, s);
+}
+
+template <class Cfg>
+using NsRow = LdRowBf16<Cfg::BM, 32, Cfg::NT>;
+
+template <class Cfg>
+hipError_t ns_gram_t(const NsGramArgs& a, int members, hipStream_t s) {
+  GemmParams<EpiNSGram::Args> p{};
+  p.a = with_rows(a.x, a.M);
+  p.b0 = with_rows(a.x, a.M);
+  p.e.a = a.a;
+  p.M = a.M; p.N = a.M; p.K = a.K;
+  p.splits = 1; p.kchunk = 0; p.tri = 0;
+  return run<Cfg, NsRow<Cfg>, NsRow<Cfg>, EpiNSGram>(p, members, s);
+}
+
+template <class Cfg>
+hipError_t ns_poly_t(const NsPolyArgs& a, int members, hipStream_t s) {
+  GemmParams<EpiNSPoly::Args> p{};
+  p.a = with_rows(a.a, a.M);
+  p.b0 = with_rows(a.a, a.M);   // A is symmetric: A A = A A^T
+  p.e.a = a.a; p.e.bp = a.bp; p.e.bp32 = a.bp32; p.e.b = a.b; p.e.c = a.c;
+  p.e.has32 = a.M <= kNsSplitRows;
+  p.M = a.M; p.N = a.M; p.K = a.M;
+  p.splits = 1; p.kchunk = 0; p.tri = 0;
+  return run<Cfg, NsRow<Cfg>, NsRow<Cfg>, EpiNSPoly>(p, members, s);
+}
+
+template <class Cfg, typename OUT_T>
+hipError_t ns_apply_t(const NsApplyArgs& a, int members, hipStream_t s) {
+  GemmParams<typename EpiNSApply<OUT_T>::Args> p{};
+  p.a = with_rows(a.bp, a.M);
+  p.b0 = with_rows(a.xbt, a.N);   // element (j, k) = X^T[j][k] = X[k][j]
+  p.e.x32 = a.x32; p.e.xb = a.xb_next; p.e.xbt = a.xbt_next; p.e.out = a.out;
+  p.e.a = a.a; p.e.last = a.last; p.e.out_transposed = a.out_transposed;
+  p.M = a.M; p.N = a.N; p.K = a.M;
+  p.splits = 1; p.kchunk = 0; p.tri = 0;
+  return run<Cfg, NsRow<Cfg>, NsRow<Cfg>, EpiNSApply<OUT_T>>(p, members, s);
+}
+
+// Small Gram side: split bf16 products from the fp32 Bp and the fp32 iterate
+// (read transposed: element (j, k) = X[k][j]).
+template <typename OUT_T>
+hipError_t ns_apply_split_t(const NsApplyArgs& a, int members, hipStream_t s) {
+  GemmParams<typename EpiNSApply<OUT_T>::Args> p{};
+  p.a = with_rows(a.bp32, a.M);
+  p.b0 = with_rows(a.x32, a.N);
+  p.e.x32 = a.x32; p.e.xb = a.xb_next; p.e.xbt = a.xbt_next; p.e.out = a.out;
+  p.e.a = a.a; p.e.last = a.last; p.e.out_transposed = a.out_transposed;
+  p.M = a.M; p.N = a.N; p.K = a.M;
+  p.splits = 1; p.kchunk = 0; p.tri = 0;
+  return run<CfgSplit, RowF32<128, 256, 2>, ColF32<128, 256, 2>, EpiNSApply<OUT_T>>(p, members, s);
+}
+
+}  // namespace
+
+hipError_t launch_dion_left(const DionLeftArgs& a, bool bf16, int members, hipStream_t s) {
+  return bf16 ? dion_left_t<uint16_t>(a, members, s) : dion_left_t<float>(a, members, s);
+}
+
+hipError_t launch_dion_right(const DionRightArgs& a, bool bf16, int members, hipStream_t s) {
+  return bf16 ? dion_right_t<uint16_t>(a, members, s) : dion_right_t<float>(a, members, s);
+}
+
+hipError_t launch_apply_t(const ApplyArgs& a, int members, hipStream_t s) {
+  GemmParams<EpiStoreF32::Args> p{};
+  p.a = with_rows(a.pt, a.M);
+  p.b0 = with_rows(a.tt, a.r);   // element (j, k) = T^T[j][k], zero for k > j
+  p.e.c = a.out;
+  p.e.split_stride = 0;
+  p.e.has_t = 0;
+  p.M = a.M; p.N = a.r; p.K = a.r;
+  p.splits = 1; p.kchunk = 0; p.tri = 1;
+  return run<CfgSplit, RowF32<128, 256, 2>, RowF32<128, 256, 2>, EpiStoreF32>(p, members, s);
+}
+
+hipError_t launch_dion_update(const DionUpdateArgs& a, bool bf16, int members, hipStream_t s) {
+  return bf16 ? dion_update_t<uint16_t, CfgUpdBf, 1>(a, members, s)
+              : dion_update_t<float, CfgUpdF32, 2>(a, members, s);
+}
+
+hipError_t launch_ns_gram(const NsGramArgs& a, int members, hipStream_t s) {
+  return a.M > 128 ? ns_gram_t<CfgNsBig>(a, members, s) : ns_gram_t<CfgNsSmall>(a, members, s);
+}
+
+hipError_t launch_ns_poly(const NsPolyArgs& a, int members, hipStream_t s) {
+  return a.M > 128 ? ns_poly_t<CfgNsBig>(a, members, s) : ns_poly_t<CfgNsSmall>(a, members, s);
+}
+
+hipError_t launch_ns_apply(const NsApplyArgs& a, bool out_bf16, int members, hipStream_t s) {
+  if (a.M <= kNsSplitRows)
+    return out_bf16 ? ns_apply_split_t<uint16_t>(a, members, s) : ns_apply_split_t<float>(a, members, s);
+  if (a.M > 128)
+    return out_bf16 ? ns_apply_t<CfgNsBig, uint16_t>(a, members, s)
+                    : ns_apply_t<CfgNsBig, float>(a, members, s);
+  return out_bf16 ? ns_apply_t<CfgNsSmall, uint16_t>(a, members, s)
+                  : ns_apply_t<CfgNsSmall, float>(a, members, s);
+}
+
+}  // namespace ortho

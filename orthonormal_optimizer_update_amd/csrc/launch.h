@@ -1,0 +1,137 @@
+// Host-side launchers of the gfx950 kernels (internal to libortho.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace ortho {
+
+struct RedArgs {
+  const float* part;          // member 0 partials; slices of rows x cols (ld = cols)
+  int64_t part_member_stride;
+  int64_t slice;              // elements per slice
+  int splits, rows, cols;
+  MatArg out;                 // fp32 destination
+  float* colsq;               // optional per-64-row-block column sums of squares
+  int64_t colsq_member_stride;
+};
+
+struct ColnormArgs {
+  MatArg r;                   // fp32 source
+  MatArg q;                   // fp32 destination
+  const float* colsq;
+  int64_t colsq_member_stride;
+  int nrb, rows, cols;
+  int32_t* status;
+};
+
+struct SumsqArgs {
+  MatArg g;
+  float* partial;
+  int64_t partial_stride;
+  int64_t chunk;
+};
+
+struct NsInitArgs {
+  MatArg g;            // caller's input (storage dtype)
+  MatArg x32, xb, xbt; // iterate (M x N fp32), bf16 M x N, bf16 N x M
+  const float* scale;
+  int64_t scale_stride;
+  int M, N;            // wide orientation, M <= N
+  int transposed;      // X = G^T
+};
+
+struct Gram64Args {
+  MatArg p;            // fp32 m x r
+  double* part;        // slices of r x r
+  int64_t part_member_stride;
+  int64_t slice;
+  int m, r, kchunk;
+};
+
+struct CholArgs {
+  const double* part;  // Gram slices (lower tiles valid)
+  int64_t part_member_stride;
+  int64_t slice;
+  int splits;
+  double* s;           // r x r: scaled Gram, then L (lower)
+  double* x;           // r x r: L^{-1} (lower)
+  double* d;           // r: column scaling 1/sqrt(W_ii)
+  int64_t mat_stride, vec_stride;
+  int r;
+  int32_t* status;
+};
+
+hipError_t launch_reduce_splits(const RedArgs& a, int members, hipStream_t s);
+hipError_t launch_colnorm(const ColnormArgs& a, int members, hipStream_t s);
+hipError_t launch_sumsq(const SumsqArgs& a, int nblocks, int members, bool bf16, hipStream_t s);
+hipError_t launch_ns_scale(const float* partial, int64_t partial_stride, int nparts, float* scale,
+                           int64_t scale_stride, float eps, int members, hipStream_t s);
+hipError_t launch_ns_init(const NsInitArgs& a, int members, bool bf16, hipStream_t s);
+hipError_t launch_ns_store(const NsInitArgs& a, const MatArg& out, int members, bool bf16,
+                           hipStream_t s);
+hipError_t launch_gram64(const Gram64Args& a, int splits, int members, hipStream_t s);
+hipError_t launch_cholesky_inverse(const CholArgs& a, float* tt, int64_t tt_stride, int members,
+                                   hipStream_t s);
+
+// --- GEMM-family sweeps (kernels_gemm.hip) ---------------------------------
+
+// Dion sweep 1: C = (M + G) Q, C is m x r.  G/X dtype: bf16 (true) or fp32.
+// Writes split-K slices to `out` (slice stride `split_stride`, ld = r) or, with
+// splits == 1, directly.
+struct DionLeftArgs {
+  MatArg m, g, q;
+  MatArg out;
+  int64_t split_stride;
+  int M, N, r;           // B is M x N
+  int splits, kchunk;
+};
+hipError_t launch_dion_left(const DionLeftArgs& a, bool bf16, int members, hipStream_t s);
+
+// Dion sweep 2: C = (M + G)^T P, C is n x r (split-K over m).
+struct DionRightArgs {
+  MatArg m, g, p;
+  MatArg out;
+  int64_t split_stride;
+  int M, N, r;
+  int splits, kchunk;
+};
+hipError_t launch_dion_right(const DionRightArgs& a, bool bf16, int members, hipStream_t s);
+
+// Orthonormalisation apply: P1 = Pt * T with T upper triangular, given as T^T
+// (r x r fp32, row-major).
+struct ApplyArgs {
+  MatArg pt, tt;
+  MatArg out;
+  int M, r;
+};
+hipError_t launch_apply_t(const ApplyArgs& a, int members, hipStream_t s);
+
+// Dion sweep 3: M <- (M+G) - c1 P R^T,  X <- X - c2 P Q'^T.
+struct DionUpdateArgs {
+  MatArg p, r, q;        // P m x r, R n x r, Q' n x r (fp32)
+  MatArg m, g, x;
+  float c1, c2;
+  int M, N, rank;
+};
+hipError_t launch_dion_update(const DionUpdateArgs& a, bool bf16, int members, hipStream_t s);
+
+// Newton-Schulz products (bf16 operands, fp32 accumulation).
+struct NsGramArgs { MatArg x; MatArg a; int M, K; };                 // A = X X^T
+struct NsPolyArgs { MatArg a; MatArg bp; MatArg bp32; float b, c; int M; };  // Bp = bA + cAA
+// X = aX + Bp X.  When M <= kNsSplitRows the product uses split bf16 operands
+// read from bp32 and the fp32 iterate (one row tile, so updating the iterate in
+// place cannot race with another tile's reads).
+constexpr int kNsSplitRows = 128;
+struct NsApplyArgs {
+  MatArg bp, xbt, x32, xb_next, xbt_next, out, bp32;
+  float a;
+  int M, N, last, out_transposed;
+};
+hipError_t launch_ns_gram(const NsGramArgs& a, int members, hipStream_t s);
+hipError_t launch_ns_poly(const NsPolyArgs& a, int members, hipStream_t s);
+hipError_t launch_ns_apply(const NsApplyArgs& a, bool out_bf16, int members, hipStream_t s);
+
+}  // namespace ortho

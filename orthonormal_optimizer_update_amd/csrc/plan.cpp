@@ -1,0 +1,186 @@
+// Workspace planning and argument validation (host only, no HIP calls).
+#include "plan.h"
+
+#include <math.h>
+
+namespace ortho {
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t{1} << 30);   // rows/cols index with int32
+constexpr int kTargetWorkgroups = 512;            // ~2 workgroups per CU
+constexpr int kMinSplitK = 256;                   // rows per split-K slice, at least
+
+size_t align_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Split a reduction of length K so that tiles * members * splits reaches the
+// target, with each slice a multiple of 32 and at least kMinSplitK long.
+void choose_split(int64_t K, int64_t tiles, int members, int* splits, int* kchunk) {
+  int64_t want = cdiv(kTargetWorkgroups, tiles * members);
+  int64_t cap = K / kMinSplitK;
+  if (cap < 1) cap = 1;
+  if (want > cap) want = cap;
+  if (want < 1) want = 1;
+  int64_t kc = cdiv(cdiv(K, want), 32) * 32;
+  *kchunk = static_cast<int>(kc);
+  *splits = static_cast<int>(cdiv(K, kc));
+}
+
+bool finite(float v) { return isfinite(v) != 0; }
+
+ortho_status check_mat(const ortho_mat& a) {
+  if (a.data == nullptr) return ORTHO_E_NULL;
+  if (a.rows < 1 || a.cols < 1 || a.rows > kMaxDim || a.cols > kMaxDim) return ORTHO_E_SHAPE;
+  if (a.ld < a.cols || a.ld > (int64_t{1} << 40)) return ORTHO_E_LAYOUT;
+  if (a.dtype != ORTHO_F32 && a.dtype != ORTHO_BF16) return ORTHO_E_DTYPE;
+  return ORTHO_OK;
+}
+
+bool same_geometry(const ortho_mat& a, const ortho_mat& b) {
+  return a.rows == b.rows && a.cols == b.cols && a.dtype == b.dtype;
+}
+
+}  // namespace
+
+bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* p) {
+  if (m < 1 || n < 1 || r < 1 || batch < 1 || m > kMaxDim || n > kMaxDim) return false;
+  if (r > m || r > n || r > 16384) return false;
+  DionPlan d{};
+  d.m = m;
+  d.n = n;
+  d.r = r;
+  d.chunk = batch < kMaxMembersPerLaunch ? batch : kMaxMembersPerLaunch;
+  choose_split(n, cdiv(m, 128) * cdiv(r, 128), d.chunk, &d.split_left, &d.kchunk_left);
+  choose_split(m, cdiv(n, 128) * cdiv(r, 128), d.chunk, &d.split_right, &d.kchunk_right);
+  const int64_t tg = cdiv(r, 64);
+  choose_split(m, tg * (tg + 1) / 2, d.chunk, &d.split_gram, &d.kchunk_gram);
+  d.nrb = static_cast<int>(cdiv(n, 64));
+  d.rp = cdiv(r, 4) * 4;
+  const size_t mr = static_cast<size_t>(m) * r, nr = static_cast<size_t>(n) * r;
+  const size_t mrp = static_cast<size_t>(m) * d.rp, nrp = static_cast<size_t>(n) * d.rp;
+  const size_t rr = static_cast<size_t>(r) * r;
+  size_t part = static_cast<size_t>(d.split_left) * mr * 4;
+  const size_t pr = static_cast<size_t>(d.split_right) * nr * 4;
+  const size_t pg = static_cast<size_t>(d.split_gram) * rr * 8;
+  if (pr > part) part = pr;
+  if (pg > part) part = pg;
+  size_t o = 0;
+  d.off_pt = o;    o = align_up(o + mrp * 4);
+  d.off_p1 = o;    o = align_up(o + mrp * 4);
+  d.off_part = o;  o = align_up(o + part);
+  d.off_s = o;     o = align_up(o + rr * 8);
+  d.off_x = o;     o = align_up(o + rr * 8);
+  d.off_d = o;     o = align_up(o + static_cast<size_t>(r) * 8);
+  d.off_tt = o;    o = align_up(o + rr * 4);
+  d.off_r = o;     o = align_up(o + nrp * 4);
+  d.off_colsq = o; o = align_up(o + static_cast<size_t>(d.nrb) * r * 4);
+  d.member_bytes = o;
+  d.total_bytes = o * static_cast<size_t>(d.chunk);
+  *p = d;
+  return true;
+}
+
+bool plan_ns(int64_t m, int64_t n, int32_t batch, NsPlan* p) {
+  if (m < 1 || n < 1 || batch < 1 || m > kMaxDim || n > kMaxDim) return false;
+  NsPlan s{};
+  s.transposed = m > n;
+  s.M = s.transposed ? n : m;
+  s.N = s.transposed ? m : n;
+  s.chunk = batch < kMaxMembersPerLaunch ? batch : kMaxMembersPerLaunch;
+  const int64_t total = m * n;
+  int64_t parts = cdiv(total, 16384);
+  if (parts > 2048) parts = 2048;
+  if (parts < 1) parts = 1;
+  s.part_chunk = cdiv(total, parts);
+  s.nparts = static_cast<int>(cdiv(total, s.part_chunk));
+  s.ld_x = cdiv(s.N, 8) * 8;
+  s.ld_xt = cdiv(s.M, 8) * 8;
+  const size_t mn = static_cast<size_t>(s.M) * s.ld_x, nm = static_cast<size_t>(s.N) * s.ld_xt;
+  const size_t mm = static_cast<size_t>(s.M) * s.ld_xt;
+  size_t o = 0;
+  s.off_x32 = o;     o = align_up(o + mn * 4);
+  s.off_xb0 = o;     o = align_up(o + mn * 2);
+  s.off_xb1 = o;     o = align_up(o + mn * 2);
+  s.off_xbt0 = o;    o = align_up(o + nm * 2);
+  s.off_xbt1 = o;    o = align_up(o + nm * 2);
+  s.off_a = o;       o = align_up(o + mm * 2);
+  s.off_bp = o;      o = align_up(o + mm * 2);
+  // fp32 copy of Bp, used by the split-precision apply when M <= 128
+  s.off_bp32 = o;    o = align_up(o + (s.M <= 128 ? mm * 4 : 0));
+  s.off_partial = o; o = align_up(o + static_cast<size_t>(s.nparts) * 4);
+  s.off_scale = o;   o = align_up(o + 4);
+  s.member_bytes = o;
+  s.total_bytes = o * static_cast<size_t>(s.chunk);
+  *p = s;
+  return true;
+}
+
+ortho_status validate_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, const ortho_mat* M,
+                           const ortho_mat* Q, int32_t r, float mu, float lr, float scale,
+                           const ortho_mat* P_out, const ortho_mat* R_out, const void* ws,
+                           size_t ws_bytes) {
+  if (batch < 1) return ORTHO_E_PARAM;
+  if (!X || !G || !M || !Q) return ORTHO_E_NULL;
+  if (!(mu >= 0.f && mu <= 1.f) || !finite(lr) || !finite(scale)) return ORTHO_E_PARAM;
+  for (int32_t b = 0; b < batch; ++b) {
+    ortho_status st;
+    if ((st = check_mat(X[b])) != ORTHO_OK) return st;
+    if ((st = check_mat(G[b])) != ORTHO_OK) return st;
+    if ((st = check_mat(M[b])) != ORTHO_OK) return st;
+    if ((st = check_mat(Q[b])) != ORTHO_OK) return st;
+    if (G[b].dtype != X[b].dtype || M[b].dtype != ORTHO_F32 || Q[b].dtype != ORTHO_F32)
+      return ORTHO_E_DTYPE;
+    if (G[b].rows != X[b].rows || G[b].cols != X[b].cols || M[b].rows != X[b].rows ||
+        M[b].cols != X[b].cols || Q[b].rows != X[b].cols)
+      return ORTHO_E_SHAPE;
+    if (b > 0) {
+      if (!same_geometry(X[b], X[0])) return ORTHO_E_SHAPE;
+      if (X[b].ld != X[0].ld || G[b].ld != G[0].ld || M[b].ld != M[0].ld || Q[b].ld != Q[0].ld)
+        return ORTHO_E_LAYOUT;
+    }
+  }
+  const int64_t m = X[0].rows, n = X[0].cols;
+  if (r < 1 || r > m || r > n || r > 16384 || Q[0].cols != r) return ORTHO_E_RANK;
+  if (P_out) {
+    ortho_status st = check_mat(*P_out);
+    if (st != ORTHO_OK) return st;
+    if (P_out->dtype != ORTHO_F32) return ORTHO_E_DTYPE;
+    if (P_out->rows != m || P_out->cols != r) return ORTHO_E_SHAPE;
+  }
+  if (R_out) {
+    ortho_status st = check_mat(*R_out);
+    if (st != ORTHO_OK) return st;
+    if (R_out->dtype != ORTHO_F32) return ORTHO_E_DTYPE;
+    if (R_out->rows != n || R_out->cols != r) return ORTHO_E_SHAPE;
+  }
+  DionPlan plan;
+  if (!plan_dion(m, n, r, batch, &plan)) return ORTHO_E_SHAPE;
+  if (ws == nullptr || ws_bytes < plan.total_bytes) return ORTHO_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kWsAlign != 0) return ORTHO_E_WORKSPACE;
+  return ORTHO_OK;
+}
+
+ortho_status validate_ns(int32_t batch, const ortho_mat* G, const ortho_mat* Out, int32_t steps,
+                         const float* abc, const void* ws, size_t ws_bytes) {
+  if (batch < 1 || steps < 0) return ORTHO_E_PARAM;
+  if (!G || !Out) return ORTHO_E_NULL;
+  if (abc && (!finite(abc[0]) || !finite(abc[1]) || !finite(abc[2]))) return ORTHO_E_PARAM;
+  for (int32_t b = 0; b < batch; ++b) {
+    ortho_status st;
+    if ((st = check_mat(G[b])) != ORTHO_OK) return st;
+    if ((st = check_mat(Out[b])) != ORTHO_OK) return st;
+    if (!same_geometry(G[b], Out[b])) return Out[b].dtype != G[b].dtype ? ORTHO_E_DTYPE : ORTHO_E_SHAPE;
+    if (b > 0) {
+      if (!same_geometry(G[b], G[0])) return ORTHO_E_SHAPE;
+      if (G[b].ld != G[0].ld || Out[b].ld != Out[0].ld) return ORTHO_E_LAYOUT;
+    }
+  }
+  NsPlan plan;
+  if (!plan_ns(G[0].rows, G[0].cols, batch, &plan)) return ORTHO_E_SHAPE;
+  if (ws == nullptr || ws_bytes < plan.total_bytes) return ORTHO_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kWsAlign != 0) return ORTHO_E_WORKSPACE;
+  return ORTHO_OK;
+}
+
+}  // namespace ortho

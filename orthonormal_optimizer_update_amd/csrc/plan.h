@@ -1,0 +1,55 @@
+// Workspace planning and argument validation for libortho.so.  Plain C++ with
+// no HIP calls, so it can be built and tested on a host without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ortho.h"
+
+namespace ortho {
+
+constexpr int kMaxMembersPerLaunch = 16;  // must match kMaxBatch in common.h
+constexpr size_t kWsAlign = 256;
+
+// Byte offsets of one member's regions inside the Dion workspace, and the
+// split-K factors chosen for the three reductions over a long dimension.
+struct DionPlan {
+  int64_t m, n;
+  int r;
+  int64_t rp;                // leading dimension of m x r / n x r fp32 buffers (r rounded to 4)
+  int chunk;                 // members per launch
+  int split_left, kchunk_left;    // B Q: split over n
+  int split_right, kchunk_right;  // B^T P: split over m
+  int split_gram, kchunk_gram;    // P^T P: split over m
+  int nrb;                   // 64-row blocks of R (column-norm partials)
+  size_t off_pt, off_p1, off_part, off_s, off_x, off_d, off_tt, off_r, off_colsq;
+  size_t member_bytes;       // stride between members
+  size_t total_bytes;
+};
+
+struct NsPlan {
+  int64_t M, N;              // wide orientation, M <= N
+  int transposed;
+  int64_t ld_x, ld_xt;       // leading dims of the M x N and N x M / M x M buffers (rounded to 8)
+  int chunk;
+  int nparts;
+  int64_t part_chunk;        // elements per sum-of-squares block
+  size_t off_x32, off_xb0, off_xb1, off_xbt0, off_xbt1, off_a, off_bp, off_bp32, off_partial,
+      off_scale;
+  size_t member_bytes;
+  size_t total_bytes;
+};
+
+bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* out);
+bool plan_ns(int64_t m, int64_t n, int32_t batch, NsPlan* out);
+
+ortho_status validate_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, const ortho_mat* M,
+                           const ortho_mat* Q, int32_t r, float mu, float lr, float scale,
+                           const ortho_mat* P_out, const ortho_mat* R_out, const void* ws,
+                           size_t ws_bytes);
+
+ortho_status validate_ns(int32_t batch, const ortho_mat* G, const ortho_mat* Out, int32_t steps,
+                         const float* abc, const void* ws, size_t ws_bytes);
+
+}  // namespace ortho
