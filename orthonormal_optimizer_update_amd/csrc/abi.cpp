@@ -99,28 +99,36 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       ORTHO_TRY(launch_reduce_splits(ra, nb, s));
     }
 
-    // Orthonormalisation: two Cholesky-QR passes with an fp64 Gram.
-    for (int pass = 0; pass < 2; ++pass) {
-      const MatArg& src = pass == 0 ? tPt : tP1;
-      const MatArg& dst = pass == 0 ? tP1 : tPt;
-      Gram64Args ga;
-      ga.p = src; ga.part = part_d; ga.part_member_stride = static_cast<int64_t>(mb / 8);
-      ga.slice = static_cast<int64_t>(r) * r; ga.m = mi; ga.r = r; ga.kchunk = pl.kchunk_gram;
-      ORTHO_TRY(launch_gram64(ga, pl.split_gram, nb, s));
-      CholArgs ca;
-      ca.part = part_d; ca.part_member_stride = static_cast<int64_t>(mb / 8);
-      ca.slice = static_cast<int64_t>(r) * r; ca.splits = pl.split_gram;
-      ca.s = reinterpret_cast<double*>(base + pl.off_s);
-      ca.x = reinterpret_cast<double*>(base + pl.off_x);
-      ca.d = reinterpret_cast<double*>(base + pl.off_d);
-      ca.mat_stride = static_cast<int64_t>(mb / 8); ca.vec_stride = static_cast<int64_t>(mb / 8);
-      ca.r = r; ca.status = status;
-      ORTHO_TRY(launch_cholesky_inverse(ca, reinterpret_cast<float*>(base + pl.off_tt),
-                                        static_cast<int64_t>(mb / 4), nb, s));
-      ApplyArgs aa;
-      aa.pt = src; aa.tt = tTt; aa.out = dst; aa.M = mi; aa.r = r;
-      ORTHO_TRY(launch_apply_t(aa, nb, s));
-    }
+    // Orthonormalisation of P_tilde (Q-factor of its thin QR, diag(R) > 0).
+    // Pass 1: fp64 Gram, column-scaled fp64 Cholesky and triangular inverse,
+    // P1 = P_tilde T1 with bf16x6 products (T1 = D L^-T, upper triangular).
+    Gram64Args ga;
+    ga.p = tPt; ga.part = part_d; ga.part_member_stride = static_cast<int64_t>(mb / 8);
+    ga.slice = static_cast<int64_t>(r) * r; ga.m = mi; ga.r = r; ga.kchunk = pl.kchunk_gram;
+    ORTHO_TRY(launch_gram64(ga, pl.split_gram, nb, s));
+    CholArgs ca;
+    ca.part = part_d; ca.part_member_stride = static_cast<int64_t>(mb / 8);
+    ca.slice = static_cast<int64_t>(r) * r; ca.splits = pl.split_gram;
+    ca.s = reinterpret_cast<double*>(base + pl.off_s);
+    ca.x = reinterpret_cast<double*>(base + pl.off_x);
+    ca.d = reinterpret_cast<double*>(base + pl.off_d);
+    ca.mat_stride = static_cast<int64_t>(mb / 8); ca.vec_stride = static_cast<int64_t>(mb / 8);
+    ca.r = r; ca.status = status;
+    float* tt = reinterpret_cast<float*>(base + pl.off_tt);
+    ORTHO_TRY(launch_cholesky_inverse(ca, tt, static_cast<int64_t>(mb / 4), nb, s));
+    ApplyArgs aa;
+    aa.pt = tPt; aa.tt = tTt; aa.out = tP1; aa.M = mi; aa.r = r;
+    ORTHO_TRY(launch_apply_t(aa, true, nb, s));
+    // Pass 2: P1 is orthonormal to about 2^-24 * cond; E = P1^T P1 - I (bf16x3)
+    // and the first-order factor T2 = I - Phi(E)^T give P = P1 T2.
+    GramTnArgs g2;
+    g2.p = tP1; g2.out = tPart; g2.split_stride = static_cast<int64_t>(r) * r;
+    g2.m = mi; g2.r = r; g2.splits = pl.split_gram2; g2.kchunk = pl.kchunk_gram2;
+    ORTHO_TRY(launch_gram_tn(g2, nb, s));
+    ORTHO_TRY(launch_correction(part_f, static_cast<int64_t>(mb / 4), static_cast<int64_t>(r) * r,
+                                pl.split_gram2, r, tt, static_cast<int64_t>(mb / 4), nb, s));
+    aa.pt = tP1; aa.out = tPt;
+    ORTHO_TRY(launch_apply_t(aa, false, nb, s));
 
     // Sweep 2: R = (M + G)^T P, then Q' = column-normalised R.
     DionRightArgs rb;

@@ -1,13 +1,15 @@
 // Generic LDS-staged MFMA GEMM for gfx950:  C[i, j] = sum_k A[i, k] * Bop[j, k]
 // ("NT" form: both operands are consumed with the reduction index k contiguous
 // in LDS).  Loaders bring a tile of each operand from HBM into registers, turn
-// it into one or two bf16 pieces (x = hi + lo) and store it to LDS in the
+// it into one to three bf16 pieces (x = hi + lo + ...) and store it to LDS in the
 // k-contiguous layout the MFMA fragments want; transposing loaders do the
 // transpose in registers, so every global access stays row-coalesced.
 //
-// Products: PRODS = 1 uses hi*hi; PRODS = 3 adds lo*hi and hi*lo, which gives
-// products close to fp32 accuracy from bf16 matrix cores.  NBOP = 2 runs two
-// right operands against the same left tile with two accumulator sets.
+// Products: PRODS = 1 uses hi*hi; PRODS = 3 (two pieces, x = hi + lo) adds
+// lo*hi and hi*lo, about 2^-16 relative accuracy; PRODS = 6 (three pieces
+// x = p0 + p1 + p2) keeps every product p_i*q_j with i + j <= 2, about fp32
+// accuracy.  NBOP = 2 runs two right operands against the same left tile with
+// two accumulator sets.
 //
 // Matrix core: v_mfma_f32_32x32x16_bf16.  Each lane supplies eight consecutive
 // k values of one row (lanes 0-31: k 0-7, lanes 32-63: k 8-15) for both A and
@@ -34,7 +36,9 @@ struct GemmCfg {
   static constexpr int STAGE = NA * A_ELEMS + NBOP * NB * B_ELEMS;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(BK % 16 == 0, "BK must be a multiple of 16");
-  static_assert(PRODS == 1 || (PRODS == 3 && NA == 2 && NB == 2), "bad product set");
+  static_assert(PRODS == 1 || (PRODS == 3 && NA == 2 && NB == 2) ||
+                    (PRODS == 6 && NA == 3 && NB == 3),
+                "bad product set");
 };
 
 // ---------------------------------------------------------------------------
@@ -49,6 +53,21 @@ __device__ __forceinline__ void put4(bf16* s, int pstride, float a, float b, flo
   if constexpr (NP == 1) {
     bf16x4 h = {to_bf16(a), to_bf16(b), to_bf16(c), to_bf16(d)};
     *reinterpret_cast<bf16x4*>(s) = h;
+  } else if constexpr (NP == 3) {
+    const float x[4] = {a, b, c, d};
+    bf16x4 p0, p1, p2;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bf16 h = to_bf16(x[t]);
+      const float r1 = x[t] - static_cast<float>(h);   // exact
+      const bf16 mid = to_bf16(r1);
+      p0[t] = h;
+      p1[t] = mid;
+      p2[t] = to_bf16(r1 - static_cast<float>(mid));   // exact argument
+    }
+    *reinterpret_cast<bf16x4*>(s) = p0;
+    *reinterpret_cast<bf16x4*>(s + pstride) = p1;
+    *reinterpret_cast<bf16x4*>(s + 2 * pstride) = p2;
   } else {
     bf16 h0, h1, h2, h3, l0, l1, l2, l3;
     split_bf16(a, h0, l0);
@@ -314,7 +333,12 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(GemmParams<typename Epi::
         for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int j = 0; j < NI; ++j) {
-            if constexpr (Cfg::PRODS == 3) {
+            if constexpr (Cfg::PRODS == 6) {
+              acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[2][i], bfr[0][j], acc[q][i][j], 0, 0, 0);
+              acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], bfr[1][j], acc[q][i][j], 0, 0, 0);
+              acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bfr[2][j], acc[q][i][j], 0, 0, 0);
+            }
+            if constexpr (Cfg::PRODS >= 3) {
               acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], bfr[0][j], acc[q][i][j], 0, 0, 0);
               acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bfr[1][j], acc[q][i][j], 0, 0, 0);
             }

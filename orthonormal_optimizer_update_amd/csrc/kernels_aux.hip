@@ -260,9 +260,13 @@ __global__ __launch_bounds__(256) void chol_prep_kernel(CholArgs a) {
   if (i == j) d[i] = di;
 }
 
-// Factor the nb x nb diagonal block k of S in LDS (S_kk = L_kk L_kk^T), write
-// L_kk back, and write its inverse as block (k, k) of X.  A pivot that is not
-// positive is replaced by a tiny positive shift and flagged.
+// Pivots below this (the scaled Gram has unit diagonal) are treated as a
+// numerical rank deficiency and replaced by it.
+constexpr double kPivMin = 1e-14;
+
+// Factor the nb x nb diagonal block kb of S in LDS (S_kk = L_kk L_kk^T), write
+// L_kk back, and write its inverse as block (kb, kb) of X.  Each thread owns a
+// 4 x 4 block of the 64 x 64 tile; every column step takes two barriers.
 __global__ __launch_bounds__(256) void chol_diag_kernel(CholArgs a, int kb) {
   __shared__ double L[64][65];
   __shared__ double Xi[64][65];
@@ -272,75 +276,140 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(CholArgs a, int kb) {
   const int r = a.r;
   const int o = kb * 64;
   const int nb = min(64, r - o);
-  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int i = e >> 6, j = e & 63;
-    L[i][j] = (i < nb && j <= i) ? S[(int64_t)(o + i) * r + o + j] : 0.0;
-    Xi[i][j] = 0.0;
-  }
-  __syncthreads();
+  const int ti = (threadIdx.x >> 4) * 4, tj = (threadIdx.x & 15) * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int gi = ti + i, gj = tj + j;
+      L[gi][gj] = (gi < nb && gj <= gi) ? S[(int64_t)(o + gi) * r + o + gj] : 0.0;
+      Xi[gi][gj] = (gi == gj && gi < nb) ? 1.0 : 0.0;
+    }
+  bool shifted = false;
   for (int j = 0; j < nb; ++j) {
-    if (threadIdx.x == 0) {
-      double piv = L[j][j];
-      if (!(piv > 1e-14) && piv == piv) {
-        piv = 1e-14;
-        if (a.status) atomicOr(a.status, 1);
+    __syncthreads();
+    double piv = L[j][j];
+    if (!(piv > kPivMin) && piv == piv) {
+      piv = kPivMin;
+      shifted = true;
+    }
+    const double ljj = sqrt(piv), inv = 1.0 / ljj;
+    // trailing update with the unscaled column j: L[i][c] -= L[i][j] L[c][j] / piv
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int gi = ti + i;
+      if (gi <= j || gi >= nb) continue;
+      const double lij = L[gi][j] * inv;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int gc = tj + c;
+        if (gc > j && gc <= gi) L[gi][gc] -= lij * (L[gc][j] * inv);
       }
-      L[j][j] = sqrt(piv);
     }
     __syncthreads();
-    const double ljj = L[j][j];
-    for (int i = j + 1 + threadIdx.x; i < nb; i += 256) L[i][j] /= ljj;
+    if (tj <= j && j < tj + 4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int gi = ti + i;
+        if (gi > j && gi < nb) L[gi][j] *= inv;
+        else if (gi == j) L[j][j] = ljj;
+      }
+    }
+  }
+  if (shifted && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
+  // Inverse by right-looking forward substitution on L X = I: row t is final
+  // once divided by L[t][t]; its multiple is removed from every row below.
+  for (int t = 0; t < nb; ++t) {
     __syncthreads();
-    const int T = nb - j - 1;
-    for (int e = threadIdx.x; e < T * T; e += 256) {
-      const int ii = j + 1 + e / T, cc = j + 1 + e % T;
-      if (cc <= ii) L[ii][cc] -= L[ii][j] * L[cc][j];
+    const double dinv = 1.0 / L[t][t];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int gi = ti + i;
+      if (gi <= t || gi >= nb) continue;
+      const double f = L[gi][t] * dinv;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int gc = tj + c;
+        if (gc <= t) Xi[gi][gc] -= f * Xi[t][gc];
+      }
     }
-    __syncthreads();  // the next pivot and column read the updated trailing block
+    __syncthreads();
+    if (ti <= t && t < ti + 4) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (tj + c <= t) Xi[t][tj + c] *= dinv;
+    }
   }
   __syncthreads();
-  // Inverse of the lower-triangular L: one column per thread.
-  if (threadIdx.x < nb) {
-    const int c = threadIdx.x;
-    Xi[c][c] = 1.0 / L[c][c];
-    for (int i = c + 1; i < nb; ++i) {
-      double s = 0.0;
-      for (int t = c; t < i; ++t) s += L[i][t] * Xi[t][c];
-      Xi[i][c] = -s / L[i][i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int gi = ti + i, gj = tj + j;
+      if (gi < nb && gj <= gi) {
+        S[(int64_t)(o + gi) * r + o + gj] = L[gi][gj];
+        X[(int64_t)(o + gi) * r + o + gj] = Xi[gi][gj];
+      }
     }
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int i = e >> 6, j = e & 63;
-    if (i < nb && j <= i) {
-      S[(int64_t)(o + i) * r + o + j] = L[i][j];
-      X[(int64_t)(o + i) * r + o + j] = Xi[i][j];
-    }
-  }
 }
 
-// C (64 x 64 tile) = A * B^T (TRANS_B) or A * B, fp64, K = 64, A and B tiles
-// read from row-major r x r matrices.  Each thread owns a 4 x 4 block.
+// acc (64 x 64 tile, four waves of 32 x 32) = A * B^T (TRANS_B) or A * B with
+// K = 64, fp64, A and B tiles read from row-major r x r matrices, on
+// v_mfma_f64_16x16x4_f64.  Result element e of acc[i][j] in lane l is row
+// wa*32 + i*16 + l/16 + 4e, column wb*32 + j*16 + l%16 (wa, wb: wave quadrant).
 template <bool TRANS_B>
 __device__ void tile_gemm64(const double* A, const double* B, int r, int ar, int ac, int br,
-                            int bc, double (*sA)[65], double (*sB)[65], double acc[4][4]) {
+                            int bc, double (*sA)[65], double (*sB)[65], doublex4 acc[2][2]) {
   for (int e = threadIdx.x; e < 64 * 64; e += 256) {
     const int i = e >> 6, j = e & 63;
     sA[i][j] = (ar + i < r && ac + j < r) ? A[(int64_t)(ar + i) * r + ac + j] : 0.0;
     sB[i][j] = (br + i < r && bc + j < r) ? B[(int64_t)(br + i) * r + bc + j] : 0.0;
   }
   __syncthreads();
-  const int ti = (threadIdx.x >> 4) * 4, tj = (threadIdx.x & 15) * 4;
-  for (int i = 0; i < 4; ++i)
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-  for (int t = 0; t < 64; ++t) {
-    double av[4], bv[4];
-    for (int i = 0; i < 4; ++i) av[i] = sA[ti + i][t];
-    for (int j = 0; j < 4; ++j) bv[j] = TRANS_B ? sB[tj + j][t] : sB[t][tj + j];
-    for (int i = 0; i < 4; ++i)
-      for (int j = 0; j < 4; ++j) acc[i][j] += av[i] * bv[j];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wa = wave >> 1, wb = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = doublex4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+  for (int kk = 0; kk < 64; kk += 4) {
+    double af[2], bf[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) af[i] = sA[wa * 32 + i * 16 + (lane & 15)][kk + (lane >> 4)];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      bf[j] = TRANS_B ? sB[wb * 32 + j * 16 + (lane & 15)][kk + (lane >> 4)]
+                      : sB[kk + (lane >> 4)][wb * 32 + j * 16 + (lane & 15)];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[i], bf[j], acc[i][j], 0, 0, 0);
   }
   __syncthreads();
+}
+
+// Write (or subtract) a tile_gemm64 result at (orow, ocol) of an r x r matrix;
+// lower_only keeps the strictly-upper part of a diagonal tile untouched.
+__device__ __forceinline__ void tile_store64(double* out, int r, int orow, int ocol,
+                                             const doublex4 acc[2][2], bool subtract,
+                                             bool lower_only) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wa = wave >> 1, wb = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = orow + wa * 32 + i * 16 + (lane >> 4) + 4 * e;
+        const int cc = ocol + wb * 32 + j * 16 + (lane & 15);
+        if (rr < r && cc < r && (!lower_only || cc <= rr)) {
+          double* dst = out + (int64_t)rr * r + cc;
+          *dst = subtract ? *dst - acc[i][j][e] : acc[i][j][e];
+        }
+      }
 }
 
 // Panel step for block column kb (tile index t):
@@ -355,22 +424,16 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(CholArgs a, int kb) {
   const int r = a.r, nblk = (r + 63) / 64;
   const int T = nblk - kb - 1;
   const int t = blockIdx.x;
-  double acc[4][4];
-  int orow, ocol;
-  double* out;
+  doublex4 acc[2][2];
   if (t < T) {
     const int ib = kb + 1 + t;
     tile_gemm64<true>(S, X, r, ib * 64, kb * 64, kb * 64, kb * 64, sA, sB, acc);
-    out = S; orow = ib * 64; ocol = kb * 64;
+    tile_store64(S, r, ib * 64, kb * 64, acc, false, false);
   } else {
     const int jb = t - T;
     tile_gemm64<false>(X, X, r, kb * 64, kb * 64, kb * 64, jb * 64, sA, sB, acc);
-    out = X; orow = kb * 64; ocol = jb * 64;
+    tile_store64(X, r, kb * 64, jb * 64, acc, false, false);
   }
-  const int ti = (threadIdx.x >> 4) * 4, tj = (threadIdx.x & 15) * 4;
-  for (int i = 0; i < 4; ++i)
-    for (int j = 0; j < 4; ++j)
-      if (orow + ti + i < r && ocol + tj + j < r) out[(int64_t)(orow + ti + i) * r + ocol + tj + j] = acc[i][j];
 }
 
 // Trailing update after block column kb (tile index t):
@@ -386,32 +449,21 @@ __global__ __launch_bounds__(256) void chol_update_kernel(CholArgs a, int kb) {
   const int T = nblk - kb - 1;
   const int ntri = T * (T + 1) / 2;
   int t = blockIdx.x;
-  double acc[4][4];
-  int ib, jb;
-  double* out;
+  doublex4 acc[2][2];
   if (t < ntri) {
     int ti = static_cast<int>((sqrt(8.0 * t + 1.0) - 1.0) * 0.5);
     while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
     while (ti * (ti + 1) / 2 > t) --ti;
     const int tj = t - ti * (ti + 1) / 2;
-    ib = kb + 1 + ti;
-    jb = kb + 1 + tj;
+    const int ib = kb + 1 + ti, jb = kb + 1 + tj;
     tile_gemm64<true>(S, S, r, ib * 64, kb * 64, jb * 64, kb * 64, sA, sB, acc);
-    out = S;
+    tile_store64(S, r, ib * 64, jb * 64, acc, true, ib == jb);
   } else {
     t -= ntri;
-    ib = kb + 1 + t / (kb + 1);
-    jb = t % (kb + 1);
+    const int ib = kb + 1 + t / (kb + 1), jb = t % (kb + 1);
     tile_gemm64<false>(S, X, r, ib * 64, kb * 64, kb * 64, jb * 64, sA, sB, acc);
-    out = X;
+    tile_store64(X, r, ib * 64, jb * 64, acc, true, false);
   }
-  const int ti = (threadIdx.x >> 4) * 4, tj = (threadIdx.x & 15) * 4;
-  const int orow = ib * 64, ocol = jb * 64;
-  for (int i = 0; i < 4; ++i)
-    for (int j = 0; j < 4; ++j) {
-      const int rr = orow + ti + i, cc = ocol + tj + j;
-      if (rr < r && cc < r && (out == X || cc <= rr)) out[(int64_t)rr * r + cc] -= acc[i][j];
-    }
 }
 
 // T^T[j][k] = Linv[j][k] * d[k] for k <= j, else 0, as fp32: the right factor
@@ -426,6 +478,28 @@ __global__ __launch_bounds__(256) void make_t_kernel(CholArgs a, float* tt, int6
   const int k = blockIdx.x * 16 + (threadIdx.x & 15);
   if (j >= r || k >= r) return;
   out[(int64_t)j * r + k] = k <= j ? static_cast<float>(X[(int64_t)j * r + k] * d[k]) : 0.f;
+}
+
+// First-order correction of a nearly orthonormal basis P1: with
+// E = P1^T P1 - I (summed from split-K slices), T2 = I - Phi(E)^T where Phi(E)
+// is the lower triangle of E with its diagonal halved; T2^T is written (lower
+// triangular) so that P = P1 T2 has orthonormal columns up to O(|E|^2) and the
+// same positive-diagonal QR basis.
+__global__ __launch_bounds__(256) void correction_kernel(const float* part, int64_t part_member_stride,
+                                                         int64_t slice, int splits, int r, float* tt,
+                                                         int64_t tt_stride) {
+  const int member = blockIdx.z;
+  const int j = blockIdx.y * 16 + (threadIdx.x >> 4);
+  const int k = blockIdx.x * 16 + (threadIdx.x & 15);
+  if (j >= r || k >= r) return;
+  float v = 0.f;
+  if (k <= j) {
+    const float* p = part + member * part_member_stride + (int64_t)j * r + k;
+    double w = 0.0;
+    for (int s = 0; s < splits; ++s) w += p[s * slice];
+    v = k == j ? static_cast<float>(1.0 - 0.5 * (w - 1.0)) : static_cast<float>(-w);
+  }
+  tt[member * tt_stride + (int64_t)j * r + k] = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -471,6 +545,13 @@ hipError_t launch_ns_store(const NsInitArgs& a, const MatArg& out, int members, 
   dim3 grid(cdiv(a.N, 16), cdiv(a.M, 16), members);
   if (bf16) hipLaunchKernelGGL(ns_store_kernel<uint16_t>, grid, dim3(256), 0, s, a, out);
   else hipLaunchKernelGGL(ns_store_kernel<float>, grid, dim3(256), 0, s, a, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_correction(const float* part, int64_t part_member_stride, int64_t slice, int splits,
+                             int r, float* tt, int64_t tt_stride, int members, hipStream_t s) {
+  hipLaunchKernelGGL(correction_kernel, dim3(cdiv(r, 16), cdiv(r, 16), members), dim3(256), 0, s, part,
+                     part_member_stride, slice, splits, r, tt, tt_stride);
   return hipGetLastError();
 }
 

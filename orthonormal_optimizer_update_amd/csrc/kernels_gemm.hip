@@ -30,6 +30,8 @@ MatArg with_rows(MatArg a, int rows) {
 // Tall-skinny Dion contractions: 128 x 128 tiles, 4 waves, two bf16 pieces per
 // operand and three products (hi*hi + lo*hi + hi*lo).
 using CfgSplit = GemmCfg<128, 128, 32, 2, 2, 2, 2, 3, 1>;
+// The same with three pieces and six products (fp32-level products).
+using CfgSplit6 = GemmCfg<128, 128, 32, 2, 2, 3, 3, 6, 1>;
 // Dion sweep 3 with bf16 weights: one product, two right operands.
 using CfgUpdBf = GemmCfg<128, 128, 32, 2, 2, 1, 1, 1, 2>;
 // Dion sweep 3 with fp32 weights: split products, two right operands.
@@ -48,7 +50,7 @@ using ColF32 = LdCol<ROWS, 32, NT, NP, float, false, float>;
 template <int ROWS, int NT, int NP, typename GT>
 using ColMG = LdCol<ROWS, 32, NT, NP, float, true, GT>;
 
-template <typename GT>
+template <typename GT, class Cfg, int NP>
 hipError_t dion_left_t(const DionLeftArgs& a, int members, hipStream_t s) {
   GemmParams<EpiStoreF32::Args> p{};
   p.a = with_rows(a.m, a.M);
@@ -59,10 +61,10 @@ hipError_t dion_left_t(const DionLeftArgs& a, int members, hipStream_t s) {
   p.e.has_t = 0;
   p.M = a.M; p.N = a.r; p.K = a.N;
   p.splits = a.splits; p.kchunk = a.kchunk; p.tri = 0;
-  return run<CfgSplit, RowMG<128, 256, 2, GT>, ColF32<128, 256, 2>, EpiStoreF32>(p, members, s);
+  return run<Cfg, RowMG<128, 256, NP, GT>, ColF32<128, 256, NP>, EpiStoreF32>(p, members, s);
 }
 
-template <typename GT>
+template <typename GT, class Cfg, int NP>
 hipError_t dion_right_t(const DionRightArgs& a, int members, hipStream_t s) {
   GemmParams<EpiStoreF32::Args> p{};
   p.a = with_rows(a.m, a.N);   // element (j, i) = M[i][j] + G[i][j]
@@ -73,7 +75,7 @@ hipError_t dion_right_t(const DionRightArgs& a, int members, hipStream_t s) {
   p.e.has_t = 0;
   p.M = a.N; p.N = a.r; p.K = a.M;
   p.splits = a.splits; p.kchunk = a.kchunk; p.tri = 0;
-  return run<CfgSplit, ColMG<128, 256, 2, GT>, ColF32<128, 256, 2>, EpiStoreF32>(p, members, s);
+  return run<Cfg, ColMG<128, 256, NP, GT>, ColF32<128, 256, NP>, EpiStoreF32>(p, members, s);
 }
 
 template <typename XT, class Cfg, int NP>
@@ -143,15 +145,18 @@ hipError_t ns_apply_split_t(const NsApplyArgs& a, int members, hipStream_t s) {
 
 }  // namespace
 
+// bf16 weights: bf16x3 sweeps.  fp32 weights: bf16x6 sweeps.
 hipError_t launch_dion_left(const DionLeftArgs& a, bool bf16, int members, hipStream_t s) {
-  return bf16 ? dion_left_t<uint16_t>(a, members, s) : dion_left_t<float>(a, members, s);
+  return bf16 ? dion_left_t<uint16_t, CfgSplit, 2>(a, members, s)
+              : dion_left_t<float, CfgSplit6, 3>(a, members, s);
 }
 
 hipError_t launch_dion_right(const DionRightArgs& a, bool bf16, int members, hipStream_t s) {
-  return bf16 ? dion_right_t<uint16_t>(a, members, s) : dion_right_t<float>(a, members, s);
+  return bf16 ? dion_right_t<uint16_t, CfgSplit, 2>(a, members, s)
+              : dion_right_t<float, CfgSplit6, 3>(a, members, s);
 }
 
-hipError_t launch_apply_t(const ApplyArgs& a, int members, hipStream_t s) {
+hipError_t launch_apply_t(const ApplyArgs& a, bool six_products, int members, hipStream_t s) {
   GemmParams<EpiStoreF32::Args> p{};
   p.a = with_rows(a.pt, a.M);
   p.b0 = with_rows(a.tt, a.r);   // element (j, k) = T^T[j][k], zero for k > j
@@ -160,7 +165,21 @@ hipError_t launch_apply_t(const ApplyArgs& a, int members, hipStream_t s) {
   p.e.has_t = 0;
   p.M = a.M; p.N = a.r; p.K = a.r;
   p.splits = 1; p.kchunk = 0; p.tri = 1;
+  if (six_products)
+    return run<CfgSplit6, RowF32<128, 256, 3>, RowF32<128, 256, 3>, EpiStoreF32>(p, members, s);
   return run<CfgSplit, RowF32<128, 256, 2>, RowF32<128, 256, 2>, EpiStoreF32>(p, members, s);
+}
+
+hipError_t launch_gram_tn(const GramTnArgs& a, int members, hipStream_t s) {
+  GemmParams<EpiStoreF32::Args> p{};
+  p.a = with_rows(a.p, a.r);     // element (j, i) = P[i][j]
+  p.b0 = with_rows(a.p, a.r);
+  p.e.c = a.out;
+  p.e.split_stride = a.splits > 1 ? a.split_stride : 0;
+  p.e.has_t = 0;
+  p.M = a.r; p.N = a.r; p.K = a.m;
+  p.splits = a.splits; p.kchunk = a.kchunk; p.tri = 0;
+  return run<CfgSplit, ColF32<128, 256, 2>, ColF32<128, 256, 2>, EpiStoreF32>(p, members, s);
 }
 
 hipError_t launch_dion_update(const DionUpdateArgs& a, bool bf16, int members, hipStream_t s) {

@@ -107,7 +107,23 @@ struct ApplyArgs {
   MatArg out;
   int M, r;
 };
-hipError_t launch_apply_t(const ApplyArgs& a, int members, hipStream_t s);
+hipError_t launch_apply_t(const ApplyArgs& a, bool six_products, int members, hipStream_t s);
+
+// Gram of an m x r fp32 matrix, C = P^T P (r x r), bf16x3 products, split-K
+// slices (ld = r, slice stride split_stride) when splits > 1.
+struct GramTnArgs {
+  MatArg p;
+  MatArg out;
+  int64_t split_stride;
+  int m, r, splits, kchunk;
+};
+hipError_t launch_gram_tn(const GramTnArgs& a, int members, hipStream_t s);
+
+// T2^T = I - Phi(E) with E = W2 - I (W2 summed from `splits` r x r slices) and
+// Phi(E) the lower triangle of E with its diagonal halved: the first-order
+// inverse Cholesky factor of a nearly orthonormal basis.
+hipError_t launch_correction(const float* part, int64_t part_member_stride, int64_t slice, int splits,
+                             int r, float* tt, int64_t tt_stride, int members, hipStream_t s);
 
 // Dion sweep 3: M <- (M+G) - c1 P R^T,  X <- X - c2 P Q'^T.
 struct DionUpdateArgs {

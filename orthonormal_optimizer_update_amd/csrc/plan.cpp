@@ -55,6 +55,7 @@ bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* p) {
   choose_split(m, cdiv(n, 128) * cdiv(r, 128), d.chunk, &d.split_right, &d.kchunk_right);
   const int64_t tg = cdiv(r, 64);
   choose_split(m, tg * (tg + 1) / 2, d.chunk, &d.split_gram, &d.kchunk_gram);
+  choose_split(m, cdiv(r, 128) * cdiv(r, 128), d.chunk, &d.split_gram2, &d.kchunk_gram2);
   d.nrb = static_cast<int>(cdiv(n, 64));
   d.rp = cdiv(r, 4) * 4;
   const size_t mr = static_cast<size_t>(m) * r, nr = static_cast<size_t>(n) * r;
@@ -63,8 +64,10 @@ bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* p) {
   size_t part = static_cast<size_t>(d.split_left) * mr * 4;
   const size_t pr = static_cast<size_t>(d.split_right) * nr * 4;
   const size_t pg = static_cast<size_t>(d.split_gram) * rr * 8;
+  const size_t pg2 = static_cast<size_t>(d.split_gram2) * rr * 4;
   if (pr > part) part = pr;
   if (pg > part) part = pg;
+  if (pg2 > part) part = pg2;
   size_t o = 0;
   d.off_pt = o;    o = align_up(o + mrp * 4);
   d.off_p1 = o;    o = align_up(o + mrp * 4);

@@ -21,7 +21,8 @@ struct DionPlan {
   int chunk;                 // members per launch
   int split_left, kchunk_left;    // B Q: split over n
   int split_right, kchunk_right;  // B^T P: split over m
-  int split_gram, kchunk_gram;    // P^T P: split over m
+  int split_gram, kchunk_gram;    // fp64 P^T P: split over m
+  int split_gram2, kchunk_gram2;  // bf16x3 P1^T P1 (correction pass): split over m
   int nrb;                   // 64-row blocks of R (column-norm partials)
   size_t off_pt, off_p1, off_part, off_s, off_x, off_d, off_tt, off_r, off_colsq;
   size_t member_bytes;       // stride between members

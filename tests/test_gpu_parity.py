@@ -139,13 +139,13 @@ def test_dion_deterministic():
 
 
 def test_dion_rank_deficient_flags_status():
-    """Rank(B) < r: the Cholesky pivot shift and/or zero-column bit is set and
-    every output stays finite (outside the parity contract)."""
+    """B Q exactly rank deficient (two identical columns of Q, so two bitwise
+    identical columns of B Q): the Cholesky pivot shift bit is set and every
+    output stays finite (outside the parity contract)."""
     m, n, r = 64, 48, 8
-    rng = np.random.default_rng(5)
-    G = np.outer(rng.standard_normal(m), rng.standard_normal(n)).astype(np.float32)
-    X = np.zeros((m, n), np.float32)
-    Q0 = synth.right_factor0(1005, n, r)
+    X, G, Q0 = synth.small_case(5, m, n, r, "f32")
+    Q0 = Q0.copy()
+    Q0[:, 1] = Q0[:, 0]
     note("dion rank deficient")
     gpu = gpu_dion_step(X, G, np.zeros_like(X), Q0, 0.9, 0.1, "f32")
     assert gpu["status"] != 0
