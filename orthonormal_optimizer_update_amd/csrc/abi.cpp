@@ -80,6 +80,9 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     const MatArg tPart = ws_table(base, mb, pl.off_part, nb, r, 0, r, 4, 16);
     const MatArg tR = ws_table(base, mb, pl.off_r, nb, rp, ni, r, 4, 16);
     const MatArg tTt = ws_table(base, mb, pl.off_tt, nb, r, r, r, 4, 16);
+    const MatArg tPb = ws_table(base, mb, pl.off_pb, nb, pl.rpb, mi, r, 2, 16);
+    const MatArg tRb = ws_table(base, mb, pl.off_rb, nb, pl.rpb, ni, r, 2, 16);
+    const MatArg tQb = ws_table(base, mb, pl.off_qb, nb, pl.rpb, ni, r, 2, 16);
     float* part_f = reinterpret_cast<float*>(base + pl.off_part);
     double* part_d = reinterpret_cast<double*>(base + pl.off_part);
 
@@ -118,6 +121,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     ORTHO_TRY(launch_cholesky_inverse(ca, tt, static_cast<int64_t>(mb / 4), nb, s));
     ApplyArgs aa;
     aa.pt = tPt; aa.tt = tTt; aa.out = tP1; aa.M = mi; aa.r = r;
+    aa.out_bf16 = tPb; aa.has_bf16 = 0;
     ORTHO_TRY(launch_apply_t(aa, true, nb, s));
     // Pass 2: P1 is orthonormal to about 2^-24 * cond; E = P1^T P1 - I (bf16x3)
     // and the first-order factor T2 = I - Phi(E)^T give P = P1 T2.
@@ -127,7 +131,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     ORTHO_TRY(launch_gram_tn(g2, nb, s));
     ORTHO_TRY(launch_correction(part_f, static_cast<int64_t>(mb / 4), static_cast<int64_t>(r) * r,
                                 pl.split_gram2, r, tt, static_cast<int64_t>(mb / 4), nb, s));
-    aa.pt = tP1; aa.out = tPt;
+    aa.pt = tP1; aa.out = tPt; aa.has_bf16 = bf;   // bf16 P feeds the last sweep
     ORTHO_TRY(launch_apply_t(aa, false, nb, s));
 
     // Sweep 2: R = (M + G)^T P, then Q' = column-normalised R.
@@ -147,6 +151,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     ColnormArgs cn;
     cn.r = tR; cn.q = tQ; cn.colsq = rr.colsq; cn.colsq_member_stride = rr.colsq_member_stride;
     cn.nrb = pl.nrb; cn.rows = ni; cn.cols = r; cn.status = status;
+    cn.rb = tRb; cn.qb = tQb; cn.c1 = 1.0f - mu; cn.c2 = lr * scale; cn.has_bf16 = bf;
     ORTHO_TRY(launch_colnorm(cn, nb, s));
 
     if (P_out)
@@ -159,6 +164,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     // Sweep 3: error feedback into M and the weight update into X.
     DionUpdateArgs ua;
     ua.p = tPt; ua.r = tR; ua.q = tQ; ua.m = tM; ua.g = tG; ua.x = tX;
+    ua.pb = tPb; ua.rb = tRb; ua.qb = tQb;
     ua.c1 = 1.0f - mu; ua.c2 = lr * scale;
     ua.M = mi; ua.N = ni; ua.rank = r;
     ORTHO_TRY(launch_dion_update(ua, bf, nb, s));

@@ -13,15 +13,19 @@ struct EpiStoreF32 {
     int64_t split_stride;  // elements between split-K slices (0: no split)
     MatArg ct;             // transposed copy, fp32 (used when has_t)
     int has_t;
+    MatArg cb;             // bf16 copy (used when has_b)
+    int has_b;
   };
   float* c;
   float* ct;
-  int64_t ld, ldt;
-  bool has_t;
+  uint16_t* cb;
+  int64_t ld, ldt, ldb;
+  bool has_t, has_b;
   __device__ EpiStoreF32(const Args& a, int bi, int split)
       : c(static_cast<float*>(const_cast<void*>(a.c.p[bi])) + split * a.split_stride),
         ct(a.has_t ? static_cast<float*>(const_cast<void*>(a.ct.p[bi])) : nullptr),
-        ld(a.c.ld), ldt(a.ct.ld), has_t(a.has_t) {}
+        cb(a.has_b ? static_cast<uint16_t*>(const_cast<void*>(a.cb.p[bi])) : nullptr),
+        ld(a.c.ld), ldt(a.ct.ld), ldb(a.cb.ld), has_t(a.has_t), has_b(a.has_b) {}
   __device__ __forceinline__ void apply(int row0, int col, int M, int N, float v0, float v1,
                                         float v2, float v3) {
     if (col >= N) return;
@@ -33,6 +37,11 @@ struct EpiStoreF32 {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         if (row0 + t < M) ct[(int64_t)col * ldt + row0 + t] = v[t];
+    }
+    if (has_b) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (row0 + t < M) cb[(int64_t)(row0 + t) * ldb + col] = to_bf16_bits(v[t]);
     }
   }
 };
@@ -123,6 +132,7 @@ struct EpiNSApply {
                                         float v2, float v3) {
     if (col >= N) return;
     const float v[4] = {v0, v1, v2, v3};
+    uint16_t hb[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int row = row0 + t;
@@ -134,9 +144,20 @@ struct EpiNSApply {
         else store_from_f32<OUT_T>(out, (int64_t)row * ldo + col, xn);
       } else {
         x32[ix] = xn;
-        const uint16_t hb = to_bf16_bits(xn);
-        xb[(int64_t)row * ldb + col] = hb;
-        xbt[(int64_t)col * ldbt + row] = hb;
+        hb[t] = to_bf16_bits(xn);
+        xb[(int64_t)row * ldb + col] = hb[t];
+      }
+    }
+    if (!last) {
+      // The four rows are consecutive elements of one row of X^T: one 8-byte
+      // store when they are all inside (row0 is a multiple of 4 and the
+      // transposed buffer's leading dimension a multiple of 8).
+      uint16_t* dst = xbt + (int64_t)col * ldbt + row0;
+      if (row0 + 4 <= M) {
+        *reinterpret_cast<uint2*>(dst) =
+            make_uint2(hb[0] | (uint32_t(hb[1]) << 16), hb[2] | (uint32_t(hb[3]) << 16));
+      } else {
+        for (int t = 0; t < 4 && row0 + t < M; ++t) dst[t] = hb[t];
       }
     }
   }

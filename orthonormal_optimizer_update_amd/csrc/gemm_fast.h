@@ -1,0 +1,139 @@
+// Large bf16 "NT" GEMM for the Newton-Schulz products on gfx950:
+//   C[i, j] = sum_k A[i, k] * B[j, k],  A: M x K, B: N x K, both row-major bf16
+// (k contiguous), fp32 accumulation, result handed to an epilogue policy with
+// the same interface as gemm_kernel's.
+//
+// 256 x 256 x 64 block tile, 4 waves in a 2 x 2 grid, 128 x 128 per wave
+// (4 x 4 v_mfma_f32_32x32x16_bf16 accumulators).  Operand tiles go straight
+// from HBM/L2 into LDS with global_load_lds_dwordx4 (each lane's 16 bytes land
+// at LDS base + 16 * lane), two stages, one barrier per 64-wide k step.  The
+// LDS row of a tile is 8 chunks of 16 bytes; chunk c of row r is stored at
+// position c ^ ((r >> 1) & 7), which each lane realises by choosing which
+// global chunk it fetches, so that the fragment reads of 16 consecutive rows
+// hit 64 distinct banks.
+//
+// Requirements (checked by the launcher): M, N multiples of 256, K a multiple
+// of 64, 16-byte aligned rows.
+#pragma once
+
+#include "gemm_core.h"
+
+namespace ortho {
+
+namespace fast {
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int TILE_BYTES = BM * BK * 2;  // 32 KB per operand per stage
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) const void* glb_ptr_t;
+
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+
+// Issue the loads of one 256 x 64 operand tile into LDS (8 instructions per
+// wave; instruction q of wave w fills rows (8w + q) * 8 .. + 7).
+__device__ __forceinline__ void load_tile(const uint16_t* src, int64_t ld, int row0, int k0,
+                                          char* lds_tile, int wave, int lane) {
+  const int sub = lane >> 3;            // row within the 8-row group
+  const int pos = lane & 7;             // stored chunk position
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int row = (wave * 8 + q) * 8 + sub;
+    const int chunk = swz(row, pos);    // logical chunk this lane fetches
+    const uint16_t* g = src + (int64_t)(row0 + row) * ld + k0 + chunk * 8;
+    // address-space casts (generic -> global / local) need C-style casts
+    __builtin_amdgcn_global_load_lds((glb_ptr_t)(g), (lds_ptr_t)(lds_tile + (wave * 8 + q) * 1024),
+                                     16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ bf16x8 read_frag(const char* lds_tile, int row, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(lds_tile + (row * 8 + swz(row, chunk)) * 16);
+}
+
+}  // namespace fast
+
+template <class Epi>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_256(GemmParams<typename Epi::Args> p) {
+  using namespace fast;
+  __shared__ __attribute__((aligned(1024))) char smem_fast[2 * 2 * TILE_BYTES];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // Tile order: each XCD (workgroup id mod 8) gets a contiguous run of
+  // logical tiles, walked in groups of 4 tile rows so that a run shares A row
+  // blocks and B column blocks in that XCD's L2.
+  const int nwg = gridDim.x;
+  int t = blockIdx.x;
+  if ((nwg & 7) == 0) t = (t & 7) * (nwg >> 3) + (t >> 3);
+  const int tiles_n = p.tiles_n, tiles_m = nwg / tiles_n;
+  const int group = 4 * tiles_n;
+  const int first_m = (t / group) * 4;
+  const int gsize = min(tiles_m - first_m, 4);
+  const int tm = first_m + (t % group) % gsize;
+  const int tn = (t % group) / gsize;
+  const int bi = blockIdx.y;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const uint16_t* A = static_cast<const uint16_t*>(p.a.p[bi]);
+  const uint16_t* B = static_cast<const uint16_t*>(p.b0.p[bi]);
+  const int64_t lda = p.a.ld, ldb = p.b0.ld;
+  const int nk = p.K / BK;
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  auto sa = [&](int st) { return smem_fast + st * 2 * TILE_BYTES; };
+  auto sb = [&](int st) { return smem_fast + st * 2 * TILE_BYTES + TILE_BYTES; };
+
+  load_tile(A, lda, m0, 0, sa(0), wave, lane);
+  load_tile(B, ldb, n0, 0, sb(0), wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const int frow = lane & 31, fchunk = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) {
+      load_tile(A, lda, m0, (kt + 1) * BK, sa(cur ^ 1), wave, lane);
+      load_tile(B, ldb, n0, (kt + 1) * BK, sb(cur ^ 1), wave, lane);
+    }
+    const char* ta = sa(cur);
+    const char* tb = sb(cur);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = read_frag(ta, wm * 128 + i * 32 + frow, kk * 2 + fchunk);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bfr[j] = read_frag(tb, wn * 128 + j * 32 + frow, kk * 2 + fchunk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  Epi epi(p.e, bi, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int row0 = m0 + wm * 128 + i * 32 + g * 8 + (lane >> 5) * 4;
+        const int col = n0 + wn * 128 + j * 32 + (lane & 31);
+        epi.apply(row0, col, p.M, p.N, acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1],
+                  acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]);
+      }
+}
+
+}  // namespace ortho

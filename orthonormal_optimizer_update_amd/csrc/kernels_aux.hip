@@ -71,10 +71,18 @@ __global__ __launch_bounds__(256) void colnorm_kernel(ColnormArgs a) {
   const int cc = threadIdx.x & 63;
   const int c = c0 + cc;
   if (c >= a.cols) return;
+  uint16_t* rb = a.has_bf16 ? static_cast<uint16_t*>(const_cast<void*>(a.rb.p[bi])) : nullptr;
+  uint16_t* qb = a.has_bf16 ? static_cast<uint16_t*>(const_cast<void*>(a.qb.p[bi])) : nullptr;
   for (int rr = threadIdx.x >> 6; rr < 64; rr += 4) {
     const int row = blockIdx.y * 64 + rr;
     if (row >= a.rows) break;
-    q[(int64_t)row * a.q.ld + c] = r[(int64_t)row * a.r.ld + c] * inv[cc];
+    const float rv = r[(int64_t)row * a.r.ld + c];
+    const float qv = rv * inv[cc];
+    q[(int64_t)row * a.q.ld + c] = qv;
+    if (rb) {
+      rb[(int64_t)row * a.rb.ld + c] = to_bf16_bits(a.c1 * rv);
+      qb[(int64_t)row * a.qb.ld + c] = to_bf16_bits(a.c2 * qv);
+    }
   }
 }
 
@@ -177,8 +185,8 @@ __global__ __launch_bounds__(256) void ns_store_kernel(NsInitArgs a, MatArg out)
 // across the four result registers, unlike the fp32-result instructions).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void gram64_kernel(Gram64Args a) {
-  __shared__ double sa[32][66];
-  __shared__ double sb[32][66];
+  __shared__ double sa[2][32][66];
+  __shared__ double sb[2][32][66];
   const int member = blockIdx.z;
   const float* P = static_cast<const float*>(a.p.p[member]);
   double* part = a.part + member * a.part_member_stride + blockIdx.y * a.slice;
@@ -188,39 +196,66 @@ __global__ __launch_bounds__(256) void gram64_kernel(Gram64Args a) {
   while ((ta + 1) * (ta + 2) / 2 <= t) ++ta;
   while (ta * (ta + 1) / 2 > t) --ta;
   const int tb = t - ta * (ta + 1) / 2;
+  const bool diag = ta == tb;
   const int a0 = ta * 64, b0 = tb * 64;
   const int r = a.r;
   const int kbeg = blockIdx.y * a.kchunk;
   const int kend = min(a.m, kbeg + a.kchunk);
+  const int nk = kend > kbeg ? (kend - kbeg + 31) / 32 : 0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wa = wave >> 1, wb = wave & 1;
-  doublex4 acc[2][2];
-  for (int i = 0; i < 2; ++i)
-    for (int j = 0; j < 2; ++j) acc[i][j] = doublex4{0.0, 0.0, 0.0, 0.0};
-  for (int k0 = kbeg; k0 < kend; k0 += 32) {
-    // 32 rows x 64 cols of each operand; 256 threads x 8 elements
-    for (int e = threadIdx.x; e < 32 * 64; e += 256) {
+  // each thread moves 8 elements of each 32 x 64 operand tile
+  float va[8], vb[8];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int e = threadIdx.x + q * 256;
       const int kr = e >> 6, cc = e & 63;
       const int gk = k0 + kr;
-      const bool okk = gk < kend;
-      sa[kr][cc] = (okk && a0 + cc < r) ? (double)P[(int64_t)gk * a.p.ld + a0 + cc] : 0.0;
-      sb[kr][cc] = (okk && b0 + cc < r) ? (double)P[(int64_t)gk * a.p.ld + b0 + cc] : 0.0;
+      const bool ok = gk < kend;
+      const float* row = P + (int64_t)gk * a.p.ld;
+      va[q] = (ok && a0 + cc < r) ? row[a0 + cc] : 0.f;
+      if (!diag) vb[q] = (ok && b0 + cc < r) ? row[b0 + cc] : 0.f;
     }
+  };
+  auto store = [&](int st) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int e = threadIdx.x + q * 256;
+      sa[st][e >> 6][e & 63] = static_cast<double>(va[q]);
+      if (!diag) sb[st][e >> 6][e & 63] = static_cast<double>(vb[q]);
+    }
+  };
+  doublex4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = doublex4{0.0, 0.0, 0.0, 0.0};
+  if (nk > 0) {
+    load(kbeg);
+    store(0);
+  }
+  for (int kt = 0; kt < nk; ++kt) {
     __syncthreads();
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) load(kbeg + (kt + 1) * 32);
+    double (*A)[66] = sa[cur];
+    double (*B)[66] = diag ? sa[cur] : sb[cur];
 #pragma unroll
     for (int kk = 0; kk < 32; kk += 4) {
       double af[2], bf[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = sa[kk + (lane >> 4)][wa * 32 + i * 16 + (lane & 15)];
+      for (int i = 0; i < 2; ++i) af[i] = A[kk + (lane >> 4)][wa * 32 + i * 16 + (lane & 15)];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bf[j] = sb[kk + (lane >> 4)][wb * 32 + j * 16 + (lane & 15)];
+      for (int j = 0; j < 2; ++j) bf[j] = B[kk + (lane >> 4)][wb * 32 + j * 16 + (lane & 15)];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
-    __syncthreads();
+    if (more) store(cur ^ 1);
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -264,18 +299,41 @@ __global__ __launch_bounds__(256) void chol_prep_kernel(CholArgs a) {
 // numerical rank deficiency and replaced by it.
 constexpr double kPivMin = 1e-14;
 
-// Factor the nb x nb diagonal block kb of S in LDS (S_kk = L_kk L_kk^T), write
-// L_kk back, and write its inverse as block (kb, kb) of X.  Each thread owns a
-// 4 x 4 block of the 64 x 64 tile; every column step takes two barriers.
+// Broadcast lane `lane` (wave-uniform) of a double to the whole wave.
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t bits = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(bits)), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(bits >> 32)), lane);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// 1/sqrt(x) for x > 0: hardware estimate refined by two Newton steps.
+__device__ __forceinline__ double rsqrt_f64(double x) {
+  double y = __builtin_amdgcn_rsq(x);
+  y = y * (1.5 - 0.5 * x * y * y);
+  y = y * (1.5 - 0.5 * x * y * y);
+  return y;
+}
+
+// Factor the nb x nb diagonal block kb of S (S_kk = L_kk L_kk^T) and invert
+// L_kk, both in LDS, then write L_kk into S and L_kk^{-1} into block (kb, kb)
+// of X.  Blocked by 8-column panels:
+//   wave 0 factors the panel in registers (lane i holds row i; pivots and
+//   column entries move by readlane) and finishes the matching 8-row block of
+//   the inverse (lane c holds column c of Y, forward substitution with L_pp);
+//   then every thread applies the two rank-8 updates with that panel:
+//   L[i][c] -= L[i][p] L[c][p]^T (trailing block) and Y[i][c] -= L[i][p] X[p][c]
+//   (rows below the panel), with Y starting as the identity.
 __global__ __launch_bounds__(256) void chol_diag_kernel(CholArgs a, int kb) {
   __shared__ double L[64][65];
-  __shared__ double Xi[64][65];
+  __shared__ double Y[64][65];
   const int member = blockIdx.x;
   double* S = a.s + member * a.mat_stride;
   double* X = a.x + member * a.mat_stride;
   const int r = a.r;
   const int o = kb * 64;
   const int nb = min(64, r - o);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ti = (threadIdx.x >> 4) * 4, tj = (threadIdx.x & 15) * 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -283,64 +341,81 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(CholArgs a, int kb) {
     for (int j = 0; j < 4; ++j) {
       const int gi = ti + i, gj = tj + j;
       L[gi][gj] = (gi < nb && gj <= gi) ? S[(int64_t)(o + gi) * r + o + gj] : 0.0;
-      Xi[gi][gj] = (gi == gj && gi < nb) ? 1.0 : 0.0;
+      Y[gi][gj] = (gi == gj && gi < nb) ? 1.0 : 0.0;
     }
   bool shifted = false;
-  for (int j = 0; j < nb; ++j) {
+  for (int j0 = 0; j0 < nb; j0 += 8) {
     __syncthreads();
-    double piv = L[j][j];
-    if (!(piv > kPivMin) && piv == piv) {
-      piv = kPivMin;
-      shifted = true;
+    if (wave == 0) {
+      double pc[8], invd[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        pc[c] = L[lane][j0 + c];
+        invd[c] = 0.0;
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int jc = j0 + c;
+        if (jc < nb) {
+          double piv = readlane_f64(pc[c], jc);
+          if (!(piv > kPivMin) && piv == piv) {
+            piv = kPivMin;
+            shifted = true;
+          }
+          const double inv = rsqrt_f64(piv);
+          invd[c] = inv;
+          pc[c] = lane == jc ? piv * inv : (lane > jc ? pc[c] * inv : 0.0);
+#pragma unroll
+          for (int c2 = c + 1; c2 < 8; ++c2) {
+            const double lcj = readlane_f64(pc[c], j0 + c2);
+            if (lane > jc) pc[c2] -= pc[c] * lcj;
+          }
+        }
+      }
+      // Block row j0/8 of the inverse: X_p = L_pp^{-1} Y_p, lane = column.
+      double y[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) y[t] = Y[j0 + t][lane];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        double acc = y[t];
+#pragma unroll
+        for (int u = 0; u < t; ++u) acc -= readlane_f64(pc[u], j0 + t) * y[u];
+        y[t] = acc * invd[t];
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) L[lane][j0 + c] = pc[c];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) Y[j0 + t][lane] = y[t];
     }
-    const double ljj = sqrt(piv), inv = 1.0 / ljj;
-    // trailing update with the unscaled column j: L[i][c] -= L[i][j] L[c][j] / piv
+    __syncthreads();
+    const int pe = j0 + 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int gi = ti + i;
-      if (gi <= j || gi >= nb) continue;
-      const double lij = L[gi][j] * inv;
+      if (gi >= nb || gi < pe) continue;
+      double li[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) li[u] = L[gi][j0 + u];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int gc = tj + c;
-        if (gc > j && gc <= gi) L[gi][gc] -= lij * (L[gc][j] * inv);
+        if (gc >= pe && gc <= gi) {
+          double acc = 0.0;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) acc += li[u] * L[gc][j0 + u];
+          L[gi][gc] -= acc;
+        } else if (gc < pe) {
+          double acc = 0.0;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) acc += li[u] * Y[j0 + u][gc];
+          Y[gi][gc] -= acc;
+        }
       }
-    }
-    __syncthreads();
-    if (tj <= j && j < tj + 4) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int gi = ti + i;
-        if (gi > j && gi < nb) L[gi][j] *= inv;
-        else if (gi == j) L[j][j] = ljj;
-      }
-    }
-  }
-  if (shifted && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
-  // Inverse by right-looking forward substitution on L X = I: row t is final
-  // once divided by L[t][t]; its multiple is removed from every row below.
-  for (int t = 0; t < nb; ++t) {
-    __syncthreads();
-    const double dinv = 1.0 / L[t][t];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int gi = ti + i;
-      if (gi <= t || gi >= nb) continue;
-      const double f = L[gi][t] * dinv;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int gc = tj + c;
-        if (gc <= t) Xi[gi][gc] -= f * Xi[t][gc];
-      }
-    }
-    __syncthreads();
-    if (ti <= t && t < ti + 4) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (tj + c <= t) Xi[t][tj + c] *= dinv;
     }
   }
   __syncthreads();
+  if (shifted && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -348,7 +423,7 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(CholArgs a, int kb) {
       const int gi = ti + i, gj = tj + j;
       if (gi < nb && gj <= gi) {
         S[(int64_t)(o + gi) * r + o + gj] = L[gi][gj];
-        X[(int64_t)(o + gi) * r + o + gj] = Xi[gi][gj];
+        X[(int64_t)(o + gi) * r + o + gj] = Y[gi][gj];
       }
     }
 }
@@ -360,10 +435,19 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(CholArgs a, int kb) {
 template <bool TRANS_B>
 __device__ void tile_gemm64(const double* A, const double* B, int r, int ar, int ac, int br,
                             int bc, double (*sA)[65], double (*sB)[65], doublex4 acc[2][2]) {
-  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+  double va[16], vb[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {  // all 32 loads in flight before any LDS store
+    const int e = threadIdx.x + q * 256;
     const int i = e >> 6, j = e & 63;
-    sA[i][j] = (ar + i < r && ac + j < r) ? A[(int64_t)(ar + i) * r + ac + j] : 0.0;
-    sB[i][j] = (br + i < r && bc + j < r) ? B[(int64_t)(br + i) * r + bc + j] : 0.0;
+    va[q] = (ar + i < r && ac + j < r) ? A[(int64_t)(ar + i) * r + ac + j] : 0.0;
+    vb[q] = (br + i < r && bc + j < r) ? B[(int64_t)(br + i) * r + bc + j] : 0.0;
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int e = threadIdx.x + q * 256;
+    sA[e >> 6][e & 63] = va[q];
+    sB[e >> 6][e & 63] = vb[q];
   }
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

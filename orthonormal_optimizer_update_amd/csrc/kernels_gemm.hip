@@ -2,6 +2,7 @@
 // Newton-Schulz paths, and their host launchers.
 #include "epilogues.h"
 #include "gemm_core.h"
+#include "gemm_fast.h"
 #include "launch.h"
 
 namespace ortho {
@@ -32,8 +33,9 @@ MatArg with_rows(MatArg a, int rows) {
 using CfgSplit = GemmCfg<128, 128, 32, 2, 2, 2, 2, 3, 1>;
 // The same with three pieces and six products (fp32-level products).
 using CfgSplit6 = GemmCfg<128, 128, 32, 2, 2, 3, 3, 6, 1>;
-// Dion sweep 3 with bf16 weights: one product, two right operands.
-using CfgUpdBf = GemmCfg<128, 128, 32, 2, 2, 1, 1, 1, 2>;
+// Dion sweep 3 with bf16 weights: one product from pre-converted bf16 factors,
+// two right operands, 256 x 128 tiles with 8 waves.
+using CfgUpdBf = GemmCfg<256, 128, 32, 4, 2, 1, 1, 1, 2>;
 // Dion sweep 3 with fp32 weights: split products, two right operands.
 using CfgUpdF32 = GemmCfg<128, 128, 32, 2, 2, 2, 2, 3, 2>;
 // Newton-Schulz: 256 x 256 tiles with 8 waves for large matrices, 128 x 128
@@ -78,9 +80,8 @@ hipError_t dion_right_t(const DionRightArgs& a, int members, hipStream_t s) {
   return run<Cfg, ColMG<128, 256, NP, GT>, ColF32<128, 256, NP>, EpiStoreF32>(p, members, s);
 }
 
-template <typename XT, class Cfg, int NP>
-hipError_t dion_update_t(const DionUpdateArgs& a, int members, hipStream_t s) {
-  GemmParams<typename EpiDion<XT>::Args> p{};
+hipError_t dion_update_f32(const DionUpdateArgs& a, int members, hipStream_t s) {
+  GemmParams<typename EpiDion<float>::Args> p{};
   p.a = with_rows(a.p, a.M);
   p.b0 = with_rows(a.r, a.N);
   p.b1 = with_rows(a.q, a.N);
@@ -88,11 +89,40 @@ hipError_t dion_update_t(const DionUpdateArgs& a, int members, hipStream_t s) {
   p.e.c1 = a.c1; p.e.c2 = a.c2;
   p.M = a.M; p.N = a.N; p.K = a.rank;
   p.splits = 1; p.kchunk = 0; p.tri = 0;
-  return run<Cfg, RowF32<128, 256, NP>, RowF32<128, 256, NP>, EpiDion<XT>>(p, members, s);
+  return run<CfgUpdF32, RowF32<128, 256, 2>, RowF32<128, 256, 2>, EpiDion<float>>(p, members, s);
+}
+
+hipError_t dion_update_bf16(const DionUpdateArgs& a, int members, hipStream_t s) {
+  GemmParams<typename EpiDion<uint16_t>::Args> p{};
+  p.a = with_rows(a.pb, a.M);
+  p.b0 = with_rows(a.rb, a.N);
+  p.b1 = with_rows(a.qb, a.N);
+  p.e.m = a.m; p.e.g = a.g; p.e.x = a.x;
+  p.e.c1 = 1.0f; p.e.c2 = 1.0f;   // factors arrive pre-scaled
+  p.M = a.M; p.N = a.N; p.K = a.rank;
+  p.splits = 1; p.kchunk = 0; p.tri = 0;
+  return run<CfgUpdBf, LdRowBf16<256, 32, 512>, LdRowBf16<128, 32, 512>, EpiDion<uint16_t>>(
+      p, members, s);
 }
 
 template <class Cfg>
 using NsRow = LdRowBf16<Cfg::BM, 32, Cfg::NT>;
+
+// The 256 x 256 x 64 direct-to-LDS kernel applies when the product tiles
+// exactly and every operand row is 16-byte aligned.
+bool fast_ok(int M, int N, int K, const MatArg& a, const MatArg& b) {
+  return M % 256 == 0 && N % 256 == 0 && K % 64 == 0 && a.vec && b.vec && a.ld % 8 == 0 &&
+         b.ld % 8 == 0;
+}
+
+template <class Epi>
+hipError_t run_fast(GemmParams<typename Epi::Args>& p, int members, hipStream_t s) {
+  p.tiles_n = p.N / 256;
+  p.splits = 1;
+  dim3 grid((p.M / 256) * p.tiles_n, members);
+  hipLaunchKernelGGL((gemm_bf16_256<Epi>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
 
 template <class Cfg>
 hipError_t ns_gram_t(const NsGramArgs& a, int members, hipStream_t s) {
@@ -102,6 +132,7 @@ hipError_t ns_gram_t(const NsGramArgs& a, int members, hipStream_t s) {
   p.e.a = a.a;
   p.M = a.M; p.N = a.M; p.K = a.K;
   p.splits = 1; p.kchunk = 0; p.tri = 0;
+  if (fast_ok(p.M, p.N, p.K, p.a, p.b0)) return run_fast<EpiNSGram>(p, members, s);
   return run<Cfg, NsRow<Cfg>, NsRow<Cfg>, EpiNSGram>(p, members, s);
 }
 
@@ -114,6 +145,7 @@ hipError_t ns_poly_t(const NsPolyArgs& a, int members, hipStream_t s) {
   p.e.has32 = a.M <= kNsSplitRows;
   p.M = a.M; p.N = a.M; p.K = a.M;
   p.splits = 1; p.kchunk = 0; p.tri = 0;
+  if (fast_ok(p.M, p.N, p.K, p.a, p.b0)) return run_fast<EpiNSPoly>(p, members, s);
   return run<Cfg, NsRow<Cfg>, NsRow<Cfg>, EpiNSPoly>(p, members, s);
 }
 
@@ -126,6 +158,7 @@ hipError_t ns_apply_t(const NsApplyArgs& a, int members, hipStream_t s) {
   p.e.a = a.a; p.e.last = a.last; p.e.out_transposed = a.out_transposed;
   p.M = a.M; p.N = a.N; p.K = a.M;
   p.splits = 1; p.kchunk = 0; p.tri = 0;
+  if (fast_ok(p.M, p.N, p.K, p.a, p.b0)) return run_fast<EpiNSApply<OUT_T>>(p, members, s);
   return run<Cfg, NsRow<Cfg>, NsRow<Cfg>, EpiNSApply<OUT_T>>(p, members, s);
 }
 
@@ -163,6 +196,8 @@ hipError_t launch_apply_t(const ApplyArgs& a, bool six_products, int members, hi
   p.e.c = a.out;
   p.e.split_stride = 0;
   p.e.has_t = 0;
+  p.e.cb = a.out_bf16;
+  p.e.has_b = a.has_bf16;
   p.M = a.M; p.N = a.r; p.K = a.r;
   p.splits = 1; p.kchunk = 0; p.tri = 1;
   if (six_products)
@@ -183,8 +218,7 @@ hipError_t launch_gram_tn(const GramTnArgs& a, int members, hipStream_t s) {
 }
 
 hipError_t launch_dion_update(const DionUpdateArgs& a, bool bf16, int members, hipStream_t s) {
-  return bf16 ? dion_update_t<uint16_t, CfgUpdBf, 1>(a, members, s)
-              : dion_update_t<float, CfgUpdF32, 2>(a, members, s);
+  return bf16 ? dion_update_bf16(a, members, s) : dion_update_f32(a, members, s);
 }
 
 hipError_t launch_ns_gram(const NsGramArgs& a, int members, hipStream_t s) {

@@ -25,6 +25,10 @@ struct ColnormArgs {
   int64_t colsq_member_stride;
   int nrb, rows, cols;
   int32_t* status;
+  // optional bf16 operands of the last sweep: rb = c1 * R, qb = c2 * Q'
+  MatArg rb, qb;
+  float c1, c2;
+  int has_bf16;
 };
 
 struct SumsqArgs {
@@ -105,6 +109,8 @@ hipError_t launch_dion_right(const DionRightArgs& a, bool bf16, int members, hip
 struct ApplyArgs {
   MatArg pt, tt;
   MatArg out;
+  MatArg out_bf16;   // optional bf16 copy of the result (has_bf16)
+  int has_bf16;
   int M, r;
 };
 hipError_t launch_apply_t(const ApplyArgs& a, bool six_products, int members, hipStream_t s);
@@ -125,9 +131,12 @@ hipError_t launch_gram_tn(const GramTnArgs& a, int members, hipStream_t s);
 hipError_t launch_correction(const float* part, int64_t part_member_stride, int64_t slice, int splits,
                              int r, float* tt, int64_t tt_stride, int members, hipStream_t s);
 
-// Dion sweep 3: M <- (M+G) - c1 P R^T,  X <- X - c2 P Q'^T.
+// Dion sweep 3: M <- (M+G) - c1 P R^T,  X <- X - c2 P Q'^T.  With bf16
+// weights the factors come pre-scaled as bf16 (pb, rb = c1 R, qb = c2 Q');
+// with fp32 weights as fp32 (p, r, q) scaled in the epilogue.
 struct DionUpdateArgs {
   MatArg p, r, q;        // P m x r, R n x r, Q' n x r (fp32)
+  MatArg pb, rb, qb;     // bf16 copies (bf16 weights)
   MatArg m, g, x;
   float c1, c2;
   int M, N, rank;

@@ -78,6 +78,10 @@ bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* p) {
   d.off_tt = o;    o = align_up(o + rr * 4);
   d.off_r = o;     o = align_up(o + nrp * 4);
   d.off_colsq = o; o = align_up(o + static_cast<size_t>(d.nrb) * r * 4);
+  d.rpb = cdiv(r, 8) * 8;
+  d.off_pb = o;    o = align_up(o + static_cast<size_t>(m) * d.rpb * 2);
+  d.off_rb = o;    o = align_up(o + static_cast<size_t>(n) * d.rpb * 2);
+  d.off_qb = o;    o = align_up(o + static_cast<size_t>(n) * d.rpb * 2);
   d.member_bytes = o;
   d.total_bytes = o * static_cast<size_t>(d.chunk);
   *p = d;

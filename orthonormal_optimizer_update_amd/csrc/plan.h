@@ -25,6 +25,8 @@ struct DionPlan {
   int split_gram2, kchunk_gram2;  // bf16x3 P1^T P1 (correction pass): split over m
   int nrb;                   // 64-row blocks of R (column-norm partials)
   size_t off_pt, off_p1, off_part, off_s, off_x, off_d, off_tt, off_r, off_colsq;
+  int64_t rpb;               // leading dimension of the bf16 factor copies (r rounded to 8)
+  size_t off_pb, off_rb, off_qb;  // bf16 P, (1-mu) R, lr*scale*Q' for the last sweep
   size_t member_bytes;       // stride between members
   size_t total_bytes;
 };
