@@ -26,6 +26,9 @@ COMMON_FLAGS = [
     "--offload-arch=gfx950",
     # never emit packed-fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the unrolled epilogues index the accumulator arrays with constants only if
+    # every loop over them is fully unrolled; the default size limit is too low
+    "-mllvm", "-pragma-unroll-threshold=200000",
 ]
 
 

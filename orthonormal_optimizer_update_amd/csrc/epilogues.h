@@ -1,5 +1,9 @@
-// Epilogue policies for gemm_kernel.  apply() receives rows row0..row0+3 of
-// column col (acc values v0..v3); apply2() also receives a second accumulator.
+// Epilogue policies for the GEMM kernels.  apply() receives rows row0..row0+3
+// of column col (acc values v0..v3); apply2() also receives a second
+// accumulator.  A policy with kPreload = true also provides init() (init2()),
+// which sets the accumulators before the main loop: terms of the result that
+// come from memory are loaded there, where no store precedes them and the loads
+// can all be in flight at once, so the epilogue itself only stores.
 #pragma once
 
 #include "common.h"
@@ -8,6 +12,7 @@ namespace ortho {
 
 // fp32 store of C (optionally also C^T), or of one split-K slice of C.
 struct EpiStoreF32 {
+  static constexpr bool kPreload = false;
   struct Args {
     MatArg c;              // destination, fp32
     int64_t split_stride;  // elements between split-K slices (0: no split)
@@ -48,6 +53,7 @@ struct EpiStoreF32 {
 
 // Newton-Schulz Gram A = X X^T, stored as bf16.
 struct EpiNSGram {
+  static constexpr bool kPreload = false;
   struct Args {
     MatArg a;  // bf16 bits, M x N
   };
@@ -65,8 +71,11 @@ struct EpiNSGram {
   }
 };
 
-// Newton-Schulz polynomial Bp = b A + c (A A), stored as bf16.
+// Newton-Schulz polynomial Bp = b A + c (A A), stored as bf16 (and fp32 when
+// has32).  The accumulator starts at (b/c) A, so the result is c * acc (c != 0;
+// the launcher handles c == 0 without a product).
 struct EpiNSPoly {
+  static constexpr bool kPreload = true;
   struct Args {
     MatArg a;     // bf16 A (read)
     MatArg bp;    // bf16 Bp (written)
@@ -78,12 +87,18 @@ struct EpiNSPoly {
   uint16_t* bp;
   float* bp32;
   int64_t lda, ldb, ldb32;
-  float b, c;
+  float boc, c;
   __device__ EpiNSPoly(const Args& g, int bi, int)
       : a(static_cast<const uint16_t*>(g.a.p[bi])),
         bp(static_cast<uint16_t*>(const_cast<void*>(g.bp.p[bi]))),
         bp32(g.has32 ? static_cast<float*>(const_cast<void*>(g.bp32.p[bi])) : nullptr),
-        lda(g.a.ld), ldb(g.bp.ld), ldb32(g.bp32.ld), b(g.b), c(g.c) {}
+        lda(g.a.ld), ldb(g.bp.ld), ldb32(g.bp32.ld), boc(g.b / g.c), c(g.c) {}
+  __device__ __forceinline__ void init(int row0, int col, int M, int N, float* v) const {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      v[t] = (col < N && row0 + t < M) ? boc * bf16_bits_to_f32(a[(int64_t)(row0 + t) * lda + col])
+                                       : 0.f;
+  }
   __device__ __forceinline__ void apply(int row0, int col, int M, int N, float v0, float v1,
                                         float v2, float v3) {
     if (col >= N) return;
@@ -91,20 +106,21 @@ struct EpiNSPoly {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       if (row0 + t < M) {
-        const float av = bf16_bits_to_f32(a[(int64_t)(row0 + t) * lda + col]);
-        const float y = b * av + c * v[t];
+        const float y = c * v[t];
         bp[(int64_t)(row0 + t) * ldb + col] = to_bf16_bits(y);
         if (bp32) bp32[(int64_t)(row0 + t) * ldb32 + col] = y;
       }
   }
 };
 
-// Newton-Schulz apply X <- a X + Bp X.  The fp32 iterate is updated in place;
-// bf16 copies in both orientations feed the next iteration's products.  On the
-// last iteration the result goes to the caller's output instead, in its dtype,
-// transposed back when the input was tall.
+// Newton-Schulz apply X <- a X + Bp X.  The accumulator starts at a X (the
+// fp32 iterate), so the result is the accumulator: it overwrites the fp32
+// iterate and its bf16 copies in both orientations, or, on the last
+// iteration, goes to the caller's output in its dtype (transposed back when
+// the input was tall).
 template <typename OUT_T>
 struct EpiNSApply {
+  static constexpr bool kPreload = true;
   struct Args {
     MatArg x32;   // fp32 iterate, M x N (read and written)
     MatArg xb;    // bf16 M x N (written unless last)
@@ -128,46 +144,56 @@ struct EpiNSApply {
         out(static_cast<OUT_T*>(const_cast<void*>(g.out.p[bi]))),
         ldx(g.x32.ld), ldb(g.xb.ld), ldbt(g.xbt.ld), ldo(g.out.ld), a(g.a), last(g.last),
         out_t(g.out_transposed) {}
+  __device__ __forceinline__ void init(int row0, int col, int M, int N, float* v) const {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      v[t] = (col < N && row0 + t < M) ? a * x32[(int64_t)(row0 + t) * ldx + col] : 0.f;
+  }
   __device__ __forceinline__ void apply(int row0, int col, int M, int N, float v0, float v1,
                                         float v2, float v3) {
     if (col >= N) return;
     const float v[4] = {v0, v1, v2, v3};
-    uint16_t hb[4] = {0, 0, 0, 0};
+    if (last) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int row = row0 + t;
+        if (row >= M) continue;
+        if (out_t) store_from_f32<OUT_T>(out, (int64_t)col * ldo + row, v[t]);
+        else store_from_f32<OUT_T>(out, (int64_t)row * ldo + col, v[t]);
+      }
+      return;
+    }
+    uint16_t hb[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
+      hb[t] = to_bf16_bits(v[t]);
       const int row = row0 + t;
-      if (row >= M) continue;
-      const int64_t ix = (int64_t)row * ldx + col;
-      const float xn = a * x32[ix] + v[t];
-      if (last) {
-        if (out_t) store_from_f32<OUT_T>(out, (int64_t)col * ldo + row, xn);
-        else store_from_f32<OUT_T>(out, (int64_t)row * ldo + col, xn);
-      } else {
-        x32[ix] = xn;
-        hb[t] = to_bf16_bits(xn);
+      if (row < M) {
+        x32[(int64_t)row * ldx + col] = v[t];
         xb[(int64_t)row * ldb + col] = hb[t];
       }
     }
-    if (!last) {
-      // The four rows are consecutive elements of one row of X^T: one 8-byte
-      // store when they are all inside (row0 is a multiple of 4 and the
-      // transposed buffer's leading dimension a multiple of 8).
-      uint16_t* dst = xbt + (int64_t)col * ldbt + row0;
-      if (row0 + 4 <= M) {
-        *reinterpret_cast<uint2*>(dst) =
-            make_uint2(hb[0] | (uint32_t(hb[1]) << 16), hb[2] | (uint32_t(hb[3]) << 16));
-      } else {
-        for (int t = 0; t < 4 && row0 + t < M; ++t) dst[t] = hb[t];
-      }
+    // The four rows are consecutive elements of one row of X^T: one 8-byte
+    // store when they are all inside (row0 is a multiple of 4 and the
+    // transposed buffer's leading dimension a multiple of 8).
+    uint16_t* dst = xbt + (int64_t)col * ldbt + row0;
+    if (row0 + 4 <= M) {
+      *reinterpret_cast<uint2*>(dst) =
+          make_uint2(hb[0] | (uint32_t(hb[1]) << 16), hb[2] | (uint32_t(hb[3]) << 16));
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (row0 + t < M) dst[t] = hb[t];
     }
   }
 };
 
-// Dion sweep 3: with B = M + G recomputed from the inputs,
+// Dion sweep 3 (fp32 weights): with B = M + G recomputed from the inputs,
 //   M <- B - c1 * (P R^T),   X <- X - c2 * (P Q'^T)
-// where c1 = 1 - mu and c2 = lr * scale.  X is rounded to its storage dtype.
+// where c1 = 1 - mu and c2 = lr * scale.
 template <typename XT>
 struct EpiDion {
+  static constexpr bool kPreload = false;
   struct Args {
     MatArg m;  // fp32 momentum (read and written)
     MatArg g;  // gradient, XT
@@ -200,6 +226,51 @@ struct EpiDion {
       const float bval = m[im] + load_as_f32<XT>(g, ig);
       m[im] = bval - c1 * u[t];
       store_from_f32<XT>(x, ix, load_as_f32<XT>(x, ix) - c2 * w[t]);
+    }
+  }
+};
+
+// Dion sweep 3 (bf16 weights) with the factors pre-scaled (R by c1, Q' by
+// c2): the accumulators start at -(M + G) and -X, so after the products
+// M' = -acc1 and X' = -acc2 (rounded to bf16); the epilogue only stores.
+struct EpiDionPre {
+  static constexpr bool kPreload = true;
+  struct Args {
+    MatArg m;  // fp32 momentum (read and written)
+    MatArg g;  // bf16 gradient
+    MatArg x;  // bf16 weight (read and written)
+    float c1, c2;
+  };
+  float* m;
+  const uint16_t* g;
+  uint16_t* x;
+  int64_t ldm, ldg, ldx;
+  __device__ EpiDionPre(const Args& e, int bi, int)
+      : m(static_cast<float*>(const_cast<void*>(e.m.p[bi]))),
+        g(static_cast<const uint16_t*>(e.g.p[bi])),
+        x(static_cast<uint16_t*>(const_cast<void*>(e.x.p[bi]))),
+        ldm(e.m.ld), ldg(e.g.ld), ldx(e.x.ld) {}
+  __device__ __forceinline__ void init2(int row0, int col, int M, int N, float* u, float* w) const {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = row0 + t;
+      const bool ok = col < N && row < M;
+      u[t] = ok ? -(m[(int64_t)row * ldm + col] + bf16_bits_to_f32(g[(int64_t)row * ldg + col])) : 0.f;
+      w[t] = ok ? -bf16_bits_to_f32(x[(int64_t)row * ldx + col]) : 0.f;
+    }
+  }
+  __device__ __forceinline__ void apply2(int row0, int col, int M, int N, float u0, float u1,
+                                         float u2, float u3, float w0, float w1, float w2,
+                                         float w3) {
+    if (col >= N) return;
+    const float u[4] = {u0, u1, u2, u3};
+    const float w[4] = {w0, w1, w2, w3};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = row0 + t;
+      if (row >= M) continue;
+      m[(int64_t)row * ldm + col] = -u[t];
+      x[(int64_t)row * ldx + col] = to_bf16_bits(-w[t]);
     }
   }
 };

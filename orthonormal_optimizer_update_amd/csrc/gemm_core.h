@@ -278,6 +278,29 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(GemmParams<typename Epi::
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[q][i][j][e] = 0.f;
 
+  Epi epi(p.e, bi, split);
+  if constexpr (Epi::kPreload) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int row0 = m0 + wm * Cfg::WTM + i * 32 + g * 8 + (lane >> 5) * 4;
+          const int col = n0 + wn * Cfg::WTN + j * 32 + (lane & 31);
+          float u[4], w[4];
+          if constexpr (NBOP == 1) {
+            epi.init(row0, col, p.M, p.N, u);
+          } else {
+            epi.init2(row0, col, p.M, p.N, u, w);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[NBOP - 1][i][j][g * 4 + t] = w[t];
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[0][i][j][g * 4 + t] = u[t];
+        }
+  }
+
   LA la(p.a, p.a2, bi);
   LB lb0(p.b0, p.b0s, bi);
   LB lb1(NBOP == 2 ? p.b1 : p.b0, NBOP == 2 ? p.b1s : p.b0s, bi);
@@ -356,7 +379,6 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(GemmParams<typename Epi::
 
   // Epilogue: hand each lane's four consecutive rows of one column to the
   // policy, which applies bounds and writes.
-  Epi epi(p.e, bi, split);
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll

@@ -88,6 +88,26 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256(GemmParams<typename Epi:
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+  Epi epi(p.e, bi, 0);
+  if constexpr (Epi::kPreload) {
+    // one accumulator row (64 values per lane) at a time keeps the loads in
+    // flight without running out of registers next to the accumulators
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float u[4];
+          epi.init(m0 + wm * 128 + i * 32 + g * 8 + (lane >> 5) * 4,
+                   n0 + wn * 128 + j * 32 + (lane & 31), p.M, p.N, u);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[i][j][g * 4 + t] = u[t];
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
   auto sa = [&](int st) { return smem_fast + st * 2 * TILE_BYTES; };
   auto sb = [&](int st) { return smem_fast + st * 2 * TILE_BYTES + TILE_BYTES; };
 
@@ -97,9 +117,21 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256(GemmParams<typename Epi:
   __syncthreads();
 
   const int frow = lane & 31, fchunk = lane >> 5;
+  // Fragments are double-buffered in registers: the reads for k step kk + 1
+  // are issued before the 16 products of step kk, so LDS latency overlaps the
+  // matrix cores (also across the k-tile barrier).
+  bf16x8 fa[2][4], fb[2][4];
+  auto read_frags = [&](bf16x8 (&a)[4], bf16x8 (&b)[4], const char* ta, const char* tb, int kk) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = read_frag(ta, wm * 128 + i * 32 + frow, kk * 2 + fchunk);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = read_frag(tb, wn * 128 + j * 32 + frow, kk * 2 + fchunk);
+  };
+  read_frags(fa[0], fb[0], sa(0), sb(0), 0);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) {
+    const bool more = kt + 1 < nk;
+    if (more) {
       load_tile(A, lda, m0, (kt + 1) * BK, sa(cur ^ 1), wave, lane);
       load_tile(B, ldb, n0, (kt + 1) * BK, sb(cur ^ 1), wave, lane);
     }
@@ -107,22 +139,30 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256(GemmParams<typename Epi:
     const char* tb = sb(cur);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = read_frag(ta, wm * 128 + i * 32 + frow, kk * 2 + fchunk);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[j] = read_frag(tb, wn * 128 + j * 32 + frow, kk * 2 + fchunk);
+      if (kk < 3) read_frags(fa[(kk + 1) & 1], fb[(kk + 1) & 1], ta, tb, kk + 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
     }
+    // Instruction order for the scheduler: tile loads first, then for each k
+    // step the next step's 8 fragment reads interleaved with its 16 products.
+    __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);  // VMEM reads (tile loads)
+#pragma unroll
+    for (int kk = 0; kk < 3; ++kk) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (more) read_frags(fa[0], fb[0], sa(cur ^ 1), sb(cur ^ 1), 0);
   }
 
-  Epi epi(p.e, bi, 0);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll

@@ -90,21 +90,22 @@ __global__ __launch_bounds__(256) void colnorm_kernel(ColnormArgs a) {
 // Newton-Schulz normalisation
 // ---------------------------------------------------------------------------
 
-// Partial sums of squares of G: block b of member bi covers elements
-// [b*chunk, (b+1)*chunk) in row-major order of the logical m x n matrix.
+// Partial sums of squares of G: block b of member bi covers rows
+// [b*rows, (b+1)*rows) of the m x n input; threads stride along the row.
 template <typename T>
 __global__ __launch_bounds__(256) void sumsq_kernel(SumsqArgs a) {
   __shared__ float red[256];
   const int bi = blockIdx.y;
   const T* g = static_cast<const T*>(a.g.p[bi]);
-  const int64_t total = (int64_t)a.g.rows * a.g.cols;
-  const int64_t beg = (int64_t)blockIdx.x * a.chunk;
-  const int64_t end = beg + a.chunk < total ? beg + a.chunk : total;
+  const int r0 = blockIdx.x * a.chunk;
+  const int r1 = min(a.g.rows, r0 + static_cast<int>(a.chunk));
   float s = 0.f;
-  for (int64_t e = beg + threadIdx.x; e < end; e += 256) {
-    const int64_t r = e / a.g.cols, c = e % a.g.cols;
-    const float v = load_as_f32<T>(g, r * a.g.ld + c);
-    s += v * v;
+  for (int r = r0; r < r1; ++r) {
+    const T* row = g + (int64_t)r * a.g.ld;
+    for (int c = threadIdx.x; c < a.g.cols; c += 256) {
+      const float v = load_as_f32<T>(row, c);
+      s += v * v;
+    }
   }
   red[threadIdx.x] = s;
   __syncthreads();
@@ -115,15 +116,22 @@ __global__ __launch_bounds__(256) void sumsq_kernel(SumsqArgs a) {
   if (threadIdx.x == 0) a.partial[bi * a.partial_stride + blockIdx.x] = red[0];
 }
 
-// scale = 1 / (sqrt(sum of partials) + eps), summed in fp64 in block order.
+// scale = 1 / (sqrt(sum of partials) + eps), summed in fp64: each of 64 threads
+// takes a fixed strided subset, then a fixed-order tree (deterministic).
 __global__ __launch_bounds__(64) void ns_scale_kernel(const float* partial, int64_t partial_stride,
                                                       int nparts, float* scale, int64_t scale_stride,
                                                       float eps) {
-  if (threadIdx.x != 0) return;
+  __shared__ double red[64];
   const int bi = blockIdx.x;
   double s = 0.0;
-  for (int i = 0; i < nparts; ++i) s += partial[bi * partial_stride + i];
-  scale[bi * scale_stride] = static_cast<float>(1.0 / (sqrt(s) + (double)eps));
+  for (int i = threadIdx.x; i < nparts; i += 64) s += partial[bi * partial_stride + i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 32; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) scale[bi * scale_stride] = static_cast<float>(1.0 / (sqrt(red[0]) + (double)eps));
 }
 
 // X0 = scale * G (wide orientation: rows <= cols, transposing a tall G), into
@@ -175,6 +183,22 @@ __global__ __launch_bounds__(256) void ns_store_kernel(NsInitArgs a, MatArg out)
   const float v = x32[(int64_t)i * a.x32.ld + j];
   if (a.transposed) store_from_f32<T>(o, (int64_t)j * out.ld + i, v);
   else store_from_f32<T>(o, (int64_t)i * out.ld + j, v);
+}
+
+// Bp = b A when the quintic coefficient c is zero (no product needed).
+__global__ __launch_bounds__(256) void ns_linear_kernel(NsPolyArgs a) {
+  const int bi = blockIdx.z;
+  const int i = blockIdx.y * 16 + (threadIdx.x >> 4);
+  const int j = blockIdx.x * 16 + (threadIdx.x & 15);
+  if (i >= a.M || j >= a.M) return;
+  const uint16_t* A = static_cast<const uint16_t*>(a.a.p[bi]);
+  uint16_t* bp = static_cast<uint16_t*>(const_cast<void*>(a.bp.p[bi]));
+  const float y = a.b * bf16_bits_to_f32(A[(int64_t)i * a.a.ld + j]);
+  bp[(int64_t)i * a.bp.ld + j] = to_bf16_bits(y);
+  if (a.M <= kNsSplitRows) {
+    float* b32 = static_cast<float*>(const_cast<void*>(a.bp32.p[bi]));
+    b32[(int64_t)i * a.bp32.ld + j] = y;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -636,6 +660,12 @@ hipError_t launch_correction(const float* part, int64_t part_member_stride, int6
                              int r, float* tt, int64_t tt_stride, int members, hipStream_t s) {
   hipLaunchKernelGGL(correction_kernel, dim3(cdiv(r, 16), cdiv(r, 16), members), dim3(256), 0, s, part,
                      part_member_stride, slice, splits, r, tt, tt_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_ns_linear(const NsPolyArgs& a, int members, hipStream_t s) {
+  dim3 grid(cdiv(a.M, 16), cdiv(a.M, 16), members);
+  hipLaunchKernelGGL(ns_linear_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -93,7 +93,7 @@ hipError_t dion_update_f32(const DionUpdateArgs& a, int members, hipStream_t s) 
 }
 
 hipError_t dion_update_bf16(const DionUpdateArgs& a, int members, hipStream_t s) {
-  GemmParams<typename EpiDion<uint16_t>::Args> p{};
+  GemmParams<EpiDionPre::Args> p{};
   p.a = with_rows(a.pb, a.M);
   p.b0 = with_rows(a.rb, a.N);
   p.b1 = with_rows(a.qb, a.N);
@@ -101,8 +101,7 @@ hipError_t dion_update_bf16(const DionUpdateArgs& a, int members, hipStream_t s)
   p.e.c1 = 1.0f; p.e.c2 = 1.0f;   // factors arrive pre-scaled
   p.M = a.M; p.N = a.N; p.K = a.rank;
   p.splits = 1; p.kchunk = 0; p.tri = 0;
-  return run<CfgUpdBf, LdRowBf16<256, 32, 512>, LdRowBf16<128, 32, 512>, EpiDion<uint16_t>>(
-      p, members, s);
+  return run<CfgUpdBf, LdRowBf16<256, 32, 512>, LdRowBf16<128, 32, 512>, EpiDionPre>(p, members, s);
 }
 
 template <class Cfg>
@@ -226,6 +225,7 @@ hipError_t launch_ns_gram(const NsGramArgs& a, int members, hipStream_t s) {
 }
 
 hipError_t launch_ns_poly(const NsPolyArgs& a, int members, hipStream_t s) {
+  if (a.c == 0.0f) return launch_ns_linear(a, members, s);
   return a.M > 128 ? ns_poly_t<CfgNsBig>(a, members, s) : ns_poly_t<CfgNsSmall>(a, members, s);
 }
 

@@ -35,7 +35,7 @@ struct SumsqArgs {
   MatArg g;
   float* partial;
   int64_t partial_stride;
-  int64_t chunk;
+  int64_t chunk;       // rows per block
 };
 
 struct NsInitArgs {
@@ -157,6 +157,7 @@ struct NsApplyArgs {
 };
 hipError_t launch_ns_gram(const NsGramArgs& a, int members, hipStream_t s);
 hipError_t launch_ns_poly(const NsPolyArgs& a, int members, hipStream_t s);
+hipError_t launch_ns_linear(const NsPolyArgs& a, int members, hipStream_t s);  // c == 0
 hipError_t launch_ns_apply(const NsApplyArgs& a, bool out_bf16, int members, hipStream_t s);
 
 }  // namespace ortho

@@ -95,12 +95,13 @@ bool plan_ns(int64_t m, int64_t n, int32_t batch, NsPlan* p) {
   s.M = s.transposed ? n : m;
   s.N = s.transposed ? m : n;
   s.chunk = batch < kMaxMembersPerLaunch ? batch : kMaxMembersPerLaunch;
-  const int64_t total = m * n;
-  int64_t parts = cdiv(total, 16384);
+  // sum-of-squares blocks: whole rows, about 16K elements each, at most 2048
+  int64_t parts = cdiv(m * n, 16384);
   if (parts > 2048) parts = 2048;
+  if (parts > m) parts = m;
   if (parts < 1) parts = 1;
-  s.part_chunk = cdiv(total, parts);
-  s.nparts = static_cast<int>(cdiv(total, s.part_chunk));
+  s.part_chunk = cdiv(m, parts);
+  s.nparts = static_cast<int>(cdiv(m, s.part_chunk));
   s.ld_x = cdiv(s.N, 8) * 8;
   s.ld_xt = cdiv(s.M, 8) * 8;
   const size_t mn = static_cast<size_t>(s.M) * s.ld_x, nm = static_cast<size_t>(s.N) * s.ld_xt;

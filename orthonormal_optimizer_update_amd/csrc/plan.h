@@ -37,7 +37,7 @@ struct NsPlan {
   int64_t ld_x, ld_xt;       // leading dims of the M x N and N x M / M x M buffers (rounded to 8)
   int chunk;
   int nparts;
-  int64_t part_chunk;        // elements per sum-of-squares block
+  int64_t part_chunk;        // rows per sum-of-squares block
   size_t off_x32, off_xb0, off_xb1, off_xbt0, off_xbt1, off_a, off_bp, off_bp32, off_partial,
       off_scale;
   size_t member_bytes;
