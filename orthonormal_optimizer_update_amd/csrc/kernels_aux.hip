@@ -40,6 +40,47 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(RedArgs a) {
   }
 }
 
+// The same reduction with four consecutive columns per thread (16-byte loads
+// and stores) for column counts and strides that allow it.  A block covers 64
+// columns x 64 rows: 16 column quads x 16 row groups of 4 rows each; splits
+// are summed in slice order as above.  grid (ceil(cols/64), ceil(rows/64),
+// members).
+__global__ __launch_bounds__(256) void reduce_splits_vec_kernel(RedArgs a) {
+  __shared__ float red[16][65];
+  const int bi = blockIdx.z;
+  const float* part = a.part + bi * a.part_member_stride;
+  float* out = static_cast<float*>(const_cast<void*>(a.out.p[bi]));
+  const int cq = threadIdx.x & 15, rg = threadIdx.x >> 4;
+  const int c = blockIdx.x * 64 + cq * 4;
+  const int rbase = blockIdx.y * 64;
+  floatx4 sq = {0.f, 0.f, 0.f, 0.f};
+  if (c < a.cols) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = rbase + rg + 16 * j;
+      if (r >= a.rows) break;
+      const float* src = part + (int64_t)r * a.cols + c;
+      floatx4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int k = 0; k < a.splits; ++k) s += *reinterpret_cast<const floatx4*>(src + k * a.slice);
+      *reinterpret_cast<floatx4*>(out + (int64_t)r * a.out.ld + c) = s;
+      sq += s * s;
+    }
+  }
+  if (a.colsq) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) red[rg][cq * 4 + t] = sq[t];
+    __syncthreads();
+    const int cc = blockIdx.x * 64 + threadIdx.x;
+    if (threadIdx.x < 64 && cc < a.cols) {
+      float tot = 0.f;
+#pragma unroll
+      for (int g = 0; g < 16; ++g) tot += red[g][threadIdx.x];
+      a.colsq[bi * a.colsq_member_stride + (int64_t)blockIdx.y * a.cols + cc] = tot;
+    }
+  }
+}
+
 // Column normalisation Q'[:, j] = R[:, j] / |R[:, j]|, from the per-row-block
 // column sums of squares (summed in block order).  A zero column gives a zero
 // column and sets ORTHO_DEV_ZERO_COLUMN.
@@ -345,9 +386,12 @@ __device__ __forceinline__ double rsqrt_f64(double x) {
 //   wave 0 factors the panel in registers (lane i holds row i; pivots and
 //   column entries move by readlane) and finishes the matching 8-row block of
 //   the inverse (lane c holds column c of Y, forward substitution with L_pp);
-//   then every thread applies the two rank-8 updates with that panel:
-//   L[i][c] -= L[i][p] L[c][p]^T (trailing block) and Y[i][c] -= L[i][p] X[p][c]
-//   (rows below the panel), with Y starting as the identity.
+//   then the four waves apply the two rank-8 updates with that panel as 16 x 16
+//   fp64 MFMA tiles: L[i][c] -= L[i][p] L[c][p]^T (trailing block) and
+//   Y[i][c] -= L[i][p] X[p][c] (rows below the panel), with Y starting as the
+//   identity.  A tile column c takes its right operand from L (c at or beyond
+//   the panel's end) or from the finished inverse rows (c before it); the two
+//   regions written are disjoint from the panel columns and rows read.
 __global__ __launch_bounds__(256) void chol_diag_kernel(CholArgs a, int kb) {
   __shared__ double L[64][65];
   __shared__ double Y[64][65];
@@ -414,26 +458,41 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(CholArgs a, int kb) {
     }
     __syncthreads();
     const int pe = j0 + 8;
+    if (pe < nb) {
+      // lower 16 x 16 tiles (tr, tc), tc <= tr, with rows reaching past the panel
+      const int tr0 = pe >> 4;
+      const int ntr = 4 - tr0;
+      const int npairs = ntr * tr0 + ntr * (ntr + 1) / 2;
+      for (int q = wave; q < npairs; q += 4) {
+        int tr, tc;
+        if (q < ntr * tr0) {
+          tr = tr0 + q / tr0;
+          tc = q % tr0;
+        } else {
+          int u = q - ntr * tr0, t = 0;
+          while (u > t) { u -= t + 1; ++t; }
+          tr = tr0 + t;
+          tc = tr0 + u;
+        }
+        doublex4 acc = {0.0, 0.0, 0.0, 0.0};
+        const int arow = tr * 16 + (lane & 15);
+        const int bcol = tc * 16 + (lane & 15);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int gi = ti + i;
-      if (gi >= nb || gi < pe) continue;
-      double li[8];
+        for (int ks = 0; ks < 2; ++ks) {
+          const int k = j0 + ks * 4 + (lane >> 4);
+          const double av = L[arow][k];
+          const double bv = bcol >= pe ? L[bcol][k] : Y[k][bcol];
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
+        }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) li[u] = L[gi][j0 + u];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int gc = tj + c;
-        if (gc >= pe && gc <= gi) {
-          double acc = 0.0;
-#pragma unroll
-          for (int u = 0; u < 8; ++u) acc += li[u] * L[gc][j0 + u];
-          L[gi][gc] -= acc;
-        } else if (gc < pe) {
-          double acc = 0.0;
-#pragma unroll
-          for (int u = 0; u < 8; ++u) acc += li[u] * Y[j0 + u][gc];
-          Y[gi][gc] -= acc;
+        for (int e = 0; e < 4; ++e) {
+          const int gi = tr * 16 + (lane >> 4) + 4 * e;
+          if (gi < pe || gi >= nb) continue;
+          if (bcol >= pe) {
+            if (bcol <= gi) L[gi][bcol] -= acc[e];
+          } else {
+            Y[gi][bcol] -= acc[e];
+          }
         }
       }
     }
@@ -617,7 +676,10 @@ static inline int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 
 
 hipError_t launch_reduce_splits(const RedArgs& a, int members, hipStream_t s) {
   dim3 grid(cdiv(a.cols, 64), cdiv(a.rows, 64), members);
-  hipLaunchKernelGGL(reduce_splits_kernel, grid, dim3(256), 0, s, a);
+  const bool vec = a.cols % 4 == 0 && a.slice % 4 == 0 && a.part_member_stride % 4 == 0 &&
+                   a.out.vec && (reinterpret_cast<uintptr_t>(a.part) & 15) == 0;
+  if (vec) hipLaunchKernelGGL(reduce_splits_vec_kernel, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(reduce_splits_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
