@@ -10,6 +10,43 @@
 
 namespace ortho {
 
+// Tile-aligned interface used by the 256 x 256 kernel (every tile is full):
+//   kFastPre      0: accumulators start at zero; 1: at fast_pre_scale() times a
+//                 bf16 M x N matrix; 2: the same for an fp32 matrix
+//                 (fast_pre_src(), fast_pre_ld()).  The kernel stages that
+//                 matrix through LDS with coalesced copies.
+//   fast_store4   receives four consecutive columns of one row of the result.
+//   kFastT / fast_store_t4  receive four consecutive rows of one column
+//                 (transposed outputs), straight from the accumulators.
+
+__device__ __forceinline__ uint2 pack_bf16x4(floatx4 v) {
+  return make_uint2(to_bf16_bits(v[0]) | (uint32_t(to_bf16_bits(v[1])) << 16),
+                    to_bf16_bits(v[2]) | (uint32_t(to_bf16_bits(v[3])) << 16));
+}
+
+// Four consecutive values at p[idx..idx+3]; one vector store when vec.
+template <class T>
+__device__ __forceinline__ void store4_from_f32(T* p, int64_t idx, floatx4 v, bool vec);
+template <>
+__device__ __forceinline__ void store4_from_f32<float>(float* p, int64_t idx, floatx4 v, bool vec) {
+  if (vec) {
+    *reinterpret_cast<floatx4*>(p + idx) = v;
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) p[idx + t] = v[t];
+  }
+}
+template <>
+__device__ __forceinline__ void store4_from_f32<uint16_t>(uint16_t* p, int64_t idx, floatx4 v,
+                                                          bool vec) {
+  if (vec) {
+    *reinterpret_cast<uint2*>(p + idx) = pack_bf16x4(v);
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) p[idx + t] = to_bf16_bits(v[t]);
+  }
+}
+
 // fp32 store of C (optionally also C^T), or of one split-K slice of C.
 struct EpiStoreF32 {
   static constexpr bool kPreload = false;
@@ -61,6 +98,15 @@ struct EpiNSGram {
   int64_t ld;
   __device__ EpiNSGram(const Args& g, int bi, int)
       : a(static_cast<uint16_t*>(const_cast<void*>(g.a.p[bi]))), ld(g.a.ld) {}
+  static constexpr int kFastPre = 0;
+  static constexpr bool kFastT = false;
+  __device__ const void* fast_pre_src() const { return nullptr; }
+  __device__ int64_t fast_pre_ld() const { return 0; }
+  __device__ float fast_pre_scale() const { return 0.f; }
+  __device__ __forceinline__ void fast_store4(int row, int col, floatx4 v) {
+    *reinterpret_cast<uint2*>(a + (int64_t)row * ld + col) = pack_bf16x4(v);
+  }
+  __device__ __forceinline__ void fast_store_t4(int, int, floatx4) {}
   __device__ __forceinline__ void apply(int row0, int col, int M, int N, float v0, float v1,
                                         float v2, float v3) {
     if (col >= N) return;
@@ -93,6 +139,17 @@ struct EpiNSPoly {
         bp(static_cast<uint16_t*>(const_cast<void*>(g.bp.p[bi]))),
         bp32(g.has32 ? static_cast<float*>(const_cast<void*>(g.bp32.p[bi])) : nullptr),
         lda(g.a.ld), ldb(g.bp.ld), ldb32(g.bp32.ld), boc(g.b / g.c), c(g.c) {}
+  static constexpr int kFastPre = 1;
+  static constexpr bool kFastT = false;
+  __device__ const void* fast_pre_src() const { return a; }
+  __device__ int64_t fast_pre_ld() const { return lda; }
+  __device__ float fast_pre_scale() const { return boc; }
+  __device__ __forceinline__ void fast_store4(int row, int col, floatx4 v) {
+    const floatx4 y = c * v;
+    *reinterpret_cast<uint2*>(bp + (int64_t)row * ldb + col) = pack_bf16x4(y);
+    if (bp32) *reinterpret_cast<floatx4*>(bp32 + (int64_t)row * ldb32 + col) = y;
+  }
+  __device__ __forceinline__ void fast_store_t4(int, int, floatx4) {}
   __device__ __forceinline__ void init(int row0, int col, int M, int N, float* v) const {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -136,14 +193,35 @@ struct EpiNSApply {
   OUT_T* out;
   int64_t ldx, ldb, ldbt, ldo;
   float a;
-  bool last, out_t;
+  bool last, out_t, out_vec;
   __device__ EpiNSApply(const Args& g, int bi, int)
       : x32(static_cast<float*>(const_cast<void*>(g.x32.p[bi]))),
         xb(static_cast<uint16_t*>(const_cast<void*>(g.xb.p[bi]))),
         xbt(static_cast<uint16_t*>(const_cast<void*>(g.xbt.p[bi]))),
         out(static_cast<OUT_T*>(const_cast<void*>(g.out.p[bi]))),
         ldx(g.x32.ld), ldb(g.xb.ld), ldbt(g.xbt.ld), ldo(g.out.ld), a(g.a), last(g.last),
-        out_t(g.out_transposed) {}
+        out_t(g.out_transposed), out_vec(g.out.vec) {}
+  static constexpr int kFastPre = 2;
+  static constexpr bool kFastT = true;
+  __device__ const void* fast_pre_src() const { return x32; }
+  __device__ int64_t fast_pre_ld() const { return ldx; }
+  __device__ float fast_pre_scale() const { return a; }
+  __device__ __forceinline__ void fast_store4(int row, int col, floatx4 v) {
+    if (last) {
+      if (!out_t) store4_from_f32<OUT_T>(out, (int64_t)row * ldo + col, v, out_vec);
+      return;
+    }
+    *reinterpret_cast<floatx4*>(x32 + (int64_t)row * ldx + col) = v;
+    *reinterpret_cast<uint2*>(xb + (int64_t)row * ldb + col) = pack_bf16x4(v);
+  }
+  // rows row0..row0+3 of column col: consecutive elements of one row of X^T
+  __device__ __forceinline__ void fast_store_t4(int col, int row0, floatx4 v) {
+    if (last) {
+      if (out_t) store4_from_f32<OUT_T>(out, (int64_t)col * ldo + row0, v, out_vec);
+      return;
+    }
+    *reinterpret_cast<uint2*>(xbt + (int64_t)col * ldbt + row0) = pack_bf16x4(v);
+  }
   __device__ __forceinline__ void init(int row0, int col, int M, int N, float* v) const {
 #pragma unroll
     for (int t = 0; t < 4; ++t)

@@ -89,22 +89,61 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256(GemmParams<typename Epi:
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   Epi epi(p.e, bi, 0);
-  if constexpr (Epi::kPreload) {
-    // one accumulator row (64 values per lane) at a time keeps the loads in
-    // flight without running out of registers next to the accumulators
+  if constexpr (Epi::kFastPre != 0) {
+    // Accumulators start at scale * S for a matrix S of the output's shape:
+    // S's tile is copied row-major into LDS (1 KB per wave instruction, 128 KB
+    // per pass), then each wave reads its own elements in accumulator order.
+    // bf16: one pass of all 256 rows.  fp32: two passes; pass p holds, for
+    // both row halves h of the tile, rows h * 128 + p * 64 .. + 63 (LDS row
+    // h * 64 + r), i.e. accumulator rows i = 2p, 2p + 1 of every wave.
+    constexpr bool kBf = Epi::kFastPre == 1;
+    constexpr int kEsz = kBf ? 2 : 4;
+    constexpr int kRowsPerPass = kBf ? 256 : 128;
+    constexpr int kRowsPerInstr = kBf ? 2 : 1;
+    constexpr int kInstrPerWave = kRowsPerPass / kRowsPerInstr / 4;
+    const char* src = static_cast<const char*>(epi.fast_pre_src());
+    const int64_t ldp = epi.fast_pre_ld();
+    const float sc = epi.fast_pre_scale();
+    const int lrow = kBf ? (lane >> 5) : 0;
+    const int lcol = kBf ? (lane & 31) * 8 : lane * 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int pass = 0; pass < 256 / kRowsPerPass; ++pass) {
+#pragma unroll 8
+      for (int q = 0; q < kInstrPerWave; ++q) {
+        const int ins = wave * kInstrPerWave + q;
+        const int rl = ins * kRowsPerInstr + lrow;  // LDS row
+        const int row = m0 + (kBf ? rl : (rl >> 6) * 128 + pass * 64 + (rl & 63));
+        const char* g = src + ((int64_t)row * ldp + n0 + lcol) * kEsz;
+        __builtin_amdgcn_global_load_lds((glb_ptr_t)(g), (lds_ptr_t)(smem_fast + ins * 1024), 16, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+        for (int i = 0; i < 4; ++i) {
+          if (!kBf && (i >> 1) != pass) continue;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float u[4];
-          epi.init(m0 + wm * 128 + i * 32 + g * 8 + (lane >> 5) * 4,
-                   n0 + wn * 128 + j * 32 + (lane & 31), p.M, p.N, u);
+          for (int j = 0; j < 4; ++j) {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) acc[i][j][g * 4 + t] = u[t];
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                const int rw = i * 32 + g * 8 + (lane >> 5) * 4 + t;  // row within the wave's 128
+                const int rl = kBf ? wm * 128 + rw : wm * 64 + (rw & 63);
+                const int cl = wn * 128 + j * 32 + (lane & 31);
+                float v;
+                if constexpr (kBf)
+                  v = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(smem_fast)[rl * 256 + cl]);
+                else
+                  v = reinterpret_cast<const float*>(smem_fast)[rl * 256 + cl];
+                acc[i][j][g * 4 + t] = sc * v;
+              }
+            // one accumulator tile at a time keeps the values' live ranges short
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
-      __builtin_amdgcn_sched_barrier(0);
+      }
+      __syncthreads();
     }
   }
 
@@ -127,8 +166,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256(GemmParams<typename Epi:
 #pragma unroll
     for (int j = 0; j < 4; ++j) b[j] = read_frag(tb, wn * 128 + j * 32 + frow, kk * 2 + fchunk);
   };
-  read_frags(fa[0], fb[0], sa(0), sb(0), 0);
-  for (int kt = 0; kt < nk; ++kt) {
+  // One 64-wide k tile: loads of the next tile into the other stage, four
+  // 16-wide steps of products on this one, barrier, first fragments of the
+  // next tile.
+  auto k_tile = [&](int kt) {
     const int cur = kt & 1;
     const bool more = kt + 1 < nk;
     if (more) {
@@ -161,19 +202,57 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256(GemmParams<typename Epi:
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (more) read_frags(fa[0], fb[0], sa(cur ^ 1), sb(cur ^ 1), 0);
-  }
+  };
+  read_frags(fa[0], fb[0], sa(0), sb(0), 0);
+  // The first tile is peeled (K >= 64 is checked by the launcher): the
+  // accumulators' initial values then feed products directly instead of also
+  // reaching the epilogue through a zero-trip path.
+  k_tile(0);
+  for (int kt = 1; kt < nk; ++kt) k_tile(kt);
 
+  // Transposed outputs straight from the accumulators (four consecutive rows
+  // of one column per lane).
+  if constexpr (Epi::kFastT) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int row0 = m0 + wm * 128 + i * 32 + g * 8 + (lane >> 5) * 4;
-        const int col = n0 + wn * 128 + j * 32 + (lane & 31);
-        epi.apply(row0, col, p.M, p.N, acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1],
-                  acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]);
-      }
+        for (int g = 0; g < 4; ++g) {
+          const int row0 = m0 + wm * 128 + i * 32 + g * 8 + (lane >> 5) * 4;
+          const int col = n0 + wn * 128 + j * 32 + (lane & 31);
+          const floatx4 v = {acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
+                             acc[i][j][g * 4 + 3]};
+          epi.fast_store_t4(col, row0, v);
+        }
+  }
+  // Row-major outputs through LDS in two passes; pass p stages accumulator
+  // rows i = 2p, 2p + 1 of every wave (tile rows h * 128 + p * 64 .. + 63 of
+  // both row halves h, at LDS row h * 64 + r), then each wave hands one
+  // 256-wide row at a time to the policy, four columns per lane.  The main
+  // loop's last barrier has released the LDS.
+  float* stage = reinterpret_cast<float*>(smem_fast);
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int i = 2 * pass; i < 2 * pass + 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            stage[(wm * 64 + (i & 1) * 32 + g * 8 + (lane >> 5) * 4 + t) * 256 + wn * 128 + j * 32 +
+                  (lane & 31)] = acc[i][j][g * 4 + t];
+    __syncthreads();
+#pragma unroll 4
+    for (int q = 0; q < 32; ++q) {
+      const int rl = q * 4 + wave;
+      const floatx4 v = *reinterpret_cast<const floatx4*>(stage + rl * 256 + lane * 4);
+      epi.fast_store4(m0 + (rl >> 6) * 128 + pass * 64 + (rl & 63), n0 + lane * 4, v);
+    }
+    __syncthreads();
+  }
 }
 
 }  // namespace ortho
