@@ -374,10 +374,10 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
 
 // 1/sqrt(x) for x > 0: hardware estimate refined by two Newton steps.
 __device__ __forceinline__ double rsqrt_f64(double x) {
-  double y = __builtin_amdgcn_rsq(x);
-  y = y * (1.5 - 0.5 * x * y * y);
-  y = y * (1.5 - 0.5 * x * y * y);
-  return y;
+  // hardware estimate, then one Newton step (relative error about the square
+  // of the estimate's, far below what the Gram's conditioning can use)
+  const double y = __builtin_amdgcn_rsq(x);
+  return y * (1.5 - 0.5 * x * y * y);
 }
 
 // Factor the nb x nb diagonal block kb of S (S_kk = L_kk L_kk^T) and invert
@@ -402,15 +402,24 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(CholArgs a, int kb) {
   const int o = kb * 64;
   const int nb = min(64, r - o);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ti = (threadIdx.x >> 4) * 4, tj = (threadIdx.x & 15) * 4;
+  // element (gi, gj) = (q * 4 + wave, lane): each wave moves whole 64-wide
+  // rows (coalesced, and bank-conflict free with the 65-double pitch)
+  // Every load is issued before any is used (clamped addresses; the triangle
+  // is cut with a bit mask, so no load is predicated and stale words in the
+  // upper triangle, NaN patterns included, never reach the arithmetic).
+  uint64_t v[16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int q = 0; q < 16; ++q) {
+    const int gi = q * 4 + wave, gj = lane;
+    v[q] = reinterpret_cast<const uint64_t*>(S)[(int64_t)(o + min(gi, nb - 1)) * r + o + min(gj, nb - 1)];
+  }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int gi = ti + i, gj = tj + j;
-      L[gi][gj] = (gi < nb && gj <= gi) ? S[(int64_t)(o + gi) * r + o + gj] : 0.0;
-      Y[gi][gj] = (gi == gj && gi < nb) ? 1.0 : 0.0;
-    }
+  for (int q = 0; q < 16; ++q) {
+    const int gi = q * 4 + wave, gj = lane;
+    const uint64_t keep = (gi < nb && gj <= gi) ? ~0ull : 0ull;
+    L[gi][gj] = __longlong_as_double(static_cast<long long>(v[q] & keep));
+    Y[gi][gj] = (gi == gj && gi < nb) ? 1.0 : 0.0;
+  }
   bool shifted = false;
   for (int j0 = 0; j0 < nb; j0 += 8) {
     __syncthreads();
@@ -463,7 +472,12 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(CholArgs a, int kb) {
       const int tr0 = pe >> 4;
       const int ntr = 4 - tr0;
       const int npairs = ntr * tr0 + ntr * (ntr + 1) / 2;
-      for (int q = wave; q < npairs; q += 4) {
+      // at most 10 tiles, so at most three per wave: unrolled, so that the
+      // three product chains overlap
+#pragma unroll
+      for (int qq = 0; qq < 3; ++qq) {
+        const int q = wave + 4 * qq;
+        if (q >= npairs) break;
         int tr, tc;
         if (q < ntr * tr0) {
           tr = tr0 + q / tr0;
@@ -484,15 +498,23 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(CholArgs a, int kb) {
           const double bv = bcol >= pe ? L[bcol][k] : Y[k][bcol];
           acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
         }
+        // Branch-free read-modify-write: every lane reads its four targets,
+        // then writes them back, changed where the update applies.  Elements
+        // left unchanged are owned by no other tile, so the write-back of
+        // their own value races with nothing.
+        double* dst[4];
+        double old[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int gi = tr * 16 + (lane >> 4) + 4 * e;
-          if (gi < pe || gi >= nb) continue;
-          if (bcol >= pe) {
-            if (bcol <= gi) L[gi][bcol] -= acc[e];
-          } else {
-            Y[gi][bcol] -= acc[e];
-          }
+          dst[e] = bcol >= pe ? &L[gi][bcol] : &Y[gi][bcol];
+          old[e] = *dst[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int gi = tr * 16 + (lane >> 4) + 4 * e;
+          const bool upd = gi >= pe && gi < nb && (bcol < pe || bcol <= gi);
+          *dst[e] = upd ? old[e] - acc[e] : old[e];
         }
       }
     }
@@ -500,15 +522,13 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(CholArgs a, int kb) {
   __syncthreads();
   if (shifted && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int gi = ti + i, gj = tj + j;
-      if (gi < nb && gj <= gi) {
-        S[(int64_t)(o + gi) * r + o + gj] = L[gi][gj];
-        X[(int64_t)(o + gi) * r + o + gj] = Y[gi][gj];
-      }
+  for (int q = 0; q < 16; ++q) {
+    const int gi = q * 4 + wave, gj = lane;
+    if (gi < nb && gj <= gi) {
+      S[(int64_t)(o + gi) * r + o + gj] = L[gi][gj];
+      X[(int64_t)(o + gi) * r + o + gj] = Y[gi][gj];
     }
+  }
 }
 
 // acc (64 x 64 tile, four waves of 32 x 32) = A * B^T (TRANS_B) or A * B with

@@ -21,7 +21,7 @@ from __future__ import annotations
 
 import numpy as np
 
-ROLE_X, ROLE_Q0, ROLE_PLANT, ROLE_NOISE = 0, 1, 2, 3
+ROLE_X, ROLE_Q0, ROLE_PLANT, ROLE_NOISE, ROLE_LAYOUT = 0, 1, 2, 3, 4
 
 WORKLOADS = {
     1: dict(name="single-256x256-f32", dtype="f32",
@@ -121,3 +121,14 @@ def small_case(seed: int, m: int, n: int, r: int, dtype: str, planted_rank: int 
     S = planted(wid, m, n, planted_rank, planted_ratio) if planted_rank else None
     G = gradient(wid, m, n, 1, dtype, planted_part=S)
     return X, G, Q0
+
+
+def block_layout(workload: int, m: int, n: int, r: int, blocks: int):
+    """Scattered block-diagonal layout for full-size structural cases: block i
+    owns rows perm_m[i*m/k : (i+1)*m/k] of an m x n matrix, columns
+    perm_n[i*n/k : (i+1)*n/k], and columns i*r/k .. (i+1)*r/k - 1 of an
+    n x r (or m x r) factor.  Returns (perm_m, perm_n) as int64 arrays."""
+    if m % blocks or n % blocks or r % blocks:
+        raise ValueError("block count must divide m, n and r")
+    rng = _rng(workload, ROLE_LAYOUT, 0, m * 1000003 + n * 1009 + r)
+    return rng.permutation(m).astype(np.int64), rng.permutation(n).astype(np.int64)
