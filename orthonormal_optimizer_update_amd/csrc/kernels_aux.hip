@@ -392,10 +392,8 @@ __device__ __forceinline__ double rsqrt_f64(double x) {
 //   identity.  A tile column c takes its right operand from L (c at or beyond
 //   the panel's end) or from the finished inverse rows (c before it); the two
 //   regions written are disjoint from the panel columns and rows read.
-__global__ __launch_bounds__(256) void chol_diag_kernel(CholArgs a, int kb) {
-  __shared__ double L[64][65];
-  __shared__ double Y[64][65];
-  const int member = blockIdx.x;
+__device__ void chol_diag_block(const CholArgs& a, int kb, int member, double (*L)[65],
+                                double (*Y)[65]) {
   double* S = a.s + member * a.mat_stride;
   double* X = a.x + member * a.mat_stride;
   const int r = a.r;
@@ -433,21 +431,29 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(CholArgs a, int kb) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const int jc = j0 + c;
-        if (jc < nb) {
-          double piv = readlane_f64(pc[c], jc);
-          if (!(piv > kPivMin) && piv == piv) {
-            piv = kPivMin;
-            shifted = true;
-          }
-          const double inv = rsqrt_f64(piv);
-          invd[c] = inv;
-          pc[c] = lane == jc ? piv * inv : (lane > jc ? pc[c] * inv : 0.0);
-#pragma unroll
-          for (int c2 = c + 1; c2 < 8; ++c2) {
-            const double lcj = readlane_f64(pc[c], j0 + c2);
-            if (lane > jc) pc[c2] -= pc[c] * lcj;
-          }
+        // Branch-free column step.  A padding column (jc >= nb, all zero)
+        // takes pivot 1 and changes nothing that is stored.
+        const bool live = jc < nb;
+        double piv = readlane_f64(pc[c], jc);
+        if (live && !(piv > kPivMin) && piv == piv) {
+          piv = kPivMin;
+          shifted = true;
         }
+        piv = live ? piv : 1.0;
+        const double inv = rsqrt_f64(piv);
+        invd[c] = inv;
+        // The rest of the panel is updated with the unscaled column and
+        // 1/pivot, l_i l_j = a_i a_j / piv, so the broadcasts need not wait
+        // for the scaling.  Every lane is updated: on rows at or above jc the
+        // touched entries lie above the diagonal and are zeroed when their own
+        // column is scaled.
+        const double d = inv * inv;
+#pragma unroll
+        for (int c2 = c + 1; c2 < 8; ++c2) {
+          const double acj = readlane_f64(pc[c], j0 + c2);
+          pc[c2] -= pc[c] * (acj * d);
+        }
+        pc[c] = lane == jc ? piv * inv : (lane > jc ? pc[c] * inv : 0.0);
       }
       // Block row j0/8 of the inverse: X_p = L_pp^{-1} Y_p, lane = column.
       double y[8];
@@ -529,6 +535,12 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(CholArgs a, int kb) {
       X[(int64_t)(o + gi) * r + o + gj] = Y[gi][gj];
     }
   }
+}
+
+__global__ __launch_bounds__(256) void chol_diag_kernel(CholArgs a, int kb) {
+  __shared__ double L[64][65];
+  __shared__ double Y[64][65];
+  chol_diag_block(a, kb, blockIdx.x, L, Y);
 }
 
 // acc (64 x 64 tile, four waves of 32 x 32) = A * B^T (TRANS_B) or A * B with
@@ -645,6 +657,14 @@ __global__ __launch_bounds__(256) void chol_update_kernel(CholArgs a, int kb) {
     const int ib = kb + 1 + ti, jb = kb + 1 + tj;
     tile_gemm64<true>(S, S, r, ib * 64, kb * 64, jb * 64, kb * 64, sA, sB, acc);
     tile_store64(S, r, ib * 64, jb * 64, acc, true, ib == jb);
+    if (t == 0) {
+      // Tile (kb+1, kb+1) has now received every update it will get: this
+      // workgroup factors it (the next diagonal block) while the others finish
+      // the trailing update.  The barrier orders its own stores before the
+      // reloads and releases the operand tiles' LDS for the factorisation.
+      __syncthreads();
+      chol_diag_block(a, kb + 1, member, sA, sB);
+    }
   } else {
     t -= ntri;
     const int ib = kb + 1 + t / (kb + 1), jb = t % (kb + 1);
@@ -763,8 +783,10 @@ hipError_t launch_cholesky_inverse(const CholArgs& a, float* tt, int64_t tt_stri
                                    hipStream_t s) {
   const int r = a.r, nblk = cdiv(r, 64);
   hipLaunchKernelGGL(chol_prep_kernel, dim3(cdiv(r, 16), cdiv(r, 16), members), dim3(256), 0, s, a);
+  // Block 0 is factored on its own; block kb + 1 is factored by the update
+  // launch of step kb (its workgroup 0), so each later step is two launches.
+  hipLaunchKernelGGL(chol_diag_kernel, dim3(members), dim3(256), 0, s, a, 0);
   for (int kb = 0; kb < nblk; ++kb) {
-    hipLaunchKernelGGL(chol_diag_kernel, dim3(members), dim3(256), 0, s, a, kb);
     const int T = nblk - kb - 1;
     const int npanel = T + kb;
     if (npanel > 0)
