@@ -30,6 +30,12 @@ sys.path.insert(0, ROOT)
 METRIC = "optimizer steps/sec & ms/step vs matrix size, rank frac 1/4,1/16; % HBM/MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+# HBM bytes per launch of the product kernel (mean over the Gram, polynomial
+# and apply launches on 4096 x 4096), from rocprofv3 FETCH_SIZE and WRITE_SIZE
+# passes over `bench.py --counter-sample`, each scaled by the same counter's
+# reading for a 256 MiB elementwise copy (fetch factor 2.0, write factor 1.0).
+# Set to None whenever the kernel changes, until the passes are taken again.
+TRAFFIC_BYTES_PER_LAUNCH = 2.709e8
 
 
 def parse():
@@ -39,6 +45,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--counter-sample", action="store_true",
+                   help="run 2 Newton-Schulz iterations and a 256 MiB device copy, print "
+                        "nothing else (for rocprofv3 --pmc passes)")
     return p.parse_args()
 
 
@@ -136,6 +145,18 @@ def main():
     torch.cuda.set_device(0)
     names, run_path, ns_steps, info, (m, n) = workload2(torch, api, synth)
 
+    if args.counter_sample:
+        # The product kernel's HBM traffic per launch, and a plain copy of
+        # known size (256 MiB read + 256 MiB written) that calibrates the
+        # FETCH_SIZE / WRITE_SIZE counters.
+        ns_steps(2)
+        src = torch.ones(64 * 1024 * 1024, device="cuda", dtype=torch.float32)
+        dst = torch.empty_like(src)
+        torch.mul(src, 2.0, out=dst)  # elementwise copy kernel: 256 MiB in, 256 MiB out
+        torch.cuda.synchronize()
+        print("counter sample done", flush=True)
+        return
+
     for i in range(args.warmup):
         for nm in names:
             run_path(nm, i)
@@ -177,7 +198,7 @@ def main():
     flops = 2.0 * m * m * n
     achieved = flops / (gemm_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": TRAFFIC_BYTES_PER_LAUNCH,
                 "kernel": "gemm_bf16_256 (Newton-Schulz products X X^T, b A + c A^2, a X + Bp X; "
                           "bf16 MFMA 32x32x16, 256x256 tiles, direct-to-LDS operand copies)",
                 "avg_launch_ms": gemm_ms, "flops_per_launch": flops}

@@ -15,6 +15,8 @@ namespace ortho {
 //                 bf16 M x N matrix; 2: the same for an fp32 matrix
 //                 (fast_pre_src(), fast_pre_ld()).  The kernel stages that
 //                 matrix through LDS with coalesced copies.
+//   kFastPre2     0, or 1: a second (bf16) matrix added the same way
+//                 (fast_pre2_src(), fast_pre2_ld(), fast_pre2_scale()).
 //   fast_store4   receives four consecutive columns of one row of the result.
 //   kFastT / fast_store_t4  receive four consecutive rows of one column
 //                 (transposed outputs), straight from the accumulators.
@@ -99,6 +101,7 @@ struct EpiNSGram {
   __device__ EpiNSGram(const Args& g, int bi, int)
       : a(static_cast<uint16_t*>(const_cast<void*>(g.a.p[bi]))), ld(g.a.ld) {}
   static constexpr int kFastPre = 0;
+  static constexpr int kFastPre2 = 0;
   static constexpr bool kFastT = false;
   __device__ const void* fast_pre_src() const { return nullptr; }
   __device__ int64_t fast_pre_ld() const { return 0; }
@@ -107,6 +110,9 @@ struct EpiNSGram {
     *reinterpret_cast<uint2*>(a + (int64_t)row * ld + col) = pack_bf16x4(v);
   }
   __device__ __forceinline__ void fast_store_t4(int, int, floatx4) {}
+  __device__ const void* fast_pre2_src() const { return nullptr; }
+  __device__ int64_t fast_pre2_ld() const { return 0; }
+  __device__ float fast_pre2_scale() const { return 0.f; }
   __device__ __forceinline__ void apply(int row0, int col, int M, int N, float v0, float v1,
                                         float v2, float v3) {
     if (col >= N) return;
@@ -140,6 +146,7 @@ struct EpiNSPoly {
         bp32(g.has32 ? static_cast<float*>(const_cast<void*>(g.bp32.p[bi])) : nullptr),
         lda(g.a.ld), ldb(g.bp.ld), ldb32(g.bp32.ld), boc(g.b / g.c), c(g.c) {}
   static constexpr int kFastPre = 1;
+  static constexpr int kFastPre2 = 0;
   static constexpr bool kFastT = false;
   __device__ const void* fast_pre_src() const { return a; }
   __device__ int64_t fast_pre_ld() const { return lda; }
@@ -150,6 +157,9 @@ struct EpiNSPoly {
     if (bp32) *reinterpret_cast<floatx4*>(bp32 + (int64_t)row * ldb32 + col) = y;
   }
   __device__ __forceinline__ void fast_store_t4(int, int, floatx4) {}
+  __device__ const void* fast_pre2_src() const { return nullptr; }
+  __device__ int64_t fast_pre2_ld() const { return 0; }
+  __device__ float fast_pre2_scale() const { return 0.f; }
   __device__ __forceinline__ void init(int row0, int col, int M, int N, float* v) const {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -202,6 +212,7 @@ struct EpiNSApply {
         ldx(g.x32.ld), ldb(g.xb.ld), ldbt(g.xbt.ld), ldo(g.out.ld), a(g.a), last(g.last),
         out_t(g.out_transposed), out_vec(g.out.vec) {}
   static constexpr int kFastPre = 2;
+  static constexpr int kFastPre2 = 0;
   static constexpr bool kFastT = true;
   __device__ const void* fast_pre_src() const { return x32; }
   __device__ int64_t fast_pre_ld() const { return ldx; }
@@ -214,6 +225,9 @@ struct EpiNSApply {
     *reinterpret_cast<floatx4*>(x32 + (int64_t)row * ldx + col) = v;
     *reinterpret_cast<uint2*>(xb + (int64_t)row * ldb + col) = pack_bf16x4(v);
   }
+  __device__ const void* fast_pre2_src() const { return nullptr; }
+  __device__ int64_t fast_pre2_ld() const { return 0; }
+  __device__ float fast_pre2_scale() const { return 0.f; }
   // rows row0..row0+3 of column col: consecutive elements of one row of X^T
   __device__ __forceinline__ void fast_store_t4(int col, int row0, floatx4 v) {
     if (last) {
@@ -353,4 +367,61 @@ struct EpiDionPre {
   }
 };
 
+// Dion update on the 256 x 256 kernel, bf16 weights, as two launches whose
+// products P (c1 R)^T and P (c2 Q')^T arrive pre-scaled (bf16 operands):
+//   momentum: accumulators start at -(M + G); M' = -acc = B - c1 P R^T;
+//   weight:   accumulators start at -X;       X' = -acc = X - c2 P Q'^T,
+//             rounded to bf16.
+struct EpiDionFastM {
+  static constexpr bool kPreload = false;
+  struct Args {
+    MatArg m;  // fp32 momentum (read and written)
+    MatArg g;  // bf16 gradient
+  };
+  float* m;
+  const uint16_t* g;
+  int64_t ldm, ldg;
+  __device__ EpiDionFastM(const Args& e, int bi, int)
+      : m(static_cast<float*>(const_cast<void*>(e.m.p[bi]))),
+        g(static_cast<const uint16_t*>(e.g.p[bi])), ldm(e.m.ld), ldg(e.g.ld) {}
+  static constexpr int kFastPre = 2;
+  static constexpr int kFastPre2 = 1;
+  static constexpr bool kFastT = false;
+  __device__ const void* fast_pre_src() const { return m; }
+  __device__ int64_t fast_pre_ld() const { return ldm; }
+  __device__ float fast_pre_scale() const { return -1.f; }
+  __device__ const void* fast_pre2_src() const { return g; }
+  __device__ int64_t fast_pre2_ld() const { return ldg; }
+  __device__ float fast_pre2_scale() const { return -1.f; }
+  __device__ __forceinline__ void fast_store4(int row, int col, floatx4 v) {
+    *reinterpret_cast<floatx4*>(m + (int64_t)row * ldm + col) = -v;
+  }
+  __device__ __forceinline__ void fast_store_t4(int, int, floatx4) {}
+};
+
+struct EpiDionFastX {
+  static constexpr bool kPreload = false;
+  struct Args {
+    MatArg x;  // bf16 weight (read and written)
+  };
+  uint16_t* x;
+  int64_t ldx;
+  __device__ EpiDionFastX(const Args& e, int bi, int)
+      : x(static_cast<uint16_t*>(const_cast<void*>(e.x.p[bi]))), ldx(e.x.ld) {}
+  static constexpr int kFastPre = 1;
+  static constexpr int kFastPre2 = 0;
+  static constexpr bool kFastT = false;
+  __device__ const void* fast_pre_src() const { return x; }
+  __device__ int64_t fast_pre_ld() const { return ldx; }
+  __device__ float fast_pre_scale() const { return -1.f; }
+  __device__ const void* fast_pre2_src() const { return nullptr; }
+  __device__ int64_t fast_pre2_ld() const { return 0; }
+  __device__ float fast_pre2_scale() const { return 0.f; }
+  __device__ __forceinline__ void fast_store4(int row, int col, floatx4 v) {
+    *reinterpret_cast<uint2*>(x + (int64_t)row * ldx + col) = pack_bf16x4(-v);
+  }
+  __device__ __forceinline__ void fast_store_t4(int, int, floatx4) {}
+};
+
 }  // namespace ortho
+

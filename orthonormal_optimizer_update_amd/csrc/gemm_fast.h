@@ -53,6 +53,68 @@ __device__ __forceinline__ bf16x8 read_frag(const char* lds_tile, int row, int c
 
 }  // namespace fast
 
+// Accumulators (+)= scale * S for a matrix S of the output's shape (bf16 or
+// fp32, leading dimension ld): S's tile is copied row-major into LDS (1 KB per
+// wave instruction, 128 KB per pass), then each wave reads its own elements in
+// accumulator order.  bf16: one pass of all 256 rows.  fp32: two passes; pass
+// p holds, for both row halves h of the tile, rows h * 128 + p * 64 .. + 63
+// (LDS row h * 64 + r), i.e. accumulator rows i = 2p, 2p + 1 of every wave.
+// Ends with a barrier, so the caller may reuse the LDS.
+template <bool kBf, bool kAcc>
+__device__ __forceinline__ void fast_preload(floatx16 (&acc)[4][4], const void* srcv, int64_t ldp,
+                                             float sc, int m0, int n0, char* smem, int wave,
+                                             int lane) {
+  using namespace fast;
+  constexpr int kEsz = kBf ? 2 : 4;
+  constexpr int kRowsPerPass = kBf ? 256 : 128;
+  constexpr int kRowsPerInstr = kBf ? 2 : 1;
+  constexpr int kInstrPerWave = kRowsPerPass / kRowsPerInstr / 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const char* src = static_cast<const char*>(srcv);
+  const int lrow = kBf ? (lane >> 5) : 0;
+  const int lcol = kBf ? (lane & 31) * 8 : lane * 4;
+#pragma unroll
+  for (int pass = 0; pass < 256 / kRowsPerPass; ++pass) {
+#pragma unroll 8
+    for (int q = 0; q < kInstrPerWave; ++q) {
+      const int ins = wave * kInstrPerWave + q;
+      const int rl = ins * kRowsPerInstr + lrow;  // LDS row
+      const int row = m0 + (kBf ? rl : (rl >> 6) * 128 + pass * 64 + (rl & 63));
+      const char* g = src + ((int64_t)row * ldp + n0 + lcol) * kEsz;
+      __builtin_amdgcn_global_load_lds((glb_ptr_t)(g), (lds_ptr_t)(smem + ins * 1024), 16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (!kBf && (i >> 1) != pass) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int rw = i * 32 + g * 8 + (lane >> 5) * 4 + t;  // row within the wave's 128
+            const int rl = kBf ? wm * 128 + rw : wm * 64 + (rw & 63);
+            const int cl = wn * 128 + j * 32 + (lane & 31);
+            float v;
+            if constexpr (kBf)
+              v = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(smem)[rl * 256 + cl]);
+            else
+              v = reinterpret_cast<const float*>(smem)[rl * 256 + cl];
+            if constexpr (kAcc)
+              acc[i][j][g * 4 + t] += sc * v;
+            else
+              acc[i][j][g * 4 + t] = sc * v;
+          }
+        // one accumulator tile at a time keeps the values' live ranges short
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <class Epi>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_256(GemmParams<typename Epi::Args> p) {
   using namespace fast;
@@ -89,63 +151,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256(GemmParams<typename Epi:
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   Epi epi(p.e, bi, 0);
-  if constexpr (Epi::kFastPre != 0) {
-    // Accumulators start at scale * S for a matrix S of the output's shape:
-    // S's tile is copied row-major into LDS (1 KB per wave instruction, 128 KB
-    // per pass), then each wave reads its own elements in accumulator order.
-    // bf16: one pass of all 256 rows.  fp32: two passes; pass p holds, for
-    // both row halves h of the tile, rows h * 128 + p * 64 .. + 63 (LDS row
-    // h * 64 + r), i.e. accumulator rows i = 2p, 2p + 1 of every wave.
-    constexpr bool kBf = Epi::kFastPre == 1;
-    constexpr int kEsz = kBf ? 2 : 4;
-    constexpr int kRowsPerPass = kBf ? 256 : 128;
-    constexpr int kRowsPerInstr = kBf ? 2 : 1;
-    constexpr int kInstrPerWave = kRowsPerPass / kRowsPerInstr / 4;
-    const char* src = static_cast<const char*>(epi.fast_pre_src());
-    const int64_t ldp = epi.fast_pre_ld();
-    const float sc = epi.fast_pre_scale();
-    const int lrow = kBf ? (lane >> 5) : 0;
-    const int lcol = kBf ? (lane & 31) * 8 : lane * 4;
-#pragma unroll
-    for (int pass = 0; pass < 256 / kRowsPerPass; ++pass) {
-#pragma unroll 8
-      for (int q = 0; q < kInstrPerWave; ++q) {
-        const int ins = wave * kInstrPerWave + q;
-        const int rl = ins * kRowsPerInstr + lrow;  // LDS row
-        const int row = m0 + (kBf ? rl : (rl >> 6) * 128 + pass * 64 + (rl & 63));
-        const char* g = src + ((int64_t)row * ldp + n0 + lcol) * kEsz;
-        __builtin_amdgcn_global_load_lds((glb_ptr_t)(g), (lds_ptr_t)(smem_fast + ins * 1024), 16, 0, 0);
-      }
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (!kBf && (i >> 1) != pass) continue;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-#pragma unroll
-              for (int t = 0; t < 4; ++t) {
-                const int rw = i * 32 + g * 8 + (lane >> 5) * 4 + t;  // row within the wave's 128
-                const int rl = kBf ? wm * 128 + rw : wm * 64 + (rw & 63);
-                const int cl = wn * 128 + j * 32 + (lane & 31);
-                float v;
-                if constexpr (kBf)
-                  v = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(smem_fast)[rl * 256 + cl]);
-                else
-                  v = reinterpret_cast<const float*>(smem_fast)[rl * 256 + cl];
-                acc[i][j][g * 4 + t] = sc * v;
-              }
-            // one accumulator tile at a time keeps the values' live ranges short
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
+  if constexpr (Epi::kFastPre != 0)
+    fast_preload<Epi::kFastPre == 1, false>(acc, epi.fast_pre_src(), epi.fast_pre_ld(),
+                                            epi.fast_pre_scale(), m0, n0, smem_fast, wave, lane);
+  if constexpr (Epi::kFastPre2 != 0)
+    fast_preload<true, true>(acc, epi.fast_pre2_src(), epi.fast_pre2_ld(), epi.fast_pre2_scale(),
+                             m0, n0, smem_fast, wave, lane);
 
   auto sa = [&](int st) { return smem_fast + st * 2 * TILE_BYTES; };
   auto sb = [&](int st) { return smem_fast + st * 2 * TILE_BYTES + TILE_BYTES; };

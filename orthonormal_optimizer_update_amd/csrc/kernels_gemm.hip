@@ -92,7 +92,39 @@ hipError_t dion_update_f32(const DionUpdateArgs& a, int members, hipStream_t s) 
   return run<CfgUpdF32, RowF32<128, 256, 2>, RowF32<128, 256, 2>, EpiDion<float>>(p, members, s);
 }
 
+bool fast_ok(int M, int N, int K, const MatArg& a, const MatArg& b);
+template <class Epi>
+hipError_t run_fast(GemmParams<typename Epi::Args>& p, int members, hipStream_t s);
+
+// Every member's rows start on 16-byte boundaries (direct-to-LDS copies).
+static bool rows16(const MatArg& t, int members, size_t esz) {
+  if ((static_cast<size_t>(t.ld) * esz) % 16 != 0) return false;
+  for (int i = 0; i < members; ++i)
+    if (reinterpret_cast<uintptr_t>(t.p[i]) % 16 != 0) return false;
+  return true;
+}
+
 hipError_t dion_update_bf16(const DionUpdateArgs& a, int members, hipStream_t s) {
+  // At small ranks the step is bound by its 14 mn bytes, which the fused
+  // 256 x 128 two-accumulator kernel streams as well; from r = 1024 on the
+  // products dominate and the 256 x 256 kernel is faster.
+  if (a.rank >= 1024 && fast_ok(a.M, a.N, a.rank, a.pb, a.rb) && a.qb.vec && a.qb.ld % 8 == 0 &&
+      rows16(a.m, members, 4) && rows16(a.g, members, 2) && rows16(a.x, members, 2)) {
+    // two launches of the 256 x 256 kernel: momentum, then weight
+    GemmParams<EpiDionFastM::Args> pm{};
+    pm.a = with_rows(a.pb, a.M);
+    pm.b0 = with_rows(a.rb, a.N);
+    pm.e.m = a.m; pm.e.g = a.g;
+    pm.M = a.M; pm.N = a.N; pm.K = a.rank;
+    hipError_t e = run_fast<EpiDionFastM>(pm, members, s);
+    if (e != hipSuccess) return e;
+    GemmParams<EpiDionFastX::Args> px{};
+    px.a = with_rows(a.pb, a.M);
+    px.b0 = with_rows(a.qb, a.N);
+    px.e.x = a.x;
+    px.M = a.M; px.N = a.N; px.K = a.rank;
+    return run_fast<EpiDionFastX>(px, members, s);
+  }
   GemmParams<EpiDionPre::Args> p{};
   p.a = with_rows(a.pb, a.M);
   p.b0 = with_rows(a.rb, a.N);
