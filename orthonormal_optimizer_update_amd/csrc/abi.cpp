@@ -86,6 +86,40 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     float* part_f = reinterpret_cast<float*>(base + pl.off_part);
     double* part_d = reinterpret_cast<double*>(base + pl.off_part);
 
+    // Sweeps on the 256 x 256 kernel over bf16x2 pieces (bf16 weights, sizes
+    // multiples of 256, 16-byte rows of M and Q; G rows 8-byte aligned).
+    const bool fast_sw = bf && pl.fast_sweeps && tM.vec && tQ.vec && tG.vec;
+    if (fast_sw) {
+      const MatArg tBhi = ws_table(base, mb, pl.off_bhi, nb, n, mi, ni, 2, 16);
+      const MatArg tBlo = ws_table(base, mb, pl.off_blo, nb, n, mi, ni, 2, 16);
+      const MatArg tBhiT = ws_table(base, mb, pl.off_bhit, nb, m, ni, mi, 2, 16);
+      const MatArg tBloT = ws_table(base, mb, pl.off_blot, nb, m, ni, mi, 2, 16);
+      const MatArg tQhiT = ws_table(base, mb, pl.off_qhit, nb, n, r, ni, 2, 16);
+      const MatArg tQloT = ws_table(base, mb, pl.off_qlot, nb, n, r, ni, 2, 16);
+      SplitSumArgs sa;
+      sa.m = tM; sa.g = tG; sa.hi = tBhi; sa.lo = tBlo; sa.hit = tBhiT; sa.lot = tBloT;
+      sa.rows = mi; sa.cols = ni;
+      ORTHO_TRY(launch_split_sum(sa, nb, s));
+      SplitTArgs qa;
+      qa.src = tQ; qa.hit = tQhiT; qa.lot = tQloT; qa.rows = ni; qa.cols = r;
+      ORTHO_TRY(launch_split_t(qa, nb, s));
+      // Sweep 1 over n: P_tilde = (Bhi, Blo) (Qhi, Qlo)^T
+      Split3Args l3;
+      l3.ahi = tBhi; l3.alo = tBlo; l3.bhi = tQhiT; l3.blo = tQloT;
+      l3.out = pl.split_fl > 1 ? tPart : tPt;
+      l3.split_stride = m * r;
+      l3.M = mi; l3.N = r; l3.K = ni;
+      l3.splits = pl.split_fl; l3.kchunk = pl.kchunk_fl;
+      ORTHO_TRY(launch_fast_split3(l3, nb, s));
+      if (pl.split_fl > 1) {
+        RedArgs ra;
+        ra.part = part_f; ra.part_member_stride = static_cast<int64_t>(mb / 4);
+        ra.slice = m * r; ra.splits = pl.split_fl; ra.rows = mi; ra.cols = r;
+        ra.out = tPt; ra.colsq = nullptr; ra.colsq_member_stride = 0;
+        ORTHO_TRY(launch_reduce_splits(ra, nb, s));
+      }
+    }
+
     // Sweep 1: P_tilde = (M + G) Q.
     DionLeftArgs la;
     la.m = tM; la.g = tG; la.q = tQ;
@@ -93,8 +127,8 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     la.split_stride = m * r;
     la.M = mi; la.N = ni; la.r = r;
     la.splits = pl.split_left; la.kchunk = pl.kchunk_left;
-    ORTHO_TRY(launch_dion_left(la, bf, nb, s));
-    if (pl.split_left > 1) {
+    if (!fast_sw) ORTHO_TRY(launch_dion_left(la, bf, nb, s));
+    if (!fast_sw && pl.split_left > 1) {
       RedArgs ra;
       ra.part = part_f; ra.part_member_stride = static_cast<int64_t>(mb / 4);
       ra.slice = m * r; ra.splits = pl.split_left; ra.rows = mi; ra.cols = r;
@@ -135,15 +169,34 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     ORTHO_TRY(launch_apply_t(aa, false, nb, s));
 
     // Sweep 2: R = (M + G)^T P, then Q' = column-normalised R.
-    DionRightArgs rb;
-    rb.m = tM; rb.g = tG; rb.p = tPt; rb.out = tPart;
-    rb.split_stride = n * r;
-    rb.M = mi; rb.N = ni; rb.r = r;
-    rb.splits = pl.split_right; rb.kchunk = pl.kchunk_right;
-    ORTHO_TRY(launch_dion_right(rb, bf, nb, s));
+    int split_r = pl.split_right;
+    if (fast_sw) {
+      // over m: R = (Bhi^T, Blo^T) (Phi^T, Plo^T)^T
+      const MatArg tBhiT = ws_table(base, mb, pl.off_bhit, nb, m, ni, mi, 2, 16);
+      const MatArg tBloT = ws_table(base, mb, pl.off_blot, nb, m, ni, mi, 2, 16);
+      const MatArg tPhiT = ws_table(base, mb, pl.off_phit, nb, m, r, mi, 2, 16);
+      const MatArg tPloT = ws_table(base, mb, pl.off_plot, nb, m, r, mi, 2, 16);
+      SplitTArgs pa;
+      pa.src = tPt; pa.hit = tPhiT; pa.lot = tPloT; pa.rows = mi; pa.cols = r;
+      ORTHO_TRY(launch_split_t(pa, nb, s));
+      Split3Args r3;
+      r3.ahi = tBhiT; r3.alo = tBloT; r3.bhi = tPhiT; r3.blo = tPloT;
+      r3.out = tPart; r3.split_stride = n * r;
+      r3.M = ni; r3.N = r; r3.K = mi;
+      r3.splits = pl.split_fr; r3.kchunk = pl.kchunk_fr;
+      ORTHO_TRY(launch_fast_split3(r3, nb, s));
+      split_r = pl.split_fr;
+    } else {
+      DionRightArgs rb;
+      rb.m = tM; rb.g = tG; rb.p = tPt; rb.out = tPart;
+      rb.split_stride = n * r;
+      rb.M = mi; rb.N = ni; rb.r = r;
+      rb.splits = pl.split_right; rb.kchunk = pl.kchunk_right;
+      ORTHO_TRY(launch_dion_right(rb, bf, nb, s));
+    }
     RedArgs rr;
     rr.part = part_f; rr.part_member_stride = static_cast<int64_t>(mb / 4);
-    rr.slice = n * r; rr.splits = pl.split_right; rr.rows = ni; rr.cols = r;
+    rr.slice = n * r; rr.splits = split_r; rr.rows = ni; rr.cols = r;
     rr.out = tR;
     rr.colsq = reinterpret_cast<float*>(base + pl.off_colsq);
     rr.colsq_member_stride = static_cast<int64_t>(mb / 4);

@@ -15,6 +15,8 @@ namespace ortho {
 //                 bf16 M x N matrix; 2: the same for an fp32 matrix
 //                 (fast_pre_src(), fast_pre_ld()).  The kernel stages that
 //                 matrix through LDS with coalesced copies.
+//   kSegs         1, or 3: the product is a*b0 + a*b0s + a2*b0 over bf16x2
+//                 pieces (hi*hi + hi*lo + lo*hi).
 //   kFastPre2     0, or 1: a second (bf16) matrix added the same way
 //                 (fast_pre2_src(), fast_pre2_ld(), fast_pre2_scale()).
 //   fast_store4   receives four consecutive columns of one row of the result.
@@ -101,6 +103,7 @@ struct EpiNSGram {
   __device__ EpiNSGram(const Args& g, int bi, int)
       : a(static_cast<uint16_t*>(const_cast<void*>(g.a.p[bi]))), ld(g.a.ld) {}
   static constexpr int kFastPre = 0;
+  static constexpr int kSegs = 1;
   static constexpr int kFastPre2 = 0;
   static constexpr bool kFastT = false;
   __device__ const void* fast_pre_src() const { return nullptr; }
@@ -146,6 +149,7 @@ struct EpiNSPoly {
         bp32(g.has32 ? static_cast<float*>(const_cast<void*>(g.bp32.p[bi])) : nullptr),
         lda(g.a.ld), ldb(g.bp.ld), ldb32(g.bp32.ld), boc(g.b / g.c), c(g.c) {}
   static constexpr int kFastPre = 1;
+  static constexpr int kSegs = 1;
   static constexpr int kFastPre2 = 0;
   static constexpr bool kFastT = false;
   __device__ const void* fast_pre_src() const { return a; }
@@ -212,6 +216,7 @@ struct EpiNSApply {
         ldx(g.x32.ld), ldb(g.xb.ld), ldbt(g.xbt.ld), ldo(g.out.ld), a(g.a), last(g.last),
         out_t(g.out_transposed), out_vec(g.out.vec) {}
   static constexpr int kFastPre = 2;
+  static constexpr int kSegs = 1;
   static constexpr int kFastPre2 = 0;
   static constexpr bool kFastT = true;
   __device__ const void* fast_pre_src() const { return x32; }
@@ -385,6 +390,7 @@ struct EpiDionFastM {
       : m(static_cast<float*>(const_cast<void*>(e.m.p[bi]))),
         g(static_cast<const uint16_t*>(e.g.p[bi])), ldm(e.m.ld), ldg(e.g.ld) {}
   static constexpr int kFastPre = 2;
+  static constexpr int kSegs = 1;
   static constexpr int kFastPre2 = 1;
   static constexpr bool kFastT = false;
   __device__ const void* fast_pre_src() const { return m; }
@@ -409,6 +415,7 @@ struct EpiDionFastX {
   __device__ EpiDionFastX(const Args& e, int bi, int)
       : x(static_cast<uint16_t*>(const_cast<void*>(e.x.p[bi]))), ldx(e.x.ld) {}
   static constexpr int kFastPre = 1;
+  static constexpr int kSegs = 1;
   static constexpr int kFastPre2 = 0;
   static constexpr bool kFastT = false;
   __device__ const void* fast_pre_src() const { return x; }
@@ -423,5 +430,35 @@ struct EpiDionFastX {
   __device__ __forceinline__ void fast_store_t4(int, int, floatx4) {}
 };
 
+// fp32 store of C, or of split-K slice `split` of C, from the 256 x 256 kernel
+// over bf16x2 pieces (three segments).
+struct EpiFastSplitF32 {
+  static constexpr bool kPreload = false;
+  struct Args {
+    MatArg c;              // destination, fp32 (ld a multiple of 4, 16-byte aligned)
+    int64_t split_stride;  // elements between split-K slices
+  };
+  float* c;
+  int64_t ld;
+  __device__ EpiFastSplitF32(const Args& a, int bi, int split)
+      : c(static_cast<float*>(const_cast<void*>(a.c.p[bi])) + split * a.split_stride),
+        ld(a.c.ld) {}
+  static constexpr int kFastPre = 0;
+  static constexpr int kSegs = 3;
+  static constexpr int kFastPre2 = 0;
+  static constexpr bool kFastT = false;
+  __device__ const void* fast_pre_src() const { return nullptr; }
+  __device__ int64_t fast_pre_ld() const { return 0; }
+  __device__ float fast_pre_scale() const { return 0.f; }
+  __device__ const void* fast_pre2_src() const { return nullptr; }
+  __device__ int64_t fast_pre2_ld() const { return 0; }
+  __device__ float fast_pre2_scale() const { return 0.f; }
+  __device__ __forceinline__ void fast_store4(int row, int col, floatx4 v) {
+    *reinterpret_cast<floatx4*>(c + (int64_t)row * ld + col) = v;
+  }
+  __device__ __forceinline__ void fast_store_t4(int, int, floatx4) {}
+};
+
 }  // namespace ortho
+
 

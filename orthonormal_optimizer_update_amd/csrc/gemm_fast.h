@@ -13,7 +13,7 @@
 // hit 64 distinct banks.
 //
 // Requirements (checked by the launcher): M, N multiples of 256, K a multiple
-// of 64, 16-byte aligned rows.
+// of 64, 16-byte aligned rows; every split-K slice holds at least one k tile.
 #pragma once
 
 #include "gemm_core.h"
@@ -134,13 +134,26 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256(GemmParams<typename Epi:
   const int gsize = min(tiles_m - first_m, 4);
   const int tm = first_m + (t % group) % gsize;
   const int tn = (t % group) / gsize;
-  const int bi = blockIdx.y;
+  // blockIdx.y = member * splits + split (split-K over the k tiles)
+  const int bi = blockIdx.y / p.splits, split = blockIdx.y % p.splits;
   const int m0 = tm * BM, n0 = tn * BN;
 
+  // With Epi::kSegs == 3 the reduction runs over three segments of length K,
+  // (a, b0), (a, b0s), (a2, b0): hi*hi + hi*lo + lo*hi of bf16x2 pieces.
   const uint16_t* A = static_cast<const uint16_t*>(p.a.p[bi]);
   const uint16_t* B = static_cast<const uint16_t*>(p.b0.p[bi]);
+  const uint16_t* A2 = Epi::kSegs == 3 ? static_cast<const uint16_t*>(p.a2.p[bi]) : A;
+  const uint16_t* B2 = Epi::kSegs == 3 ? static_cast<const uint16_t*>(p.b0s.p[bi]) : B;
   const int64_t lda = p.a.ld, ldb = p.b0.ld;
-  const int nk = p.K / BK;
+  const int nks = p.K / BK;                       // k tiles per segment
+  const int kt_begin = split * p.kchunk;          // this split's k tiles
+  const int kt_end = min(kt_begin + p.kchunk, nks * Epi::kSegs);
+  auto seg_a = [&](int kt) { return Epi::kSegs == 3 && kt >= 2 * nks ? A2 : A; };
+  auto seg_b = [&](int kt) { return Epi::kSegs == 3 && kt >= nks && kt < 2 * nks ? B2 : B; };
+  auto seg_k = [&](int kt) {  // k offset within the segment (no division)
+    if constexpr (Epi::kSegs == 3) kt -= kt >= 2 * nks ? 2 * nks : (kt >= nks ? nks : 0);
+    return kt * BK;
+  };
 
   floatx16 acc[4][4];
 #pragma unroll
@@ -150,7 +163,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256(GemmParams<typename Epi:
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  Epi epi(p.e, bi, 0);
+  Epi epi(p.e, bi, split);
   if constexpr (Epi::kFastPre != 0)
     fast_preload<Epi::kFastPre == 1, false>(acc, epi.fast_pre_src(), epi.fast_pre_ld(),
                                             epi.fast_pre_scale(), m0, n0, smem_fast, wave, lane);
@@ -161,8 +174,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256(GemmParams<typename Epi:
   auto sa = [&](int st) { return smem_fast + st * 2 * TILE_BYTES; };
   auto sb = [&](int st) { return smem_fast + st * 2 * TILE_BYTES + TILE_BYTES; };
 
-  load_tile(A, lda, m0, 0, sa(0), wave, lane);
-  load_tile(B, ldb, n0, 0, sb(0), wave, lane);
+  load_tile(seg_a(kt_begin), lda, m0, seg_k(kt_begin), sa(0), wave, lane);
+  load_tile(seg_b(kt_begin), ldb, n0, seg_k(kt_begin), sb(0), wave, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -181,11 +194,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256(GemmParams<typename Epi:
   // 16-wide steps of products on this one, barrier, first fragments of the
   // next tile.
   auto k_tile = [&](int kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
+    const int cur = (kt - kt_begin) & 1;
+    const bool more = kt + 1 < kt_end;
     if (more) {
-      load_tile(A, lda, m0, (kt + 1) * BK, sa(cur ^ 1), wave, lane);
-      load_tile(B, ldb, n0, (kt + 1) * BK, sb(cur ^ 1), wave, lane);
+      load_tile(seg_a(kt + 1), lda, m0, seg_k(kt + 1), sa(cur ^ 1), wave, lane);
+      load_tile(seg_b(kt + 1), ldb, n0, seg_k(kt + 1), sb(cur ^ 1), wave, lane);
     }
     const char* ta = sa(cur);
     const char* tb = sb(cur);
@@ -218,8 +231,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256(GemmParams<typename Epi:
   // The first tile is peeled (K >= 64 is checked by the launcher): the
   // accumulators' initial values then feed products directly instead of also
   // reaching the epilogue through a zero-trip path.
-  k_tile(0);
-  for (int kt = 1; kt < nk; ++kt) k_tile(kt);
+  k_tile(kt_begin);
+  for (int kt = kt_begin + 1; kt < kt_end; ++kt) k_tile(kt);
 
   // Transposed outputs straight from the accumulators (four consecutive rows
   // of one column per lane).

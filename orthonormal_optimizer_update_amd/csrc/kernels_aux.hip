@@ -81,20 +81,112 @@ __global__ __launch_bounds__(256) void reduce_splits_vec_kernel(RedArgs a) {
   }
 }
 
+// bf16x2 pieces of B = M + G (row-major and transposed) and of the transpose
+// of an fp32 matrix, for the 256 x 256 product kernel.  64 x 64 tiles of 256
+// threads; thread t handles columns 4 (t & 15) .. + 3 of rows (t >> 4) + 16 q;
+// the transposed pieces are staged in LDS and written 4 elements per lane.
+// grid (cols / 64, rows / 64, members).
+__device__ __forceinline__ uint2 pack4(const uint16_t (&h)[4]) {
+  return make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
+}
+
+template <bool kSum>
+__device__ __forceinline__ void split_tile(const float* src, int64_t lds_, const uint16_t* g,
+                                           int64_t ldg, uint16_t* hi, uint16_t* lo, int64_t ldo,
+                                           uint16_t* hit, uint16_t* lot, int64_t ldt, int r0,
+                                           int c0) {
+  __shared__ uint16_t th[64][68];
+  __shared__ uint16_t tl[64][68];
+  const int cl = (threadIdx.x & 15) * 4;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int rl = (threadIdx.x >> 4) + 16 * q;
+    const int64_t row = r0 + rl;
+    floatx4 v = *reinterpret_cast<const floatx4*>(src + row * lds_ + c0 + cl);
+    if constexpr (kSum) {
+      const uint2 gv = *reinterpret_cast<const uint2*>(g + row * ldg + c0 + cl);
+      v[0] += bf16_bits_to_f32(gv.x & 0xFFFF);
+      v[1] += bf16_bits_to_f32(gv.x >> 16);
+      v[2] += bf16_bits_to_f32(gv.y & 0xFFFF);
+      v[3] += bf16_bits_to_f32(gv.y >> 16);
+    }
+    uint16_t h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bf16 bh, bl;
+      split_bf16(v[e], bh, bl);
+      h[e] = __builtin_bit_cast(uint16_t, bh);
+      l[e] = __builtin_bit_cast(uint16_t, bl);
+      th[cl + e][rl] = h[e];
+      tl[cl + e][rl] = l[e];
+    }
+    if constexpr (kSum) {
+      *reinterpret_cast<uint2*>(hi + row * ldo + c0 + cl) = pack4(h);
+      *reinterpret_cast<uint2*>(lo + row * ldo + c0 + cl) = pack4(l);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int j = (threadIdx.x >> 4) + 16 * q;  // row of the transposed tile
+    const int i4 = (threadIdx.x & 15) * 4;
+    uint16_t h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h[e] = th[j][i4 + e];
+      l[e] = tl[j][i4 + e];
+    }
+    *reinterpret_cast<uint2*>(hit + (int64_t)(c0 + j) * ldt + r0 + i4) = pack4(h);
+    *reinterpret_cast<uint2*>(lot + (int64_t)(c0 + j) * ldt + r0 + i4) = pack4(l);
+  }
+}
+
+__global__ __launch_bounds__(256) void split_sum_kernel(SplitSumArgs a) {
+  const int bi = blockIdx.z;
+  split_tile<true>(static_cast<const float*>(a.m.p[bi]), a.m.ld,
+                   static_cast<const uint16_t*>(a.g.p[bi]), a.g.ld,
+                   static_cast<uint16_t*>(const_cast<void*>(a.hi.p[bi])),
+                   static_cast<uint16_t*>(const_cast<void*>(a.lo.p[bi])), a.hi.ld,
+                   static_cast<uint16_t*>(const_cast<void*>(a.hit.p[bi])),
+                   static_cast<uint16_t*>(const_cast<void*>(a.lot.p[bi])), a.hit.ld,
+                   blockIdx.y * 64, blockIdx.x * 64);
+}
+
+__global__ __launch_bounds__(256) void split_t_kernel(SplitTArgs a) {
+  const int bi = blockIdx.z;
+  split_tile<false>(static_cast<const float*>(a.src.p[bi]), a.src.ld, nullptr, 0, nullptr, nullptr,
+                    0, static_cast<uint16_t*>(const_cast<void*>(a.hit.p[bi])),
+                    static_cast<uint16_t*>(const_cast<void*>(a.lot.p[bi])), a.hit.ld,
+                    blockIdx.y * 64, blockIdx.x * 64);
+}
+
 // Column normalisation Q'[:, j] = R[:, j] / |R[:, j]|, from the per-row-block
 // column sums of squares (summed in block order).  A zero column gives a zero
 // column and sets ORTHO_DEV_ZERO_COLUMN.
 __global__ __launch_bounds__(256) void colnorm_kernel(ColnormArgs a) {
   __shared__ float inv[64];
+  __shared__ float part[4][64];
   const int bi = blockIdx.z;
   const int c0 = blockIdx.x * 64;
+  {
+    // four thread groups sum every fourth row block, then combine in a fixed
+    // order (the unrolled loads of a group are all in flight together)
+    const int g = threadIdx.x >> 6, cc = threadIdx.x & 63, c = c0 + cc;
+    float s = 0.f;
+    if (c < a.cols) {
+      const float* cs = a.colsq + bi * a.colsq_member_stride + c;
+#pragma unroll 8
+      for (int b = g; b < a.nrb; b += 4) s += cs[(int64_t)b * a.cols];
+    }
+    part[g][cc] = s;
+  }
+  __syncthreads();
   if (threadIdx.x < 64) {
     const int c = c0 + threadIdx.x;
     float v = 0.f;
     if (c < a.cols) {
-      const float* cs = a.colsq + bi * a.colsq_member_stride;
-      float s = 0.f;
-      for (int b = 0; b < a.nrb; ++b) s += cs[(int64_t)b * a.cols + c];
+      const float s = (part[0][threadIdx.x] + part[1][threadIdx.x]) +
+                      (part[2][threadIdx.x] + part[3][threadIdx.x]);
       if (s > 0.f) {
         v = 1.0f / sqrtf(s);
       } else if (!(s != s)) {
@@ -350,6 +442,7 @@ __global__ __launch_bounds__(256) void chol_prep_kernel(CholArgs a) {
   if (j > i) return;
   auto sum = [&](int u, int v) {
     double s = 0.0;
+#pragma unroll 8
     for (int k = 0; k < a.splits; ++k) s += part[k * a.slice + (int64_t)u * r + v];
     return s;
   };
@@ -703,6 +796,7 @@ __global__ __launch_bounds__(256) void correction_kernel(const float* part, int6
   if (k <= j) {
     const float* p = part + member * part_member_stride + (int64_t)j * r + k;
     double w = 0.0;
+#pragma unroll 8
     for (int s = 0; s < splits; ++s) w += p[s * slice];
     v = k == j ? static_cast<float>(1.0 - 0.5 * (w - 1.0)) : static_cast<float>(-w);
   }
@@ -720,6 +814,16 @@ hipError_t launch_reduce_splits(const RedArgs& a, int members, hipStream_t s) {
                    a.out.vec && (reinterpret_cast<uintptr_t>(a.part) & 15) == 0;
   if (vec) hipLaunchKernelGGL(reduce_splits_vec_kernel, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(reduce_splits_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_sum(const SplitSumArgs& a, int members, hipStream_t s) {
+  hipLaunchKernelGGL(split_sum_kernel, dim3(a.cols / 64, a.rows / 64, members), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_t(const SplitTArgs& a, int members, hipStream_t s) {
+  hipLaunchKernelGGL(split_t_kernel, dim3(a.cols / 64, a.rows / 64, members), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

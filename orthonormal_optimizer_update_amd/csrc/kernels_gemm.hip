@@ -149,8 +149,11 @@ bool fast_ok(int M, int N, int K, const MatArg& a, const MatArg& b) {
 template <class Epi>
 hipError_t run_fast(GemmParams<typename Epi::Args>& p, int members, hipStream_t s) {
   p.tiles_n = p.N / 256;
-  p.splits = 1;
-  dim3 grid((p.M / 256) * p.tiles_n, members);
+  if (p.splits < 1 || p.kchunk < 1) {  // one slice over every k tile
+    p.splits = 1;
+    p.kchunk = (p.K / 64) * Epi::kSegs;
+  }
+  dim3 grid((p.M / 256) * p.tiles_n, members * p.splits);
   hipLaunchKernelGGL((gemm_bf16_256<Epi>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
@@ -269,6 +272,19 @@ hipError_t launch_ns_apply(const NsApplyArgs& a, bool out_bf16, int members, hip
                     : ns_apply_t<CfgNsBig, float>(a, members, s);
   return out_bf16 ? ns_apply_t<CfgNsSmall, uint16_t>(a, members, s)
                   : ns_apply_t<CfgNsSmall, float>(a, members, s);
+}
+
+hipError_t launch_fast_split3(const Split3Args& a, int members, hipStream_t s) {
+  GemmParams<EpiFastSplitF32::Args> p{};
+  p.a = with_rows(a.ahi, a.M);
+  p.a2 = with_rows(a.alo, a.M);
+  p.b0 = with_rows(a.bhi, a.N);
+  p.b0s = with_rows(a.blo, a.N);
+  p.e.c = a.out;
+  p.e.split_stride = a.split_stride;
+  p.M = a.M; p.N = a.N; p.K = a.K;
+  p.splits = a.splits; p.kchunk = a.kchunk;
+  return run_fast<EpiFastSplitF32>(p, members, s);
 }
 
 }  // namespace ortho

@@ -68,6 +68,36 @@ struct CholArgs {
   int32_t* status;
 };
 
+// bf16x2 pieces (x = hi + lo + O(2^-16 |x|)) for the 256 x 256 product kernel.
+// B = M + G of an m x n fp32 M and bf16 G, written row-major (hi, lo: m x n)
+// and transposed (hit, lot: n x m).  rows, cols multiples of 64; M rows 16-byte
+// aligned, G and outputs 8-byte aligned.
+struct SplitSumArgs {
+  MatArg m, g;
+  MatArg hi, lo, hit, lot;
+  int rows, cols;
+};
+hipError_t launch_split_sum(const SplitSumArgs& a, int members, hipStream_t s);
+// Transposed pieces of an fp32 rows x cols matrix: hit, lot are cols x rows.
+struct SplitTArgs {
+  MatArg src;
+  MatArg hit, lot;
+  int rows, cols;
+};
+hipError_t launch_split_t(const SplitTArgs& a, int members, hipStream_t s);
+
+// C (+ split-K slices) = A B^T over bf16x2 pieces, hi*hi + hi*lo + lo*hi, on
+// the 256 x 256 kernel: A pieces M x K, B pieces N x K (k contiguous), C fp32
+// M x N.  M, N multiples of 256, K a multiple of 64; kchunk k tiles per split.
+struct Split3Args {
+  MatArg ahi, alo, bhi, blo;
+  MatArg out;
+  int64_t split_stride;
+  int M, N, K;
+  int splits, kchunk;
+};
+hipError_t launch_fast_split3(const Split3Args& a, int members, hipStream_t s);
+
 hipError_t launch_reduce_splits(const RedArgs& a, int members, hipStream_t s);
 hipError_t launch_colnorm(const ColnormArgs& a, int members, hipStream_t s);
 hipError_t launch_sumsq(const SumsqArgs& a, int nblocks, int members, bool bf16, hipStream_t s);

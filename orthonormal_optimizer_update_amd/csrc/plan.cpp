@@ -27,6 +27,19 @@ void choose_split(int64_t K, int64_t tiles, int members, int* splits, int* kchun
   *splits = static_cast<int>(cdiv(K, kc));
 }
 
+// Split nkt k tiles so that tiles * members * splits reaches one workgroup per
+// CU of the 256 x 256 kernel, with at least 8 k tiles per split.
+void choose_split_tiles(int64_t nkt, int64_t tiles, int members, int* splits, int* kchunk) {
+  int64_t want = cdiv(256, tiles * members);
+  int64_t cap = nkt / 8;
+  if (cap < 1) cap = 1;
+  if (want > cap) want = cap;
+  if (want < 1) want = 1;
+  const int64_t kc = cdiv(nkt, want);
+  *kchunk = static_cast<int>(kc);
+  *splits = static_cast<int>(cdiv(nkt, kc));
+}
+
 bool finite(float v) { return isfinite(v) != 0; }
 
 ortho_status check_mat(const ortho_mat& a) {
@@ -68,6 +81,18 @@ bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* p) {
   if (pr > part) part = pr;
   if (pg > part) part = pg;
   if (pg2 > part) part = pg2;
+  // From r = 512 on the sweeps are product-bound and the pieces pass pays for
+  // itself; below, the fused loaders (which also leave M and G in the
+  // Infinity Cache for the last sweep) are as fast.
+  d.fast_sweeps = m % 256 == 0 && n % 256 == 0 && r % 256 == 0 && r >= 512;
+  if (d.fast_sweeps) {
+    choose_split_tiles(3 * n / 64, (m / 256) * (r / 256), d.chunk, &d.split_fl, &d.kchunk_fl);
+    choose_split_tiles(3 * m / 64, (n / 256) * (r / 256), d.chunk, &d.split_fr, &d.kchunk_fr);
+    const size_t pfl = static_cast<size_t>(d.split_fl) * mr * 4;
+    const size_t pfr = static_cast<size_t>(d.split_fr) * nr * 4;
+    if (pfl > part) part = pfl;
+    if (pfr > part) part = pfr;
+  }
   size_t o = 0;
   d.off_pt = o;    o = align_up(o + mrp * 4);
   d.off_p1 = o;    o = align_up(o + mrp * 4);
@@ -82,6 +107,17 @@ bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* p) {
   d.off_pb = o;    o = align_up(o + static_cast<size_t>(m) * d.rpb * 2);
   d.off_rb = o;    o = align_up(o + static_cast<size_t>(n) * d.rpb * 2);
   d.off_qb = o;    o = align_up(o + static_cast<size_t>(n) * d.rpb * 2);
+  if (d.fast_sweeps) {
+    const size_t mn2 = static_cast<size_t>(m) * n * 2;
+    d.off_bhi = o;   o = align_up(o + mn2);
+    d.off_blo = o;   o = align_up(o + mn2);
+    d.off_bhit = o;  o = align_up(o + mn2);
+    d.off_blot = o;  o = align_up(o + mn2);
+    d.off_qhit = o;  o = align_up(o + nr * 2);
+    d.off_qlot = o;  o = align_up(o + nr * 2);
+    d.off_phit = o;  o = align_up(o + mr * 2);
+    d.off_plot = o;  o = align_up(o + mr * 2);
+  }
   d.member_bytes = o;
   d.total_bytes = o * static_cast<size_t>(d.chunk);
   *p = d;

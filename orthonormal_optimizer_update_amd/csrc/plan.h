@@ -27,6 +27,12 @@ struct DionPlan {
   size_t off_pt, off_p1, off_part, off_s, off_x, off_d, off_tt, off_r, off_colsq;
   int64_t rpb;               // leading dimension of the bf16 factor copies (r rounded to 8)
   size_t off_pb, off_rb, off_qb;  // bf16 P, (1-mu) R, lr*scale*Q' for the last sweep
+  // Sweeps on the 256 x 256 kernel (m, n, r multiples of 256, bf16 weights):
+  // bf16x2 pieces of B = M + G (m x n) and B^T, of Q^T (r x n) and of P^T (r x m),
+  // and split-K factors in k tiles of the three-segment reductions.
+  bool fast_sweeps;
+  int split_fl, kchunk_fl, split_fr, kchunk_fr;
+  size_t off_bhi, off_blo, off_bhit, off_blot, off_qhit, off_qlot, off_phit, off_plot;
   size_t member_bytes;       // stride between members
   size_t total_bytes;
 };
