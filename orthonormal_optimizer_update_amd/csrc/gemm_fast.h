@@ -6,14 +6,27 @@
 // 256 x 256 x 64 block tile, 4 waves in a 2 x 2 grid, 128 x 128 per wave
 // (4 x 4 v_mfma_f32_32x32x16_bf16 accumulators).  Operand tiles go straight
 // from HBM/L2 into LDS with global_load_lds_dwordx4 (each lane's 16 bytes land
-// at LDS base + 16 * lane), two stages, one barrier per 64-wide k step.  The
-// LDS row of a tile is 8 chunks of 16 bytes; chunk c of row r is stored at
-// position c ^ ((r >> 1) & 7), which each lane realises by choosing which
-// global chunk it fetches, so that the fragment reads of 16 consecutive rows
-// hit 64 distinct banks.
+// at M0 + 16 * lane), two stages, one barrier per 64-wide k step.  The LDS row
+// of a tile is 8 chunks of 16 bytes; chunk c of row r is stored at position
+// c ^ ((r >> 1) & 7), which each lane realises by choosing which global chunk
+// it fetches, so that the fragment reads of 16 consecutive rows hit 64
+// distinct banks.
+//
+// Issue order inside a k tile is fixed by hand (scheduling fences): each of
+// the 8 slots of a 16-wide k step holds one fragment read for the next step,
+// in the order the next step's products consume them (a0 b0 b1 b2 b3 a1 a2
+// a3), and two products; the 16 tile loads of the next tile ride in the slots
+// of the first step.  The barrier sits before the last step's products, so the
+// first fragment reads of the next tile overlap them.  The tile loads are
+// written as inline assembly with a scalar base address and a per-lane 32-bit
+// offset: the compiler treats the LDS-DMA builtin as an unordered LDS event
+// and would then wait for every outstanding fragment read before each product
+// step; with the loads hidden from it, its LDS waits count exactly, and the
+// kernel waits for the loads itself (s_waitcnt before the barrier).
 //
 // Requirements (checked by the launcher): M, N multiples of 256, K a multiple
-// of 64, 16-byte aligned rows; every split-K slice holds at least one k tile.
+// of 64, 16-byte aligned rows, 256 rows of an operand within 4 GiB of bytes;
+// every split-K slice holds at least one k tile.
 #pragma once
 
 #include "gemm_core.h"
@@ -26,25 +39,35 @@ constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int TILE_BYTES = BM * BK * 2;  // 32 KB per operand per stage
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) const void* glb_ptr_t;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
-// Issue the loads of one 256 x 64 operand tile into LDS (8 instructions per
-// wave; instruction q of wave w fills rows (8w + q) * 8 .. + 7).
-__device__ __forceinline__ void load_tile(const uint16_t* src, int64_t ld, int row0, int k0,
-                                          char* lds_tile, int wave, int lane) {
-  const int sub = lane >> 3;            // row within the 8-row group
-  const int pos = lane & 7;             // stored chunk position
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int row = (wave * 8 + q) * 8 + sub;
-    const int chunk = swz(row, pos);    // logical chunk this lane fetches
-    const uint16_t* g = src + (int64_t)(row0 + row) * ld + k0 + chunk * 8;
-    // address-space casts (generic -> global / local) need C-style casts
-    __builtin_amdgcn_global_load_lds((glb_ptr_t)(g), (lds_ptr_t)(lds_tile + (wave * 8 + q) * 1024),
-                                     16, 0, 0);
-  }
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane.  lds must
+// be wave-uniform.  The compiler does not look inside the assembly for
+// hazards, so it carries its own wait states: five before anything in it (a
+// vector instruction that wrote an SGPR the load reads, e.g. a readfirstlane
+// of the base, needs five before a vector memory instruction), and one between
+// the M0 write and the load.  The caller waits (vmcnt) before the LDS is read.
+__device__ __forceinline__ void dma16(unsigned voff, const char* sbase, unsigned lds) {
+  asm volatile("s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void dma16_flat(const void* addr, unsigned lds) {
+  asm volatile("s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(addr), "s"(lds) : "memory");
+}
+
+// A pointer the caller knows to be wave-uniform, in scalar registers.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ unsigned lds_addr(const char* p) {
+  // address-space cast (generic -> local) needs a C-style cast
+  return __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_ptr_t)(p));
 }
 
 __device__ __forceinline__ bf16x8 read_frag(const char* lds_tile, int row, int chunk) {
@@ -73,6 +96,7 @@ __device__ __forceinline__ void fast_preload(floatx16 (&acc)[4][4], const void* 
   const char* src = static_cast<const char*>(srcv);
   const int lrow = kBf ? (lane >> 5) : 0;
   const int lcol = kBf ? (lane & 31) * 8 : lane * 4;
+  const unsigned lds0 = lds_addr(smem);
 #pragma unroll
   for (int pass = 0; pass < 256 / kRowsPerPass; ++pass) {
 #pragma unroll 8
@@ -81,7 +105,7 @@ __device__ __forceinline__ void fast_preload(floatx16 (&acc)[4][4], const void* 
       const int rl = ins * kRowsPerInstr + lrow;  // LDS row
       const int row = m0 + (kBf ? rl : (rl >> 6) * 128 + pass * 64 + (rl & 63));
       const char* g = src + ((int64_t)row * ldp + n0 + lcol) * kEsz;
-      __builtin_amdgcn_global_load_lds((glb_ptr_t)(g), (lds_ptr_t)(smem + ins * 1024), 16, 0, 0);
+      dma16_flat(g, lds0 + ins * 1024);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -119,7 +143,8 @@ template <class Epi>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_256(GemmParams<typename Epi::Args> p) {
   using namespace fast;
   __shared__ __attribute__((aligned(1024))) char smem_fast[2 * 2 * TILE_BYTES];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   // Tile order: each XCD (workgroup id mod 8) gets a contiguous run of
@@ -148,11 +173,18 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256(GemmParams<typename Epi:
   const int nks = p.K / BK;                       // k tiles per segment
   const int kt_begin = split * p.kchunk;          // this split's k tiles
   const int kt_end = min(kt_begin + p.kchunk, nks * Epi::kSegs);
-  auto seg_a = [&](int kt) { return Epi::kSegs == 3 && kt >= 2 * nks ? A2 : A; };
-  auto seg_b = [&](int kt) { return Epi::kSegs == 3 && kt >= nks && kt < 2 * nks ? B2 : B; };
   auto seg_k = [&](int kt) {  // k offset within the segment (no division)
     if constexpr (Epi::kSegs == 3) kt -= kt >= 2 * nks ? 2 * nks : (kt >= nks ? nks : 0);
     return kt * BK;
+  };
+  // byte address of row m0 / n0 of tile kt (uniform: scalar registers)
+  auto base_a = [&](int kt) {
+    const uint16_t* src = Epi::kSegs == 3 && kt >= 2 * nks ? A2 : A;
+    return uniform_ptr(reinterpret_cast<const char*>(src + (int64_t)m0 * lda + seg_k(kt)));
+  };
+  auto base_b = [&](int kt) {
+    const uint16_t* src = Epi::kSegs == 3 && kt >= nks && kt < 2 * nks ? B2 : B;
+    return uniform_ptr(reinterpret_cast<const char*>(src + (int64_t)n0 * ldb + seg_k(kt)));
   };
 
   floatx16 acc[4][4];
@@ -164,75 +196,109 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256(GemmParams<typename Epi:
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   Epi epi(p.e, bi, split);
-  if constexpr (Epi::kFastPre != 0)
-    fast_preload<Epi::kFastPre == 1, false>(acc, epi.fast_pre_src(), epi.fast_pre_ld(),
-                                            epi.fast_pre_scale(), m0, n0, smem_fast, wave, lane);
-  if constexpr (Epi::kFastPre2 != 0)
-    fast_preload<true, true>(acc, epi.fast_pre2_src(), epi.fast_pre2_ld(), epi.fast_pre2_scale(),
-                             m0, n0, smem_fast, wave, lane);
 
   auto sa = [&](int st) { return smem_fast + st * 2 * TILE_BYTES; };
   auto sb = [&](int st) { return smem_fast + st * 2 * TILE_BYTES + TILE_BYTES; };
+  const unsigned lds0 = lds_addr(smem_fast);
 
-  load_tile(seg_a(kt_begin), lda, m0, seg_k(kt_begin), sa(0), wave, lane);
-  load_tile(seg_b(kt_begin), ldb, n0, seg_k(kt_begin), sb(0), wave, lane);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // Tile loads: instruction q (0..7 rows of A, 8..15 rows of B) of wave w
+  // fills rows (8w + q % 8) * 8 .. + 7 of its operand tile; lane = 8 * (row
+  // within the group) + stored chunk position.  Per-lane byte offsets from
+  // the tile's first row are loop-invariant.
+  const int sub = lane >> 3, pos = lane & 7;
+  unsigned offa[8], offb[8];
+#pragma unroll
+  for (int qq = 0; qq < 8; ++qq) {
+    const int row = (wave * 8 + qq) * 8 + sub;
+    const int chunk = swz(row, pos);  // logical chunk this lane fetches
+    offa[qq] = static_cast<unsigned>((row * lda + chunk * 8) * 2);
+    offb[qq] = static_cast<unsigned>((row * ldb + chunk * 8) * 2);
+  }
+  auto load_one = [&](int q, const char* ba, const char* bb, int st) {
+    const int qq = q & 7;
+    if (q < 8) dma16(offa[qq], ba, lds0 + st * 2 * TILE_BYTES + (wave * 8 + qq) * 1024);
+    else dma16(offb[qq], bb, lds0 + st * 2 * TILE_BYTES + TILE_BYTES + (wave * 8 + qq) * 1024);
+  };
 
   const int frow = lane & 31, fchunk = lane >> 5;
-  // Fragments are double-buffered in registers: the reads for k step kk + 1
-  // are issued before the 16 products of step kk, so LDS latency overlaps the
-  // matrix cores (also across the k-tile barrier).
+  // Fragments of two consecutive 16-wide k steps: read q of step kk goes to
+  // buffer kk & 1 in consumption order a0 b0 b1 b2 b3 a1 a2 a3.
   bf16x8 fa[2][4], fb[2][4];
-  auto read_frags = [&](bf16x8 (&a)[4], bf16x8 (&b)[4], const char* ta, const char* tb, int kk) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = read_frag(ta, wm * 128 + i * 32 + frow, kk * 2 + fchunk);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = read_frag(tb, wn * 128 + j * 32 + frow, kk * 2 + fchunk);
+  auto read_one = [&](int buf, int q, const char* ta, const char* tb, int kk) {
+    if (q == 0) fa[buf][0] = read_frag(ta, wm * 128 + frow, kk * 2 + fchunk);
+    else if (q <= 4) fb[buf][q - 1] = read_frag(tb, wn * 128 + (q - 1) * 32 + frow, kk * 2 + fchunk);
+    else fa[buf][q - 4] = read_frag(ta, wm * 128 + (q - 4) * 32 + frow, kk * 2 + fchunk);
   };
-  // One 64-wide k tile: loads of the next tile into the other stage, four
-  // 16-wide steps of products on this one, barrier, first fragments of the
-  // next tile.
+  // product pair q: accumulators (q / 2, 2 (q % 2)) and (q / 2, 2 (q % 2) + 1)
+  auto mfma_pair = [&](int buf, int q) {
+    const int i = q >> 1, j0 = (q & 1) * 2;
+    acc[i][j0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j0], acc[i][j0], 0, 0, 0);
+    acc[i][j0 + 1] =
+        __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j0 + 1], acc[i][j0 + 1], 0, 0, 0);
+  };
+
+  {
+    const char* ba = base_a(kt_begin);
+    const char* bb = base_b(kt_begin);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) load_one(q, ba, bb, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 8; ++q) read_one(0, q, sa(0), sb(0), 0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // One 64-wide k tile on stage cur while the next tile streams into the other
+  // stage.  The last tile reloads itself into the free stage (no branch; the
+  // copy is never read), and the fragment reads of the "next" tile after the
+  // last barrier likewise go unused.
   auto k_tile = [&](int kt) {
     const int cur = (kt - kt_begin) & 1;
-    const bool more = kt + 1 < kt_end;
-    if (more) {
-      load_tile(seg_a(kt + 1), lda, m0, seg_k(kt + 1), sa(cur ^ 1), wave, lane);
-      load_tile(seg_b(kt + 1), ldb, n0, seg_k(kt + 1), sb(cur ^ 1), wave, lane);
-    }
+    const int kn = kt + 1 < kt_end ? kt + 1 : kt;
+    const char* ba = base_a(kn);
+    const char* bb = base_b(kn);
     const char* ta = sa(cur);
     const char* tb = sb(cur);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (kk < 3) read_frags(fa[(kk + 1) & 1], fb[(kk + 1) & 1], ta, tb, kk + 1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
-    }
-    // Instruction order for the scheduler: tile loads first, then for each k
-    // step the next step's 8 fragment reads interleaved with its 16 products.
-    __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);  // VMEM reads (tile loads)
 #pragma unroll
     for (int kk = 0; kk < 3; ++kk) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
+        if (kk == 0) {
+          load_one(2 * q, ba, bb, cur ^ 1);
+          load_one(2 * q + 1, ba, bb, cur ^ 1);
+        }
+        read_one((kk + 1) & 1, q, ta, tb, kk + 1);
+        mfma_pair(kk & 1, q);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    // The last step's fragments are in registers: wait for this wave's tile
+    // loads and fragment reads, then the barrier hands stage cur over to the
+    // next tile's loads and stage cur ^ 1 to the fragment reads.
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (more) read_frags(fa[0], fb[0], sa(cur ^ 1), sb(cur ^ 1), 0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      read_one(0, q, sa(cur ^ 1), sb(cur ^ 1), 0);
+      mfma_pair(1, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
-  read_frags(fa[0], fb[0], sa(0), sb(0), 0);
-  // The first tile is peeled (K >= 64 is checked by the launcher): the
-  // accumulators' initial values then feed products directly instead of also
-  // reaching the epilogue through a zero-trip path.
-  k_tile(kt_begin);
-  for (int kt = kt_begin + 1; kt < kt_end; ++kt) k_tile(kt);
+  for (int kt = kt_begin; kt < kt_end; ++kt) k_tile(kt);
+
+  // Memory terms of the policy (scale * S) join the products after the loop:
+  // accumulators that start at zero keep the loop free of live-in values.
+  // The loop's last barrier has released the tile stages (what is still read
+  // after it is never used).
+  if constexpr (Epi::kFastPre != 0)
+    fast_preload<Epi::kFastPre == 1, true>(acc, epi.fast_pre_src(), epi.fast_pre_ld(),
+                                           epi.fast_pre_scale(), m0, n0, smem_fast, wave, lane);
+  if constexpr (Epi::kFastPre2 != 0)
+    fast_preload<true, true>(acc, epi.fast_pre2_src(), epi.fast_pre2_ld(), epi.fast_pre2_scale(),
+                             m0, n0, smem_fast, wave, lane);
 
   // Transposed outputs straight from the accumulators (four consecutive rows
   // of one column per lane).

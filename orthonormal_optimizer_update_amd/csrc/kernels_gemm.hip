@@ -140,14 +140,18 @@ template <class Cfg>
 using NsRow = LdRowBf16<Cfg::BM, 32, Cfg::NT>;
 
 // The 256 x 256 x 64 direct-to-LDS kernel applies when the product tiles
-// exactly and every operand row is 16-byte aligned.
+// exactly, every operand row is 16-byte aligned and a 256-row block of an
+// operand spans less than 2 GiB (per-lane 32-bit load offsets).
 bool fast_ok(int M, int N, int K, const MatArg& a, const MatArg& b) {
   return M % 256 == 0 && N % 256 == 0 && K % 64 == 0 && a.vec && b.vec && a.ld % 8 == 0 &&
-         b.ld % 8 == 0;
+         b.ld % 8 == 0 && a.ld <= (int64_t{1} << 22) && b.ld <= (int64_t{1} << 22);
 }
 
 template <class Epi>
 hipError_t run_fast(GemmParams<typename Epi::Args>& p, int members, hipStream_t s) {
+  // the second pieces share the first pieces' row strides
+  if (Epi::kSegs == 3 && (p.a2.ld != p.a.ld || p.b0s.ld != p.b0.ld)) return hipErrorInvalidValue;
+  if (p.a.ld > (int64_t{1} << 22) || p.b0.ld > (int64_t{1} << 22)) return hipErrorInvalidValue;
   p.tiles_n = p.N / 256;
   if (p.splits < 1 || p.kchunk < 1) {  // one slice over every k tile
     p.splits = 1;
