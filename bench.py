@@ -35,7 +35,7 @@ PEAK_HBM_GBS = 8000.0
 # passes over `bench.py --counter-sample`, each scaled by the same counter's
 # reading for a 256 MiB elementwise copy (fetch factor 2.0, write factor 1.0).
 # Set to None whenever the kernel changes, until the passes are taken again.
-TRAFFIC_BYTES_PER_LAUNCH = 2.647e8
+TRAFFIC_BYTES_PER_LAUNCH = 2.797e8
 
 
 def parse():
@@ -179,7 +179,11 @@ def main():
         per_path[nm] = {"ms": tp.ms / args.steps, "steps_per_s": 1000.0 * args.steps / tp.ms}
 
     # Dominant kernel: the Newton-Schulz MFMA GEMM (three launches per
-    # iteration, each 2*m*m*n flops at m = n).  Its average launch time is
+    # iteration).  Work per iteration is counted densely, 4 m m n + 2 m^3 (Gram,
+    # polynomial, apply).  The Gram and the polynomial are symmetric and the
+    # kernel computes only their tiles on and above the diagonal, so the
+    # products it executes are reported beside the dense rate.  Its average
+    # launch time is
     # (time of 6 iterations - time of 1 iteration) / 15, on the same stream:
     # both runs launch the same normalisation kernels, and both keep the GPU
     # busy for far longer than the host needs to issue a call, so the
@@ -195,13 +199,19 @@ def main():
         for _ in range(reps):
             ns_steps(1)
     gemm_ms = (t6.ms - t1.ms) / reps / 15.0
-    flops = 2.0 * m * m * n
+    flops = (4.0 * m * m * n + 2.0 * m ** 3) / 3.0  # dense count, mean per launch
     achieved = flops / (gemm_ms * 1e-3) / 1e12
+    tiles = m // 256
+    sym_frac = (tiles * (tiles + 1) // 2) / float(tiles * tiles)  # tiles computed, Gram and polynomial
+    executed = (2.0 * m * m * n * sym_frac + 2.0 * m ** 3 * sym_frac + 2.0 * m * m * n) / 3.0
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": TRAFFIC_BYTES_PER_LAUNCH,
                 "kernel": "gemm_bf16_256 (Newton-Schulz products X X^T, b A + c A^2, a X + Bp X; "
-                          "bf16 MFMA 32x32x16, 256x256 tiles, direct-to-LDS operand copies)",
-                "avg_launch_ms": gemm_ms, "flops_per_launch": flops}
+                          "bf16 MFMA 32x32x16, 256x256 tiles, direct-to-LDS operand copies; the two "
+                          "symmetric products on their upper tiles only)",
+                "avg_launch_ms": gemm_ms, "flops_per_launch": flops,
+                "executed_flops_per_launch": executed,
+                "executed_tflops": executed / (gemm_ms * 1e-3) / 1e12}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -22,6 +22,9 @@ namespace ortho {
 //   fast_store4   receives four consecutive columns of one row of the result.
 //   kFastT / fast_store_t4  receive four consecutive rows of one column
 //                 (transposed outputs), straight from the accumulators.
+//   kFastSym      the result is symmetric: with GemmParams::sym the kernel
+//                 computes the tiles on and above the diagonal only and hands
+//                 each off-diagonal tile to fast_store_t4 as well (its mirror).
 
 __device__ __forceinline__ uint2 pack_bf16x4(floatx4 v) {
   return make_uint2(to_bf16_bits(v[0]) | (uint32_t(to_bf16_bits(v[1])) << 16),
@@ -106,13 +109,17 @@ struct EpiNSGram {
   static constexpr int kSegs = 1;
   static constexpr int kFastPre2 = 0;
   static constexpr bool kFastT = false;
+  static constexpr bool kFastSym = true;
   __device__ const void* fast_pre_src() const { return nullptr; }
   __device__ int64_t fast_pre_ld() const { return 0; }
   __device__ float fast_pre_scale() const { return 0.f; }
   __device__ __forceinline__ void fast_store4(int row, int col, floatx4 v) {
     *reinterpret_cast<uint2*>(a + (int64_t)row * ld + col) = pack_bf16x4(v);
   }
-  __device__ __forceinline__ void fast_store_t4(int, int, floatx4) {}
+  // mirror: A[col][row0 .. row0 + 3] = A[row0 .. row0 + 3][col]
+  __device__ __forceinline__ void fast_store_t4(int col, int row0, floatx4 v) {
+    *reinterpret_cast<uint2*>(a + (int64_t)col * ld + row0) = pack_bf16x4(v);
+  }
   __device__ const void* fast_pre2_src() const { return nullptr; }
   __device__ int64_t fast_pre2_ld() const { return 0; }
   __device__ float fast_pre2_scale() const { return 0.f; }
@@ -152,6 +159,7 @@ struct EpiNSPoly {
   static constexpr int kSegs = 1;
   static constexpr int kFastPre2 = 0;
   static constexpr bool kFastT = false;
+  static constexpr bool kFastSym = true;
   __device__ const void* fast_pre_src() const { return a; }
   __device__ int64_t fast_pre_ld() const { return lda; }
   __device__ float fast_pre_scale() const { return boc; }
@@ -160,7 +168,12 @@ struct EpiNSPoly {
     *reinterpret_cast<uint2*>(bp + (int64_t)row * ldb + col) = pack_bf16x4(y);
     if (bp32) *reinterpret_cast<floatx4*>(bp32 + (int64_t)row * ldb32 + col) = y;
   }
-  __device__ __forceinline__ void fast_store_t4(int, int, floatx4) {}
+  // mirror: Bp[col][row0 .. row0 + 3] = Bp[row0 .. row0 + 3][col]
+  __device__ __forceinline__ void fast_store_t4(int col, int row0, floatx4 v) {
+    const floatx4 y = c * v;
+    *reinterpret_cast<uint2*>(bp + (int64_t)col * ldb + row0) = pack_bf16x4(y);
+    if (bp32) *reinterpret_cast<floatx4*>(bp32 + (int64_t)col * ldb32 + row0) = y;
+  }
   __device__ const void* fast_pre2_src() const { return nullptr; }
   __device__ int64_t fast_pre2_ld() const { return 0; }
   __device__ float fast_pre2_scale() const { return 0.f; }
@@ -219,6 +232,7 @@ struct EpiNSApply {
   static constexpr int kSegs = 1;
   static constexpr int kFastPre2 = 0;
   static constexpr bool kFastT = true;
+  static constexpr bool kFastSym = false;
   __device__ const void* fast_pre_src() const { return x32; }
   __device__ int64_t fast_pre_ld() const { return ldx; }
   __device__ float fast_pre_scale() const { return a; }
@@ -393,6 +407,7 @@ struct EpiDionFastM {
   static constexpr int kSegs = 1;
   static constexpr int kFastPre2 = 1;
   static constexpr bool kFastT = false;
+  static constexpr bool kFastSym = false;
   __device__ const void* fast_pre_src() const { return m; }
   __device__ int64_t fast_pre_ld() const { return ldm; }
   __device__ float fast_pre_scale() const { return -1.f; }
@@ -418,6 +433,7 @@ struct EpiDionFastX {
   static constexpr int kSegs = 1;
   static constexpr int kFastPre2 = 0;
   static constexpr bool kFastT = false;
+  static constexpr bool kFastSym = false;
   __device__ const void* fast_pre_src() const { return x; }
   __device__ int64_t fast_pre_ld() const { return ldx; }
   __device__ float fast_pre_scale() const { return -1.f; }
@@ -447,6 +463,7 @@ struct EpiFastSplitF32 {
   static constexpr int kSegs = 3;
   static constexpr int kFastPre2 = 0;
   static constexpr bool kFastT = false;
+  static constexpr bool kFastSym = false;
   __device__ const void* fast_pre_src() const { return nullptr; }
   __device__ int64_t fast_pre_ld() const { return 0; }
   __device__ float fast_pre_scale() const { return 0.f; }

@@ -244,6 +244,7 @@ struct GemmParams {
   int splits;        // split-K factor (blockIdx.y = member * splits + split)
   int kchunk;        // k range per split, a multiple of BK
   int tri;           // right operand is zero for k > j (triangular factor)
+  int sym;           // 256x256 kernel: C symmetric, upper tiles only (mirrored on store)
 };
 
 template <class Cfg, class LA, class LB, class Epi>

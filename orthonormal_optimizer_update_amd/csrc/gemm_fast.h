@@ -153,12 +153,25 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256(GemmParams<typename Epi:
   const int nwg = gridDim.x;
   int t = blockIdx.x;
   if ((nwg & 7) == 0) t = (t & 7) * (nwg >> 3) + (t >> 3);
-  const int tiles_n = p.tiles_n, tiles_m = nwg / tiles_n;
-  const int group = 4 * tiles_n;
-  const int first_m = (t / group) * 4;
-  const int gsize = min(tiles_m - first_m, 4);
-  const int tm = first_m + (t % group) % gsize;
-  const int tn = (t % group) / gsize;
+  const int tiles_n = p.tiles_n;
+  int tm, tn;
+  if (Epi::kFastSym && p.sym) {
+    // symmetric result: tiles on and above the diagonal, row by row
+    int rem = t;
+    tm = 0;
+    while (rem >= tiles_n - tm) {
+      rem -= tiles_n - tm;
+      ++tm;
+    }
+    tn = tm + rem;
+  } else {
+    const int tiles_m = nwg / tiles_n;
+    const int group = 4 * tiles_n;
+    const int first_m = (t / group) * 4;
+    const int gsize = min(tiles_m - first_m, 4);
+    tm = first_m + (t % group) % gsize;
+    tn = (t % group) / gsize;
+  }
   // blockIdx.y = member * splits + split (split-K over the k tiles)
   const int bi = blockIdx.y / p.splits, split = blockIdx.y % p.splits;
   const int m0 = tm * BM, n0 = tn * BN;
@@ -301,8 +314,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256(GemmParams<typename Epi:
                              m0, n0, smem_fast, wave, lane);
 
   // Transposed outputs straight from the accumulators (four consecutive rows
-  // of one column per lane).
-  if constexpr (Epi::kFastT) {
+  // of one column per lane): a transposed copy, or the mirror tile (tn, tm)
+  // of a symmetric result.
+  if (Epi::kFastT || (Epi::kFastSym && p.sym && tm != tn)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll

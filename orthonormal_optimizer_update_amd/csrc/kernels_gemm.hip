@@ -157,7 +157,10 @@ hipError_t run_fast(GemmParams<typename Epi::Args>& p, int members, hipStream_t 
     p.splits = 1;
     p.kchunk = (p.K / 64) * Epi::kSegs;
   }
-  dim3 grid((p.M / 256) * p.tiles_n, members * p.splits);
+  // symmetric results (Gram, polynomial): tiles on and above the diagonal
+  if (p.sym && (!Epi::kFastSym || p.M != p.N)) return hipErrorInvalidValue;
+  const int tiles = p.sym ? p.tiles_n * (p.tiles_n + 1) / 2 : (p.M / 256) * p.tiles_n;
+  dim3 grid(tiles, members * p.splits);
   hipLaunchKernelGGL((gemm_bf16_256<Epi>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
@@ -170,7 +173,10 @@ hipError_t ns_gram_t(const NsGramArgs& a, int members, hipStream_t s) {
   p.e.a = a.a;
   p.M = a.M; p.N = a.M; p.K = a.K;
   p.splits = 1; p.kchunk = 0; p.tri = 0;
-  if (fast_ok(p.M, p.N, p.K, p.a, p.b0)) return run_fast<EpiNSGram>(p, members, s);
+  if (fast_ok(p.M, p.N, p.K, p.a, p.b0)) {
+    p.sym = 1;  // X X^T: upper tiles, mirrored
+    return run_fast<EpiNSGram>(p, members, s);
+  }
   return run<Cfg, NsRow<Cfg>, NsRow<Cfg>, EpiNSGram>(p, members, s);
 }
 
@@ -183,7 +189,10 @@ hipError_t ns_poly_t(const NsPolyArgs& a, int members, hipStream_t s) {
   p.e.has32 = a.M <= kNsSplitRows;
   p.M = a.M; p.N = a.M; p.K = a.M;
   p.splits = 1; p.kchunk = 0; p.tri = 0;
-  if (fast_ok(p.M, p.N, p.K, p.a, p.b0)) return run_fast<EpiNSPoly>(p, members, s);
+  if (fast_ok(p.M, p.N, p.K, p.a, p.b0)) {
+    p.sym = 1;  // b A + c A A is symmetric with A: upper tiles, mirrored
+    return run_fast<EpiNSPoly>(p, members, s);
+  }
   return run<Cfg, NsRow<Cfg>, NsRow<Cfg>, EpiNSPoly>(p, members, s);
 }
 
