@@ -70,6 +70,27 @@ def test_ns_planted_square_4096():
     assert rel(got, oracle.newton_schulz(G)) <= TOL["bf16"]
 
 
+def test_ns_wide_2048x8192_deterministic():
+    """A wide 2048 x 8192 matrix (Gram over 36 tiles on and above the
+    diagonal, mirrored): matches the oracle and gives the same bits on a second
+    run."""
+    G = synth.gradient(11, 2048, 8192, 1, "bf16")
+    note("ns 2048x8192")
+    got = gpu_ns(G, "bf16")
+    assert rel(got, oracle.newton_schulz(G)) <= TOL["bf16"]
+    again = gpu_ns(G, "bf16")
+    assert np.array_equal(got, again)
+
+
+def test_ns_square_4096_deterministic():
+    """Two runs of the 4096 x 4096 iteration give the same bits."""
+    G = synth.gradient(12, 4096, 4096, 1, "bf16")
+    note("ns 4096 deterministic")
+    a = gpu_ns(G, "bf16", steps=2)
+    b = gpu_ns(G, "bf16", steps=2)
+    assert np.array_equal(a, b)
+
+
 # ----------------------------------------------------------------------------
 # Dion
 # ----------------------------------------------------------------------------
