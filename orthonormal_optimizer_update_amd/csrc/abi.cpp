@@ -96,15 +96,15 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       const MatArg tBloT = ws_table(base, mb, pl.off_blot, nb, m, ni, mi, 2, 16);
       const MatArg tQhiT = ws_table(base, mb, pl.off_qhit, nb, n, r, ni, 2, 16);
       const MatArg tQloT = ws_table(base, mb, pl.off_qlot, nb, n, r, ni, 2, 16);
-      SplitSumArgs sa;
+      SplitSumArgs sa{};
       sa.m = tM; sa.g = tG; sa.hi = tBhi; sa.lo = tBlo; sa.hit = tBhiT; sa.lot = tBloT;
       sa.rows = mi; sa.cols = ni;
       ORTHO_TRY(launch_split_sum(sa, nb, s));
-      SplitTArgs qa;
+      SplitTArgs qa{};
       qa.src = tQ; qa.hit = tQhiT; qa.lot = tQloT; qa.rows = ni; qa.cols = r;
       ORTHO_TRY(launch_split_t(qa, nb, s));
       // Sweep 1 over n: P_tilde = (Bhi, Blo) (Qhi, Qlo)^T
-      Split3Args l3;
+      Split3Args l3{};
       l3.ahi = tBhi; l3.alo = tBlo; l3.bhi = tQhiT; l3.blo = tQloT;
       l3.out = pl.split_fl > 1 ? tPart : tPt;
       l3.split_stride = m * r;
@@ -112,7 +112,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       l3.splits = pl.split_fl; l3.kchunk = pl.kchunk_fl;
       ORTHO_TRY(launch_fast_split3(l3, nb, s));
       if (pl.split_fl > 1) {
-        RedArgs ra;
+        RedArgs ra{};
         ra.part = part_f; ra.part_member_stride = static_cast<int64_t>(mb / 4);
         ra.slice = m * r; ra.splits = pl.split_fl; ra.rows = mi; ra.cols = r;
         ra.out = tPt; ra.colsq = nullptr; ra.colsq_member_stride = 0;
@@ -121,7 +121,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     }
 
     // Sweep 1: P_tilde = (M + G) Q.
-    DionLeftArgs la;
+    DionLeftArgs la{};
     la.m = tM; la.g = tG; la.q = tQ;
     la.out = pl.split_left > 1 ? tPart : tPt;
     la.split_stride = m * r;
@@ -129,7 +129,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     la.splits = pl.split_left; la.kchunk = pl.kchunk_left;
     if (!fast_sw) ORTHO_TRY(launch_dion_left(la, bf, nb, s));
     if (!fast_sw && pl.split_left > 1) {
-      RedArgs ra;
+      RedArgs ra{};
       ra.part = part_f; ra.part_member_stride = static_cast<int64_t>(mb / 4);
       ra.slice = m * r; ra.splits = pl.split_left; ra.rows = mi; ra.cols = r;
       ra.out = tPt; ra.colsq = nullptr; ra.colsq_member_stride = 0;
@@ -139,11 +139,11 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     // Orthonormalisation of P_tilde (Q-factor of its thin QR, diag(R) > 0).
     // Pass 1: fp64 Gram, column-scaled fp64 Cholesky and triangular inverse,
     // P1 = P_tilde T1 with bf16x6 products (T1 = D L^-T, upper triangular).
-    Gram64Args ga;
+    Gram64Args ga{};
     ga.p = tPt; ga.part = part_d; ga.part_member_stride = static_cast<int64_t>(mb / 8);
     ga.slice = static_cast<int64_t>(r) * r; ga.m = mi; ga.r = r; ga.kchunk = pl.kchunk_gram;
     ORTHO_TRY(launch_gram64(ga, pl.split_gram, nb, s));
-    CholArgs ca;
+    CholArgs ca{};
     ca.part = part_d; ca.part_member_stride = static_cast<int64_t>(mb / 8);
     ca.slice = static_cast<int64_t>(r) * r; ca.splits = pl.split_gram;
     ca.s = reinterpret_cast<double*>(base + pl.off_s);
@@ -153,13 +153,72 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     ca.r = r; ca.status = status;
     float* tt = reinterpret_cast<float*>(base + pl.off_tt);
     ORTHO_TRY(launch_cholesky_inverse(ca, tt, static_cast<int64_t>(mb / 4), nb, s));
-    ApplyArgs aa;
+    if (fast_sw && pl.fast_ortho) {
+      // The same three products on the 256 x 256 kernel over bf16 pieces
+      // (split-K, fixed-order reduce).  A pieces go to the row-major B-piece
+      // buffer and B pieces to the second one: sweep 1 is done with both.
+      // (m, r multiples of 256: every piece starts 256-byte aligned)
+      const size_t mr2 = static_cast<size_t>(mi) * r * 2;
+      const size_t rr2 = static_cast<size_t>(r) * r * 2;
+      MatArg ap[3], bp[3];
+      for (int k = 0; k < 3; ++k) {
+        ap[k] = ws_table(base, mb, pl.off_bhi + k * mr2, nb, r, mi, r, 2, 16);
+        bp[k] = ws_table(base, mb, pl.off_blo + k * rr2, nb, r, r, r, 2, 16);
+      }
+      const MatArg tPhiT = ws_table(base, mb, pl.off_phit, nb, m, r, mi, 2, 16);
+      const MatArg tPloT = ws_table(base, mb, pl.off_plot, nb, m, r, mi, 2, 16);
+      const int64_t mr = static_cast<int64_t>(mi) * r;
+      // P1 = P~ T1, six products of bf16x3 pieces
+      SplitRowsArgs sp{};
+      sp.src = tPt; sp.piece[0] = ap[0]; sp.piece[1] = ap[1]; sp.piece[2] = ap[2];
+      sp.rows = mi; sp.cols = r; sp.np = 3;
+      ORTHO_TRY(launch_split_rows(sp, nb, s));
+      SplitRowsArgs st{};
+      st.src = tTt; st.piece[0] = bp[0]; st.piece[1] = bp[1]; st.piece[2] = bp[2];
+      st.rows = r; st.cols = r; st.np = 3;
+      ORTHO_TRY(launch_split_rows(st, nb, s));
+      Split6Args a6{};
+      for (int k = 0; k < 3; ++k) { a6.a[k] = ap[k]; a6.b[k] = bp[k]; }
+      a6.out = tPart; a6.split_stride = mr;
+      a6.M = mi; a6.N = r; a6.K = r; a6.splits = pl.split_ap6; a6.kchunk = pl.kchunk_ap6;
+      ORTHO_TRY(launch_fast_split6(a6, nb, s));
+      RedArgs rp1{};
+      rp1.part = part_f; rp1.part_member_stride = static_cast<int64_t>(mb / 4);
+      rp1.slice = mr; rp1.splits = pl.split_ap6; rp1.rows = mi; rp1.cols = r;
+      rp1.out = tP1; rp1.has_bf16 = 0; rp1.colsq = nullptr; rp1.colsq_member_stride = 0;
+      ORTHO_TRY(launch_reduce_splits(rp1, nb, s));
+      // Pass 2 (see below): E = P1^T P1 over m, bf16x3 of the transposed P1
+      SplitTArgs pt{};
+      pt.src = tP1; pt.hit = tPhiT; pt.lot = tPloT; pt.rows = mi; pt.cols = r;
+      ORTHO_TRY(launch_split_t(pt, nb, s));
+      Split3Args e3{};
+      e3.ahi = tPhiT; e3.alo = tPloT; e3.bhi = tPhiT; e3.blo = tPloT;
+      e3.out = tPart; e3.split_stride = static_cast<int64_t>(r) * r;
+      e3.M = r; e3.N = r; e3.K = mi; e3.splits = pl.split_e; e3.kchunk = pl.kchunk_e;
+      ORTHO_TRY(launch_fast_split3(e3, nb, s));
+      ORTHO_TRY(launch_correction(part_f, static_cast<int64_t>(mb / 4), static_cast<int64_t>(r) * r,
+                                  pl.split_e, r, tt, static_cast<int64_t>(mb / 4), nb, s));
+      // P = P1 T2, bf16x3; the bf16 copy of P feeds the last sweep
+      sp.src = tP1; sp.np = 2;
+      ORTHO_TRY(launch_split_rows(sp, nb, s));
+      st.np = 2;
+      ORTHO_TRY(launch_split_rows(st, nb, s));
+      Split3Args a3{};
+      a3.ahi = ap[0]; a3.alo = ap[1]; a3.bhi = bp[0]; a3.blo = bp[1];
+      a3.out = tPart; a3.split_stride = mr;
+      a3.M = mi; a3.N = r; a3.K = r; a3.splits = pl.split_ap3; a3.kchunk = pl.kchunk_ap3;
+      ORTHO_TRY(launch_fast_split3(a3, nb, s));
+      RedArgs rp2 = rp1;
+      rp2.splits = pl.split_ap3; rp2.out = tPt; rp2.out_bf16 = tPb; rp2.has_bf16 = 1;
+      ORTHO_TRY(launch_reduce_splits(rp2, nb, s));
+    } else {
+    ApplyArgs aa{};
     aa.pt = tPt; aa.tt = tTt; aa.out = tP1; aa.M = mi; aa.r = r;
     aa.out_bf16 = tPb; aa.has_bf16 = 0;
     ORTHO_TRY(launch_apply_t(aa, true, nb, s));
     // Pass 2: P1 is orthonormal to about 2^-24 * cond; E = P1^T P1 - I (bf16x3)
     // and the first-order factor T2 = I - Phi(E)^T give P = P1 T2.
-    GramTnArgs g2;
+    GramTnArgs g2{};
     g2.p = tP1; g2.out = tPart; g2.split_stride = static_cast<int64_t>(r) * r;
     g2.m = mi; g2.r = r; g2.splits = pl.split_gram2; g2.kchunk = pl.kchunk_gram2;
     ORTHO_TRY(launch_gram_tn(g2, nb, s));
@@ -167,6 +226,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
                                 pl.split_gram2, r, tt, static_cast<int64_t>(mb / 4), nb, s));
     aa.pt = tP1; aa.out = tPt; aa.has_bf16 = bf;   // bf16 P feeds the last sweep
     ORTHO_TRY(launch_apply_t(aa, false, nb, s));
+    }
 
     // Sweep 2: R = (M + G)^T P, then Q' = column-normalised R.
     int split_r = pl.split_right;
@@ -176,10 +236,10 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       const MatArg tBloT = ws_table(base, mb, pl.off_blot, nb, m, ni, mi, 2, 16);
       const MatArg tPhiT = ws_table(base, mb, pl.off_phit, nb, m, r, mi, 2, 16);
       const MatArg tPloT = ws_table(base, mb, pl.off_plot, nb, m, r, mi, 2, 16);
-      SplitTArgs pa;
+      SplitTArgs pa{};
       pa.src = tPt; pa.hit = tPhiT; pa.lot = tPloT; pa.rows = mi; pa.cols = r;
       ORTHO_TRY(launch_split_t(pa, nb, s));
-      Split3Args r3;
+      Split3Args r3{};
       r3.ahi = tBhiT; r3.alo = tBloT; r3.bhi = tPhiT; r3.blo = tPloT;
       r3.out = tPart; r3.split_stride = n * r;
       r3.M = ni; r3.N = r; r3.K = mi;
@@ -187,21 +247,21 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       ORTHO_TRY(launch_fast_split3(r3, nb, s));
       split_r = pl.split_fr;
     } else {
-      DionRightArgs rb;
+      DionRightArgs rb{};
       rb.m = tM; rb.g = tG; rb.p = tPt; rb.out = tPart;
       rb.split_stride = n * r;
       rb.M = mi; rb.N = ni; rb.r = r;
       rb.splits = pl.split_right; rb.kchunk = pl.kchunk_right;
       ORTHO_TRY(launch_dion_right(rb, bf, nb, s));
     }
-    RedArgs rr;
+    RedArgs rr{};
     rr.part = part_f; rr.part_member_stride = static_cast<int64_t>(mb / 4);
     rr.slice = n * r; rr.splits = split_r; rr.rows = ni; rr.cols = r;
     rr.out = tR;
     rr.colsq = reinterpret_cast<float*>(base + pl.off_colsq);
     rr.colsq_member_stride = static_cast<int64_t>(mb / 4);
     ORTHO_TRY(launch_reduce_splits(rr, nb, s));
-    ColnormArgs cn;
+    ColnormArgs cn{};
     cn.r = tR; cn.q = tQ; cn.colsq = rr.colsq; cn.colsq_member_stride = rr.colsq_member_stride;
     cn.nrb = pl.nrb; cn.rows = ni; cn.cols = r; cn.status = status;
     cn.rb = tRb; cn.qb = tQb; cn.c1 = 1.0f - mu; cn.c2 = lr * scale; cn.has_bf16 = bf;
@@ -215,7 +275,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
                                  hipMemcpyDeviceToDevice, s));
 
     // Sweep 3: error feedback into M and the weight update into X.
-    DionUpdateArgs ua;
+    DionUpdateArgs ua{};
     ua.p = tPt; ua.r = tR; ua.q = tQ; ua.m = tM; ua.g = tG; ua.x = tX;
     ua.pb = tPb; ua.rb = tRb; ua.qb = tQb;
     ua.c1 = 1.0f - mu; ua.c2 = lr * scale;
@@ -252,13 +312,13 @@ ortho_status run_ns(int32_t batch, const ortho_mat* G, const ortho_mat* Out, int
     float* partial = reinterpret_cast<float*>(base + pl.off_partial);
     float* scl = reinterpret_cast<float*>(base + pl.off_scale);
 
-    SumsqArgs sa;
+    SumsqArgs sa{};
     sa.g = tG; sa.partial = partial; sa.partial_stride = static_cast<int64_t>(mb / 4);
     sa.chunk = pl.part_chunk;
     ORTHO_TRY(launch_sumsq(sa, pl.nparts, nb, bf, s));
     ORTHO_TRY(launch_ns_scale(partial, static_cast<int64_t>(mb / 4), pl.nparts, scl,
                               static_cast<int64_t>(mb / 4), kNsEps, nb, s));
-    NsInitArgs ia;
+    NsInitArgs ia{};
     ia.g = tG; ia.x32 = x32; ia.xb = xb[0]; ia.xbt = xbt[0];
     ia.scale = scl; ia.scale_stride = static_cast<int64_t>(mb / 4);
     ia.M = M; ia.N = N; ia.transposed = pl.transposed;
@@ -266,13 +326,13 @@ ortho_status run_ns(int32_t batch, const ortho_mat* G, const ortho_mat* Out, int
     if (steps == 0) ORTHO_TRY(launch_ns_store(ia, tOut, nb, bf, s));
     for (int it = 0; it < steps; ++it) {
       const int cur = it & 1;
-      NsGramArgs g1;
+      NsGramArgs g1{};
       g1.x = xb[cur]; g1.a = ta; g1.M = M; g1.K = N;
       ORTHO_TRY(launch_ns_gram(g1, nb, s));
-      NsPolyArgs g2;
+      NsPolyArgs g2{};
       g2.a = ta; g2.bp = tbp; g2.bp32 = tbp32; g2.b = b; g2.c = c; g2.M = M;
       ORTHO_TRY(launch_ns_poly(g2, nb, s));
-      NsApplyArgs g3;
+      NsApplyArgs g3{};
       g3.bp = tbp; g3.xbt = xbt[cur]; g3.x32 = x32; g3.xb_next = xb[cur ^ 1];
       g3.xbt_next = xbt[cur ^ 1]; g3.out = tOut; g3.bp32 = tbp32; g3.a = a;
       g3.M = M; g3.N = N; g3.last = it == steps - 1; g3.out_transposed = pl.transposed;

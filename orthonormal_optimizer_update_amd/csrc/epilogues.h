@@ -447,8 +447,9 @@ struct EpiDionFastX {
 };
 
 // fp32 store of C, or of split-K slice `split` of C, from the 256 x 256 kernel
-// over bf16x2 pieces (three segments).
-struct EpiFastSplitF32 {
+// over bf16 pieces (kS segments: 3 for bf16x2 pieces, 6 for bf16x3 pieces).
+template <int kS>
+struct EpiFastSplitSegs {
   static constexpr bool kPreload = false;
   struct Args {
     MatArg c;              // destination, fp32 (ld a multiple of 4, 16-byte aligned)
@@ -456,11 +457,11 @@ struct EpiFastSplitF32 {
   };
   float* c;
   int64_t ld;
-  __device__ EpiFastSplitF32(const Args& a, int bi, int split)
+  __device__ EpiFastSplitSegs(const Args& a, int bi, int split)
       : c(static_cast<float*>(const_cast<void*>(a.c.p[bi])) + split * a.split_stride),
         ld(a.c.ld) {}
   static constexpr int kFastPre = 0;
-  static constexpr int kSegs = 3;
+  static constexpr int kSegs = kS;
   static constexpr int kFastPre2 = 0;
   static constexpr bool kFastT = false;
   static constexpr bool kFastSym = false;
@@ -475,6 +476,8 @@ struct EpiFastSplitF32 {
   }
   __device__ __forceinline__ void fast_store_t4(int, int, floatx4) {}
 };
+using EpiFastSplitF32 = EpiFastSplitSegs<3>;   // bf16x3
+using EpiFastSplit6F32 = EpiFastSplitSegs<6>;  // bf16x6
 
 }  // namespace ortho
 

@@ -245,6 +245,7 @@ struct GemmParams {
   int kchunk;        // k range per split, a multiple of BK
   int tri;           // right operand is zero for k > j (triangular factor)
   int sym;           // 256x256 kernel: C symmetric, upper tiles only (mirrored on store)
+  MatArg a3, b0t;    // 256x256 kernel, six k segments: third pieces of A and B
 };
 
 template <class Cfg, class LA, class LB, class Epi>

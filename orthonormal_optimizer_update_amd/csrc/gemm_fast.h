@@ -176,28 +176,39 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256(GemmParams<typename Epi:
   const int bi = blockIdx.y / p.splits, split = blockIdx.y % p.splits;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  // With Epi::kSegs == 3 the reduction runs over three segments of length K,
-  // (a, b0), (a, b0s), (a2, b0): hi*hi + hi*lo + lo*hi of bf16x2 pieces.
+  // Epi::kSegs > 1: the reduction runs over segments of length K, each the
+  // product of one piece of A and one piece of B (bf16 pieces of fp32 data,
+  // x = p0 + p1 (+ p2)), in the order
+  //   kSegs == 3: p0 q0, p0 q1, p1 q0                        (bf16x3)
+  //   kSegs == 6: p0 q0, p0 q1, p1 q0, p0 q2, p1 q1, p2 q0   (bf16x6)
+  // with p0..p2 = a, a2, a3 and q0..q2 = b0, b0s, b0t.
+  static_assert(Epi::kSegs == 1 || Epi::kSegs == 3 || Epi::kSegs == 6, "segment count");
   const uint16_t* A = static_cast<const uint16_t*>(p.a.p[bi]);
   const uint16_t* B = static_cast<const uint16_t*>(p.b0.p[bi]);
-  const uint16_t* A2 = Epi::kSegs == 3 ? static_cast<const uint16_t*>(p.a2.p[bi]) : A;
-  const uint16_t* B2 = Epi::kSegs == 3 ? static_cast<const uint16_t*>(p.b0s.p[bi]) : B;
+  const uint16_t* A2 = Epi::kSegs > 1 ? static_cast<const uint16_t*>(p.a2.p[bi]) : A;
+  const uint16_t* B2 = Epi::kSegs > 1 ? static_cast<const uint16_t*>(p.b0s.p[bi]) : B;
+  const uint16_t* A3 = Epi::kSegs == 6 ? static_cast<const uint16_t*>(p.a3.p[bi]) : A;
+  const uint16_t* B3 = Epi::kSegs == 6 ? static_cast<const uint16_t*>(p.b0t.p[bi]) : B;
   const int64_t lda = p.a.ld, ldb = p.b0.ld;
   const int nks = p.K / BK;                       // k tiles per segment
   const int kt_begin = split * p.kchunk;          // this split's k tiles
   const int kt_end = min(kt_begin + p.kchunk, nks * Epi::kSegs);
-  auto seg_k = [&](int kt) {  // k offset within the segment (no division)
-    if constexpr (Epi::kSegs == 3) kt -= kt >= 2 * nks ? 2 * nks : (kt >= nks ? nks : 0);
-    return kt * BK;
+  auto seg_of = [&](int kt) {  // segment of k tile kt (no division)
+    int sg = 0;
+#pragma unroll
+    for (int t = 1; t < Epi::kSegs; ++t) sg += kt >= t * nks;
+    return sg;
   };
   // byte address of row m0 / n0 of tile kt (uniform: scalar registers)
   auto base_a = [&](int kt) {
-    const uint16_t* src = Epi::kSegs == 3 && kt >= 2 * nks ? A2 : A;
-    return uniform_ptr(reinterpret_cast<const char*>(src + (int64_t)m0 * lda + seg_k(kt)));
+    const int sg = seg_of(kt);
+    const uint16_t* src = sg == 5 ? A3 : (sg == 2 || sg == 4 ? A2 : A);
+    return uniform_ptr(reinterpret_cast<const char*>(src + (int64_t)m0 * lda + (kt - sg * nks) * BK));
   };
   auto base_b = [&](int kt) {
-    const uint16_t* src = Epi::kSegs == 3 && kt >= nks && kt < 2 * nks ? B2 : B;
-    return uniform_ptr(reinterpret_cast<const char*>(src + (int64_t)n0 * ldb + seg_k(kt)));
+    const int sg = seg_of(kt);
+    const uint16_t* src = sg == 3 ? B3 : (sg == 1 || sg == 4 ? B2 : B);
+    return uniform_ptr(reinterpret_cast<const char*>(src + (int64_t)n0 * ldb + (kt - sg * nks) * BK));
   };
 
   floatx16 acc[4][4];

@@ -64,6 +64,13 @@ __global__ __launch_bounds__(256) void reduce_splits_vec_kernel(RedArgs a) {
 #pragma unroll 4
       for (int k = 0; k < a.splits; ++k) s += *reinterpret_cast<const floatx4*>(src + k * a.slice);
       *reinterpret_cast<floatx4*>(out + (int64_t)r * a.out.ld + c) = s;
+      if (a.has_bf16) {
+        uint16_t* ob = static_cast<uint16_t*>(const_cast<void*>(a.out_bf16.p[bi]));
+        const uint16_t h[4] = {to_bf16_bits(s[0]), to_bf16_bits(s[1]), to_bf16_bits(s[2]),
+                               to_bf16_bits(s[3])};
+        *reinterpret_cast<uint2*>(ob + (int64_t)r * a.out_bf16.ld + c) =
+            make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
+      }
       sq += s * s;
     }
   }
@@ -77,6 +84,31 @@ __global__ __launch_bounds__(256) void reduce_splits_vec_kernel(RedArgs a) {
 #pragma unroll
       for (int g = 0; g < 16; ++g) tot += red[g][threadIdx.x];
       a.colsq[bi * a.colsq_member_stride + (int64_t)blockIdx.y * a.cols + cc] = tot;
+    }
+  }
+}
+
+// NP bf16 pieces of an fp32 matrix (x = p0 + p1 (+ p2)); 64 x 64 tiles, each
+// thread four consecutive columns of four rows (ragged edges elementwise).
+template <int NP>
+__global__ __launch_bounds__(256) void split_rows_kernel(SplitRowsArgs a) {
+  const int bi = blockIdx.z;
+  const float* src = static_cast<const float*>(a.src.p[bi]);
+  const int c = blockIdx.x * 64 + (threadIdx.x & 15) * 4;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = blockIdx.y * 64 + (threadIdx.x >> 4) + 16 * q;
+    if (r >= a.rows) break;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (c + t >= a.cols) break;
+      float x = src[(int64_t)r * a.src.ld + c + t];
+#pragma unroll
+      for (int k = 0; k < NP; ++k) {
+        const uint16_t h = to_bf16_bits(x);
+        static_cast<uint16_t*>(const_cast<void*>(a.piece[k].p[bi]))[(int64_t)r * a.piece[k].ld + c + t] = h;
+        x -= bf16_bits_to_f32(h);
+      }
     }
   }
 }
@@ -814,6 +846,14 @@ hipError_t launch_reduce_splits(const RedArgs& a, int members, hipStream_t s) {
                    a.out.vec && (reinterpret_cast<uintptr_t>(a.part) & 15) == 0;
   if (vec) hipLaunchKernelGGL(reduce_splits_vec_kernel, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(reduce_splits_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_rows(const SplitRowsArgs& a, int members, hipStream_t s) {
+  if (a.np != 2 && a.np != 3) return hipErrorInvalidValue;
+  dim3 grid(cdiv(a.cols, 64), cdiv(a.rows, 64), members);
+  if (a.np == 2) hipLaunchKernelGGL(split_rows_kernel<2>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(split_rows_kernel<3>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

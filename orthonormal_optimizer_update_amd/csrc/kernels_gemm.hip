@@ -149,8 +149,9 @@ bool fast_ok(int M, int N, int K, const MatArg& a, const MatArg& b) {
 
 template <class Epi>
 hipError_t run_fast(GemmParams<typename Epi::Args>& p, int members, hipStream_t s) {
-  // the second pieces share the first pieces' row strides
-  if (Epi::kSegs == 3 && (p.a2.ld != p.a.ld || p.b0s.ld != p.b0.ld)) return hipErrorInvalidValue;
+  // every piece shares the first piece's row stride
+  if (Epi::kSegs > 1 && (p.a2.ld != p.a.ld || p.b0s.ld != p.b0.ld)) return hipErrorInvalidValue;
+  if (Epi::kSegs == 6 && (p.a3.ld != p.a.ld || p.b0t.ld != p.b0.ld)) return hipErrorInvalidValue;
   if (p.a.ld > (int64_t{1} << 22) || p.b0.ld > (int64_t{1} << 22)) return hipErrorInvalidValue;
   p.tiles_n = p.N / 256;
   if (p.splits < 1 || p.kchunk < 1) {  // one slice over every k tile
@@ -285,6 +286,21 @@ hipError_t launch_ns_apply(const NsApplyArgs& a, bool out_bf16, int members, hip
                     : ns_apply_t<CfgNsBig, float>(a, members, s);
   return out_bf16 ? ns_apply_t<CfgNsSmall, uint16_t>(a, members, s)
                   : ns_apply_t<CfgNsSmall, float>(a, members, s);
+}
+
+hipError_t launch_fast_split6(const Split6Args& a, int members, hipStream_t s) {
+  GemmParams<EpiFastSplit6F32::Args> p{};
+  p.a = with_rows(a.a[0], a.M);
+  p.a2 = with_rows(a.a[1], a.M);
+  p.a3 = with_rows(a.a[2], a.M);
+  p.b0 = with_rows(a.b[0], a.N);
+  p.b0s = with_rows(a.b[1], a.N);
+  p.b0t = with_rows(a.b[2], a.N);
+  p.e.c = a.out;
+  p.e.split_stride = a.split_stride;
+  p.M = a.M; p.N = a.N; p.K = a.K;
+  p.splits = a.splits; p.kchunk = a.kchunk;
+  return run_fast<EpiFastSplit6F32>(p, members, s);
 }
 
 hipError_t launch_fast_split3(const Split3Args& a, int members, hipStream_t s) {

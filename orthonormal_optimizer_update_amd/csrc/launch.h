@@ -14,6 +14,8 @@ struct RedArgs {
   int64_t slice;              // elements per slice
   int splits, rows, cols;
   MatArg out;                 // fp32 destination
+  MatArg out_bf16;            // optional bf16 copy of the result (has_bf16; vector path only)
+  int has_bf16;
   float* colsq;               // optional per-64-row-block column sums of squares
   int64_t colsq_member_stride;
 };
@@ -97,6 +99,25 @@ struct Split3Args {
   int splits, kchunk;
 };
 hipError_t launch_fast_split3(const Split3Args& a, int members, hipStream_t s);
+// The same over bf16x3 pieces (x = p0 + p1 + p2), six products p0 q0, p0 q1,
+// p1 q0, p0 q2, p1 q1, p2 q0 (fp32-accurate products of fp32 data).
+struct Split6Args {
+  MatArg a[3], b[3];
+  MatArg out;
+  int64_t split_stride;
+  int M, N, K;
+  int splits, kchunk;
+};
+hipError_t launch_fast_split6(const Split6Args& a, int members, hipStream_t s);
+// np (2 or 3) row-major bf16 pieces of an fp32 rows x cols matrix:
+// x = p0 + p1 (+ p2), each piece rounded to nearest even from what the
+// earlier pieces leave.  grid over 64 x 64 tiles.
+struct SplitRowsArgs {
+  MatArg src;
+  MatArg piece[3];
+  int rows, cols, np;
+};
+hipError_t launch_split_rows(const SplitRowsArgs& a, int members, hipStream_t s);
 
 hipError_t launch_reduce_splits(const RedArgs& a, int members, hipStream_t s);
 hipError_t launch_colnorm(const ColnormArgs& a, int members, hipStream_t s);

@@ -92,6 +92,17 @@ bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* p) {
     const size_t pfr = static_cast<size_t>(d.split_fr) * nr * 4;
     if (pfl > part) part = pfl;
     if (pfr > part) part = pfr;
+    // three m x r (and r x r) piece sets fit in one m x n piece buffer
+    d.fast_ortho = 3 * r <= n;
+    if (d.fast_ortho) {
+      choose_split_tiles(6 * r / 64, (m / 256) * (r / 256), d.chunk, &d.split_ap6, &d.kchunk_ap6);
+      choose_split_tiles(3 * r / 64, (m / 256) * (r / 256), d.chunk, &d.split_ap3, &d.kchunk_ap3);
+      choose_split_tiles(3 * m / 64, (r / 256) * (r / 256), d.chunk, &d.split_e, &d.kchunk_e);
+      const size_t pa = static_cast<size_t>(d.split_ap6 > d.split_ap3 ? d.split_ap6 : d.split_ap3) * mr * 4;
+      const size_t pe = static_cast<size_t>(d.split_e) * rr * 4;
+      if (pa > part) part = pa;
+      if (pe > part) part = pe;
+    }
   }
   size_t o = 0;
   d.off_pt = o;    o = align_up(o + mrp * 4);

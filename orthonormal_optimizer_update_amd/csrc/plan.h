@@ -33,6 +33,12 @@ struct DionPlan {
   bool fast_sweeps;
   int split_fl, kchunk_fl, split_fr, kchunk_fr;
   size_t off_bhi, off_blo, off_bhit, off_blot, off_qhit, off_qlot, off_phit, off_plot;
+  // Orthonormalisation products on the 256 x 256 kernel (with fast_sweeps and
+  // 3 r <= n): bf16 pieces in the B-piece buffers, free between the sweeps.
+  int fast_ortho;
+  int split_ap6, kchunk_ap6;  // P1 = P~ T1, six segments of r
+  int split_ap3, kchunk_ap3;  // P = P1 T2, three segments of r
+  int split_e, kchunk_e;      // E = P1^T P1, three segments of m
   size_t member_bytes;       // stride between members
   size_t total_bytes;
 };
