@@ -458,6 +458,106 @@ __global__ __launch_bounds__(256) void gram64_kernel(Gram64Args a) {
       }
 }
 
+// fp64 Gram slices of P (m x r fp32) for r a multiple of 128: 128 x 128 lower
+// tiles (tb <= ta) of r x r, four waves of 64 x 64 (4 x 4 fp64 16 x 16 x 4
+// products), k in tiles of 32 rows of P.  Operand tiles are staged in LDS as
+// fp32 (row pitch 144 floats: the fragment reads of four consecutive k rows
+// fall on distinct banks) and widened to fp64 as fragments are read; the next
+// k step's fragments are read while this step's products run.  Same output as
+// gram64_kernel: slice blockIdx.y of part, element (row, col) at row * r + col.
+// grid (T (T + 1) / 2 tiles, splits, members), T = r / 128.
+__global__ __launch_bounds__(256) void gram64_big_kernel(Gram64Args a) {
+  constexpr int kPitch = 144;
+  __shared__ __attribute__((aligned(16))) float sa[2][32 * kPitch];
+  __shared__ __attribute__((aligned(16))) float sb[2][32 * kPitch];
+  const int member = blockIdx.z;
+  const float* P = static_cast<const float*>(a.p.p[member]);
+  double* part = a.part + member * a.part_member_stride + blockIdx.y * a.slice;
+  const int t = blockIdx.x;
+  int ta = static_cast<int>((sqrt(8.0 * t + 1.0) - 1.0) * 0.5);
+  while ((ta + 1) * (ta + 2) / 2 <= t) ++ta;
+  while (ta * (ta + 1) / 2 > t) --ta;
+  const int tb = t - ta * (ta + 1) / 2;
+  const bool diag = ta == tb;
+  const int a0 = ta * 128, b0 = tb * 128;
+  const int r = a.r;
+  const int kbeg = blockIdx.y * a.kchunk;
+  const int kend = min(a.m, kbeg + a.kchunk);
+  const int nk = kend > kbeg ? (kend - kbeg + 31) / 32 : 0;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wa = wave >> 1, wb = wave & 1;
+  // thread: float4 at column 4 (tid & 31) of k rows (tid >> 5) + 8 q
+  const int lc = (threadIdx.x & 31) * 4, lk = threadIdx.x >> 5;
+  floatx4 va[4], vb[4];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int gk = k0 + lk + 8 * q;
+      const bool ok = gk < kend;
+      const float* row = P + (int64_t)(ok ? gk : kbeg) * a.p.ld;
+      const floatx4 x = *reinterpret_cast<const floatx4*>(row + a0 + lc);
+      va[q] = ok ? x : floatx4{0.f, 0.f, 0.f, 0.f};
+      if (!diag) {
+        const floatx4 y = *reinterpret_cast<const floatx4*>(row + b0 + lc);
+        vb[q] = ok ? y : floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+  auto store = [&](int st) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      *reinterpret_cast<floatx4*>(&sa[st][(lk + 8 * q) * kPitch + lc]) = va[q];
+      if (!diag) *reinterpret_cast<floatx4*>(&sb[st][(lk + 8 * q) * kPitch + lc]) = vb[q];
+    }
+  };
+  doublex4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = doublex4{0.0, 0.0, 0.0, 0.0};
+  if (nk > 0) {
+    load(kbeg);
+    store(0);
+  }
+  const int fk = lane >> 4, fc = lane & 15;
+  for (int kt = 0; kt < nk; ++kt) {
+    __syncthreads();
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) load(kbeg + (kt + 1) * 32);
+    const float* A = sa[cur];
+    const float* B = diag ? sa[cur] : sb[cur];
+    double af[2][4], bf[2][4];
+    auto frags = [&](int buf, int kk) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[buf][i] = static_cast<double>(A[(kk + fk) * kPitch + wa * 64 + i * 16 + fc]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bf[buf][j] = static_cast<double>(B[(kk + fk) * kPitch + wb * 64 + j * 16 + fc]);
+    };
+    frags(0, 0);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      if (s < 7) frags((s + 1) & 1, (s + 1) * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[s & 1][i], bf[s & 1][j], acc[i][j], 0, 0, 0);
+    }
+    if (more) store(cur ^ 1);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = a0 + wa * 64 + i * 16 + fk + 4 * e;
+        const int col = b0 + wb * 64 + j * 16 + fc;
+        part[(int64_t)row * r + col] = acc[i][j][e];
+      }
+}
+
 // Sum the Gram slices and scale to unit diagonal: S = D W D with
 // d_i = 1 / sqrt(W_ii) (lower triangle), zero the inverse buffer, write d.
 __global__ __launch_bounds__(256) void chol_prep_kernel(CholArgs a) {
@@ -916,6 +1016,13 @@ hipError_t launch_ns_linear(const NsPolyArgs& a, int members, hipStream_t s) {
 }
 
 hipError_t launch_gram64(const Gram64Args& a, int splits, int members, hipStream_t s) {
+  // 128 x 128 tiles from r = 1024 on (the plan splits k for them)
+  if (a.r % 128 == 0 && a.r >= 1024 && a.kchunk % 32 == 0 && a.p.vec && a.p.ld % 4 == 0) {
+    const int tb = a.r / 128;
+    dim3 grid(tb * (tb + 1) / 2, splits, members);
+    hipLaunchKernelGGL(gram64_big_kernel, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const int tb = cdiv(a.r, 64);
   dim3 grid(tb * (tb + 1) / 2, splits, members);
   hipLaunchKernelGGL(gram64_kernel, grid, dim3(256), 0, s, a);

@@ -68,6 +68,19 @@ bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* p) {
   choose_split(m, cdiv(n, 128) * cdiv(r, 128), d.chunk, &d.split_right, &d.kchunk_right);
   const int64_t tg = cdiv(r, 64);
   choose_split(m, tg * (tg + 1) / 2, d.chunk, &d.split_gram, &d.kchunk_gram);
+  if (r % 128 == 0 && r >= 1024) {
+    // 128 x 128 fp64 Gram tiles (from 36 tiles on; fewer leave the chip
+    // idle): at most one workgroup per CU (a second round on a few CUs would
+    // double the time), at least eight 32-row k tiles each
+    const int64_t tb = r / 128, tiles = tb * (tb + 1) / 2 * d.chunk;
+    int64_t want = 256 / tiles, cap = m / 256;
+    if (cap < 1) cap = 1;
+    if (want > cap) want = cap;
+    if (want < 1) want = 1;
+    const int64_t kc = cdiv(cdiv(m, want), 32) * 32;
+    d.kchunk_gram = static_cast<int>(kc);
+    d.split_gram = static_cast<int>(cdiv(m, kc));
+  }
   choose_split(m, cdiv(r, 128) * cdiv(r, 128), d.chunk, &d.split_gram2, &d.kchunk_gram2);
   d.nrb = static_cast<int>(cdiv(n, 64));
   d.rp = cdiv(r, 4) * 4;
