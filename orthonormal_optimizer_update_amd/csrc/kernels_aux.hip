@@ -257,7 +257,9 @@ __global__ __launch_bounds__(256) void colnorm_kernel(ColnormArgs a) {
 
 // Partial sums of squares of G: block b of member bi covers rows
 // [b*rows, (b+1)*rows) of the m x n input; threads stride along the row.
-template <typename T>
+// kVec: rows 16-byte aligned and cols a multiple of 16 bytes; each thread then
+// reads 16 bytes (8 bf16 or 4 fp32) per step.
+template <typename T, bool kVec>
 __global__ __launch_bounds__(256) void sumsq_kernel(SumsqArgs a) {
   __shared__ float red[256];
   const int bi = blockIdx.y;
@@ -265,11 +267,33 @@ __global__ __launch_bounds__(256) void sumsq_kernel(SumsqArgs a) {
   const int r0 = blockIdx.x * a.chunk;
   const int r1 = min(a.g.rows, r0 + static_cast<int>(a.chunk));
   float s = 0.f;
-  for (int r = r0; r < r1; ++r) {
-    const T* row = g + (int64_t)r * a.g.ld;
-    for (int c = threadIdx.x; c < a.g.cols; c += 256) {
-      const float v = load_as_f32<T>(row, c);
-      s += v * v;
+  if constexpr (kVec) {
+    constexpr int kE = 16 / sizeof(T);
+    for (int r = r0; r < r1; ++r) {
+      const T* row = g + (int64_t)r * a.g.ld;
+      for (int c = threadIdx.x * kE; c < a.g.cols; c += 256 * kE) {
+        const uint4 w = *reinterpret_cast<const uint4*>(row + c);
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if constexpr (sizeof(T) == 2) {
+            const float lo = __uint_as_float(u[q] << 16), hi = __uint_as_float(u[q] & 0xffff0000u);
+            s += lo * lo;
+            s += hi * hi;
+          } else {
+            const float v = __uint_as_float(u[q]);
+            s += v * v;
+          }
+        }
+      }
+    }
+  } else {
+    for (int r = r0; r < r1; ++r) {
+      const T* row = g + (int64_t)r * a.g.ld;
+      for (int c = threadIdx.x; c < a.g.cols; c += 256) {
+        const float v = load_as_f32<T>(row, c);
+        s += v * v;
+      }
     }
   }
   red[threadIdx.x] = s;
@@ -975,8 +999,19 @@ hipError_t launch_colnorm(const ColnormArgs& a, int members, hipStream_t s) {
 
 hipError_t launch_sumsq(const SumsqArgs& a, int nblocks, int members, bool bf16, hipStream_t s) {
   dim3 grid(nblocks, members);
-  if (bf16) hipLaunchKernelGGL(sumsq_kernel<uint16_t>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(sumsq_kernel<float>, grid, dim3(256), 0, s, a);
+  // 16-byte loads need every row of every member on a 16-byte boundary
+  const size_t esz = bf16 ? 2 : 4;
+  bool vec = (static_cast<size_t>(a.g.cols) * esz) % 16 == 0 &&
+             (static_cast<size_t>(a.g.ld) * esz) % 16 == 0;
+  for (int i = 0; i < members && vec; ++i)
+    vec = (reinterpret_cast<uintptr_t>(a.g.p[i]) & 15) == 0;
+  if (bf16) {
+    if (vec) hipLaunchKernelGGL((sumsq_kernel<uint16_t, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((sumsq_kernel<uint16_t, false>), grid, dim3(256), 0, s, a);
+  } else {
+    if (vec) hipLaunchKernelGGL((sumsq_kernel<float, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((sumsq_kernel<float, false>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
