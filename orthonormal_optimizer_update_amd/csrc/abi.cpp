@@ -85,6 +85,16 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     const MatArg tQb = ws_table(base, mb, pl.off_qb, nb, pl.rpb, ni, r, 2, 16);
     float* part_f = reinterpret_cast<float*>(base + pl.off_part);
     double* part_d = reinterpret_cast<double*>(base + pl.off_part);
+    // bf16 pieces of the orthonormalisation products on the 256 x 256 kernel:
+    // A pieces (m x r) in the row-major B-piece buffer and B pieces (r x r) in
+    // the second one, both free once sweep 1 is done (3 r <= n; m, r multiples
+    // of 256, so every piece starts 256-byte aligned).
+    MatArg ap[3], bp[3];
+    for (int k = 0; k < 3; ++k) {
+      ap[k] = ws_table(base, mb, pl.off_bhi + k * static_cast<size_t>(mi) * r * 2, nb, r, mi, r, 2, 16);
+      bp[k] = ws_table(base, mb, pl.off_blo + k * static_cast<size_t>(r) * r * 2, nb, r, r, r, 2, 16);
+    }
+    bool pt_pieces = false;  // P_tilde's bf16x3 pieces already in ap
 
     // Sweeps on the 256 x 256 kernel over bf16x2 pieces (bf16 weights, sizes
     // multiples of 256, 16-byte rows of M and Q; G rows 8-byte aligned).
@@ -111,7 +121,17 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       l3.M = mi; l3.N = r; l3.K = ni;
       l3.splits = pl.split_fl; l3.kchunk = pl.kchunk_fl;
       ORTHO_TRY(launch_fast_split3(l3, nb, s));
-      if (pl.split_fl > 1) {
+      if (pl.split_fl > 1 && pl.fast_ortho) {
+        // the reduce also writes the bf16x3 pieces of P_tilde for P1 = P~ T1
+        RedPiecesArgs ra{};
+        ra.part = part_f; ra.part_member_stride = static_cast<int64_t>(mb / 4);
+        ra.slice = m * r; ra.splits = pl.split_fl; ra.rows = mi; ra.cols = r;
+        ra.out = tPt; ra.has_out = 1;
+        for (int k = 0; k < 3; ++k) ra.piece[k] = ap[k];
+        ra.np = 3;
+        ORTHO_TRY(launch_reduce_pieces(ra, nb, s));
+        pt_pieces = true;
+      } else if (pl.split_fl > 1) {
         RedArgs ra{};
         ra.part = part_f; ra.part_member_stride = static_cast<int64_t>(mb / 4);
         ra.slice = m * r; ra.splits = pl.split_fl; ra.rows = mi; ra.cols = r;
@@ -155,24 +175,18 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     ORTHO_TRY(launch_cholesky_inverse(ca, tt, static_cast<int64_t>(mb / 4), nb, s));
     if (fast_sw && pl.fast_ortho) {
       // The same three products on the 256 x 256 kernel over bf16 pieces
-      // (split-K, fixed-order reduce).  A pieces go to the row-major B-piece
-      // buffer and B pieces to the second one: sweep 1 is done with both.
-      // (m, r multiples of 256: every piece starts 256-byte aligned)
-      const size_t mr2 = static_cast<size_t>(mi) * r * 2;
-      const size_t rr2 = static_cast<size_t>(r) * r * 2;
-      MatArg ap[3], bp[3];
-      for (int k = 0; k < 3; ++k) {
-        ap[k] = ws_table(base, mb, pl.off_bhi + k * mr2, nb, r, mi, r, 2, 16);
-        bp[k] = ws_table(base, mb, pl.off_blo + k * rr2, nb, r, r, r, 2, 16);
-      }
+      // (split-K, fixed-order reduces that also write the next product's
+      // pieces).
       const MatArg tPhiT = ws_table(base, mb, pl.off_phit, nb, m, r, mi, 2, 16);
       const MatArg tPloT = ws_table(base, mb, pl.off_plot, nb, m, r, mi, 2, 16);
       const int64_t mr = static_cast<int64_t>(mi) * r;
       // P1 = P~ T1, six products of bf16x3 pieces
-      SplitRowsArgs sp{};
-      sp.src = tPt; sp.piece[0] = ap[0]; sp.piece[1] = ap[1]; sp.piece[2] = ap[2];
-      sp.rows = mi; sp.cols = r; sp.np = 3;
-      ORTHO_TRY(launch_split_rows(sp, nb, s));
+      if (!pt_pieces) {
+        SplitRowsArgs sp{};
+        sp.src = tPt; sp.piece[0] = ap[0]; sp.piece[1] = ap[1]; sp.piece[2] = ap[2];
+        sp.rows = mi; sp.cols = r; sp.np = 3;
+        ORTHO_TRY(launch_split_rows(sp, nb, s));
+      }
       SplitRowsArgs st{};
       st.src = tTt; st.piece[0] = bp[0]; st.piece[1] = bp[1]; st.piece[2] = bp[2];
       st.rows = r; st.cols = r; st.np = 3;
@@ -182,15 +196,14 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       a6.out = tPart; a6.split_stride = mr;
       a6.M = mi; a6.N = r; a6.K = r; a6.splits = pl.split_ap6; a6.kchunk = pl.kchunk_ap6;
       ORTHO_TRY(launch_fast_split6(a6, nb, s));
-      RedArgs rp1{};
+      // P1 itself is not kept: the reduce writes its bf16x2 pieces, row-major
+      // for P = P1 T2 and transposed for E = P1^T P1 (pass 2, see below).
+      RedPiecesArgs rp1{};
       rp1.part = part_f; rp1.part_member_stride = static_cast<int64_t>(mb / 4);
       rp1.slice = mr; rp1.splits = pl.split_ap6; rp1.rows = mi; rp1.cols = r;
-      rp1.out = tP1; rp1.has_bf16 = 0; rp1.colsq = nullptr; rp1.colsq_member_stride = 0;
-      ORTHO_TRY(launch_reduce_splits(rp1, nb, s));
-      // Pass 2 (see below): E = P1^T P1 over m, bf16x3 of the transposed P1
-      SplitTArgs pt{};
-      pt.src = tP1; pt.hit = tPhiT; pt.lot = tPloT; pt.rows = mi; pt.cols = r;
-      ORTHO_TRY(launch_split_t(pt, nb, s));
+      rp1.piece[0] = ap[0]; rp1.piece[1] = ap[1]; rp1.np = 2;
+      rp1.tpiece[0] = tPhiT; rp1.tpiece[1] = tPloT; rp1.has_t = 1;
+      ORTHO_TRY(launch_reduce_pieces(rp1, nb, s));
       Split3Args e3{};
       e3.ahi = tPhiT; e3.alo = tPloT; e3.bhi = tPhiT; e3.blo = tPloT;
       e3.out = tPart; e3.split_stride = static_cast<int64_t>(r) * r;
@@ -198,9 +211,8 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       ORTHO_TRY(launch_fast_split3(e3, nb, s));
       ORTHO_TRY(launch_correction(part_f, static_cast<int64_t>(mb / 4), static_cast<int64_t>(r) * r,
                                   pl.split_e, r, tt, static_cast<int64_t>(mb / 4), nb, s));
-      // P = P1 T2, bf16x3; the bf16 copy of P feeds the last sweep
-      sp.src = tP1; sp.np = 2;
-      ORTHO_TRY(launch_split_rows(sp, nb, s));
+      // P = P1 T2, bf16x3; the bf16 copy and the transposed pieces of P feed
+      // sweeps 2 and 3
       st.np = 2;
       ORTHO_TRY(launch_split_rows(st, nb, s));
       Split3Args a3{};
@@ -208,9 +220,12 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       a3.out = tPart; a3.split_stride = mr;
       a3.M = mi; a3.N = r; a3.K = r; a3.splits = pl.split_ap3; a3.kchunk = pl.kchunk_ap3;
       ORTHO_TRY(launch_fast_split3(a3, nb, s));
-      RedArgs rp2 = rp1;
-      rp2.splits = pl.split_ap3; rp2.out = tPt; rp2.out_bf16 = tPb; rp2.has_bf16 = 1;
-      ORTHO_TRY(launch_reduce_splits(rp2, nb, s));
+      RedPiecesArgs rp2{};
+      rp2.part = part_f; rp2.part_member_stride = static_cast<int64_t>(mb / 4);
+      rp2.slice = mr; rp2.splits = pl.split_ap3; rp2.rows = mi; rp2.cols = r;
+      rp2.out = tPt; rp2.has_out = 1; rp2.out_bf16 = tPb; rp2.has_bf16 = 1;
+      rp2.tpiece[0] = tPhiT; rp2.tpiece[1] = tPloT; rp2.has_t = 1;
+      ORTHO_TRY(launch_reduce_pieces(rp2, nb, s));
     } else {
     ApplyArgs aa{};
     aa.pt = tPt; aa.tt = tTt; aa.out = tP1; aa.M = mi; aa.r = r;
@@ -236,9 +251,11 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       const MatArg tBloT = ws_table(base, mb, pl.off_blot, nb, m, ni, mi, 2, 16);
       const MatArg tPhiT = ws_table(base, mb, pl.off_phit, nb, m, r, mi, 2, 16);
       const MatArg tPloT = ws_table(base, mb, pl.off_plot, nb, m, r, mi, 2, 16);
-      SplitTArgs pa{};
-      pa.src = tPt; pa.hit = tPhiT; pa.lot = tPloT; pa.rows = mi; pa.cols = r;
-      ORTHO_TRY(launch_split_t(pa, nb, s));
+      if (!pl.fast_ortho) {  // else the last orthonormalisation reduce wrote them
+        SplitTArgs pa{};
+        pa.src = tPt; pa.hit = tPhiT; pa.lot = tPloT; pa.rows = mi; pa.cols = r;
+        ORTHO_TRY(launch_split_t(pa, nb, s));
+      }
       Split3Args r3{};
       r3.ahi = tBhiT; r3.alo = tBloT; r3.bhi = tPhiT; r3.blo = tPloT;
       r3.out = tPart; r3.split_stride = n * r;

@@ -173,6 +173,69 @@ __device__ __forceinline__ void split_tile(const float* src, int64_t lds_, const
   }
 }
 
+// Split-K sum of a 64 x 64 tile, then its bf16 forms (see RedPiecesArgs).
+// Thread t: columns 4 (t & 15) .. + 3 of rows (t >> 4) + 16 q; the transposed
+// pieces are staged in LDS and written 4 elements per lane.
+__global__ __launch_bounds__(256) void reduce_pieces_kernel(RedPiecesArgs a) {
+  __shared__ uint16_t th[64][68];
+  __shared__ uint16_t tl[64][68];
+  const int bi = blockIdx.z;
+  const float* part = a.part + bi * a.part_member_stride;
+  const int cl = (threadIdx.x & 15) * 4;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int rl = (threadIdx.x >> 4) + 16 * q;
+    const int64_t row = r0 + rl;
+    const float* src = part + row * a.cols + c0 + cl;
+    floatx4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int k = 0; k < a.splits; ++k) v += *reinterpret_cast<const floatx4*>(src + k * a.slice);
+    if (a.has_out)
+      *reinterpret_cast<floatx4*>(static_cast<float*>(const_cast<void*>(a.out.p[bi])) + row * a.out.ld + c0 + cl) = v;
+    if (a.has_bf16) {
+      const uint16_t h[4] = {to_bf16_bits(v[0]), to_bf16_bits(v[1]), to_bf16_bits(v[2]), to_bf16_bits(v[3])};
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(const_cast<void*>(a.out_bf16.p[bi])) + row * a.out_bf16.ld + c0 + cl) = pack4(h);
+    }
+    floatx4 x = v;
+    for (int pc = 0; pc < a.np; ++pc) {
+      uint16_t h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[e] = to_bf16_bits(x[e]);
+        x[e] -= bf16_bits_to_f32(h[e]);
+      }
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(const_cast<void*>(a.piece[pc].p[bi])) + row * a.piece[pc].ld + c0 + cl) = pack4(h);
+    }
+    if (a.has_t) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bf16 bh, bl;
+        split_bf16(v[e], bh, bl);
+        th[cl + e][rl] = __builtin_bit_cast(uint16_t, bh);
+        tl[cl + e][rl] = __builtin_bit_cast(uint16_t, bl);
+      }
+    }
+  }
+  if (!a.has_t) return;  // uniform over the grid
+  __syncthreads();
+  uint16_t* hit = static_cast<uint16_t*>(const_cast<void*>(a.tpiece[0].p[bi]));
+  uint16_t* lot = static_cast<uint16_t*>(const_cast<void*>(a.tpiece[1].p[bi]));
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int j = (threadIdx.x >> 4) + 16 * q;  // row of the transposed tile
+    const int i4 = (threadIdx.x & 15) * 4;
+    uint16_t h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h[e] = th[j][i4 + e];
+      l[e] = tl[j][i4 + e];
+    }
+    *reinterpret_cast<uint2*>(hit + (int64_t)(c0 + j) * a.tpiece[0].ld + r0 + i4) = pack4(h);
+    *reinterpret_cast<uint2*>(lot + (int64_t)(c0 + j) * a.tpiece[1].ld + r0 + i4) = pack4(l);
+  }
+}
+
 __global__ __launch_bounds__(256) void split_sum_kernel(SplitSumArgs a) {
   const int bi = blockIdx.z;
   split_tile<true>(static_cast<const float*>(a.m.p[bi]), a.m.ld,
@@ -970,6 +1033,12 @@ hipError_t launch_reduce_splits(const RedArgs& a, int members, hipStream_t s) {
                    a.out.vec && (reinterpret_cast<uintptr_t>(a.part) & 15) == 0;
   if (vec) hipLaunchKernelGGL(reduce_splits_vec_kernel, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(reduce_splits_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_pieces(const RedPiecesArgs& a, int members, hipStream_t s) {
+  if (a.rows % 64 != 0 || a.cols % 64 != 0 || a.np < 0 || a.np > 3) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(reduce_pieces_kernel, dim3(a.cols / 64, a.rows / 64, members), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -118,6 +118,25 @@ struct SplitRowsArgs {
   int rows, cols, np;
 };
 hipError_t launch_split_rows(const SplitRowsArgs& a, int members, hipStream_t s);
+// Sum of split-K slices (as RedArgs, rows x cols with ld = cols; rows and cols
+// multiples of 64, 16-byte aligned rows), written as any of: fp32 (has_out),
+// bf16 (has_bf16), np (2 or 3) row-major bf16 pieces, and the transposed
+// bf16x2 pieces (has_t; cols x rows).
+struct RedPiecesArgs {
+  const float* part;
+  int64_t part_member_stride;
+  int64_t slice;
+  int splits, rows, cols;
+  MatArg out;
+  int has_out;
+  MatArg out_bf16;
+  int has_bf16;
+  MatArg piece[3];
+  int np;
+  MatArg tpiece[2];
+  int has_t;
+};
+hipError_t launch_reduce_pieces(const RedPiecesArgs& a, int members, hipStream_t s);
 
 hipError_t launch_reduce_splits(const RedArgs& a, int members, hipStream_t s);
 hipError_t launch_colnorm(const ColnormArgs& a, int members, hipStream_t s);
