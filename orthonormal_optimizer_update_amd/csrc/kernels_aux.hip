@@ -676,6 +676,10 @@ __global__ __launch_bounds__(256) void chol_prep_kernel(CholArgs a) {
 // numerical rank deficiency and replaced by it.
 constexpr double kPivMin = 1e-14;
 
+// Pitch (doubles) of the 64 x 64 fp64 LDS tiles of the Cholesky kernels: rows
+// start 16-byte aligned.
+constexpr int kCP = 66;
+
 // Broadcast lane `lane` (wave-uniform) of a double to the whole wave.
 __device__ __forceinline__ double readlane_f64(double v, int lane) {
   const uint64_t bits = __builtin_bit_cast(uint64_t, v);
@@ -684,39 +688,141 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
   return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-// 1/sqrt(x) for x > 0: hardware estimate refined by two Newton steps.
+// 1/x and 1/sqrt(x) for x > 0: hardware estimate and one Newton step (relative
+// error about the square of the estimate's, far below what the Gram's
+// conditioning can use).
+__device__ __forceinline__ double rcp_f64(double x) {
+  const double y = __builtin_amdgcn_rcp(x);
+  return y * fma(-x, y, 2.0);
+}
 __device__ __forceinline__ double rsqrt_f64(double x) {
-  // hardware estimate, then one Newton step (relative error about the square
-  // of the estimate's, far below what the Gram's conditioning can use)
   const double y = __builtin_amdgcn_rsq(x);
   return y * (1.5 - 0.5 * x * y * y);
 }
 
+// One 16 x 16 tile of a phase's rank-8 update in chol_diag_block: y = 0 for
+// the factor L, 1 for the inverse Y; tile row and column.
+struct CholTile {
+  int y, tr, tc;
+};
+
+// Tiles of phase p: the L-tiles tc0 <= tc <= tr (tc0 = (8p + 8) / 16, the
+// tile column holding the first column past panel p) in row order, then the
+// Y-tiles on tile rows 8p/16..3 and tile columns 0..(8p - 1)/16.  At most ten.
+__host__ __device__ constexpr int chol_ntile(int p) {
+  const int tl = 4 - ((8 * p + 8) >> 4);
+  const int ncy = p > 0 ? ((8 * p - 1) >> 4) + 1 : 0;
+  return tl * (tl + 1) / 2 + (4 - ((8 * p) >> 4)) * ncy;
+}
+__host__ __device__ constexpr CholTile chol_tile(int p, int s) {
+  const int tc0 = (8 * p + 8) >> 4, tl = 4 - tc0, nl = tl * (tl + 1) / 2;
+  if (s < nl) {
+    int ta = 0;
+    while ((ta + 1) * (ta + 2) / 2 <= s) ++ta;
+    return CholTile{0, tc0 + ta, tc0 + s - ta * (ta + 1) / 2};
+  }
+  const int ncy = ((8 * p - 1) >> 4) + 1, u = s - nl;
+  return CholTile{1, ((8 * p) >> 4) + u / ncy, u % ncy};
+}
+
+// Operands of tile S of phase P (lane: (lane & 15, lane >> 4) is (row, k) of
+// the left operand and (column, row) of the target):
+//   L-tile: L[i][c] -= sum over k in panel P of L[i][k] L[c][k]
+//   Y-tile: Y[i][c] -= sum over k in panel P - 1 of L[i][k] X[k][c]
+// (ly: L at 0, Y at 64 rows; pitch kCP.)  Every offset is a constant.
+template <int P, int S>
+__device__ __forceinline__ void chol_tile_load(const double* ly, int lane_a, int lane_t, double* av,
+                                               double* bv, double* old) {
+  constexpr CholTile t = chol_tile(P, S);
+  constexpr int kb = 8 * P - 8 * t.y;
+  constexpr int offa = t.tr * 16 * kCP + kb;
+  av[0] = ly[lane_a + offa];
+  av[1] = ly[lane_a + offa + 4];
+  if constexpr (t.y != 0) {
+    constexpr int offb = (64 + kb) * kCP + t.tc * 16;
+    bv[0] = ly[lane_t + offb];
+    bv[1] = ly[lane_t + offb + 4 * kCP];
+  } else {
+    constexpr int offb = t.tc * 16 * kCP + kb;
+    bv[0] = ly[lane_a + offb];
+    bv[1] = ly[lane_a + offb + 4];
+  }
+  constexpr int offt = (t.y * 64 + t.tr * 16) * kCP + t.tc * 16;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) old[e] = ly[lane_t + offt + e * 4 * kCP];
+}
+
+// Product and masked write-back of tile S of phase P: an element changes
+// where the update applies (L: row >= pe, pe <= col <= row; Y: row >= 8P,
+// col < 8P), so no element outside the update is written.
+template <int P, int S>
+__device__ __forceinline__ void chol_tile_apply(double* ly, int lane, int lane_t, const double* av,
+                                                const double* bv, const double* old) {
+  constexpr CholTile t = chol_tile(P, S);
+  constexpr int j0 = 8 * P, pe = j0 + 8;
+  constexpr int offt = (t.y * 64 + t.tr * 16) * kCP + t.tc * 16;
+  doublex4 acc = {0.0, 0.0, 0.0, 0.0};
+  acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av[0], bv[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av[1], bv[1], acc, 0, 0, 0);
+  const int col = t.tc * 16 + (lane & 15);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int row = t.tr * 16 + (lane >> 4) + 4 * e;
+    const bool ok = t.y != 0 ? (row >= j0 && col < j0) : (row >= pe && col >= pe && col <= row);
+    if (ok) ly[lane_t + offt + e * 4 * kCP] = old[e] - acc[e];
+  }
+}
+
+// Tiles W, W + 4, W + 8 of phase P (wave W): all loads, then the products.
+template <int P, int W>
+__device__ __forceinline__ void chol_tiles(double* ly, int lane) {
+  constexpr int nt = chol_ntile(P);
+  const int lane_a = (lane & 15) * kCP + (lane >> 4), lane_t = (lane >> 4) * kCP + (lane & 15);
+  double av[3][2], bv[3][2], old[3][4];
+  if constexpr (W < nt) chol_tile_load<P, W>(ly, lane_a, lane_t, av[0], bv[0], old[0]);
+  if constexpr (W + 4 < nt) chol_tile_load<P, W + 4>(ly, lane_a, lane_t, av[1], bv[1], old[1]);
+  if constexpr (W + 8 < nt) chol_tile_load<P, W + 8>(ly, lane_a, lane_t, av[2], bv[2], old[2]);
+  if constexpr (W < nt) chol_tile_apply<P, W>(ly, lane, lane_t, av[0], bv[0], old[0]);
+  if constexpr (W + 4 < nt) chol_tile_apply<P, W + 4>(ly, lane, lane_t, av[1], bv[1], old[1]);
+  if constexpr (W + 8 < nt) chol_tile_apply<P, W + 8>(ly, lane, lane_t, av[2], bv[2], old[2]);
+}
+
+template <int P>
+__device__ __forceinline__ void chol_tiles_wave(double* ly, int lane, int wave) {
+  if (wave == 0) chol_tiles<P, 0>(ly, lane);
+  else if (wave == 1) chol_tiles<P, 1>(ly, lane);
+  else if (wave == 2) chol_tiles<P, 2>(ly, lane);
+  else chol_tiles<P, 3>(ly, lane);
+}
+
 // Factor the nb x nb diagonal block kb of S (S_kk = L_kk L_kk^T) and invert
-// L_kk, both in LDS, then write L_kk into S and L_kk^{-1} into block (kb, kb)
-// of X.  Blocked by 8-column panels:
-//   wave 0 factors the panel in registers (lane i holds row i; pivots and
-//   column entries move by readlane) and finishes the matching 8-row block of
-//   the inverse (lane c holds column c of Y, forward substitution with L_pp);
-//   then the four waves apply the two rank-8 updates with that panel as 16 x 16
-//   fp64 MFMA tiles: L[i][c] -= L[i][p] L[c][p]^T (trailing block) and
-//   Y[i][c] -= L[i][p] X[p][c] (rows below the panel), with Y starting as the
-//   identity.  A tile column c takes its right operand from L (c at or beyond
-//   the panel's end) or from the finished inverse rows (c before it); the two
-//   regions written are disjoint from the panel columns and rows read.
-__device__ void chol_diag_block(const CholArgs& a, int kb, int member, double (*L)[65],
-                                double (*Y)[65]) {
+// L_kk in LDS (LY[0] = L, LY[1] = Y, dinv: 64 doubles), then write L_kk into S
+// and L_kk^{-1} into block (kb, kb) of X.  A block smaller than 64 is padded
+// with the identity, which factors to itself.  Right-looking over 8-column
+// panels p, one phase each:
+//   wave 0 factors panel p in registers (lane i holds row i; pivots and column
+//   entries move by readlane) while wave 1 solves block row p - 1 of the
+//   inverse, X_{p-1} = L_{p-1,p-1}^{-1} Y_{p-1} (lane c holds column c);
+//   then the four waves apply the rank-8 updates as 16 x 16 fp64 MFMA tiles
+//   (chol_tile_load): of L by panel p beyond it, and of Y by X_{p-1} below
+//   it, Y starting as the identity.  The tile work of each (phase, wave) is
+//   compiled with constant offsets.
+__device__ void chol_diag_block(const CholArgs& a, int kb, int member, double (*LY)[64][kCP],
+                                double* dinv) {
   double* S = a.s + member * a.mat_stride;
   double* X = a.x + member * a.mat_stride;
   const int r = a.r;
   const int o = kb * 64;
   const int nb = min(64, r - o);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  double (*L)[kCP] = LY[0];
+  double (*Y)[kCP] = LY[1];
+  double* ly = &LY[0][0][0];
   // element (gi, gj) = (q * 4 + wave, lane): each wave moves whole 64-wide
-  // rows (coalesced, and bank-conflict free with the 65-double pitch)
-  // Every load is issued before any is used (clamped addresses; the triangle
-  // is cut with a bit mask, so no load is predicated and stale words in the
-  // upper triangle, NaN patterns included, never reach the arithmetic).
+  // rows.  Every load is issued before any is used (clamped addresses; the
+  // triangle is cut with a select, so stale words in the upper triangle, NaN
+  // patterns included, never reach the arithmetic).
   uint64_t v[16];
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
@@ -726,117 +832,77 @@ __device__ void chol_diag_block(const CholArgs& a, int kb, int member, double (*
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int gi = q * 4 + wave, gj = lane;
-    const uint64_t keep = (gi < nb && gj <= gi) ? ~0ull : 0ull;
-    L[gi][gj] = __longlong_as_double(static_cast<long long>(v[q] & keep));
-    Y[gi][gj] = (gi == gj && gi < nb) ? 1.0 : 0.0;
+    const double id = gi == gj ? 1.0 : 0.0;
+    L[gi][gj] = (gi < nb && gj <= gi) ? __longlong_as_double(static_cast<long long>(v[q])) : id;
+    Y[gi][gj] = id;
   }
   bool shifted = false;
-  for (int j0 = 0; j0 < nb; j0 += 8) {
+  // block row q of the inverse, by wave 1 (lane c: column c)
+  auto solve_rows = [&](int q) {
+    const int jq = q * 8;
+    double y[8], lq[8][8], dq[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      y[t] = Y[jq + t][lane];
+      dq[t] = dinv[jq + t];
+#pragma unroll
+      for (int u = 0; u < t; ++u) lq[t][u] = L[jq + t][jq + u];
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      double acc = y[t];
+#pragma unroll
+      for (int u = 0; u < t; ++u) acc = fma(-lq[t][u], y[u], acc);
+      y[t] = acc * dq[t];
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) Y[jq + t][lane] = y[t];
+  };
+  for (int p = 0; p < 8; ++p) {
+    const int j0 = p * 8;
     __syncthreads();
     if (wave == 0) {
       double pc[8], invd[8];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        pc[c] = L[lane][j0 + c];
-        invd[c] = 0.0;
-      }
+      for (int c = 0; c < 8; ++c) pc[c] = L[lane][j0 + c];
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const int jc = j0 + c;
-        // Branch-free column step.  A padding column (jc >= nb, all zero)
-        // takes pivot 1 and changes nothing that is stored.
-        const bool live = jc < nb;
-        double piv = readlane_f64(pc[c], jc);
-        if (live && !(piv > kPivMin) && piv == piv) {
-          piv = kPivMin;
-          shifted = true;
-        }
-        piv = live ? piv : 1.0;
-        const double inv = rsqrt_f64(piv);
-        invd[c] = inv;
-        // The rest of the panel is updated with the unscaled column and
-        // 1/pivot, l_i l_j = a_i a_j / piv, so the broadcasts need not wait
-        // for the scaling.  Every lane is updated: on rows at or above jc the
-        // touched entries lie above the diagonal and are zeroed when their own
-        // column is scaled.
-        const double d = inv * inv;
+        const double a0 = readlane_f64(pc[c], jc);
+        shifted |= !(a0 > kPivMin);
+        // maxNum: a NaN pivot is replaced too (and flagged)
+        const double piv = fmax(a0, kPivMin);
+        const double rs = rsqrt_f64(piv);
+        invd[c] = rs;
+        // scaled column; rows above jc hold entries above the diagonal: zeroed
+        const double x = lane == jc ? piv : pc[c];
+        pc[c] = lane >= jc ? x * rs : 0.0;
 #pragma unroll
-        for (int c2 = c + 1; c2 < 8; ++c2) {
-          const double acj = readlane_f64(pc[c], j0 + c2);
-          pc[c2] -= pc[c] * (acj * d);
-        }
-        pc[c] = lane == jc ? piv * inv : (lane > jc ? pc[c] * inv : 0.0);
-      }
-      // Block row j0/8 of the inverse: X_p = L_pp^{-1} Y_p, lane = column.
-      double y[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) y[t] = Y[j0 + t][lane];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        double acc = y[t];
-#pragma unroll
-        for (int u = 0; u < t; ++u) acc -= readlane_f64(pc[u], j0 + t) * y[u];
-        y[t] = acc * invd[t];
+        for (int c2 = c + 1; c2 < 8; ++c2) pc[c2] = fma(-pc[c], readlane_f64(pc[c], j0 + c2), pc[c2]);
       }
 #pragma unroll
       for (int c = 0; c < 8; ++c) L[lane][j0 + c] = pc[c];
+      if (lane == 0) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) Y[j0 + t][lane] = y[t];
+        for (int c = 0; c < 8; ++c) dinv[j0 + c] = invd[c];
+      }
+    } else if (wave == 1 && p > 0) {
+      solve_rows(p - 1);
     }
     __syncthreads();
-    const int pe = j0 + 8;
-    if (pe < nb) {
-      // lower 16 x 16 tiles (tr, tc), tc <= tr, with rows reaching past the panel
-      const int tr0 = pe >> 4;
-      const int ntr = 4 - tr0;
-      const int npairs = ntr * tr0 + ntr * (ntr + 1) / 2;
-      // at most 10 tiles, so at most three per wave: unrolled, so that the
-      // three product chains overlap
-#pragma unroll
-      for (int qq = 0; qq < 3; ++qq) {
-        const int q = wave + 4 * qq;
-        if (q >= npairs) break;
-        int tr, tc;
-        if (q < ntr * tr0) {
-          tr = tr0 + q / tr0;
-          tc = q % tr0;
-        } else {
-          int u = q - ntr * tr0, t = 0;
-          while (u > t) { u -= t + 1; ++t; }
-          tr = tr0 + t;
-          tc = tr0 + u;
-        }
-        doublex4 acc = {0.0, 0.0, 0.0, 0.0};
-        const int arow = tr * 16 + (lane & 15);
-        const int bcol = tc * 16 + (lane & 15);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int k = j0 + ks * 4 + (lane >> 4);
-          const double av = L[arow][k];
-          const double bv = bcol >= pe ? L[bcol][k] : Y[k][bcol];
-          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
-        }
-        // Branch-free read-modify-write: every lane reads its four targets,
-        // then writes them back, changed where the update applies.  Elements
-        // left unchanged are owned by no other tile, so the write-back of
-        // their own value races with nothing.
-        double* dst[4];
-        double old[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int gi = tr * 16 + (lane >> 4) + 4 * e;
-          dst[e] = bcol >= pe ? &L[gi][bcol] : &Y[gi][bcol];
-          old[e] = *dst[e];
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int gi = tr * 16 + (lane >> 4) + 4 * e;
-          const bool upd = gi >= pe && gi < nb && (bcol < pe || bcol <= gi);
-          *dst[e] = upd ? old[e] - acc[e] : old[e];
-        }
-      }
+    switch (p) {
+      case 0: chol_tiles_wave<0>(ly, lane, wave); break;
+      case 1: chol_tiles_wave<1>(ly, lane, wave); break;
+      case 2: chol_tiles_wave<2>(ly, lane, wave); break;
+      case 3: chol_tiles_wave<3>(ly, lane, wave); break;
+      case 4: chol_tiles_wave<4>(ly, lane, wave); break;
+      case 5: chol_tiles_wave<5>(ly, lane, wave); break;
+      case 6: chol_tiles_wave<6>(ly, lane, wave); break;
+      default: chol_tiles_wave<7>(ly, lane, wave); break;
     }
   }
+  __syncthreads();
+  if (wave == 1) solve_rows(7);
   __syncthreads();
   if (shifted && threadIdx.x == 0 && a.status) atomicOr(a.status, 1);
 #pragma unroll
@@ -850,9 +916,9 @@ __device__ void chol_diag_block(const CholArgs& a, int kb, int member, double (*
 }
 
 __global__ __launch_bounds__(256) void chol_diag_kernel(CholArgs a, int kb) {
-  __shared__ double L[64][65];
-  __shared__ double Y[64][65];
-  chol_diag_block(a, kb, blockIdx.x, L, Y);
+  __shared__ double LY[2][64][kCP];
+  __shared__ double dinv[64];
+  chol_diag_block(a, kb, blockIdx.x, LY, dinv);
 }
 
 // acc (64 x 64 tile, four waves of 32 x 32) = A * B^T (TRANS_B) or A * B with
@@ -861,7 +927,7 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(CholArgs a, int kb) {
 // wa*32 + i*16 + l/16 + 4e, column wb*32 + j*16 + l%16 (wa, wb: wave quadrant).
 template <bool TRANS_B>
 __device__ void tile_gemm64(const double* A, const double* B, int r, int ar, int ac, int br,
-                            int bc, double (*sA)[65], double (*sB)[65], doublex4 acc[2][2]) {
+                            int bc, double (*sA)[kCP], double (*sB)[kCP], doublex4 acc[2][2]) {
   double va[16], vb[16];
 #pragma unroll
   for (int q = 0; q < 16; ++q) {  // all 32 loads in flight before any LDS store
@@ -927,8 +993,9 @@ __device__ __forceinline__ void tile_store64(double* out, int r, int orow, int o
 //   t <  T:  L_ik = S_ik * Linv_kk^T        for i = kb + 1 + t
 //   t >= T:  X_kj = Linv_kk * Y_kj           for j = t - T  (j < kb)
 __global__ __launch_bounds__(256) void chol_panel_kernel(CholArgs a, int kb) {
-  __shared__ double sA[64][65];
-  __shared__ double sB[64][65];
+  __shared__ double sAB[2][64][kCP];
+  double (*sA)[kCP] = sAB[0];
+  double (*sB)[kCP] = sAB[1];
   const int member = blockIdx.y;
   double* S = a.s + member * a.mat_stride;
   double* X = a.x + member * a.mat_stride;
@@ -951,8 +1018,10 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(CholArgs a, int kb) {
 //   t <  T(T+1)/2:  S_ij -= L_ik L_jk^T   for kb < j <= i
 //   otherwise:      Y_ij -= L_ik X_kj     for i > kb, j <= kb
 __global__ __launch_bounds__(256) void chol_update_kernel(CholArgs a, int kb) {
-  __shared__ double sA[64][65];
-  __shared__ double sB[64][65];
+  __shared__ double sAB[2][64][kCP];
+  __shared__ double dinv[64];
+  double (*sA)[kCP] = sAB[0];
+  double (*sB)[kCP] = sAB[1];
   const int member = blockIdx.y;
   double* S = a.s + member * a.mat_stride;
   double* X = a.x + member * a.mat_stride;
@@ -975,7 +1044,7 @@ __global__ __launch_bounds__(256) void chol_update_kernel(CholArgs a, int kb) {
       // the trailing update.  The barrier orders its own stores before the
       // reloads and releases the operand tiles' LDS for the factorisation.
       __syncthreads();
-      chol_diag_block(a, kb + 1, member, sA, sB);
+      chol_diag_block(a, kb + 1, member, sAB, dinv);
     }
   } else {
     t -= ntri;
