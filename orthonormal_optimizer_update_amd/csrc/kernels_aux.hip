@@ -921,28 +921,32 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(CholArgs a, int kb) {
   chol_diag_block(a, kb, blockIdx.x, LY, dinv);
 }
 
-// acc (64 x 64 tile, four waves of 32 x 32) = A * B^T (TRANS_B) or A * B with
-// K = 64, fp64, A and B tiles read from row-major r x r matrices, on
-// v_mfma_f64_16x16x4_f64.  Result element e of acc[i][j] in lane l is row
-// wa*32 + i*16 + l/16 + 4e, column wb*32 + j*16 + l%16 (wa, wb: wave quadrant).
-template <bool TRANS_B>
-__device__ void tile_gemm64(const double* A, const double* B, int r, int ar, int ac, int br,
-                            int bc, double (*sA)[kCP], double (*sB)[kCP], doublex4 acc[2][2]) {
-  double va[16], vb[16];
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {  // all 32 loads in flight before any LDS store
-    const int e = threadIdx.x + q * 256;
-    const int i = e >> 6, j = e & 63;
-    va[q] = (ar + i < r && ac + j < r) ? A[(int64_t)(ar + i) * r + ac + j] : 0.0;
-    vb[q] = (br + i < r && bc + j < r) ? B[(int64_t)(br + i) * r + bc + j] : 0.0;
-  }
+// 64 x 64 fp64 tiles of row-major r x r matrices through LDS (pitch kCP),
+// four waves of 32 x 32 on v_mfma_f64_16x16x4f64.  Element e of acc[i][j] in
+// lane l is row wa * 32 + i * 16 + l / 16 + 4 e, column wb * 32 + j * 16 +
+// l % 16 (wa, wb: the wave's quadrant).
+
+// Tile at (row0, col0) into registers, zero outside the matrix.
+__device__ __forceinline__ void tile_fetch64(const double* A, int r, int row0, int col0, double v[16]) {
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int e = threadIdx.x + q * 256;
-    sA[e >> 6][e & 63] = va[q];
-    sB[e >> 6][e & 63] = vb[q];
+    const int i = e >> 6, j = e & 63;
+    v[q] = (row0 + i < r && col0 + j < r) ? A[(int64_t)(row0 + i) * r + col0 + j] : 0.0;
   }
-  __syncthreads();
+}
+__device__ __forceinline__ void tile_put_regs(const double v[16], double (*sT)[kCP]) {
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int e = threadIdx.x + q * 256;
+    sT[e >> 6][e & 63] = v[q];
+  }
+}
+
+// acc = A B^T (TRANS_B) or A B, K = 64, both operands in LDS.
+template <bool TRANS_B>
+__device__ __forceinline__ void tile_mma64(const double (*sA)[kCP], const double (*sB)[kCP],
+                                           doublex4 acc[2][2]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wa = wave >> 1, wb = wave & 1;
 #pragma unroll
@@ -964,14 +968,25 @@ __device__ void tile_gemm64(const double* A, const double* B, int r, int ar, int
       for (int j = 0; j < 2; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[i], bf[j], acc[i][j], 0, 0, 0);
   }
-  __syncthreads();
 }
 
-// Write (or subtract) a tile_gemm64 result at (orow, ocol) of an r x r matrix;
-// lower_only keeps the strictly-upper part of a diagonal tile untouched.
-__device__ __forceinline__ void tile_store64(double* out, int r, int orow, int ocol,
-                                             const doublex4 acc[2][2], bool subtract,
-                                             bool lower_only) {
+// acc into an LDS tile.
+__device__ __forceinline__ void tile_put_acc(const doublex4 acc[2][2], double (*sT)[kCP]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wa = wave >> 1, wb = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        sT[wa * 32 + i * 16 + (lane >> 4) + 4 * e][wb * 32 + j * 16 + (lane & 15)] = acc[i][j][e];
+}
+
+// Subtract acc from the tile at (orow, ocol) of an r x r matrix; lower_only
+// keeps the strictly-upper part of a diagonal tile untouched.
+__device__ __forceinline__ void tile_sub64(double* out, int r, int orow, int ocol,
+                                           const doublex4 acc[2][2], bool lower_only) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wa = wave >> 1, wb = wave & 1;
 #pragma unroll
@@ -984,88 +999,122 @@ __device__ __forceinline__ void tile_store64(double* out, int r, int orow, int o
         const int cc = ocol + wb * 32 + j * 16 + (lane & 15);
         if (rr < r && cc < r && (!lower_only || cc <= rr)) {
           double* dst = out + (int64_t)rr * r + cc;
-          *dst = subtract ? *dst - acc[i][j][e] : acc[i][j][e];
+          *dst = *dst - acc[i][j][e];
         }
       }
 }
 
-// Panel step for block column kb (tile index t):
-//   t <  T:  L_ik = S_ik * Linv_kk^T        for i = kb + 1 + t
-//   t >= T:  X_kj = Linv_kk * Y_kj           for j = t - T  (j < kb)
-__global__ __launch_bounds__(256) void chol_panel_kernel(CholArgs a, int kb) {
-  __shared__ double sAB[2][64][kCP];
-  double (*sA)[kCP] = sAB[0];
-  double (*sB)[kCP] = sAB[1];
-  const int member = blockIdx.y;
-  double* S = a.s + member * a.mat_stride;
-  double* X = a.x + member * a.mat_stride;
-  const int r = a.r, nblk = (r + 63) / 64;
-  const int T = nblk - kb - 1;
-  const int t = blockIdx.x;
-  doublex4 acc[2][2];
-  if (t < T) {
-    const int ib = kb + 1 + t;
-    tile_gemm64<true>(S, X, r, ib * 64, kb * 64, kb * 64, kb * 64, sA, sB, acc);
-    tile_store64(S, r, ib * 64, kb * 64, acc, false, false);
-  } else {
-    const int jb = t - T;
-    tile_gemm64<false>(X, X, r, kb * 64, kb * 64, kb * 64, jb * 64, sA, sB, acc);
-    tile_store64(X, r, kb * 64, jb * 64, acc, false, false);
-  }
-}
-
-// Trailing update after block column kb (tile index t):
+// Trailing update after block column kb.  The panel is formed in LDS by the
+// workgroups that use it: L_ik = S_ik Linv_kk^T for i > kb, and X_kj =
+// Linv_kk Y_kj for j < kb (X_kk = Linv_kk); block row kb of X keeps Y_kj
+// (make_t_kernel forms X_kj from it), and block column kb of S keeps S_ik.
 //   t <  T(T+1)/2:  S_ij -= L_ik L_jk^T   for kb < j <= i
 //   otherwise:      Y_ij -= L_ik X_kj     for i > kb, j <= kb
+// Workgroup 0 then factors diagonal block kb + 1, whose tile it has just
+// finished (no other workgroup writes it).
 __global__ __launch_bounds__(256) void chol_update_kernel(CholArgs a, int kb) {
-  __shared__ double sAB[2][64][kCP];
+  __shared__ double sT[3][64][kCP];
   __shared__ double dinv[64];
-  double (*sA)[kCP] = sAB[0];
-  double (*sB)[kCP] = sAB[1];
   const int member = blockIdx.y;
   double* S = a.s + member * a.mat_stride;
   double* X = a.x + member * a.mat_stride;
   const int r = a.r, nblk = (r + 63) / 64;
   const int T = nblk - kb - 1;
   const int ntri = T * (T + 1) / 2;
+  const int k0 = kb * 64;
   int t = blockIdx.x;
-  doublex4 acc[2][2];
+  doublex4 acc[2][2], acc2[2][2];
+  double v0[16], v1[16], v2[16];
   if (t < ntri) {
     int ti = static_cast<int>((sqrt(8.0 * t + 1.0) - 1.0) * 0.5);
     while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
     while (ti * (ti + 1) / 2 > t) --ti;
     const int tj = t - ti * (ti + 1) / 2;
     const int ib = kb + 1 + ti, jb = kb + 1 + tj;
-    tile_gemm64<true>(S, S, r, ib * 64, kb * 64, jb * 64, kb * 64, sA, sB, acc);
-    tile_store64(S, r, ib * 64, jb * 64, acc, true, ib == jb);
+    const bool two = ib != jb;
+    tile_fetch64(S, r, ib * 64, k0, v0);
+    tile_fetch64(X, r, k0, k0, v1);
+    if (two) tile_fetch64(S, r, jb * 64, k0, v2);
+    tile_put_regs(v0, sT[0]);
+    tile_put_regs(v1, sT[1]);
+    if (two) tile_put_regs(v2, sT[2]);
+    __syncthreads();
+    tile_mma64<true>(sT[0], sT[1], acc);              // L_ik
+    if (two) tile_mma64<true>(sT[2], sT[1], acc2);    // L_jk
+    __syncthreads();
+    tile_put_acc(acc, sT[0]);
+    if (two) tile_put_acc(acc2, sT[2]);
+    __syncthreads();
+    tile_mma64<true>(sT[0], two ? sT[2] : sT[0], acc);
+    tile_sub64(S, r, ib * 64, jb * 64, acc, !two);
     if (t == 0) {
-      // Tile (kb+1, kb+1) has now received every update it will get: this
-      // workgroup factors it (the next diagonal block) while the others finish
-      // the trailing update.  The barrier orders its own stores before the
-      // reloads and releases the operand tiles' LDS for the factorisation.
+      // Orders this workgroup's stores before the diagonal block's reloads
+      // and releases the LDS tiles.
       __syncthreads();
-      chol_diag_block(a, kb + 1, member, sAB, dinv);
+      chol_diag_block(a, kb + 1, member, sT, dinv);
     }
   } else {
     t -= ntri;
     const int ib = kb + 1 + t / (kb + 1), jb = t % (kb + 1);
-    tile_gemm64<false>(S, X, r, ib * 64, kb * 64, kb * 64, jb * 64, sA, sB, acc);
-    tile_store64(X, r, ib * 64, jb * 64, acc, true, false);
+    const bool below = jb < kb;
+    tile_fetch64(S, r, ib * 64, k0, v0);
+    tile_fetch64(X, r, k0, k0, v1);
+    if (below) tile_fetch64(X, r, k0, jb * 64, v2);
+    tile_put_regs(v0, sT[0]);
+    tile_put_regs(v1, sT[1]);
+    if (below) tile_put_regs(v2, sT[2]);
+    __syncthreads();
+    tile_mma64<true>(sT[0], sT[1], acc);                 // L_ik
+    if (below) tile_mma64<false>(sT[1], sT[2], acc2);    // X_kj
+    __syncthreads();
+    tile_put_acc(acc, sT[0]);
+    if (below) tile_put_acc(acc2, sT[2]);
+    __syncthreads();
+    tile_mma64<false>(sT[0], below ? sT[2] : sT[1], acc);
+    tile_sub64(X, r, ib * 64, jb * 64, acc, false);
   }
 }
 
-// T^T[j][k] = Linv[j][k] * d[k] for k <= j, else 0, as fp32: the right factor
-// of P1 = P_tilde * T with T = D L^{-T} upper triangular.
+// T^T[j][k] = X[j][k] d[k] for k <= j, else 0, as fp32, on 64 x 64 tiles:
+// the right factor of P1 = P_tilde T with T = D L^{-T} upper triangular.
+// Diagonal tiles of X are L_jj^{-1}; a tile below the diagonal is formed as
+// X_jk = L_jj^{-1} Y_jk from the Y block the factorisation left there.
 __global__ __launch_bounds__(256) void make_t_kernel(CholArgs a, float* tt, int64_t tt_stride) {
+  __shared__ double sT[2][64][kCP];
   const int member = blockIdx.z;
   const double* X = a.x + member * a.mat_stride;
   const double* d = a.d + member * a.vec_stride;
   float* out = tt + member * tt_stride;
   const int r = a.r;
-  const int j = blockIdx.y * 16 + (threadIdx.x >> 4);
-  const int k = blockIdx.x * 16 + (threadIdx.x & 15);
-  if (j >= r || k >= r) return;
-  out[(int64_t)j * r + k] = k <= j ? static_cast<float>(X[(int64_t)j * r + k] * d[k]) : 0.f;
+  const int jb = blockIdx.y, kb = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (kb >= jb) {
+    for (int q = 0; q < 16; ++q) {
+      const int j = jb * 64 + q * 4 + wave, k = kb * 64 + lane;
+      if (j < r && k < r)
+        out[(int64_t)j * r + k] = (kb == jb && k <= j) ? static_cast<float>(X[(int64_t)j * r + k] * d[k]) : 0.f;
+    }
+    return;
+  }
+  double v0[16], v1[16];
+  tile_fetch64(X, r, jb * 64, jb * 64, v0);
+  tile_fetch64(X, r, jb * 64, kb * 64, v1);
+  tile_put_regs(v0, sT[0]);
+  tile_put_regs(v1, sT[1]);
+  __syncthreads();
+  doublex4 acc[2][2];
+  tile_mma64<false>(sT[0], sT[1], acc);
+  const int wa = wave >> 1, wb = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = jb * 64 + wa * 32 + i * 16 + (lane >> 4) + 4 * e;
+        const int k = kb * 64 + wb * 32 + jj * 16 + (lane & 15);
+        if (j < r && k < r) out[(int64_t)j * r + k] = static_cast<float>(acc[i][jj][e] * d[k]);
+      }
 }
 
 // First-order correction of a nearly orthonormal basis P1: with
@@ -1208,19 +1257,14 @@ hipError_t launch_cholesky_inverse(const CholArgs& a, float* tt, int64_t tt_stri
   const int r = a.r, nblk = cdiv(r, 64);
   hipLaunchKernelGGL(chol_prep_kernel, dim3(cdiv(r, 16), cdiv(r, 16), members), dim3(256), 0, s, a);
   // Block 0 is factored on its own; block kb + 1 is factored by the update
-  // launch of step kb (its workgroup 0), so each later step is two launches.
+  // launch of step kb (its workgroup 0), so each later step is one launch.
   hipLaunchKernelGGL(chol_diag_kernel, dim3(members), dim3(256), 0, s, a, 0);
-  for (int kb = 0; kb < nblk; ++kb) {
+  for (int kb = 0; kb + 1 < nblk; ++kb) {
     const int T = nblk - kb - 1;
-    const int npanel = T + kb;
-    if (npanel > 0)
-      hipLaunchKernelGGL(chol_panel_kernel, dim3(npanel, members), dim3(256), 0, s, a, kb);
     const int nupd = T * (T + 1) / 2 + T * (kb + 1);
-    if (nupd > 0)
-      hipLaunchKernelGGL(chol_update_kernel, dim3(nupd, members), dim3(256), 0, s, a, kb);
+    hipLaunchKernelGGL(chol_update_kernel, dim3(nupd, members), dim3(256), 0, s, a, kb);
   }
-  hipLaunchKernelGGL(make_t_kernel, dim3(cdiv(r, 16), cdiv(r, 16), members), dim3(256), 0, s, a, tt,
-                     tt_stride);
+  hipLaunchKernelGGL(make_t_kernel, dim3(nblk, nblk, members), dim3(256), 0, s, a, tt, tt_stride);
   return hipGetLastError();
 }
 
