@@ -93,6 +93,10 @@ hipError_t dion_update_f32(const DionUpdateArgs& a, int members, hipStream_t s) 
 }
 
 bool fast_ok(int M, int N, int K, const MatArg& a, const MatArg& b);
+// Up to this rank the streaming update (memory terms loaded under the products,
+// 16-byte accesses) beats both the 256 x 128 two-accumulator kernel and the
+// 256 x 256 pair.
+constexpr int kUpdStreamMaxRank = 512;
 template <class Epi>
 hipError_t run_fast(GemmParams<typename Epi::Args>& p, int members, hipStream_t s);
 
@@ -105,6 +109,8 @@ static bool rows16(const MatArg& t, int members, size_t esz) {
 }
 
 hipError_t dion_update_bf16(const DionUpdateArgs& a, int members, hipStream_t s) {
+  if (a.rank <= kUpdStreamMaxRank && dion_update_stream_ok(a, members))
+    return launch_dion_update_stream(a, members, s);
   // At small ranks the step is bound by its 14 mn bytes, which the fused
   // 256 x 128 two-accumulator kernel streams as well; from r = 1024 on the
   // products dominate and the 256 x 256 kernel is faster.

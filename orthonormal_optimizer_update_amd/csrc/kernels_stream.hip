@@ -1,0 +1,223 @@
+// Dion's third sweep as an HBM-streaming kernel (bf16 weights, fp32 momentum):
+//
+//   M' = (M + G) - P (c1 R)^T          error feedback (paper page: the
+//                                       momentum keeps what the low-rank
+//                                       update did not apply; MSR talk)
+//   X' = X - P (c2 Q')^T               SGD-form weight step, rounded to bf16
+//
+// The factors arrive as bf16 copies with the scales already applied, so both
+// products are single bf16 products with fp32 accumulation.  The sweep moves
+// 14 bytes per element of X (read M, G, X; write M, X) and does 4r flops per
+// element, so below the bf16 ridge it is bound by HBM, not by the matrix cores.
+//
+// Layout of the work:
+// - A workgroup owns a 128 x 32 tile of M and X: four waves, each a 32 x 32
+//   block (one 32-row strip).
+// - The products are formed transposed, C^T = R P^T, so the fp32 accumulator of
+//   lane l, element e is C[i0 + l%32][j0 + 8*(e/4) + 4*(l/32) + e%4]: four
+//   consecutive columns of one row.  Every memory term is then one 16-byte load
+//   (M) or 8-byte load (G, X) per four elements, and so is every store.
+// - The R and Q' rows of the tile go through LDS in chunks of 256 k, shared by
+//   the four waves; P fragments come straight from global memory (each wave
+//   reads only its own rows).  A chunk's factor loads are issued first, then
+//   every memory term of the tile, so the products start as soon as the
+//   (L2-resident) factors have arrived while the HBM reads are still in flight.
+// - Small tiles let three workgroups share a CU, so one's epilogue and loads
+//   overlap the others' products.
+#include "launch.h"
+
+namespace ortho {
+
+namespace {
+
+constexpr int kUpdRows = 128;   // tile rows (4 waves x 32)
+constexpr int kUpdCols = 32;    // tile columns
+constexpr int kUpdKc = 256;     // k per chunk staged in LDS
+constexpr int kUpdLds = kUpdKc + 8;  // bf16 per LDS row; +16 B spreads rows over the banks
+constexpr int kUpdStage = kUpdCols * (kUpdKc / 8) / 256;  // 16-byte pieces per thread per factor
+
+struct UpdStreamParams {
+  MatArg m, g, x;      // fp32 momentum, bf16 gradient, bf16 weight
+  MatArg pb, rb, qb;   // bf16 P (m x r), c1 R (n x r), c2 Q' (n x r)
+  int M, N, K;         // K = r = 256 or 512
+  int tiles_j;         // N / 32
+};
+
+typedef uint32_t uint2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ floatx4 bf16x4_bits_to_f32(uint2v u) {
+  floatx4 v;
+  v[0] = __uint_as_float(u[0] << 16);
+  v[1] = __uint_as_float(u[0] & 0xffff0000u);
+  v[2] = __uint_as_float(u[1] << 16);
+  v[3] = __uint_as_float(u[1] & 0xffff0000u);
+  return v;
+}
+
+__device__ __forceinline__ uint2v f32x4_to_bf16_bits(floatx4 v) {
+  const uint32_t a = to_bf16_bits(v[0]), b = to_bf16_bits(v[1]);
+  const uint32_t c = to_bf16_bits(v[2]), d = to_bf16_bits(v[3]);
+  uint2v r;
+  r[0] = a | (b << 16);
+  r[1] = c | (d << 16);
+  return r;
+}
+
+// Loads of one 256-k chunk: thread t stages 16-byte pieces t, t + 256, ... of
+// the 32 x 32 grid of pieces that covers factor rows 0..31 (from r0 and q0),
+// k in [kc, kc + 256), and takes its own 16 P fragments.
+__device__ __forceinline__ void upd_chunk_load(uint4 (&stR)[kUpdStage], uint4 (&stQ)[kUpdStage],
+                                               bf16x8 (&pf)[kUpdKc / 16], const uint16_t* r0,
+                                               int64_t ldr, const uint16_t* q0, int64_t ldq,
+                                               const uint16_t* prow, int kc, int tid) {
+#pragma unroll
+  for (int u = 0; u < kUpdStage; ++u) {
+    const int idx = tid + u * 256;
+    const int64_t r = idx >> 5;
+    const int c = kc + (idx & 31) * 8;
+    stR[u] = *reinterpret_cast<const uint4*>(r0 + r * ldr + c);
+    stQ[u] = *reinterpret_cast<const uint4*>(q0 + r * ldq + c);
+  }
+#pragma unroll
+  for (int s = 0; s < kUpdKc / 16; ++s) pf[s] = *reinterpret_cast<const bf16x8*>(prow + kc + 16 * s);
+}
+
+// NCH chunks of 256 k (r = 256 NCH).  Every loop is unrolled, so the code is
+// straight-line and each wait for a load names exactly that load: the memory
+// terms issued after a chunk's factor loads stay in flight under its products.
+template <int NCH>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(NCH == 1 ? 3 : 2, NCH == 1 ? 3 : 2)))
+void dion_update_stream_kernel(UpdStreamParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t sR[kUpdCols * kUpdLds];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[kUpdCols * kUpdLds];
+  constexpr int kSteps = kUpdKc / 16;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bi = blockIdx.y;
+
+  // Consecutive workgroup ids go round-robin over the 8 XCDs: give each XCD a
+  // contiguous run of tiles, column tile innermost, so that each XCD streams a
+  // band of whole rows (every DRAM page it opens is read and written in full)
+  // and its P rows stay in its L2.
+  int bid = blockIdx.x;
+  const int nwg = gridDim.x;
+  if ((nwg & 7) == 0) bid = (bid & 7) * (nwg >> 3) + (bid >> 3);
+  const int ti = bid / p.tiles_j, tj = bid % p.tiles_j;
+  const int i0 = ti * kUpdRows + wave * 32;
+  const int j0 = tj * kUpdCols;
+  const int row = i0 + (lane & 31);
+  const int h = lane >> 5;
+
+  float* mp = static_cast<float*>(const_cast<void*>(p.m.p[bi]));
+  const uint16_t* gp = static_cast<const uint16_t*>(p.g.p[bi]);
+  uint16_t* xp = static_cast<uint16_t*>(const_cast<void*>(p.x.p[bi]));
+  const uint16_t* pbp = static_cast<const uint16_t*>(p.pb.p[bi]);
+  const uint16_t* rbp = static_cast<const uint16_t*>(p.rb.p[bi]);
+  const uint16_t* qbp = static_cast<const uint16_t*>(p.qb.p[bi]);
+
+  float* mrow = mp + static_cast<int64_t>(row) * p.m.ld;
+  const uint16_t* grow = gp + static_cast<int64_t>(row) * p.g.ld;
+  uint16_t* xrow = xp + static_cast<int64_t>(row) * p.x.ld;
+  const uint16_t* prow = pbp + static_cast<int64_t>(row) * p.pb.ld + 8 * h;
+  const int frag = (lane & 31) * kUpdLds + 8 * h;
+
+  uint4 stR[kUpdStage], stQ[kUpdStage];
+  bf16x8 pf[kSteps];
+  upd_chunk_load(stR, stQ, pf, rbp + static_cast<int64_t>(j0) * p.rb.ld, p.rb.ld,
+                 qbp + static_cast<int64_t>(j0) * p.qb.ld, p.qb.ld, prow, 0, tid);
+
+  // Memory terms of this lane: group g holds columns j0 + 8 g + 4 h + (0..3).
+  floatx4 mv[4];
+  uint2v gv[4], xv[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int col = j0 + 8 * g + 4 * h;
+    mv[g] = *reinterpret_cast<const floatx4*>(mrow + col);
+    gv[g] = *reinterpret_cast<const uint2v*>(grow + col);
+    xv[g] = *reinterpret_cast<const uint2v*>(xrow + col);
+  }
+
+  floatx16 accM, accX;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    accM[e] = 0.f;
+    accX[e] = 0.f;
+  }
+
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+    if (ch > 0) {
+      __syncthreads();  // every wave is done with the last chunk
+    }
+#pragma unroll
+    for (int u = 0; u < kUpdStage; ++u) {
+      const int idx = tid + u * 256;
+      const int r = idx >> 5, c = (idx & 31) * 8;
+      *reinterpret_cast<uint4*>(sR + r * kUpdLds + c) = stR[u];
+      *reinterpret_cast<uint4*>(sQ + r * kUpdLds + c) = stQ[u];
+    }
+    __syncthreads();
+    bf16x8 pc[kSteps];
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) pc[s] = pf[s];
+    if (ch + 1 < NCH)
+      upd_chunk_load(stR, stQ, pf, rbp + static_cast<int64_t>(j0) * p.rb.ld, p.rb.ld,
+                     qbp + static_cast<int64_t>(j0) * p.qb.ld, p.qb.ld, prow, (ch + 1) * kUpdKc, tid);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const bf16x8 r0 = *reinterpret_cast<const bf16x8*>(sR + frag + 16 * s);
+      const bf16x8 q0 = *reinterpret_cast<const bf16x8*>(sQ + frag + 16 * s);
+      accM = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r0, pc[s], accM, 0, 0, 0);
+      accX = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q0, pc[s], accX, 0, 0, 0);
+    }
+  }
+
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int col = j0 + 8 * g + 4 * h;
+    const floatx4 gf = bf16x4_bits_to_f32(gv[g]);
+    const floatx4 xf = bf16x4_bits_to_f32(xv[g]);
+    floatx4 mo, xo;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      mo[t] = (mv[g][t] + gf[t]) - accM[4 * g + t];
+      xo[t] = xf[t] - accX[4 * g + t];
+    }
+    *reinterpret_cast<floatx4*>(mrow + col) = mo;
+    *reinterpret_cast<uint2v*>(xrow + col) = f32x4_to_bf16_bits(xo);
+  }
+}
+
+bool aligned_rows(const MatArg& t, int members, size_t esz, size_t bytes) {
+  if ((static_cast<size_t>(t.ld) * esz) % bytes != 0) return false;
+  for (int i = 0; i < members; ++i)
+    if (reinterpret_cast<uintptr_t>(t.p[i]) % bytes != 0) return false;
+  return true;
+}
+
+}  // namespace
+
+bool dion_update_stream_ok(const DionUpdateArgs& a, int members) {
+  return a.M % kUpdRows == 0 && a.N % kUpdCols == 0 && (a.rank == 256 || a.rank == 512) &&
+         aligned_rows(a.m, members, 4, 16) && aligned_rows(a.g, members, 2, 8) &&
+         aligned_rows(a.x, members, 2, 8) && aligned_rows(a.pb, members, 2, 16) &&
+         aligned_rows(a.rb, members, 2, 16) && aligned_rows(a.qb, members, 2, 16);
+}
+
+hipError_t launch_dion_update_stream(const DionUpdateArgs& a, int members, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0 || members <= 0) return hipSuccess;
+  if (!dion_update_stream_ok(a, members)) return hipErrorInvalidValue;
+  UpdStreamParams p{};
+  p.m = a.m; p.g = a.g; p.x = a.x;
+  p.pb = a.pb; p.rb = a.rb; p.qb = a.qb;
+  p.M = a.M; p.N = a.N; p.K = a.rank;
+  p.tiles_j = a.N / kUpdCols;
+  dim3 grid((a.M / kUpdRows) * p.tiles_j, members);
+  if (a.rank == 256)
+    hipLaunchKernelGGL(dion_update_stream_kernel<1>, grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(dion_update_stream_kernel<2>, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace ortho

@@ -212,6 +212,10 @@ struct DionUpdateArgs {
   int M, N, rank;
 };
 hipError_t launch_dion_update(const DionUpdateArgs& a, bool bf16, int members, hipStream_t s);
+// bf16 weights, r = 256 or 512, M % 128 == 0, N % 32 == 0, 16-byte rows of M and
+// the bf16 factors, 8-byte rows of G and X: the HBM-streaming update kernel.
+bool dion_update_stream_ok(const DionUpdateArgs& a, int members);
+hipError_t launch_dion_update_stream(const DionUpdateArgs& a, int members, hipStream_t s);
 
 // Newton-Schulz products (bf16 operands, fp32 accumulation).
 struct NsGramArgs { MatArg x; MatArg a; int M, K; };                 // A = X X^T

@@ -96,7 +96,10 @@ def test_ns_square_4096_deterministic():
 # ----------------------------------------------------------------------------
 
 DION_SHAPES = [(96, 80, 16), (300, 200, 37), (513, 257, 64), (128, 1000, 128), (1000, 128, 100),
-               (40, 30, 30), (7, 9, 1), (700, 900, 250)]
+               (40, 30, 30), (7, 9, 1), (700, 900, 250),
+               # bf16: whole 128 x 32 tiles of the streaming update at r = 256 and
+               # r = 512
+               (384, 352, 256), (768, 1024, 512)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
