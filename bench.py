@@ -8,9 +8,12 @@ planted rank-32 part of 10x norm) is the whole hot path once:
     newton_schulz, 5 iterations, on the same matrix.
 Inputs are synthetic, seeded and resident in HBM before timing starts.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|3|4|5]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sizes]
 
-Prints ONE JSON line.  The oracle is timed on the host cores on a bounded
+Prints ONE JSON line.  Besides the headline step it carries a per-size table
+(time per call, modeled GB/s and TFLOP/s and their fraction of peak) for square
+matrices from 1024 to 8192 at rank fractions 1/4 and 1/16 and for the
+Llama-405B weight shapes, measured after the timed region.  The oracle is timed on the host cores on a bounded
 sample (one step of the same workload) as the reported CPU baseline.
 """
 
@@ -45,6 +48,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-sizes", action="store_true",
+                   help="skip the per-size table (square 1024-8192 and the Llama-405B shapes)")
     p.add_argument("--counter-sample", action="store_true",
                    help="run 2 Newton-Schulz iterations and a 256 MiB device copy, print "
                         "nothing else (for rocprofv3 --pmc passes)")
@@ -104,6 +109,79 @@ def workload2(torch, api, synth):
     info = dict(workload=wl["name"], m=m, n=n, ranks=wl["ranks"], ns_iterations=5,
                 mu=mu, lr=lr, x_dtype="bf16", momentum_dtype="f32")
     return names, run_path, ns_steps, info, (m, n)
+
+
+# Per-size table, outside the timed region: time per call of each path on
+# square matrices and on the Llama-405B weight shapes.  Inputs are drawn on the
+# device from a seeded generator (X ~ N(0, 0.02^2), G ~ N(0, 1), Q0 Gaussian with
+# unit columns), bf16 weights and gradients, fp32 momentum.
+SIZE_CASES = [
+    # (name, m, n, ranks, ns, timed calls)
+    ("square-1024", 1024, 1024, (256, 64), True, 10),
+    ("square-2048", 2048, 2048, (512, 128), True, 10),
+    ("square-4096", 4096, 4096, (1024, 256), True, 10),
+    ("square-8192", 8192, 8192, (2048, 512), True, 5),
+    ("llama405b-16384x16384", 16384, 16384, (4096, 1024), True, 2),
+    ("llama405b-16384x53248", 16384, 53248, (4096, 1024), False, 2),
+]
+
+
+def dion_model(m, n, r):
+    """Algorithmic bytes (bf16 X and G, fp32 M, fp32 factors) and dense flops of one
+    Dion step: three sweeps of M + G, the weight read and written once, and four
+    rank-r products."""
+    return 26.0 * m * n + 16.0 * (m + n) * r, 8.0 * m * n * r
+
+
+def ns_model(m, n, iters=5):
+    a, b = min(m, n), max(m, n)
+    return (3.0 * 2 * a * b + 12.0 * a * a) * iters, (4.0 * a * a * b + 2.0 * a ** 3) * iters
+
+
+def size_table(torch, api, warmup=1):
+    dev = "cuda"
+    out = {}
+    for ci, (name, m, n, ranks, ns, calls) in enumerate(SIZE_CASES):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1000 + ci)
+        X = (torch.randn(m, n, generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+        G = torch.randn(m, n, generator=gen, device=dev).to(torch.bfloat16)
+        row = {}
+
+        def timed(fn):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            with Timer(torch) as t:
+                for _ in range(calls):
+                    fn()
+            return t.ms / calls
+
+        for r in ranks:
+            M = torch.zeros(m, n, device=dev)
+            Q = torch.randn(n, r, generator=gen, device=dev)
+            Q /= Q.norm(dim=0, keepdim=True)
+            ws = api.workspace(api.dion_workspace_size(m, n, r), dev)
+            ms = timed(lambda: api.dion_step(X, G, M, Q, 0.95, 0.01, ws=ws))
+            nbytes, flops = dion_model(m, n, r)
+            gbs, tfs = nbytes / (ms * 1e-3) / 1e9, flops / (ms * 1e-3) / 1e12
+            row[f"dion_r{r}"] = {"ms": ms, "steps_per_s": 1000.0 / ms, "rank_frac": f"1/{min(m, n) // r}",
+                                 "GB/s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
+                                 "TFLOP/s": tfs, "mfma_frac": tfs / PEAK_BF16_TFLOPS}
+            del M, Q, ws
+        if ns:
+            ws = api.workspace(api.ns_workspace_size(m, n), dev)
+            o = torch.empty_like(G)
+            ms = timed(lambda: api.newton_schulz(G, out=o, steps=5, ws=ws))
+            nbytes, flops = ns_model(m, n)
+            tfs = flops / (ms * 1e-3) / 1e12
+            row["ns5"] = {"ms": ms, "steps_per_s": 1000.0 / ms, "TFLOP/s": tfs,
+                          "mfma_frac": tfs / PEAK_BF16_TFLOPS}
+            del ws, o
+        out[name] = row
+        del X, G
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(synth, oracle):
@@ -213,6 +291,8 @@ def main():
                 "executed_flops_per_launch": executed,
                 "executed_tflops": executed / (gemm_ms * 1e-3) / 1e12}
 
+    sizes = None if args.no_sizes else size_table(torch, api)
+
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import dion_ref as oracle  # reported CPU baseline only
@@ -223,7 +303,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic", "config": info, "paths": per_path, "roofline": roofline,
-        "cpu_baseline": cpu,
+        "cpu_baseline": cpu, "sizes": sizes,
     }
     print(json.dumps(line))
 
