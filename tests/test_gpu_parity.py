@@ -186,3 +186,29 @@ def test_dion_zero_gradient():
     assert gpu["status"] & api.DEV_ZERO_COLUMN
     assert np.all(gpu["M"] == 0) and np.all(gpu["Q"] == 0)
     assert np.array_equal(gpu["X"], X.astype(np.float64))
+
+
+@pytest.mark.parametrize("shape", [(384, 352, 256), (768, 1024, 512), (300, 200, 37)])
+def test_dion_padded_leading_dims(shape):
+    """X, G and M as column views of wider buffers (ld > cols), bf16: the step
+    matches the oracle and writes nothing outside the views."""
+    m, n, r = shape
+    X, G, Q0 = synth.small_case(40 + r, m, n, r, "bf16", planted_rank=4)
+    pad = 64
+    bufs = {}
+    for name, a, dt in (("X", X, "bf16"), ("G", G, "bf16"), ("M", np.zeros_like(X), "f32")):
+        full = np.full((m, n + pad), 7.0, np.float32)
+        full[:, :n] = a
+        bufs[name] = to_dev(full, dt)
+    tQ = to_dev(Q0, "f32")
+    P = torch.empty(m, r, dtype=torch.float32, device="cuda")
+    note(f"dion padded ld {shape}")
+    api.dion_step(bufs["X"][:, :n], bufs["G"][:, :n], bufs["M"][:, :n], tQ, 0.95, 0.01, P_out=P)
+    torch.cuda.synchronize()
+    ref = oracle.dion_step(X, G, np.zeros_like(X), Q0, 0.95, 0.01, x_dtype="bf16")
+    for name in ("X", "G", "M"):
+        assert np.all(to_host(bufs[name])[:, n:] == 7.0), f"{name} written outside its view"
+    assert rel(to_host(bufs["M"])[:, :n], ref["M"]) <= TOL["bf16"]
+    assert rel(to_host(tQ), ref["Q"]) <= TOL["bf16"]
+    assert rel(to_host(P), ref["P"]) <= TOL["bf16"]
+    assert rel(to_host(bufs["X"])[:, :n], ref["X_exact"]) <= TOL["bf16"]
