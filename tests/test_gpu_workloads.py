@@ -117,3 +117,56 @@ def test_per_head_whole_matrix_dion():
     worst, recs = run_dion_parity(X, Gs, Q0, wl["mu"], wl["lr"], "bf16", label="cfg4")
     print(worst)
     assert max(worst.values()) <= TOL["bf16"], recs
+
+
+def test_paths_on_separate_streams_match_one_stream():
+    """The bench step's three independent calls (Dion at r = n/4 and n/16 and
+    Newton-Schulz on the same gradient), run on three streams at once, give the
+    same bits as the same calls one after another on one stream."""
+    m = n = 1024
+    S = synth.planted(2, m, n, 32, synth.WORKLOADS[2]["planted_ratio"])
+    G = to_dev(synth.gradient(2, m, n, 1, "bf16", planted_part=S), "bf16")
+    X0 = to_dev(synth.weight(2, m, n, "bf16"), "bf16")
+
+    def fresh():
+        st = {}
+        for r in (256, 64):
+            st[r] = dict(X=X0.clone(), M=torch.zeros(m, n, device="cuda"),
+                         Q=to_dev(synth.right_factor0(2, n, r), "f32"),
+                         ws=api.workspace(api.dion_workspace_size(m, n, r), "cuda"))
+        st["ns"] = dict(out=torch.empty_like(G), ws=api.workspace(api.ns_workspace_size(m, n), "cuda"))
+        return st
+
+    def run(st, key):
+        for _ in range(2):
+            if key == "ns":
+                api.newton_schulz(G, out=st["ns"]["out"], steps=5, ws=st["ns"]["ws"])
+            else:
+                d = st[key]
+                api.dion_step(d["X"], G, d["M"], d["Q"], 0.95, 0.01, ws=d["ws"])
+
+    note("paths one stream")
+    one = fresh()
+    for key in (256, 64, "ns"):
+        run(one, key)
+    torch.cuda.synchronize()
+
+    note("paths three streams")
+    many = fresh()
+    torch.cuda.synchronize()
+    main = torch.cuda.current_stream()
+    fork = torch.cuda.Event()
+    fork.record(main)
+    streams = {key: torch.cuda.Stream() for key in (256, 64, "ns")}
+    for key, s in streams.items():
+        s.wait_event(fork)
+        with torch.cuda.stream(s):
+            run(many, key)
+    for s in streams.values():
+        main.wait_stream(s)
+    torch.cuda.synchronize()
+
+    for r in (256, 64):
+        for k in ("X", "M", "Q"):
+            assert torch.equal(one[r][k], many[r][k]), (r, k)
+    assert torch.equal(one["ns"]["out"], many["ns"]["out"])
