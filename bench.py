@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--one-stream", action="store_true",
+                   help="time the step with its paths one after another on one stream (kernel "
+                        "profiles: every launch then runs alone)")
     p.add_argument("--no-sizes", action="store_true",
                    help="skip the per-size table (square 1024-8192 and the Llama-405B shapes)")
     p.add_argument("--counter-sample", action="store_true",
@@ -247,6 +250,10 @@ def main():
     side = {nm: torch.cuda.Stream() for nm in names}
 
     def step(i):
+        if args.one_stream:
+            for nm in names:
+                run_path(nm, i)
+            return
         fork = torch.cuda.Event()
         fork.record(main)
         done = []
@@ -331,6 +338,7 @@ def main():
     line = {
         "metric": METRIC, "value": 1000.0 / ms_step, "unit": "steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "streams": 1 if args.one_stream else len(names),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic", "config": info, "ms_per_step_one_stream": ms_serial,
         "paths": per_path, "roofline": roofline,
