@@ -40,6 +40,12 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<bf16>(x));
 }
 
+// Four fp32 values as four bf16 (RNE), packed for one 8-byte store.
+__device__ __forceinline__ uint2 pack_bf16x4(floatx4 v) {
+  return make_uint2(to_bf16_bits(v[0]) | (uint32_t(to_bf16_bits(v[1])) << 16),
+                    to_bf16_bits(v[2]) | (uint32_t(to_bf16_bits(v[3])) << 16));
+}
+
 // x = hi + lo + O(2^-16 |x|): hi is x rounded to bf16, lo is the exact fp32
 // remainder rounded to bf16.
 __device__ __forceinline__ void split_bf16(float x, bf16& hi, bf16& lo) {

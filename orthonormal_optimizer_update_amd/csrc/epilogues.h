@@ -26,11 +26,6 @@ namespace ortho {
 //                 computes the tiles on and above the diagonal only and hands
 //                 each off-diagonal tile to fast_store_t4 as well (its mirror).
 
-__device__ __forceinline__ uint2 pack_bf16x4(floatx4 v) {
-  return make_uint2(to_bf16_bits(v[0]) | (uint32_t(to_bf16_bits(v[1])) << 16),
-                    to_bf16_bits(v[2]) | (uint32_t(to_bf16_bits(v[3])) << 16));
-}
-
 // Four consecutive values at p[idx..idx+3]; one vector store when vec.
 template <class T>
 __device__ __forceinline__ void store4_from_f32(T* p, int64_t idx, floatx4 v, bool vec);

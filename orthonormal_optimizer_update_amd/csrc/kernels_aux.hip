@@ -387,7 +387,17 @@ __global__ __launch_bounds__(64) void ns_scale_kernel(const float* partial, int6
 }
 
 // X0 = scale * G (wide orientation: rows <= cols, transposing a tall G), into
-// the fp32 iterate and its two bf16 copies.  64 x 64 tiles through LDS.
+// the fp32 iterate and its two bf16 copies.  64 x 64 tiles through LDS; each
+// thread moves four consecutive elements of a row per access (16-byte fp32 and
+// 8-byte bf16 accesses where the row has them, element by element at the
+// matrix edge).
+template <typename T>
+__device__ __forceinline__ void load4_scaled(const T* row, int c, int limit, bool vec, float sc,
+                                             float v[4]) {
+  const float4 f = load4<T>(row, c, limit, vec);
+  v[0] = f.x * sc; v[1] = f.y * sc; v[2] = f.z * sc; v[3] = f.w * sc;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void ns_init_kernel(NsInitArgs a) {
   __shared__ float tile[64][65];
@@ -398,27 +408,60 @@ __global__ __launch_bounds__(256) void ns_init_kernel(NsInitArgs a) {
   uint16_t* xbt = static_cast<uint16_t*>(const_cast<void*>(a.xbt.p[bi]));
   const float sc = a.scale[bi * a.scale_stride];
   const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;  // tile of X (M x N)
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  // Load tile[ii][jj] = X[i0+ii][j0+jj], reading G row-coalesced.
-  for (int k = ty; k < 64; k += 4) {
+  const int c4 = (threadIdx.x & 15) * 4, r16 = threadIdx.x >> 4;
+  // tile[ii][jj] = X[i0+ii][j0+jj], reading G four elements of a row at a time
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int rr = r16 + 16 * q;
+    float v[4];
     if (!a.transposed) {
-      const int i = i0 + k, j = j0 + tx;
-      tile[k][tx] = (i < a.M && j < a.N) ? load_as_f32<T>(g, (int64_t)i * a.g.ld + j) * sc : 0.f;
+      const int i = i0 + rr;
+      if (i < a.M) {
+        load4_scaled<T>(g + (int64_t)i * a.g.ld, j0 + c4, a.N, a.g.vec, sc, v);
+      } else {
+        v[0] = v[1] = v[2] = v[3] = 0.f;
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) tile[rr][c4 + t] = v[t];
     } else {
-      const int j = j0 + k, i = i0 + tx;  // X[i][j] = G[j][i]
-      tile[tx][k] = (i < a.M && j < a.N) ? load_as_f32<T>(g, (int64_t)j * a.g.ld + i) * sc : 0.f;
+      const int j = j0 + rr;  // X[i][j] = G[j][i]: row j of G holds column j of X
+      if (j < a.N) {
+        load4_scaled<T>(g + (int64_t)j * a.g.ld, i0 + c4, a.M, a.g.vec, sc, v);
+      } else {
+        v[0] = v[1] = v[2] = v[3] = 0.f;
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) tile[c4 + t][rr] = v[t];
     }
   }
   __syncthreads();
-  for (int k = ty; k < 64; k += 4) {
-    const int i = i0 + k, j = j0 + tx;
-    if (i < a.M && j < a.N) {
-      const float v = tile[k][tx];
-      x32[(int64_t)i * a.x32.ld + j] = v;
-      xb[(int64_t)i * a.xb.ld + j] = to_bf16_bits(v);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int rr = r16 + 16 * q;
+    // row-major copies: X[i0 + rr][j0 + c4 ..]
+    const int i = i0 + rr, j = j0 + c4;
+    if (i < a.M) {
+      const floatx4 v = {tile[rr][c4], tile[rr][c4 + 1], tile[rr][c4 + 2], tile[rr][c4 + 3]};
+      if (j + 4 <= a.N) {
+        *reinterpret_cast<floatx4*>(x32 + (int64_t)i * a.x32.ld + j) = v;
+        *reinterpret_cast<uint2*>(xb + (int64_t)i * a.xb.ld + j) = pack_bf16x4(v);
+      } else {
+        for (int t = 0; t < 4 && j + t < a.N; ++t) {
+          x32[(int64_t)i * a.x32.ld + j + t] = v[t];
+          xb[(int64_t)i * a.xb.ld + j + t] = to_bf16_bits(v[t]);
+        }
+      }
     }
-    const int jt = j0 + k, it = i0 + tx;  // X^T[jt][it]
-    if (it < a.M && jt < a.N) xbt[(int64_t)jt * a.xbt.ld + it] = to_bf16_bits(tile[tx][k]);
+    // transposed copy: X^T[j0 + rr][i0 + c4 ..] = X[i0 + c4 ..][j0 + rr]
+    const int jt = j0 + rr, it = i0 + c4;
+    if (jt < a.N) {
+      const floatx4 v = {tile[c4][rr], tile[c4 + 1][rr], tile[c4 + 2][rr], tile[c4 + 3][rr]};
+      if (it + 4 <= a.M) {
+        *reinterpret_cast<uint2*>(xbt + (int64_t)jt * a.xbt.ld + it) = pack_bf16x4(v);
+      } else {
+        for (int t = 0; t < 4 && it + t < a.M; ++t) xbt[(int64_t)jt * a.xbt.ld + it + t] = to_bf16_bits(v[t]);
+      }
+    }
   }
 }
 
