@@ -255,61 +255,87 @@ __global__ __launch_bounds__(256) void split_t_kernel(SplitTArgs a) {
                     blockIdx.y * 64, blockIdx.x * 64);
 }
 
-// Column normalisation Q'[:, j] = R[:, j] / |R[:, j]|, from the per-row-block
-// column sums of squares (summed in block order).  A zero column gives a zero
-// column and sets ORTHO_DEV_ZERO_COLUMN.
-__global__ __launch_bounds__(256) void colnorm_kernel(ColnormArgs a) {
-  __shared__ float inv[64];
+// Column normalisation Q'[:, j] = R[:, j] / |R[:, j]|, in two launches.
+// colnorm_inv_kernel sums the per-row-block column sums of squares in block
+// order (four thread groups take every fourth block, combined in a fixed order)
+// and writes 1/|R[:, j]| over row block 0's sums.  A zero column gives a zero
+// column and sets ORTHO_DEV_ZERO_COLUMN; NaN propagates.
+__global__ __launch_bounds__(256) void colnorm_inv_kernel(ColnormArgs a) {
   __shared__ float part[4][64];
-  const int bi = blockIdx.z;
-  const int c0 = blockIdx.x * 64;
-  {
-    // four thread groups sum every fourth row block, then combine in a fixed
-    // order (the unrolled loads of a group are all in flight together)
-    const int g = threadIdx.x >> 6, cc = threadIdx.x & 63, c = c0 + cc;
-    float s = 0.f;
-    if (c < a.cols) {
-      const float* cs = a.colsq + bi * a.colsq_member_stride + c;
+  const int bi = blockIdx.y;
+  const int g = threadIdx.x >> 6, cc = threadIdx.x & 63, c = blockIdx.x * 64 + cc;
+  float* cs = a.colsq + bi * a.colsq_member_stride;
+  float s = 0.f;
+  if (c < a.cols) {
 #pragma unroll 8
-      for (int b = g; b < a.nrb; b += 4) s += cs[(int64_t)b * a.cols];
-    }
-    part[g][cc] = s;
+    for (int b = g; b < a.nrb; b += 4) s += cs[(int64_t)b * a.cols + c];
   }
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    const int c = c0 + threadIdx.x;
-    float v = 0.f;
-    if (c < a.cols) {
-      const float s = (part[0][threadIdx.x] + part[1][threadIdx.x]) +
-                      (part[2][threadIdx.x] + part[3][threadIdx.x]);
-      if (s > 0.f) {
-        v = 1.0f / sqrtf(s);
-      } else if (!(s != s)) {
-        v = 0.f;
-        if (a.status && blockIdx.y == 0) atomicOr(a.status, 2);
-      } else {
-        v = s;  // NaN propagates
-      }
+  part[g][cc] = s;
+  __syncthreads();  // every read of row block 0 is done before it is overwritten
+  if (threadIdx.x < 64 && c < a.cols) {
+    const float t = (part[0][cc] + part[1][cc]) + (part[2][cc] + part[3][cc]);
+    float v;
+    if (t > 0.f) {
+      v = 1.0f / sqrtf(t);
+    } else if (!(t != t)) {
+      v = 0.f;
+      if (a.status) atomicOr(a.status, 2);
+    } else {
+      v = t;
     }
-    inv[threadIdx.x] = v;
+    cs[c] = v;
   }
-  __syncthreads();
+}
+
+// Q' = R diag(inv), and the bf16 operands of the last sweep; 64 x 64 tiles,
+// four consecutive columns per thread (16-byte fp32 and 8-byte bf16 accesses
+// where the row has them).
+__global__ __launch_bounds__(256) void colnorm_kernel(ColnormArgs a) {
+  const int bi = blockIdx.z;
+  const float* inv = a.colsq + bi * a.colsq_member_stride;
   const float* r = static_cast<const float*>(a.r.p[bi]);
   float* q = static_cast<float*>(const_cast<void*>(a.q.p[bi]));
-  const int cc = threadIdx.x & 63;
-  const int c = c0 + cc;
-  if (c >= a.cols) return;
   uint16_t* rb = a.has_bf16 ? static_cast<uint16_t*>(const_cast<void*>(a.rb.p[bi])) : nullptr;
   uint16_t* qb = a.has_bf16 ? static_cast<uint16_t*>(const_cast<void*>(a.qb.p[bi])) : nullptr;
-  for (int rr = threadIdx.x >> 6; rr < 64; rr += 4) {
-    const int row = blockIdx.y * 64 + rr;
+  const int c = blockIdx.x * 64 + (threadIdx.x & 15) * 4;
+  if (c >= a.cols) return;
+  const bool full = c + 4 <= a.cols;
+  float iv[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) iv[t] = c + t < a.cols ? inv[c + t] : 0.f;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int row = blockIdx.y * 64 + (threadIdx.x >> 4) + 16 * q4;
     if (row >= a.rows) break;
-    const float rv = r[(int64_t)row * a.r.ld + c];
-    const float qv = rv * inv[cc];
-    q[(int64_t)row * a.q.ld + c] = qv;
+    const float* rrow = r + (int64_t)row * a.r.ld;
+    floatx4 rv, qv;
+    if (full && a.r.vec) {
+      rv = *reinterpret_cast<const floatx4*>(rrow + c);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) rv[t] = c + t < a.cols ? rrow[c + t] : 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) qv[t] = rv[t] * iv[t];
+    float* qrow = q + (int64_t)row * a.q.ld;
+    if (full && a.q.vec) {
+      *reinterpret_cast<floatx4*>(qrow + c) = qv;
+    } else {
+      for (int t = 0; t < 4 && c + t < a.cols; ++t) qrow[c + t] = qv[t];
+    }
     if (rb) {
-      rb[(int64_t)row * a.rb.ld + c] = to_bf16_bits(a.c1 * rv);
-      qb[(int64_t)row * a.qb.ld + c] = to_bf16_bits(a.c2 * qv);
+      const floatx4 rs = a.c1 * rv, qs = a.c2 * qv;
+      uint16_t* rbrow = rb + (int64_t)row * a.rb.ld;
+      uint16_t* qbrow = qb + (int64_t)row * a.qb.ld;
+      if (full) {
+        *reinterpret_cast<uint2*>(rbrow + c) = pack_bf16x4(rs);
+        *reinterpret_cast<uint2*>(qbrow + c) = pack_bf16x4(qs);
+      } else {
+        for (int t = 0; t < 4 && c + t < a.cols; ++t) {
+          rbrow[c + t] = to_bf16_bits(rs[t]);
+          qbrow[c + t] = to_bf16_bits(qs[t]);
+        }
+      }
     }
   }
 }
@@ -1222,6 +1248,9 @@ hipError_t launch_split_t(const SplitTArgs& a, int members, hipStream_t s) {
 }
 
 hipError_t launch_colnorm(const ColnormArgs& a, int members, hipStream_t s) {
+  hipLaunchKernelGGL(colnorm_inv_kernel, dim3(cdiv(a.cols, 64), members), dim3(256), 0, s, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   dim3 grid(cdiv(a.cols, 64), cdiv(a.rows, 64), members);
   hipLaunchKernelGGL(colnorm_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();

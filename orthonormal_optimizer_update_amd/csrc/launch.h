@@ -23,7 +23,7 @@ struct RedArgs {
 struct ColnormArgs {
   MatArg r;                   // fp32 source
   MatArg q;                   // fp32 destination
-  const float* colsq;
+  float* colsq;               // per-row-block column sums of squares; row 0 receives 1/norm
   int64_t colsq_member_stride;
   int nrb, rows, cols;
   int32_t* status;
