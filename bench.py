@@ -56,8 +56,8 @@ def parse():
     p.add_argument("--no-sizes", action="store_true",
                    help="skip the per-size table (square 1024-8192 and the Llama-405B shapes)")
     p.add_argument("--counter-sample", action="store_true",
-                   help="run 2 Newton-Schulz iterations and a 256 MiB device copy, print "
-                        "nothing else (for rocprofv3 --pmc passes)")
+                   help="run 2 Newton-Schulz iterations, one Dion step at each rank and a "
+                        "256 MiB device copy, print nothing else (for rocprofv3 --pmc passes)")
     return p.parse_args()
 
 
@@ -233,6 +233,9 @@ def main():
         # known size (256 MiB read + 256 MiB written) that calibrates the
         # FETCH_SIZE / WRITE_SIZE counters.
         ns_steps(2)
+        for nm in names:  # one Dion step at each rank (the streaming and 256 x 256 updates)
+            if nm.startswith("dion"):
+                run_path(nm, 0)
         src = torch.ones(64 * 1024 * 1024, device="cuda", dtype=torch.float32)
         dst = torch.empty_like(src)
         torch.mul(src, 2.0, out=dst)  # elementwise copy kernel: 256 MiB in, 256 MiB out

@@ -95,14 +95,23 @@ void dion_update_stream_kernel(UpdStreamParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bi = blockIdx.y;
 
-  // Consecutive workgroup ids go round-robin over the 8 XCDs: give each XCD a
-  // contiguous run of tiles, column tile innermost, so that each XCD streams a
-  // band of whole rows and its P rows stay in its L2 (measured slightly faster
-  // than the column-tile-outermost order).
-  int bid = blockIdx.x;
-  const int nwg = gridDim.x;
-  if ((nwg & 7) == 0) bid = (bid & 7) * (nwg >> 3) + (bid >> 3);
-  const int ti = bid / p.tiles_j, tj = bid % p.tiles_j;
+  // Consecutive workgroup ids go round-robin over the 8 XCDs.  When the tile
+  // grid splits into 2 x 4 blocks, XCD x takes block (x / 4, x % 4), column
+  // tile innermost: its P rows and its c1 R, c2 Q' rows (a quarter of the
+  // columns) then both stay in its L2.  Walking all columns per row band
+  // instead re-fetched all of R and Q' for every band, about as many bytes as
+  // the sweep's own reads.
+  const int tiles_i = p.M / kUpdRows;
+  int ti, tj;
+  if ((gridDim.x & 7) == 0 && (tiles_i & 1) == 0 && (p.tiles_j & 3) == 0) {
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    const int bj = p.tiles_j >> 2;
+    ti = (xcd >> 2) * (tiles_i >> 1) + local / bj;
+    tj = (xcd & 3) * bj + local % bj;
+  } else {
+    ti = blockIdx.x / p.tiles_j;
+    tj = blockIdx.x % p.tiles_j;
+  }
   const int i0 = ti * kUpdRows + wave * 32;
   const int j0 = tj * kUpdCols;
   const int row = i0 + (lane & 31);
