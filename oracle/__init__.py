@@ -20,6 +20,12 @@ public pages about microsoft/dion):
   agentlenshq "microsoft/dion", section "How it works"; paper page "Dion:
   Distributed Orthonormalized Updates", abstract.
 
+* ``muon_step`` -- the Muon step around the Newton-Schulz path: a heavy-ball
+  momentum buffer, its Newton-Schulz orthogonalisation, and the SGD-form update.
+  Same talk, same passages.  The momentum form is the plainest reading and
+  "parity unpinned" as to fidelity: the pages name Muon's momentum but print no
+  formula; the pins check the step against its own definition.
+
 Every reading that the pages leave open (where mu enters, the QR sign
 convention, column normalisation of the new right factor, the Newton-Schulz
 coefficients) is listed in the design doc together with the reason for it.
@@ -41,4 +47,6 @@ from .dion_ref import (  # noqa: F401
     dion_step_batched,
     newton_schulz,
     newton_schulz_batched,
+    muon_step,
+    muon_step_batched,
 )

@@ -190,3 +190,42 @@ def _ns_step(Xk, a, b, c):
 def newton_schulz_batched(Gs, steps=5, abc=MUON_ABC, eps=NS_EPS):
     """Independent Newton-Schulz on each matrix of a group (e.g. per-head blocks)."""
     return [newton_schulz(G, steps, abc, eps) for G in Gs]
+
+
+# ----------------------------------------------------------------------------
+# Muon step: momentum buffer, Newton-Schulz orthogonalisation, SGD-form update
+# ----------------------------------------------------------------------------
+
+def _muon_momentum(M, G, mu):
+    """Heavy-ball momentum buffer M' = mu M + G (the plainest reading; the pages
+    name Muon's momentum but print no formula for it)."""
+    return mu * M + G
+
+
+def muon_step(X, G, M, mu: float, lr: float, scale: float = 1.0, steps: int = 5,
+              abc=MUON_ABC, eps: float = NS_EPS, x_dtype: str = "bf16") -> dict:
+    """One Muon step on one matrix, in fp64.
+
+    MSR talk "Dion: The distributed orthonormal update revolution is here":
+    Muon orthogonalises the momentum-accumulated gradient with Newton-Schulz
+    iterations (passage on Muon's dense matrix products) and applies it in the
+    SGD form X - lr * update (passage contrasting SGD with orthonormal updates).
+        M' = mu M + G
+        U  = newton_schulz(M', steps, abc, eps)
+        X' = X - lr * scale * U, rounded to ``x_dtype``
+    Returns ``X`` (rounded), ``X_exact``, ``dX`` (= -lr * scale * U), ``M`` and
+    ``U``.
+    """
+    X, G, M = _f64(X), _f64(G), _f64(M)
+    M_new = _muon_momentum(M, G, float(mu))
+    U = newton_schulz(M_new, steps, abc, eps)
+    dX = -float(lr) * float(scale) * U
+    X_exact = X + dX
+    return dict(X=round_to_dtype(X_exact, x_dtype), X_exact=X_exact, dX=dX, M=M_new, U=U)
+
+
+def muon_step_batched(Xs, Gs, Ms, mu, lr, scale=1.0, steps=5, abc=MUON_ABC, eps=NS_EPS,
+                      x_dtype="bf16"):
+    """A group of independent same-shape matrices: one ``muon_step`` each."""
+    return [muon_step(X, G, M, mu, lr, scale, steps, abc, eps, x_dtype)
+            for X, G, M in zip(Xs, Gs, Ms)]

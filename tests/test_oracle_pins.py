@@ -326,3 +326,58 @@ def test_mutant_ns_normalization_caught(monkeypatch, rng):
     G = 3.0 * rng.standard_normal((16, 24))
     monkeypatch.setattr(dion_ref, "_ns_normalize", lambda X, eps: X / (np.abs(X).max() + eps))
     assert not (ns_closed_form_err(G) <= 1e-6)
+
+
+
+# ----------------------------------------------------------------------------
+# Muon step
+# ----------------------------------------------------------------------------
+
+def _muon_pins(rng):
+    """Max error over the Muon pins: momentum closed form over several steps,
+    reduction to the SVD closed form of Newton-Schulz, the update identity and
+    scale invariance of the orthogonalised momentum."""
+    errs = []
+    m, n, mu = 18, 26, 0.9
+    X = rng.standard_normal((m, n)) * 0.02
+    Gs = [rng.standard_normal((m, n)) for _ in range(4)]
+    M = np.zeros((m, n))
+    for G in Gs:
+        out = oracle.muon_step(X, G, M, mu, lr=0.0, x_dtype="f32")
+        M = out["M"]
+    # heavy-ball momentum: M_T = sum_t mu^(T-t) G_t
+    closed = sum(mu ** (len(Gs) - 1 - t) * G for t, G in enumerate(Gs))
+    errs.append(np.abs(M - closed).max() / np.abs(closed).max())
+    # the orthogonalised direction is U f(S) V^T of the momentum's SVD
+    errs.append(np.abs(out["U"] - quintic_spectral(out["M"])).max())
+    # SGD form: X' - X = -lr s U, and lr = 0 leaves X unchanged
+    o2 = oracle.muon_step(X, Gs[0], M, mu, lr=0.03, scale=1.7, x_dtype="f32")
+    errs.append(np.abs((o2["X_exact"] - X) + 0.03 * 1.7 * o2["U"]).max())
+    errs.append(np.abs(out["X_exact"] - X).max())
+    # mu = 0 forgets the buffer: U = NS(G)
+    o3 = oracle.muon_step(X, Gs[1], 5.0 * M, 0.0, lr=0.01, x_dtype="f32")
+    errs.append(np.abs(o3["U"] - oracle.newton_schulz(Gs[1])).max())
+    # the iteration normalises the buffer, not the gradient: scaling both M and
+    # G by 3 leaves U unchanged (eps = 0 makes the invariance exact)
+    o4 = oracle.muon_step(X, 3.0 * Gs[2], 3.0 * M, mu, lr=0.01, eps=0.0, x_dtype="f32")
+    o5 = oracle.muon_step(X, Gs[2], M, mu, lr=0.01, eps=0.0, x_dtype="f32")
+    errs.append(np.abs(o4["U"] - o5["U"]).max())
+    return max(errs)
+
+
+def test_muon_pins(rng):
+    assert _muon_pins(np.random.default_rng(11)) <= 1e-12
+
+
+MUON_MUTANTS = {
+    "momentum_weights_swapped": ("_muon_momentum", lambda M, G, mu: M + mu * G),
+    "momentum_dropped": ("_muon_momentum", lambda M, G, mu: G),
+    "ema_momentum": ("_muon_momentum", lambda M, G, mu: mu * M + (1.0 - mu) * G),
+}
+
+
+@pytest.mark.parametrize("name", list(MUON_MUTANTS))
+def test_mutant_muon_caught(monkeypatch, name):
+    attr, fn = MUON_MUTANTS[name]
+    monkeypatch.setattr(dion_ref, attr, fn)
+    assert not (_muon_pins(np.random.default_rng(11)) <= 1e-6)
