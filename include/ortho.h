@@ -2,7 +2,7 @@
  * ortho.h -- C-ABI of libortho.so: the per-matrix orthonormalized optimizer step
  * on one AMD Instinct MI355X (gfx950).
  *
- * Two operations, each for one matrix and for a group of same-shape matrices:
+ * Three operations, each for one matrix and for a group of same-shape matrices:
  *
  *   dion_step      Dion's amortised power iteration with error feedback.
  *                  MSR talk "Dion: The distributed orthonormal update revolution
@@ -16,6 +16,8 @@
  *                      M' = B - (1 - mu) P R^T               (error feedback)
  *                      Q' = R with unit-norm columns
  *                      X' = X - lr * scale * P Q'^T          (SGD form)
+ *   muon_step      the whole Muon step around newton_schulz: momentum buffer,
+ *                  its orthogonalisation, SGD-form update (declared below).
  *   newton_schulz  Muon's Newton-Schulz orthogonalisation, the full-rank
  *                  comparison path.  Same talk, passage contrasting SGD with an
  *                  orthonormal update (take U V^T of the SVD) and the passage on
@@ -145,6 +147,34 @@ ortho_status newton_schulz(ortho_mat G, ortho_mat Out, int32_t steps, const floa
 ortho_status newton_schulz_batched(int32_t batch, const ortho_mat* G, const ortho_mat* Out,
                                    int32_t steps, const float* abc, void* ws, size_t ws_bytes,
                                    void* stream);
+
+/* Bytes of device workspace for muon_step (batch = 1) or muon_step_batched on
+ * `batch` matrices of m x n.  Returns 0 for invalid arguments. */
+size_t ortho_muon_workspace_size(int64_t m, int64_t n, int32_t batch);
+
+/* One Muon step on one matrix: the steps on either side of newton_schulz.
+ * MSR talk "Dion: The distributed orthonormal update revolution is here",
+ * passage on Muon orthogonalising the momentum-accumulated gradient with dense
+ * Newton-Schulz matrix products, and passage on the SGD-form update:
+ *     M  = mu M + G                     (heavy-ball momentum buffer)
+ *     U  = newton_schulz(M, steps, abc) (as newton_schulz above)
+ *     X  = X - lr * scale * U,  rounded to nearest even into X's dtype.
+ *   X      m x n, ORTHO_BF16 or ORTHO_F32, updated in place.
+ *   G      m x n, same dtype as X, read only.
+ *   M      m x n, ORTHO_F32, updated in place (start it at zero).
+ *   steps  >= 0 Newton-Schulz iterations; abc as for newton_schulz.
+ *   mu in [0, 1]; lr and scale finite, else ORTHO_E_PARAM.
+ *   ws     >= ortho_muon_workspace_size(m, n, 1) bytes, 256-byte aligned.
+ * Errors are returned before anything is enqueued. */
+ortho_status muon_step(ortho_mat X, ortho_mat G, ortho_mat M, int32_t steps, const float* abc,
+                       float mu, float lr, float scale, void* ws, size_t ws_bytes, void* stream);
+
+/* muon_step on `batch` independent same-shape matrices (HOST arrays of
+ * descriptors; every member shares (m, n, dtype) and each operand's ld), each
+ * orthogonalised on its own. */
+ortho_status muon_step_batched(int32_t batch, const ortho_mat* X, const ortho_mat* G,
+                               const ortho_mat* M, int32_t steps, const float* abc, float mu,
+                               float lr, float scale, void* ws, size_t ws_bytes, void* stream);
 
 /* Static English description of a status code. */
 const char* ortho_status_str(int32_t status);

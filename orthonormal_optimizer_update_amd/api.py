@@ -52,6 +52,14 @@ _SIGS = {
     "newton_schulz_batched": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(OrthoMat), ctypes.POINTER(OrthoMat),
                                              ctypes.c_int32, ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                              ctypes.c_size_t, ctypes.c_void_p]),
+    "ortho_muon_workspace_size": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]),
+    "muon_step": (ctypes.c_int, [OrthoMat, OrthoMat, OrthoMat, ctypes.c_int32, ctypes.POINTER(ctypes.c_float),
+                                 ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
+                                 ctypes.c_size_t, ctypes.c_void_p]),
+    "muon_step_batched": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(OrthoMat), ctypes.POINTER(OrthoMat),
+                                         ctypes.POINTER(OrthoMat), ctypes.c_int32,
+                                         ctypes.POINTER(ctypes.c_float), ctypes.c_float, ctypes.c_float,
+                                         ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "ortho_status_str": (ctypes.c_char_p, [ctypes.c_int32]),
     "ortho_abi_version": (ctypes.c_int32, []),
 }
@@ -187,3 +195,31 @@ def newton_schulz_batched(Gs: Sequence, outs: Optional[Sequence] = None, steps: 
                                      _stream_ptr(Gs[0].device))
     _check("newton_schulz_batched", st)
     return outs
+
+
+def muon_workspace_size(m: int, n: int, batch: int = 1) -> int:
+    return int(lib().ortho_muon_workspace_size(m, n, batch))
+
+
+def muon_step(X, G, M, mu: float, lr: float, scale: float = 1.0, steps: int = 5, abc=None, ws=None):
+    """One Muon step in place on (X, M); see ``muon_step`` in ortho.h."""
+    if ws is None:
+        ws = workspace(muon_workspace_size(X.size(0), X.size(1)), X.device)
+    st = lib().muon_step(mat(X), mat(G), mat(M), steps, _abc(abc), mu, lr, scale, _ptr(ws),
+                         ws.numel(), _stream_ptr(X.device))
+    _check("muon_step", st)
+
+
+def muon_step_batched(Xs: Sequence, Gs: Sequence, Ms: Sequence, mu: float, lr: float,
+                      scale: float = 1.0, steps: int = 5, abc=None, ws=None):
+    """Muon on a group of same-shape matrices in one call."""
+    b = len(Xs)
+    arr = OrthoMat * b
+    X = arr(*[mat(t) for t in Xs])
+    G = arr(*[mat(t) for t in Gs])
+    M = arr(*[mat(t) for t in Ms])
+    if ws is None:
+        ws = workspace(muon_workspace_size(Xs[0].size(0), Xs[0].size(1), b), Xs[0].device)
+    st = lib().muon_step_batched(b, X, G, M, steps, _abc(abc), mu, lr, scale, _ptr(ws), ws.numel(),
+                                 _stream_ptr(Xs[0].device))
+    _check("muon_step_batched", st)

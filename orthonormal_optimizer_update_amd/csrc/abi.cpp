@@ -359,9 +359,64 @@ ortho_status run_ns(int32_t batch, const ortho_mat* G, const ortho_mat* Out, int
   return ORTHO_OK;
 }
 
+// Muon step on each member: M = mu M + G; U = Newton-Schulz of M (fp32, in
+// the workspace after the Newton-Schulz part); X = X - lr * scale * U.  Launch
+// chunks as in run_ns, so U needs one slot per member of a chunk.
+ortho_status run_muon(int32_t batch, const ortho_mat* X, const ortho_mat* G, const ortho_mat* M,
+                      int32_t steps, const float* abc, float mu, float lr, float scale, void* ws,
+                      void* stream) {
+  MuonPlan pl;
+  const int64_t m = X[0].rows, n = X[0].cols;
+  if (!plan_muon(m, n, batch, &pl)) return ORTHO_E_SHAPE;
+  const bool bf = X[0].dtype == ORTHO_BF16;
+  const hipStream_t s = as_stream(stream);
+  char* base = static_cast<char*>(ws);
+  const size_t gvec = bf ? 8 : 16;
+  const int chunk = pl.ns.chunk;
+  for (int b0 = 0; b0 < batch; b0 += chunk) {
+    const int nb = batch - b0 < chunk ? batch - b0 : chunk;
+    MuonArgs a{};
+    a.m = user_table(M, b0, nb, 16);
+    a.g = user_table(G, b0, nb, gvec);
+    a.x = user_table(X, b0, nb, gvec);
+    a.u = ws_table(base, pl.u_bytes, pl.off_u, nb, pl.ld_u, static_cast<int>(m), static_cast<int>(n),
+                   4, 16);
+    a.mu = mu; a.c = lr * scale;
+    a.rows = static_cast<int>(m); a.cols = static_cast<int>(n);
+    ORTHO_TRY(launch_muon_momentum(a, bf, nb, s));
+    ortho_mat us[kMaxBatch];
+    for (int i = 0; i < nb; ++i)
+      us[i] = ortho_mat{base + pl.off_u + i * pl.u_bytes, m, n, pl.ld_u, ORTHO_F32};
+    const ortho_status st = run_ns(nb, M + b0, us, steps, abc, ws, stream);
+    if (st != ORTHO_OK) return st;
+    ORTHO_TRY(launch_muon_update(a, bf, nb, s));
+  }
+  return ORTHO_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t ortho_muon_workspace_size(int64_t m, int64_t n, int32_t batch) {
+  MuonPlan p;
+  return plan_muon(m, n, batch, &p) ? p.total_bytes : 0;
+}
+
+ortho_status muon_step(ortho_mat X, ortho_mat G, ortho_mat M, int32_t steps, const float* abc,
+                       float mu, float lr, float scale, void* ws, size_t ws_bytes, void* stream) {
+  const ortho_status st = validate_muon(1, &X, &G, &M, steps, abc, mu, lr, scale, ws, ws_bytes);
+  if (st != ORTHO_OK) return st;
+  return run_muon(1, &X, &G, &M, steps, abc, mu, lr, scale, ws, stream);
+}
+
+ortho_status muon_step_batched(int32_t batch, const ortho_mat* X, const ortho_mat* G,
+                               const ortho_mat* M, int32_t steps, const float* abc, float mu,
+                               float lr, float scale, void* ws, size_t ws_bytes, void* stream) {
+  const ortho_status st = validate_muon(batch, X, G, M, steps, abc, mu, lr, scale, ws, ws_bytes);
+  if (st != ORTHO_OK) return st;
+  return run_muon(batch, X, G, M, steps, abc, mu, lr, scale, ws, stream);
+}
 
 size_t ortho_dion_workspace_size(int64_t m, int64_t n, int32_t r, int32_t batch) {
   DionPlan p;

@@ -341,6 +341,55 @@ __global__ __launch_bounds__(256) void colnorm_kernel(ColnormArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Muon step around Newton-Schulz: momentum buffer and SGD-form update
+// ---------------------------------------------------------------------------
+
+// M = mu M + G (heavy-ball momentum buffer, fp32), four columns of a row per
+// thread; blockIdx.y = row, blockIdx.z = member.
+template <typename GT>
+__global__ __launch_bounds__(256) void muon_momentum_kernel(MuonArgs a) {
+  const int bi = blockIdx.z;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c >= a.cols) return;
+  for (int row = blockIdx.y; row < a.rows; row += gridDim.y) {
+  float* m = static_cast<float*>(const_cast<void*>(a.m.p[bi])) + (int64_t)row * a.m.ld;
+  const GT* g = static_cast<const GT*>(a.g.p[bi]) + (int64_t)row * a.g.ld;
+  const float4 gv = load4<GT>(g, c, a.cols, a.g.vec);
+  const float4 mv = load4<float>(m, c, a.cols, a.m.vec);
+  const float4 r = make_float4(a.mu * mv.x + gv.x, a.mu * mv.y + gv.y, a.mu * mv.z + gv.z,
+                               a.mu * mv.w + gv.w);
+  if (a.m.vec && c + 4 <= a.cols) {
+    *reinterpret_cast<float4*>(m + c) = r;
+  } else {
+    for (int t = 0; t < 4 && c + t < a.cols; ++t) m[c + t] = f4_get(r, t);
+  }
+  }
+}
+
+// X = X - c U (U the fp32 orthogonalised momentum), rounded to X's dtype.
+template <typename XT>
+__global__ __launch_bounds__(256) void muon_update_kernel(MuonArgs a) {
+  const int bi = blockIdx.z;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c >= a.cols) return;
+  for (int row = blockIdx.y; row < a.rows; row += gridDim.y) {
+  XT* x = static_cast<XT*>(const_cast<void*>(a.x.p[bi])) + (int64_t)row * a.x.ld;
+  const float* u = static_cast<const float*>(a.u.p[bi]) + (int64_t)row * a.u.ld;
+  const float4 uv = load4<float>(u, c, a.cols, a.u.vec);
+  const float4 xv = load4<XT>(x, c, a.cols, a.x.vec);
+  const floatx4 r = {xv.x - a.c * uv.x, xv.y - a.c * uv.y, xv.z - a.c * uv.z, xv.w - a.c * uv.w};
+  if (a.x.vec && c + 4 <= a.cols) {
+    if constexpr (sizeof(XT) == 2)
+      *reinterpret_cast<uint2*>(x + c) = pack_bf16x4(r);
+    else
+      *reinterpret_cast<floatx4*>(x + c) = r;
+  } else {
+    for (int t = 0; t < 4 && c + t < a.cols; ++t) store_from_f32<XT>(x, c + t, r[t]);
+  }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Newton-Schulz normalisation
 // ---------------------------------------------------------------------------
 
@@ -1234,6 +1283,24 @@ hipError_t launch_split_rows(const SplitRowsArgs& a, int members, hipStream_t s)
   dim3 grid(cdiv(a.cols, 64), cdiv(a.rows, 64), members);
   if (a.np == 2) hipLaunchKernelGGL(split_rows_kernel<2>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(split_rows_kernel<3>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_muon_momentum(const MuonArgs& a, bool g_bf16, int members, hipStream_t s) {
+  dim3 grid(cdiv(a.cols, 1024), a.rows < 65535 ? a.rows : 65535, members);
+  if (g_bf16)
+    hipLaunchKernelGGL(muon_momentum_kernel<uint16_t>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(muon_momentum_kernel<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_muon_update(const MuonArgs& a, bool x_bf16, int members, hipStream_t s) {
+  dim3 grid(cdiv(a.cols, 1024), a.rows < 65535 ? a.rows : 65535, members);
+  if (x_bf16)
+    hipLaunchKernelGGL(muon_update_kernel<uint16_t>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(muon_update_kernel<float>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

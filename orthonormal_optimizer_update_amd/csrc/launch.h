@@ -217,6 +217,16 @@ hipError_t launch_dion_update(const DionUpdateArgs& a, bool bf16, int members, h
 bool dion_update_stream_ok(const DionUpdateArgs& a, int members);
 hipError_t launch_dion_update_stream(const DionUpdateArgs& a, int members, hipStream_t s);
 
+// Muon step: M = mu M + G (fp32 momentum), then X = X - c U after Newton-Schulz
+// of M into the fp32 U.  Grid: 1024 columns x one row per workgroup.
+struct MuonArgs {
+  MatArg m, g, x, u;
+  float mu, c;
+  int rows, cols;
+};
+hipError_t launch_muon_momentum(const MuonArgs& a, bool g_bf16, int members, hipStream_t s);
+hipError_t launch_muon_update(const MuonArgs& a, bool x_bf16, int members, hipStream_t s);
+
 // Newton-Schulz products (bf16 operands, fp32 accumulation).
 struct NsGramArgs { MatArg x; MatArg a; int M, K; };                 // A = X X^T
 struct NsPolyArgs { MatArg a; MatArg bp; MatArg bp32; float b, c; int M; };  // Bp = bA + cAA

@@ -184,6 +184,17 @@ bool plan_ns(int64_t m, int64_t n, int32_t batch, NsPlan* p) {
   return true;
 }
 
+bool plan_muon(int64_t m, int64_t n, int32_t batch, MuonPlan* p) {
+  MuonPlan d{};
+  if (!plan_ns(m, n, batch, &d.ns)) return false;
+  d.ld_u = cdiv(n, 4) * 4;
+  d.off_u = align_up(d.ns.total_bytes);
+  d.u_bytes = align_up(static_cast<size_t>(m) * d.ld_u * 4);
+  d.total_bytes = d.off_u + d.u_bytes * static_cast<size_t>(d.ns.chunk);
+  *p = d;
+  return true;
+}
+
 ortho_status validate_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, const ortho_mat* M,
                            const ortho_mat* Q, int32_t r, float mu, float lr, float scale,
                            const ortho_mat* P_out, const ortho_mat* R_out, const void* ws,
@@ -246,6 +257,34 @@ ortho_status validate_ns(int32_t batch, const ortho_mat* G, const ortho_mat* Out
   }
   NsPlan plan;
   if (!plan_ns(G[0].rows, G[0].cols, batch, &plan)) return ORTHO_E_SHAPE;
+  if (ws == nullptr || ws_bytes < plan.total_bytes) return ORTHO_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kWsAlign != 0) return ORTHO_E_WORKSPACE;
+  return ORTHO_OK;
+}
+
+ortho_status validate_muon(int32_t batch, const ortho_mat* X, const ortho_mat* G, const ortho_mat* M,
+                           int32_t steps, const float* abc, float mu, float lr, float scale,
+                           const void* ws, size_t ws_bytes) {
+  if (batch < 1 || steps < 0) return ORTHO_E_PARAM;
+  if (!X || !G || !M) return ORTHO_E_NULL;
+  if (!(mu >= 0.f && mu <= 1.f) || !finite(lr) || !finite(scale)) return ORTHO_E_PARAM;
+  if (abc && (!finite(abc[0]) || !finite(abc[1]) || !finite(abc[2]))) return ORTHO_E_PARAM;
+  for (int32_t b = 0; b < batch; ++b) {
+    ortho_status st;
+    if ((st = check_mat(X[b])) != ORTHO_OK) return st;
+    if ((st = check_mat(G[b])) != ORTHO_OK) return st;
+    if ((st = check_mat(M[b])) != ORTHO_OK) return st;
+    if (G[b].dtype != X[b].dtype || M[b].dtype != ORTHO_F32) return ORTHO_E_DTYPE;
+    if (G[b].rows != X[b].rows || G[b].cols != X[b].cols || M[b].rows != X[b].rows ||
+        M[b].cols != X[b].cols)
+      return ORTHO_E_SHAPE;
+    if (b > 0) {
+      if (!same_geometry(X[b], X[0])) return ORTHO_E_SHAPE;
+      if (X[b].ld != X[0].ld || G[b].ld != G[0].ld || M[b].ld != M[0].ld) return ORTHO_E_LAYOUT;
+    }
+  }
+  MuonPlan plan;
+  if (!plan_muon(X[0].rows, X[0].cols, batch, &plan)) return ORTHO_E_SHAPE;
   if (ws == nullptr || ws_bytes < plan.total_bytes) return ORTHO_E_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) % kWsAlign != 0) return ORTHO_E_WORKSPACE;
   return ORTHO_OK;

@@ -56,7 +56,18 @@ struct NsPlan {
   size_t total_bytes;
 };
 
+// Muon step: the Newton-Schulz workspace followed, per member of a launch
+// chunk, by the fp32 orthogonalised momentum U (m x ld_u, ld_u = n rounded to 4).
+struct MuonPlan {
+  NsPlan ns;
+  int64_t ld_u;
+  size_t off_u;              // after the Newton-Schulz part
+  size_t u_bytes;            // per member
+  size_t total_bytes;
+};
+
 bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* out);
+bool plan_muon(int64_t m, int64_t n, int32_t batch, MuonPlan* out);
 bool plan_ns(int64_t m, int64_t n, int32_t batch, NsPlan* out);
 
 ortho_status validate_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, const ortho_mat* M,
@@ -66,5 +77,9 @@ ortho_status validate_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G
 
 ortho_status validate_ns(int32_t batch, const ortho_mat* G, const ortho_mat* Out, int32_t steps,
                          const float* abc, const void* ws, size_t ws_bytes);
+
+ortho_status validate_muon(int32_t batch, const ortho_mat* X, const ortho_mat* G, const ortho_mat* M,
+                           int32_t steps, const float* abc, float mu, float lr, float scale,
+                           const void* ws, size_t ws_bytes);
 
 }  // namespace ortho

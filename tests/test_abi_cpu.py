@@ -24,6 +24,7 @@ def test_header_declares_expected_entry_points():
     names = header_functions()
     for n in ["dion_step", "dion_step_ex", "dion_step_batched", "newton_schulz",
               "newton_schulz_batched", "ortho_dion_workspace_size", "ortho_ns_workspace_size",
+              "muon_step", "muon_step_batched", "ortho_muon_workspace_size",
               "ortho_status_str", "ortho_abi_version"]:
         assert n in names
 
@@ -146,6 +147,31 @@ def test_ns_argument_errors():
     arr = api.OrthoMat * 2
     assert L.newton_schulz_batched(2, arr(G, M(64, 48, BF, ld=50)), arr(O, O), 5, None, ws,
                                    api.ns_workspace_size(64, 48, 2), None) == 5
+
+
+def test_muon_argument_errors():
+    L = api.lib()
+    wsb = api.muon_workspace_size(64, 48)
+    assert wsb >= api.ns_workspace_size(64, 48) + 64 * 48 * 4
+    ws = ctypes.c_void_p(FAKE)
+    X, G, Mo = M(64, 48, BF), M(64, 48, BF), M(64, 48, F)
+    call = lambda x=X, g=G, m=Mo, steps=5, abc=None, mu=0.95, lr=0.02, w=ws, b=wsb: L.muon_step(
+        x, g, m, steps, abc, mu, lr, 1.0, w, b, None)
+    assert call(steps=-1) == 7
+    assert call(mu=1.5) == 7
+    assert call(lr=float("inf")) == 7
+    assert call(abc=(ctypes.c_float * 3)(1.0, float("nan"), 0.0)) == 7
+    assert call(g=M(64, 48, F)) == 3            # G must have X's dtype
+    assert call(m=M(64, 48, BF)) == 3           # momentum is fp32
+    assert call(m=M(64, 47, F)) == 2
+    assert call(x=M(64, 48, BF, data=None)) == 1
+    assert call(w=None) == 6
+    assert call(b=wsb - 1) == 6
+    arr = api.OrthoMat * 2
+    assert L.muon_step_batched(2, arr(X, M(64, 48, BF, ld=56)), arr(G, G), arr(Mo, Mo), 5, None,
+                               0.95, 0.02, 1.0, ws, api.muon_workspace_size(64, 48, 2), None) == 5
+    assert L.muon_step_batched(0, arr(X, X), arr(G, G), arr(Mo, Mo), 5, None, 0.95, 0.02, 1.0, ws,
+                               wsb, None) == 7
 
 
 def test_valid_call_without_gpu_reports_hip_error():

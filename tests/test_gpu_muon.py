@@ -1,0 +1,119 @@
+"""Parity of the Muon step (momentum buffer, Newton-Schulz of it, SGD-form
+update) through the C-ABI with the fp64 oracle.  Each side carries its own
+state (X, M) through the steps.  Tolerances: 1e-4 for the fp32 momentum buffer
+(a sum, exact up to fp32 rounding), 2e-2 for the update and the new weight (the
+Newton-Schulz products use bf16 matrix cores for either input dtype)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from orthonormal_optimizer_update_amd import api, synth
+
+from parity_util import TOL, note, rel, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    api.lib()
+    torch.cuda.set_device(0)
+
+
+def gpu_muon(X, G, M, mu, lr, dtype, scale=1.0, ws=None):
+    """One step on host arrays: returns X', M' and dX (from a twin call with X = 0)."""
+    out = {}
+    for twin in (False, True):
+        tX = to_dev(np.zeros_like(X) if twin else X, dtype)
+        tG = to_dev(G, dtype)
+        tM = to_dev(M, "f32")
+        api.muon_step(tX, tG, tM, mu, lr, scale, ws=ws)
+        torch.cuda.synchronize()
+        if twin:
+            out["dX"] = to_host(tX)
+            out["twin_M"] = to_host(tM)
+        else:
+            out["X"], out["M"] = to_host(tX), to_host(tM)
+    return out
+
+
+def run_muon_parity(X, Gs, mu, lr, dtype, label):
+    m, n = X.shape
+    ws = api.workspace(api.muon_workspace_size(m, n), "cuda")
+    Xg, Mg = X.astype(np.float64), np.zeros((m, n))
+    Xo, Mo = Xg.copy(), Mg.copy()
+    worst = {}
+    for t, G in enumerate(Gs):
+        note(f"muon {label} {m}x{n} {dtype} step {t + 1}")
+        gpu = gpu_muon(Xg, G, Mg, mu, lr, dtype, ws=ws)
+        ref = oracle.muon_step(Xo, G, Mo, mu, lr, x_dtype=dtype)
+        for k in ("X", "M", "dX"):
+            assert np.all(np.isfinite(gpu[k])), k
+        assert np.array_equal(gpu["twin_M"], gpu["M"])
+        errs = dict(M=rel(gpu["M"], ref["M"]), dX=rel(gpu["dX"], ref["dX"]),
+                    X=rel(gpu["X"], ref["X_exact"]))
+        for k, v in errs.items():
+            worst[k] = max(worst.get(k, 0.0), v)
+        Xg, Mg = gpu["X"], gpu["M"]
+        Xo, Mo = ref["X"], ref["M"]
+    return worst
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(96, 160), (300, 100), (257, 513), (1, 50), (384, 384)])
+def test_muon_small(shape, dtype):
+    m, n = shape
+    X, G1, _ = synth.small_case(60 + m, m, n, 1, dtype, planted_rank=min(4, m, n))
+    Gs = [G1] + [synth.gradient(1060 + m, m, n, t, dtype) for t in (2, 3)]
+    worst = run_muon_parity(X, Gs, mu=0.95, lr=0.02, dtype=dtype, label="small")
+    print(shape, dtype, worst)
+    assert worst["M"] <= TOL["f32"]
+    assert worst["dX"] <= TOL["bf16"] and worst["X"] <= TOL["bf16"]
+
+
+def test_muon_square_4096_planted():
+    """The 4096 x 4096 bf16 workload (planted rank-32 gradient), two steps."""
+    wl = synth.WORKLOADS[2]
+    X = synth.weight(2, 4096, 4096, "bf16")
+    S = synth.planted(2, 4096, 4096, 32, wl["planted_ratio"])
+    Gs = [synth.gradient(2, 4096, 4096, t, "bf16", planted_part=S) for t in (1, 2)]
+    worst = run_muon_parity(X, Gs, mu=0.95, lr=0.02, dtype="bf16", label="cfg2")
+    print(worst)
+    assert worst["M"] <= TOL["f32"]
+    assert worst["dX"] <= TOL["bf16"] and worst["X"] <= TOL["bf16"]
+
+
+def test_muon_mu_zero_and_lr_zero():
+    X, G, _ = synth.small_case(71, 128, 192, 1, "bf16")
+    M0 = synth.gradient(72, 128, 192, 1, "f32")
+    note("muon mu=0")
+    gpu = gpu_muon(X, G, M0, 0.0, 0.05, "bf16")
+    assert rel(gpu["dX"], -0.05 * oracle.newton_schulz(G)) <= TOL["bf16"]
+    note("muon lr=0")
+    gpu = gpu_muon(X, G, M0, 0.9, 0.0, "bf16")
+    assert np.array_equal(gpu["X"], X.astype(np.float64))
+    assert rel(gpu["M"], 0.9 * M0 + G) <= TOL["f32"]
+
+
+def test_muon_batched_equals_single():
+    """A group through muon_step_batched gives the bits of one call per member."""
+    m, n, b = 256, 384, 3
+    Xs = [synth.weight(80, m, n, "bf16", index=i) for i in range(b)]
+    Gs = [synth.gradient(80, m, n, 1 + i, "bf16") for i in range(b)]
+    single = []
+    note("muon batched vs single")
+    for X, G in zip(Xs, Gs):
+        tX, tG, tM = to_dev(X, "bf16"), to_dev(G, "bf16"), torch.zeros(m, n, device="cuda")
+        api.muon_step(tX, tG, tM, 0.9, 0.03)
+        single.append((tX, tM))
+    tXs = [to_dev(X, "bf16") for X in Xs]
+    tGs = [to_dev(G, "bf16") for G in Gs]
+    tMs = [torch.zeros(m, n, device="cuda") for _ in range(b)]
+    api.muon_step_batched(tXs, tGs, tMs, 0.9, 0.03)
+    torch.cuda.synchronize()
+    for (sx, sm), bx, bm in zip(single, tXs, tMs):
+        assert torch.equal(sx, bx) and torch.equal(sm, bm)
