@@ -15,7 +15,8 @@ Inputs are synthetic, seeded and resident in HBM before timing starts.
 Prints ONE JSON line.  Besides the headline step it carries a per-size table
 (time per call, modeled GB/s and TFLOP/s and their fraction of peak) for square
 matrices from 1024 to 8192 at rank fractions 1/4 and 1/16 and for the
-Llama-405B weight shapes, measured after the timed region.  The oracle is timed on the host cores on a bounded
+Llama-405B weight shapes, with the whole Muon step (momentum, NS x5, update)
+beside NS, measured after the timed region.  The oracle is timed on the host cores on a bounded
 sample (one step of the same workload) as the reported CPU baseline.
 """
 
@@ -183,6 +184,14 @@ def size_table(torch, api, warmup=1):
             row["ns5"] = {"ms": ms, "steps_per_s": 1000.0 / ms, "TFLOP/s": tfs,
                           "mfma_frac": tfs / PEAK_BF16_TFLOPS}
             del ws, o
+            # the whole Muon step: momentum buffer, NS x5 of it, weight update
+            M = torch.zeros(m, n, device=dev)
+            ws = api.workspace(api.muon_workspace_size(m, n), dev)
+            ms = timed(lambda: api.muon_step(X, G, M, 0.95, 0.02, ws=ws))
+            tfs = flops / (ms * 1e-3) / 1e12
+            row["muon5"] = {"ms": ms, "steps_per_s": 1000.0 / ms, "TFLOP/s": tfs,
+                            "mfma_frac": tfs / PEAK_BF16_TFLOPS}
+            del M, ws
         out[name] = row
         del X, G
         torch.cuda.empty_cache()
