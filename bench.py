@@ -16,7 +16,8 @@ Prints ONE JSON line.  Besides the headline step it carries a per-size table
 (time per call, modeled GB/s and TFLOP/s and their fraction of peak) for square
 matrices from 1024 to 8192 at rank fractions 1/4 and 1/16 and for the
 Llama-405B weight shapes, with the whole Muon step (momentum, NS x5, update)
-beside NS, measured after the timed region.  The oracle is timed on the host cores on a bounded
+beside NS, and the time per step of the other named workloads (256 x 256 fp32,
+the 12-layer GPT parameter groups, per-head NS), measured after the timed region.  The oracle is timed on the host cores on a bounded
 sample (one step of the same workload) as the reported CPU baseline.
 """
 
@@ -55,7 +56,8 @@ def parse():
                    help="time the step with its paths one after another on one stream (kernel "
                         "profiles: every launch then runs alone)")
     p.add_argument("--no-sizes", action="store_true",
-                   help="skip the per-size table (square 1024-8192 and the Llama-405B shapes)")
+                   help="skip the per-size table (square 1024-8192 and the Llama-405B shapes) "
+                        "and the other workloads (256x256 fp32, GPT-12 groups, per-head NS)")
     p.add_argument("--counter-sample", action="store_true",
                    help="run 2 Newton-Schulz iterations, one Dion step at each rank and a "
                         "256 MiB device copy, print nothing else (for rocprofv3 --pmc passes)")
@@ -195,6 +197,82 @@ def size_table(torch, api, warmup=1):
         out[name] = row
         del X, G
         torch.cuda.empty_cache()
+    return out
+
+
+def workload_table(torch, api, synth, calls=10):
+    """Time per step of the other named workloads, after the timed region: the
+    256 x 256 fp32 weight (Dion r = 64), the 12-layer d = 2048 GPT parameter set
+    (three shape-grouped Dion calls at r = 1/4 of the small side) and the
+    per-head split of a 4096 x 4096 projection (32 row blocks of 128 x 4096,
+    batched Newton-Schulz x5).  Inputs are drawn on the device from a seeded
+    generator with the workloads' distributions."""
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2000)
+    out = {}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        with Timer(torch) as t:
+            for _ in range(calls):
+                fn()
+        return t.ms / calls
+
+    def unit_cols(n, r):
+        q = torch.randn(n, r, generator=gen, device=dev)
+        return q / q.norm(dim=0, keepdim=True)
+
+    # single 256 x 256 fp32 weight, r = 64
+    wl = synth.WORKLOADS[1]
+    X = torch.randn(256, 256, generator=gen, device=dev) * 0.02
+    G = torch.randn(256, 256, generator=gen, device=dev)
+    M = torch.zeros(256, 256, device=dev)
+    Q = unit_cols(256, 64)
+    ws = api.workspace(api.dion_workspace_size(256, 256, 64), dev)
+    ms = timed(lambda: api.dion_step(X, G, M, Q, wl["mu"], wl["lr"], ws=ws))
+    out[wl["name"]] = {"dion_r64_ms": ms, "steps_per_s": 1000.0 / ms}
+
+    # 12-layer d = 2048 GPT parameter set, one shape-grouped call per shape
+    wl = synth.WORKLOADS[3]
+    groups = []
+    nbytes = flops = 0.0
+    for count, m, n in wl["groups"]:
+        r = min(m, n) // 4
+        Xs = [(torch.randn(m, n, generator=gen, device=dev) * 0.02).to(torch.bfloat16) for _ in range(count)]
+        Gs = [torch.randn(m, n, generator=gen, device=dev).to(torch.bfloat16) for _ in range(count)]
+        Ms = [torch.zeros(m, n, device=dev) for _ in range(count)]
+        Qs = [unit_cols(n, r) for _ in range(count)]
+        ws = api.workspace(api.dion_workspace_size(m, n, r, count), dev)
+        groups.append((Xs, Gs, Ms, Qs, ws))
+        b, f = dion_model(m, n, r)
+        nbytes += count * b
+        flops += count * f
+
+    def gpt_step():
+        for Xs, Gs, Ms, Qs, ws in groups:
+            api.dion_step_batched(Xs, Gs, Ms, Qs, wl["mu"], wl["lr"], ws=ws)
+    ms = timed(gpt_step)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out[wl["name"]] = {"dion_r_quarter_ms": ms, "steps_per_s": 1000.0 / ms, "matrices": 72,
+                       "GB/s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
+                       "TFLOP/s": flops / (ms * 1e-3) / 1e12}
+    del groups
+    torch.cuda.empty_cache()
+
+    # per-head: 32 row blocks of 128 x 4096 of one 4096 x 4096 projection
+    wl = synth.WORKLOADS[4]
+    G = torch.randn(4096, 4096, generator=gen, device=dev).to(torch.bfloat16)
+    O = torch.empty_like(G)
+    heads = [G[128 * h:128 * (h + 1)] for h in range(32)]
+    outs = [O[128 * h:128 * (h + 1)] for h in range(32)]
+    ws = api.workspace(api.ns_workspace_size(128, 4096, 32), dev)
+    ms = timed(lambda: api.newton_schulz_batched(heads, outs, steps=5, ws=ws))
+    nb, f = ns_model(128, 4096)
+    out[wl["name"]] = {"ns5_per_head_ms": ms, "steps_per_s": 1000.0 / ms, "heads": 32,
+                       "GB/s": 32 * nb / (ms * 1e-3) / 1e9,
+                       "hbm_frac": 32 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     return out
 
 
@@ -341,6 +419,7 @@ def main():
                 "executed_tflops": executed / (gemm_ms * 1e-3) / 1e12}
 
     sizes = None if args.no_sizes else size_table(torch, api)
+    workloads = None if args.no_sizes else workload_table(torch, api, synth)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -354,7 +433,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic", "config": info, "ms_per_step_one_stream": ms_serial,
         "paths": per_path, "roofline": roofline,
-        "cpu_baseline": cpu, "sizes": sizes,
+        "cpu_baseline": cpu, "sizes": sizes, "workloads": workloads,
     }
     print(json.dumps(line))
 

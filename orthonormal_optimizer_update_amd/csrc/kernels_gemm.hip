@@ -279,6 +279,20 @@ hipError_t launch_ns_gram(const NsGramArgs& a, int members, hipStream_t s) {
   return a.M > 128 ? ns_gram_t<CfgNsBig>(a, members, s) : ns_gram_t<CfgNsSmall>(a, members, s);
 }
 
+hipError_t launch_ns_gram_split(const NsGramArgs& a, const MatArg& part, int64_t split_stride,
+                                int splits, int kchunk, int members, hipStream_t s) {
+  if (a.M > 128 || splits < 2 || kchunk % 32 != 0) return hipErrorInvalidValue;
+  GemmParams<EpiStoreF32::Args> p{};
+  p.a = with_rows(a.x, a.M);
+  p.b0 = with_rows(a.x, a.M);
+  p.e.c = part;
+  p.e.split_stride = split_stride;
+  p.e.has_t = 0;
+  p.M = a.M; p.N = a.M; p.K = a.K;
+  p.splits = splits; p.kchunk = kchunk; p.tri = 0;
+  return run<CfgNsSmall, NsRow<CfgNsSmall>, NsRow<CfgNsSmall>, EpiStoreF32>(p, members, s);
+}
+
 hipError_t launch_ns_poly(const NsPolyArgs& a, int members, hipStream_t s) {
   if (a.c == 0.0f) return launch_ns_linear(a, members, s);
   return a.M > 128 ? ns_poly_t<CfgNsBig>(a, members, s) : ns_poly_t<CfgNsSmall>(a, members, s);

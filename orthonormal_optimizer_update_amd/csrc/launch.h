@@ -240,6 +240,10 @@ struct NsApplyArgs {
   int M, N, last, out_transposed;
 };
 hipError_t launch_ns_gram(const NsGramArgs& a, int members, hipStream_t s);
+// X X^T for a Gram side of at most 128 rows, split over k into fp32 partials
+// (member pointers in `part`, slice `split_stride` elements apart, ld = M).
+hipError_t launch_ns_gram_split(const NsGramArgs& a, const MatArg& part, int64_t split_stride,
+                                int splits, int kchunk, int members, hipStream_t s);
 hipError_t launch_ns_poly(const NsPolyArgs& a, int members, hipStream_t s);
 hipError_t launch_ns_linear(const NsPolyArgs& a, int members, hipStream_t s);  // c == 0
 hipError_t launch_ns_apply(const NsApplyArgs& a, bool out_bf16, int members, hipStream_t s);

@@ -176,6 +176,18 @@ bool plan_ns(int64_t m, int64_t n, int32_t batch, NsPlan* p) {
   s.off_bp = o;      o = align_up(o + mm * 2);
   // fp32 copy of Bp, used by the split-precision apply when M <= 128
   s.off_bp32 = o;    o = align_up(o + (s.M <= 128 ? mm * 4 : 0));
+  s.gram_splits = 1;
+  s.gram_kchunk = 0;
+  if (s.M <= 128 && s.M % 64 == 0) {
+    // one workgroup per CU over the chunk's members, at least 8 k steps of 32 each
+    int64_t want = cdiv(256, s.chunk), cap = s.N / 256;
+    if (want > cap) want = cap;
+    if (want > 1) {
+      s.gram_kchunk = static_cast<int>(cdiv(cdiv(s.N, want), 32) * 32);
+      s.gram_splits = static_cast<int>(cdiv(s.N, s.gram_kchunk));
+    }
+  }
+  s.off_gpart = o;   o = align_up(o + (s.gram_splits > 1 ? static_cast<size_t>(s.gram_splits) * mm * 4 : 0));
   s.off_partial = o; o = align_up(o + static_cast<size_t>(s.nparts) * 4);
   s.off_scale = o;   o = align_up(o + 4);
   s.member_bytes = o;

@@ -52,6 +52,11 @@ struct NsPlan {
   int64_t part_chunk;        // rows per sum-of-squares block
   size_t off_x32, off_xb0, off_xb1, off_xbt0, off_xbt1, off_a, off_bp, off_bp32, off_partial,
       off_scale;
+  // Gram side of 64 or 128 rows: X X^T is one tile per member, so it is split
+  // over k (gram_splits slices of gram_kchunk columns, fp32 partials at
+  // off_gpart) and reduced in a fixed order into A.
+  int gram_splits, gram_kchunk;
+  size_t off_gpart;
   size_t member_bytes;
   size_t total_bytes;
 };
