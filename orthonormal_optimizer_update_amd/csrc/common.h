@@ -16,7 +16,7 @@ typedef double doublex4 __attribute__((ext_vector_type(4)));
 
 // Most matrices one launch may address through its pointer tables.  Larger
 // groups are issued as several launches.
-constexpr int kMaxBatch = 16;
+constexpr int kMaxBatch = 32;
 
 // One operand as a kernel sees it: a pointer per group member, a leading
 // dimension shared by the group, its logical extent and whether 16-byte vector

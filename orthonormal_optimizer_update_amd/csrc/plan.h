@@ -9,7 +9,7 @@
 
 namespace ortho {
 
-constexpr int kMaxMembersPerLaunch = 16;  // must match kMaxBatch in common.h
+constexpr int kMaxMembersPerLaunch = 32;  // must match kMaxBatch in common.h
 constexpr size_t kWsAlign = 256;
 
 // Byte offsets of one member's regions inside the Dion workspace, and the
