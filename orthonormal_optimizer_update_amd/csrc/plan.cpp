@@ -200,7 +200,17 @@ bool plan_muon(int64_t m, int64_t n, int32_t batch, MuonPlan* p) {
   MuonPlan d{};
   if (!plan_ns(m, n, batch, &d.ns)) return false;
   d.ld_u = cdiv(n, 4) * 4;
-  d.off_u = align_up(d.ns.total_bytes);
+  // The step runs Newton-Schulz once per launch chunk, each call laid out for
+  // its own member count; U goes after the larger of the full and the last
+  // chunk's layouts.
+  size_t ns_bytes = d.ns.total_bytes;
+  const int32_t last = batch % d.ns.chunk;
+  if (last != 0) {
+    NsPlan tail;
+    if (!plan_ns(m, n, last, &tail)) return false;
+    if (tail.total_bytes > ns_bytes) ns_bytes = tail.total_bytes;
+  }
+  d.off_u = align_up(ns_bytes);
   d.u_bytes = align_up(static_cast<size_t>(m) * d.ld_u * 4);
   d.total_bytes = d.off_u + d.u_bytes * static_cast<size_t>(d.ns.chunk);
   *p = d;
