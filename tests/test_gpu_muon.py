@@ -117,3 +117,20 @@ def test_muon_batched_equals_single():
     torch.cuda.synchronize()
     for (sx, sm), bx, bm in zip(single, tXs, tMs):
         assert torch.equal(sx, bx) and torch.equal(sm, bm)
+
+
+def test_muon_batched_ragged_chunks():
+    """35 members: one launch chunk of 32 and a ragged one of 3 (each Newton-Schulz
+    call laid out for its own member count); every member matches its single call."""
+    m, n, b = 128, 256, 35
+    Gs = [to_dev(synth.gradient(81, m, n, 1, "bf16", index=i), "bf16") for i in range(b)]
+    X0 = [to_dev(synth.weight(81, m, n, "bf16", index=i), "bf16") for i in range(b)]
+    note("muon batched 35 members")
+    Xs = [x.clone() for x in X0]
+    Ms = [torch.zeros(m, n, device="cuda") for _ in range(b)]
+    api.muon_step_batched(Xs, Gs, Ms, 0.9, 0.03)
+    for i in range(b):
+        x, mm = X0[i].clone(), torch.zeros(m, n, device="cuda")
+        api.muon_step(x, Gs[i], mm, 0.9, 0.03)
+        torch.cuda.synchronize()
+        assert torch.equal(x, Xs[i]) and torch.equal(mm, Ms[i]), i
