@@ -26,9 +26,12 @@ public pages about microsoft/dion):
   "parity unpinned" as to fidelity: the pages name Muon's momentum but print no
   formula; the pins check the step against its own definition.
 
-Every reading that the pages leave open (where mu enters, the QR sign
-convention, column normalisation of the new right factor, the Newton-Schulz
-coefficients) is listed in the design doc together with the reason for it.
+Where the pages leave a step open, the oracle takes the plainest reading they
+support: mu is the error-feedback decay (B = M + G, M' = B - (1 - mu) P R^T);
+P is the Q-factor of the thin QR with a positive diagonal in R; the new right
+factor is R with unit-norm columns; the update scale is 1; Newton-Schulz uses
+Muon's quintic (3.4445, -4.7750, 2.0315), eps = 1e-7, and works on the wide
+orientation; Muon's momentum is the heavy-ball buffer mu M + G.
 
 Pins: ``tests/test_oracle_pins.py`` checks these functions against closed forms
 (SVD), invariants of the definitions, and an independent brute-force
