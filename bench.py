@@ -303,7 +303,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU sharding "
-              "is not part of this build.", file=sys.stderr)
+              "is not implemented.", file=sys.stderr)
         sys.exit(2)
     if args.workload != 2:
         print("only --workload 2 is a bench line; the other workloads are parity cases",
