@@ -170,3 +170,16 @@ def test_paths_on_separate_streams_match_one_stream():
         for k in ("X", "M", "Q"):
             assert torch.equal(one[r][k], many[r][k]), (r, k)
     assert torch.equal(one["ns"]["out"], many["ns"]["out"])
+
+
+def test_batched_newton_schulz_ragged_chunks_split_gram():
+    """40 blocks of 64 x 512: two launch chunks (32 + 8) with the Gram split
+    over k (a 64-row Gram side); every member matches the oracle."""
+    b, m, n = 40, 64, 512
+    Gs = [synth.gradient(90, m, n, 1, "bf16", index=i) for i in range(b)]
+    tG = [to_dev(g, "bf16") for g in Gs]
+    note("ns batched 40 x 64x512")
+    outs = api.newton_schulz_batched(tG, steps=5)
+    torch.cuda.synchronize()
+    for i in range(b):
+        assert rel(to_host(outs[i]), oracle.newton_schulz(Gs[i])) <= TOL["bf16"], i
