@@ -93,10 +93,6 @@ hipError_t dion_update_f32(const DionUpdateArgs& a, int members, hipStream_t s) 
 }
 
 bool fast_ok(int M, int N, int K, const MatArg& a, const MatArg& b);
-// Up to this rank the streaming update (memory terms loaded under the products,
-// 16-byte accesses) beats both the 256 x 128 two-accumulator kernel and the
-// 256 x 256 pair.
-constexpr int kUpdStreamMaxRank = 512;
 template <class Epi>
 hipError_t run_fast(GemmParams<typename Epi::Args>& p, int members, hipStream_t s);
 
@@ -109,12 +105,12 @@ static bool rows16(const MatArg& t, int members, size_t esz) {
 }
 
 hipError_t dion_update_bf16(const DionUpdateArgs& a, int members, hipStream_t s) {
-  if (a.rank <= kUpdStreamMaxRank && dion_update_stream_ok(a, members))
-    return launch_dion_update_stream(a, members, s);
-  // At small ranks the step is bound by its 14 mn bytes, which the fused
-  // 256 x 128 two-accumulator kernel streams as well; from r = 1024 on the
-  // products dominate and the 256 x 256 kernel is faster.
-  if (a.rank >= 1024 && fast_ok(a.M, a.N, a.rank, a.pb, a.rb) && a.qb.vec && a.qb.ld % 8 == 0 &&
+  // From r = 512 on, the products weigh enough that the 256 x 256 pair is the
+  // fastest (12-layer GPT groups at r = 512: 15.7 ms per step against 16.5 with
+  // the streaming kernel); at r = 256 the step is bound by its 14 mn bytes and
+  // the streaming kernel (memory terms loaded under the products, 16-byte
+  // accesses) is; the two-accumulator 256 x 128 kernel takes every other case.
+  if (a.rank >= 512 && fast_ok(a.M, a.N, a.rank, a.pb, a.rb) && a.qb.vec && a.qb.ld % 8 == 0 &&
       rows16(a.m, members, 4) && rows16(a.g, members, 2) && rows16(a.x, members, 2)) {
     // two launches of the 256 x 256 kernel: momentum, then weight
     GemmParams<EpiDionFastM::Args> pm{};
@@ -131,6 +127,7 @@ hipError_t dion_update_bf16(const DionUpdateArgs& a, int members, hipStream_t s)
     px.M = a.M; px.N = a.N; px.K = a.rank;
     return run_fast<EpiDionFastX>(px, members, s);
   }
+  if (dion_update_stream_ok(a, members)) return launch_dion_update_stream(a, members, s);
   GemmParams<EpiDionPre::Args> p{};
   p.a = with_rows(a.pb, a.M);
   p.b0 = with_rows(a.rb, a.N);

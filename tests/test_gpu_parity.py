@@ -97,9 +97,10 @@ def test_ns_square_4096_deterministic():
 
 DION_SHAPES = [(96, 80, 16), (300, 200, 37), (513, 257, 64), (128, 1000, 128), (1000, 128, 100),
                (40, 30, 30), (7, 9, 1), (700, 900, 250),
-               # bf16: whole 128 x 32 tiles of the streaming update at r = 256 and
-               # r = 512; r = 1024 on the two-accumulator kernel (1152 rows: not 256-divisible)
-               (384, 352, 256), (768, 1024, 512), (1152, 2048, 1024)]
+               # bf16: the streaming update at r = 256 and (rows not 256-divisible)
+               # r = 512; the 256 x 256 pair at r = 512; r = 1024 on the
+               # two-accumulator kernel (1152 rows: not 256-divisible)
+               (384, 352, 256), (640, 1056, 512), (768, 1024, 512), (1152, 2048, 1024)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
