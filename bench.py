@@ -10,7 +10,7 @@ The three are independent and run on three streams; the same steps on one
 stream are reported beside the headline.
 Inputs are synthetic, seeded and resident in HBM before timing starts.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sizes]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sizes] [--workload 1|2|3|4]
 
 Prints ONE JSON line.  Besides the headline step it carries a per-size table
 (time per call, modeled GB/s and TFLOP/s and their fraction of peak) for square
@@ -200,13 +200,13 @@ def size_table(torch, api, warmup=1):
     return out
 
 
-def workload_table(torch, api, synth, calls=10):
-    """Time per step of the other named workloads, after the timed region: the
-    256 x 256 fp32 weight (Dion r = 64), the 12-layer d = 2048 GPT parameter set
-    (three shape-grouped Dion calls at r = 1/4 of the small side) and the
-    per-head split of a 4096 x 4096 projection (32 row blocks of 128 x 4096,
-    batched Newton-Schulz x5).  Inputs are drawn on the device from a seeded
-    generator with the workloads' distributions."""
+def workload_table(torch, api, synth, calls=10, only=None):
+    """Time per step of the other named workloads (all of them, or workload
+    ``only``): the 256 x 256 fp32 weight (Dion r = 64), the 12-layer d = 2048
+    GPT parameter set (three shape-grouped Dion calls at r = 1/4 of the small
+    side) and the per-head split of a 4096 x 4096 projection (32 row blocks of
+    128 x 4096, batched Newton-Schulz x5).  Inputs are drawn on the device from
+    a seeded generator with the workloads' distributions."""
     dev = "cuda"
     gen = torch.Generator(device=dev)
     gen.manual_seed(2000)
@@ -224,55 +224,56 @@ def workload_table(torch, api, synth, calls=10):
         q = torch.randn(n, r, generator=gen, device=dev)
         return q / q.norm(dim=0, keepdim=True)
 
-    # single 256 x 256 fp32 weight, r = 64
-    wl = synth.WORKLOADS[1]
-    X = torch.randn(256, 256, generator=gen, device=dev) * 0.02
-    G = torch.randn(256, 256, generator=gen, device=dev)
-    M = torch.zeros(256, 256, device=dev)
-    Q = unit_cols(256, 64)
-    ws = api.workspace(api.dion_workspace_size(256, 256, 64), dev)
-    ms = timed(lambda: api.dion_step(X, G, M, Q, wl["mu"], wl["lr"], ws=ws))
-    out[wl["name"]] = {"dion_r64_ms": ms, "steps_per_s": 1000.0 / ms}
+    if only in (None, 1):  # single 256 x 256 fp32 weight, r = 64
+        wl = synth.WORKLOADS[1]
+        X = torch.randn(256, 256, generator=gen, device=dev) * 0.02
+        G = torch.randn(256, 256, generator=gen, device=dev)
+        M = torch.zeros(256, 256, device=dev)
+        Q = unit_cols(256, 64)
+        ws = api.workspace(api.dion_workspace_size(256, 256, 64), dev)
+        ms = timed(lambda: api.dion_step(X, G, M, Q, wl["mu"], wl["lr"], ws=ws))
+        out[wl["name"]] = {"dion_r64_ms": ms, "steps_per_s": 1000.0 / ms}
 
-    # 12-layer d = 2048 GPT parameter set, one shape-grouped call per shape
-    wl = synth.WORKLOADS[3]
-    groups = []
-    nbytes = flops = 0.0
-    for count, m, n in wl["groups"]:
-        r = min(m, n) // 4
-        Xs = [(torch.randn(m, n, generator=gen, device=dev) * 0.02).to(torch.bfloat16) for _ in range(count)]
-        Gs = [torch.randn(m, n, generator=gen, device=dev).to(torch.bfloat16) for _ in range(count)]
-        Ms = [torch.zeros(m, n, device=dev) for _ in range(count)]
-        Qs = [unit_cols(n, r) for _ in range(count)]
-        ws = api.workspace(api.dion_workspace_size(m, n, r, count), dev)
-        groups.append((Xs, Gs, Ms, Qs, ws))
-        b, f = dion_model(m, n, r)
-        nbytes += count * b
-        flops += count * f
+    if only in (None, 3):  # 12-layer d = 2048 GPT parameter set, one call per shape group
+        wl = synth.WORKLOADS[3]
+        groups = []
+        nbytes = flops = 0.0
+        for count, m, n in wl["groups"]:
+            r = min(m, n) // 4
+            Xs = [(torch.randn(m, n, generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+                  for _ in range(count)]
+            Gs = [torch.randn(m, n, generator=gen, device=dev).to(torch.bfloat16) for _ in range(count)]
+            Ms = [torch.zeros(m, n, device=dev) for _ in range(count)]
+            Qs = [unit_cols(n, r) for _ in range(count)]
+            ws = api.workspace(api.dion_workspace_size(m, n, r, count), dev)
+            groups.append((Xs, Gs, Ms, Qs, ws))
+            b, f = dion_model(m, n, r)
+            nbytes += count * b
+            flops += count * f
 
-    def gpt_step():
-        for Xs, Gs, Ms, Qs, ws in groups:
-            api.dion_step_batched(Xs, Gs, Ms, Qs, wl["mu"], wl["lr"], ws=ws)
-    ms = timed(gpt_step)
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    out[wl["name"]] = {"dion_r_quarter_ms": ms, "steps_per_s": 1000.0 / ms, "matrices": 72,
-                       "GB/s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
-                       "TFLOP/s": flops / (ms * 1e-3) / 1e12}
-    del groups
-    torch.cuda.empty_cache()
+        def gpt_step():
+            for Xs, Gs, Ms, Qs, ws in groups:
+                api.dion_step_batched(Xs, Gs, Ms, Qs, wl["mu"], wl["lr"], ws=ws)
+        ms = timed(gpt_step)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[wl["name"]] = {"dion_r_quarter_ms": ms, "steps_per_s": 1000.0 / ms, "matrices": 72,
+                           "GB/s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
+                           "TFLOP/s": flops / (ms * 1e-3) / 1e12}
+        del groups
+        torch.cuda.empty_cache()
 
-    # per-head: 32 row blocks of 128 x 4096 of one 4096 x 4096 projection
-    wl = synth.WORKLOADS[4]
-    G = torch.randn(4096, 4096, generator=gen, device=dev).to(torch.bfloat16)
-    O = torch.empty_like(G)
-    heads = [G[128 * h:128 * (h + 1)] for h in range(32)]
-    outs = [O[128 * h:128 * (h + 1)] for h in range(32)]
-    ws = api.workspace(api.ns_workspace_size(128, 4096, 32), dev)
-    ms = timed(lambda: api.newton_schulz_batched(heads, outs, steps=5, ws=ws))
-    nb, f = ns_model(128, 4096)
-    out[wl["name"]] = {"ns5_per_head_ms": ms, "steps_per_s": 1000.0 / ms, "heads": 32,
-                       "GB/s": 32 * nb / (ms * 1e-3) / 1e9,
-                       "hbm_frac": 32 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    if only in (None, 4):  # per-head: 32 row blocks of 128 x 4096 of one 4096 x 4096 projection
+        wl = synth.WORKLOADS[4]
+        G = torch.randn(4096, 4096, generator=gen, device=dev).to(torch.bfloat16)
+        O = torch.empty_like(G)
+        heads = [G[128 * h:128 * (h + 1)] for h in range(32)]
+        outs = [O[128 * h:128 * (h + 1)] for h in range(32)]
+        ws = api.workspace(api.ns_workspace_size(128, 4096, 32), dev)
+        ms = timed(lambda: api.newton_schulz_batched(heads, outs, steps=5, ws=ws))
+        nb, _ = ns_model(128, 4096)
+        gbs = 32 * nb / (ms * 1e-3) / 1e9
+        out[wl["name"]] = {"ns5_per_head_ms": ms, "steps_per_s": 1000.0 / ms, "heads": 32,
+                           "GB/s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS}
     return out
 
 
@@ -305,14 +306,20 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU sharding "
               "is not implemented.", file=sys.stderr)
         sys.exit(2)
-    if args.workload != 2:
-        print("only --workload 2 is a bench line; the other workloads are parity cases",
-              file=sys.stderr)
+    if args.workload not in (1, 2, 3, 4):
+        print("--workload 1, 2 (the bench line), 3 or 4; the Llama-405B shapes are in the per-size "
+              "table of the default run", file=sys.stderr)
         sys.exit(2)
     import torch
     from orthonormal_optimizer_update_amd import api, synth
     api.lib()
     torch.cuda.set_device(0)
+    if args.workload != 2:
+        # one named workload alone, after one warm-up (for kernel profiles of it)
+        table = workload_table(torch, api, synth, calls=args.steps, only=args.workload)
+        name, row = next(iter(table.items()))
+        print(json.dumps({"workload": name, **row}))
+        return
     names, run_path, ns_steps, info, (m, n) = workload2(torch, api, synth)
 
     if args.counter_sample:
