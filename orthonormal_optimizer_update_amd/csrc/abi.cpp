@@ -345,22 +345,35 @@ ortho_status run_ns(int32_t batch, const ortho_mat* G, const ortho_mat* Out, int
       const int cur = it & 1;
       NsGramArgs g1{};
       g1.x = xb[cur]; g1.a = ta; g1.M = M; g1.K = N;
+      const bool small_poly = pl.gram_splits > 1 && c != 0.0f;
       if (pl.gram_splits > 1) {
         const MatArg gpart = ws_table(base, mb, pl.off_gpart, nb, M, M, M, 4, 16);
         const int64_t slice = static_cast<int64_t>(M) * M;
         ORTHO_TRY(launch_ns_gram_split(g1, gpart, slice, pl.gram_splits, pl.gram_kchunk, nb, s));
-        RedPiecesArgs rg{};
-        rg.part = reinterpret_cast<const float*>(base + pl.off_gpart);
-        rg.part_member_stride = static_cast<int64_t>(mb / 4);
-        rg.slice = slice; rg.splits = pl.gram_splits; rg.rows = M; rg.cols = M;
-        rg.out_bf16 = ta; rg.has_bf16 = 1;
-        ORTHO_TRY(launch_reduce_pieces(rg, nb, s));
+        if (small_poly) {
+          // the reduce and the polynomial in one launch, one workgroup per member
+          NsSmallPolyArgs sp{};
+          sp.part = reinterpret_cast<const float*>(base + pl.off_gpart);
+          sp.part_member_stride = static_cast<int64_t>(mb / 4);
+          sp.slice = slice; sp.splits = pl.gram_splits; sp.M = M;
+          sp.bp = tbp; sp.bp32 = tbp32; sp.b = b; sp.c = c;
+          ORTHO_TRY(launch_ns_small_poly(sp, nb, s));
+        } else {
+          RedPiecesArgs rg{};
+          rg.part = reinterpret_cast<const float*>(base + pl.off_gpart);
+          rg.part_member_stride = static_cast<int64_t>(mb / 4);
+          rg.slice = slice; rg.splits = pl.gram_splits; rg.rows = M; rg.cols = M;
+          rg.out_bf16 = ta; rg.has_bf16 = 1;
+          ORTHO_TRY(launch_reduce_pieces(rg, nb, s));
+        }
       } else {
         ORTHO_TRY(launch_ns_gram(g1, nb, s));
       }
-      NsPolyArgs g2{};
-      g2.a = ta; g2.bp = tbp; g2.bp32 = tbp32; g2.b = b; g2.c = c; g2.M = M;
-      ORTHO_TRY(launch_ns_poly(g2, nb, s));
+      if (!small_poly) {
+        NsPolyArgs g2{};
+        g2.a = ta; g2.bp = tbp; g2.bp32 = tbp32; g2.b = b; g2.c = c; g2.M = M;
+        ORTHO_TRY(launch_ns_poly(g2, nb, s));
+      }
       NsApplyArgs g3{};
       g3.bp = tbp; g3.xbt = xbt[cur]; g3.x32 = x32; g3.xb_next = xb[cur ^ 1];
       g3.xbt_next = xbt[cur ^ 1]; g3.out = tOut; g3.bp32 = tbp32; g3.a = a;

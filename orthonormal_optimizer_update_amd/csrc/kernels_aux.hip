@@ -340,6 +340,93 @@ __global__ __launch_bounds__(256) void colnorm_kernel(ColnormArgs a) {
   }
 }
 
+// Newton-Schulz polynomial for a Gram side of M = 64 or 128 rows, fused with the
+// reduction of the split Gram.  One workgroup per member: A = the sum of the
+// k-split partials in slice order, rounded to bf16 into LDS (the value the
+// separate reduce would store); then Bp = c ((b/c) A + A A) on the matrix cores
+// with A read from LDS for both operands (A is symmetric).  The 2 x 2 wave
+// layout, the preloaded (b/c) A term and the k order of the products are those
+// of the 128 x 128 product kernel, so the result has the same bits.
+template <int M>
+__global__ __launch_bounds__(256) void ns_small_poly_kernel(NsSmallPolyArgs a) {
+  constexpr int LD = M + 8;           // bf16 per LDS row; +16 B spreads rows over the banks
+  constexpr int WT = M / 2, NB = WT / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[M * LD];
+  const int bi = blockIdx.x;
+  const float* part = a.part + bi * a.part_member_stride;
+  // each thread owns PER groups of four; all PER loads of one slice are issued
+  // before any is summed, so the slices cost a few load latencies, not M * M / 1024
+  constexpr int PER = M * M / 4 / 256;
+  floatx4 v[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) v[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+  for (int sl = 0; sl < a.splits; ++sl) {
+    const float* src = part + sl * a.slice;
+    floatx4 t[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q)
+      t[q] = *reinterpret_cast<const floatx4*>(src + (threadIdx.x + q * 256) * 4);
+#pragma unroll
+    for (int q = 0; q < PER; ++q) v[q] += t[q];
+  }
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int e4 = threadIdx.x + q * 256;
+    const int i = e4 / (M / 4), j = (e4 % (M / 4)) * 4;
+    *reinterpret_cast<uint2*>(sA + i * LD + j) = pack_bf16x4(v[q]);
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const float boc = a.b / a.c;
+  floatx16 acc[NB][NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int row = wm * WT + i * 32 + g * 8 + (lane >> 5) * 4 + t;
+          const int col = wn * WT + j * 32 + (lane & 31);
+          acc[i][j][g * 4 + t] = boc * bf16_bits_to_f32(sA[row * LD + col]);
+        }
+  const int fk = (lane >> 5) * 8;
+#pragma unroll
+  for (int k0 = 0; k0 < M; k0 += 16) {
+    bf16x8 af[NB], bfr[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      af[i] = *reinterpret_cast<const bf16x8*>(sA + (wm * WT + i * 32 + (lane & 31)) * LD + k0 + fk);
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      bfr[j] = *reinterpret_cast<const bf16x8*>(sA + (wn * WT + j * 32 + (lane & 31)) * LD + k0 + fk);
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  }
+  uint16_t* bp = static_cast<uint16_t*>(const_cast<void*>(a.bp.p[bi]));
+  float* bp32 = static_cast<float*>(const_cast<void*>(a.bp32.p[bi]));
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int row = wm * WT + i * 32 + g * 8 + (lane >> 5) * 4 + t;
+          const int col = wn * WT + j * 32 + (lane & 31);
+          const float y = a.c * acc[i][j][g * 4 + t];
+          bp[(int64_t)row * a.bp.ld + col] = to_bf16_bits(y);
+          bp32[(int64_t)row * a.bp32.ld + col] = y;
+        }
+}
+
 // ---------------------------------------------------------------------------
 // Muon step around Newton-Schulz: momentum buffer and SGD-form update
 // ---------------------------------------------------------------------------
@@ -1283,6 +1370,16 @@ hipError_t launch_split_rows(const SplitRowsArgs& a, int members, hipStream_t s)
   dim3 grid(cdiv(a.cols, 64), cdiv(a.rows, 64), members);
   if (a.np == 2) hipLaunchKernelGGL(split_rows_kernel<2>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(split_rows_kernel<3>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ns_small_poly(const NsSmallPolyArgs& a, int members, hipStream_t s) {
+  if (a.M == 128)
+    hipLaunchKernelGGL(ns_small_poly_kernel<128>, dim3(members), dim3(256), 0, s, a);
+  else if (a.M == 64)
+    hipLaunchKernelGGL(ns_small_poly_kernel<64>, dim3(members), dim3(256), 0, s, a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -245,6 +245,17 @@ hipError_t launch_ns_gram(const NsGramArgs& a, int members, hipStream_t s);
 hipError_t launch_ns_gram_split(const NsGramArgs& a, const MatArg& part, int64_t split_stride,
                                 int splits, int kchunk, int members, hipStream_t s);
 hipError_t launch_ns_poly(const NsPolyArgs& a, int members, hipStream_t s);
+// Gram side of 64 or 128 rows after the split Gram: per member, A = sum of the
+// k-split partials (slice order) rounded to bf16, then Bp = c ((b/c) A + A A) into
+// bp (bf16) and bp32 (fp32), in one launch with one workgroup per member.
+struct NsSmallPolyArgs {
+  const float* part;
+  int64_t part_member_stride, slice;
+  int splits, M;
+  MatArg bp, bp32;
+  float b, c;
+};
+hipError_t launch_ns_small_poly(const NsSmallPolyArgs& a, int members, hipStream_t s);
 hipError_t launch_ns_linear(const NsPolyArgs& a, int members, hipStream_t s);  // c == 0
 hipError_t launch_ns_apply(const NsApplyArgs& a, bool out_bf16, int members, hipStream_t s);
 
