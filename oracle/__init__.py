@@ -20,6 +20,15 @@ public pages about microsoft/dion):
   agentlenshq "microsoft/dion", section "How it works"; paper page "Dion:
   Distributed Orthonormalized Updates", abstract.
 
+* ``normuon_step`` -- the Muon step with neuron-wise (row) normalisation of the
+  orthogonalised momentum before the update (``row_normalize``).  agentlenshq
+  "microsoft/dion", section "How it works"; hysenlabs "Microsoft Dion:
+  orthonormal optimizers that assume DTensor parallelism", section "Dion3 is not
+  a retuning of Dion2, and the README says so".  The
+  pages print no formula: the reading is a stateless rescale of every row to
+  the common norm ||U||_F / sqrt(m), which keeps the total norm; "parity
+  unpinned" as to fidelity, pinned against its own definition.
+
 * ``muon_step`` -- the Muon step around the Newton-Schulz path: a heavy-ball
   momentum buffer, its Newton-Schulz orthogonalisation, and the SGD-form update.
   Same talk, same passages.  The momentum form is the plainest reading and
@@ -52,4 +61,7 @@ from .dion_ref import (  # noqa: F401
     newton_schulz_batched,
     muon_step,
     muon_step_batched,
+    row_normalize,
+    normuon_step,
+    normuon_step_batched,
 )

@@ -71,3 +71,15 @@ def newton_schulz(G, steps, abc, eps):
         BX = matmul(Bp, Xk)
         Xk = [[a * Xk[i][j] + BX[i][j] for j in range(len(Xk[0]))] for i in range(len(Xk))]
     return transpose(Xk) if tall else Xk
+
+
+def row_normalize(U):
+    """Rows rescaled to the common norm sqrt(sum of all squares / rows), each
+    by its own exactly rounded norm; zero rows stay zero."""
+    U = _mat(U)
+    m = len(U)
+    norms = [math.sqrt(math.fsum(v * v for v in row)) for row in U]
+    total = math.sqrt(math.fsum(v * v for row in U for v in row))
+    target = total / math.sqrt(m)
+    return [[v * target / nrm for v in row] if nrm > 0.0 else [0.0] * len(row)
+            for row, nrm in zip(U, norms)]

@@ -229,3 +229,54 @@ def muon_step_batched(Xs, Gs, Ms, mu, lr, scale=1.0, steps=5, abc=MUON_ABC, eps=
     """A group of independent same-shape matrices: one ``muon_step`` each."""
     return [muon_step(X, G, M, mu, lr, scale, steps, abc, eps, x_dtype)
             for X, G, M in zip(Xs, Gs, Ms)]
+
+
+def row_normalize(U):
+    """Neuron-wise normalisation of an orthogonalised update, in fp64.
+
+    Pages: agentlenshq "microsoft/dion", section "How it works" (NorMuon adds
+    neuron-wise normalisation to Muon), and hysenlabs "Microsoft Dion:
+    orthonormal optimizers that assume DTensor parallelism", section "Dion3 is
+    not a retuning of Dion2, and the README says so" (per-neuron normalisation
+    redistributes the update across rows).
+    Neither page prints a formula; the plainest reading they support is a
+    stateless rescale of each row (one output neuron) to a common norm that
+    keeps the update's total Frobenius norm:
+        t   = ||U||_F / sqrt(m)
+        V_i = U_i * t / ||U_i||_2      (a zero row stays zero)
+    """
+    U = _f64(U)
+    m = U.shape[0]
+    row_sq = np.einsum("ij,ij->i", U, U)
+    target = np.sqrt(row_sq.sum() / m) if m > 0 else 0.0
+    f = np.zeros(m)
+    nz = row_sq > 0.0
+    f[nz] = target / np.sqrt(row_sq[nz])
+    return U * f[:, None]
+
+
+def normuon_step(X, G, M, mu: float, lr: float, scale: float = 1.0, steps: int = 5,
+                 abc=MUON_ABC, eps: float = NS_EPS, x_dtype: str = "bf16") -> dict:
+    """One NorMuon step: the Muon step with the orthogonalised momentum
+    normalised per neuron (row) before it is applied.
+        M' = mu M + G
+        U  = newton_schulz(M', steps, abc, eps)
+        V  = row_normalize(U)
+        X' = X - lr * scale * V, rounded to ``x_dtype``
+    Returns ``X`` (rounded), ``X_exact``, ``dX`` (= -lr * scale * V), ``M``,
+    ``U`` and ``V``.
+    """
+    X, G, M = _f64(X), _f64(G), _f64(M)
+    M_new = _muon_momentum(M, G, float(mu))
+    U = newton_schulz(M_new, steps, abc, eps)
+    V = row_normalize(U)
+    dX = -float(lr) * float(scale) * V
+    X_exact = X + dX
+    return dict(X=round_to_dtype(X_exact, x_dtype), X_exact=X_exact, dX=dX, M=M_new, U=U, V=V)
+
+
+def normuon_step_batched(Xs, Gs, Ms, mu, lr, scale=1.0, steps=5, abc=MUON_ABC, eps=NS_EPS,
+                         x_dtype="bf16"):
+    """A group of independent same-shape matrices: one ``normuon_step`` each."""
+    return [normuon_step(X, G, M, mu, lr, scale, steps, abc, eps, x_dtype)
+            for X, G, M in zip(Xs, Gs, Ms)]

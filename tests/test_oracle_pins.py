@@ -381,3 +381,88 @@ def test_mutant_muon_caught(monkeypatch, name):
     attr, fn = MUON_MUTANTS[name]
     monkeypatch.setattr(dion_ref, attr, fn)
     assert not (_muon_pins(np.random.default_rng(11)) <= 1e-6)
+
+
+# ----------------------------------------------------------------------------
+# NorMuon step: neuron-wise (row) normalisation of the orthogonalised momentum
+# ----------------------------------------------------------------------------
+
+def _normuon_pins(rng):
+    """Max error over the row-normalisation pins: equal row norms, total norm
+    kept, each row a positive multiple of its input row, idempotence, fixed
+    points (orthogonal and orthonormal-row matrices), a diagonal closed form,
+    the zero-row case, a loop formulation, and the step built around it."""
+    errs = []
+    for shape in [(14, 23), (23, 14)]:
+        U = rng.standard_normal(shape) * rng.uniform(0.1, 3.0, size=(shape[0], 1))
+        V = dion_ref.row_normalize(U)
+        rn = np.linalg.norm(V, axis=1)
+        errs.append(np.abs(rn - rn.mean()).max())
+        errs.append(abs(np.linalg.norm(V) - np.linalg.norm(U)) / np.linalg.norm(U))
+        cos = (V * U).sum(1) / (np.linalg.norm(V, axis=1) * np.linalg.norm(U, axis=1))
+        errs.append(np.abs(cos - 1.0).max())
+        errs.append(np.abs(dion_ref.row_normalize(V) - V).max())
+    # rows of an orthogonal matrix, or of a matrix with orthonormal rows, already
+    # share one norm with the right total: fixed points
+    Qsq = np.linalg.qr(rng.standard_normal((12, 12)))[0]
+    errs.append(np.abs(dion_ref.row_normalize(Qsq) - Qsq).max())
+    W = np.linalg.qr(rng.standard_normal((20, 9)))[0].T
+    errs.append(np.abs(dion_ref.row_normalize(W) - W).max())
+    # diag(d): row i is d_i e_i, so it becomes sign(d_i) times the RMS of d
+    d = np.array([3.0, -0.5, 2.0, 0.25, -1.0])
+    V = dion_ref.row_normalize(np.diag(d))
+    errs.append(np.abs(V - np.diag(np.sign(d) * np.sqrt(np.mean(d * d)))).max())
+    # a zero row stays zero and scaling the input scales the output
+    U = rng.standard_normal((6, 8))
+    U[2] = 0.0
+    V = dion_ref.row_normalize(U)
+    errs.append(np.abs(V[2]).max())
+    errs.append(np.abs(dion_ref.row_normalize(2.5 * U) - 2.5 * V).max())
+    # independent loop formulation
+    U = rng.standard_normal((5, 7)) * np.array([[0.3], [1.0], [4.0], [0.7], [2.0]])
+    errs.append(np.abs(dion_ref.row_normalize(U) - np.array(brute.row_normalize(U))).max())
+    # the step: heavy-ball buffer, Newton-Schulz closed form, row normalisation,
+    # SGD form; for a wide matrix the exact polar factor has unit rows, so the
+    # normalisation only corrects the quintic's spread
+    m, n, mu = 10, 24, 0.9
+    X = rng.standard_normal((m, n)) * 0.02
+    M = rng.standard_normal((m, n))
+    G = rng.standard_normal((m, n))
+    out = dion_ref.normuon_step(X, G, M, mu, lr=0.03, scale=1.3, x_dtype="f32")
+    errs.append(np.abs(out["M"] - (mu * M + G)).max())
+    errs.append(np.abs(out["U"] - quintic_spectral(out["M"])).max())
+    errs.append(np.abs(out["V"] - dion_ref.row_normalize(out["U"])).max())
+    errs.append(np.abs((out["X_exact"] - X) + 0.03 * 1.3 * out["V"]).max())
+    rn = np.linalg.norm(out["V"], axis=1)
+    errs.append(np.abs(rn - np.linalg.norm(out["U"]) / np.sqrt(m)).max())
+    return max(errs)
+
+
+def test_normuon_pins():
+    assert _normuon_pins(np.random.default_rng(23)) <= 1e-12
+
+
+_ROW_NORMALIZE = dion_ref.row_normalize
+
+
+def _col_normalize(U):
+    return _ROW_NORMALIZE(np.asarray(U).T).T
+
+
+NORMUON_MUTANTS = {
+    "columns_instead_of_rows": ("row_normalize", _col_normalize),
+    "unit_rows": ("row_normalize",
+                  lambda U: np.asarray(U) / np.linalg.norm(U, axis=1, keepdims=True)),
+    "target_over_m": ("row_normalize",
+                      lambda U: np.asarray(U) * (np.linalg.norm(U) / len(U))
+                      / np.linalg.norm(U, axis=1, keepdims=True)),
+    "normalisation_dropped": ("row_normalize", lambda U: np.asarray(U, dtype=np.float64)),
+}
+
+
+@pytest.mark.parametrize("name", list(NORMUON_MUTANTS))
+def test_mutant_normuon_caught(monkeypatch, name):
+    attr, fn = NORMUON_MUTANTS[name]
+    monkeypatch.setattr(dion_ref, attr, fn)
+    # the loop formulation and the closed forms do not go through the mutant
+    assert not (_normuon_pins(np.random.default_rng(23)) <= 1e-6)
