@@ -194,6 +194,14 @@ def size_table(torch, api, warmup=1):
             row["muon5"] = {"ms": ms, "steps_per_s": 1000.0 / ms, "TFLOP/s": tfs,
                             "mfma_frac": tfs / PEAK_BF16_TFLOPS}
             del M, ws
+            # NorMuon: the Muon step with the orthogonalised rows normalised
+            M = torch.zeros(m, n, device=dev)
+            ws = api.workspace(api.normuon_workspace_size(m, n), dev)
+            ms = timed(lambda: api.normuon_step(X, G, M, 0.95, 0.02, ws=ws))
+            tfs = flops / (ms * 1e-3) / 1e12
+            row["normuon5"] = {"ms": ms, "steps_per_s": 1000.0 / ms, "TFLOP/s": tfs,
+                               "mfma_frac": tfs / PEAK_BF16_TFLOPS}
+            del M, ws
         out[name] = row
         del X, G
         torch.cuda.empty_cache()

@@ -2,7 +2,7 @@
  * ortho.h -- C-ABI of libortho.so: the per-matrix orthonormalized optimizer step
  * on one AMD Instinct MI355X (gfx950).
  *
- * Three operations, each for one matrix and for a group of same-shape matrices:
+ * Four operations, each for one matrix and for a group of same-shape matrices:
  *
  *   dion_step      Dion's amortised power iteration with error feedback.
  *                  MSR talk "Dion: The distributed orthonormal update revolution
@@ -18,6 +18,8 @@
  *                      X' = X - lr * scale * P Q'^T          (SGD form)
  *   muon_step      the whole Muon step around newton_schulz: momentum buffer,
  *                  its orthogonalisation, SGD-form update (declared below).
+ *   normuon_step   muon_step with the orthogonalised momentum normalised per
+ *                  neuron (row) before the update (declared below).
  *   newton_schulz  Muon's Newton-Schulz orthogonalisation, the full-rank
  *                  comparison path.  Same talk, passage contrasting SGD with an
  *                  orthonormal update (take U V^T of the SVD) and the passage on
@@ -175,6 +177,37 @@ ortho_status muon_step(ortho_mat X, ortho_mat G, ortho_mat M, int32_t steps, con
 ortho_status muon_step_batched(int32_t batch, const ortho_mat* X, const ortho_mat* G,
                                const ortho_mat* M, int32_t steps, const float* abc, float mu,
                                float lr, float scale, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of device workspace for normuon_step (batch = 1) or
+ * normuon_step_batched on `batch` matrices of m x n: the Muon workspace plus m
+ * floats per member.  Returns 0 for invalid arguments. */
+size_t ortho_normuon_workspace_size(int64_t m, int64_t n, int32_t batch);
+
+/* One NorMuon step: muon_step with the orthogonalised momentum normalised per
+ * neuron (row) before it is applied.  agentlenshq "microsoft/dion", section
+ * "How it works" (NorMuon adds neuron-wise normalisation to Muon); hysenlabs
+ * "Microsoft Dion: orthonormal optimizers that assume DTensor parallelism",
+ * section "Dion3 is not a retuning of Dion2, and the README says so"
+ * (per-neuron normalisation redistributes the update across rows).  The pages
+ * print no formula; this is the stateless reading that keeps the total norm:
+ *     M  = mu M + G
+ *     U  = newton_schulz(M, steps, abc)
+ *     V  = U with row i scaled by t / |U_i|,  t = |U|_F / sqrt(m)
+ *          (a zero row stays zero)
+ *     X  = X - lr * scale * V,  rounded to nearest even into X's dtype.
+ * Arguments, layouts, ownership and errors as for muon_step, with
+ *   ws     >= ortho_normuon_workspace_size(m, n, 1) bytes, 256-byte aligned. */
+ortho_status normuon_step(ortho_mat X, ortho_mat G, ortho_mat M, int32_t steps, const float* abc,
+                          float mu, float lr, float scale, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* normuon_step on `batch` independent same-shape matrices (HOST arrays of
+ * descriptors, as for muon_step_batched); each member's rows are normalised
+ * against its own total norm. */
+ortho_status normuon_step_batched(int32_t batch, const ortho_mat* X, const ortho_mat* G,
+                                  const ortho_mat* M, int32_t steps, const float* abc, float mu,
+                                  float lr, float scale, void* ws, size_t ws_bytes,
+                                  void* stream);
 
 /* Static English description of a status code. */
 const char* ortho_status_str(int32_t status);

@@ -60,6 +60,14 @@ _SIGS = {
                                          ctypes.POINTER(OrthoMat), ctypes.c_int32,
                                          ctypes.POINTER(ctypes.c_float), ctypes.c_float, ctypes.c_float,
                                          ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "ortho_normuon_workspace_size": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]),
+    "normuon_step": (ctypes.c_int, [OrthoMat, OrthoMat, OrthoMat, ctypes.c_int32, ctypes.POINTER(ctypes.c_float),
+                                    ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
+                                    ctypes.c_size_t, ctypes.c_void_p]),
+    "normuon_step_batched": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(OrthoMat), ctypes.POINTER(OrthoMat),
+                                            ctypes.POINTER(OrthoMat), ctypes.c_int32,
+                                            ctypes.POINTER(ctypes.c_float), ctypes.c_float, ctypes.c_float,
+                                            ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "ortho_status_str": (ctypes.c_char_p, [ctypes.c_int32]),
     "ortho_abi_version": (ctypes.c_int32, []),
 }
@@ -223,3 +231,32 @@ def muon_step_batched(Xs: Sequence, Gs: Sequence, Ms: Sequence, mu: float, lr: f
     st = lib().muon_step_batched(b, X, G, M, steps, _abc(abc), mu, lr, scale, _ptr(ws), ws.numel(),
                                  _stream_ptr(Xs[0].device))
     _check("muon_step_batched", st)
+
+
+def normuon_workspace_size(m: int, n: int, batch: int = 1) -> int:
+    return int(lib().ortho_normuon_workspace_size(m, n, batch))
+
+
+def normuon_step(X, G, M, mu: float, lr: float, scale: float = 1.0, steps: int = 5, abc=None,
+                 ws=None):
+    """One NorMuon step in place on (X, M); see ``normuon_step`` in ortho.h."""
+    if ws is None:
+        ws = workspace(normuon_workspace_size(X.size(0), X.size(1)), X.device)
+    st = lib().normuon_step(mat(X), mat(G), mat(M), steps, _abc(abc), mu, lr, scale, _ptr(ws),
+                            ws.numel(), _stream_ptr(X.device))
+    _check("normuon_step", st)
+
+
+def normuon_step_batched(Xs: Sequence, Gs: Sequence, Ms: Sequence, mu: float, lr: float,
+                         scale: float = 1.0, steps: int = 5, abc=None, ws=None):
+    """NorMuon on a group of same-shape matrices in one call."""
+    b = len(Xs)
+    arr = OrthoMat * b
+    X = arr(*[mat(t) for t in Xs])
+    G = arr(*[mat(t) for t in Gs])
+    M = arr(*[mat(t) for t in Ms])
+    if ws is None:
+        ws = workspace(normuon_workspace_size(Xs[0].size(0), Xs[0].size(1), b), Xs[0].device)
+    st = lib().normuon_step_batched(b, X, G, M, steps, _abc(abc), mu, lr, scale, _ptr(ws),
+                                    ws.numel(), _stream_ptr(Xs[0].device))
+    _check("normuon_step_batched", st)

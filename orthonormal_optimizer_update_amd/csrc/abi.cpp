@@ -389,10 +389,10 @@ ortho_status run_ns(int32_t batch, const ortho_mat* G, const ortho_mat* Out, int
 // chunks as in run_ns, so U needs one slot per member of a chunk.
 ortho_status run_muon(int32_t batch, const ortho_mat* X, const ortho_mat* G, const ortho_mat* M,
                       int32_t steps, const float* abc, float mu, float lr, float scale, void* ws,
-                      void* stream) {
+                      void* stream, bool row_norm = false) {
   MuonPlan pl;
   const int64_t m = X[0].rows, n = X[0].cols;
-  if (!plan_muon(m, n, batch, &pl)) return ORTHO_E_SHAPE;
+  if (!plan_muon(m, n, batch, &pl, row_norm)) return ORTHO_E_SHAPE;
   const bool bf = X[0].dtype == ORTHO_BF16;
   const hipStream_t s = as_stream(stream);
   char* base = static_cast<char*>(ws);
@@ -414,6 +414,17 @@ ortho_status run_muon(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       us[i] = ortho_mat{base + pl.off_u + i * pl.u_bytes, m, n, pl.ld_u, ORTHO_F32};
     const ortho_status st = run_ns(nb, M + b0, us, steps, abc, ws, stream);
     if (st != ORTHO_OK) return st;
+    if (row_norm) {
+      // NorMuon: every row of U scaled to the common norm |U|_F / sqrt(m)
+      RowNormArgs rn{};
+      rn.u = a.u;
+      rn.rowf = reinterpret_cast<float*>(base + pl.off_rowf);
+      rn.rowf_stride = static_cast<int64_t>(pl.rowf_bytes / 4);
+      rn.rows = a.rows; rn.cols = a.cols;
+      ORTHO_TRY(launch_row_factors(rn, nb, s));
+      a.rowf = rn.rowf;
+      a.rowf_stride = rn.rowf_stride;
+    }
     ORTHO_TRY(launch_muon_update(a, bf, nb, s));
   }
   return ORTHO_OK;
@@ -441,6 +452,29 @@ ortho_status muon_step_batched(int32_t batch, const ortho_mat* X, const ortho_ma
   const ortho_status st = validate_muon(batch, X, G, M, steps, abc, mu, lr, scale, ws, ws_bytes);
   if (st != ORTHO_OK) return st;
   return run_muon(batch, X, G, M, steps, abc, mu, lr, scale, ws, stream);
+}
+
+size_t ortho_normuon_workspace_size(int64_t m, int64_t n, int32_t batch) {
+  MuonPlan p;
+  return plan_muon(m, n, batch, &p, true) ? p.total_bytes : 0;
+}
+
+ortho_status normuon_step(ortho_mat X, ortho_mat G, ortho_mat M, int32_t steps, const float* abc,
+                          float mu, float lr, float scale, void* ws, size_t ws_bytes,
+                          void* stream) {
+  const ortho_status st =
+      validate_muon(1, &X, &G, &M, steps, abc, mu, lr, scale, ws, ws_bytes, true);
+  if (st != ORTHO_OK) return st;
+  return run_muon(1, &X, &G, &M, steps, abc, mu, lr, scale, ws, stream, true);
+}
+
+ortho_status normuon_step_batched(int32_t batch, const ortho_mat* X, const ortho_mat* G,
+                                  const ortho_mat* M, int32_t steps, const float* abc, float mu,
+                                  float lr, float scale, void* ws, size_t ws_bytes, void* stream) {
+  const ortho_status st =
+      validate_muon(batch, X, G, M, steps, abc, mu, lr, scale, ws, ws_bytes, true);
+  if (st != ORTHO_OK) return st;
+  return run_muon(batch, X, G, M, steps, abc, mu, lr, scale, ws, stream, true);
 }
 
 size_t ortho_dion_workspace_size(int64_t m, int64_t n, int32_t r, int32_t batch) {

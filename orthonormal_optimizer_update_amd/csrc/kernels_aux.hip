@@ -464,7 +464,8 @@ __global__ __launch_bounds__(256) void muon_update_kernel(MuonArgs a) {
   const float* u = static_cast<const float*>(a.u.p[bi]) + (int64_t)row * a.u.ld;
   const float4 uv = load4<float>(u, c, a.cols, a.u.vec);
   const float4 xv = load4<XT>(x, c, a.cols, a.x.vec);
-  const floatx4 r = {xv.x - a.c * uv.x, xv.y - a.c * uv.y, xv.z - a.c * uv.z, xv.w - a.c * uv.w};
+  const float cc = a.rowf ? a.c * a.rowf[bi * a.rowf_stride + row] : a.c;
+  const floatx4 r = {xv.x - cc * uv.x, xv.y - cc * uv.y, xv.z - cc * uv.z, xv.w - cc * uv.w};
   if (a.x.vec && c + 4 <= a.cols) {
     if constexpr (sizeof(XT) == 2)
       *reinterpret_cast<uint2*>(x + c) = pack_bf16x4(r);
@@ -473,6 +474,65 @@ __global__ __launch_bounds__(256) void muon_update_kernel(MuonArgs a) {
   } else {
     for (int t = 0; t < 4 && c + t < a.cols; ++t) store_from_f32<XT>(x, c + t, r[t]);
   }
+  }
+}
+
+// Sum over the 256 threads of a workgroup in a fixed order (butterfly within
+// each wave, then the four wave sums pairwise); every thread gets the total.
+__device__ __forceinline__ float block_sum256(float v, float* part4) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) part4[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float t = (part4[0] + part4[1]) + (part4[2] + part4[3]);
+  __syncthreads();
+  return t;
+}
+
+// Neuron-wise normalisation, first pass: the sum of squares of row blockIdx.x
+// of U, four consecutive columns per thread.
+__global__ __launch_bounds__(256) void row_sumsq_kernel(RowNormArgs a) {
+  __shared__ float part4[4];
+  const int bi = blockIdx.y, row = blockIdx.x;
+  const float* u = static_cast<const float*>(a.u.p[bi]) + (int64_t)row * a.u.ld;
+  // four 16-byte loads in flight per thread per step (zeros past the row end)
+  float s = 0.f;
+  for (int c = threadIdx.x * 4; c < a.cols; c += 4096) {
+    float4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = load4<float>(u, c + k * 1024, a.cols, a.u.vec);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s += (v[k].x * v[k].x + v[k].y * v[k].y) + (v[k].z * v[k].z + v[k].w * v[k].w);
+  }
+  const float t = block_sum256(s, part4);
+  if (threadIdx.x == 0) a.rowf[bi * a.rowf_stride + row] = t;
+}
+
+// Second pass, one workgroup per member: t^2 = (sum of the row sums) / rows,
+// then each row sum q becomes t / sqrt(q) (0 when q = 0).  Each thread
+// rewrites only the entries it summed, after the total is formed.
+__global__ __launch_bounds__(256) void row_factor_kernel(RowNormArgs a) {
+  __shared__ float part4[4];
+  float* f = a.rowf + blockIdx.x * a.rowf_stride;
+  float s = 0.f;
+  // eight loads in flight per thread per step
+  for (int i0 = threadIdx.x; i0 < a.rows; i0 += 2048) {
+    float q[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) q[k] = i0 + k * 256 < a.rows ? f[i0 + k * 256] : 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += q[k];
+  }
+  const float total = block_sum256(s, part4);
+  const float t = sqrtf(total / static_cast<float>(a.rows));
+  for (int i0 = threadIdx.x; i0 < a.rows; i0 += 2048) {
+    float q[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) q[k] = i0 + k * 256 < a.rows ? f[i0 + k * 256] : 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (i0 + k * 256 < a.rows)
+        f[i0 + k * 256] = q[k] > 0.f ? t / sqrtf(q[k]) : (q[k] == 0.f ? 0.f : q[k]);
   }
 }
 
@@ -1398,6 +1458,15 @@ hipError_t launch_muon_update(const MuonArgs& a, bool x_bf16, int members, hipSt
     hipLaunchKernelGGL(muon_update_kernel<uint16_t>, grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(muon_update_kernel<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_factors(const RowNormArgs& a, int members, hipStream_t s) {
+  if (a.rows < 1) return hipSuccess;
+  hipLaunchKernelGGL(row_sumsq_kernel, dim3(a.rows, members), dim3(256), 0, s, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(row_factor_kernel, dim3(members), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

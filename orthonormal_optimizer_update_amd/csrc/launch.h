@@ -223,7 +223,20 @@ struct MuonArgs {
   MatArg m, g, x, u;
   float mu, c;
   int rows, cols;
+  const float* rowf;       // per-row factors of U (NULL: none), rowf_stride floats per member
+  int64_t rowf_stride;
 };
+// Neuron-wise normalisation factors of U (fp32, rows x cols per member):
+// rowf[i] = t / |U_i| with t = |U|_F / sqrt(rows), 0 for a zero row.  Two
+// launches: one workgroup per row sums its squares, then one workgroup per
+// member sums the rows in a fixed order and turns the sums into factors.
+struct RowNormArgs {
+  MatArg u;
+  float* rowf;
+  int64_t rowf_stride;
+  int rows, cols;
+};
+hipError_t launch_row_factors(const RowNormArgs& a, int members, hipStream_t s);
 hipError_t launch_muon_momentum(const MuonArgs& a, bool g_bf16, int members, hipStream_t s);
 hipError_t launch_muon_update(const MuonArgs& a, bool x_bf16, int members, hipStream_t s);
 

@@ -196,7 +196,7 @@ bool plan_ns(int64_t m, int64_t n, int32_t batch, NsPlan* p) {
   return true;
 }
 
-bool plan_muon(int64_t m, int64_t n, int32_t batch, MuonPlan* p) {
+bool plan_muon(int64_t m, int64_t n, int32_t batch, MuonPlan* p, bool row_norm) {
   MuonPlan d{};
   if (!plan_ns(m, n, batch, &d.ns)) return false;
   d.ld_u = cdiv(n, 4) * 4;
@@ -212,7 +212,10 @@ bool plan_muon(int64_t m, int64_t n, int32_t batch, MuonPlan* p) {
   }
   d.off_u = align_up(ns_bytes);
   d.u_bytes = align_up(static_cast<size_t>(m) * d.ld_u * 4);
-  d.total_bytes = d.off_u + d.u_bytes * static_cast<size_t>(d.ns.chunk);
+  d.off_rowf = align_up(d.off_u + d.u_bytes * static_cast<size_t>(d.ns.chunk));
+  d.rowf_bytes = row_norm ? align_up(static_cast<size_t>(m) * 4) : 0;
+  d.total_bytes = row_norm ? d.off_rowf + d.rowf_bytes * static_cast<size_t>(d.ns.chunk)
+                           : d.off_u + d.u_bytes * static_cast<size_t>(d.ns.chunk);
   *p = d;
   return true;
 }
@@ -286,7 +289,7 @@ ortho_status validate_ns(int32_t batch, const ortho_mat* G, const ortho_mat* Out
 
 ortho_status validate_muon(int32_t batch, const ortho_mat* X, const ortho_mat* G, const ortho_mat* M,
                            int32_t steps, const float* abc, float mu, float lr, float scale,
-                           const void* ws, size_t ws_bytes) {
+                           const void* ws, size_t ws_bytes, bool row_norm) {
   if (batch < 1 || steps < 0) return ORTHO_E_PARAM;
   if (!X || !G || !M) return ORTHO_E_NULL;
   if (!(mu >= 0.f && mu <= 1.f) || !finite(lr) || !finite(scale)) return ORTHO_E_PARAM;
@@ -306,7 +309,7 @@ ortho_status validate_muon(int32_t batch, const ortho_mat* X, const ortho_mat* G
     }
   }
   MuonPlan plan;
-  if (!plan_muon(X[0].rows, X[0].cols, batch, &plan)) return ORTHO_E_SHAPE;
+  if (!plan_muon(X[0].rows, X[0].cols, batch, &plan, row_norm)) return ORTHO_E_SHAPE;
   if (ws == nullptr || ws_bytes < plan.total_bytes) return ORTHO_E_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) % kWsAlign != 0) return ORTHO_E_WORKSPACE;
   return ORTHO_OK;

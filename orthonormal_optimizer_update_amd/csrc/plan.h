@@ -68,11 +68,13 @@ struct MuonPlan {
   int64_t ld_u;
   size_t off_u;              // after the Newton-Schulz part
   size_t u_bytes;            // per member
+  size_t off_rowf;           // NorMuon: row factors of U, rows floats per member
+  size_t rowf_bytes;         // per member (0 for Muon)
   size_t total_bytes;
 };
 
 bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* out);
-bool plan_muon(int64_t m, int64_t n, int32_t batch, MuonPlan* out);
+bool plan_muon(int64_t m, int64_t n, int32_t batch, MuonPlan* out, bool row_norm = false);
 bool plan_ns(int64_t m, int64_t n, int32_t batch, NsPlan* out);
 
 ortho_status validate_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, const ortho_mat* M,
@@ -85,6 +87,6 @@ ortho_status validate_ns(int32_t batch, const ortho_mat* G, const ortho_mat* Out
 
 ortho_status validate_muon(int32_t batch, const ortho_mat* X, const ortho_mat* G, const ortho_mat* M,
                            int32_t steps, const float* abc, float mu, float lr, float scale,
-                           const void* ws, size_t ws_bytes);
+                           const void* ws, size_t ws_bytes, bool row_norm = false);
 
 }  // namespace ortho

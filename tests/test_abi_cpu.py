@@ -25,6 +25,7 @@ def test_header_declares_expected_entry_points():
     for n in ["dion_step", "dion_step_ex", "dion_step_batched", "newton_schulz",
               "newton_schulz_batched", "ortho_dion_workspace_size", "ortho_ns_workspace_size",
               "muon_step", "muon_step_batched", "ortho_muon_workspace_size",
+              "normuon_step", "normuon_step_batched", "ortho_normuon_workspace_size",
               "ortho_status_str", "ortho_abi_version"]:
         assert n in names
 
@@ -174,6 +175,33 @@ def test_muon_argument_errors():
                                0.95, 0.02, 1.0, ws, api.muon_workspace_size(64, 48, 2), None) == 5
     assert L.muon_step_batched(0, arr(X, X), arr(G, G), arr(Mo, Mo), 5, None, 0.95, 0.02, 1.0, ws,
                                wsb, None) == 7
+
+
+def test_normuon_argument_errors():
+    """NorMuon validates as Muon does, against its own (larger) workspace: the
+    Muon workspace plus one fp32 factor per row and member."""
+    L = api.lib()
+    wsb = api.normuon_workspace_size(64, 48)
+    assert wsb >= api.muon_workspace_size(64, 48) + 64 * 4
+    assert api.normuon_workspace_size(64, 48, 3) >= api.muon_workspace_size(64, 48, 3) + 3 * 64 * 4
+    assert api.normuon_workspace_size(0, 48) == 0
+    ws = ctypes.c_void_p(FAKE)
+    X, G, Mo = M(64, 48, BF), M(64, 48, BF), M(64, 48, F)
+    call = lambda x=X, g=G, m=Mo, steps=5, mu=0.95, lr=0.02, w=ws, b=wsb: L.normuon_step(
+        x, g, m, steps, None, mu, lr, 1.0, w, b, None)
+    assert call(steps=-1) == 7
+    assert call(mu=-0.1) == 7
+    assert call(lr=float("nan")) == 7
+    assert call(g=M(64, 48, F)) == 3
+    assert call(m=M(64, 48, BF)) == 3
+    assert call(m=M(63, 48, F)) == 2
+    assert call(w=None) == 6
+    # a Muon-sized workspace is too small for NorMuon
+    assert call(b=api.muon_workspace_size(64, 48)) == 6
+    assert call(w=ctypes.c_void_p(FAKE + 64)) == 6   # not 256-byte aligned
+    arr = api.OrthoMat * 2
+    assert L.normuon_step_batched(2, arr(X, M(64, 40, BF)), arr(G, G), arr(Mo, Mo), 5, None, 0.95,
+                                  0.02, 1.0, ws, api.normuon_workspace_size(64, 48, 2), None) == 2
 
 
 def test_valid_call_without_gpu_reports_hip_error():
