@@ -27,7 +27,8 @@ def _gpu():
 # Newton-Schulz
 # ----------------------------------------------------------------------------
 
-NS_SHAPES = [(64, 64), (100, 300), (300, 100), (257, 513), (1, 50), (128, 4096), (520, 520)]
+NS_SHAPES = [(64, 64), (100, 300), (300, 100), (257, 513), (1, 50), (128, 4096), (520, 520),
+             (128, 1000), (64, 333), (333, 128)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
