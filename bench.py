@@ -376,12 +376,21 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region: exactly K whole steps.
+    # Timed region: exactly K whole steps.  An event on the main stream after
+    # each step (every path has joined it by then) splits the region into
+    # per-step times for the median and the 10th/90th percentiles.
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     with Timer(torch) as t:
+        bounds[0].record(main)
         for i in range(args.steps):
             step(i)
+            bounds[i + 1].record(main)
     torch.cuda.synchronize()
     ms_step = t.ms / args.steps
+    per_step = sorted(bounds[i].elapsed_time(bounds[i + 1]) for i in range(args.steps))
+
+    def pct(q):
+        return per_step[min(len(per_step) - 1, int(round(q * (len(per_step) - 1))))]
 
     # The same steps with the paths one after another on one stream.
     with Timer(torch) as ts:
@@ -444,6 +453,7 @@ def main():
     line = {
         "metric": METRIC, "value": 1000.0 / ms_step, "unit": "steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "ms_per_step_median": pct(0.5), "ms_per_step_p10": pct(0.1), "ms_per_step_p90": pct(0.9),
         "streams": 1 if args.one_stream else len(names),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic", "config": info, "ms_per_step_one_stream": ms_serial,
