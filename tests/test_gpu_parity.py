@@ -50,6 +50,15 @@ def test_ns_zero_steps0_and_custom_coefficients():
     note("ns cubic coefficients")
     cubic = (1.5, -0.5, 0.0)
     assert rel(gpu_ns(G, "bf16", steps=8, abc=cubic), oracle.newton_schulz(G, 8, cubic)) <= TOL["bf16"]
+    # 64- and 128-row sides wide enough for the k-split Gram: with c = 0 the
+    # split partials go through the plain reduce and the linear polynomial,
+    # otherwise through the fused one-workgroup-per-member polynomial
+    _, G2, _ = synth.small_case(4, 128, 1024, 1, "bf16", x_scale=1.0)
+    note("ns cubic 128x1024 (split Gram, c = 0)")
+    assert rel(gpu_ns(G2, "bf16", steps=8, abc=cubic), oracle.newton_schulz(G2, 8, cubic)) <= TOL["bf16"]
+    _, G3, _ = synth.small_case(5, 64, 768, 1, "f32", x_scale=1.0)
+    note("ns quintic 64x768 (split Gram, fused polynomial)")
+    assert rel(gpu_ns(G3, "f32"), oracle.newton_schulz(G3)) <= TOL["bf16"]
 
 
 def test_ns_output_may_alias_input():
