@@ -335,8 +335,13 @@ ortho_status run_ns(int32_t batch, const ortho_mat* G, const ortho_mat* Out, int
     ORTHO_TRY(launch_sumsq(sa, pl.nparts, nb, bf, s));
     ORTHO_TRY(launch_ns_scale(partial, static_cast<int64_t>(mb / 4), pl.nparts, scl,
                               static_cast<int64_t>(mb / 4), kNsEps, nb, s));
+    // With a side of at most kNsSplitRows rows the apply takes both operands
+    // from the fp32 iterate, so no transposed bf16 copy is written.
+    const bool keep_t = M > kNsSplitRows;
+    MatArg no_t;
+    memset(&no_t, 0, sizeof(no_t));
     NsInitArgs ia{};
-    ia.g = tG; ia.x32 = x32; ia.xb = xb[0]; ia.xbt = xbt[0];
+    ia.g = tG; ia.x32 = x32; ia.xb = xb[0]; ia.xbt = keep_t ? xbt[0] : no_t;
     ia.scale = scl; ia.scale_stride = static_cast<int64_t>(mb / 4);
     ia.M = M; ia.N = N; ia.transposed = pl.transposed;
     ORTHO_TRY(launch_ns_init(ia, nb, bf, s));
@@ -375,8 +380,8 @@ ortho_status run_ns(int32_t batch, const ortho_mat* G, const ortho_mat* Out, int
         ORTHO_TRY(launch_ns_poly(g2, nb, s));
       }
       NsApplyArgs g3{};
-      g3.bp = tbp; g3.xbt = xbt[cur]; g3.x32 = x32; g3.xb_next = xb[cur ^ 1];
-      g3.xbt_next = xbt[cur ^ 1]; g3.out = tOut; g3.bp32 = tbp32; g3.a = a;
+      g3.bp = tbp; g3.xbt = keep_t ? xbt[cur] : no_t; g3.x32 = x32; g3.xb_next = xb[cur ^ 1];
+      g3.xbt_next = keep_t ? xbt[cur ^ 1] : no_t; g3.out = tOut; g3.bp32 = tbp32; g3.a = a;
       g3.M = M; g3.N = N; g3.last = it == steps - 1; g3.out_transposed = pl.transposed;
       ORTHO_TRY(launch_ns_apply(g3, bf, nb, s));
     }

@@ -281,7 +281,9 @@ struct EpiNSApply {
     }
     // The four rows are consecutive elements of one row of X^T: one 8-byte
     // store when they are all inside (row0 is a multiple of 4 and the
-    // transposed buffer's leading dimension a multiple of 8).
+    // transposed buffer's leading dimension a multiple of 8).  No transposed
+    // copy is kept when no product reads it (xbt NULL).
+    if (xbt == nullptr) return;
     uint16_t* dst = xbt + (int64_t)col * ldbt + row0;
     if (row0 + 4 <= M) {
       *reinterpret_cast<uint2*>(dst) =

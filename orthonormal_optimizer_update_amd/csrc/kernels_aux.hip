@@ -675,8 +675,9 @@ __global__ __launch_bounds__(256) void ns_init_kernel(NsInitArgs a) {
       }
     }
     // transposed copy: X^T[j0 + rr][i0 + c4 ..] = X[i0 + c4 ..][j0 + rr]
+    // (not kept when no product reads it: xbt is NULL then)
     const int jt = j0 + rr, it = i0 + c4;
-    if (jt < a.N) {
+    if (xbt != nullptr && jt < a.N) {
       const floatx4 v = {tile[c4][rr], tile[c4 + 1][rr], tile[c4 + 2][rr], tile[c4 + 3][rr]};
       if (it + 4 <= a.M) {
         *reinterpret_cast<uint2*>(xbt + (int64_t)jt * a.xbt.ld + it) = pack_bf16x4(v);
