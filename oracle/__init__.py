@@ -56,12 +56,8 @@ from .dion_ref import (  # noqa: F401
     round_to_dtype,
     qr_positive,
     dion_step,
-    dion_step_batched,
     newton_schulz,
-    newton_schulz_batched,
     muon_step,
-    muon_step_batched,
     row_normalize,
     normuon_step,
-    normuon_step_batched,
 )

@@ -149,12 +149,6 @@ def dion_step(X, G, M, Q, mu: float, lr: float, scale: float = 1.0,
                 M=M_new, Q=Q_new, P=P, R=R, B=B, P_tilde=P_tilde, col_norms=norms)
 
 
-def dion_step_batched(Xs, Gs, Ms, Qs, mu, lr, scale=1.0, x_dtype="bf16"):
-    """A group of independent same-shape matrices: one ``dion_step`` each."""
-    return [dion_step(X, G, M, Q, mu, lr, scale, x_dtype)
-            for X, G, M, Q in zip(Xs, Gs, Ms, Qs)]
-
-
 # ----------------------------------------------------------------------------
 # Newton-Schulz (Muon)
 # ----------------------------------------------------------------------------
@@ -187,11 +181,6 @@ def _ns_step(Xk, a, b, c):
     return a * Xk + Bp @ Xk
 
 
-def newton_schulz_batched(Gs, steps=5, abc=MUON_ABC, eps=NS_EPS):
-    """Independent Newton-Schulz on each matrix of a group (e.g. per-head blocks)."""
-    return [newton_schulz(G, steps, abc, eps) for G in Gs]
-
-
 # ----------------------------------------------------------------------------
 # Muon step: momentum buffer, Newton-Schulz orthogonalisation, SGD-form update
 # ----------------------------------------------------------------------------
@@ -222,13 +211,6 @@ def muon_step(X, G, M, mu: float, lr: float, scale: float = 1.0, steps: int = 5,
     dX = -float(lr) * float(scale) * U
     X_exact = X + dX
     return dict(X=round_to_dtype(X_exact, x_dtype), X_exact=X_exact, dX=dX, M=M_new, U=U)
-
-
-def muon_step_batched(Xs, Gs, Ms, mu, lr, scale=1.0, steps=5, abc=MUON_ABC, eps=NS_EPS,
-                      x_dtype="bf16"):
-    """A group of independent same-shape matrices: one ``muon_step`` each."""
-    return [muon_step(X, G, M, mu, lr, scale, steps, abc, eps, x_dtype)
-            for X, G, M in zip(Xs, Gs, Ms)]
 
 
 def row_normalize(U):
@@ -273,10 +255,3 @@ def normuon_step(X, G, M, mu: float, lr: float, scale: float = 1.0, steps: int =
     dX = -float(lr) * float(scale) * V
     X_exact = X + dX
     return dict(X=round_to_dtype(X_exact, x_dtype), X_exact=X_exact, dX=dX, M=M_new, U=U, V=V)
-
-
-def normuon_step_batched(Xs, Gs, Ms, mu, lr, scale=1.0, steps=5, abc=MUON_ABC, eps=NS_EPS,
-                         x_dtype="bf16"):
-    """A group of independent same-shape matrices: one ``normuon_step`` each."""
-    return [normuon_step(X, G, M, mu, lr, scale, steps, abc, eps, x_dtype)
-            for X, G, M in zip(Xs, Gs, Ms)]

@@ -195,9 +195,20 @@ def test_dion_special_cases(rng):
 
 
 def test_dion_zero_column_gives_zero_q(rng):
+    """A column of R that is exactly zero gives an exactly zero column of the
+    new right factor (not 0/0); every other column gets unit norm."""
+    from oracle.dion_ref import _column_normalize
+    R = rng.standard_normal((9, 4))
+    R[:, 2] = 0.0
+    Qn, norms = _column_normalize(R)
+    assert norms[2] == 0.0 and np.all(norms[[0, 1, 3]] > 0)
+    assert np.all(Qn[:, 2] == 0.0)
+    assert np.abs(np.linalg.norm(Qn[:, [0, 1, 3]], axis=0) - 1.0).max() <= 1e-15
+    assert np.abs(Qn[:, [0, 1, 3]] * norms[[0, 1, 3]] - R[:, [0, 1, 3]]).max() <= 1e-15
+    # and through a whole step: a rank-1 B leaves finite factors
     m, n, r = 10, 8, 3
     B = np.zeros((m, n))
-    B[:, 0] = rng.standard_normal(m)          # rank 1, so two columns of R vanish
+    B[:, 0] = rng.standard_normal(m)
     Q = rng.standard_normal((n, r))
     out = oracle.dion_step(np.zeros((m, n)), B, np.zeros((m, n)), Q, 0.9, 0.1)
     assert np.all(np.isfinite(out["Q"]))
