@@ -137,8 +137,11 @@ ortho_status dion_step_batched(int32_t batch, const ortho_mat* X, const ortho_ma
  *   steps >= 0 iterations.
  *   abc  HOST pointer to 3 floats (a, b, c), or NULL for Muon's quintic
  *        (3.4445, -4.7750, 2.0315).
- * The iterate is kept in fp32; the three products per iteration use bf16
- * matrix-core operands with fp32 accumulation.  eps = 1e-7; G = 0 gives 0. */
+ * The iterate is kept in fp32.  For ORTHO_BF16 inputs the three products per
+ * iteration use bf16 matrix-core operands with fp32 accumulation; for ORTHO_F32
+ * inputs they use fp32-accurate products (each fp32 operand split into three
+ * bf16 pieces, the six leading piece products accumulated in fp32), so the
+ * result holds fp32-level accuracy.  eps = 1e-7; G = 0 gives 0. */
 ortho_status newton_schulz(ortho_mat G, ortho_mat Out, int32_t steps, const float* abc,
                            void* ws, size_t ws_bytes, void* stream);
 
@@ -164,7 +167,9 @@ size_t ortho_muon_workspace_size(int64_t m, int64_t n, int32_t batch);
  *   X      m x n, ORTHO_BF16 or ORTHO_F32, updated in place.
  *   G      m x n, same dtype as X, read only.
  *   M      m x n, ORTHO_F32, updated in place (start it at zero).
- *   steps  >= 0 Newton-Schulz iterations; abc as for newton_schulz.
+ *   steps  >= 0 Newton-Schulz iterations; abc as for newton_schulz.  The
+ *          products are fp32-accurate when X is ORTHO_F32 and bf16 when X is
+ *          ORTHO_BF16 (the momentum is fp32 either way).
  *   mu in [0, 1]; lr and scale finite, else ORTHO_E_PARAM.
  *   ws     >= ortho_muon_workspace_size(m, n, 1) bytes, 256-byte aligned.
  * Errors are returned before anything is enqueued. */

@@ -141,7 +141,23 @@ def workspace(nbytes: int, device):
 
 def dion_step(X, G, M, Q, mu: float, lr: float, scale: float = 1.0, ws=None, P_out=None,
               R_out=None, dev_status=None):
-    """One Dion step in place on (X, M, Q); see ``dion_step_ex`` in ortho.h."""
+    """One Dion step in place on (X, M, Q): ``dion_step`` of ortho.h, or
+    ``dion_step_ex`` when a scale other than 1 or an optional output is given."""
+    r = Q.size(1)
+    if ws is None:
+        ws = workspace(dion_workspace_size(X.size(0), X.size(1), r), X.device)
+    if scale == 1.0 and P_out is None and R_out is None and dev_status is None:
+        st = lib().dion_step(mat(X), mat(G), mat(M), mat(Q), r, mu, lr, _ptr(ws), ws.numel(),
+                             _stream_ptr(X.device))
+        _check("dion_step", st)
+        return
+    dion_step_ex(X, G, M, Q, mu, lr, scale, ws, P_out, R_out, dev_status)
+
+
+def dion_step_ex(X, G, M, Q, mu: float, lr: float, scale: float = 1.0, ws=None, P_out=None,
+                 R_out=None, dev_status=None):
+    """``dion_step_ex`` of ortho.h: a Dion step with an update scale and the
+    optional outputs P, R and the device status word."""
     r = Q.size(1)
     if ws is None:
         ws = workspace(dion_workspace_size(X.size(0), X.size(1), r), X.device)

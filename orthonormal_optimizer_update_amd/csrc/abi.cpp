@@ -302,8 +302,55 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
   return ORTHO_OK;
 }
 
+// fp32-accurate Newton-Schulz (`precise`): the three products of every
+// iteration on bf16x6 splits of fp32 operands.  The iterate ping-pongs between
+// the fp32 slot and the region of the two bf16 copies (which holds M x ld_x
+// fp32); the fp32 Gram takes the two transposed-copy regions and the fp32 Bp
+// the A and Bp regions, so the workspace size does not depend on the dtype.
+ortho_status run_ns_precise(const NsPlan& pl, int nb, const MatArg& tG, const MatArg& tOut,
+                            bool out_bf, int32_t steps, float a, float b, float c, char* base,
+                            hipStream_t s) {
+  const size_t mb = pl.member_bytes;
+  const int M = static_cast<int>(pl.M), N = static_cast<int>(pl.N);
+  const MatArg xs[2] = {ws_table(base, mb, pl.off_x32, nb, pl.ld_x, M, N, 4, 16),
+                        ws_table(base, mb, pl.off_xb0, nb, pl.ld_x, M, N, 4, 16)};
+  float* partial = reinterpret_cast<float*>(base + pl.off_partial);
+  float* scl = reinterpret_cast<float*>(base + pl.off_scale);
+  SumsqArgs sa{};
+  sa.g = tG; sa.partial = partial; sa.partial_stride = static_cast<int64_t>(mb / 4);
+  sa.chunk = pl.part_chunk;
+  ORTHO_TRY(launch_sumsq(sa, pl.nparts, nb, out_bf, s));
+  ORTHO_TRY(launch_ns_scale(partial, static_cast<int64_t>(mb / 4), pl.nparts, scl,
+                            static_cast<int64_t>(mb / 4), kNsEps, nb, s));
+  MatArg none;
+  memset(&none, 0, sizeof(none));
+  NsInitArgs ia{};
+  ia.g = tG; ia.x32 = xs[0]; ia.xb = none; ia.xbt = none;
+  ia.scale = scl; ia.scale_stride = static_cast<int64_t>(mb / 4);
+  ia.M = M; ia.N = N; ia.transposed = pl.transposed;
+  ORTHO_TRY(launch_ns_init(ia, nb, out_bf, s));
+  if (steps == 0) ORTHO_TRY(launch_ns_store(ia, tOut, nb, out_bf, s));
+  Ns32Args na{};
+  na.a32 = ws_table(base, mb, pl.off_xbt0, nb, pl.ld_xt, M, M, 4, 16);
+  na.bp32 = ws_table(base, mb, pl.off_a, nb, pl.ld_xt, M, M, 4, 16);
+  na.out = tOut;
+  na.a = a; na.b = b; na.c = c;
+  na.M = M; na.N = N; na.out_transposed = pl.transposed;
+  for (int it = 0; it < steps; ++it) {
+    na.x = xs[it & 1];
+    na.xn = xs[(it & 1) ^ 1];
+    na.last = it == steps - 1;
+    ORTHO_TRY(launch_ns32_gram(na, nb, s));
+    ORTHO_TRY(launch_ns32_poly(na, nb, s));
+    ORTHO_TRY(launch_ns32_apply(na, out_bf, nb, s));
+  }
+  return ORTHO_OK;
+}
+
+// Newton-Schulz over a group.  The products use bf16 operands with fp32
+// accumulation, or fp32-accurate split products when `precise` (fp32 inputs).
 ortho_status run_ns(int32_t batch, const ortho_mat* G, const ortho_mat* Out, int32_t steps,
-                    const float* abc, void* ws, void* stream) {
+                    const float* abc, void* ws, void* stream, bool precise) {
   NsPlan pl;
   if (!plan_ns(G[0].rows, G[0].cols, batch, &pl)) return ORTHO_E_SHAPE;
   const bool bf = G[0].dtype == ORTHO_BF16;
@@ -318,6 +365,11 @@ ortho_status run_ns(int32_t batch, const ortho_mat* G, const ortho_mat* Out, int
     const int nb = batch - b0 < pl.chunk ? batch - b0 : pl.chunk;
     const MatArg tG = user_table(G, b0, nb, gvec);
     const MatArg tOut = user_table(Out, b0, nb, gvec);
+    if (precise) {
+      const ortho_status st = run_ns_precise(pl, nb, tG, tOut, bf, steps, a, b, c, base, s);
+      if (st != ORTHO_OK) return st;
+      continue;
+    }
     const MatArg x32 = ws_table(base, mb, pl.off_x32, nb, pl.ld_x, M, N, 4, 16);
     const MatArg xb[2] = {ws_table(base, mb, pl.off_xb0, nb, pl.ld_x, M, N, 2, 16),
                           ws_table(base, mb, pl.off_xb1, nb, pl.ld_x, M, N, 2, 16)};
@@ -417,7 +469,9 @@ ortho_status run_muon(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     ortho_mat us[kMaxBatch];
     for (int i = 0; i < nb; ++i)
       us[i] = ortho_mat{base + pl.off_u + i * pl.u_bytes, m, n, pl.ld_u, ORTHO_F32};
-    const ortho_status st = run_ns(nb, M + b0, us, steps, abc, ws, stream);
+    // the fp32 momentum is orthogonalised with fp32-accurate products when
+    // the weights are fp32, with bf16 products when they are bf16
+    const ortho_status st = run_ns(nb, M + b0, us, steps, abc, ws, stream, !bf);
     if (st != ORTHO_OK) return st;
     if (row_norm) {
       // NorMuon: every row of U scaled to the common norm |U|_F / sqrt(m)
@@ -520,7 +574,7 @@ ortho_status newton_schulz(ortho_mat G, ortho_mat Out, int32_t steps, const floa
                            size_t ws_bytes, void* stream) {
   const ortho_status st = validate_ns(1, &G, &Out, steps, abc, ws, ws_bytes);
   if (st != ORTHO_OK) return st;
-  return run_ns(1, &G, &Out, steps, abc, ws, stream);
+  return run_ns(1, &G, &Out, steps, abc, ws, stream, G.dtype == ORTHO_F32);
 }
 
 ortho_status newton_schulz_batched(int32_t batch, const ortho_mat* G, const ortho_mat* Out,
@@ -528,7 +582,7 @@ ortho_status newton_schulz_batched(int32_t batch, const ortho_mat* G, const orth
                                    void* stream) {
   const ortho_status st = validate_ns(batch, G, Out, steps, abc, ws, ws_bytes);
   if (st != ORTHO_OK) return st;
-  return run_ns(batch, G, Out, steps, abc, ws, stream);
+  return run_ns(batch, G, Out, steps, abc, ws, stream, G[0].dtype == ORTHO_F32);
 }
 
 const char* ortho_status_str(int32_t status) {

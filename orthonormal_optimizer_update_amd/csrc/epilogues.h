@@ -248,6 +248,7 @@ struct EpiNSApply {
       if (out_t) store4_from_f32<OUT_T>(out, (int64_t)col * ldo + row0, v, out_vec);
       return;
     }
+    if (xbt == nullptr) return;  // no product reads a transposed copy
     *reinterpret_cast<uint2*>(xbt + (int64_t)col * ldbt + row0) = pack_bf16x4(v);
   }
   __device__ __forceinline__ void init(int row0, int col, int M, int N, float* v) const {
@@ -292,6 +293,78 @@ struct EpiNSApply {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         if (row0 + t < M) dst[t] = hb[t];
+    }
+  }
+};
+
+// Newton-Schulz with fp32-accurate products (fp32 inputs): the polynomial
+// Bp = b A + c (A A) from the fp32 Gram, stored as fp32.
+struct EpiNSPoly32 {
+  static constexpr bool kPreload = false;
+  struct Args {
+    MatArg a32;   // fp32 A (read)
+    MatArg bp32;  // fp32 Bp (written)
+    float b, c;
+  };
+  const float* a;
+  float* bp;
+  int64_t lda, ldb;
+  float b, c;
+  __device__ EpiNSPoly32(const Args& g, int bi, int)
+      : a(static_cast<const float*>(g.a32.p[bi])),
+        bp(static_cast<float*>(const_cast<void*>(g.bp32.p[bi]))),
+        lda(g.a32.ld), ldb(g.bp32.ld), b(g.b), c(g.c) {}
+  __device__ __forceinline__ void apply(int row0, int col, int M, int N, float v0, float v1,
+                                        float v2, float v3) {
+    if (col >= N) return;
+    const float v[4] = {v0, v1, v2, v3};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = row0 + t;
+      if (row < M) bp[(int64_t)row * ldb + col] = b * a[(int64_t)row * lda + col] + c * v[t];
+    }
+  }
+};
+
+// Newton-Schulz apply with fp32-accurate products: X' = a X + Bp X, read from
+// one fp32 iterate and written to the other (the product of every row tile
+// reads all rows of X, so the update cannot be made in place), or, on the last
+// iteration, to the caller's output in its dtype (transposed back when the
+// input was tall).
+template <typename OUT_T>
+struct EpiNSApply32 {
+  static constexpr bool kPreload = false;
+  struct Args {
+    MatArg x;      // fp32 iterate (read)
+    MatArg xn;     // fp32 next iterate (written unless last)
+    MatArg out;    // caller's output (written when last)
+    float a;
+    int last;
+    int out_transposed;  // out is N x M
+  };
+  const float* x;
+  float* xn;
+  OUT_T* out;
+  int64_t ldx, ldn, ldo;
+  float a;
+  bool last, out_t;
+  __device__ EpiNSApply32(const Args& g, int bi, int)
+      : x(static_cast<const float*>(g.x.p[bi])),
+        xn(g.last ? nullptr : static_cast<float*>(const_cast<void*>(g.xn.p[bi]))),
+        out(g.last ? static_cast<OUT_T*>(const_cast<void*>(g.out.p[bi])) : nullptr),
+        ldx(g.x.ld), ldn(g.xn.ld), ldo(g.out.ld), a(g.a), last(g.last), out_t(g.out_transposed) {}
+  __device__ __forceinline__ void apply(int row0, int col, int M, int N, float v0, float v1,
+                                        float v2, float v3) {
+    if (col >= N) return;
+    const float v[4] = {v0, v1, v2, v3};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = row0 + t;
+      if (row >= M) continue;
+      const float y = a * x[(int64_t)row * ldx + col] + v[t];
+      if (!last) xn[(int64_t)row * ldn + col] = y;
+      else if (out_t) store_from_f32<OUT_T>(out, (int64_t)col * ldo + row, y);
+      else store_from_f32<OUT_T>(out, (int64_t)row * ldo + col, y);
     }
   }
 };

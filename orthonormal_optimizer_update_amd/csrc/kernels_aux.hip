@@ -661,16 +661,17 @@ __global__ __launch_bounds__(256) void ns_init_kernel(NsInitArgs a) {
   for (int q = 0; q < 4; ++q) {
     const int rr = r16 + 16 * q;
     // row-major copies: X[i0 + rr][j0 + c4 ..]
+    // (xb is NULL when the products take fp32 operands)
     const int i = i0 + rr, j = j0 + c4;
     if (i < a.M) {
       const floatx4 v = {tile[rr][c4], tile[rr][c4 + 1], tile[rr][c4 + 2], tile[rr][c4 + 3]};
       if (j + 4 <= a.N) {
         *reinterpret_cast<floatx4*>(x32 + (int64_t)i * a.x32.ld + j) = v;
-        *reinterpret_cast<uint2*>(xb + (int64_t)i * a.xb.ld + j) = pack_bf16x4(v);
+        if (xb != nullptr) *reinterpret_cast<uint2*>(xb + (int64_t)i * a.xb.ld + j) = pack_bf16x4(v);
       } else {
         for (int t = 0; t < 4 && j + t < a.N; ++t) {
           x32[(int64_t)i * a.x32.ld + j + t] = v[t];
-          xb[(int64_t)i * a.xb.ld + j + t] = to_bf16_bits(v[t]);
+          if (xb != nullptr) xb[(int64_t)i * a.xb.ld + j + t] = to_bf16_bits(v[t]);
         }
       }
     }

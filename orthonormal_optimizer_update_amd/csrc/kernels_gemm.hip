@@ -298,11 +298,49 @@ hipError_t launch_ns_poly(const NsPolyArgs& a, int members, hipStream_t s) {
 hipError_t launch_ns_apply(const NsApplyArgs& a, bool out_bf16, int members, hipStream_t s) {
   if (a.M <= kNsSplitRows)
     return out_bf16 ? ns_apply_split_t<uint16_t>(a, members, s) : ns_apply_split_t<float>(a, members, s);
-  if (a.M > 128)
-    return out_bf16 ? ns_apply_t<CfgNsBig, uint16_t>(a, members, s)
-                    : ns_apply_t<CfgNsBig, float>(a, members, s);
-  return out_bf16 ? ns_apply_t<CfgNsSmall, uint16_t>(a, members, s)
-                  : ns_apply_t<CfgNsSmall, float>(a, members, s);
+  // larger sides read X^T as bf16, and every iteration but the last writes it
+  if (a.xbt.p[0] == nullptr || (!a.last && a.xbt_next.p[0] == nullptr)) return hipErrorInvalidValue;
+  return out_bf16 ? ns_apply_t<CfgNsBig, uint16_t>(a, members, s)
+                  : ns_apply_t<CfgNsBig, float>(a, members, s);
+}
+
+// Newton-Schulz with fp32-accurate products: bf16x6 splits of the fp32
+// operands, formed in the loaders of the 128 x 128 kernel.
+hipError_t launch_ns32_gram(const Ns32Args& a, int members, hipStream_t s) {
+  GemmParams<EpiStoreF32::Args> p{};
+  p.a = with_rows(a.x, a.M);
+  p.b0 = with_rows(a.x, a.M);    // element (j, k) = X[j][k]
+  p.e.c = a.a32;
+  p.e.split_stride = 0;
+  p.M = a.M; p.N = a.M; p.K = a.N;
+  p.splits = 1; p.kchunk = 0; p.tri = 0;
+  return run<CfgSplit6, RowF32<128, 256, 3>, RowF32<128, 256, 3>, EpiStoreF32>(p, members, s);
+}
+
+hipError_t launch_ns32_poly(const Ns32Args& a, int members, hipStream_t s) {
+  GemmParams<EpiNSPoly32::Args> p{};
+  p.a = with_rows(a.a32, a.M);
+  p.b0 = with_rows(a.a32, a.M);  // A is symmetric: A A = A A^T
+  p.e.a32 = a.a32; p.e.bp32 = a.bp32; p.e.b = a.b; p.e.c = a.c;
+  p.M = a.M; p.N = a.M; p.K = a.M;
+  p.splits = 1; p.kchunk = 0; p.tri = 0;
+  return run<CfgSplit6, RowF32<128, 256, 3>, RowF32<128, 256, 3>, EpiNSPoly32>(p, members, s);
+}
+
+template <typename OUT_T>
+hipError_t ns32_apply_t(const Ns32Args& a, int members, hipStream_t s) {
+  GemmParams<typename EpiNSApply32<OUT_T>::Args> p{};
+  p.a = with_rows(a.bp32, a.M);
+  p.b0 = with_rows(a.x, a.N);    // element (j, k) = X[k][j]
+  p.e.x = a.x; p.e.xn = a.xn; p.e.out = a.out;
+  p.e.a = a.a; p.e.last = a.last; p.e.out_transposed = a.out_transposed;
+  p.M = a.M; p.N = a.N; p.K = a.M;
+  p.splits = 1; p.kchunk = 0; p.tri = 0;
+  return run<CfgSplit6, RowF32<128, 256, 3>, ColF32<128, 256, 3>, EpiNSApply32<OUT_T>>(p, members, s);
+}
+
+hipError_t launch_ns32_apply(const Ns32Args& a, bool out_bf16, int members, hipStream_t s) {
+  return out_bf16 ? ns32_apply_t<uint16_t>(a, members, s) : ns32_apply_t<float>(a, members, s);
 }
 
 hipError_t launch_fast_split6(const Split6Args& a, int members, hipStream_t s) {

@@ -270,6 +270,19 @@ struct NsSmallPolyArgs {
 };
 hipError_t launch_ns_small_poly(const NsSmallPolyArgs& a, int members, hipStream_t s);
 hipError_t launch_ns_linear(const NsPolyArgs& a, int members, hipStream_t s);  // c == 0
+// Newton-Schulz with fp32-accurate products (fp32 inputs): bf16x6 splits of
+// the fp32 operands.  A32 = X X^T; Bp32 = b A32 + c A32 A32; then
+// Xn = a X + Bp32 X, or the caller's output on the last iteration.
+struct Ns32Args {
+  MatArg x, xn;        // fp32 iterates M x N (read / written)
+  MatArg a32, bp32;    // fp32 M x M
+  MatArg out;          // caller's output (storage dtype; N x M when out_transposed)
+  float a, b, c;
+  int M, N, last, out_transposed;
+};
+hipError_t launch_ns32_gram(const Ns32Args& a, int members, hipStream_t s);
+hipError_t launch_ns32_poly(const Ns32Args& a, int members, hipStream_t s);
+hipError_t launch_ns32_apply(const Ns32Args& a, bool out_bf16, int members, hipStream_t s);
 hipError_t launch_ns_apply(const NsApplyArgs& a, bool out_bf16, int members, hipStream_t s);
 
 }  // namespace ortho

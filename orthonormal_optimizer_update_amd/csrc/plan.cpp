@@ -238,6 +238,9 @@ ortho_status validate_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G
     if (G[b].rows != X[b].rows || G[b].cols != X[b].cols || M[b].rows != X[b].rows ||
         M[b].cols != X[b].cols || Q[b].rows != X[b].cols)
       return ORTHO_E_SHAPE;
+    // every member's right factor has exactly r columns (the kernels read and
+    // write r columns of each)
+    if (Q[b].cols != r) return ORTHO_E_RANK;
     if (b > 0) {
       if (!same_geometry(X[b], X[0])) return ORTHO_E_SHAPE;
       if (X[b].ld != X[0].ld || G[b].ld != G[0].ld || M[b].ld != M[0].ld || Q[b].ld != Q[0].ld)

@@ -125,10 +125,19 @@ def small_case(seed: int, m: int, n: int, r: int, dtype: str, planted_rank: int 
 
 def block_layout(workload: int, m: int, n: int, r: int, blocks: int):
     """Scattered block-diagonal layout for full-size structural cases: block i
-    owns rows perm_m[i*m/k : (i+1)*m/k] of an m x n matrix, columns
-    perm_n[i*n/k : (i+1)*n/k], and columns i*r/k .. (i+1)*r/k - 1 of an
-    n x r (or m x r) factor.  Returns (perm_m, perm_n) as int64 arrays."""
+    owns rows perm_m[i*m/k : (i+1)*m/k] of an m x n matrix and columns
+    perm_n[i*n/k : (i+1)*n/k].  Returns (perm_m, perm_n) as int64 arrays."""
+    return block_layout_r(workload, m, n, r, blocks)[:2]
+
+
+def block_layout_r(workload: int, m: int, n: int, r: int, blocks: int):
+    """block_layout plus a permutation of the r factor columns: block i also
+    owns columns sorted(perm_r[i*r/k : (i+1)*r/k]) of an n x r (or m x r)
+    factor, so the blocks' factor columns interleave.  Returns (perm_m,
+    perm_n, perm_r) as int64 arrays; the first two equal block_layout's."""
     if m % blocks or n % blocks or r % blocks:
         raise ValueError("block count must divide m, n and r")
     rng = _rng(workload, ROLE_LAYOUT, 0, m * 1000003 + n * 1009 + r)
-    return rng.permutation(m).astype(np.int64), rng.permutation(n).astype(np.int64)
+    perm_m = rng.permutation(m).astype(np.int64)
+    perm_n = rng.permutation(n).astype(np.int64)
+    return perm_m, perm_n, rng.permutation(r).astype(np.int64)

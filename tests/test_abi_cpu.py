@@ -132,6 +132,10 @@ def test_dion_batched_errors():
     assert call(2, arr(M(64, 48, BF), M(64, 48, BF, ld=64))) == 5   # members differ in ld
     assert L.dion_step_batched(2, X, G, Mo, Q, 8, 0.9, 0.1, 1.0, None, ctypes.c_void_p(FAKE),
                                wsb - 256, None) == 6
+    # a member whose right factor is narrower than r (same ld) is a rank error
+    Qn = arr(M(48, 8, F), M(48, 4, F, ld=8))
+    assert L.dion_step_batched(2, X, G, Mo, Qn, 8, 0.9, 0.1, 1.0, None, ctypes.c_void_p(FAKE),
+                               wsb, None) == 4
 
 
 def test_ns_argument_errors():

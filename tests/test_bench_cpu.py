@@ -22,7 +22,7 @@ def test_bench_models():
     # 26 bytes per element of the 4096^2 matrix plus 16 (m + n) r of factors
     nbytes, flops = bench.dion_model(4096, 4096, 256)
     assert nbytes == 26 * 4096 * 4096 + 16 * 8192 * 256
-    assert flops == 8 * 4096 * 4096 * 256
+    assert flops == 8 * 4096 * 4096 * 256 + 2 * 4096 * 256 ** 2 + 3 * 4096 * 256
     # Newton-Schulz on the wide orientation: 4 m^2 n + 2 m^3 per iteration
     _, f = bench.ns_model(8192, 2048, iters=1)
     assert f == 4 * 2048 ** 2 * 8192 + 2 * 2048 ** 3

@@ -7,9 +7,14 @@ The fp64 oracle cannot run these shapes whole in test time, so the inputs carry
 an exact structure that reduces the full-size step to small independent
 problems.  The gradient is block diagonal after row and column permutations
 (16 blocks), and Q0 is block diagonal with the same column blocks and r/16
-columns per block.  Then P~ = B Q, its Gram matrix, the Cholesky factor, the
-QR factor, R = B^T P and the column norms all act block by block; the result is
-exact, not approximate, so:
+columns per block, those columns scattered over the r columns (each block's
+in increasing order).  Then P~ = B Q, its Gram matrix, the Cholesky factor,
+the QR factor, R = B^T P and the column norms all act block by block: a
+column's Gram-Schmidt projections on other blocks' columns are exact zeros,
+and the Cholesky factor's cross-block entries are exact zeros, while every
+64 x 64 tile of the Gram and of the factor mixes columns of many blocks, so
+the blocked factorisation runs on dense tiles.  The result is exact, not
+approximate, so:
   * two blocks per case are compared with the oracle run on that block alone,
     at the bf16 tolerance;
   * everything off the blocks must come out bit for bit as the structure
@@ -64,10 +69,10 @@ def test_config5_dion_block_structured(m, n, r):
     wl = synth.WORKLOADS[5]
     mu, lr = wl["mu"], wl["lr"]
     mb, nb, rb = m // K, n // K, r // K
-    perm_m, perm_n = synth.block_layout(5, m, n, r, K)
+    perm_m, perm_n, perm_r = synth.block_layout_r(5, m, n, r, K)
     rows = [perm_m[i * mb:(i + 1) * mb] for i in range(K)]
     cols = [perm_n[i * nb:(i + 1) * nb] for i in range(K)]
-    rcols = [np.arange(i * rb, (i + 1) * rb) for i in range(K)]
+    rcols = [np.sort(perm_r[i * rb:(i + 1) * rb]) for i in range(K)]
 
     note(f"config5 dion {m}x{n} r={r}: building inputs")
     gen = torch.Generator(device="cuda")

@@ -72,7 +72,7 @@ def test_muon_small(shape, dtype):
     worst = run_muon_parity(X, Gs, mu=0.95, lr=0.02, dtype=dtype, label="small")
     print(shape, dtype, worst)
     assert worst["M"] <= TOL["f32"]
-    assert worst["dX"] <= TOL["bf16"] and worst["X"] <= TOL["bf16"]
+    assert worst["dX"] <= TOL[dtype] and worst["X"] <= TOL[dtype]
 
 
 def test_muon_square_4096_planted():

@@ -76,7 +76,7 @@ def test_normuon_small(shape, dtype):
     worst = run_normuon_parity(X, Gs, mu=0.95, lr=0.02, dtype=dtype, label="small", scale=1.3)
     print(shape, dtype, worst)
     assert worst["M"] <= TOL["f32"]
-    assert worst["dX"] <= TOL["bf16"] and worst["X"] <= TOL["bf16"]
+    assert worst["dX"] <= TOL[dtype] and worst["X"] <= TOL[dtype]
     # dX is stored in X's dtype: bf16 rounding moves each row norm slightly
     assert worst["rows"] <= TOL[dtype]
 
@@ -106,7 +106,7 @@ def test_normuon_zero_row_stays_zero():
     gpu = gpu_normuon(X, G, np.zeros((m, n)), 0.9, 0.05, "f32")
     ref = oracle.normuon_step(X, G, np.zeros((m, n)), 0.9, 0.05, x_dtype="f32")
     assert np.all(gpu["dX"][5] == 0.0)
-    assert rel(gpu["dX"], ref["dX"]) <= TOL["bf16"]
+    assert rel(gpu["dX"], ref["dX"]) <= TOL["f32"]
 
 
 def test_normuon_batched_equals_single():

@@ -1,7 +1,6 @@
 """Parity of the HIP path (through the C-ABI) with the fp64 oracle on the same
-seeded inputs.  Tolerances are relative Frobenius errors: 1e-4 for fp32 Dion
-inputs, 2e-2 for bf16 inputs with fp32 accumulation (and for Newton-Schulz,
-whose products use bf16 matrix cores for both input dtypes)."""
+seeded inputs.  Tolerances are relative Frobenius errors: 1e-4 for fp32 inputs
+(Dion and Newton-Schulz), 2e-2 for bf16 inputs with fp32 accumulation."""
 
 import numpy as np
 import pytest
@@ -38,7 +37,7 @@ def test_ns_small(shape, dtype):
     note(f"ns {shape} {dtype}")
     got = gpu_ns(G, dtype)
     want = oracle.newton_schulz(G)
-    assert rel(got, want) <= TOL["bf16"]
+    assert rel(got, want) <= TOL[dtype]
 
 
 def test_ns_zero_steps0_and_custom_coefficients():
@@ -57,8 +56,25 @@ def test_ns_zero_steps0_and_custom_coefficients():
     note("ns cubic 128x1024 (split Gram, c = 0)")
     assert rel(gpu_ns(G2, "bf16", steps=8, abc=cubic), oracle.newton_schulz(G2, 8, cubic)) <= TOL["bf16"]
     _, G3, _ = synth.small_case(5, 64, 768, 1, "f32", x_scale=1.0)
-    note("ns quintic 64x768 (split Gram, fused polynomial)")
-    assert rel(gpu_ns(G3, "f32"), oracle.newton_schulz(G3)) <= TOL["bf16"]
+    note("ns quintic 64x768 bf16 (split Gram, fused polynomial)")
+    assert rel(gpu_ns(G3, "bf16"), oracle.newton_schulz(G3)) <= TOL["bf16"]
+    # fp32 inputs take fp32-accurate products
+    note("ns quintic 64x768 f32")
+    assert rel(gpu_ns(G3, "f32"), oracle.newton_schulz(G3)) <= TOL["f32"]
+    note("ns cubic 128x1024 f32")
+    assert rel(gpu_ns(G2, "f32", steps=8, abc=cubic), oracle.newton_schulz(G2, 8, cubic)) <= TOL["f32"]
+
+
+def test_ns_f32_planted_1024x1536():
+    """fp32 input with a dominant rank-32 part: fp32-accurate products, both
+    orientations."""
+    S = synth.planted(22, 1024, 1536, 32, 10.0)
+    G = synth.gradient(22, 1024, 1536, 1, "f32", planted_part=S)
+    note("ns f32 planted 1024x1536")
+    assert rel(gpu_ns(G, "f32"), oracle.newton_schulz(G)) <= TOL["f32"]
+    note("ns f32 planted 1536x1024")
+    Gt = np.ascontiguousarray(G.T)
+    assert rel(gpu_ns(Gt, "f32"), oracle.newton_schulz(Gt)) <= TOL["f32"]
 
 
 def test_ns_output_may_alias_input():
