@@ -81,7 +81,9 @@ typedef enum {
   ORTHO_E_LAYOUT = 5,     /* ld < cols, or a size too large to index */
   ORTHO_E_WORKSPACE = 6,  /* ws is NULL or ws_bytes is below the required size */
   ORTHO_E_PARAM = 7,      /* mu outside [0,1], non-finite lr/scale/abc, steps < 0, batch < 1 */
-  ORTHO_E_HIP = 8         /* a HIP launch failed (no device, invalid stream, ...) */
+  ORTHO_E_HIP = 8,        /* a HIP launch failed (no device, invalid stream, ...) */
+  ORTHO_E_SCRATCH = 9     /* dion_step_noalloc: the problem needs more than
+                             ORTHO_NOALLOC_SCRATCH_BYTES of workspace */
 } ortho_status;
 
 #define ORTHO_DEV_CHOL_SHIFT 1
@@ -120,6 +122,25 @@ ortho_status dion_step_ex(ortho_mat X, ortho_mat G, ortho_mat M, ortho_mat Q, in
                           float mu, float lr, float scale, const ortho_mat* P_out,
                           const ortho_mat* R_out, int32_t* dev_status, void* ws,
                           size_t ws_bytes, void* stream);
+
+/* dion_step for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same step, arguments, layouts and errors as dion_step, with no workspace
+ * argument.  The workspace comes from a static device array of
+ * ORTHO_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds on every GPU it
+ * runs on until the process ends (enough for, e.g., 4096 x 4096 at r = 256 or
+ * 256 x 256 at r = 64); a problem whose workspace
+ * (ortho_dion_workspace_size(m, n, r, 1)) is larger returns ORTHO_E_SCRATCH
+ * before anything is enqueued.  The array of the current device is used, so
+ * the stream must belong to the current device.  The call itself allocates and
+ * frees nothing; its first call on a device looks up that device's copy of the
+ * array once.  All calls on one GPU share the array: two calls that overlap on
+ * one GPU (different streams, or different host threads) race and give wrong
+ * results; serialise them on one stream.  No part of the array needs to start
+ * at zero. */
+#define ORTHO_NOALLOC_SCRATCH_BYTES (64u << 20)
+ortho_status dion_step_noalloc(ortho_mat X, ortho_mat G, ortho_mat M, ortho_mat Q, int32_t r,
+                               float mu, float lr, void* stream);
 
 /* Dion on a group of `batch` independent matrices that share (m, n, dtype) and
  * rank r: the shape-grouped round that the repository summary describes for

@@ -17,6 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libortho.so")
 
 ORTHO_F32, ORTHO_BF16 = 0, 1
+ORTHO_E_SCRATCH = 9
+NOALLOC_SCRATCH_BYTES = 64 << 20
 DEV_CHOL_SHIFT, DEV_ZERO_COLUMN = 1, 2
 MUON_ABC = (3.4445, -4.7750, 2.0315)
 
@@ -68,6 +70,8 @@ _SIGS = {
                                             ctypes.POINTER(OrthoMat), ctypes.c_int32,
                                             ctypes.POINTER(ctypes.c_float), ctypes.c_float, ctypes.c_float,
                                             ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "dion_step_noalloc": (ctypes.c_int, [OrthoMat, OrthoMat, OrthoMat, OrthoMat, ctypes.c_int32,
+                                         ctypes.c_float, ctypes.c_float, ctypes.c_void_p]),
     "ortho_status_str": (ctypes.c_char_p, [ctypes.c_int32]),
     "ortho_abi_version": (ctypes.c_int32, []),
 }
@@ -166,6 +170,14 @@ def dion_step_ex(X, G, M, Q, mu: float, lr: float, scale: float = 1.0, ws=None, 
     st = lib().dion_step_ex(mat(X), mat(G), mat(M), mat(Q), r, mu, lr, scale, pm, rm,
                             _ptr(dev_status), _ptr(ws), ws.numel(), _stream_ptr(X.device))
     _check("dion_step_ex", st)
+
+
+def dion_step_noalloc(X, G, M, Q, mu: float, lr: float):
+    """``dion_step_noalloc`` of ortho.h: a Dion step whose workspace is the
+    library's static device array (no allocation by the library or here)."""
+    st = lib().dion_step_noalloc(mat(X), mat(G), mat(M), mat(Q), Q.size(1), mu, lr,
+                                 _stream_ptr(X.device))
+    _check("dion_step_noalloc", st)
 
 
 def dion_step_batched(Xs: Sequence, Gs: Sequence, Ms: Sequence, Qs: Sequence, mu: float, lr: float,

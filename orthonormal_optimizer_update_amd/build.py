@@ -19,7 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libortho.so")
 
-SOURCES = ["kernels_gemm.hip", "kernels_aux.hip", "kernels_stream.hip", "abi.cpp", "plan.cpp"]
+SOURCES = ["kernels_gemm.hip", "kernels_aux.hip", "kernels_stream.hip", "noalloc.hip", "abi.cpp",
+           "plan.cpp"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

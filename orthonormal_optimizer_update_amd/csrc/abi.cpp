@@ -6,6 +6,7 @@
 #include "../../include/ortho.h"
 #include "launch.h"
 #include "plan.h"
+#include "run.h"
 
 using namespace ortho;
 
@@ -491,6 +492,14 @@ ortho_status run_muon(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
 
 }  // namespace
 
+namespace ortho {
+ortho_status dion_run(int32_t batch, const ortho_mat* X, const ortho_mat* G, const ortho_mat* M,
+                      const ortho_mat* Q, int32_t r, float mu, float lr, float scale, void* ws,
+                      void* stream) {
+  return run_dion(batch, X, G, M, Q, r, mu, lr, scale, nullptr, nullptr, nullptr, ws, stream);
+}
+}  // namespace ortho
+
 extern "C" {
 
 size_t ortho_muon_workspace_size(int64_t m, int64_t n, int32_t batch) {
@@ -596,6 +605,8 @@ const char* ortho_status_str(int32_t status) {
     case ORTHO_E_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
     case ORTHO_E_PARAM: return "invalid scalar parameter (mu, lr, scale, abc, steps or batch)";
     case ORTHO_E_HIP: return "a HIP launch failed";
+    case ORTHO_E_SCRATCH:
+      return "the problem needs more scratch memory than the no-allocation entry point holds";
     default: return "unknown status";
   }
 }

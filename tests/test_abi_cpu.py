@@ -138,6 +138,20 @@ def test_dion_batched_errors():
                                wsb, None) == 4
 
 
+def test_dion_noalloc_argument_errors():
+    """Argument errors and the scratch limit come back before any device call."""
+    L = api.lib()
+    X, G, Mo, Q = M(64, 48, BF), M(64, 48, BF), M(64, 48, F), M(48, 8, F)
+    assert L.dion_step_noalloc(X, G, Mo, Q, 8, 1.5, 0.1, None) == 7
+    assert L.dion_step_noalloc(X, G, Mo, Q, 9, 0.9, 0.1, None) == 4
+    assert L.dion_step_noalloc(M(64, 48, BF, data=None), G, Mo, Q, 8, 0.9, 0.1, None) == 1
+    assert L.dion_step_noalloc(X, M(64, 48, F), Mo, Q, 8, 0.9, 0.1, None) == 3
+    big = (M(4096, 4096, BF), M(4096, 4096, BF), M(4096, 4096, F), M(4096, 1024, F))
+    assert api.dion_workspace_size(4096, 4096, 1024) > api.NOALLOC_SCRATCH_BYTES
+    assert L.dion_step_noalloc(*big, 1024, 0.9, 0.1, None) == api.ORTHO_E_SCRATCH
+    assert "scratch" in api.status_str(api.ORTHO_E_SCRATCH)
+
+
 def test_ns_argument_errors():
     L = api.lib()
     wsb = api.ns_workspace_size(64, 48)
