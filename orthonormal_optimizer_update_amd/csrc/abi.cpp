@@ -348,6 +348,67 @@ ortho_status run_ns_precise(const NsPlan& pl, int nb, const MatArg& tG, const Ma
   return ORTHO_OK;
 }
 
+// Gram Newton-Schulz (bf16-product path, Gram side M <= 128 with N >= 4 M).
+// Wide G (no transposition): X_0 = sc G is never formed; A_0 = sc^2 G G^T
+// (exact bf16 products for bf16 G, bf16x3 for fp32 G, k-split), the iteration
+// on the M x M side gives sc Q_steps, and the apply writes (sc Q_steps) G to
+// the caller's output.  Tall G: X_0 = sc G^T goes through the fp32 iterate
+// first, and the output is written transposed back.
+ortho_status run_ns_gram(const NsPlan& pl, int nb, const ortho_mat* G, int b0, const MatArg& tG,
+                         const MatArg& tOut, bool g_bf, int32_t steps, float a, float b, float c,
+                         char* base, hipStream_t s) {
+  const size_t mb = pl.member_bytes;
+  const int M = static_cast<int>(pl.M), N = static_cast<int>(pl.N);
+  const MatArg x32 = ws_table(base, mb, pl.off_x32, nb, pl.ld_x, M, N, 4, 16);
+  const MatArg tbp32 = ws_table(base, mb, pl.off_bp32, nb, pl.ld_xt, M, M, 4, 16);
+  float* partial = reinterpret_cast<float*>(base + pl.off_partial);
+  float* scl = reinterpret_cast<float*>(base + pl.off_scale);
+  SumsqArgs sa{};
+  sa.g = tG; sa.partial = partial; sa.partial_stride = static_cast<int64_t>(mb / 4);
+  sa.chunk = pl.part_chunk;
+  ORTHO_TRY(launch_sumsq(sa, pl.nparts, nb, g_bf, s));
+  ORTHO_TRY(launch_ns_scale(partial, static_cast<int64_t>(mb / 4), pl.nparts, scl,
+                            static_cast<int64_t>(mb / 4), kNsEps, nb, s));
+  const bool direct = !pl.transposed;
+  if (!direct) {
+    MatArg none;
+    memset(&none, 0, sizeof(none));
+    NsInitArgs ia{};
+    ia.g = tG; ia.x32 = x32; ia.xb = none; ia.xbt = none;
+    ia.scale = scl; ia.scale_stride = static_cast<int64_t>(mb / 4);
+    ia.M = M; ia.N = N; ia.transposed = 1;
+    ORTHO_TRY(launch_ns_init(ia, nb, g_bf, s));
+  }
+  const MatArg gpart = ws_table(base, mb, pl.off_gns_part, nb, M, M, M, 4, 4);
+  const int64_t slice = static_cast<int64_t>(M) * M;
+  NsGramArgs g1{};
+  g1.M = M; g1.K = N;
+  if (direct) {
+    // 16-byte row loads of bf16 G need 16-byte aligned rows
+    g1.x = user_table(G, b0, nb, 16);
+    ORTHO_TRY(launch_ns_gram_g(g1, g_bf, gpart, slice, pl.gns_splits, pl.gns_kchunk, nb, s));
+  } else {
+    g1.x = x32;
+    ORTHO_TRY(launch_ns_gram_g(g1, false, gpart, slice, pl.gns_splits, pl.gns_kchunk, nb, s));
+  }
+  NsGramIterArgs gi{};
+  gi.part = reinterpret_cast<const float*>(base + pl.off_gns_part);
+  gi.part_member_stride = static_cast<int64_t>(mb / 4);
+  gi.slice = slice; gi.splits = pl.gns_splits;
+  gi.scale = direct ? scl : nullptr;
+  gi.scale_stride = static_cast<int64_t>(mb / 4);
+  gi.a0 = ws_table(base, mb, pl.off_gns_a0, nb, pl.gns_mp, pl.gns_mp, pl.gns_mp, 2, 16);
+  gi.q = tbp32;
+  gi.a = a; gi.b = b; gi.c = c;
+  gi.M = M; gi.steps = steps;
+  ORTHO_TRY(launch_ns_gram_iter(gi, nb, s));
+  NsGramApplyArgs ap{};
+  ap.q = tbp32; ap.x = direct ? tG : x32; ap.out = tOut;
+  ap.M = M; ap.N = N; ap.out_transposed = !direct;
+  ORTHO_TRY(launch_ns_gram_apply(ap, direct && g_bf, g_bf, nb, s));
+  return ORTHO_OK;
+}
+
 // Newton-Schulz over a group.  The products use bf16 operands with fp32
 // accumulation, or fp32-accurate split products when `precise` (fp32 inputs).
 ortho_status run_ns(int32_t batch, const ortho_mat* G, const ortho_mat* Out, int32_t steps,
@@ -368,6 +429,11 @@ ortho_status run_ns(int32_t batch, const ortho_mat* G, const ortho_mat* Out, int
     const MatArg tOut = user_table(Out, b0, nb, gvec);
     if (precise) {
       const ortho_status st = run_ns_precise(pl, nb, tG, tOut, bf, steps, a, b, c, base, s);
+      if (st != ORTHO_OK) return st;
+      continue;
+    }
+    if (pl.gram_ns && steps > 0) {
+      const ortho_status st = run_ns_gram(pl, nb, G, b0, tG, tOut, bf, steps, a, b, c, base, s);
       if (st != ORTHO_OK) return st;
       continue;
     }

@@ -369,6 +369,35 @@ struct EpiNSApply32 {
   }
 };
 
+// A result written straight to the caller's output in its dtype, transposed
+// when out_transposed (Gram Newton-Schulz apply).
+template <typename OUT_T>
+struct EpiStoreOut {
+  static constexpr bool kPreload = false;
+  struct Args {
+    MatArg out;
+    int out_transposed;
+  };
+  OUT_T* out;
+  int64_t ldo;
+  bool out_t;
+  __device__ EpiStoreOut(const Args& g, int bi, int)
+      : out(static_cast<OUT_T*>(const_cast<void*>(g.out.p[bi]))), ldo(g.out.ld),
+        out_t(g.out_transposed) {}
+  __device__ __forceinline__ void apply(int row0, int col, int M, int N, float v0, float v1,
+                                        float v2, float v3) {
+    if (col >= N) return;
+    const float v[4] = {v0, v1, v2, v3};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = row0 + t;
+      if (row >= M) continue;
+      if (out_t) store_from_f32<OUT_T>(out, (int64_t)col * ldo + row, v[t]);
+      else store_from_f32<OUT_T>(out, (int64_t)row * ldo + col, v[t]);
+    }
+  }
+};
+
 // Dion sweep 3 (fp32 weights): with B = M + G recomputed from the inputs,
 //   M <- B - c1 * (P R^T),   X <- X - c2 * (P Q'^T)
 // where c1 = 1 - mu and c2 = lr * scale.

@@ -5,7 +5,9 @@
 // k-contiguous layout the MFMA fragments want; transposing loaders do the
 // transpose in registers, so every global access stays row-coalesced.
 //
-// Products: PRODS = 1 uses hi*hi; PRODS = 3 (two pieces, x = hi + lo) adds
+// Products: PRODS = 1 uses hi*hi; PRODS = 2 (two pieces of the left operand,
+// one of the right: a right operand that is exact in bf16) adds lo*hi;
+// PRODS = 3 (two pieces, x = hi + lo) adds
 // lo*hi and hi*lo, about 2^-16 relative accuracy; PRODS = 6 (three pieces
 // x = p0 + p1 + p2) keeps every product p_i*q_j with i + j <= 2, about fp32
 // accuracy.  NBOP = 2 runs two right operands against the same left tile with
@@ -36,8 +38,8 @@ struct GemmCfg {
   static constexpr int STAGE = NA * A_ELEMS + NBOP * NB * B_ELEMS;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(BK % 16 == 0, "BK must be a multiple of 16");
-  static_assert(PRODS == 1 || (PRODS == 3 && NA == 2 && NB == 2) ||
-                    (PRODS == 6 && NA == 3 && NB == 3),
+  static_assert(PRODS == 1 || (PRODS == 2 && NA == 2 && NB == 1) ||
+                    (PRODS == 3 && NA == 2 && NB == 2) || (PRODS == 6 && NA == 3 && NB == 3),
                 "bad product set");
 };
 
@@ -367,6 +369,8 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(GemmParams<typename Epi::
               acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], bfr[0][j], acc[q][i][j], 0, 0, 0);
               acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bfr[1][j], acc[q][i][j], 0, 0, 0);
             }
+            if constexpr (Cfg::PRODS == 2)
+              acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], bfr[0][j], acc[q][i][j], 0, 0, 0);
             acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bfr[0][j], acc[q][i][j], 0, 0, 0);
           }
       }

@@ -290,6 +290,62 @@ hipError_t launch_ns_gram_split(const NsGramArgs& a, const MatArg& part, int64_t
   return run<CfgNsSmall, NsRow<CfgNsSmall>, NsRow<CfgNsSmall>, EpiStoreF32>(p, members, s);
 }
 
+hipError_t launch_ns_gram32_split(const NsGramArgs& a, const MatArg& part, int64_t split_stride,
+                                  int splits, int kchunk, int members, hipStream_t s) {
+  if (a.M > 128 || splits < 1 || kchunk % 32 != 0) return hipErrorInvalidValue;
+  GemmParams<EpiStoreF32::Args> p{};
+  p.a = with_rows(a.x, a.M);
+  p.b0 = with_rows(a.x, a.M);   // element (j, k) = X[j][k]
+  p.e.c = part;
+  p.e.split_stride = split_stride;
+  p.e.has_t = 0;
+  p.M = a.M; p.N = a.M; p.K = a.K;
+  p.splits = splits; p.kchunk = kchunk; p.tri = 0;
+  return run<CfgSplit, RowF32<128, 256, 2>, RowF32<128, 256, 2>, EpiStoreF32>(p, members, s);
+}
+
+hipError_t launch_ns_gram_g(const NsGramArgs& a, bool g_bf16, const MatArg& part,
+                            int64_t split_stride, int splits, int kchunk, int members,
+                            hipStream_t s) {
+  if (!g_bf16) return launch_ns_gram32_split(a, part, split_stride, splits, kchunk, members, s);
+  if (a.M > 128 || splits < 1 || kchunk % 32 != 0) return hipErrorInvalidValue;
+  GemmParams<EpiStoreF32::Args> p{};
+  p.a = with_rows(a.x, a.M);
+  p.b0 = with_rows(a.x, a.M);   // element (j, k) = G[j][k]
+  p.e.c = part;
+  p.e.split_stride = split_stride;
+  p.e.has_t = 0;
+  p.M = a.M; p.N = a.M; p.K = a.K;
+  p.splits = splits; p.kchunk = kchunk; p.tri = 0;
+  return run<CfgNsSmall, NsRow<CfgNsSmall>, NsRow<CfgNsSmall>, EpiStoreF32>(p, members, s);
+}
+
+// Two pieces of the fp32 left operand against an exact bf16 right operand.
+using CfgSplit2 = GemmCfg<128, 128, 32, 2, 2, 2, 1, 2, 1>;
+
+template <class Cfg, class LB, typename OUT_T>
+hipError_t ns_gram_apply_t(const NsGramApplyArgs& a, int members, hipStream_t s) {
+  GemmParams<typename EpiStoreOut<OUT_T>::Args> p{};
+  p.a = with_rows(a.q, a.M);
+  p.b0 = with_rows(a.x, a.N);   // element (j, k) = x[k][j]
+  p.e.out = a.out;
+  p.e.out_transposed = a.out_transposed;
+  p.M = a.M; p.N = a.N; p.K = a.M;
+  p.splits = 1; p.kchunk = 0; p.tri = 0;
+  return run<Cfg, RowF32<128, 256, Cfg::NA>, LB, EpiStoreOut<OUT_T>>(p, members, s);
+}
+
+hipError_t launch_ns_gram_apply(const NsGramApplyArgs& a, bool x_bf16, bool out_bf16, int members,
+                                hipStream_t s) {
+  if (a.M > 128) return hipErrorInvalidValue;
+  using ColBf = LdCol<128, 32, 256, 1, uint16_t, false, uint16_t>;
+  if (x_bf16)
+    return out_bf16 ? ns_gram_apply_t<CfgSplit2, ColBf, uint16_t>(a, members, s)
+                    : ns_gram_apply_t<CfgSplit2, ColBf, float>(a, members, s);
+  return out_bf16 ? ns_gram_apply_t<CfgSplit, ColF32<128, 256, 2>, uint16_t>(a, members, s)
+                  : ns_gram_apply_t<CfgSplit, ColF32<128, 256, 2>, float>(a, members, s);
+}
+
 hipError_t launch_ns_poly(const NsPolyArgs& a, int members, hipStream_t s) {
   if (a.c == 0.0f) return launch_ns_linear(a, members, s);
   return a.M > 128 ? ns_poly_t<CfgNsBig>(a, members, s) : ns_poly_t<CfgNsSmall>(a, members, s);

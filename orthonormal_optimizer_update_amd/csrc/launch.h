@@ -283,6 +283,41 @@ struct Ns32Args {
 hipError_t launch_ns32_gram(const Ns32Args& a, int members, hipStream_t s);
 hipError_t launch_ns32_poly(const Ns32Args& a, int members, hipStream_t s);
 hipError_t launch_ns32_apply(const Ns32Args& a, bool out_bf16, int members, hipStream_t s);
+
+// Gram Newton-Schulz on a Gram side of M <= 128 rows: A_0 = X_0 X_0^T from the
+// fp32 iterate with bf16x3 products, split over k into fp32 slices (ld M)...
+hipError_t launch_ns_gram32_split(const NsGramArgs& a, const MatArg& part, int64_t split_stride,
+                                  int splits, int kchunk, int members, hipStream_t s);
+// ...then, one workgroup per member, the iteration on the M x M side with
+// bf16x6 products: Q_{k+1} = (a I + b A_k + c A_k^2) Q_k, A_k = Q_k A_0 Q_k^T,
+// Q_0 = I, for `steps` >= 1 iterations; Q_steps goes to q (fp32 M x M).  The
+// apply X = Q_steps X_0 is launch_ns_apply with a = 0 and bp32 = q.
+struct NsGramIterArgs {
+  const float* part;           // member 0's k-split Gram slices (ld M)
+  int64_t part_member_stride, slice;
+  int splits;
+  const float* scale;          // per-member factor sc (NULL: 1): A_0 = sc^2 * sum, q = sc * Q
+  int64_t scale_stride;
+  MatArg a0;                   // scratch per member: three bf16 MP x MP pieces (ld MP, MP = 64 or 128)
+  MatArg q;                    // fp32 result, M x M
+  float a, b, c;
+  int M, steps;
+};
+hipError_t launch_ns_gram_iter(const NsGramIterArgs& a, int members, hipStream_t s);
+// The Gram of the caller's wide G itself (M <= 128 rows): exact bf16 products
+// for bf16 G, bf16x3 for fp32 G; k-split fp32 slices (ld M) as above.
+hipError_t launch_ns_gram_g(const NsGramArgs& a, bool g_bf16, const MatArg& part,
+                            int64_t split_stride, int splits, int kchunk, int members,
+                            hipStream_t s);
+// The apply of Gram Newton-Schulz: out = Q x (M x N), Q fp32 M x M (two bf16
+// pieces), x M x N (bf16: exact; fp32: two pieces); out in its dtype,
+// transposed (N x M) when out_transposed.
+struct NsGramApplyArgs {
+  MatArg q, x, out;
+  int M, N, out_transposed;
+};
+hipError_t launch_ns_gram_apply(const NsGramApplyArgs& a, bool x_bf16, bool out_bf16, int members,
+                                hipStream_t s);
 hipError_t launch_ns_apply(const NsApplyArgs& a, bool out_bf16, int members, hipStream_t s);
 
 }  // namespace ortho

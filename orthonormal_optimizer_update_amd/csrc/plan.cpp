@@ -188,6 +188,25 @@ bool plan_ns(int64_t m, int64_t n, int32_t batch, NsPlan* p) {
     }
   }
   s.off_gpart = o;   o = align_up(o + (s.gram_splits > 1 ? static_cast<size_t>(s.gram_splits) * mm * 4 : 0));
+  // Gram Newton-Schulz when the Gram side is small against the long side
+  s.gram_ns = s.M <= 128 && s.N >= 4 * s.M;
+  s.gns_splits = 1;
+  s.gns_kchunk = static_cast<int>(cdiv(s.N, 32) * 32);
+  s.gns_mp = s.M <= 64 ? 64 : 128;
+  if (s.gram_ns) {
+    // one workgroup per CU over the chunk's members, at least 8 k steps of 32
+    int64_t want = cdiv(256, s.chunk), cap = s.N / 256;
+    if (want > cap) want = cap;
+    if (want > 1) {
+      s.gns_kchunk = static_cast<int>(cdiv(cdiv(s.N, want), 32) * 32);
+      s.gns_splits = static_cast<int>(cdiv(s.N, s.gns_kchunk));
+    }
+  }
+  const size_t gmm = static_cast<size_t>(s.M) * s.M;
+  s.off_gns_part = o;
+  o = align_up(o + (s.gram_ns ? static_cast<size_t>(s.gns_splits) * gmm * 4 : 0));
+  s.off_gns_a0 = o;
+  o = align_up(o + (s.gram_ns ? static_cast<size_t>(s.gns_mp) * s.gns_mp * 6 : 0));
   s.off_partial = o; o = align_up(o + static_cast<size_t>(s.nparts) * 4);
   s.off_scale = o;   o = align_up(o + 4);
   s.member_bytes = o;

@@ -57,6 +57,12 @@ struct NsPlan {
   // off_gpart) and reduced in a fixed order into A.
   int gram_splits, gram_kchunk;
   size_t off_gpart;
+  // Gram Newton-Schulz (bf16 products, M <= 128 and N >= 4 M): k-split fp32
+  // slices of X_0 X_0^T (ld M) and A_0's three bf16 MP x MP pieces (MP = M
+  // rounded up to 64 or 128) per member.
+  int gram_ns;
+  int gns_splits, gns_kchunk, gns_mp;
+  size_t off_gns_part, off_gns_a0;
   size_t member_bytes;
   size_t total_bytes;
 };
