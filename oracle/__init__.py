@@ -13,6 +13,11 @@ public pages about microsoft/dion):
   the U V^T factor of the SVD.  MSR talk "Dion: The distributed orthonormal
   update revolution is here", passage contrasting SGD with orthonormal updates
   and the passage on Muon's dense Newton-Schulz matrix products.
+* ``gram_newton_schulz`` -- the same iteration written on the small Gram side
+  (X_k = Q_k X_0 with Q_k m x m), the optional Gram Newton-Schulz that hysenlabs
+  "Microsoft Dion: orthonormal optimizers that assume DTensor parallelism" names
+  in its section on installing with the optional kernels.  No formula is
+  printed; the reading is this exact algebraic rewrite.
 * ``dion_step`` -- Dion's amortised power iteration (one power-iteration step
   per optimizer step, warm-started from the previous right factor), the low-rank
   fraction, error feedback, and the SGD-form weight update.  Same talk, passages
@@ -57,6 +62,7 @@ from .dion_ref import (  # noqa: F401
     qr_positive,
     dion_step,
     newton_schulz,
+    gram_newton_schulz,
     muon_step,
     row_normalize,
     normuon_step,

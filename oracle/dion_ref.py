@@ -181,6 +181,38 @@ def _ns_step(Xk, a, b, c):
     return a * Xk + Bp @ Xk
 
 
+def gram_newton_schulz(G, steps: int = 5, abc=MUON_ABC, eps: float = NS_EPS) -> np.ndarray:
+    """The Newton-Schulz iteration run on the Gram side, in fp64.
+
+    hysenlabs "Microsoft Dion: orthonormal optimizers that assume DTensor
+    parallelism", section on installing from git with the optional kernels,
+    names a Gram Newton-Schulz option; the pages give no formula.  The reading:
+    the same iteration as ``newton_schulz``, expressed through the small Gram
+    matrix.  On the wide orientation (rows <= cols) with X_0 the normalised
+    input, every iterate is X_k = Q_k X_0 for an m x m matrix Q_k, and
+        A_0     = X_0 X_0^T
+        A_k     = Q_k A_0 Q_k^T                (= X_k X_k^T)
+        Q_{k+1} = (a I + b A_k + c A_k A_k) Q_k,   Q_0 = I
+    so the result Q_steps X_0 equals ``newton_schulz`` up to rounding, while the
+    wide matrix takes part in two products only.
+    """
+    a, b, c = (float(v) for v in abc)
+    G = _f64(G)
+    tall = G.shape[0] > G.shape[1]
+    X0 = _ns_normalize(G.T if tall else G, eps)
+    A0 = X0 @ X0.T
+    Q = np.eye(X0.shape[0])
+    for _ in range(steps):
+        Q = _gram_ns_step(Q, A0, a, b, c)
+    out = Q @ X0
+    return out.T if tall else out
+
+
+def _gram_ns_step(Q, A0, a, b, c):
+    A = Q @ A0 @ Q.T
+    return (a * np.eye(Q.shape[0]) + b * A + c * (A @ A)) @ Q
+
+
 # ----------------------------------------------------------------------------
 # Muon step: momentum buffer, Newton-Schulz orthogonalisation, SGD-form update
 # ----------------------------------------------------------------------------

@@ -477,3 +477,60 @@ def test_mutant_normuon_caught(monkeypatch, name):
     monkeypatch.setattr(dion_ref, attr, fn)
     # the loop formulation and the closed forms do not go through the mutant
     assert not (_normuon_pins(np.random.default_rng(23)) <= 1e-6)
+
+
+# ----------------------------------------------------------------------------
+# Gram Newton-Schulz: the iteration on the Gram side
+# ----------------------------------------------------------------------------
+
+def gram_ns_err(G, **kw):
+    """Max error of the Gram-side oracle against the SVD closed form."""
+    return np.abs(oracle.gram_newton_schulz(G, **kw) - quintic_spectral(G, **kw)).max()
+
+
+@pytest.mark.parametrize("shape", [(8, 40), (40, 8), (16, 16), (1, 9), (5, 64)])
+def test_gram_ns_matches_spectral_closed_form(rng, shape):
+    G = rng.standard_normal(shape)
+    assert gram_ns_err(G) <= 1e-12
+    cubic = (1.5, -0.5, 0.0)
+    assert gram_ns_err(G, steps=7, abc=cubic) <= 1e-12
+    assert gram_ns_err(G, steps=0) <= 1e-15
+
+
+def test_gram_ns_low_rank_and_zero(rng):
+    """Rank-deficient inputs: nothing is inverted, so the null directions stay
+    exactly null; a zero input gives a zero output."""
+    G = rng.standard_normal((12, 2)) @ rng.standard_normal((2, 50))
+    assert gram_ns_err(G) <= 1e-12
+    assert np.all(oracle.gram_newton_schulz(np.zeros((6, 30))) == 0)
+
+
+def test_gram_ns_iterates_are_products_of_the_input(rng):
+    """Each Gram-side step equals one Newton-Schulz step of X_k = Q_k X_0."""
+    X0 = rng.standard_normal((6, 30)) / 10.0
+    a, b, c = oracle.MUON_ABC
+    Q = np.eye(6)
+    Xk = X0.copy()
+    for _ in range(4):
+        Q = dion_ref._gram_ns_step(Q, X0 @ X0.T, a, b, c)
+        Xk = dion_ref._ns_step(Xk, a, b, c)
+        assert np.abs(Q @ X0 - Xk).max() <= 1e-13
+
+
+@pytest.mark.parametrize("mutant", ["no_transpose_q", "stale_gram", "drop_update"])
+def test_mutant_gram_ns_caught(rng, monkeypatch, mutant):
+    def no_transpose_q(Q, A0, a, b, c):     # A_k = Q A_0 (Q^T dropped)
+        A = Q @ A0
+        return (a * np.eye(Q.shape[0]) + b * A + c * (A @ A)) @ Q
+
+    def stale_gram(Q, A0, a, b, c):         # A_k = A_0 every step
+        A = A0
+        return (a * np.eye(Q.shape[0]) + b * A + c * (A @ A)) @ Q
+
+    def drop_update(Q, A0, a, b, c):        # Q_{k+1} = P_k (no Q_k factor)
+        A = Q @ A0 @ Q.T
+        return a * np.eye(Q.shape[0]) + b * A + c * (A @ A)
+
+    monkeypatch.setattr(dion_ref, "_gram_ns_step", locals()[mutant])
+    G = rng.standard_normal((8, 40))
+    assert not (gram_ns_err(G) <= 1e-6)
