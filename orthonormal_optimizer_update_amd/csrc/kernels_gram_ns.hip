@@ -32,9 +32,10 @@ __device__ __forceinline__ floatx16 mfma(const bf16x8& x, const bf16x8& y, const
 // zero).  Q_k and one work matrix (T, A_k, then P_k) live in LDS as two bf16
 // pieces each (x = hi + lo + O(2^-16 |x|); row pitch MP + 8 elements), so the
 // products read their fragments directly; A_0 lives in the member's global
-// scratch as three pieces and is read from L2 once per iteration.  Products
-// C = X Y read rows of Y for its columns, i.e. form X Y^T, which is X Y for the
-// symmetric Y used here (A_0, Q_k, A_k).  Precision, from emulating the
+// scratch as three pieces and is read from L2 once per iteration.  The products
+// T = Q_k A_0 (A_0 is exactly symmetric), A_k = T Q_k^T and S = A_k A_k^T read
+// rows of their right operand; Q_{k+1} = P_k Q_k reads Q_k's columns (see
+// prod_lc).  Precision, from emulating the
 // iteration against fp64: hi*hi + hi*lo + lo*hi for T Q_k, A_k A_k and P_k Q_k,
 // and the five products of Q_k's two pieces with A_0's three pieces (i + j <=
 // 2) for Q_k A_0, whose small eigen-directions need them (rank-1 inputs).
@@ -103,69 +104,135 @@ __global__ __launch_bounds__(256) void ns_gram_iter_kernel(NsGramIterArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   };
-  // acc = X Y^T over k < MP, both from LDS pieces: hi*hi + hi*lo + lo*hi
+  // acc = X Y^T over k < MP, both from LDS pieces: hi*hi + hi*lo + lo*hi.
+  // The fragments of the next k step are read while this step's products run,
+  // and each product kind goes over all accumulators before the next kind, so
+  // consecutive products never wait on each other.
   auto prod_ll = [&](const uint16_t* X, const uint16_t* Y) {
     zero();
-#pragma unroll 2
-    for (int k0 = 0; k0 < MP; k0 += 16) {
-      bf16x8 xh[NB], xl[NB], yh[NB], yl[NB];
+    bf16x8 xh[2][NB], xl[2][NB], yh[2][NB], yl[2][NB];
+    auto load = [&](int buf, int k0) {
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         const int o = (wm * WT + i * 32 + fr) * LD + k0 + fk;
-        xh[i] = ld8(X + o);
-        xl[i] = ld8(X + PS + o);
+        xh[buf][i] = ld8(X + o);
+        xl[buf][i] = ld8(X + PS + o);
       }
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int o = (wn * WT + j * 32 + fr) * LD + k0 + fk;
-        yh[j] = ld8(Y + o);
-        yl[j] = ld8(Y + PS + o);
+        yh[buf][j] = ld8(Y + o);
+        yl[buf][j] = ld8(Y + PS + o);
       }
+    };
+    load(0, 0);
+#pragma unroll
+    for (int k0 = 0; k0 < MP; k0 += 16) {
+      const int cur = (k0 >> 4) & 1;
+      if (k0 + 16 < MP) load(cur ^ 1, k0 + 16);
 #pragma unroll
       for (int i = 0; i < NB; ++i)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          acc[i][j] = mfma(xl[i], yh[j], acc[i][j]);
-          acc[i][j] = mfma(xh[i], yl[j], acc[i][j]);
-          acc[i][j] = mfma(xh[i], yh[j], acc[i][j]);
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma(xh[cur][i], yh[cur][j], acc[i][j]);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma(xh[cur][i], yl[cur][j], acc[i][j]);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma(xl[cur][i], yh[cur][j], acc[i][j]);
+    }
+  };
+  // acc = X Y with Y read down its columns (both from LDS pieces, hi*hi +
+  // hi*lo + lo*hi).  Q_{k+1} = P_k Q_k needs the true product: Q_k is symmetric
+  // only up to rounding, and P_k Q_k^T lets that asymmetry grow with the
+  // iteration's gain on rank-deficient inputs (found by emulating the kernel's
+  // arithmetic against fp64: 1e-1 instead of 1.5e-3 on a rank-1 input).
+  auto prod_lc = [&](const uint16_t* X, const uint16_t* Y) {
+    zero();
+    bf16x8 xh[2][NB], xl[2][NB], yh[2][NB], yl[2][NB];
+    auto load = [&](int buf, int k0) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int o = (wm * WT + i * 32 + fr) * LD + k0 + fk;
+        xh[buf][i] = ld8(X + o);
+        xl[buf][i] = ld8(X + PS + o);
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int col = wn * WT + j * 32 + fr;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int o = (k0 + fk + t) * LD + col;
+          yh[buf][j][t] = __builtin_bit_cast(bf16, Y[o]);
+          yl[buf][j][t] = __builtin_bit_cast(bf16, Y[PS + o]);
         }
+      }
+    };
+    load(0, 0);
+#pragma unroll
+    for (int k0 = 0; k0 < MP; k0 += 16) {
+      const int cur = (k0 >> 4) & 1;
+      if (k0 + 16 < MP) load(cur ^ 1, k0 + 16);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma(xh[cur][i], yh[cur][j], acc[i][j]);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma(xh[cur][i], yl[cur][j], acc[i][j]);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma(xl[cur][i], yh[cur][j], acc[i][j]);
     }
   };
   // acc = X A_0 (A_0 symmetric): X's two LDS pieces against A_0's three
   // global pieces, the five products with piece indices summing to <= 2; the
-  // A_0 fragments of the next k step are loaded while this one's run
+  // fragments of the next k step are loaded while this one's run
   auto prod_lg = [&](const uint16_t* X) {
     zero();
-    bf16x8 g[2][NB][3];
-    auto load_g = [&](int buf, int k0) {
+    bf16x8 g[2][NB][3], xh[2][NB], xl[2][NB];
+    auto load = [&](int buf, int k0) {
 #pragma unroll
       for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int p = 0; p < 3; ++p)
           g[buf][j][p] = ld8(a0 + p * MP * MP + (wn * WT + j * 32 + fr) * MP + k0 + fk);
-    };
-    load_g(0, 0);
-#pragma unroll
-    for (int k0 = 0; k0 < MP; k0 += 16) {
-      const int cur = (k0 >> 4) & 1;
-      if (k0 + 16 < MP) load_g(cur ^ 1, k0 + 16);
-      bf16x8 xh[NB], xl[NB];
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         const int o = (wm * WT + i * 32 + fr) * LD + k0 + fk;
-        xh[i] = ld8(X + o);
-        xl[i] = ld8(X + PS + o);
+        xh[buf][i] = ld8(X + o);
+        xl[buf][i] = ld8(X + PS + o);
       }
+    };
+    load(0, 0);
+#pragma unroll
+    for (int k0 = 0; k0 < MP; k0 += 16) {
+      const int cur = (k0 >> 4) & 1;
+      if (k0 + 16 < MP) load(cur ^ 1, k0 + 16);
 #pragma unroll
       for (int i = 0; i < NB; ++i)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          acc[i][j] = mfma(xh[i], g[cur][j][2], acc[i][j]);
-          acc[i][j] = mfma(xl[i], g[cur][j][1], acc[i][j]);
-          acc[i][j] = mfma(xh[i], g[cur][j][1], acc[i][j]);
-          acc[i][j] = mfma(xl[i], g[cur][j][0], acc[i][j]);
-          acc[i][j] = mfma(xh[i], g[cur][j][0], acc[i][j]);
-        }
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma(xh[cur][i], g[cur][j][0], acc[i][j]);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma(xh[cur][i], g[cur][j][1], acc[i][j]);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma(xl[cur][i], g[cur][j][0], acc[i][j]);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma(xh[cur][i], g[cur][j][2], acc[i][j]);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma(xl[cur][i], g[cur][j][1], acc[i][j]);
     }
   };
   // element (row, col) of accumulator (i, j), register g * 4 + t
@@ -233,7 +300,7 @@ __global__ __launch_bounds__(256) void ns_gram_iter_kernel(NsGramIterArgs a) {
     prod_lg(sQ);           // T = Q_k A_0
     store(sW);             // sW held P_{k-1}, last read before the previous barrier
     __syncthreads();
-    prod_ll(sW, sQ);       // A_k = T Q_k
+    prod_ll(sW, sQ);       // A_k = T Q_k^T
 #pragma unroll
     for (int i = 0; i < NB; ++i)
 #pragma unroll
@@ -241,12 +308,12 @@ __global__ __launch_bounds__(256) void ns_gram_iter_kernel(NsGramIterArgs a) {
     __syncthreads();
     store(sW);
     __syncthreads();
-    prod_ll(sW, sW);       // A_k^2
+    prod_ll(sW, sW);       // S = A_k A_k^T
     poly();                // P_k
     __syncthreads();
     store(sW);
     __syncthreads();
-    prod_ll(sW, sQ);       // Q_{k+1} = P_k Q_k
+    prod_lc(sW, sQ);       // Q_{k+1} = P_k Q_k
     if (k + 1 < a.steps) {
       __syncthreads();
       store(sQ);

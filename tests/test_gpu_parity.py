@@ -239,3 +239,54 @@ def test_dion_padded_leading_dims(shape):
     assert rel(to_host(tQ), ref["Q"]) <= TOL["bf16"]
     assert rel(to_host(P), ref["P"]) <= TOL["bf16"]
     assert rel(to_host(bufs["X"])[:, :n], ref["X_exact"]) <= TOL["bf16"]
+
+
+# ----------------------------------------------------------------------------
+# Gram Newton-Schulz: bf16 products, Gram side of at most 128 rows, long side
+# at least four times longer (the iteration runs on the M x M side)
+# ----------------------------------------------------------------------------
+
+GRAM_NS_CASES = [(128, 4096), (64, 512), (100, 600), (1, 50), (37, 1000), (1000, 100),
+                 (512, 128), (128, 1000)]
+
+
+@pytest.mark.parametrize("shape", GRAM_NS_CASES)
+def test_gram_ns_matches_oracle(shape):
+    m, n = shape
+    _, G, _ = synth.small_case(7, m, n, 1, "bf16", x_scale=1.0)
+    note(f"gram ns {shape}")
+    got = gpu_ns(G, "bf16")
+    assert rel(got, oracle.gram_newton_schulz(G)) <= TOL["bf16"]
+    assert rel(got, oracle.newton_schulz(G)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("kind", ["rank1", "rank8", "planted"])
+def test_gram_ns_low_rank_inputs(kind):
+    """Rank-deficient and planted 128 x 4096 inputs (small eigen-directions of the
+    Gram matrix are where the side iteration loses precision)."""
+    m, n = 128, 4096
+    rng = np.random.default_rng({"rank1": 1, "rank8": 8, "planted": 32}[kind])
+    if kind == "planted":
+        S = synth.planted(23, m, n, 32, 10.0)
+        G = synth.gradient(23, m, n, 1, "bf16", planted_part=S)
+    else:
+        k = 1 if kind == "rank1" else 8
+        G = synth.to_storage(rng.standard_normal((m, k)) @ rng.standard_normal((k, n)), "bf16")
+    note(f"gram ns {kind}")
+    got = gpu_ns(G, "bf16")
+    err = rel(got, oracle.gram_newton_schulz(G))
+    print(kind, err)
+    assert err <= TOL["bf16"]
+
+
+def test_gram_ns_steps_and_coefficients():
+    _, G, _ = synth.small_case(8, 96, 640, 1, "bf16", x_scale=1.0)
+    for steps in (1, 2, 7):
+        note(f"gram ns steps={steps}")
+        assert rel(gpu_ns(G, "bf16", steps=steps), oracle.gram_newton_schulz(G, steps)) <= TOL["bf16"]
+    cubic = (1.5, -0.5, 0.0)
+    note("gram ns cubic")
+    assert rel(gpu_ns(G, "bf16", steps=8, abc=cubic),
+               oracle.gram_newton_schulz(G, 8, cubic)) <= TOL["bf16"]
+    note("gram ns zero input")
+    assert np.all(gpu_ns(np.zeros((96, 640), np.float32), "bf16") == 0)
