@@ -83,6 +83,39 @@ __device__ __forceinline__ void put4(bf16* s, int pstride, float a, float b, flo
   }
 }
 
+// Four consecutive elements as loaded, before any conversion: fp32 as a
+// float4, bf16 as the raw 8 bytes.  Loaders of one source keep this form until
+// store(), with rows outside the matrix masked by a zero limit rather than a
+// branch (measured: the triangular and correction applies of the
+// orthonormalisation 29 -> 24 us and 28 -> 22 us at 4096 x 256).  Loaders that
+// add two sources (M + G) add at load time: deferring that add to store()
+// measured slower (Dion sweeps at 4096 x 4096, r = 256: 81 -> 101 us and
+// 78 -> 89 us).
+template <typename T> struct Raw4;
+template <> struct Raw4<float> { typedef float4 type; };
+template <> struct Raw4<uint16_t> { typedef uint2 type; };
+
+template <typename T>
+__device__ __forceinline__ typename Raw4<T>::type load_raw4(const T* row, int c, int limit, bool vec);
+template <>
+__device__ __forceinline__ float4 load_raw4<float>(const float* row, int c, int limit, bool vec) {
+  return load4<float>(row, c, limit, vec);
+}
+template <>
+__device__ __forceinline__ uint2 load_raw4<uint16_t>(const uint16_t* row, int c, int limit, bool vec) {
+  if (vec && c + 4 <= limit) return *reinterpret_cast<const uint2*>(row + c);
+  uint16_t t[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) t[j] = (c + j < limit) ? row[c + j] : 0;
+  return make_uint2(t[0] | (uint32_t(t[1]) << 16), t[2] | (uint32_t(t[3]) << 16));
+}
+
+__device__ __forceinline__ float4 raw_to_f4(const float4& v) { return v; }
+__device__ __forceinline__ float4 raw_to_f4(const uint2& u) {
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+
 // Row-major source, k contiguous: element (i, k) = S[i*ld + k].  The source
 // is SRC_T (float or bf16 bits); with ADD = true the element is
 // S[i*ld+k] + S2[i*ld2+k] (momentum plus gradient).
@@ -96,27 +129,34 @@ struct LdRow {
   int64_t ld, ld2;
   int rows;
   bool vec;
-  float4 v[NCH];
+  typename Raw4<SRC_T>::type v[ADD ? 1 : NCH];
+  float4 vs[ADD ? NCH : 1];   // M + G
 
   __device__ LdRow(const MatArg& a, const MatArg& a2, int bi)
       : p(static_cast<const SRC_T*>(a.p[bi])),
         p2(ADD ? static_cast<const SRC2_T*>(a2.p[bi]) : nullptr),
         ld(a.ld), ld2(a2.ld), rows(a.rows), vec(a.vec && (!ADD || a2.vec)) {}
 
+  // Without ADD, rows past the end load nothing: every column index is then
+  // past the zero limit.
   __device__ __forceinline__ void load(int row0, int k0, int kend) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int idx = threadIdx.x + c * NT;
       const int r = idx / CPR, kc = (idx % CPR) * 4;
       const int gr = row0 + r;
-      if (gr < rows) {
-        v[c] = load4<SRC_T>(p + gr * ld, k0 + kc, kend, vec);
-        if constexpr (ADD) {
-          float4 g = load4<SRC2_T>(p2 + gr * ld2, k0 + kc, kend, vec);
-          v[c].x += g.x; v[c].y += g.y; v[c].z += g.z; v[c].w += g.w;
+      const bool in = gr < rows;
+      const int grc = in ? gr : 0;
+      if constexpr (ADD) {
+        if (in) {
+          vs[c] = load4<SRC_T>(p + gr * ld, k0 + kc, kend, vec);
+          const float4 g = load4<SRC2_T>(p2 + gr * ld2, k0 + kc, kend, vec);
+          vs[c].x += g.x; vs[c].y += g.y; vs[c].z += g.z; vs[c].w += g.w;
+        } else {
+          vs[c] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
       } else {
-        v[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+        v[c] = load_raw4<SRC_T>(p + grc * ld, k0 + kc, in ? kend : 0, vec);
       }
     }
   }
@@ -127,7 +167,10 @@ struct LdRow {
     for (int c = 0; c < NCH; ++c) {
       const int idx = threadIdx.x + c * NT;
       const int r = idx / CPR, kc = (idx % CPR) * 4;
-      put4<NP>(s + r * LDS_LD + kc, pstride, v[c].x, v[c].y, v[c].z, v[c].w);
+      float4 x;
+      if constexpr (ADD) x = vs[c];
+      else x = raw_to_f4(v[c]);
+      put4<NP>(s + r * LDS_LD + kc, pstride, x.x, x.y, x.z, x.w);
     }
   }
 };
@@ -189,13 +232,16 @@ struct LdCol {
   int64_t ld, ld2;
   int rows;
   bool vec;
-  float4 v[NCH][4];
+  typename Raw4<SRC_T>::type v[ADD ? 1 : NCH][4];
+  float4 vs[ADD ? NCH : 1][4];   // M + G
 
   __device__ LdCol(const MatArg& a, const MatArg& a2, int bi)
       : p(static_cast<const SRC_T*>(a.p[bi])),
         p2(ADD ? static_cast<const SRC2_T*>(a2.p[bi]) : nullptr),
         ld(a.ld), ld2(a2.ld), rows(a.rows), vec(a.vec && (!ADD || a2.vec)) {}
 
+  // Without ADD, source rows past kend load nothing: every column index is
+  // then past the zero limit.
   __device__ __forceinline__ void load(int row0, int k0, int kend) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -204,14 +250,18 @@ struct LdCol {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int gk = k0 + kc + t;
-        if (gk < kend) {
-          v[c][t] = load4<SRC_T>(p + gk * ld, row0 + jc, rows, vec);
-          if constexpr (ADD) {
-            float4 g = load4<SRC2_T>(p2 + gk * ld2, row0 + jc, rows, vec);
-            v[c][t].x += g.x; v[c][t].y += g.y; v[c][t].z += g.z; v[c][t].w += g.w;
+        const bool in = gk < kend;
+        const int gkc = in ? gk : 0;
+        if constexpr (ADD) {
+          if (in) {
+            vs[c][t] = load4<SRC_T>(p + gk * ld, row0 + jc, rows, vec);
+            const float4 g = load4<SRC2_T>(p2 + gk * ld2, row0 + jc, rows, vec);
+            vs[c][t].x += g.x; vs[c][t].y += g.y; vs[c][t].z += g.z; vs[c][t].w += g.w;
+          } else {
+            vs[c][t] = make_float4(0.f, 0.f, 0.f, 0.f);
           }
         } else {
-          v[c][t] = make_float4(0.f, 0.f, 0.f, 0.f);
+          v[c][t] = load_raw4<SRC_T>(p + gkc * ld, row0 + jc, in ? rows : 0, vec);
         }
       }
     }
@@ -223,10 +273,16 @@ struct LdCol {
     for (int c = 0; c < NCH; ++c) {
       const int idx = threadIdx.x + c * NT;
       const int jc = (idx % JC) * 4, kc = (idx / JC) * 4;
-      put4<NP>(s + (jc + 0) * LDS_LD + kc, pstride, v[c][0].x, v[c][1].x, v[c][2].x, v[c][3].x);
-      put4<NP>(s + (jc + 1) * LDS_LD + kc, pstride, v[c][0].y, v[c][1].y, v[c][2].y, v[c][3].y);
-      put4<NP>(s + (jc + 2) * LDS_LD + kc, pstride, v[c][0].z, v[c][1].z, v[c][2].z, v[c][3].z);
-      put4<NP>(s + (jc + 3) * LDS_LD + kc, pstride, v[c][0].w, v[c][1].w, v[c][2].w, v[c][3].w);
+      float4 x[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if constexpr (ADD) x[t] = vs[c][t];
+        else x[t] = raw_to_f4(v[c][t]);
+      }
+      put4<NP>(s + (jc + 0) * LDS_LD + kc, pstride, x[0].x, x[1].x, x[2].x, x[3].x);
+      put4<NP>(s + (jc + 1) * LDS_LD + kc, pstride, x[0].y, x[1].y, x[2].y, x[3].y);
+      put4<NP>(s + (jc + 2) * LDS_LD + kc, pstride, x[0].z, x[1].z, x[2].z, x[3].z);
+      put4<NP>(s + (jc + 3) * LDS_LD + kc, pstride, x[0].w, x[1].w, x[2].w, x[3].w);
     }
   }
 };
