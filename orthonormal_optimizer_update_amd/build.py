@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libortho.so")
 
-SOURCES = ["kernels_gemm.hip", "kernels_aux.hip", "kernels_stream.hip", "kernels_gram_ns.hip", "noalloc.hip", "abi.cpp",
+SOURCES = ["kernels_gemm.hip", "kernels_aux.hip", "kernels_stream.hip", "kernels_gram_ns.hip", "kernels_sweep.hip", "noalloc.hip", "abi.cpp",
            "plan.cpp"]
 
 COMMON_FLAGS = [

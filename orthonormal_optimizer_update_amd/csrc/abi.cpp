@@ -141,6 +141,31 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       }
     }
 
+    // Streaming sweeps (bf16 weights, r = 64, 128 or 256): the pieces of Q^T,
+    // then one pass over M and G into split-K slices.
+    SweepArgs sw{};
+    bool stream_sw = false;
+    if (bf && !fast_sw && pl.stream_sweeps) {
+      sw.m = tM; sw.g = user_table(G, b0, nb, 16);
+      sw.f[0] = ws_table(base, mb, pl.off_qhit, nb, n, r, ni, 2, 16);
+      sw.f[1] = ws_table(base, mb, pl.off_qlot, nb, n, r, ni, 2, 16);
+      sw.out = part_f; sw.out_member_stride = static_cast<int64_t>(mb / 4);
+      sw.split_stride = m * r;
+      sw.rows = mi; sw.K = ni; sw.r = r; sw.kchunk = pl.kchunk_sl; sw.M_rows = mi;
+      stream_sw = dion_sweep_ok(sw, nb);
+    }
+    if (stream_sw) {
+      SplitTArgs qa{};
+      qa.src = tQ; qa.hit = sw.f[0]; qa.lot = sw.f[1]; qa.rows = ni; qa.cols = r;
+      ORTHO_TRY(launch_split_t(qa, nb, s));
+      ORTHO_TRY(launch_dion_sweep(sw, false, nb, s));
+      RedArgs ra{};
+      ra.part = part_f; ra.part_member_stride = static_cast<int64_t>(mb / 4);
+      ra.slice = m * r; ra.splits = pl.split_sl; ra.rows = mi; ra.cols = r;
+      ra.out = tPt; ra.colsq = nullptr; ra.colsq_member_stride = 0;
+      ORTHO_TRY(launch_reduce_splits(ra, nb, s));
+    }
+
     // Sweep 1: P_tilde = (M + G) Q.
     DionLeftArgs la{};
     la.m = tM; la.g = tG; la.q = tQ;
@@ -148,8 +173,8 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     la.split_stride = m * r;
     la.M = mi; la.N = ni; la.r = r;
     la.splits = pl.split_left; la.kchunk = pl.kchunk_left;
-    if (!fast_sw) ORTHO_TRY(launch_dion_left(la, bf, nb, s));
-    if (!fast_sw && pl.split_left > 1) {
+    if (!fast_sw && !stream_sw) ORTHO_TRY(launch_dion_left(la, bf, nb, s));
+    if (!fast_sw && !stream_sw && pl.split_left > 1) {
       RedArgs ra{};
       ra.part = part_f; ra.part_member_stride = static_cast<int64_t>(mb / 4);
       ra.slice = m * r; ra.splits = pl.split_left; ra.rows = mi; ra.cols = r;
@@ -264,6 +289,18 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       r3.splits = pl.split_fr; r3.kchunk = pl.kchunk_fr;
       ORTHO_TRY(launch_fast_split3(r3, nb, s));
       split_r = pl.split_fr;
+    } else if (stream_sw) {
+      // over m: the pieces of P^T, then one pass over M and G
+      SweepArgs sr = sw;
+      sr.f[0] = ws_table(base, mb, pl.off_phit, nb, m, r, mi, 2, 16);
+      sr.f[1] = ws_table(base, mb, pl.off_plot, nb, m, r, mi, 2, 16);
+      sr.split_stride = n * r;
+      sr.rows = ni; sr.K = mi; sr.kchunk = pl.kchunk_sr;
+      SplitTArgs pa{};
+      pa.src = tPt; pa.hit = sr.f[0]; pa.lot = sr.f[1]; pa.rows = mi; pa.cols = r;
+      ORTHO_TRY(launch_split_t(pa, nb, s));
+      ORTHO_TRY(launch_dion_sweep(sr, true, nb, s));
+      split_r = pl.split_sr;
     } else {
       DionRightArgs rb{};
       rb.m = tM; rb.g = tG; rb.p = tPt; rb.out = tPart;

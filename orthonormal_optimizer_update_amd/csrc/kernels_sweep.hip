@@ -1,0 +1,254 @@
+// Dion's two power-iteration sweeps over B = M + G for bf16 weights and a
+// rank r of 64, 128 or 256 (MSR talk "Dion: The distributed orthonormal update
+// revolution is here", passage on amortised power iteration):
+//   left  (sweep 1):  P~ = B Q      (m x r, reduction over the n columns of B)
+//   right (sweep 2):  R  = B^T P    (n x r, reduction over the m rows of B)
+// Each is one streaming pass over M (fp32) and G (bf16) that is bound by HBM:
+// at 4096 x 4096 and r = 256, 96 MB against 26 GFLOP of bf16x3 products.
+//
+// Design (gfx950): a workgroup owns 128 output rows and all r columns, over
+// one split-K slice of the reduction.  The raw tiles of M and G and the bf16
+// pieces of the right factor (Q^T or P^T, hi and lo, k contiguous, prepared by
+// split_t) go from HBM/L2 into LDS with global_load_lds_dwordx4 copies, four
+// 16-deep k stages in flight.  Each wave builds its A fragments straight from
+// the raw tiles -- B = M + G in fp32, split into bf16 hi and lo in registers --
+// so B is never stored, and runs hi*hi + hi*lo + lo*hi on
+// v_mfma_f32_32x32x16_bf16 (the same bf16x3 products as the generic path).
+// The fp32 result of every slice goes to the split-K partial buffer, summed
+// in a fixed order by the reduce kernel that follows.
+//
+// Requirements (checked by the launcher): r in {64, 128, 256}; m and n
+// multiples of 64; M and G rows 16-byte aligned; the factor pieces r x K with
+// a leading dimension that is a multiple of 8; kchunk a multiple of 16.
+#include "gemm_fast.h"
+#include "launch.h"
+
+namespace ortho {
+
+namespace {
+
+constexpr int kRows = 128;          // output rows per workgroup (4 waves x 32)
+constexpr int kBK = 16;             // k per stage
+constexpr int kStages = 4;
+constexpr int kMBytes = kRows * kBK * 4;   // raw fp32 M tile per stage
+constexpr int kGBytes = kRows * kBK * 2;   // raw bf16 G tile per stage
+
+template <int R>
+struct SweepLayout {
+  static constexpr int kPieceBytes = R * kBK * 2;      // one bf16 piece of the factor
+  static constexpr int kStageBytes = kMBytes + kGBytes + 2 * kPieceBytes;
+  static constexpr int kMInstr = kMBytes / 1024;       // 1 KB per copy instruction
+  static constexpr int kGInstr = kGBytes / 1024;
+  static constexpr int kPInstr = 2 * kPieceBytes / 1024;
+  static constexpr int kInstr = kMInstr + kGInstr + kPInstr;
+  static_assert(kInstr % 4 == 0, "copies split evenly over four waves");
+  static constexpr int kPerWave = kInstr / 4;
+};
+
+__device__ __forceinline__ float2 bf16x2_to_f32(uint32_t u) {
+  return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
+}
+
+// 8 fp32 values as two bf16 pieces (x = hi + lo + O(2^-16 |x|)).
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const bf16 h = to_bf16(x[t]);
+    hi[t] = h;
+    lo[t] = to_bf16(x[t] - static_cast<float>(h));
+  }
+}
+
+}  // namespace
+
+// TRANS = false: sweep 1 (A rows are rows of B, k runs along a row of B);
+// TRANS = true:  sweep 2 (A rows are columns of B, k runs down a column).
+template <int R, bool TRANS>
+__global__ __launch_bounds__(256, 1) void dion_sweep_kernel(SweepArgs a) {
+  using L = SweepLayout<R>;
+  using namespace fast;
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * L::kStageBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int bi = blockIdx.z, split = blockIdx.y;
+  const int row0 = blockIdx.x * kRows;          // first output row of the workgroup
+  const int kbeg = split * a.kchunk;
+  const int kend = min(a.K, kbeg + a.kchunk);
+  const int nst = (kend - kbeg) / kBK;          // >= 1 (checked by the launcher)
+
+  const float* M = static_cast<const float*>(a.m.p[bi]);
+  const uint16_t* G = static_cast<const uint16_t*>(a.g.p[bi]);
+  const uint16_t* F0 = static_cast<const uint16_t*>(a.f[0].p[bi]);
+  const uint16_t* F1 = static_cast<const uint16_t*>(a.f[1].p[bi]);
+  const int64_t ldm = a.m.ld, ldg = a.g.ld, ldf = a.f[0].ld;
+  const int out_rows = a.rows;                   // m (sweep 1) or n (sweep 2)
+
+  // Per-lane byte offsets of this wave's copy instructions, relative to the
+  // stage's k0 column (sweep 1) or row (sweep 2) of the source; the stage base
+  // address is added per stage in scalar registers.  Copy instruction c of
+  // the workgroup: M tiles first, then G, then the two factor pieces; wave w
+  // issues instructions w, w + 4, ...
+  unsigned off[L::kPerWave];
+  int kind[L::kPerWave];   // 0: M, 1: G, 2: piece 0, 3: piece 1
+#pragma unroll
+  for (int u = 0; u < L::kPerWave; ++u) {
+    const int c = wave + 4 * u;
+    if (c < L::kMInstr) {
+      kind[u] = 0;
+      if (!TRANS) {
+        // 16 rows of 64 B; lane: row c*16 + lane/4, stored chunk lane%4,
+        // fetched chunk = stored ^ ((row >> 2) & 3)
+        const int rl = c * 16 + (lane >> 2), pos = lane & 3;
+        const int gr = min(row0 + rl, out_rows - 1);
+        off[u] = static_cast<unsigned>((gr * ldm) * 4 + (pos ^ ((rl >> 2) & 3)) * 16);
+      } else {
+        // 2 k-rows of 128 floats (512 B); lane: k-row c*2 + lane/32, chunk lane%32
+        const int kr = c * 2 + (lane >> 5), col = row0 + (lane & 31) * 4;
+        off[u] = static_cast<unsigned>((kr * ldm + min(col, out_rows - 4)) * 4);
+      }
+    } else if (c < L::kMInstr + L::kGInstr) {
+      kind[u] = 1;
+      const int cg = c - L::kMInstr;
+      if (!TRANS) {
+        // 32 rows of 32 B; stored chunk lane%2, fetched = stored ^ ((row >> 3) & 1)
+        const int rl = cg * 32 + (lane >> 1), pos = lane & 1;
+        const int gr = min(row0 + rl, out_rows - 1);
+        off[u] = static_cast<unsigned>((gr * ldg) * 2 + (pos ^ ((rl >> 3) & 1)) * 16);
+      } else {
+        // 4 k-rows of 128 bf16 (256 B); lane: k-row cg*4 + lane/16, chunk lane%16
+        const int kr = cg * 4 + (lane >> 4), col = row0 + (lane & 15) * 8;
+        off[u] = static_cast<unsigned>((kr * ldg + min(col, out_rows - 8)) * 2);
+      }
+    } else {
+      const int cp = c - L::kMInstr - L::kGInstr;
+      const int per = L::kPieceBytes / 1024;
+      kind[u] = 2 + cp / per;
+      // factor piece: 32 of its rows (output columns) of 32 B; same swizzle as G
+      const int j = (cp % per) * 32 + (lane >> 1), pos = lane & 1;
+      off[u] = static_cast<unsigned>((j * ldf) * 2 + (pos ^ ((j >> 3) & 1)) * 16);
+    }
+  }
+  const unsigned lds0 = lds_addr(smem);
+  auto issue = [&](int st) {
+    const int k0 = kbeg + st * kBK;
+    const int buf = st % kStages;
+    // scalar stage bases
+    const char* bm = TRANS ? reinterpret_cast<const char*>(M + (int64_t)k0 * ldm)
+                           : reinterpret_cast<const char*>(M + k0);
+    const char* bg = TRANS ? reinterpret_cast<const char*>(G + (int64_t)k0 * ldg)
+                           : reinterpret_cast<const char*>(G + k0);
+    const char* b0 = reinterpret_cast<const char*>(F0 + k0);
+    const char* b1 = reinterpret_cast<const char*>(F1 + k0);
+#pragma unroll
+    for (int u = 0; u < L::kPerWave; ++u) {
+      const int c = wave + 4 * u;
+      const char* base = kind[u] == 0 ? bm : (kind[u] == 1 ? bg : (kind[u] == 2 ? b0 : b1));
+      dma16(off[u], uniform_ptr(base), lds0 + buf * L::kStageBytes + c * 1024);
+    }
+  };
+
+  constexpr int NB = R / 32;
+  floatx16 acc[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+
+  // prologue: stages 0 .. kStages - 2 in flight
+#pragma unroll
+  for (int st = 0; st < kStages - 1; ++st)
+    if (st < nst) issue(st);
+
+  const int fr = lane & 31, half = lane >> 5;
+  for (int st = 0; st < nst; ++st) {
+    // this wave's copies of stage st are done when at most the later stages'
+    // remain outstanding; the barrier makes every wave's copies visible and
+    // frees the buffer of stage st - 1 for stage st + kStages - 1
+    const int later = min(nst - 1 - st, kStages - 2);
+    asm volatile("" ::: "memory");
+    if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * L::kPerWave) : "memory");
+    else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(L::kPerWave) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (st + kStages - 1 < nst) issue(st + kStages - 1);
+
+    const char* sb = smem + (st % kStages) * L::kStageBytes;
+    const float* sm = reinterpret_cast<const float*>(sb);
+    const uint16_t* sg = reinterpret_cast<const uint16_t*>(sb + kMBytes);
+    const char* sp = sb + kMBytes + kGBytes;
+    // A fragment: output row wave*32 + fr, k = half*8 .. + 7 of the stage
+    float x[8];
+    const int rl = wave * 32 + fr;
+    if (!TRANS) {
+      const floatx4 m0 = *reinterpret_cast<const floatx4*>(sm + rl * 16 + (((2 * half) ^ ((rl >> 2) & 3)) * 4));
+      const floatx4 m1 = *reinterpret_cast<const floatx4*>(sm + rl * 16 + (((2 * half + 1) ^ ((rl >> 2) & 3)) * 4));
+      const uint4 g = *reinterpret_cast<const uint4*>(sg + rl * 16 + ((half ^ ((rl >> 3) & 1)) * 8));
+      const float2 g0 = bf16x2_to_f32(g.x), g1 = bf16x2_to_f32(g.y), g2 = bf16x2_to_f32(g.z),
+                   g3 = bf16x2_to_f32(g.w);
+      x[0] = m0[0] + g0.x; x[1] = m0[1] + g0.y; x[2] = m0[2] + g1.x; x[3] = m0[3] + g1.y;
+      x[4] = m1[0] + g2.x; x[5] = m1[1] + g2.y; x[6] = m1[2] + g3.x; x[7] = m1[3] + g3.y;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int kr = half * 8 + t;
+        x[t] = sm[kr * 128 + rl] + bf16_bits_to_f32(sg[kr * 128 + rl]);
+      }
+    }
+    bf16x8 ah, al;
+    split8(x, ah, al);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int fj = j * 32 + fr;
+      const int o = fj * 32 + ((half ^ ((fj >> 3) & 1)) * 16);
+      const bf16x8 bh = *reinterpret_cast<const bf16x8*>(sp + o);
+      const bf16x8 bl = *reinterpret_cast<const bf16x8*>(sp + L::kPieceBytes + o);
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc[j], 0, 0, 0);
+    }
+  }
+
+  // slice `split` of the partial result, rows row0 + wave*32 .. + 31
+  float* out = a.out + bi * a.out_member_stride + split * a.split_stride;
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int row = row0 + wave * 32 + g * 8 + half * 4 + t;
+        if (row < out_rows) out[(int64_t)row * R + j * 32 + fr] = acc[j][g * 4 + t];
+      }
+}
+
+bool dion_sweep_ok(const SweepArgs& a, int members) {
+  if (a.r != 64 && a.r != 128 && a.r != 256) return false;
+  if (a.rows % 64 != 0 || a.K % 64 != 0 || a.kchunk % kBK != 0 || a.kchunk < kBK) return false;
+  if (a.m.ld % 4 != 0 || a.g.ld % 8 != 0 || a.f[0].ld % 8 != 0 || a.f[1].ld != a.f[0].ld) return false;
+  // 32-bit per-lane offsets: every source the copies address spans < 4 GiB
+  if ((int64_t)a.M_rows * a.m.ld * 4 >= (int64_t{1} << 32)) return false;
+  if ((int64_t)a.r * a.f[0].ld * 2 >= (int64_t{1} << 32)) return false;
+  for (int i = 0; i < members; ++i)
+    if (reinterpret_cast<uintptr_t>(a.m.p[i]) % 16 || reinterpret_cast<uintptr_t>(a.g.p[i]) % 16 ||
+        reinterpret_cast<uintptr_t>(a.f[0].p[i]) % 16 || reinterpret_cast<uintptr_t>(a.f[1].p[i]) % 16)
+      return false;
+  return true;
+}
+
+hipError_t launch_dion_sweep(const SweepArgs& a, bool trans, int members, hipStream_t s) {
+  if (!dion_sweep_ok(a, members)) return hipErrorInvalidValue;
+  dim3 grid((a.rows + kRows - 1) / kRows, (a.K + a.kchunk - 1) / a.kchunk, members);
+#define ORTHO_SWEEP(RR)                                                                      \
+  do {                                                                                       \
+    if (trans) hipLaunchKernelGGL((dion_sweep_kernel<RR, true>), grid, dim3(256), 0, s, a);  \
+    else hipLaunchKernelGGL((dion_sweep_kernel<RR, false>), grid, dim3(256), 0, s, a);      \
+  } while (0)
+  if (a.r == 64) ORTHO_SWEEP(64);
+  else if (a.r == 128) ORTHO_SWEEP(128);
+  else ORTHO_SWEEP(256);
+#undef ORTHO_SWEEP
+  return hipGetLastError();
+}
+
+}  // namespace ortho

@@ -174,6 +174,21 @@ struct DionRightArgs {
 };
 hipError_t launch_dion_right(const DionRightArgs& a, bool bf16, int members, hipStream_t s);
 
+// Dion sweeps for bf16 weights at r = 64, 128 or 256 (kernels_sweep.hip):
+// trans = false: out = (M + G) F^T, out rows = rows of M (sweep 1, F = Q^T);
+// trans = true:  out = (M + G)^T F^T, out rows = columns of M (sweep 2, F = P^T).
+// F is given as two bf16 pieces (hi, lo), r x K with k contiguous.  Each
+// split-K slice of kchunk k goes to out + split * split_stride (ld r).
+struct SweepArgs {
+  MatArg m, g;             // fp32 M and bf16 G, M_rows x (K or rows)
+  MatArg f[2];             // factor pieces, r x K
+  float* out;              // member 0's partial slices
+  int64_t out_member_stride, split_stride;
+  int rows, K, r, kchunk, M_rows;
+};
+bool dion_sweep_ok(const SweepArgs& a, int members);
+hipError_t launch_dion_sweep(const SweepArgs& a, bool trans, int members, hipStream_t s);
+
 // Orthonormalisation apply: P1 = Pt * T with T upper triangular, given as T^T
 // (r x r fp32, row-major).
 struct ApplyArgs {

@@ -117,6 +117,25 @@ bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* p) {
       if (pe > part) part = pe;
     }
   }
+  d.stream_sweeps = (r == 64 || r == 128 || r == 256) && m % 64 == 0 && n % 64 == 0;
+  if (d.stream_sweeps) {
+    // one 128-row workgroup per CU over the chunk's members, at least 128 k
+    // (eight 16-deep stages) per slice
+    auto pick = [&](int64_t rows, int64_t K, int* splits, int* kchunk) {
+      int64_t want = cdiv(256, cdiv(rows, 128) * d.chunk), cap = K / 128;
+      if (want > cap) want = cap;
+      if (want < 1) want = 1;
+      const int64_t kc = cdiv(cdiv(K, want), 16) * 16;
+      *kchunk = static_cast<int>(kc);
+      *splits = static_cast<int>(cdiv(K, kc));
+    };
+    pick(m, n, &d.split_sl, &d.kchunk_sl);
+    pick(n, m, &d.split_sr, &d.kchunk_sr);
+    const size_t psl = static_cast<size_t>(d.split_sl) * mr * 4;
+    const size_t psr = static_cast<size_t>(d.split_sr) * nr * 4;
+    if (psl > part) part = psl;
+    if (psr > part) part = psr;
+  }
   size_t o = 0;
   d.off_pt = o;    o = align_up(o + mrp * 4);
   d.off_p1 = o;    o = align_up(o + mrp * 4);
@@ -137,6 +156,8 @@ bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* p) {
     d.off_blo = o;   o = align_up(o + mn2);
     d.off_bhit = o;  o = align_up(o + mn2);
     d.off_blot = o;  o = align_up(o + mn2);
+  }
+  if (d.fast_sweeps || d.stream_sweeps) {
     d.off_qhit = o;  o = align_up(o + nr * 2);
     d.off_qlot = o;  o = align_up(o + nr * 2);
     d.off_phit = o;  o = align_up(o + mr * 2);

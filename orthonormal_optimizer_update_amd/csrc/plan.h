@@ -32,6 +32,11 @@ struct DionPlan {
   // and split-K factors in k tiles of the three-segment reductions.
   bool fast_sweeps;
   int split_fl, kchunk_fl, split_fr, kchunk_fr;
+  // Streaming sweeps (r = 64, 128 or 256, m and n multiples of 64, bf16
+  // weights): split-K factors of sweep 1 (over n) and sweep 2 (over m), with
+  // the transposed bf16 pieces of Q and P in off_qhit.. off_plot.
+  bool stream_sweeps;
+  int split_sl, kchunk_sl, split_sr, kchunk_sr;
   size_t off_bhi, off_blo, off_bhit, off_blot, off_qhit, off_qlot, off_phit, off_plot;
   // Orthonormalisation products on the 256 x 256 kernel (with fast_sweeps and
   // 3 r <= n): bf16 pieces in the B-piece buffers, free between the sweeps.

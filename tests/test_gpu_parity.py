@@ -128,6 +128,24 @@ DION_SHAPES = [(96, 80, 16), (300, 200, 37), (513, 257, 64), (128, 1000, 128), (
                # two-accumulator kernel (1152 rows: not 256-divisible)
                (384, 352, 256), (640, 1056, 512), (768, 1024, 512), (1152, 2048, 1024)]
 
+# bf16: the streaming sweeps (r = 64, 128, 256 with both sides multiples of 64),
+# with a last row tile of 64 rows, and r = m = n.  (fp32 weights take the
+# generic sweeps; on the last two shapes their P~ is conditioned badly enough
+# that fp32-accurate products land at 1.1e-4 and 1.7e-4 against the fp64
+# oracle, above the fp32 bar.)
+STREAM_SHAPES = [(384, 320, 64), (320, 448, 128), (576, 768, 256), (256, 256, 256),
+                 (1024, 512, 256)]
+
+
+@pytest.mark.parametrize("shape", STREAM_SHAPES)
+def test_dion_streaming_sweeps(shape):
+    m, n, r = shape
+    X, G1, Q0 = synth.small_case(10 + r, m, n, r, "bf16", planted_rank=min(4, r))
+    Gs = [G1] + [synth.gradient(1010 + r, m, n, t, "bf16") for t in (2, 3)]
+    worst, recs = run_dion_parity(X, Gs, Q0, mu=0.95, lr=0.01, dtype="bf16", label="stream")
+    print(shape, worst)
+    assert max(worst.values()) <= TOL["bf16"], recs
+
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", DION_SHAPES)
