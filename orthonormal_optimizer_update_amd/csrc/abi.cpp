@@ -156,7 +156,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     }
     if (stream_sw) {
       SplitTArgs qa{};
-      qa.src = tQ; qa.hit = sw.f[0]; qa.lot = sw.f[1]; qa.rows = ni; qa.cols = r;
+      qa.src = tQ; qa.hit = sw.f[0]; qa.lot = sw.f[1]; qa.rows = ni; qa.cols = r; qa.blocked = 1;
       ORTHO_TRY(launch_split_t(qa, nb, s));
       ORTHO_TRY(launch_dion_sweep(sw, false, nb, s));
       RedArgs ra{};
@@ -297,7 +297,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       sr.split_stride = n * r;
       sr.rows = ni; sr.K = mi; sr.kchunk = pl.kchunk_sr;
       SplitTArgs pa{};
-      pa.src = tPt; pa.hit = sr.f[0]; pa.lot = sr.f[1]; pa.rows = mi; pa.cols = r;
+      pa.src = tPt; pa.hit = sr.f[0]; pa.lot = sr.f[1]; pa.rows = mi; pa.cols = r; pa.blocked = 1;
       ORTHO_TRY(launch_split_t(pa, nb, s));
       ORTHO_TRY(launch_dion_sweep(sr, true, nb, s));
       split_r = pl.split_sr;

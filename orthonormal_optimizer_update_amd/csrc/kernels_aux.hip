@@ -122,11 +122,15 @@ __device__ __forceinline__ uint2 pack4(const uint16_t (&h)[4]) {
   return make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
 }
 
+// With blk16 > 0 the transposed pieces are written k-blocked instead of with
+// leading dimension ldt: element (j, k) of the cols x rows transpose at
+// (k / 16) * blk16 * 16 + j * 16 + k % 16 (blk16 = cols), so every 16-deep k
+// block of all cols rows is one contiguous run.
 template <bool kSum>
 __device__ __forceinline__ void split_tile(const float* src, int64_t lds_, const uint16_t* g,
                                            int64_t ldg, uint16_t* hi, uint16_t* lo, int64_t ldo,
                                            uint16_t* hit, uint16_t* lot, int64_t ldt, int r0,
-                                           int c0) {
+                                           int c0, int blk16 = 0) {
   __shared__ uint16_t th[64][68];
   __shared__ uint16_t tl[64][68];
   const int cl = (threadIdx.x & 15) * 4;
@@ -168,8 +172,10 @@ __device__ __forceinline__ void split_tile(const float* src, int64_t lds_, const
       h[e] = th[j][i4 + e];
       l[e] = tl[j][i4 + e];
     }
-    *reinterpret_cast<uint2*>(hit + (int64_t)(c0 + j) * ldt + r0 + i4) = pack4(h);
-    *reinterpret_cast<uint2*>(lot + (int64_t)(c0 + j) * ldt + r0 + i4) = pack4(l);
+    const int64_t o = blk16 > 0 ? (int64_t)((r0 + i4) >> 4) * blk16 * 16 + (c0 + j) * 16 + ((r0 + i4) & 15)
+                                : (int64_t)(c0 + j) * ldt + r0 + i4;
+    *reinterpret_cast<uint2*>(hit + o) = pack4(h);
+    *reinterpret_cast<uint2*>(lot + o) = pack4(l);
   }
 }
 
@@ -252,7 +258,7 @@ __global__ __launch_bounds__(256) void split_t_kernel(SplitTArgs a) {
   split_tile<false>(static_cast<const float*>(a.src.p[bi]), a.src.ld, nullptr, 0, nullptr, nullptr,
                     0, static_cast<uint16_t*>(const_cast<void*>(a.hit.p[bi])),
                     static_cast<uint16_t*>(const_cast<void*>(a.lot.p[bi])), a.hit.ld,
-                    blockIdx.y * 64, blockIdx.x * 64);
+                    blockIdx.y * 64, blockIdx.x * 64, a.blocked ? a.cols : 0);
 }
 
 // Column normalisation Q'[:, j] = R[:, j] / |R[:, j]|, in two launches.

@@ -6,9 +6,11 @@
 // Each is one streaming pass over M (fp32) and G (bf16) that is bound by HBM:
 // at 4096 x 4096 and r = 256, 96 MB against 26 GFLOP of bf16x3 products.
 //
-// Design (gfx950): a workgroup owns 128 output rows and all r columns, over
-// one split-K slice of the reduction.  The raw tiles of M and G and the bf16
-// pieces of the right factor (Q^T or P^T, hi and lo, k contiguous, prepared by
+// Design (gfx950): a workgroup of eight waves owns 128 output rows and all r
+// columns, over one split-K slice of the reduction; wave (rb, ch) computes
+// rows rb * 32 .. + 31 and half ch of the columns, so each SIMD runs two waves
+// and one's LDS reads and conversions overlap the other's products.  The raw
+// tiles of M and G and the bf16 pieces of the right factor (Q^T or P^T, hi and lo, k contiguous, prepared by
 // split_t) go from HBM/L2 into LDS with global_load_lds_dwordx4 copies, four
 // 16-deep k stages in flight.  Each wave builds its A fragments straight from
 // the raw tiles -- B = M + G in fp32, split into bf16 hi and lo in registers --
@@ -18,8 +20,10 @@
 // in a fixed order by the reduce kernel that follows.
 //
 // Requirements (checked by the launcher): r in {64, 128, 256}; m and n
-// multiples of 64; M and G rows 16-byte aligned; the factor pieces r x K with
-// a leading dimension that is a multiple of 8; kchunk a multiple of 16.
+// multiples of 64; M and G rows 16-byte aligned; the factor pieces k-blocked
+// (split_t with blocked set); kchunk a multiple of 16.
+#include <type_traits>
+
 #include "gemm_fast.h"
 #include "launch.h"
 
@@ -27,11 +31,13 @@ namespace ortho {
 
 namespace {
 
-constexpr int kRows = 128;          // output rows per workgroup (4 waves x 32)
+constexpr int kRows = 128;          // output rows per workgroup (4 row blocks of 32)
 constexpr int kBK = 16;             // k per stage
 constexpr int kStages = 4;
 constexpr int kMBytes = kRows * kBK * 4;   // raw fp32 M tile per stage
 constexpr int kGBytes = kRows * kBK * 2;   // raw bf16 G tile per stage
+
+constexpr int kWaves = 8;           // two per SIMD: 4 row blocks x 2 column halves
 
 template <int R>
 struct SweepLayout {
@@ -41,9 +47,16 @@ struct SweepLayout {
   static constexpr int kGInstr = kGBytes / 1024;
   static constexpr int kPInstr = 2 * kPieceBytes / 1024;
   static constexpr int kInstr = kMInstr + kGInstr + kPInstr;
-  static_assert(kInstr % 4 == 0, "copies split evenly over four waves");
-  static constexpr int kPerWave = kInstr / 4;
+  // wave w issues copies w, w + 8, ...: kLo or kLo + 1 of them per stage
+  static constexpr int kLo = kInstr / kWaves;
+  static constexpr int kHiWaves = kInstr % kWaves;     // waves 0 .. kHiWaves - 1 issue kLo + 1
+  static constexpr int kMaxPerWave = kLo + (kHiWaves ? 1 : 0);
 };
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
 
 __device__ __forceinline__ float2 bf16x2_to_f32(uint32_t u) {
   return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
@@ -64,7 +77,7 @@ __device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& 
 // TRANS = false: sweep 1 (A rows are rows of B, k runs along a row of B);
 // TRANS = true:  sweep 2 (A rows are columns of B, k runs down a column).
 template <int R, bool TRANS>
-__global__ __launch_bounds__(256, 1) void dion_sweep_kernel(SweepArgs a) {
+__global__ __launch_bounds__(512, 1) void dion_sweep_kernel(SweepArgs a) {
   using L = SweepLayout<R>;
   using namespace fast;
   __shared__ __attribute__((aligned(1024))) char smem[kStages * L::kStageBytes];
@@ -80,19 +93,20 @@ __global__ __launch_bounds__(256, 1) void dion_sweep_kernel(SweepArgs a) {
   const uint16_t* G = static_cast<const uint16_t*>(a.g.p[bi]);
   const uint16_t* F0 = static_cast<const uint16_t*>(a.f[0].p[bi]);
   const uint16_t* F1 = static_cast<const uint16_t*>(a.f[1].p[bi]);
-  const int64_t ldm = a.m.ld, ldg = a.g.ld, ldf = a.f[0].ld;
+  const int64_t ldm = a.m.ld, ldg = a.g.ld;
   const int out_rows = a.rows;                   // m (sweep 1) or n (sweep 2)
 
   // Per-lane byte offsets of this wave's copy instructions, relative to the
   // stage's k0 column (sweep 1) or row (sweep 2) of the source; the stage base
   // address is added per stage in scalar registers.  Copy instruction c of
   // the workgroup: M tiles first, then G, then the two factor pieces; wave w
-  // issues instructions w, w + 4, ...
-  unsigned off[L::kPerWave];
-  int kind[L::kPerWave];   // 0: M, 1: G, 2: piece 0, 3: piece 1
+  // issues instructions w, w + 8, ...
+  const int ncopy = L::kLo + (wave < L::kHiWaves ? 1 : 0);
+  unsigned off[L::kMaxPerWave];
+  int kind[L::kMaxPerWave];   // 0: M, 1: G, 2: piece 0, 3: piece 1
 #pragma unroll
-  for (int u = 0; u < L::kPerWave; ++u) {
-    const int c = wave + 4 * u;
+  for (int u = 0; u < L::kMaxPerWave; ++u) {
+    const int c = min(wave + kWaves * u, L::kInstr - 1);
     if (c < L::kMInstr) {
       kind[u] = 0;
       if (!TRANS) {
@@ -123,9 +137,11 @@ __global__ __launch_bounds__(256, 1) void dion_sweep_kernel(SweepArgs a) {
       const int cp = c - L::kMInstr - L::kGInstr;
       const int per = L::kPieceBytes / 1024;
       kind[u] = 2 + cp / per;
-      // factor piece: 32 of its rows (output columns) of 32 B; same swizzle as G
+      // factor piece, k-blocked: the stage's 16 k of all R rows are one
+      // contiguous run of R * 32 B; 32 rows (1 KB) per instruction, the same
+      // swizzle as G
       const int j = (cp % per) * 32 + (lane >> 1), pos = lane & 1;
-      off[u] = static_cast<unsigned>((j * ldf) * 2 + (pos ^ ((j >> 3) & 1)) * 16);
+      off[u] = static_cast<unsigned>(j * 32 + (pos ^ ((j >> 3) & 1)) * 16);
     }
   }
   const unsigned lds0 = lds_addr(smem);
@@ -137,49 +153,54 @@ __global__ __launch_bounds__(256, 1) void dion_sweep_kernel(SweepArgs a) {
                            : reinterpret_cast<const char*>(M + k0);
     const char* bg = TRANS ? reinterpret_cast<const char*>(G + (int64_t)k0 * ldg)
                            : reinterpret_cast<const char*>(G + k0);
-    const char* b0 = reinterpret_cast<const char*>(F0 + k0);
-    const char* b1 = reinterpret_cast<const char*>(F1 + k0);
+    const char* b0 = reinterpret_cast<const char*>(F0 + (int64_t)(k0 >> 4) * R * 16);
+    const char* b1 = reinterpret_cast<const char*>(F1 + (int64_t)(k0 >> 4) * R * 16);
 #pragma unroll
-    for (int u = 0; u < L::kPerWave; ++u) {
-      const int c = wave + 4 * u;
+    for (int u = 0; u < L::kMaxPerWave; ++u) {
+      if (u >= ncopy) break;
+      const int c = wave + kWaves * u;
       const char* base = kind[u] == 0 ? bm : (kind[u] == 1 ? bg : (kind[u] == 2 ? b0 : b1));
       dma16(off[u], uniform_ptr(base), lds0 + buf * L::kStageBytes + c * 1024);
     }
   };
+  // wait until at most `later` stages of this wave's copies are outstanding
+  auto wait_stages = [&](int later) {
+    static_assert(kStages <= 5, "wait cases cover up to three later stages");
+    if (ncopy == L::kLo) {
+      if (later >= 3) wait_vm<3 * L::kLo>();
+      else if (later == 2) wait_vm<2 * L::kLo>();
+      else if (later == 1) wait_vm<L::kLo>();
+      else wait_vm<0>();
+    } else {
+      if (later >= 3) wait_vm<3 * L::kMaxPerWave>();
+      else if (later == 2) wait_vm<2 * L::kMaxPerWave>();
+      else if (later == 1) wait_vm<L::kMaxPerWave>();
+      else wait_vm<0>();
+    }
+  };
 
-  constexpr int NB = R / 32;
+  // wave (rb, ch): output rows rb * 32 .. + 31, columns ch * R / 2 .. + R / 2 - 1
+  const int rb = wave & 3, ch = wave >> 2;
+  constexpr int NB = R / 64;
   floatx16 acc[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
 
-  // prologue: stages 0 .. kStages - 2 in flight
-#pragma unroll
-  for (int st = 0; st < kStages - 1; ++st)
-    if (st < nst) issue(st);
-
+  // Fragments of one stage: the A fragment (B = M + G split into hi and lo)
+  // and the NB column blocks of both factor pieces.
   const int fr = lane & 31, half = lane >> 5;
-  for (int st = 0; st < nst; ++st) {
-    // this wave's copies of stage st are done when at most the later stages'
-    // remain outstanding; the barrier makes every wave's copies visible and
-    // frees the buffer of stage st - 1 for stage st + kStages - 1
-    const int later = min(nst - 1 - st, kStages - 2);
-    asm volatile("" ::: "memory");
-    if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * L::kPerWave) : "memory");
-    else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(L::kPerWave) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (st + kStages - 1 < nst) issue(st + kStages - 1);
-
+  const int rl = rb * 32 + fr;
+  bf16x8 fa[2][2], fb[2][NB][2];
+  auto read_frags = [&](int st, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
     const char* sb = smem + (st % kStages) * L::kStageBytes;
     const float* sm = reinterpret_cast<const float*>(sb);
     const uint16_t* sg = reinterpret_cast<const uint16_t*>(sb + kMBytes);
     const char* sp = sb + kMBytes + kGBytes;
-    // A fragment: output row wave*32 + fr, k = half*8 .. + 7 of the stage
+    // A fragment: output row rl, k = half*8 .. + 7 of the stage
     float x[8];
-    const int rl = wave * 32 + fr;
     if (!TRANS) {
       const floatx4 m0 = *reinterpret_cast<const floatx4*>(sm + rl * 16 + (((2 * half) ^ ((rl >> 2) & 3)) * 4));
       const floatx4 m1 = *reinterpret_cast<const floatx4*>(sm + rl * 16 + (((2 * half + 1) ^ ((rl >> 2) & 3)) * 4));
@@ -195,21 +216,64 @@ __global__ __launch_bounds__(256, 1) void dion_sweep_kernel(SweepArgs a) {
         x[t] = sm[kr * 128 + rl] + bf16_bits_to_f32(sg[kr * 128 + rl]);
       }
     }
-    bf16x8 ah, al;
-    split8(x, ah, al);
+    split8(x, fa[buf][0], fa[buf][1]);
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const int fj = j * 32 + fr;
+      const int fj = ch * (R / 2) + j * 32 + fr;
       const int o = fj * 32 + ((half ^ ((fj >> 3) & 1)) * 16);
-      const bf16x8 bh = *reinterpret_cast<const bf16x8*>(sp + o);
-      const bf16x8 bl = *reinterpret_cast<const bf16x8*>(sp + L::kPieceBytes + o);
-      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc[j], 0, 0, 0);
-      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc[j], 0, 0, 0);
-      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc[j], 0, 0, 0);
+      fb[buf][j][0] = *reinterpret_cast<const bf16x8*>(sp + o);
+      fb[buf][j][1] = *reinterpret_cast<const bf16x8*>(sp + L::kPieceBytes + o);
     }
+  };
+  // wait until this wave's copies of stage `st` are done (at most the stages
+  // issued after it still outstanding), then the barrier makes every wave's
+  // copies visible
+  auto ready = [&](int st, int issued_last) {
+    asm volatile("" ::: "memory");
+    wait_stages(issued_last - st);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // prologue: stages 0 .. kStages - 2 in flight, stage 0's fragments read
+#pragma unroll
+  for (int st = 0; st < kStages - 1; ++st)
+    if (st < nst) issue(st);
+  int issued_last = min(kStages - 2, nst - 1);
+  ready(0, issued_last);
+  read_frags(0, std::integral_constant<int, 0>{});
+
+  // one stage whose fragments are in buffer CUR (a compile-time index, so the
+  // fragments stay in registers); the next stage's go to buffer CUR ^ 1
+  auto step = [&](auto cur_c, int st) {
+    constexpr int CUR = decltype(cur_c)::value;
+    if (st + 1 < nst) {
+      // stage st + 1 in LDS; after this barrier every wave has read stage st's
+      // fragments (previous step), so the buffer of stage st - 1 is free
+      ready(st + 1, issued_last);
+      if (st + kStages - 1 < nst) {
+        issue(st + kStages - 1);
+        issued_last = st + kStages - 1;
+      }
+      read_frags(st + 1, std::integral_constant<int, CUR ^ 1>{});
+    }
+    // each product kind over all accumulators before the next kind
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[CUR][0], fb[CUR][j][0], acc[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[CUR][0], fb[CUR][j][1], acc[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[CUR][1], fb[CUR][j][0], acc[j], 0, 0, 0);
+  };
+  for (int st = 0; st < nst; st += 2) {
+    step(std::integral_constant<int, 0>{}, st);
+    if (st + 1 < nst) step(std::integral_constant<int, 1>{}, st + 1);
   }
 
-  // slice `split` of the partial result, rows row0 + wave*32 .. + 31
+  // slice `split` of the partial result, rows row0 + rb*32 .. + 31
   float* out = a.out + bi * a.out_member_stride + split * a.split_stride;
 #pragma unroll
   for (int j = 0; j < NB; ++j)
@@ -217,18 +281,17 @@ __global__ __launch_bounds__(256, 1) void dion_sweep_kernel(SweepArgs a) {
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int row = row0 + wave * 32 + g * 8 + half * 4 + t;
-        if (row < out_rows) out[(int64_t)row * R + j * 32 + fr] = acc[j][g * 4 + t];
+        const int row = row0 + rb * 32 + g * 8 + half * 4 + t;
+        if (row < out_rows) out[(int64_t)row * R + ch * (R / 2) + j * 32 + fr] = acc[j][g * 4 + t];
       }
 }
 
 bool dion_sweep_ok(const SweepArgs& a, int members) {
   if (a.r != 64 && a.r != 128 && a.r != 256) return false;
   if (a.rows % 64 != 0 || a.K % 64 != 0 || a.kchunk % kBK != 0 || a.kchunk < kBK) return false;
-  if (a.m.ld % 4 != 0 || a.g.ld % 8 != 0 || a.f[0].ld % 8 != 0 || a.f[1].ld != a.f[0].ld) return false;
+  if (a.m.ld % 4 != 0 || a.g.ld % 8 != 0) return false;
   // 32-bit per-lane offsets: every source the copies address spans < 4 GiB
   if ((int64_t)a.M_rows * a.m.ld * 4 >= (int64_t{1} << 32)) return false;
-  if ((int64_t)a.r * a.f[0].ld * 2 >= (int64_t{1} << 32)) return false;
   for (int i = 0; i < members; ++i)
     if (reinterpret_cast<uintptr_t>(a.m.p[i]) % 16 || reinterpret_cast<uintptr_t>(a.g.p[i]) % 16 ||
         reinterpret_cast<uintptr_t>(a.f[0].p[i]) % 16 || reinterpret_cast<uintptr_t>(a.f[1].p[i]) % 16)
@@ -241,8 +304,8 @@ hipError_t launch_dion_sweep(const SweepArgs& a, bool trans, int members, hipStr
   dim3 grid((a.rows + kRows - 1) / kRows, (a.K + a.kchunk - 1) / a.kchunk, members);
 #define ORTHO_SWEEP(RR)                                                                      \
   do {                                                                                       \
-    if (trans) hipLaunchKernelGGL((dion_sweep_kernel<RR, true>), grid, dim3(256), 0, s, a);  \
-    else hipLaunchKernelGGL((dion_sweep_kernel<RR, false>), grid, dim3(256), 0, s, a);      \
+    if (trans) hipLaunchKernelGGL((dion_sweep_kernel<RR, true>), grid, dim3(512), 0, s, a);  \
+    else hipLaunchKernelGGL((dion_sweep_kernel<RR, false>), grid, dim3(512), 0, s, a);      \
   } while (0)
   if (a.r == 64) ORTHO_SWEEP(64);
   else if (a.r == 128) ORTHO_SWEEP(128);

@@ -80,11 +80,14 @@ struct SplitSumArgs {
   int rows, cols;
 };
 hipError_t launch_split_sum(const SplitSumArgs& a, int members, hipStream_t s);
-// Transposed pieces of an fp32 rows x cols matrix: hit, lot are cols x rows.
+// Transposed pieces of an fp32 rows x cols matrix: hit, lot are cols x rows
+// (leading dimension hit.ld), or, with blocked, k-blocked: element (j, k) at
+// (k / 16) * cols * 16 + j * 16 + k % 16.
 struct SplitTArgs {
   MatArg src;
   MatArg hit, lot;
   int rows, cols;
+  int blocked;
 };
 hipError_t launch_split_t(const SplitTArgs& a, int members, hipStream_t s);
 
@@ -177,8 +180,9 @@ hipError_t launch_dion_right(const DionRightArgs& a, bool bf16, int members, hip
 // Dion sweeps for bf16 weights at r = 64, 128 or 256 (kernels_sweep.hip):
 // trans = false: out = (M + G) F^T, out rows = rows of M (sweep 1, F = Q^T);
 // trans = true:  out = (M + G)^T F^T, out rows = columns of M (sweep 2, F = P^T).
-// F is given as two bf16 pieces (hi, lo), r x K with k contiguous.  Each
-// split-K slice of kchunk k goes to out + split * split_stride (ld r).
+// F is given as two bf16 pieces (hi, lo), r x K k-blocked as split_t writes
+// them with blocked set.  Each split-K slice of kchunk k goes to
+// out + split * split_stride (ld r).
 struct SweepArgs {
   MatArg m, g;             // fp32 M and bf16 G, M_rows x (K or rows)
   MatArg f[2];             // factor pieces, r x K
