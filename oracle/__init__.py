@@ -34,6 +34,13 @@ public pages about microsoft/dion):
   the common norm ||U||_F / sqrt(m), which keeps the total norm; "parity
   unpinned" as to fidelity, pinned against its own definition.
 
+* ``dion2_step`` -- Dion2: the k rows of B = M + G with the largest norm are
+  orthonormalised with Newton-Schulz and applied; error feedback keeps mu times
+  the applied rows and every other row whole.  agentlenshq "microsoft/dion",
+  sections "How it works" and "Highlights"; hysenlabs, section "Dion3 is not a
+  retuning of Dion2, and the README says so".  The selection rule is not
+  printed; largest row norm is the reading, "parity unpinned" as to fidelity.
+
 * ``muon_step`` -- the Muon step around the Newton-Schulz path: a heavy-ball
   momentum buffer, its Newton-Schulz orthogonalisation, and the SGD-form update.
   Same talk, same passages.  The momentum form is the plainest reading and
@@ -66,4 +73,6 @@ from .dion_ref import (  # noqa: F401
     muon_step,
     row_normalize,
     normuon_step,
+    select_rows,
+    dion2_step,
 )

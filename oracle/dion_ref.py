@@ -287,3 +287,58 @@ def normuon_step(X, G, M, mu: float, lr: float, scale: float = 1.0, steps: int =
     dX = -float(lr) * float(scale) * V
     X_exact = X + dX
     return dict(X=round_to_dtype(X_exact, x_dtype), X_exact=X_exact, dX=dX, M=M_new, U=U, V=V)
+
+
+# ----------------------------------------------------------------------------
+# Dion2: submatrix selection with error feedback
+# ----------------------------------------------------------------------------
+
+def select_rows(B, k: int) -> np.ndarray:
+    """Indices of the k rows of B with the largest l2 norm, largest first; equal
+    norms are ordered by row index (lower first), so the choice is unique.
+    A row whose norm is NaN is ordered after every other row."""
+    B = _f64(B)
+    sq = np.einsum("ij,ij->i", B, B)
+    key = np.where(np.isnan(sq), -1.0, sq)
+    order = sorted(range(B.shape[0]), key=lambda i: (-key[i], i))
+    return np.asarray(order[:k], dtype=np.int64)
+
+
+def dion2_step(X, G, M, k: int, mu: float, lr: float, scale: float = 1.0, steps: int = 5,
+               abc=MUON_ABC, eps: float = NS_EPS, x_dtype: str = "bf16",
+               selected=None) -> dict:
+    """One Dion2 step on one matrix, in fp64.
+
+    agentlenshq "microsoft/dion", sections "How it works" (Dion2 selects a
+    submatrix; every Dion variant keeps error feedback) and "Highlights" (only a
+    fraction of the momentum takes part); hysenlabs "Microsoft Dion: orthonormal
+    optimizers that assume DTensor parallelism", section "Dion3 is not a
+    retuning of Dion2, and the README says so" (mu is Dion2's error-feedback
+    decay).  No selection rule or formula is printed; the reading:
+        B   = M + G
+        S   = the k rows of B with the largest l2 norm (select_rows)
+        U   = newton_schulz(B[S], steps, abc, eps)      (orthonormalised block)
+        X'  = X, with rows S replaced by X[S] - lr * scale * U, rounded to x_dtype
+        M'  = B, with rows S replaced by mu * B[S]      (error feedback: the
+              applied block keeps the fraction mu, the rest is kept whole)
+    ``selected`` overrides S (the rows, in the order they are stacked into the
+    block).  Returns X (rounded), X_exact, dX, M, U, B, S.
+    """
+    X, G, M = _f64(X), _f64(G), _f64(M)
+    B = _momentum_accumulate(M, G)
+    import oracle.dion_ref as _self   # the module attribute, so a pin can replace it
+    S = _self.select_rows(B, k) if selected is None else np.asarray(selected, dtype=np.int64)
+    U = newton_schulz(B[S], steps, abc, eps)
+    dX = np.zeros_like(X)
+    dX[S] = -float(lr) * float(scale) * U
+    X_exact = X + dX
+    M_new = _dion2_feedback(B, S, float(mu))
+    return dict(X=round_to_dtype(X_exact, x_dtype), X_exact=X_exact, dX=dX, M=M_new, U=U, B=B, S=S)
+
+
+def _dion2_feedback(B, S, mu):
+    # the applied rows keep the fraction mu; every other row is kept whole
+    M_new = B.copy()
+    M_new[S] = mu * B[S]
+    return M_new
+

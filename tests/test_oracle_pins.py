@@ -534,3 +534,89 @@ def test_mutant_gram_ns_caught(rng, monkeypatch, mutant):
     monkeypatch.setattr(dion_ref, "_gram_ns_step", locals()[mutant])
     G = rng.standard_normal((8, 40))
     assert not (gram_ns_err(G) <= 1e-6)
+
+
+# ----------------------------------------------------------------------------
+# Dion2: row selection, orthonormalised block, error feedback
+# ----------------------------------------------------------------------------
+
+def dion2_pin_err(rng, m=12, n=20, k=5, mu=0.8, lr=0.05, scale=1.7):
+    """Max error over the Dion2 pins on one generic case: selection equals a
+    brute-force ranking of the row norms, unselected rows of M' are B and of X
+    are X, the selected update is -lr*scale times the SVD closed form of the
+    block, the applied rows of M' are mu * B."""
+    X = rng.standard_normal((m, n))
+    G = rng.standard_normal((m, n)) * (1.0 + np.arange(m))[:, None] / m
+    M = rng.standard_normal((m, n))
+    out = oracle.dion2_step(X, G, M, k, mu, lr, scale, x_dtype="f32")
+    B = M + G
+    norms = [float(np.sqrt(sum(v * v for v in row))) for row in B]
+    ranked = sorted(range(m), key=lambda i: (-norms[i], i))[:k]
+    errs = [0.0 if list(out["S"]) == ranked else 1.0]
+    rest = np.setdiff1d(np.arange(m), out["S"])
+    if rest.size:
+        errs.append(np.abs(out["M"][rest] - B[rest]).max())
+        errs.append(np.abs(out["X_exact"][rest] - X[rest]).max())
+    want = -lr * scale * quintic_spectral(B[out["S"]])
+    errs.append(np.abs(out["dX"][out["S"]] - want).max() / (lr * scale))
+    errs.append(np.abs(out["M"][out["S"]] - mu * B[out["S"]]).max())
+    return max(errs)
+
+
+def test_dion2_pins(rng):
+    assert dion2_pin_err(rng) <= 1e-12
+    assert dion2_pin_err(rng, m=7, n=30, k=7) <= 1e-12   # every row selected
+    assert dion2_pin_err(rng, m=9, n=4, k=2) <= 1e-12    # tall block
+
+
+def test_dion2_selection_ties_and_nan():
+    B = np.zeros((6, 2))
+    B[:, 0] = [3.0, 5.0, 5.0, 1.0, 4.0, 0.0]
+    assert list(oracle.select_rows(B, 3)) == [1, 2, 4]
+    B[3, 0] = np.nan
+    assert list(oracle.select_rows(B, 6)) == [1, 2, 4, 0, 5, 3]
+
+
+def test_dion2_special_cases(rng):
+    m, n, k = 10, 16, 4
+    X, G, M = (rng.standard_normal((m, n)) for _ in range(3))
+    out = oracle.dion2_step(X, G, M, k, mu=1.0, lr=0.1, x_dtype="f32")
+    assert np.array_equal(out["M"], M + G)                     # mu = 1: nothing decays
+    out = oracle.dion2_step(X, G, M, k, mu=0.0, lr=0.0, x_dtype="f32")
+    assert np.all(out["M"][out["S"]] == 0)                      # mu = 0: applied rows cleared
+    assert np.array_equal(out["X_exact"], X)                   # lr = 0: no update
+    # k = m: the block is all of B in norm order, so the update is Newton-Schulz
+    # of B with its rows permuted back
+    out = oracle.dion2_step(X, G, M, m, mu=0.5, lr=0.1, x_dtype="f32")
+    assert np.abs(out["dX"] + 0.1 * oracle.newton_schulz(M + G)).max() <= 1e-12
+
+
+def test_dion2_row_permutation_equivariance(rng):
+    m, n, k = 11, 15, 6
+    X, G, M = (rng.standard_normal((m, n)) for _ in range(3))
+    perm = rng.permutation(m)
+    a = oracle.dion2_step(X, G, M, k, 0.7, 0.05, x_dtype="f32")
+    b = oracle.dion2_step(X[perm], G[perm], M[perm], k, 0.7, 0.05, x_dtype="f32")
+    assert np.abs(a["X_exact"][perm] - b["X_exact"]).max() <= 1e-13
+    assert np.abs(a["M"][perm] - b["M"]).max() <= 1e-13
+
+
+@pytest.mark.parametrize("mutant", ["smallest_rows", "feedback_one_minus_mu", "l1_norm"])
+def test_mutant_dion2_caught(rng, monkeypatch, mutant):
+    if mutant == "smallest_rows":
+        def bad(B, k):
+            sq = np.einsum("ij,ij->i", B, B)
+            return np.argsort(sq, kind="stable")[:k]
+        monkeypatch.setattr(dion_ref, "select_rows", bad)
+    elif mutant == "feedback_one_minus_mu":
+        def bad(B, S, mu):
+            Mn = B.copy()
+            Mn[S] = (1.0 - mu) * B[S]
+            return Mn
+        monkeypatch.setattr(dion_ref, "_dion2_feedback", bad)
+    else:
+        def bad(B, k):                      # rows ranked by l1 instead of l2 norm
+            l1 = np.abs(B).sum(axis=1)
+            return np.argsort(-l1, kind="stable")[:k]
+        monkeypatch.setattr(dion_ref, "select_rows", bad)
+    assert not (dion2_pin_err(rng) <= 1e-6)
