@@ -20,6 +20,8 @@
  *                  its orthogonalisation, SGD-form update (declared below).
  *   normuon_step   muon_step with the orthogonalised momentum normalised per
  *                  neuron (row) before the update (declared below).
+ *   dion2_step     Dion2: the rows of largest norm orthonormalised and applied,
+ *                  with error feedback (declared below).
  *   newton_schulz  Muon's Newton-Schulz orthogonalisation, the full-rank
  *                  comparison path.  Same talk, passage contrasting SGD with an
  *                  orthonormal update (take U V^T of the SVD) and the passage on
@@ -234,6 +236,39 @@ ortho_status normuon_step_batched(int32_t batch, const ortho_mat* X, const ortho
                                   const ortho_mat* M, int32_t steps, const float* abc, float mu,
                                   float lr, float scale, void* ws, size_t ws_bytes,
                                   void* stream);
+
+/* Bytes of device workspace for dion2_step on an m x n matrix selecting k
+ * rows.  Returns 0 for invalid arguments. */
+size_t ortho_dion2_workspace_size(int64_t m, int64_t n, int32_t k);
+
+/* One Dion2 step on one matrix: submatrix selection with error feedback.
+ * agentlenshq "microsoft/dion", sections "How it works" (Dion2 selects a
+ * submatrix; the Dion variants keep error feedback) and "Highlights" (only a
+ * fraction of the momentum takes part); hysenlabs "Microsoft Dion: orthonormal
+ * optimizers that assume DTensor parallelism", section "Dion3 is not a
+ * retuning of Dion2, and the README says so" (mu is Dion2's error-feedback
+ * decay).  The pages print no selection rule; the reading taken:
+ *     B  = M + G
+ *     S  = the k rows of B with the largest l2 norm (equal norms: the lower
+ *          row index first; a NaN norm after every other)
+ *     U  = newton_schulz(B[S], steps, abc)   (the rows stacked in that order)
+ *     X[S] = X[S] - lr * scale * U,  rounded to nearest even into X's dtype;
+ *            the other rows of X are untouched
+ *     M  = B, with the rows S replaced by mu * B[S]
+ *   X      m x n, ORTHO_BF16 or ORTHO_F32, updated in place; m <= 65535.
+ *   G      m x n, same dtype as X, read only.
+ *   M      m x n, ORTHO_F32, updated in place (start it at zero).
+ *   k      1 <= k <= m, else ORTHO_E_RANK.
+ *   steps, abc as for newton_schulz (fp32-accurate products for ORTHO_F32
+ *          weights, bf16 products for ORTHO_BF16).
+ *   mu in [0, 1]; lr and scale finite, else ORTHO_E_PARAM.
+ *   selected  NULL, or a DEVICE array of k int32 that receives S in the order
+ *          above.
+ *   ws     >= ortho_dion2_workspace_size(m, n, k) bytes, 256-byte aligned.
+ * Errors are returned before anything is enqueued. */
+ortho_status dion2_step(ortho_mat X, ortho_mat G, ortho_mat M, int32_t k, int32_t steps,
+                        const float* abc, float mu, float lr, float scale, int32_t* selected,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* Static English description of a status code. */
 const char* ortho_status_str(int32_t status);

@@ -72,6 +72,11 @@ _SIGS = {
                                             ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "dion_step_noalloc": (ctypes.c_int, [OrthoMat, OrthoMat, OrthoMat, OrthoMat, ctypes.c_int32,
                                          ctypes.c_float, ctypes.c_float, ctypes.c_void_p]),
+    "ortho_dion2_workspace_size": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]),
+    "dion2_step": (ctypes.c_int, [OrthoMat, OrthoMat, OrthoMat, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.POINTER(ctypes.c_float), ctypes.c_float, ctypes.c_float,
+                                  ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_void_p]),
     "ortho_status_str": (ctypes.c_char_p, [ctypes.c_int32]),
     "ortho_abi_version": (ctypes.c_int32, []),
 }
@@ -288,3 +293,18 @@ def normuon_step_batched(Xs: Sequence, Gs: Sequence, Ms: Sequence, mu: float, lr
     st = lib().normuon_step_batched(b, X, G, M, steps, _abc(abc), mu, lr, scale, _ptr(ws),
                                     ws.numel(), _stream_ptr(Xs[0].device))
     _check("normuon_step_batched", st)
+
+
+def dion2_workspace_size(m: int, n: int, k: int) -> int:
+    return int(lib().ortho_dion2_workspace_size(m, n, k))
+
+
+def dion2_step(X, G, M, k: int, mu: float, lr: float, scale: float = 1.0, steps: int = 5,
+               abc=None, selected=None, ws=None):
+    """One Dion2 step in place on (X, M); see ``dion2_step`` in ortho.h.
+    ``selected`` (optional) is a device int32 tensor of k entries."""
+    if ws is None:
+        ws = workspace(dion2_workspace_size(X.size(0), X.size(1), k), X.device)
+    st = lib().dion2_step(mat(X), mat(G), mat(M), k, steps, _abc(abc), mu, lr, scale,
+                          _ptr(selected), _ptr(ws), ws.numel(), _stream_ptr(X.device))
+    _check("dion2_step", st)

@@ -19,8 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libortho.so")
 
-SOURCES = ["kernels_gemm.hip", "kernels_aux.hip", "kernels_stream.hip", "kernels_gram_ns.hip", "kernels_sweep.hip", "noalloc.hip", "abi.cpp",
-           "plan.cpp"]
+SOURCES = ["kernels_gemm.hip", "kernels_aux.hip", "kernels_stream.hip", "kernels_gram_ns.hip",
+           "kernels_sweep.hip", "kernels_dion2.hip", "noalloc.hip", "abi.cpp", "plan.cpp"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -593,6 +593,39 @@ ortho_status run_muon(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
   return ORTHO_OK;
 }
 
+ortho_status run_dion2(const ortho_mat& X, const ortho_mat& G, const ortho_mat& M, int32_t k,
+                       int32_t steps, const float* abc, float mu, float lr, float scale,
+                       int32_t* selected, void* ws, void* stream) {
+  Dion2Plan pl;
+  if (!plan_dion2(X.rows, X.cols, k, &pl)) return ORTHO_E_SHAPE;
+  const bool bf = X.dtype == ORTHO_BF16;
+  const hipStream_t s = as_stream(stream);
+  char* base = static_cast<char*>(ws);
+  const size_t gvec = bf ? 8 : 16;
+  const int m = static_cast<int>(X.rows), n = static_cast<int>(X.cols);
+  Dion2Args a{};
+  a.x = user_table(&X, 0, 1, gvec);
+  a.g = user_table(&G, 0, 1, gvec);
+  a.m = user_table(&M, 0, 1, 16);
+  a.blk = ws_table(base, 0, pl.off_blk, 1, pl.ld_blk, k, n, 4, 16);
+  a.norms = reinterpret_cast<float*>(base + pl.off_norms);
+  a.rank = reinterpret_cast<int*>(base + pl.off_rank);
+  a.sel = reinterpret_cast<int*>(base + pl.off_sel);
+  a.vec_stride = 0;
+  a.rows = m; a.cols = n; a.k = k;
+  a.mu = mu; a.c = lr * scale;
+  ORTHO_TRY(launch_dion2_select(a, bf, 1, s));
+  // Newton-Schulz of the block in place: fp32-accurate products for fp32
+  // weights, bf16 products for bf16 weights
+  const ortho_mat blk{base + pl.off_blk, k, n, pl.ld_blk, ORTHO_F32};
+  const ortho_status st = run_ns(1, &blk, &blk, steps, abc, ws, stream, !bf);
+  if (st != ORTHO_OK) return st;
+  ORTHO_TRY(launch_dion2_update(a, bf, 1, s));
+  if (selected)
+    ORTHO_TRY(hipMemcpyAsync(selected, a.sel, static_cast<size_t>(k) * 4, hipMemcpyDeviceToDevice, s));
+  return ORTHO_OK;
+}
+
 }  // namespace
 
 namespace ortho {
@@ -695,6 +728,19 @@ ortho_status newton_schulz_batched(int32_t batch, const ortho_mat* G, const orth
   const ortho_status st = validate_ns(batch, G, Out, steps, abc, ws, ws_bytes);
   if (st != ORTHO_OK) return st;
   return run_ns(batch, G, Out, steps, abc, ws, stream, G[0].dtype == ORTHO_F32);
+}
+
+size_t ortho_dion2_workspace_size(int64_t m, int64_t n, int32_t k) {
+  Dion2Plan p;
+  return plan_dion2(m, n, k, &p) ? p.total_bytes : 0;
+}
+
+ortho_status dion2_step(ortho_mat X, ortho_mat G, ortho_mat M, int32_t k, int32_t steps,
+                        const float* abc, float mu, float lr, float scale, int32_t* selected,
+                        void* ws, size_t ws_bytes, void* stream) {
+  const ortho_status st = validate_dion2(X, G, M, k, steps, abc, mu, lr, scale, ws, ws_bytes);
+  if (st != ORTHO_OK) return st;
+  return run_dion2(X, G, M, k, steps, abc, mu, lr, scale, selected, ws, stream);
 }
 
 const char* ortho_status_str(int32_t status) {

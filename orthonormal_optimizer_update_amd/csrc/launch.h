@@ -193,6 +193,23 @@ struct SweepArgs {
 bool dion_sweep_ok(const SweepArgs& a, int members);
 hipError_t launch_dion_sweep(const SweepArgs& a, bool trans, int members, hipStream_t s);
 
+// Dion2 (kernels_dion2.hip): select the k rows of B = M + G with the largest
+// norm and gather them into blk (launch_dion2_select), then, after
+// Newton-Schulz of blk in place, apply it with error feedback
+// (launch_dion2_update).  rows <= 65535.
+struct Dion2Args {
+  MatArg x, g, m;          // caller's X, G (X's dtype) and fp32 M
+  MatArg blk;              // fp32 k x cols block, ld a multiple of 4
+  float* norms;            // member 0's row sums of squares (rows)
+  int* rank;               // member 0's row ranks (rows)
+  int* sel;                // member 0's selected rows, in rank order (k)
+  int64_t vec_stride;      // elements between members' norms, rank and sel
+  int rows, cols, k;
+  float mu, c;             // c = lr * scale
+};
+hipError_t launch_dion2_select(const Dion2Args& a, bool g_bf16, int members, hipStream_t s);
+hipError_t launch_dion2_update(const Dion2Args& a, bool x_bf16, int members, hipStream_t s);
+
 // Orthonormalisation apply: P1 = Pt * T with T upper triangular, given as T^T
 // (r x r fp32, row-major).
 struct ApplyArgs {

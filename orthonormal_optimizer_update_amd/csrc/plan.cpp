@@ -260,6 +260,43 @@ bool plan_muon(int64_t m, int64_t n, int32_t batch, MuonPlan* p, bool row_norm) 
   return true;
 }
 
+bool plan_dion2(int64_t m, int64_t n, int32_t k, Dion2Plan* p) {
+  if (m < 1 || n < 1 || k < 1 || k > m || m > 65535 || n > kMaxDim) return false;
+  Dion2Plan d{};
+  if (!plan_ns(k, n, 1, &d.ns)) return false;
+  d.ld_blk = cdiv(n, 4) * 4;
+  size_t o = align_up(d.ns.total_bytes);
+  d.off_blk = o;    o = align_up(o + static_cast<size_t>(k) * d.ld_blk * 4);
+  d.off_norms = o;  o = align_up(o + static_cast<size_t>(m) * 4);
+  d.off_rank = o;   o = align_up(o + static_cast<size_t>(m) * 4);
+  d.off_sel = o;    o = align_up(o + static_cast<size_t>(k) * 4);
+  d.total_bytes = o;
+  *p = d;
+  return true;
+}
+
+ortho_status validate_dion2(const ortho_mat& X, const ortho_mat& G, const ortho_mat& M, int32_t k,
+                            int32_t steps, const float* abc, float mu, float lr, float scale,
+                            const void* ws, size_t ws_bytes) {
+  if (steps < 0) return ORTHO_E_PARAM;
+  if (!(mu >= 0.f && mu <= 1.f) || !finite(lr) || !finite(scale)) return ORTHO_E_PARAM;
+  if (abc && (!finite(abc[0]) || !finite(abc[1]) || !finite(abc[2]))) return ORTHO_E_PARAM;
+  ortho_status st;
+  if ((st = check_mat(X)) != ORTHO_OK) return st;
+  if ((st = check_mat(G)) != ORTHO_OK) return st;
+  if ((st = check_mat(M)) != ORTHO_OK) return st;
+  if (G.dtype != X.dtype || M.dtype != ORTHO_F32) return ORTHO_E_DTYPE;
+  if (G.rows != X.rows || G.cols != X.cols || M.rows != X.rows || M.cols != X.cols)
+    return ORTHO_E_SHAPE;
+  if (X.rows > 65535) return ORTHO_E_SHAPE;
+  if (k < 1 || k > X.rows) return ORTHO_E_RANK;
+  Dion2Plan plan;
+  if (!plan_dion2(X.rows, X.cols, k, &plan)) return ORTHO_E_SHAPE;
+  if (ws == nullptr || ws_bytes < plan.total_bytes) return ORTHO_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kWsAlign != 0) return ORTHO_E_WORKSPACE;
+  return ORTHO_OK;
+}
+
 ortho_status validate_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, const ortho_mat* M,
                            const ortho_mat* Q, int32_t r, float mu, float lr, float scale,
                            const ortho_mat* P_out, const ortho_mat* R_out, const void* ws,

@@ -84,7 +84,21 @@ struct MuonPlan {
   size_t total_bytes;
 };
 
+// Dion2 step on one m x n matrix with k selected rows: the Newton-Schulz
+// workspace of the k x n block first, then the block (fp32, ld_blk) and the
+// row norms, ranks and selection.
+struct Dion2Plan {
+  NsPlan ns;
+  int64_t ld_blk;
+  size_t off_blk, off_norms, off_rank, off_sel;
+  size_t total_bytes;
+};
+
 bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* out);
+bool plan_dion2(int64_t m, int64_t n, int32_t k, Dion2Plan* out);
+ortho_status validate_dion2(const ortho_mat& X, const ortho_mat& G, const ortho_mat& M, int32_t k,
+                            int32_t steps, const float* abc, float mu, float lr, float scale,
+                            const void* ws, size_t ws_bytes);
 bool plan_muon(int64_t m, int64_t n, int32_t batch, MuonPlan* out, bool row_norm = false);
 bool plan_ns(int64_t m, int64_t n, int32_t batch, NsPlan* out);
 

@@ -17,7 +17,7 @@ FAKE = 0x7F0000000000   # never dereferenced: validation fails first
 def header_functions():
     text = open(os.path.join(ROOT, "include", "ortho.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b([a-z_]+)\s*\([^;{]*\)\s*;", text)))
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\([^;{]*\)\s*;", text)))
 
 
 def test_header_declares_expected_entry_points():
@@ -26,6 +26,7 @@ def test_header_declares_expected_entry_points():
               "newton_schulz_batched", "ortho_dion_workspace_size", "ortho_ns_workspace_size",
               "muon_step", "muon_step_batched", "ortho_muon_workspace_size",
               "normuon_step", "normuon_step_batched", "ortho_normuon_workspace_size",
+              "dion2_step", "ortho_dion2_workspace_size",
               "ortho_status_str", "ortho_abi_version"]:
         assert n in names
 
@@ -150,6 +151,28 @@ def test_dion_noalloc_argument_errors():
     assert api.dion_workspace_size(4096, 4096, 1024) > api.NOALLOC_SCRATCH_BYTES
     assert L.dion_step_noalloc(*big, 1024, 0.9, 0.1, None) == api.ORTHO_E_SCRATCH
     assert "scratch" in api.status_str(api.ORTHO_E_SCRATCH)
+
+
+def test_dion2_argument_errors():
+    L = api.lib()
+    wsb = api.dion2_workspace_size(64, 48, 16)
+    assert wsb > api.ns_workspace_size(16, 48)
+    assert api.dion2_workspace_size(64, 48, 65) == 0
+    ws = ctypes.c_void_p(FAKE)
+    X, G, Mo = M(64, 48, BF), M(64, 48, BF), M(64, 48, F)
+    call = lambda *a: L.dion2_step(*a, None, ws, wsb, None)
+    assert call(X, G, Mo, 0, 5, None, 0.9, 0.1, 1.0) == 4
+    assert call(X, G, Mo, 65, 5, None, 0.9, 0.1, 1.0) == 4
+    assert call(X, G, Mo, 16, -1, None, 0.9, 0.1, 1.0) == 7
+    assert call(X, G, Mo, 16, 5, None, 1.5, 0.1, 1.0) == 7
+    assert call(X, M(64, 48, F), Mo, 16, 5, None, 0.9, 0.1, 1.0) == 3
+    assert call(X, G, M(64, 48, BF), 16, 5, None, 0.9, 0.1, 1.0) == 3
+    assert call(X, G, M(64, 40, F), 16, 5, None, 0.9, 0.1, 1.0) == 2
+    assert call(M(64, 48, BF, data=None), G, Mo, 16, 5, None, 0.9, 0.1, 1.0) == 1
+    assert L.dion2_step(X, G, Mo, 16, 5, None, 0.9, 0.1, 1.0, None, ws, wsb - 1, None) == 6
+    big = M(70000, 8, BF)
+    assert L.dion2_step(big, big, M(70000, 8, F), 4, 5, None, 0.9, 0.1, 1.0, None, ws, 1 << 40,
+                        None) == 2
 
 
 def test_ns_argument_errors():
