@@ -16,7 +16,7 @@ Prints ONE JSON line.  Besides the headline step it carries a per-size table
 (time per call, modeled GB/s and TFLOP/s and their fraction of peak) for square
 matrices from 1024 to 8192 at rank fractions 1/4 and 1/16 and for the
 Llama-405B weight shapes, with the whole Muon step (momentum, NS x5, update)
-beside NS, and the time per step of the other named workloads (256 x 256 fp32,
+and the Dion2 step (rows of largest norm, fractions 1/4 and 1/16) beside NS, and the time per step of the other named workloads (256 x 256 fp32,
 the 12-layer GPT parameter groups, per-head NS), measured after the timed region.  The oracle is timed on the host cores on a bounded
 sample (one step of the same workload) as the reported CPU baseline.
 """
@@ -203,6 +203,19 @@ def size_table(torch, api, warmup=1):
             row["normuon5"] = {"ms": ms, "steps_per_s": 1000.0 / ms, "TFLOP/s": tfs,
                                "mfma_frac": tfs / PEAK_BF16_TFLOPS}
             del M, ws
+        if m <= 65535:
+            # Dion2: the rows of largest norm (fractions 1/4 and 1/16 of the
+            # rows), Newton-Schulz x5 of that block, error feedback
+            for frac in (4, 16):
+                k = m // frac
+                M = torch.zeros(m, n, device=dev)
+                ws = api.workspace(api.dion2_workspace_size(m, n, k), dev)
+                ms = timed(lambda: api.dion2_step(X, G, M, k, 0.95, 0.01, ws=ws))
+                _, fl = ns_model(k, n)
+                tfs = fl / (ms * 1e-3) / 1e12
+                row[f"dion2_k{k}"] = {"ms": ms, "steps_per_s": 1000.0 / ms, "row_frac": f"1/{frac}",
+                                      "TFLOP/s": tfs, "mfma_frac": tfs / PEAK_BF16_TFLOPS}
+                del M, ws
         out[name] = row
         del X, G
         torch.cuda.empty_cache()
