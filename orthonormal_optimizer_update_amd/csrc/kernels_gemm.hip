@@ -4,6 +4,7 @@
 #include "gemm_core.h"
 #include "gemm_fast.h"
 #include "launch.h"
+#include "plan.h"
 
 namespace ortho {
 
@@ -240,6 +241,13 @@ hipError_t launch_dion_right(const DionRightArgs& a, bool bf16, int members, hip
               : dion_right_t<float, CfgSplit6, 3>(a, members, s);
 }
 
+// The orthonormalisation products of a small rank (r < 512) have few 128 x 128
+// tiles (m = 4096, r = 256: 64 output tiles, 4 for P1^T P1); 64 x 64 tiles,
+// four waves of 32 x 32, give the chip four times the workgroups.
+using CfgSplit6S = GemmCfg<64, 64, 32, 2, 2, 3, 3, 6, 1>;
+using CfgSplitS = GemmCfg<64, 64, 32, 2, 2, 2, 2, 3, 1>;
+using CfgSplitS64 = GemmCfg<64, 64, 64, 2, 2, 2, 2, 3, 1>;   // k 64 deep: the column loader's minimum
+
 hipError_t launch_apply_t(const ApplyArgs& a, bool six_products, int members, hipStream_t s) {
   GemmParams<EpiStoreF32::Args> p{};
   p.a = with_rows(a.pt, a.M);
@@ -251,6 +259,11 @@ hipError_t launch_apply_t(const ApplyArgs& a, bool six_products, int members, hi
   p.e.has_b = a.has_bf16;
   p.M = a.M; p.N = a.r; p.K = a.r;
   p.splits = 1; p.kchunk = 0; p.tri = 1;
+  if (static_cast<int64_t>(cdiv(a.M, 128)) * cdiv(a.r, 128) * members < 256) {
+    if (six_products)
+      return run<CfgSplit6S, RowF32<64, 256, 3>, RowF32<64, 256, 3>, EpiStoreF32>(p, members, s);
+    return run<CfgSplitS, RowF32<64, 256, 2>, RowF32<64, 256, 2>, EpiStoreF32>(p, members, s);
+  }
   if (six_products)
     return run<CfgSplit6, RowF32<128, 256, 3>, RowF32<128, 256, 3>, EpiStoreF32>(p, members, s);
   return run<CfgSplit, RowF32<128, 256, 2>, RowF32<128, 256, 2>, EpiStoreF32>(p, members, s);
@@ -265,6 +278,9 @@ hipError_t launch_gram_tn(const GramTnArgs& a, int members, hipStream_t s) {
   p.e.has_t = 0;
   p.M = a.r; p.N = a.r; p.K = a.m;
   p.splits = a.splits; p.kchunk = a.kchunk; p.tri = 0;
+  if (gram_tn_small_tiles(a.r) && a.kchunk % 64 == 0)
+    return run<CfgSplitS64, LdCol<64, 64, 256, 2, float, false, float>,
+               LdCol<64, 64, 256, 2, float, false, float>, EpiStoreF32>(p, members, s);
   return run<CfgSplit, ColF32<128, 256, 2>, ColF32<128, 256, 2>, EpiStoreF32>(p, members, s);
 }
 

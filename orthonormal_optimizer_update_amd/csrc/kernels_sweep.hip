@@ -83,8 +83,22 @@ __global__ __launch_bounds__(512, 1) void dion_sweep_kernel(SweepArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[kStages * L::kStageBytes];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int bi = blockIdx.z, split = blockIdx.y;
-  const int row0 = blockIdx.x * kRows;          // first output row of the workgroup
+  const int bi = blockIdx.z;
+  // Workgroups are dealt to the 8 XCDs round robin in launch order.  When the
+  // (row tile, split) grid divides evenly, XCD x takes the x-th eighth of the
+  // grid in split-major order, so each XCD's L2 fetches only the factor rows
+  // of its own k slices instead of all of them.
+  int tile = blockIdx.x, split = blockIdx.y;
+  {
+    const int tiles = gridDim.x, total = tiles * gridDim.y;
+    if (total % 8 == 0) {
+      const int b = blockIdx.x + tiles * blockIdx.y;
+      const int l = (b % 8) * (total / 8) + b / 8;
+      split = l / tiles;
+      tile = l - split * tiles;
+    }
+  }
+  const int row0 = tile * kRows;                // first output row of the workgroup
   const int kbeg = split * a.kchunk;
   const int kend = min(a.K, kbeg + a.kchunk);
   const int nst = (kend - kbeg) / kBK;          // >= 1 (checked by the launcher)

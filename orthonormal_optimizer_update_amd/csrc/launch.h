@@ -229,6 +229,8 @@ struct GramTnArgs {
   int64_t split_stride;
   int m, r, splits, kchunk;
 };
+// 64 x 64 tiles (k in steps of 64) where gram_tn_small_tiles(r) and kchunk is
+// a multiple of 64, else 128 x 128.
 hipError_t launch_gram_tn(const GramTnArgs& a, int members, hipStream_t s);
 
 // T2^T = I - Phi(E) with E = W2 - I (W2 summed from `splits` r x r slices) and

@@ -81,7 +81,13 @@ bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* p) {
     d.kchunk_gram = static_cast<int>(kc);
     d.split_gram = static_cast<int>(cdiv(m, kc));
   }
-  choose_split(m, cdiv(r, 128) * cdiv(r, 128), d.chunk, &d.split_gram2, &d.kchunk_gram2);
+  if (gram_tn_small_tiles(r)) {
+    choose_split(m, cdiv(r, 64) * cdiv(r, 64), d.chunk, &d.split_gram2, &d.kchunk_gram2);
+    d.kchunk_gram2 = static_cast<int>(cdiv(d.kchunk_gram2, 64) * 64);
+    d.split_gram2 = static_cast<int>(cdiv(m, d.kchunk_gram2));
+  } else {
+    choose_split(m, cdiv(r, 128) * cdiv(r, 128), d.chunk, &d.split_gram2, &d.kchunk_gram2);
+  }
   d.nrb = static_cast<int>(cdiv(n, 64));
   d.rp = cdiv(r, 4) * 4;
   const size_t mr = static_cast<size_t>(m) * r, nr = static_cast<size_t>(n) * r;

@@ -12,6 +12,10 @@ namespace ortho {
 constexpr int kMaxMembersPerLaunch = 32;  // must match kMaxBatch in common.h
 constexpr size_t kWsAlign = 256;
 
+// P1^T P1 of the correction pass runs on 64 x 64 tiles below this rank (a
+// 256 x 256 result is only 4 tiles of 128); the plan sizes its split for them.
+inline bool gram_tn_small_tiles(int r) { return r < 512; }
+
 // Byte offsets of one member's regions inside the Dion workspace, and the
 // split-K factors chosen for the three reductions over a long dimension.
 struct DionPlan {
