@@ -973,7 +973,7 @@ __device__ __forceinline__ double rsqrt_f64(double x) {
   return y * (1.5 - 0.5 * x * y * y);
 }
 
-// One 16 x 16 tile of a phase's rank-8 update in chol_diag_block: y = 0 for
+// One 16 x 16 tile of a phase's rank-8 update in chol_diag_factor: y = 0 for
 // the factor L, 1 for the inverse Y; tile row and column.
 struct CholTile {
   int y, tr, tc;
@@ -1046,26 +1046,60 @@ __device__ __forceinline__ void chol_tile_apply(double* ly, int lane, int lane_t
   }
 }
 
-// Tiles W, W + 4, W + 8 of phase P (wave W): all loads, then the products.
-template <int P, int W>
-__device__ __forceinline__ void chol_tiles(double* ly, int lane) {
-  constexpr int nt = chol_ntile(P);
-  const int lane_a = (lane & 15) * kCP + (lane >> 4), lane_t = (lane >> 4) * kCP + (lane & 15);
+// Tiles of phase P by wave, for the factorisation that runs panel P + 1 in
+// wave 0 right after its own tiles: wave 0 the L-tiles of tile column
+// tc0 = (8P + 8) / 16 (which hold panel P + 1), wave 1 every Y-tile, waves 2
+// and 3 the remaining L-tiles alternately.  chol_pick gives the index (as in
+// chol_tile) of the n-th tile of wave W, or -1.
+__host__ __device__ constexpr int chol_pick(int p, int w, int n) {
+  const int tc0 = (8 * p + 8) >> 4;
+  int seen = 0, rest = 0;
+  for (int s = 0; s < chol_ntile(p); ++s) {
+    const CholTile t = chol_tile(p, s);
+    int owner = 0;
+    if (t.y != 0) {
+      owner = 1;
+    } else if (t.tc == tc0) {
+      owner = 0;
+    } else {
+      owner = 2 + (rest & 1);
+      ++rest;
+    }
+    if (owner == w) {
+      if (seen == n) return s;
+      ++seen;
+    }
+  }
+  return -1;
+}
+
+template <int P, int W, int N>
+__device__ __forceinline__ void chol_tiles2_n(double* ly, int lane, int lane_a, int lane_t) {
+  constexpr int s0 = chol_pick(P, W, N), s1 = chol_pick(P, W, N + 1), s2 = chol_pick(P, W, N + 2);
   double av[3][2], bv[3][2], old[3][4];
-  if constexpr (W < nt) chol_tile_load<P, W>(ly, lane_a, lane_t, av[0], bv[0], old[0]);
-  if constexpr (W + 4 < nt) chol_tile_load<P, W + 4>(ly, lane_a, lane_t, av[1], bv[1], old[1]);
-  if constexpr (W + 8 < nt) chol_tile_load<P, W + 8>(ly, lane_a, lane_t, av[2], bv[2], old[2]);
-  if constexpr (W < nt) chol_tile_apply<P, W>(ly, lane, lane_t, av[0], bv[0], old[0]);
-  if constexpr (W + 4 < nt) chol_tile_apply<P, W + 4>(ly, lane, lane_t, av[1], bv[1], old[1]);
-  if constexpr (W + 8 < nt) chol_tile_apply<P, W + 8>(ly, lane, lane_t, av[2], bv[2], old[2]);
+  if constexpr (s0 >= 0) chol_tile_load<P, (s0 >= 0 ? s0 : 0)>(ly, lane_a, lane_t, av[0], bv[0], old[0]);
+  if constexpr (s1 >= 0) chol_tile_load<P, (s1 >= 0 ? s1 : 0)>(ly, lane_a, lane_t, av[1], bv[1], old[1]);
+  if constexpr (s2 >= 0) chol_tile_load<P, (s2 >= 0 ? s2 : 0)>(ly, lane_a, lane_t, av[2], bv[2], old[2]);
+  if constexpr (s0 >= 0) chol_tile_apply<P, (s0 >= 0 ? s0 : 0)>(ly, lane, lane_t, av[0], bv[0], old[0]);
+  if constexpr (s1 >= 0) chol_tile_apply<P, (s1 >= 0 ? s1 : 0)>(ly, lane, lane_t, av[1], bv[1], old[1]);
+  if constexpr (s2 >= 0) chol_tile_apply<P, (s2 >= 0 ? s2 : 0)>(ly, lane, lane_t, av[2], bv[2], old[2]);
+}
+
+// Wave W's tiles of phase P, three loads in flight at a time (at most six
+// tiles per wave).
+template <int P, int W>
+__device__ __forceinline__ void chol_tiles2(double* ly, int lane) {
+  const int lane_a = (lane & 15) * kCP + (lane >> 4), lane_t = (lane >> 4) * kCP + (lane & 15);
+  static_assert(chol_pick(P, W, 6) < 0, "more than six tiles for one wave");
+  chol_tiles2_n<P, W, 0>(ly, lane, lane_a, lane_t);
+  if constexpr (chol_pick(P, W, 3) >= 0) chol_tiles2_n<P, W, 3>(ly, lane, lane_a, lane_t);
 }
 
 template <int P>
-__device__ __forceinline__ void chol_tiles_wave(double* ly, int lane, int wave) {
-  if (wave == 0) chol_tiles<P, 0>(ly, lane);
-  else if (wave == 1) chol_tiles<P, 1>(ly, lane);
-  else if (wave == 2) chol_tiles<P, 2>(ly, lane);
-  else chol_tiles<P, 3>(ly, lane);
+__device__ __forceinline__ void chol_tiles2_wave(double* ly, int lane, int wave) {
+  if (wave == 1) chol_tiles2<P, 1>(ly, lane);
+  else if (wave == 2) chol_tiles2<P, 2>(ly, lane);
+  else chol_tiles2<P, 3>(ly, lane);
 }
 
 // Factor the nb x nb diagonal block kb of S (S_kk = L_kk L_kk^T) and invert
@@ -1080,10 +1114,11 @@ __device__ __forceinline__ void chol_tiles_wave(double* ly, int lane, int wave) 
 //   (chol_tile_load): of L by panel p beyond it, and of Y by X_{p-1} below
 //   it, Y starting as the identity.  The tile work of each (phase, wave) is
 //   compiled with constant offsets.
-__device__ void chol_diag_block(const CholArgs& a, int kb, int member, double (*LY)[64][kCP],
-                                double* dinv) {
-  double* S = a.s + member * a.mat_stride;
-  double* X = a.x + member * a.mat_stride;
+// chol_diag_load fills L (lower triangle of S_kk, identity padding) and Y = I
+// from global memory; chol_diag_factor then works from LDS alone, so a caller
+// that already holds the block can fill L itself.
+__device__ void chol_diag_load(const CholArgs& a, int kb, int member, double (*LY)[64][kCP]) {
+  const double* S = a.s + member * a.mat_stride;
   const int r = a.r;
   const int o = kb * 64;
   const int nb = min(64, r - o);
@@ -1091,7 +1126,6 @@ __device__ void chol_diag_block(const CholArgs& a, int kb, int member, double (*
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   double (*L)[kCP] = LY[0];
   double (*Y)[kCP] = LY[1];
-  double* ly = &LY[0][0][0];
   // element (gi, gj) = (q * 4 + wave, lane): each wave moves whole 64-wide
   // rows.  Every load is issued before any is used (clamped addresses; the
   // triangle is cut with a select, so stale words in the upper triangle, NaN
@@ -1109,6 +1143,20 @@ __device__ void chol_diag_block(const CholArgs& a, int kb, int member, double (*
     L[gi][gj] = (gi < nb && gj <= gi) ? __longlong_as_double(static_cast<long long>(v[q])) : id;
     Y[gi][gj] = id;
   }
+}
+
+__device__ void chol_diag_factor(const CholArgs& a, int kb, int member, double (*LY)[64][kCP],
+                                 double* dinv) {
+  double* S = a.s + member * a.mat_stride;
+  double* X = a.x + member * a.mat_stride;
+  const int r = a.r;
+  const int o = kb * 64;
+  const int nb = min(64, r - o);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  double (*L)[kCP] = LY[0];
+  double (*Y)[kCP] = LY[1];
+  double* ly = &LY[0][0][0];
   bool shifted = false;
   // block row q of the inverse, by wave 1 (lane c: column c)
   auto solve_rows = [&](int q) {
@@ -1131,47 +1179,67 @@ __device__ void chol_diag_block(const CholArgs& a, int kb, int member, double (*
 #pragma unroll
     for (int t = 0; t < 8; ++t) Y[jq + t][lane] = y[t];
   };
-  for (int p = 0; p < 8; ++p) {
+  // panel p of L, factored in registers by wave 0 (lane i: row i)
+  auto panel = [&](int p) {
     const int j0 = p * 8;
+    double pc[8], invd[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) pc[c] = L[lane][j0 + c];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int jc = j0 + c;
+      const double a0 = readlane_f64(pc[c], jc);
+      shifted |= !(a0 > kPivMin);
+      // maxNum: a NaN pivot is replaced too (and flagged)
+      const double piv = fmax(a0, kPivMin);
+      const double rs = rsqrt_f64(piv);
+      invd[c] = rs;
+      // scaled column; rows above jc hold entries above the diagonal: zeroed
+      const double x = lane == jc ? piv : pc[c];
+      pc[c] = lane >= jc ? x * rs : 0.0;
+#pragma unroll
+      for (int c2 = c + 1; c2 < 8; ++c2) pc[c2] = fma(-pc[c], readlane_f64(pc[c], j0 + c2), pc[c2]);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) L[lane][j0 + c] = pc[c];
+    if (lane == 0) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) dinv[j0 + c] = invd[c];
+    }
+  };
+  // Phase p: wave 0 applies panel p's update to the tile column holding
+  // panel p + 1 (chol_tile_load's L-tiles with tc == tc0) and goes straight on
+  // to factor panel p + 1, which needs nothing else; wave 1 solves block row
+  // p - 1 of the inverse and applies every Y-tile of the phase with it; waves
+  // 2 and 3 take the other L-tiles.  One barrier per phase.
+  __syncthreads();
+  if (wave == 0) panel(0);
+  for (int p = 0; p < 8; ++p) {
     __syncthreads();
     if (wave == 0) {
-      double pc[8], invd[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) pc[c] = L[lane][j0 + c];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int jc = j0 + c;
-        const double a0 = readlane_f64(pc[c], jc);
-        shifted |= !(a0 > kPivMin);
-        // maxNum: a NaN pivot is replaced too (and flagged)
-        const double piv = fmax(a0, kPivMin);
-        const double rs = rsqrt_f64(piv);
-        invd[c] = rs;
-        // scaled column; rows above jc hold entries above the diagonal: zeroed
-        const double x = lane == jc ? piv : pc[c];
-        pc[c] = lane >= jc ? x * rs : 0.0;
-#pragma unroll
-        for (int c2 = c + 1; c2 < 8; ++c2) pc[c2] = fma(-pc[c], readlane_f64(pc[c], j0 + c2), pc[c2]);
+      switch (p) {
+        case 0: chol_tiles2<0, 0>(ly, lane); break;
+        case 1: chol_tiles2<1, 0>(ly, lane); break;
+        case 2: chol_tiles2<2, 0>(ly, lane); break;
+        case 3: chol_tiles2<3, 0>(ly, lane); break;
+        case 4: chol_tiles2<4, 0>(ly, lane); break;
+        case 5: chol_tiles2<5, 0>(ly, lane); break;
+        case 6: chol_tiles2<6, 0>(ly, lane); break;
+        default: break;
       }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) L[lane][j0 + c] = pc[c];
-      if (lane == 0) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) dinv[j0 + c] = invd[c];
+      if (p < 7) panel(p + 1);
+    } else {
+      if (wave == 1 && p > 0) solve_rows(p - 1);
+      switch (p) {
+        case 0: chol_tiles2_wave<0>(ly, lane, wave); break;
+        case 1: chol_tiles2_wave<1>(ly, lane, wave); break;
+        case 2: chol_tiles2_wave<2>(ly, lane, wave); break;
+        case 3: chol_tiles2_wave<3>(ly, lane, wave); break;
+        case 4: chol_tiles2_wave<4>(ly, lane, wave); break;
+        case 5: chol_tiles2_wave<5>(ly, lane, wave); break;
+        case 6: chol_tiles2_wave<6>(ly, lane, wave); break;
+        default: chol_tiles2_wave<7>(ly, lane, wave); break;
       }
-    } else if (wave == 1 && p > 0) {
-      solve_rows(p - 1);
-    }
-    __syncthreads();
-    switch (p) {
-      case 0: chol_tiles_wave<0>(ly, lane, wave); break;
-      case 1: chol_tiles_wave<1>(ly, lane, wave); break;
-      case 2: chol_tiles_wave<2>(ly, lane, wave); break;
-      case 3: chol_tiles_wave<3>(ly, lane, wave); break;
-      case 4: chol_tiles_wave<4>(ly, lane, wave); break;
-      case 5: chol_tiles_wave<5>(ly, lane, wave); break;
-      case 6: chol_tiles_wave<6>(ly, lane, wave); break;
-      default: chol_tiles_wave<7>(ly, lane, wave); break;
     }
   }
   __syncthreads();
@@ -1191,7 +1259,8 @@ __device__ void chol_diag_block(const CholArgs& a, int kb, int member, double (*
 __global__ __launch_bounds__(256) void chol_diag_kernel(CholArgs a, int kb) {
   __shared__ double LY[2][64][kCP];
   __shared__ double dinv[64];
-  chol_diag_block(a, kb, blockIdx.x, LY, dinv);
+  chol_diag_load(a, kb, blockIdx.x, LY);
+  chol_diag_factor(a, kb, blockIdx.x, LY, dinv);
 }
 
 // 64 x 64 fp64 tiles of row-major r x r matrices through LDS (pitch kCP),
@@ -1277,6 +1346,82 @@ __device__ __forceinline__ void tile_sub64(double* out, int r, int orow, int oco
       }
 }
 
+// L_ik = S_ik X_kk^T with X_kk lower triangular: output tile column tj (16
+// wide) only needs k < 16 (tj + 1).  Wave w takes tile rows 2 (w & 1) and
+// 2 (w & 1) + 1 and tile columns {0, 3} (w < 2) or {1, 2} (w >= 2), 40 k steps
+// each instead of 64 for the plain 32 x 32 quadrants.
+__device__ __forceinline__ int lt_col_tile(int wave, int j) {
+  return (wave >> 1) == 0 ? (j == 0 ? 0 : 3) : (j == 0 ? 1 : 2);
+}
+template <int TJ0, int TJ1>
+__device__ __forceinline__ void tile_mma64_lt_w(const double (*sA)[kCP], const double (*sB)[kCP],
+                                                doublex4 acc[2][2], int lane, int wa) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = doublex4{0.0, 0.0, 0.0, 0.0};
+  // k steps of 4 over the longer range; tile column TJ0 stops at 16 (TJ0 + 1)
+#pragma unroll
+  for (int kk = 0; kk < 16 * TJ1 + 16; kk += 4) {
+    const double a0 = sA[wa * 32 + (lane & 15)][kk + (lane >> 4)];
+    const double a1 = sA[wa * 32 + 16 + (lane & 15)][kk + (lane >> 4)];
+    const double b1 = sB[TJ1 * 16 + (lane & 15)][kk + (lane >> 4)];
+    if (kk < 16 * TJ0 + 16) {
+      const double b0 = sB[TJ0 * 16 + (lane & 15)][kk + (lane >> 4)];
+      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
+    }
+    acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
+    acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
+  }
+}
+__device__ __forceinline__ void tile_mma64_lt(const double (*sA)[kCP], const double (*sB)[kCP],
+                                              doublex4 acc[2][2]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  if ((wave >> 1) == 0) tile_mma64_lt_w<0, 3>(sA, sB, acc, lane, wave & 1);
+  else tile_mma64_lt_w<1, 2>(sA, sB, acc, lane, wave & 1);
+}
+__device__ __forceinline__ void tile_put_acc_lt(const doublex4 acc[2][2], double (*sT)[kCP]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int wa = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        sT[wa * 32 + i * 16 + (lane >> 4) + 4 * e][lt_col_tile(wave, j) * 16 + (lane & 15)] = acc[i][j][e];
+}
+
+// The lower 16 x 16 tiles (ti >= tj) of A A^T, K = 64, spread 3, 3, 2, 2 over
+// the waves; tile n of wave w is (lower_tile_row, lower_tile_col).
+__device__ __forceinline__ int lower_ntiles(int wave) { return wave < 2 ? 3 : 2; }
+__device__ __forceinline__ int lower_tile(int wave, int n) {   // ti * 4 + tj
+  constexpr int list[4][3] = {{0, 12, 15}, {4, 5, 13}, {8, 9, 9}, {10, 14, 14}};
+  return list[wave][n];
+}
+__device__ __forceinline__ void tile_mma64_lower(const double (*sA)[kCP], doublex4 acc[3]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int nt = lower_ntiles(wave);
+#pragma unroll
+  for (int n = 0; n < 3; ++n) acc[n] = doublex4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+  for (int kk = 0; kk < 64; kk += 4) {
+#pragma unroll
+    for (int n = 0; n < 3; ++n) {
+      if (n < nt) {
+        const int t = lower_tile(wave, n), ti = t >> 2, tj = t & 3;
+        const double av = sA[ti * 16 + (lane & 15)][kk + (lane >> 4)];
+        const double bv = sA[tj * 16 + (lane & 15)][kk + (lane >> 4)];
+        acc[n] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[n], 0, 0, 0);
+      }
+    }
+  }
+}
+
 // Trailing update after block column kb.  The panel is formed in LDS by the
 // workgroups that use it: L_ik = S_ik Linv_kk^T for i > kb, and X_kj =
 // Linv_kk Y_kj for j < kb (X_kk = Linv_kk); block row kb of X keeps Y_kj
@@ -1311,20 +1456,49 @@ __global__ __launch_bounds__(256) void chol_update_kernel(CholArgs a, int kb) {
     tile_put_regs(v0, sT[0]);
     tile_put_regs(v1, sT[1]);
     if (two) tile_put_regs(v2, sT[2]);
+    // workgroup 0: the diagonal tile it factors, in flight during L_ik
+    if (t == 0) tile_fetch64(S, r, ib * 64, ib * 64, v2);
     __syncthreads();
-    tile_mma64<true>(sT[0], sT[1], acc);              // L_ik
-    if (two) tile_mma64<true>(sT[2], sT[1], acc2);    // L_jk
+    tile_mma64_lt(sT[0], sT[1], acc);              // L_ik
+    if (two) tile_mma64_lt(sT[2], sT[1], acc2);    // L_jk
     __syncthreads();
-    tile_put_acc(acc, sT[0]);
-    if (two) tile_put_acc(acc2, sT[2]);
-    __syncthreads();
-    tile_mma64<true>(sT[0], two ? sT[2] : sT[0], acc);
-    tile_sub64(S, r, ib * 64, jb * 64, acc, !two);
-    if (t == 0) {
-      // Orders this workgroup's stores before the diagonal block's reloads
-      // and releases the LDS tiles.
+    tile_put_acc_lt(acc, sT[0]);
+    if (t != 0) {
+      if (two) tile_put_acc_lt(acc2, sT[2]);
       __syncthreads();
-      chol_diag_block(a, kb + 1, member, sT, dinv);
+      tile_mma64<true>(sT[0], two ? sT[2] : sT[0], acc);
+      tile_sub64(S, r, ib * 64, jb * 64, acc, !two);
+    } else {
+      // Diagonal tile (kb + 1, kb + 1), which this workgroup then factors:
+      // L = S_ii - L_ik L_ik^T is formed in LDS (sT[1], Y = I in sT[2]) and
+      // never goes through global memory.  Lower triangle, identity padding.
+      const int nb = min(64, r - ib * 64);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int e = threadIdx.x + q * 256;
+        const int gi = e >> 6, gj = e & 63;
+        const double id = gi == gj ? 1.0 : 0.0;
+        sT[1][gi][gj] = (gi < nb && gj <= gi) ? v2[q] : id;
+        sT[2][gi][gj] = id;
+      }
+      __syncthreads();
+      doublex4 accd[3];
+      tile_mma64_lower(sT[0], accd);
+      const int lane = threadIdx.x & 63;
+      const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+      const int nt = lower_ntiles(wave);
+#pragma unroll
+      for (int n = 0; n < 3; ++n) {
+        if (n < nt) {
+          const int tt = lower_tile(wave, n), ti2 = tt >> 2, tj2 = tt & 3;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int row = ti2 * 16 + (lane >> 4) + 4 * e, col = tj2 * 16 + (lane & 15);
+            if (row < nb && col <= row) sT[1][row][col] -= accd[n][e];
+          }
+        }
+      }
+      chol_diag_factor(a, kb + 1, member, sT + 1, dinv);
     }
   } else {
     t -= ntri;
@@ -1337,10 +1511,10 @@ __global__ __launch_bounds__(256) void chol_update_kernel(CholArgs a, int kb) {
     tile_put_regs(v1, sT[1]);
     if (below) tile_put_regs(v2, sT[2]);
     __syncthreads();
-    tile_mma64<true>(sT[0], sT[1], acc);                 // L_ik
+    tile_mma64_lt(sT[0], sT[1], acc);                    // L_ik
     if (below) tile_mma64<false>(sT[1], sT[2], acc2);    // X_kj
     __syncthreads();
-    tile_put_acc(acc, sT[0]);
+    tile_put_acc_lt(acc, sT[0]);
     if (below) tile_put_acc(acc2, sT[2]);
     __syncthreads();
     tile_mma64<false>(sT[0], below ? sT[2] : sT[1], acc);
