@@ -1026,8 +1026,10 @@ __device__ __forceinline__ void chol_tile_load(const double* ly, int lane_a, int
 }
 
 // Product and masked write-back of tile S of phase P: an element changes
-// where the update applies (L: row >= pe, pe <= col <= row; Y: row >= 8P,
-// col < 8P), so no element outside the update is written.
+// where the update applies (L: row >= pe, pe + 8 <= col <= row -- the columns
+// pe .. pe + 7 of panel P + 1 are updated in registers by the wave that
+// factors it; Y: row >= 8P, col < 8P), so no element outside the update is
+// written.
 template <int P, int S>
 __device__ __forceinline__ void chol_tile_apply(double* ly, int lane, int lane_t, const double* av,
                                                 const double* bv, const double* old) {
@@ -1041,26 +1043,22 @@ __device__ __forceinline__ void chol_tile_apply(double* ly, int lane, int lane_t
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int row = t.tr * 16 + (lane >> 4) + 4 * e;
-    const bool ok = t.y != 0 ? (row >= j0 && col < j0) : (row >= pe && col >= pe && col <= row);
+    const bool ok = t.y != 0 ? (row >= j0 && col < j0) : (row >= pe && col >= pe + 8 && col <= row);
     if (ok) ly[lane_t + offt + e * 4 * kCP] = old[e] - acc[e];
   }
 }
 
-// Tiles of phase P by wave, for the factorisation that runs panel P + 1 in
-// wave 0 right after its own tiles: wave 0 the L-tiles of tile column
-// tc0 = (8P + 8) / 16 (which hold panel P + 1), wave 1 every Y-tile, waves 2
-// and 3 the remaining L-tiles alternately.  chol_pick gives the index (as in
-// chol_tile) of the n-th tile of wave W, or -1.
+// Tiles of phase P by wave, for the factorisation in which wave 0 updates and
+// factors panel P + 1 in registers during phase P: wave 1 every Y-tile, waves
+// 2 and 3 the L-tiles alternately (none for wave 0).  chol_pick gives the
+// index (as in chol_tile) of the n-th tile of wave W, or -1.
 __host__ __device__ constexpr int chol_pick(int p, int w, int n) {
-  const int tc0 = (8 * p + 8) >> 4;
   int seen = 0, rest = 0;
   for (int s = 0; s < chol_ntile(p); ++s) {
     const CholTile t = chol_tile(p, s);
     int owner = 0;
     if (t.y != 0) {
       owner = 1;
-    } else if (t.tc == tc0) {
-      owner = 0;
     } else {
       owner = 2 + (rest & 1);
       ++rest;
@@ -1179,12 +1177,11 @@ __device__ void chol_diag_factor(const CholArgs& a, int kb, int member, double (
 #pragma unroll
     for (int t = 0; t < 8; ++t) Y[jq + t][lane] = y[t];
   };
-  // panel p of L, factored in registers by wave 0 (lane i: row i)
-  auto panel = [&](int p) {
+  // panel p of L (pc: its 8 columns, lane i holding row i, with every
+  // earlier panel's update applied), factored in registers by wave 0
+  auto panel = [&](int p, double (&pc)[8]) {
     const int j0 = p * 8;
-    double pc[8], invd[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) pc[c] = L[lane][j0 + c];
+    double invd[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int jc = j0 + c;
@@ -1207,27 +1204,40 @@ __device__ void chol_diag_factor(const CholArgs& a, int kb, int member, double (
       for (int c = 0; c < 8; ++c) dinv[j0 + c] = invd[c];
     }
   };
-  // Phase p: wave 0 applies panel p's update to the tile column holding
-  // panel p + 1 (chol_tile_load's L-tiles with tc == tc0) and goes straight on
-  // to factor panel p + 1, which needs nothing else; wave 1 solves block row
-  // p - 1 of the inverse and applies every Y-tile of the phase with it; waves
-  // 2 and 3 take the other L-tiles.  One barrier per phase.
+  // Phase p: wave 0 applies panel p's rank-8 update to the 8 columns of
+  // panel p + 1 in registers (rows by lane, the 8 x 8 block of panel p on
+  // those rows read as broadcasts) and factors panel p + 1 at once, which
+  // needs nothing else; wave 1 solves block row p - 1 of the inverse and
+  // applies every Y-tile of the phase with it; waves 2 and 3 apply the
+  // L-tiles (outside panel p + 1).  One barrier per phase.
   __syncthreads();
-  if (wave == 0) panel(0);
+  if (wave == 0) {
+    double pc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) pc[c] = L[lane][c];
+    panel(0, pc);
+  }
   for (int p = 0; p < 8; ++p) {
     __syncthreads();
     if (wave == 0) {
-      switch (p) {
-        case 0: chol_tiles2<0, 0>(ly, lane); break;
-        case 1: chol_tiles2<1, 0>(ly, lane); break;
-        case 2: chol_tiles2<2, 0>(ly, lane); break;
-        case 3: chol_tiles2<3, 0>(ly, lane); break;
-        case 4: chol_tiles2<4, 0>(ly, lane); break;
-        case 5: chol_tiles2<5, 0>(ly, lane); break;
-        case 6: chol_tiles2<6, 0>(ly, lane); break;
-        default: break;
+      if (p < 7) {
+        const int j0 = p * 8, pe = j0 + 8;
+        double pc[8], lp[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) pc[c] = L[lane][pe + c];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) lp[k] = L[lane][j0 + k];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          // L[pe + c][j0 .. j0 + 7], the same address in every lane
+          double b[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) b[k] = L[pe + c][j0 + k];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) pc[c] = fma(-lp[k], b[k], pc[c]);
+        }
+        panel(p + 1, pc);
       }
-      if (p < 7) panel(p + 1);
     } else {
       if (wave == 1 && p > 0) solve_rows(p - 1);
       switch (p) {
