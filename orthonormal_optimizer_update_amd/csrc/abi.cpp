@@ -172,7 +172,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     la.out = pl.split_left > 1 ? tPart : tPt;
     la.split_stride = m * r;
     la.M = mi; la.N = ni; la.r = r;
-    la.splits = pl.split_left; la.kchunk = pl.kchunk_left;
+    la.splits = pl.split_left; la.kchunk = pl.kchunk_left; la.small = pl.small_left;
     if (!fast_sw && !stream_sw) ORTHO_TRY(launch_dion_left(la, bf, nb, s));
     if (!fast_sw && !stream_sw && pl.split_left > 1) {
       RedArgs ra{};
@@ -306,7 +306,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       rb.m = tM; rb.g = tG; rb.p = tPt; rb.out = tPart;
       rb.split_stride = n * r;
       rb.M = mi; rb.N = ni; rb.r = r;
-      rb.splits = pl.split_right; rb.kchunk = pl.kchunk_right;
+      rb.splits = pl.split_right; rb.kchunk = pl.kchunk_right; rb.small = pl.small_right;
       ORTHO_TRY(launch_dion_right(rb, bf, nb, s));
     }
     RedArgs rr{};

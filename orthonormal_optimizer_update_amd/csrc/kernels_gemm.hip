@@ -53,6 +53,11 @@ using ColF32 = LdCol<ROWS, 32, NT, NP, float, false, float>;
 template <int ROWS, int NT, int NP, typename GT>
 using ColMG = LdCol<ROWS, 32, NT, NP, float, true, GT>;
 
+// Few output tiles (few_tiles): 64 x 64 tiles, k 64 deep (the column
+// loader's minimum for 64 rows), NP bf16 pieces per operand.
+template <int NP>
+using CfgSmall = GemmCfg<64, 64, 64, 2, 2, NP, NP, NP == 3 ? 6 : 3, 1>;
+
 template <typename GT, class Cfg, int NP>
 hipError_t dion_left_t(const DionLeftArgs& a, int members, hipStream_t s) {
   GemmParams<EpiStoreF32::Args> p{};
@@ -64,6 +69,9 @@ hipError_t dion_left_t(const DionLeftArgs& a, int members, hipStream_t s) {
   p.e.has_t = 0;
   p.M = a.M; p.N = a.r; p.K = a.N;
   p.splits = a.splits; p.kchunk = a.kchunk; p.tri = 0;
+  if (a.small && a.kchunk % 64 == 0)
+    return run<CfgSmall<NP>, LdRow<64, 64, 256, NP, float, true, GT>,
+               LdCol<64, 64, 256, NP, float, false, float>, EpiStoreF32>(p, members, s);
   return run<Cfg, RowMG<128, 256, NP, GT>, ColF32<128, 256, NP>, EpiStoreF32>(p, members, s);
 }
 
@@ -78,6 +86,9 @@ hipError_t dion_right_t(const DionRightArgs& a, int members, hipStream_t s) {
   p.e.has_t = 0;
   p.M = a.N; p.N = a.r; p.K = a.M;
   p.splits = a.splits; p.kchunk = a.kchunk; p.tri = 0;
+  if (a.small && a.kchunk % 64 == 0)
+    return run<CfgSmall<NP>, LdCol<64, 64, 256, NP, float, true, GT>,
+               LdCol<64, 64, 256, NP, float, false, float>, EpiStoreF32>(p, members, s);
   return run<Cfg, ColMG<128, 256, NP, GT>, ColF32<128, 256, NP>, EpiStoreF32>(p, members, s);
 }
 
@@ -90,6 +101,9 @@ hipError_t dion_update_f32(const DionUpdateArgs& a, int members, hipStream_t s) 
   p.e.c1 = a.c1; p.e.c2 = a.c2;
   p.M = a.M; p.N = a.N; p.K = a.rank;
   p.splits = 1; p.kchunk = 0; p.tri = 0;
+  if (few_tiles(a.M, a.N, members))
+    return run<GemmCfg<64, 64, 32, 2, 2, 2, 2, 3, 2>, RowF32<64, 256, 2>, RowF32<64, 256, 2>,
+               EpiDion<float>>(p, members, s);
   return run<CfgUpdF32, RowF32<128, 256, 2>, RowF32<128, 256, 2>, EpiDion<float>>(p, members, s);
 }
 

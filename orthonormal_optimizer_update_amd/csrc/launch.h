@@ -164,6 +164,7 @@ struct DionLeftArgs {
   int64_t split_stride;
   int M, N, r;           // B is M x N
   int splits, kchunk;
+  int small;             // 64 x 64 tiles, k 64 deep (kchunk a multiple of 64)
 };
 hipError_t launch_dion_left(const DionLeftArgs& a, bool bf16, int members, hipStream_t s);
 
@@ -174,6 +175,7 @@ struct DionRightArgs {
   int64_t split_stride;
   int M, N, r;
   int splits, kchunk;
+  int small;             // 64 x 64 tiles, k 64 deep (kchunk a multiple of 64)
 };
 hipError_t launch_dion_right(const DionRightArgs& a, bool bf16, int members, hipStream_t s);
 

@@ -16,16 +16,21 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Split a reduction of length K so that tiles * members * splits reaches the
 // target, with each slice a multiple of 32 and at least kMinSplitK long.
-void choose_split(int64_t K, int64_t tiles, int members, int* splits, int* kchunk) {
+void choose_split(int64_t K, int64_t tiles, int members, int* splits, int* kchunk,
+                  int64_t min_k = kMinSplitK, int64_t multiple = 32) {
   int64_t want = cdiv(kTargetWorkgroups, tiles * members);
-  int64_t cap = K / kMinSplitK;
+  int64_t cap = K / min_k;
   if (cap < 1) cap = 1;
   if (want > cap) want = cap;
   if (want < 1) want = 1;
-  int64_t kc = cdiv(cdiv(K, want), 32) * 32;
+  int64_t kc = cdiv(cdiv(K, want), multiple) * multiple;
   *kchunk = static_cast<int>(kc);
   *splits = static_cast<int>(cdiv(K, kc));
 }
+
+// Slices of 64 (a multiple of 64 when the kernel's k step is 64) for
+// contractions with few output tiles.
+constexpr int64_t kMinSplitKSmall = 64;
 
 // Split nkt k tiles so that tiles * members * splits reaches one workgroup per
 // CU of the 256 x 256 kernel, with at least 8 k tiles per split.
@@ -64,10 +69,22 @@ bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* p) {
   d.n = n;
   d.r = r;
   d.chunk = batch < kMaxMembersPerLaunch ? batch : kMaxMembersPerLaunch;
-  choose_split(n, cdiv(m, 128) * cdiv(r, 128), d.chunk, &d.split_left, &d.kchunk_left);
-  choose_split(m, cdiv(n, 128) * cdiv(r, 128), d.chunk, &d.split_right, &d.kchunk_right);
+  d.small_left = few_tiles(m, r, d.chunk);
+  d.small_right = few_tiles(n, r, d.chunk);
+  if (d.small_left)
+    choose_split(n, cdiv(m, 64) * cdiv(r, 64), d.chunk, &d.split_left, &d.kchunk_left,
+                 kMinSplitKSmall, 64);
+  else
+    choose_split(n, cdiv(m, 128) * cdiv(r, 128), d.chunk, &d.split_left, &d.kchunk_left);
+  if (d.small_right)
+    choose_split(m, cdiv(n, 64) * cdiv(r, 64), d.chunk, &d.split_right, &d.kchunk_right,
+                 kMinSplitKSmall, 64);
+  else
+    choose_split(m, cdiv(n, 128) * cdiv(r, 128), d.chunk, &d.split_right, &d.kchunk_right);
   const int64_t tg = cdiv(r, 64);
-  choose_split(m, tg * (tg + 1) / 2, d.chunk, &d.split_gram, &d.kchunk_gram);
+  const bool small_gram = tg * (tg + 1) / 2 * d.chunk < 64;
+  choose_split(m, tg * (tg + 1) / 2, d.chunk, &d.split_gram, &d.kchunk_gram,
+               small_gram ? kMinSplitKSmall : kMinSplitK);
   if (r % 128 == 0 && r >= 1024) {
     // 128 x 128 fp64 Gram tiles (from 36 tiles on; fewer leave the chip
     // idle): at most one workgroup per CU (a second round on a few CUs would
@@ -82,9 +99,9 @@ bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* p) {
     d.split_gram = static_cast<int>(cdiv(m, kc));
   }
   if (gram_tn_small_tiles(r)) {
-    choose_split(m, cdiv(r, 64) * cdiv(r, 64), d.chunk, &d.split_gram2, &d.kchunk_gram2);
-    d.kchunk_gram2 = static_cast<int>(cdiv(d.kchunk_gram2, 64) * 64);
-    d.split_gram2 = static_cast<int>(cdiv(m, d.kchunk_gram2));
+    const int64_t t64 = cdiv(r, 64) * cdiv(r, 64);
+    choose_split(m, t64, d.chunk, &d.split_gram2, &d.kchunk_gram2,
+                 t64 * d.chunk < 64 ? kMinSplitKSmall : kMinSplitK, 64);
   } else {
     choose_split(m, cdiv(r, 128) * cdiv(r, 128), d.chunk, &d.split_gram2, &d.kchunk_gram2);
   }

@@ -16,6 +16,13 @@ constexpr size_t kWsAlign = 256;
 // 256 x 256 result is only 4 tiles of 128); the plan sizes its split for them.
 inline bool gram_tn_small_tiles(int r) { return r < 512; }
 
+// A contraction with fewer than 64 output tiles of 128 x 128 over a launch's
+// members leaves most of the chip idle: the Dion sweeps then run on 64 x 64
+// tiles (k 64 deep), and every split-K reduction may cut k down to 64.
+inline bool few_tiles(int64_t rows, int64_t cols, int members) {
+  return ((rows + 127) / 128) * ((cols + 127) / 128) * members < 64;
+}
+
 // Byte offsets of one member's regions inside the Dion workspace, and the
 // split-K factors chosen for the three reductions over a long dimension.
 struct DionPlan {
@@ -27,6 +34,7 @@ struct DionPlan {
   int split_right, kchunk_right;  // B^T P: split over m
   int split_gram, kchunk_gram;    // fp64 P^T P: split over m
   int split_gram2, kchunk_gram2;  // bf16x3 P1^T P1 (correction pass): split over m
+  int small_left, small_right;    // sweeps on 64 x 64 tiles (few_tiles), kchunk a multiple of 64
   int nrb;                   // 64-row blocks of R (column-norm partials)
   size_t off_pt, off_p1, off_part, off_s, off_x, off_d, off_tt, off_r, off_colsq;
   int64_t rpb;               // leading dimension of the bf16 factor copies (r rounded to 8)

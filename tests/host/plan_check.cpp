@@ -84,8 +84,13 @@ static void check_dion(int64_t m, int64_t n, int r, int batch) {
          p.member_bytes, p.chunk);
   EXPECT(p.rp >= r && p.rp % 4 == 0 && p.rpb >= r && p.rpb % 8 == 0, "rp %lld rpb %lld for r %d",
          (long long)p.rp, (long long)p.rpb, r);
-  check_split("left", n, p.split_left, p.kchunk_left, 32, m, n, r);
-  check_split("right", m, p.split_right, p.kchunk_right, 32, m, n, r);
+  EXPECT(p.small_left == few_tiles(m, r, p.chunk) && p.small_right == few_tiles(n, r, p.chunk),
+         "small sweeps flags (m %lld n %lld r %d)", (long long)m, (long long)n, r);
+  // the 64 x 64 sweep kernels step k by 64
+  check_split("left", n, p.split_left, p.kchunk_left, p.small_left ? 64 : 32, m, n, r);
+  check_split("right", m, p.split_right, p.kchunk_right, p.small_right ? 64 : 32, m, n, r);
+  if (p.small_left) EXPECT(p.kchunk_left % 64 == 0, "small left kchunk %d", p.kchunk_left);
+  if (p.small_right) EXPECT(p.kchunk_right % 64 == 0, "small right kchunk %d", p.kchunk_right);
   check_split("gram", m, p.split_gram, p.kchunk_gram, 32, m, n, r);
   check_split("gram2", m, p.split_gram2, p.kchunk_gram2, gram_tn_small_tiles(r) ? 64 : 32, m, n, r);
   // every split-K partial set that goes through the shared partial buffer
