@@ -506,7 +506,8 @@ ortho_status run_ns(int32_t batch, const ortho_mat* G, const ortho_mat* Out, int
       const int cur = it & 1;
       NsGramArgs g1{};
       g1.x = xb[cur]; g1.a = ta; g1.M = M; g1.K = N;
-      const bool small_poly = pl.gram_splits > 1 && c != 0.0f;
+      // the fused reduce-and-polynomial kernel holds a side of at most 128 rows
+      const bool small_poly = pl.gram_splits > 1 && c != 0.0f && M <= 128;
       if (pl.gram_splits > 1) {
         const MatArg gpart = ws_table(base, mb, pl.off_gpart, nb, M, M, M, 4, 16);
         const int64_t slice = static_cast<int64_t>(M) * M;

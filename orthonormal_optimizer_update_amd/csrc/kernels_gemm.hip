@@ -155,7 +155,7 @@ hipError_t dion_update_bf16(const DionUpdateArgs& a, int members, hipStream_t s)
 }
 
 template <class Cfg>
-using NsRow = LdRowBf16<Cfg::BM, 32, Cfg::NT>;
+using NsRow = LdRowBf16<Cfg::BM, Cfg::BK, Cfg::NT>;
 
 // The 256 x 256 x 64 direct-to-LDS kernel applies when the product tiles
 // exactly, every operand row is 16-byte aligned and a 256-row block of an
@@ -184,6 +184,20 @@ hipError_t run_fast(GemmParams<typename Epi::Args>& p, int members, hipStream_t 
   return hipGetLastError();
 }
 
+// Newton-Schulz products whose 256 x 256 grid (upper tiles for the symmetric
+// ones) would give fewer than 128 workgroups over a launch's members run on
+// the 128 x 128 kernel instead: four times the workgroups (full tiles, so the
+// symmetric products compute both halves).
+// 128 deep in k: the loop issues the next tile's loads and then runs 32
+// products per wave, which covers more of the loads' latency than 32-deep steps.
+using CfgNsMid = GemmCfg<128, 128, 128, 2, 2, 1, 1, 1, 1>;
+
+inline bool ns_few_fast_tiles(int M, int N, int members, bool sym) {
+  const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256;
+  const int64_t tiles = sym ? tm * (tm + 1) / 2 : tm * tn;
+  return tiles * members < 128;
+}
+
 template <class Cfg>
 hipError_t ns_gram_t(const NsGramArgs& a, int members, hipStream_t s) {
   GemmParams<EpiNSGram::Args> p{};
@@ -192,6 +206,8 @@ hipError_t ns_gram_t(const NsGramArgs& a, int members, hipStream_t s) {
   p.e.a = a.a;
   p.M = a.M; p.N = a.M; p.K = a.K;
   p.splits = 1; p.kchunk = 0; p.tri = 0;
+  if (ns_few_fast_tiles(a.M, a.M, members, true))
+    return run<CfgNsMid, NsRow<CfgNsMid>, NsRow<CfgNsMid>, EpiNSGram>(p, members, s);
   if (fast_ok(p.M, p.N, p.K, p.a, p.b0)) {
     p.sym = 1;  // X X^T: upper tiles, mirrored
     return run_fast<EpiNSGram>(p, members, s);
@@ -208,6 +224,8 @@ hipError_t ns_poly_t(const NsPolyArgs& a, int members, hipStream_t s) {
   p.e.has32 = a.M <= kNsSplitRows;
   p.M = a.M; p.N = a.M; p.K = a.M;
   p.splits = 1; p.kchunk = 0; p.tri = 0;
+  if (ns_few_fast_tiles(a.M, a.M, members, true))
+    return run<CfgNsMid, NsRow<CfgNsMid>, NsRow<CfgNsMid>, EpiNSPoly>(p, members, s);
   if (fast_ok(p.M, p.N, p.K, p.a, p.b0)) {
     p.sym = 1;  // b A + c A A is symmetric with A: upper tiles, mirrored
     return run_fast<EpiNSPoly>(p, members, s);
@@ -224,6 +242,8 @@ hipError_t ns_apply_t(const NsApplyArgs& a, int members, hipStream_t s) {
   p.e.a = a.a; p.e.last = a.last; p.e.out_transposed = a.out_transposed;
   p.M = a.M; p.N = a.N; p.K = a.M;
   p.splits = 1; p.kchunk = 0; p.tri = 0;
+  if (ns_few_fast_tiles(a.M, a.N, members, false))
+    return run<CfgNsMid, NsRow<CfgNsMid>, NsRow<CfgNsMid>, EpiNSApply<OUT_T>>(p, members, s);
   if (fast_ok(p.M, p.N, p.K, p.a, p.b0)) return run_fast<EpiNSApply<OUT_T>>(p, members, s);
   return run<Cfg, NsRow<Cfg>, NsRow<Cfg>, EpiNSApply<OUT_T>>(p, members, s);
 }
@@ -308,7 +328,7 @@ hipError_t launch_ns_gram(const NsGramArgs& a, int members, hipStream_t s) {
 
 hipError_t launch_ns_gram_split(const NsGramArgs& a, const MatArg& part, int64_t split_stride,
                                 int splits, int kchunk, int members, hipStream_t s) {
-  if (a.M > 128 || splits < 2 || kchunk % 32 != 0) return hipErrorInvalidValue;
+  if (splits < 2 || kchunk % 32 != 0) return hipErrorInvalidValue;
   GemmParams<EpiStoreF32::Args> p{};
   p.a = with_rows(a.x, a.M);
   p.b0 = with_rows(a.x, a.M);

@@ -222,9 +222,15 @@ bool plan_ns(int64_t m, int64_t n, int32_t batch, NsPlan* p) {
   s.off_bp32 = o;    o = align_up(o + (s.M <= 128 ? mm * 4 : 0));
   s.gram_splits = 1;
   s.gram_kchunk = 0;
-  if (s.M <= 128 && s.M % 64 == 0) {
+  // A Gram side of 64 or 128 rows is one 128 x 128 tile per member; a larger
+  // side whose symmetric 256 x 256 grid gives under 128 workgroups runs on
+  // 128 x 128 tiles (see the Newton-Schulz launchers).  Both split k (the
+  // fixed-order reduce takes sides that are multiples of 64).
+  const int64_t t256 = cdiv(s.M, 256), t128 = cdiv(s.M, 128);
+  const bool few = s.M > 128 && s.M % 64 == 0 && t256 * (t256 + 1) / 2 * s.chunk < 128;
+  if ((s.M <= 128 && s.M % 64 == 0) || few) {
     // one workgroup per CU over the chunk's members, at least 8 k steps of 32 each
-    int64_t want = cdiv(256, s.chunk), cap = s.N / 256;
+    int64_t want = cdiv(256, s.chunk * (s.M <= 128 ? 1 : t128 * t128)), cap = s.N / 256;
     if (want > cap) want = cap;
     if (want > 1) {
       s.gram_kchunk = static_cast<int>(cdiv(cdiv(s.N, want), 32) * 32);
