@@ -172,11 +172,15 @@ struct EpiNSPoly {
   __device__ const void* fast_pre2_src() const { return nullptr; }
   __device__ int64_t fast_pre2_ld() const { return 0; }
   __device__ float fast_pre2_scale() const { return 0.f; }
+  // Preloads run before the main loop: clamped addresses and a select (no
+  // branch per element), so all of a thread's loads are in flight together.
   __device__ __forceinline__ void init(int row0, int col, int M, int N, float* v) const {
+    const int cc = min(col, N - 1);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      v[t] = (col < N && row0 + t < M) ? boc * bf16_bits_to_f32(a[(int64_t)(row0 + t) * lda + col])
-                                       : 0.f;
+    for (int t = 0; t < 4; ++t) {
+      const float x = bf16_bits_to_f32(a[(int64_t)min(row0 + t, M - 1) * lda + cc]);
+      v[t] = (col < N && row0 + t < M) ? boc * x : 0.f;
+    }
   }
   __device__ __forceinline__ void apply(int row0, int col, int M, int N, float v0, float v1,
                                         float v2, float v3) {
@@ -252,9 +256,12 @@ struct EpiNSApply {
     *reinterpret_cast<uint2*>(xbt + (int64_t)col * ldbt + row0) = pack_bf16x4(v);
   }
   __device__ __forceinline__ void init(int row0, int col, int M, int N, float* v) const {
+    const int cc = min(col, N - 1);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      v[t] = (col < N && row0 + t < M) ? a * x32[(int64_t)(row0 + t) * ldx + col] : 0.f;
+    for (int t = 0; t < 4; ++t) {
+      const float x = x32[(int64_t)min(row0 + t, M - 1) * ldx + cc];
+      v[t] = (col < N && row0 + t < M) ? a * x : 0.f;
+    }
   }
   __device__ __forceinline__ void apply(int row0, int col, int M, int N, float v0, float v1,
                                         float v2, float v3) {
@@ -461,12 +468,16 @@ struct EpiDionPre {
         x(static_cast<uint16_t*>(const_cast<void*>(e.x.p[bi]))),
         ldm(e.m.ld), ldg(e.g.ld), ldx(e.x.ld) {}
   __device__ __forceinline__ void init2(int row0, int col, int M, int N, float* u, float* w) const {
+    const int cc = min(col, N - 1);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int row = row0 + t;
       const bool ok = col < N && row < M;
-      u[t] = ok ? -(m[(int64_t)row * ldm + col] + bf16_bits_to_f32(g[(int64_t)row * ldg + col])) : 0.f;
-      w[t] = ok ? -bf16_bits_to_f32(x[(int64_t)row * ldx + col]) : 0.f;
+      const int64_t rr = min(row, M - 1);
+      const float mv = m[rr * ldm + cc], gv = bf16_bits_to_f32(g[rr * ldg + cc]);
+      const float xv = bf16_bits_to_f32(x[rr * ldx + cc]);
+      u[t] = ok ? -(mv + gv) : 0.f;
+      w[t] = ok ? -xv : 0.f;
     }
   }
   __device__ __forceinline__ void apply2(int row0, int col, int M, int N, float u0, float u1,

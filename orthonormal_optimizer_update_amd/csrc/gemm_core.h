@@ -382,6 +382,61 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(GemmParams<typename Epi::
   const int frag_row = lane & 31;
   const int frag_k = (lane >> 5) * 8;
 
+  // products of one LDS stage into the accumulators
+  // Products of one LDS stage into the accumulators.  The fragments of the
+  // next 16-deep k step are read before this step's products are issued
+  // (two fragment sets, indices fixed by the full unroll), so the LDS reads'
+  // latency sits under the matrix-core work instead of in front of it.
+  auto compute = [&](int cur) {
+    const bf16* sa = stage_a(cur);
+    constexpr int KS = BK / 16;
+    bf16x8 af[2][Cfg::NA][MI];
+    bf16x8 bfr[2][NBOP][Cfg::NB][NI];
+#pragma unroll
+    for (int t = -1; t < KS; ++t) {
+      if (t + 1 < KS) {
+        const int nb = (t + 1) & 1, kk = (t + 1) * 16;
+#pragma unroll
+        for (int pa = 0; pa < Cfg::NA; ++pa)
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+            af[nb][pa][i] = *reinterpret_cast<const bf16x8*>(
+                sa + pa * Cfg::A_ELEMS + (wm * Cfg::WTM + i * 32 + frag_row) * LDS_LD + kk + frag_k);
+#pragma unroll
+        for (int q = 0; q < NBOP; ++q) {
+          const bf16* sb = stage_b(cur, q);
+#pragma unroll
+          for (int pb = 0; pb < Cfg::NB; ++pb)
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+              bfr[nb][q][pb][j] = *reinterpret_cast<const bf16x8*>(
+                  sb + pb * Cfg::B_ELEMS + (wn * Cfg::WTN + j * 32 + frag_row) * LDS_LD + kk + frag_k);
+        }
+      }
+      if (t < 0) continue;
+      const int b = t & 1;
+#pragma unroll
+      for (int q = 0; q < NBOP; ++q)
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NI; ++j) {
+            if constexpr (Cfg::PRODS == 6) {
+              acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[b][2][i], bfr[b][q][0][j], acc[q][i][j], 0, 0, 0);
+              acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[b][1][i], bfr[b][q][1][j], acc[q][i][j], 0, 0, 0);
+              acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[b][0][i], bfr[b][q][2][j], acc[q][i][j], 0, 0, 0);
+            }
+            if constexpr (Cfg::PRODS >= 3) {
+              acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[b][1][i], bfr[b][q][0][j], acc[q][i][j], 0, 0, 0);
+              acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[b][0][i], bfr[b][q][1][j], acc[q][i][j], 0, 0, 0);
+            }
+            if constexpr (Cfg::PRODS == 2)
+              acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[b][1][i], bfr[b][q][0][j], acc[q][i][j], 0, 0, 0);
+            acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[b][0][i], bfr[b][q][0][j], acc[q][i][j], 0, 0, 0);
+          }
+    }
+  };
+
   for (int kt = 0; kt < nk; ++kt) {
     __syncthreads();
     const int cur = kt & 1;
@@ -392,45 +447,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(GemmParams<typename Epi::
       lb0.load(n0, kn, kend);
       if constexpr (NBOP == 2) lb1.load(n0, kn, kend);
     }
-    const bf16* sa = stage_a(cur);
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 af[Cfg::NA][MI];
-#pragma unroll
-      for (int pa = 0; pa < Cfg::NA; ++pa)
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-          af[pa][i] = *reinterpret_cast<const bf16x8*>(
-              sa + pa * Cfg::A_ELEMS + (wm * Cfg::WTM + i * 32 + frag_row) * LDS_LD + kk + frag_k);
-#pragma unroll
-      for (int q = 0; q < NBOP; ++q) {
-        const bf16* sb = stage_b(cur, q);
-        bf16x8 bfr[Cfg::NB][NI];
-#pragma unroll
-        for (int pb = 0; pb < Cfg::NB; ++pb)
-#pragma unroll
-          for (int j = 0; j < NI; ++j)
-            bfr[pb][j] = *reinterpret_cast<const bf16x8*>(
-                sb + pb * Cfg::B_ELEMS + (wn * Cfg::WTN + j * 32 + frag_row) * LDS_LD + kk + frag_k);
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int j = 0; j < NI; ++j) {
-            if constexpr (Cfg::PRODS == 6) {
-              acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[2][i], bfr[0][j], acc[q][i][j], 0, 0, 0);
-              acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], bfr[1][j], acc[q][i][j], 0, 0, 0);
-              acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bfr[2][j], acc[q][i][j], 0, 0, 0);
-            }
-            if constexpr (Cfg::PRODS >= 3) {
-              acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], bfr[0][j], acc[q][i][j], 0, 0, 0);
-              acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bfr[1][j], acc[q][i][j], 0, 0, 0);
-            }
-            if constexpr (Cfg::PRODS == 2)
-              acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], bfr[0][j], acc[q][i][j], 0, 0, 0);
-            acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bfr[0][j], acc[q][i][j], 0, 0, 0);
-          }
-      }
-    }
+    compute(cur);
     if (more) {
       const int nxt = cur ^ 1;
       la.template store<LDS_LD>(stage_a(nxt), Cfg::A_ELEMS);

@@ -188,9 +188,9 @@ hipError_t run_fast(GemmParams<typename Epi::Args>& p, int members, hipStream_t 
 // ones) would give fewer than 128 workgroups over a launch's members run on
 // the 128 x 128 kernel instead: four times the workgroups (full tiles, so the
 // symmetric products compute both halves).
-// 128 deep in k: the loop issues the next tile's loads and then runs 32
-// products per wave, which covers more of the loads' latency than 32-deep steps.
-using CfgNsMid = GemmCfg<128, 128, 128, 2, 2, 1, 1, 1, 1>;
+// 64 deep in k: 16 products per wave cover each tile's loads, and at 73 KB of
+// LDS and 150 registers two workgroups share a CU.
+using CfgNsMid = GemmCfg<128, 128, 64, 2, 2, 1, 1, 1, 1>;
 
 inline bool ns_few_fast_tiles(int M, int N, int members, bool sym) {
   const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256;
