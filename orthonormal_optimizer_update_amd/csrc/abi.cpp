@@ -266,6 +266,12 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     ORTHO_TRY(launch_correction(part_f, static_cast<int64_t>(mb / 4), static_cast<int64_t>(r) * r,
                                 pl.split_gram2, r, tt, static_cast<int64_t>(mb / 4), nb, s));
     aa.pt = tP1; aa.out = tPt; aa.has_bf16 = bf;   // bf16 P feeds the last sweep
+    if (stream_sw) {
+      // the k-blocked transposed pieces of P that the streaming sweep 2 reads
+      aa.piece_hi = ws_table(base, mb, pl.off_phit, nb, m, r, mi, 2, 16);
+      aa.piece_lo = ws_table(base, mb, pl.off_plot, nb, m, r, mi, 2, 16);
+      aa.has_pieces = 1;
+    }
     ORTHO_TRY(launch_apply_t(aa, false, nb, s));
     }
 
@@ -296,9 +302,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       sr.f[1] = ws_table(base, mb, pl.off_plot, nb, m, r, mi, 2, 16);
       sr.split_stride = n * r;
       sr.rows = ni; sr.K = mi; sr.kchunk = pl.kchunk_sr;
-      SplitTArgs pa{};
-      pa.src = tPt; pa.hit = sr.f[0]; pa.lot = sr.f[1]; pa.rows = mi; pa.cols = r; pa.blocked = 1;
-      ORTHO_TRY(launch_split_t(pa, nb, s));
+      // (the pieces were written by the last orthonormalisation product)
       ORTHO_TRY(launch_dion_sweep(sr, true, nb, s));
       split_r = pl.split_sr;
     } else {

@@ -59,17 +59,27 @@ struct EpiStoreF32 {
     int has_t;
     MatArg cb;             // bf16 copy (used when has_b)
     int has_b;
+    // bf16 hi and lo pieces of the transpose, k-blocked: element (row k,
+    // column j) at (k / 16) * N * 16 + j * 16 + k % 16 (used when has_p; the
+    // workgroup's rows come in groups of 4 inside one block of 16)
+    MatArg phi, plo;
+    int has_p;
   };
   float* c;
   float* ct;
   uint16_t* cb;
+  uint16_t* phi;
+  uint16_t* plo;
   int64_t ld, ldt, ldb;
-  bool has_t, has_b;
+  bool has_t, has_b, has_p;
   __device__ EpiStoreF32(const Args& a, int bi, int split)
       : c(static_cast<float*>(const_cast<void*>(a.c.p[bi])) + split * a.split_stride),
         ct(a.has_t ? static_cast<float*>(const_cast<void*>(a.ct.p[bi])) : nullptr),
         cb(a.has_b ? static_cast<uint16_t*>(const_cast<void*>(a.cb.p[bi])) : nullptr),
-        ld(a.c.ld), ldt(a.ct.ld), ldb(a.cb.ld), has_t(a.has_t), has_b(a.has_b) {}
+        phi(a.has_p ? static_cast<uint16_t*>(const_cast<void*>(a.phi.p[bi])) : nullptr),
+        plo(a.has_p ? static_cast<uint16_t*>(const_cast<void*>(a.plo.p[bi])) : nullptr),
+        ld(a.c.ld), ldt(a.ct.ld), ldb(a.cb.ld), has_t(a.has_t), has_b(a.has_b),
+        has_p(a.has_p) {}
   __device__ __forceinline__ void apply(int row0, int col, int M, int N, float v0, float v1,
                                         float v2, float v3) {
     if (col >= N) return;
@@ -86,6 +96,30 @@ struct EpiStoreF32 {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         if (row0 + t < M) cb[(int64_t)(row0 + t) * ldb + col] = to_bf16_bits(v[t]);
+    }
+    if (has_p) {
+      uint16_t h[4], l[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bf16 bh, bl;
+        split_bf16(row0 + t < M ? v[t] : 0.f, bh, bl);
+        h[t] = __builtin_bit_cast(uint16_t, bh);
+        l[t] = __builtin_bit_cast(uint16_t, bl);
+      }
+      const int64_t o = (int64_t)(row0 >> 4) * N * 16 + (int64_t)col * 16 + (row0 & 15);
+      if (row0 + 3 < M) {
+        *reinterpret_cast<uint2*>(phi + o) =
+            make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
+        *reinterpret_cast<uint2*>(plo + o) =
+            make_uint2(l[0] | (uint32_t(l[1]) << 16), l[2] | (uint32_t(l[3]) << 16));
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (row0 + t < M) {
+            phi[o + t] = h[t];
+            plo[o + t] = l[t];
+          }
+      }
     }
   }
 };

@@ -920,7 +920,11 @@ __global__ __launch_bounds__(256) void gram64_big_kernel(Gram64Args a) {
 
 // Sum the Gram slices and scale to unit diagonal: S = D W D with
 // d_i = 1 / sqrt(W_ii) (lower triangle), zero the inverse buffer, write d.
+// A workgroup owns a 16 x 16 block: 32 of its threads first sum the W_ii of
+// its 16 rows and 16 columns into LDS (slice order, as for every element),
+// then every thread sums and scales its own element.
 __global__ __launch_bounds__(256) void chol_prep_kernel(CholArgs a) {
+  __shared__ double dd[2][16];
   const int member = blockIdx.z;
   const double* part = a.part + member * a.part_member_stride;
   double* S = a.s + member * a.mat_stride;
@@ -929,18 +933,27 @@ __global__ __launch_bounds__(256) void chol_prep_kernel(CholArgs a) {
   const int r = a.r;
   const int i = blockIdx.y * 16 + (threadIdx.x >> 4);
   const int j = blockIdx.x * 16 + (threadIdx.x & 15);
-  if (i >= r || j >= r) return;
-  X[(int64_t)i * r + j] = 0.0;
-  if (j > i) return;
+  if (i < r && j < r) X[(int64_t)i * r + j] = 0.0;
+  if (blockIdx.x > blockIdx.y) return;   // strictly upper block: uniform exit
   auto sum = [&](int u, int v) {
     double s = 0.0;
 #pragma unroll 8
     for (int k = 0; k < a.splits; ++k) s += part[k * a.slice + (int64_t)u * r + v];
     return s;
   };
-  const double wii = sum(i, i), wjj = sum(j, j);
-  const double di = wii > 0.0 ? 1.0 / sqrt(wii) : 1.0;
-  const double dj = wjj > 0.0 ? 1.0 / sqrt(wjj) : 1.0;
+  if (threadIdx.x < 32) {
+    const int t = threadIdx.x & 15;
+    const int q = (threadIdx.x >> 4) ? blockIdx.x * 16 + t : blockIdx.y * 16 + t;
+    double v = 1.0;
+    if (q < r) {
+      const double w = sum(q, q);
+      v = w > 0.0 ? 1.0 / sqrt(w) : 1.0;
+    }
+    dd[threadIdx.x >> 4][t] = v;
+  }
+  __syncthreads();
+  if (i >= r || j >= r || j > i) return;
+  const double di = dd[0][threadIdx.x >> 4], dj = dd[1][threadIdx.x & 15];
   S[(int64_t)i * r + j] = sum(i, j) * di * dj;
   if (i == j) d[i] = di;
 }

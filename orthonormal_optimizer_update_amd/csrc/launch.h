@@ -219,6 +219,10 @@ struct ApplyArgs {
   MatArg out;
   MatArg out_bf16;   // optional bf16 copy of the result (has_bf16)
   int has_bf16;
+  // optional k-blocked transposed bf16 pieces of the result (has_pieces):
+  // element (i, j) at (i / 16) * r * 16 + j * 16 + i % 16; M a multiple of 4
+  MatArg piece_hi, piece_lo;
+  int has_pieces;
   int M, r;
 };
 hipError_t launch_apply_t(const ApplyArgs& a, bool six_products, int members, hipStream_t s);
