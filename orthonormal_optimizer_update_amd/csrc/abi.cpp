@@ -266,6 +266,11 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     ORTHO_TRY(launch_correction(part_f, static_cast<int64_t>(mb / 4), static_cast<int64_t>(r) * r,
                                 pl.split_gram2, r, tt, static_cast<int64_t>(mb / 4), nb, s));
     aa.pt = tP1; aa.out = tPt; aa.has_bf16 = bf;   // bf16 P feeds the last sweep
+    if (bf && pl.frag_p) {
+      // and its fragment-order copy the streaming update
+      aa.frag = ws_table(base, mb, pl.off_pf, nb, r, mi, r, 2, 16);
+      aa.has_frag = 1;
+    }
     if (stream_sw) {
       // the k-blocked transposed pieces of P that the streaming sweep 2 reads
       aa.piece_hi = ws_table(base, mb, pl.off_phit, nb, m, r, mi, 2, 16);
@@ -337,6 +342,10 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     DionUpdateArgs ua{};
     ua.p = tPt; ua.r = tR; ua.q = tQ; ua.m = tM; ua.g = tG; ua.x = tX;
     ua.pb = tPb; ua.rb = tRb; ua.qb = tQb;
+    // the fragment-order P exists when the last orthonormalisation product
+    // wrote it (not on the pieces path of the 256 x 256 kernel)
+    ua.has_pf = bf && pl.frag_p && !(fast_sw && pl.fast_ortho);
+    if (ua.has_pf) ua.pf = ws_table(base, mb, pl.off_pf, nb, r, mi, r, 2, 16);
     ua.c1 = 1.0f - mu; ua.c2 = lr * scale;
     ua.M = mi; ua.N = ni; ua.rank = r;
     ORTHO_TRY(launch_dion_update(ua, bf, nb, s));

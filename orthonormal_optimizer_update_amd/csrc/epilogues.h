@@ -64,22 +64,29 @@ struct EpiStoreF32 {
     // workgroup's rows come in groups of 4 inside one block of 16)
     MatArg phi, plo;
     int has_p;
+    // bf16 copy in MFMA fragment order (used when has_f; N a multiple of 16):
+    // element (i, k) at (((i / 32) * N / 16 + k / 16) * 64 + i % 32 +
+    // 32 * (k / 8 % 2)) * 8 + k % 8
+    MatArg pf;
+    int has_f;
   };
   float* c;
   float* ct;
   uint16_t* cb;
   uint16_t* phi;
   uint16_t* plo;
+  uint16_t* pf;
   int64_t ld, ldt, ldb;
-  bool has_t, has_b, has_p;
+  bool has_t, has_b, has_p, has_f;
   __device__ EpiStoreF32(const Args& a, int bi, int split)
       : c(static_cast<float*>(const_cast<void*>(a.c.p[bi])) + split * a.split_stride),
         ct(a.has_t ? static_cast<float*>(const_cast<void*>(a.ct.p[bi])) : nullptr),
         cb(a.has_b ? static_cast<uint16_t*>(const_cast<void*>(a.cb.p[bi])) : nullptr),
         phi(a.has_p ? static_cast<uint16_t*>(const_cast<void*>(a.phi.p[bi])) : nullptr),
         plo(a.has_p ? static_cast<uint16_t*>(const_cast<void*>(a.plo.p[bi])) : nullptr),
+        pf(a.has_f ? static_cast<uint16_t*>(const_cast<void*>(a.pf.p[bi])) : nullptr),
         ld(a.c.ld), ldt(a.ct.ld), ldb(a.cb.ld), has_t(a.has_t), has_b(a.has_b),
-        has_p(a.has_p) {}
+        has_p(a.has_p), has_f(a.has_f) {}
   __device__ __forceinline__ void apply(int row0, int col, int M, int N, float v0, float v1,
                                         float v2, float v3) {
     if (col >= N) return;
@@ -96,6 +103,15 @@ struct EpiStoreF32 {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         if (row0 + t < M) cb[(int64_t)(row0 + t) * ldb + col] = to_bf16_bits(v[t]);
+    }
+    if (has_f) {
+      const int64_t ks = N >> 4;
+      const int64_t base = ((int64_t)(col >> 4) * 64 + 32 * ((col >> 3) & 1)) * 8 + (col & 7);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int i = row0 + t;
+        if (i < M) pf[(((int64_t)(i >> 5) * ks) * 64 + (i & 31)) * 8 + base] = to_bf16_bits(v[t]);
+      }
     }
     if (has_p) {
       uint16_t h[4], l[4];

@@ -293,7 +293,10 @@ hipError_t launch_apply_t(const ApplyArgs& a, bool six_products, int members, hi
   p.e.has_b = a.has_bf16;
   p.e.phi = a.piece_hi; p.e.plo = a.piece_lo;
   p.e.has_p = a.has_pieces;
+  p.e.pf = a.frag;
+  p.e.has_f = a.has_frag;
   if (a.has_pieces && a.M % 4 != 0) return hipErrorInvalidValue;
+  if (a.has_frag && a.r % 16 != 0) return hipErrorInvalidValue;
   p.M = a.M; p.N = a.r; p.K = a.r;
   p.splits = 1; p.kchunk = 0; p.tri = 1;
   if (static_cast<int64_t>(cdiv(a.M, 128)) * cdiv(a.r, 128) * members < 256) {

@@ -19,7 +19,9 @@
 //   (M) or 8-byte load (G, X) per four elements, and so is every store.
 // - The R and Q' rows of the tile go through LDS in chunks of 256 k, shared by
 //   the four waves; P fragments come straight from global memory (each wave
-//   reads only its own rows).  A chunk's factor loads are issued first, then
+//   reads only its own rows), from a copy of P stored in fragment order when
+//   one is given (one contiguous 1 KB per fragment instead of 32 rows of 32
+//   bytes: a quarter of the cache-line requests).  A chunk's factor loads are issued first, then
 //   every memory term of the tile, so the products start as soon as the
 //   (L2-resident) factors have arrived while the HBM reads are still in flight.
 // - Small tiles let three workgroups share a CU, so one's epilogue and loads
@@ -39,6 +41,8 @@ constexpr int kUpdStage = kUpdCols * (kUpdKc / 8) / 256;  // 16-byte pieces per 
 struct UpdStreamParams {
   MatArg m, g, x;      // fp32 momentum, bf16 gradient, bf16 weight
   MatArg pb, rb, qb;   // bf16 P (m x r), c1 R (n x r), c2 Q' (n x r)
+  MatArg pf;           // bf16 P in fragment order (has_pf)
+  int has_pf;
   int M, N, K;         // K = r = 256 or 512
   int tiles_j;         // N / 32
 };
@@ -65,11 +69,14 @@ __device__ __forceinline__ uint2v f32x4_to_bf16_bits(floatx4 v) {
 
 // Loads of one 256-k chunk: thread t stages 16-byte pieces t, t + 256, ... of
 // the 32 x 32 grid of pieces that covers factor rows 0..31 (from r0 and q0),
-// k in [kc, kc + 256), and takes its own 16 P fragments.
+// k in [kc, kc + 256), and takes its own 16 P fragments: from its row of P
+// (prow, pstep = 1: k steps 16 elements apart) or from the fragment-order
+// copy (prow at the lane's 8 elements of the block's first k step, pstep =
+// 512: k steps 64 lanes x 8 apart).
 __device__ __forceinline__ void upd_chunk_load(uint4 (&stR)[kUpdStage], uint4 (&stQ)[kUpdStage],
                                                bf16x8 (&pf)[kUpdKc / 16], const uint16_t* r0,
                                                int64_t ldr, const uint16_t* q0, int64_t ldq,
-                                               const uint16_t* prow, int kc, int tid) {
+                                               const uint16_t* prow, int pstep, int kc, int tid) {
 #pragma unroll
   for (int u = 0; u < kUpdStage; ++u) {
     const int idx = tid + u * 256;
@@ -79,7 +86,8 @@ __device__ __forceinline__ void upd_chunk_load(uint4 (&stR)[kUpdStage], uint4 (&
     stQ[u] = *reinterpret_cast<const uint4*>(q0 + r * ldq + c);
   }
 #pragma unroll
-  for (int s = 0; s < kUpdKc / 16; ++s) pf[s] = *reinterpret_cast<const bf16x8*>(prow + kc + 16 * s);
+  for (int s = 0; s < kUpdKc / 16; ++s)
+    pf[s] = *reinterpret_cast<const bf16x8*>(prow + (int64_t)(kc / 16 + s) * 16 * pstep);
 }
 
 // NCH chunks of 256 k (r = 256 NCH).  Every loop is unrolled, so the code is
@@ -127,13 +135,24 @@ void dion_update_stream_kernel(UpdStreamParams p) {
   float* mrow = mp + static_cast<int64_t>(row) * p.m.ld;
   const uint16_t* grow = gp + static_cast<int64_t>(row) * p.g.ld;
   uint16_t* xrow = xp + static_cast<int64_t>(row) * p.x.ld;
-  const uint16_t* prow = pbp + static_cast<int64_t>(row) * p.pb.ld + 8 * h;
+  // P fragments: 16 k steps of 16 per chunk
+  const uint16_t* prow;
+  int pstep;
+  if (p.has_pf) {
+    // block of 32 rows i0 / 32, lane's 8 elements; k step s at s * 512
+    prow = static_cast<const uint16_t*>(p.pf.p[bi]) +
+           ((static_cast<int64_t>(i0 >> 5) * (p.K >> 4)) * 64 + lane) * 8;
+    pstep = 32;
+  } else {
+    prow = pbp + static_cast<int64_t>(row) * p.pb.ld + 8 * h;
+    pstep = 1;
+  }
   const int frag = (lane & 31) * kUpdLds + 8 * h;
 
   uint4 stR[kUpdStage], stQ[kUpdStage];
   bf16x8 pf[kSteps];
   upd_chunk_load(stR, stQ, pf, rbp + static_cast<int64_t>(j0) * p.rb.ld, p.rb.ld,
-                 qbp + static_cast<int64_t>(j0) * p.qb.ld, p.qb.ld, prow, 0, tid);
+                 qbp + static_cast<int64_t>(j0) * p.qb.ld, p.qb.ld, prow, pstep, 0, tid);
 
   // Memory terms of this lane: group g holds columns j0 + 8 g + 4 h + (0..3).
   floatx4 mv[4];
@@ -171,7 +190,8 @@ void dion_update_stream_kernel(UpdStreamParams p) {
     for (int s = 0; s < kSteps; ++s) pc[s] = pf[s];
     if (ch + 1 < NCH)
       upd_chunk_load(stR, stQ, pf, rbp + static_cast<int64_t>(j0) * p.rb.ld, p.rb.ld,
-                     qbp + static_cast<int64_t>(j0) * p.qb.ld, p.qb.ld, prow, (ch + 1) * kUpdKc, tid);
+                     qbp + static_cast<int64_t>(j0) * p.qb.ld, p.qb.ld, prow, pstep,
+                     (ch + 1) * kUpdKc, tid);
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
       const bf16x8 r0 = *reinterpret_cast<const bf16x8*>(sR + frag + 16 * s);
@@ -219,6 +239,7 @@ hipError_t launch_dion_update_stream(const DionUpdateArgs& a, int members, hipSt
   UpdStreamParams p{};
   p.m = a.m; p.g = a.g; p.x = a.x;
   p.pb = a.pb; p.rb = a.rb; p.qb = a.qb;
+  p.pf = a.pf; p.has_pf = a.has_pf;
   p.M = a.M; p.N = a.N; p.K = a.rank;
   p.tiles_j = a.N / kUpdCols;
   dim3 grid((a.M / kUpdRows) * p.tiles_j, members);

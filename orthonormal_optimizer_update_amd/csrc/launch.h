@@ -223,6 +223,9 @@ struct ApplyArgs {
   // element (i, j) at (i / 16) * r * 16 + j * 16 + i % 16; M a multiple of 4
   MatArg piece_hi, piece_lo;
   int has_pieces;
+  // optional bf16 copy in MFMA fragment order (see EpiStoreF32), r % 16 == 0
+  MatArg frag;
+  int has_frag;
   int M, r;
 };
 hipError_t launch_apply_t(const ApplyArgs& a, bool six_products, int members, hipStream_t s);
@@ -251,6 +254,8 @@ hipError_t launch_correction(const float* part, int64_t part_member_stride, int6
 struct DionUpdateArgs {
   MatArg p, r, q;        // P m x r, R n x r, Q' n x r (fp32)
   MatArg pb, rb, qb;     // bf16 copies (bf16 weights)
+  MatArg pf;             // bf16 P in MFMA fragment order (has_pf; streaming update only)
+  int has_pf;
   MatArg m, g, x;
   float c1, c2;
   int M, N, rank;

@@ -173,6 +173,8 @@ bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* p) {
   d.off_pb = o;    o = align_up(o + static_cast<size_t>(m) * d.rpb * 2);
   d.off_rb = o;    o = align_up(o + static_cast<size_t>(n) * d.rpb * 2);
   d.off_qb = o;    o = align_up(o + static_cast<size_t>(n) * d.rpb * 2);
+  d.frag_p = (r == 256 || r == 512) && m % 128 == 0;
+  d.off_pf = o;    o = align_up(o + (d.frag_p ? mr * 2 : 0));
   if (d.fast_sweeps) {
     const size_t mn2 = static_cast<size_t>(m) * n * 2;
     d.off_bhi = o;   o = align_up(o + mn2);

@@ -39,6 +39,11 @@ struct DionPlan {
   size_t off_pt, off_p1, off_part, off_s, off_x, off_d, off_tt, off_r, off_colsq;
   int64_t rpb;               // leading dimension of the bf16 factor copies (r rounded to 8)
   size_t off_pb, off_rb, off_qb;  // bf16 P, (1-mu) R, lr*scale*Q' for the last sweep
+  // bf16 P in MFMA fragment order for the streaming update (frag_p): 32-row
+  // blocks, then 16-deep k steps, then 64 lanes of 8 (element (i, k) at
+  // (((i / 32) * r / 16 + k / 16) * 64 + i % 32 + 32 * (k / 8 % 2)) * 8 + k % 8)
+  bool frag_p;
+  size_t off_pf;
   // Sweeps on the 256 x 256 kernel (m, n, r multiples of 256, bf16 weights):
   // bf16x2 pieces of B = M + G (m x n) and B^T, of Q^T (r x n) and of P^T (r x m),
   // and split-K factors in k tiles of the three-segment reductions.

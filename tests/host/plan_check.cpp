@@ -124,7 +124,9 @@ static void check_dion(int64_t m, int64_t n, int r, int batch) {
       {"tt", p.off_tt, rr * 4},                {"r", p.off_r, (size_t)n * p.rp * 4},
       {"colsq", p.off_colsq, (size_t)cdiv(n, 64) * r * 4},
       {"pb", p.off_pb, (size_t)m * p.rpb * 2}, {"rb", p.off_rb, (size_t)n * p.rpb * 2},
-      {"qb", p.off_qb, (size_t)n * p.rpb * 2}};
+      {"qb", p.off_qb, (size_t)n * p.rpb * 2},
+      {"pf", p.off_pf, p.frag_p ? mr * 2 : 0}};
+  EXPECT(p.frag_p == ((r == 256 || r == 512) && m % 128 == 0), "fragment-order P flag");
   if (p.fast_sweeps)
     for (auto pr : {std::make_pair("bhi", p.off_bhi), std::make_pair("blo", p.off_blo),
                     std::make_pair("bhit", p.off_bhit), std::make_pair("blot", p.off_blot)})
