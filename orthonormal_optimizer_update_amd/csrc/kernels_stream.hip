@@ -15,8 +15,12 @@
 //   block (one 32-row strip).
 // - The products are formed transposed, C^T = R P^T, so the fp32 accumulator of
 //   lane l, element e is C[i0 + l%32][j0 + 8*(e/4) + 4*(l/32) + e%4]: four
-//   consecutive columns of one row.  Every memory term is then one 16-byte load
-//   (M) or 8-byte load (G, X) per four elements, and so is every store.
+//   consecutive columns of one row.  After the products each wave passes its
+//   two accumulator blocks through LDS (the factor staging buffer, free by
+//   then) so that lane l holds columns 4 (l % 8) .. + 3 of rows l / 8 + 8 q:
+//   every memory term and store is then one access per four elements that
+//   covers 8 whole 32-column row segments per instruction (the accumulator
+//   layout itself touched 32 rows per instruction, four times per line).
 // - The R and Q' rows of the tile go through LDS in chunks of 256 k, shared by
 //   the four waves; P fragments come straight from global memory (each wave
 //   reads only its own rows), from a copy of P stored in fragment order when
@@ -37,6 +41,10 @@ constexpr int kUpdCols = 32;    // tile columns
 constexpr int kUpdKc = 256;     // k per chunk staged in LDS
 constexpr int kUpdLds = kUpdKc + 8;  // bf16 per LDS row; +16 B spreads rows over the banks
 constexpr int kUpdStage = kUpdCols * (kUpdKc / 8) / 256;  // 16-byte pieces per thread per factor
+constexpr int kUpdTp = 36;   // floats per row of a wave's 32 x 32 transposition block
+constexpr int kUpdLdsBytes = 2 * kUpdCols * kUpdLds * 2;  // sR and sQ
+constexpr int kUpdTBytes = 4 * 2 * 32 * kUpdTp * 4;       // 4 waves x (M, X) blocks
+constexpr int kUpdShared = kUpdLdsBytes > kUpdTBytes ? kUpdLdsBytes : kUpdTBytes;
 
 struct UpdStreamParams {
   MatArg m, g, x;      // fp32 momentum, bf16 gradient, bf16 weight
@@ -96,8 +104,9 @@ __device__ __forceinline__ void upd_chunk_load(uint4 (&stR)[kUpdStage], uint4 (&
 template <int NCH>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(NCH == 1 ? 3 : 2, NCH == 1 ? 3 : 2)))
 void dion_update_stream_kernel(UpdStreamParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sR[kUpdCols * kUpdLds];
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[kUpdCols * kUpdLds];
+  __shared__ __attribute__((aligned(16))) char smem[kUpdShared];
+  uint16_t* sR = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* sQ = sR + kUpdCols * kUpdLds;
   constexpr int kSteps = kUpdKc / 16;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -132,9 +141,8 @@ void dion_update_stream_kernel(UpdStreamParams p) {
   const uint16_t* rbp = static_cast<const uint16_t*>(p.rb.p[bi]);
   const uint16_t* qbp = static_cast<const uint16_t*>(p.qb.p[bi]);
 
-  float* mrow = mp + static_cast<int64_t>(row) * p.m.ld;
-  const uint16_t* grow = gp + static_cast<int64_t>(row) * p.g.ld;
-  uint16_t* xrow = xp + static_cast<int64_t>(row) * p.x.ld;
+  // memory terms: lane l, rows i0 + l / 8 + 8 q, columns j0 + 4 (l % 8) .. + 3
+  const int mr0 = i0 + (lane >> 3), mc = j0 + 4 * (lane & 7);
   // P fragments: 16 k steps of 16 per chunk
   const uint16_t* prow;
   int pstep;
@@ -154,15 +162,14 @@ void dion_update_stream_kernel(UpdStreamParams p) {
   upd_chunk_load(stR, stQ, pf, rbp + static_cast<int64_t>(j0) * p.rb.ld, p.rb.ld,
                  qbp + static_cast<int64_t>(j0) * p.qb.ld, p.qb.ld, prow, pstep, 0, tid);
 
-  // Memory terms of this lane: group g holds columns j0 + 8 g + 4 h + (0..3).
   floatx4 mv[4];
   uint2v gv[4], xv[4];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int col = j0 + 8 * g + 4 * h;
-    mv[g] = *reinterpret_cast<const floatx4*>(mrow + col);
-    gv[g] = *reinterpret_cast<const uint2v*>(grow + col);
-    xv[g] = *reinterpret_cast<const uint2v*>(xrow + col);
+  for (int q = 0; q < 4; ++q) {
+    const int64_t rq = mr0 + 8 * q;
+    mv[q] = *reinterpret_cast<const floatx4*>(mp + rq * p.m.ld + mc);
+    gv[q] = *reinterpret_cast<const uint2v*>(gp + rq * p.g.ld + mc);
+    xv[q] = *reinterpret_cast<const uint2v*>(xp + rq * p.x.ld + mc);
   }
 
   floatx16 accM, accX;
@@ -201,19 +208,38 @@ void dion_update_stream_kernel(UpdStreamParams p) {
     }
   }
 
+  // accumulators to row-contiguous order through this wave's LDS blocks
+  __syncthreads();  // every wave is done with sR and sQ
+  float* tM = reinterpret_cast<float*>(smem) + wave * (2 * 32 * kUpdTp);
+  float* tX = tM + 32 * kUpdTp;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const int col = j0 + 8 * g + 4 * h;
-    const floatx4 gf = bf16x4_bits_to_f32(gv[g]);
-    const floatx4 xf = bf16x4_bits_to_f32(xv[g]);
+    const int c = 8 * g + 4 * h;
+    floatx4 a, b;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      a[t] = accM[4 * g + t];
+      b[t] = accX[4 * g + t];
+    }
+    *reinterpret_cast<floatx4*>(tM + (lane & 31) * kUpdTp + c) = a;
+    *reinterpret_cast<floatx4*>(tX + (lane & 31) * kUpdTp + c) = b;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int rl = (lane >> 3) + 8 * q, cl = 4 * (lane & 7);
+    const floatx4 am = *reinterpret_cast<const floatx4*>(tM + rl * kUpdTp + cl);
+    const floatx4 ax = *reinterpret_cast<const floatx4*>(tX + rl * kUpdTp + cl);
+    const floatx4 gf = bf16x4_bits_to_f32(gv[q]);
+    const floatx4 xf = bf16x4_bits_to_f32(xv[q]);
     floatx4 mo, xo;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      mo[t] = (mv[g][t] + gf[t]) - accM[4 * g + t];
-      xo[t] = xf[t] - accX[4 * g + t];
+      mo[t] = (mv[q][t] + gf[t]) - am[t];
+      xo[t] = xf[t] - ax[t];
     }
-    *reinterpret_cast<floatx4*>(mrow + col) = mo;
-    *reinterpret_cast<uint2v*>(xrow + col) = f32x4_to_bf16_bits(xo);
+    const int64_t rq = mr0 + 8 * q;
+    *reinterpret_cast<floatx4*>(mp + rq * p.m.ld + mc) = mo;
+    *reinterpret_cast<uint2v*>(xp + rq * p.x.ld + mc) = f32x4_to_bf16_bits(xo);
   }
 }
 
