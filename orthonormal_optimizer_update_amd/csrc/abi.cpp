@@ -251,6 +251,10 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       rp2.slice = mr; rp2.splits = pl.split_ap3; rp2.rows = mi; rp2.cols = r;
       rp2.out = tPt; rp2.has_out = 1; rp2.out_bf16 = tPb; rp2.has_bf16 = 1;
       rp2.tpiece[0] = tPhiT; rp2.tpiece[1] = tPloT; rp2.has_t = 1;
+      if (pl.frag_p) {
+        rp2.frag = ws_table(base, mb, pl.off_pf, nb, r, mi, r, 2, 16);
+        rp2.has_frag = 1;
+      }
       ORTHO_TRY(launch_reduce_pieces(rp2, nb, s));
     } else {
     ApplyArgs aa{};
@@ -342,9 +346,9 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     DionUpdateArgs ua{};
     ua.p = tPt; ua.r = tR; ua.q = tQ; ua.m = tM; ua.g = tG; ua.x = tX;
     ua.pb = tPb; ua.rb = tRb; ua.qb = tQb;
-    // the fragment-order P exists when the last orthonormalisation product
-    // wrote it (not on the pieces path of the 256 x 256 kernel)
-    ua.has_pf = bf && pl.frag_p && !(fast_sw && pl.fast_ortho);
+    // the fragment-order P, written by the last orthonormalisation product or
+    // its reduce
+    ua.has_pf = bf && pl.frag_p;
     if (ua.has_pf) ua.pf = ws_table(base, mb, pl.off_pf, nb, r, mi, r, 2, 16);
     ua.c1 = 1.0f - mu; ua.c2 = lr * scale;
     ua.M = mi; ua.N = ni; ua.rank = r;

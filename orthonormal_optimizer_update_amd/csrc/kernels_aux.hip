@@ -199,9 +199,17 @@ __global__ __launch_bounds__(256) void reduce_pieces_kernel(RedPiecesArgs a) {
     for (int k = 0; k < a.splits; ++k) v += *reinterpret_cast<const floatx4*>(src + k * a.slice);
     if (a.has_out)
       *reinterpret_cast<floatx4*>(static_cast<float*>(const_cast<void*>(a.out.p[bi])) + row * a.out.ld + c0 + cl) = v;
-    if (a.has_bf16) {
+    if (a.has_bf16 || a.has_frag) {
       const uint16_t h[4] = {to_bf16_bits(v[0]), to_bf16_bits(v[1]), to_bf16_bits(v[2]), to_bf16_bits(v[3])};
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(const_cast<void*>(a.out_bf16.p[bi])) + row * a.out_bf16.ld + c0 + cl) = pack4(h);
+      if (a.has_bf16)
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(const_cast<void*>(a.out_bf16.p[bi])) + row * a.out_bf16.ld + c0 + cl) = pack4(h);
+      if (a.has_frag) {
+        // element (row, k): (((row / 32) * cols / 16 + k / 16) * 64 + row % 32 +
+        // 32 * (k / 8 % 2)) * 8 + k % 8; k = c0 + cl .. + 3 share one 8-group
+        const int k = c0 + cl;
+        const int64_t o = (((row >> 5) * (a.cols >> 4) + (k >> 4)) * 64 + (row & 31) + 32 * ((k >> 3) & 1)) * 8 + (k & 7);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(const_cast<void*>(a.frag.p[bi])) + o) = pack4(h);
+      }
     }
     floatx4 x = v;
     for (int pc = 0; pc < a.np; ++pc) {
@@ -1626,6 +1634,7 @@ hipError_t launch_reduce_splits(const RedArgs& a, int members, hipStream_t s) {
 
 hipError_t launch_reduce_pieces(const RedPiecesArgs& a, int members, hipStream_t s) {
   if (a.rows % 64 != 0 || a.cols % 64 != 0 || a.np < 0 || a.np > 3) return hipErrorInvalidValue;
+  // (cols % 64 == 0 also covers the fragment order's cols % 16)
   hipLaunchKernelGGL(reduce_pieces_kernel, dim3(a.cols / 64, a.rows / 64, members), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -120,6 +120,9 @@ static bool rows16(const MatArg& t, int members, size_t esz) {
 }
 
 hipError_t dion_update_bf16(const DionUpdateArgs& a, int members, hipStream_t s) {
+  // r = 512 with P in fragment order: the streaming kernel
+  if (a.rank == 512 && a.has_pf && dion_update_stream_ok(a, members))
+    return launch_dion_update_stream(a, members, s);
   // From r = 512 on, the products weigh enough that the 256 x 256 pair is the
   // fastest (12-layer GPT groups at r = 512: 15.7 ms per step against 16.5 with
   // the streaming kernel); at r = 256 the step is bound by its 14 mn bytes and

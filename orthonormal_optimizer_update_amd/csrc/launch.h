@@ -138,6 +138,9 @@ struct RedPiecesArgs {
   int np;
   MatArg tpiece[2];
   int has_t;
+  // bf16 copy in MFMA fragment order (see EpiStoreF32), cols % 16 == 0
+  MatArg frag;
+  int has_frag;
 };
 hipError_t launch_reduce_pieces(const RedPiecesArgs& a, int members, hipStream_t s);
 
