@@ -33,7 +33,6 @@ namespace {
 
 constexpr int kRows = 128;          // output rows per workgroup (4 row blocks of 32)
 constexpr int kBK = 16;             // k per stage
-constexpr int kStages = 4;
 constexpr int kMBytes = kRows * kBK * 4;   // raw fp32 M tile per stage
 constexpr int kGBytes = kRows * kBK * 2;   // raw bf16 G tile per stage
 
@@ -43,6 +42,9 @@ template <int R>
 struct SweepLayout {
   static constexpr int kPieceBytes = R * kBK * 2;      // one bf16 piece of the factor
   static constexpr int kStageBytes = kMBytes + kGBytes + 2 * kPieceBytes;
+  // four stages in flight (five, with the waits covering them, measured slower
+  // at r = 256: 43 / 42 us against 42 / 42)
+  static constexpr int kStages = 4;
   static constexpr int kMInstr = kMBytes / 1024;       // 1 KB per copy instruction
   static constexpr int kGInstr = kGBytes / 1024;
   static constexpr int kPInstr = 2 * kPieceBytes / 1024;
@@ -56,6 +58,20 @@ struct SweepLayout {
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// wait until at most `later` stages of PER copies each are outstanding
+template <int PER>
+__device__ __forceinline__ void wait_later(int later) {
+  switch (later) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<PER>(); break;
+    case 2: wait_vm<2 * PER>(); break;
+    case 3: wait_vm<3 * PER>(); break;
+    case 4: wait_vm<4 * PER>(); break;
+    case 5: wait_vm<5 * PER>(); break;
+    default: wait_vm<6 * PER>(); break;
+  }
 }
 
 __device__ __forceinline__ float2 bf16x2_to_f32(uint32_t u) {
@@ -80,6 +96,7 @@ template <int R, bool TRANS>
 __global__ __launch_bounds__(512, 1) void dion_sweep_kernel(SweepArgs a) {
   using L = SweepLayout<R>;
   using namespace fast;
+  constexpr int kStages = L::kStages;
   __shared__ __attribute__((aligned(1024))) char smem[kStages * L::kStageBytes];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -179,18 +196,9 @@ __global__ __launch_bounds__(512, 1) void dion_sweep_kernel(SweepArgs a) {
   };
   // wait until at most `later` stages of this wave's copies are outstanding
   auto wait_stages = [&](int later) {
-    static_assert(kStages <= 5, "wait cases cover up to three later stages");
-    if (ncopy == L::kLo) {
-      if (later >= 3) wait_vm<3 * L::kLo>();
-      else if (later == 2) wait_vm<2 * L::kLo>();
-      else if (later == 1) wait_vm<L::kLo>();
-      else wait_vm<0>();
-    } else {
-      if (later >= 3) wait_vm<3 * L::kMaxPerWave>();
-      else if (later == 2) wait_vm<2 * L::kMaxPerWave>();
-      else if (later == 1) wait_vm<L::kMaxPerWave>();
-      else wait_vm<0>();
-    }
+    static_assert(kStages <= 8 && 6 * L::kMaxPerWave < 64, "wait cases cover up to six later stages");
+    if (ncopy == L::kLo) wait_later<L::kLo>(later);
+    else wait_later<L::kMaxPerWave>(later);
   };
 
   // wave (rb, ch): output rows rb * 32 .. + 31, columns ch * R / 2 .. + R / 2 - 1
