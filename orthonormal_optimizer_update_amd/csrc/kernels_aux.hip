@@ -834,7 +834,7 @@ __global__ __launch_bounds__(256) void gram64_kernel(Gram64Args a) {
 // k step's fragments are read while this step's products run.  Same output as
 // gram64_kernel: slice blockIdx.y of part, element (row, col) at row * r + col.
 // grid (T (T + 1) / 2 tiles, splits, members), T = r / 128.
-__global__ __launch_bounds__(256) void gram64_big_kernel(Gram64Args a) {
+__global__ __launch_bounds__(512) void gram64_big_kernel(Gram64Args a) {
   constexpr int kPitch = 144;
   __shared__ __attribute__((aligned(16))) float sa[2][32 * kPitch];
   __shared__ __attribute__((aligned(16))) float sb[2][32 * kPitch];
@@ -852,15 +852,17 @@ __global__ __launch_bounds__(256) void gram64_big_kernel(Gram64Args a) {
   const int kbeg = blockIdx.y * a.kchunk;
   const int kend = min(a.m, kbeg + a.kchunk);
   const int nk = kend > kbeg ? (kend - kbeg + 31) / 32 : 0;
+  // eight waves, two per SIMD: wave (wa, wb) owns rows 32 wa .. + 31 and
+  // columns 64 wb .. + 63 of the tile
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wa = wave >> 1, wb = wave & 1;
-  // thread: float4 at column 4 (tid & 31) of k rows (tid >> 5) + 8 q
+  // thread: float4 at column 4 (tid & 31) of k rows (tid >> 5) + 16 q
   const int lc = (threadIdx.x & 31) * 4, lk = threadIdx.x >> 5;
-  floatx4 va[4], vb[4];
+  floatx4 va[2], vb[2];
   auto load = [&](int k0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int gk = k0 + lk + 8 * q;
+    for (int q = 0; q < 2; ++q) {
+      const int gk = k0 + lk + 16 * q;
       const bool ok = gk < kend;
       const float* row = P + (int64_t)(ok ? gk : kbeg) * a.p.ld;
       const floatx4 x = *reinterpret_cast<const floatx4*>(row + a0 + lc);
@@ -873,14 +875,14 @@ __global__ __launch_bounds__(256) void gram64_big_kernel(Gram64Args a) {
   };
   auto store = [&](int st) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      *reinterpret_cast<floatx4*>(&sa[st][(lk + 8 * q) * kPitch + lc]) = va[q];
-      if (!diag) *reinterpret_cast<floatx4*>(&sb[st][(lk + 8 * q) * kPitch + lc]) = vb[q];
+    for (int q = 0; q < 2; ++q) {
+      *reinterpret_cast<floatx4*>(&sa[st][(lk + 16 * q) * kPitch + lc]) = va[q];
+      if (!diag) *reinterpret_cast<floatx4*>(&sb[st][(lk + 16 * q) * kPitch + lc]) = vb[q];
     }
   };
-  doublex4 acc[4][4];
+  doublex4 acc[2][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = doublex4{0.0, 0.0, 0.0, 0.0};
   if (nk > 0) {
@@ -895,10 +897,10 @@ __global__ __launch_bounds__(256) void gram64_big_kernel(Gram64Args a) {
     if (more) load(kbeg + (kt + 1) * 32);
     const float* A = sa[cur];
     const float* B = diag ? sa[cur] : sb[cur];
-    double af[2][4], bf[2][4];
+    double af[2][2], bf[2][4];
     auto frags = [&](int buf, int kk) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[buf][i] = static_cast<double>(A[(kk + fk) * kPitch + wa * 64 + i * 16 + fc]);
+      for (int i = 0; i < 2; ++i) af[buf][i] = static_cast<double>(A[(kk + fk) * kPitch + wa * 32 + i * 16 + fc]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) bf[buf][j] = static_cast<double>(B[(kk + fk) * kPitch + wb * 64 + j * 16 + fc]);
     };
@@ -907,7 +909,7 @@ __global__ __launch_bounds__(256) void gram64_big_kernel(Gram64Args a) {
     for (int s = 0; s < 8; ++s) {
       if (s < 7) frags((s + 1) & 1, (s + 1) * 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[s & 1][i], bf[s & 1][j], acc[i][j], 0, 0, 0);
@@ -915,12 +917,12 @@ __global__ __launch_bounds__(256) void gram64_big_kernel(Gram64Args a) {
     if (more) store(cur ^ 1);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = a0 + wa * 64 + i * 16 + fk + 4 * e;
+        const int row = a0 + wa * 32 + i * 16 + fk + 4 * e;
         const int col = b0 + wb * 64 + j * 16 + fc;
         part[(int64_t)row * r + col] = acc[i][j][e];
       }
@@ -1761,7 +1763,7 @@ hipError_t launch_gram64(const Gram64Args& a, int splits, int members, hipStream
   if (a.r % 128 == 0 && a.r >= 1024 && a.kchunk % 32 == 0 && a.p.vec && a.p.ld % 4 == 0) {
     const int tb = a.r / 128;
     dim3 grid(tb * (tb + 1) / 2, splits, members);
-    hipLaunchKernelGGL(gram64_big_kernel, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(gram64_big_kernel, grid, dim3(512), 0, s, a);
     return hipGetLastError();
   }
   const int tb = cdiv(a.r, 64);
