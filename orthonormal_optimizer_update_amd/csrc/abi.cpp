@@ -188,6 +188,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     Gram64Args ga{};
     ga.p = tPt; ga.part = part_d; ga.part_member_stride = static_cast<int64_t>(mb / 8);
     ga.slice = static_cast<int64_t>(r) * r; ga.m = mi; ga.r = r; ga.kchunk = pl.kchunk_gram;
+    ga.big = pl.gram_big;
     ORTHO_TRY(launch_gram64(ga, pl.split_gram, nb, s));
     CholArgs ca{};
     ca.part = part_d; ca.part_member_stride = static_cast<int64_t>(mb / 8);

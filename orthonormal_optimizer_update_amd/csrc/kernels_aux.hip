@@ -1759,8 +1759,8 @@ hipError_t launch_ns_linear(const NsPolyArgs& a, int members, hipStream_t s) {
 }
 
 hipError_t launch_gram64(const Gram64Args& a, int splits, int members, hipStream_t s) {
-  // 128 x 128 tiles from r = 1024 on (the plan splits k for them)
-  if (a.r % 128 == 0 && a.r >= 1024 && a.kchunk % 32 == 0 && a.p.vec && a.p.ld % 4 == 0) {
+  // 128 x 128 tiles where the plan chose them (and split k for them)
+  if (a.big && a.r % 128 == 0 && a.kchunk % 32 == 0 && a.p.vec && a.p.ld % 4 == 0) {
     const int tb = a.r / 128;
     dim3 grid(tb * (tb + 1) / 2, splits, members);
     hipLaunchKernelGGL(gram64_big_kernel, grid, dim3(512), 0, s, a);

@@ -55,6 +55,7 @@ struct Gram64Args {
   int64_t part_member_stride;
   int64_t slice;
   int m, r, kchunk;
+  int big;             // 128 x 128 tiles (r % 128 == 0; the plan's split is for them)
 };
 
 struct CholArgs {

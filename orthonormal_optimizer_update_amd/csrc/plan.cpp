@@ -85,10 +85,10 @@ bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* p) {
   const bool small_gram = tg * (tg + 1) / 2 * d.chunk < 64;
   choose_split(m, tg * (tg + 1) / 2, d.chunk, &d.split_gram, &d.kchunk_gram,
                small_gram ? kMinSplitKSmall : kMinSplitK);
-  if (r % 128 == 0 && r >= 1024) {
-    // 128 x 128 fp64 Gram tiles (from 36 tiles on; fewer leave the chip
-    // idle): at most one workgroup per CU (a second round on a few CUs would
-    // double the time), at least eight 32-row k tiles each
+  d.gram_big = gram_big_tiles(r, d.chunk);
+  if (d.gram_big) {
+    // 128 x 128 fp64 Gram tiles: at most one workgroup per CU (a second round
+    // on a few CUs would double the time), at least eight 32-row k tiles each
     const int64_t tb = r / 128, tiles = tb * (tb + 1) / 2 * d.chunk;
     int64_t want = 256 / tiles, cap = m / 256;
     if (cap < 1) cap = 1;

@@ -19,6 +19,14 @@ inline bool gram_tn_small_tiles(int r) { return r < 512; }
 // A contraction with fewer than 64 output tiles of 128 x 128 over a launch's
 // members leaves most of the chip idle: the Dion sweeps then run on 64 x 64
 // tiles (k 64 deep), and every split-K reduction may cut k down to 64.
+// The fp64 Gram of P~ on 128 x 128 tiles (eight waves each) from r = 1024 on
+// (at r = 512 the 64 x 64 tiles were faster, batched or not: 12-layer GPT
+// groups 468 against 434 us per call).
+inline bool gram_big_tiles(int r, int members) {
+  (void)members;
+  return r % 128 == 0 && r >= 1024;
+}
+
 inline bool few_tiles(int64_t rows, int64_t cols, int members) {
   return ((rows + 127) / 128) * ((cols + 127) / 128) * members < 64;
 }
@@ -34,6 +42,7 @@ struct DionPlan {
   int split_right, kchunk_right;  // B^T P: split over m
   int split_gram, kchunk_gram;    // fp64 P^T P: split over m
   int split_gram2, kchunk_gram2;  // bf16x3 P1^T P1 (correction pass): split over m
+  int gram_big;                   // fp64 Gram on 128 x 128 tiles (gram_big_tiles)
   int small_left, small_right;    // sweeps on 64 x 64 tiles (few_tiles), kchunk a multiple of 64
   int nrb;                   // 64-row blocks of R (column-norm partials)
   size_t off_pt, off_p1, off_part, off_s, off_x, off_d, off_tt, off_r, off_colsq;

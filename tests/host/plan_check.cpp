@@ -92,6 +92,7 @@ static void check_dion(int64_t m, int64_t n, int r, int batch) {
   if (p.small_left) EXPECT(p.kchunk_left % 64 == 0, "small left kchunk %d", p.kchunk_left);
   if (p.small_right) EXPECT(p.kchunk_right % 64 == 0, "small right kchunk %d", p.kchunk_right);
   check_split("gram", m, p.split_gram, p.kchunk_gram, 32, m, n, r);
+  EXPECT(p.gram_big == gram_big_tiles(r, p.chunk), "fp64 Gram tile choice (r %d chunk %d)", r, p.chunk);
   check_split("gram2", m, p.split_gram2, p.kchunk_gram2, gram_tn_small_tiles(r) ? 64 : 32, m, n, r);
   // every split-K partial set that goes through the shared partial buffer
   size_t part = std::max({(size_t)p.split_left * mr * 4, (size_t)p.split_right * nr * 4,
