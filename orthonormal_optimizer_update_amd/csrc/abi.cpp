@@ -88,8 +88,9 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     double* part_d = reinterpret_cast<double*>(base + pl.off_part);
     // bf16 pieces of the orthonormalisation products on the 256 x 256 kernel:
     // A pieces (m x r) in the row-major B-piece buffer and B pieces (r x r) in
-    // the second one, both free once sweep 1 is done (3 r <= n; m, r multiples
-    // of 256, so every piece starts 256-byte aligned).
+    // the second one, both free once sweep 1 is done (3 r <= n), or in regions
+    // of their own with the streaming sweeps; m, r multiples of 256, so every
+    // piece starts 256-byte aligned.
     MatArg ap[3], bp[3];
     for (int k = 0; k < 3; ++k) {
       ap[k] = ws_table(base, mb, pl.off_bhi + k * static_cast<size_t>(mi) * r * 2, nb, r, mi, r, 2, 16);
@@ -141,8 +142,8 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       }
     }
 
-    // Streaming sweeps (bf16 weights, r = 64, 128 or 256): the pieces of Q^T,
-    // then one pass over M and G into split-K slices.
+    // Streaming sweeps (bf16 weights, r = 64, 128, 256 or 512): the pieces of
+    // Q^T, then one pass over M and G into split-K slices.
     SweepArgs sw{};
     bool stream_sw = false;
     if (bf && !fast_sw && pl.stream_sweeps) {
@@ -154,16 +155,30 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       sw.rows = mi; sw.K = ni; sw.r = r; sw.kchunk = pl.kchunk_sl; sw.M_rows = mi;
       stream_sw = dion_sweep_ok(sw, nb);
     }
+    // orthonormalisation products on the 256 x 256 kernel over bf16 pieces
+    const bool fast_or = bf && pl.fast_ortho && (fast_sw || stream_sw);
     if (stream_sw) {
       SplitTArgs qa{};
       qa.src = tQ; qa.hit = sw.f[0]; qa.lot = sw.f[1]; qa.rows = ni; qa.cols = r; qa.blocked = 1;
       ORTHO_TRY(launch_split_t(qa, nb, s));
       ORTHO_TRY(launch_dion_sweep(sw, false, nb, s));
-      RedArgs ra{};
-      ra.part = part_f; ra.part_member_stride = static_cast<int64_t>(mb / 4);
-      ra.slice = m * r; ra.splits = pl.split_sl; ra.rows = mi; ra.cols = r;
-      ra.out = tPt; ra.colsq = nullptr; ra.colsq_member_stride = 0;
-      ORTHO_TRY(launch_reduce_splits(ra, nb, s));
+      if (fast_or) {
+        // the reduce also writes the bf16x3 pieces of P_tilde for P1 = P~ T1
+        RedPiecesArgs ra{};
+        ra.part = part_f; ra.part_member_stride = static_cast<int64_t>(mb / 4);
+        ra.slice = m * r; ra.splits = pl.split_sl; ra.rows = mi; ra.cols = r;
+        ra.out = tPt; ra.has_out = 1;
+        for (int k = 0; k < 3; ++k) ra.piece[k] = ap[k];
+        ra.np = 3;
+        ORTHO_TRY(launch_reduce_pieces(ra, nb, s));
+        pt_pieces = true;
+      } else {
+        RedArgs ra{};
+        ra.part = part_f; ra.part_member_stride = static_cast<int64_t>(mb / 4);
+        ra.slice = m * r; ra.splits = pl.split_sl; ra.rows = mi; ra.cols = r;
+        ra.out = tPt; ra.colsq = nullptr; ra.colsq_member_stride = 0;
+        ORTHO_TRY(launch_reduce_splits(ra, nb, s));
+      }
     }
 
     // Sweep 1: P_tilde = (M + G) Q.
@@ -200,7 +215,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     ca.r = r; ca.status = status;
     float* tt = reinterpret_cast<float*>(base + pl.off_tt);
     ORTHO_TRY(launch_cholesky_inverse(ca, tt, static_cast<int64_t>(mb / 4), nb, s));
-    if (fast_sw && pl.fast_ortho) {
+    if (fast_or) {
       // The same three products on the 256 x 256 kernel over bf16 pieces
       // (split-K, fixed-order reduces that also write the next product's
       // pieces).
@@ -252,6 +267,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       rp2.slice = mr; rp2.splits = pl.split_ap3; rp2.rows = mi; rp2.cols = r;
       rp2.out = tPt; rp2.has_out = 1; rp2.out_bf16 = tPb; rp2.has_bf16 = 1;
       rp2.tpiece[0] = tPhiT; rp2.tpiece[1] = tPloT; rp2.has_t = 1;
+      rp2.t_blocked = stream_sw;   // the streaming sweep 2 reads them k-blocked
       if (pl.frag_p) {
         rp2.frag = ws_table(base, mb, pl.off_pf, nb, r, mi, r, 2, 16);
         rp2.has_frag = 1;

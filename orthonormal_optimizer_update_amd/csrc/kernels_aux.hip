@@ -245,8 +245,13 @@ __global__ __launch_bounds__(256) void reduce_pieces_kernel(RedPiecesArgs a) {
       h[e] = th[j][i4 + e];
       l[e] = tl[j][i4 + e];
     }
-    *reinterpret_cast<uint2*>(hit + (int64_t)(c0 + j) * a.tpiece[0].ld + r0 + i4) = pack4(h);
-    *reinterpret_cast<uint2*>(lot + (int64_t)(c0 + j) * a.tpiece[1].ld + r0 + i4) = pack4(l);
+    // four consecutive rows r0 + i4 .. + 3 of column c0 + j: contiguous in both
+    // layouts (i4 % 4 == 0, so they share one 16-row block)
+    const int64_t ot = a.t_blocked
+        ? (int64_t)((r0 + i4) >> 4) * a.cols * 16 + (int64_t)(c0 + j) * 16 + ((r0 + i4) & 15)
+        : (int64_t)(c0 + j) * a.tpiece[0].ld + r0 + i4;
+    *reinterpret_cast<uint2*>(hit + ot) = pack4(h);
+    *reinterpret_cast<uint2*>(lot + ot) = pack4(l);
   }
 }
 

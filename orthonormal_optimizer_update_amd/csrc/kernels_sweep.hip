@@ -1,5 +1,5 @@
 // Dion's two power-iteration sweeps over B = M + G for bf16 weights and a
-// rank r of 64, 128 or 256 (MSR talk "Dion: The distributed orthonormal update
+// rank r of 64, 128, 256 or 512 (MSR talk "Dion: The distributed orthonormal update
 // revolution is here", passage on amortised power iteration):
 //   left  (sweep 1):  P~ = B Q      (m x r, reduction over the n columns of B)
 //   right (sweep 2):  R  = B^T P    (n x r, reduction over the m rows of B)
@@ -19,7 +19,14 @@
 // The fp32 result of every slice goes to the split-K partial buffer, summed
 // in a fixed order by the reduce kernel that follows.
 //
-// Requirements (checked by the launcher): r in {64, 128, 256}; m and n
+// At r = 512 a wave holds eight 32 x 32 accumulators, and a 44 KB stage
+// leaves room for three stages in LDS.  To keep two waves per SIMD within the
+// register file, the factor fragments of a stage are held once (not double
+// buffered): the hi*lo products run first, the next stage's lo fragments and
+// A fragment are read under the hi*hi and lo*hi products, and its hi
+// fragments after them.
+//
+// Requirements (checked by the launcher): r in {64, 128, 256, 512}; m and n
 // multiples of 64; M and G rows 16-byte aligned; the factor pieces k-blocked
 // (split_t with blocked set); kchunk a multiple of 16.
 #include <type_traits>
@@ -43,8 +50,8 @@ struct SweepLayout {
   static constexpr int kPieceBytes = R * kBK * 2;      // one bf16 piece of the factor
   static constexpr int kStageBytes = kMBytes + kGBytes + 2 * kPieceBytes;
   // four stages in flight (five, with the waits covering them, measured slower
-  // at r = 256: 43 / 42 us against 42 / 42)
-  static constexpr int kStages = 4;
+  // at r = 256: 43 / 42 us against 42 / 42); three at r = 512 (132 KB)
+  static constexpr int kStages = R == 512 ? 3 : 4;
   static constexpr int kMInstr = kMBytes / 1024;       // 1 KB per copy instruction
   static constexpr int kGInstr = kGBytes / 1024;
   static constexpr int kPInstr = 2 * kPieceBytes / 1024;
@@ -214,14 +221,26 @@ __global__ __launch_bounds__(512, 1) void dion_sweep_kernel(SweepArgs a) {
   // and the NB column blocks of both factor pieces.
   const int fr = lane & 31, half = lane >> 5;
   const int rl = rb * 32 + fr;
-  bf16x8 fa[2][2], fb[2][NB][2];
-  auto read_frags = [&](int st, auto buf_c) {
-    constexpr int buf = decltype(buf_c)::value;
+  // R <= 256: both stages' factor fragments in registers (fb[buf]); R = 512:
+  // one stage's (fb[0]), refilled piece by piece
+  constexpr int kFbBufs = R == 512 ? 1 : 2;
+  bf16x8 fa[2][2], fb[kFbBufs][NB][2];
+  // the factor fragments of piece `pc` of stage st into fb[buf]
+  auto read_factor = [&](int st, int buf, int pc) {
+    const char* sp = smem + (st % kStages) * L::kStageBytes + kMBytes + kGBytes;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int fj = ch * (R / 2) + j * 32 + fr;
+      const int o = fj * 32 + ((half ^ ((fj >> 3) & 1)) * 16);
+      fb[buf][j][pc] = *reinterpret_cast<const bf16x8*>(sp + pc * L::kPieceBytes + o);
+    }
+  };
+  // the A fragment of stage st into fa[buf]: B = M + G split into hi and lo
+  auto read_a = [&](int st, int buf) {
     const char* sb = smem + (st % kStages) * L::kStageBytes;
     const float* sm = reinterpret_cast<const float*>(sb);
     const uint16_t* sg = reinterpret_cast<const uint16_t*>(sb + kMBytes);
-    const char* sp = sb + kMBytes + kGBytes;
-    // A fragment: output row rl, k = half*8 .. + 7 of the stage
+    // output row rl, k = half*8 .. + 7 of the stage
     float x[8];
     if (!TRANS) {
       const floatx4 m0 = *reinterpret_cast<const floatx4*>(sm + rl * 16 + (((2 * half) ^ ((rl >> 2) & 3)) * 4));
@@ -239,13 +258,12 @@ __global__ __launch_bounds__(512, 1) void dion_sweep_kernel(SweepArgs a) {
       }
     }
     split8(x, fa[buf][0], fa[buf][1]);
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int fj = ch * (R / 2) + j * 32 + fr;
-      const int o = fj * 32 + ((half ^ ((fj >> 3) & 1)) * 16);
-      fb[buf][j][0] = *reinterpret_cast<const bf16x8*>(sp + o);
-      fb[buf][j][1] = *reinterpret_cast<const bf16x8*>(sp + L::kPieceBytes + o);
-    }
+  };
+  auto read_frags = [&](int st, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    read_a(st, buf);
+    read_factor(st, buf, 0);
+    read_factor(st, buf, 1);
   };
   // wait until this wave's copies of stage `st` are done (at most the stages
   // issued after it still outstanding), then the barrier makes every wave's
@@ -263,7 +281,13 @@ __global__ __launch_bounds__(512, 1) void dion_sweep_kernel(SweepArgs a) {
     if (st < nst) issue(st);
   int issued_last = min(kStages - 2, nst - 1);
   ready(0, issued_last);
-  read_frags(0, std::integral_constant<int, 0>{});
+  if constexpr (R == 512) {
+    read_a(0, 0);
+    read_factor(0, 0, 0);
+    read_factor(0, 0, 1);
+  } else {
+    read_frags(0, std::integral_constant<int, 0>{});
+  }
 
   // one stage whose fragments are in buffer CUR (a compile-time index, so the
   // fragments stay in registers); the next stage's go to buffer CUR ^ 1
@@ -290,9 +314,42 @@ __global__ __launch_bounds__(512, 1) void dion_sweep_kernel(SweepArgs a) {
     for (int j = 0; j < NB; ++j)
       acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[CUR][1], fb[CUR][j][0], acc[j], 0, 0, 0);
   };
+  // r = 512: fa[CUR] and fb[0] hold stage st on entry
+  auto step512 = [&](auto cur_c, int st) {
+    constexpr int CUR = decltype(cur_c)::value;
+    const bool more = st + 1 < nst;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[CUR][0], fb[0][j][1], acc[j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) {
+      ready(st + 1, issued_last);
+      if (st + kStages - 1 < nst) {
+        issue(st + kStages - 1);
+        issued_last = st + kStages - 1;
+      }
+      read_a(st + 1, CUR ^ 1);
+      read_factor(st + 1, 0, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[CUR][0], fb[0][j][0], acc[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[CUR][1], fb[0][j][0], acc[j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) read_factor(st + 1, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
   for (int st = 0; st < nst; st += 2) {
-    step(std::integral_constant<int, 0>{}, st);
-    if (st + 1 < nst) step(std::integral_constant<int, 1>{}, st + 1);
+    if constexpr (R == 512) {
+      step512(std::integral_constant<int, 0>{}, st);
+      if (st + 1 < nst) step512(std::integral_constant<int, 1>{}, st + 1);
+    } else {
+      step(std::integral_constant<int, 0>{}, st);
+      if (st + 1 < nst) step(std::integral_constant<int, 1>{}, st + 1);
+    }
   }
 
   // slice `split` of the partial result, rows row0 + rb*32 .. + 31
@@ -309,7 +366,7 @@ __global__ __launch_bounds__(512, 1) void dion_sweep_kernel(SweepArgs a) {
 }
 
 bool dion_sweep_ok(const SweepArgs& a, int members) {
-  if (a.r != 64 && a.r != 128 && a.r != 256) return false;
+  if (a.r != 64 && a.r != 128 && a.r != 256 && a.r != 512) return false;
   if (a.rows % 64 != 0 || a.K % 64 != 0 || a.kchunk % kBK != 0 || a.kchunk < kBK) return false;
   if (a.m.ld % 4 != 0 || a.g.ld % 8 != 0) return false;
   // 32-bit per-lane offsets: every source the copies address spans < 4 GiB
@@ -331,7 +388,8 @@ hipError_t launch_dion_sweep(const SweepArgs& a, bool trans, int members, hipStr
   } while (0)
   if (a.r == 64) ORTHO_SWEEP(64);
   else if (a.r == 128) ORTHO_SWEEP(128);
-  else ORTHO_SWEEP(256);
+  else if (a.r == 256) ORTHO_SWEEP(256);
+  else ORTHO_SWEEP(512);
 #undef ORTHO_SWEEP
   return hipGetLastError();
 }

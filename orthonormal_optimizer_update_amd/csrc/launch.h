@@ -139,6 +139,9 @@ struct RedPiecesArgs {
   int np;
   MatArg tpiece[2];
   int has_t;
+  // transposed pieces k-blocked, as the streaming sweeps read them: element
+  // (j, i) (column j, row i of the result) at (i / 16) * cols * 16 + j * 16 + i % 16
+  int t_blocked;
   // bf16 copy in MFMA fragment order (see EpiStoreF32), cols % 16 == 0
   MatArg frag;
   int has_frag;

@@ -117,10 +117,10 @@ bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* p) {
   if (pr > part) part = pr;
   if (pg > part) part = pg;
   if (pg2 > part) part = pg2;
-  // From r = 512 on the sweeps are product-bound and the pieces pass pays for
-  // itself; below, the fused loaders (which also leave M and G in the
-  // Infinity Cache for the last sweep) are as fast.
-  d.fast_sweeps = m % 256 == 0 && n % 256 == 0 && r % 256 == 0 && r >= 512;
+  // Up to r = 512 the sweeps stream M and G (below); from r = 1024 on they
+  // are product-bound and a pass that stores the pieces of B pays for itself.
+  d.stream_sweeps = (r == 64 || r == 128 || r == 256 || r == 512) && m % 64 == 0 && n % 64 == 0;
+  d.fast_sweeps = !d.stream_sweeps && m % 256 == 0 && n % 256 == 0 && r % 256 == 0 && r >= 512;
   if (d.fast_sweeps) {
     choose_split_tiles(3 * n / 64, (m / 256) * (r / 256), d.chunk, &d.split_fl, &d.kchunk_fl);
     choose_split_tiles(3 * m / 64, (n / 256) * (r / 256), d.chunk, &d.split_fr, &d.kchunk_fr);
@@ -128,19 +128,21 @@ bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* p) {
     const size_t pfr = static_cast<size_t>(d.split_fr) * nr * 4;
     if (pfl > part) part = pfl;
     if (pfr > part) part = pfr;
-    // three m x r (and r x r) piece sets fit in one m x n piece buffer
-    d.fast_ortho = 3 * r <= n;
-    if (d.fast_ortho) {
-      choose_split_tiles(6 * r / 64, (m / 256) * (r / 256), d.chunk, &d.split_ap6, &d.kchunk_ap6);
-      choose_split_tiles(3 * r / 64, (m / 256) * (r / 256), d.chunk, &d.split_ap3, &d.kchunk_ap3);
-      choose_split_tiles(3 * m / 64, (r / 256) * (r / 256), d.chunk, &d.split_e, &d.kchunk_e);
-      const size_t pa = static_cast<size_t>(d.split_ap6 > d.split_ap3 ? d.split_ap6 : d.split_ap3) * mr * 4;
-      const size_t pe = static_cast<size_t>(d.split_e) * rr * 4;
-      if (pa > part) part = pa;
-      if (pe > part) part = pe;
-    }
   }
-  d.stream_sweeps = (r == 64 || r == 128 || r == 256) && m % 64 == 0 && n % 64 == 0;
+  // The orthonormalisation products on the 256 x 256 kernel: with the piece
+  // sweeps, their pieces live in the B-piece buffers (three m x r and r x r
+  // sets fit when 3 r <= n); with the streaming sweeps at r = 512, in regions
+  // of their own.
+  d.fast_ortho = (d.fast_sweeps || (d.stream_sweeps && r == 512 && m % 256 == 0)) && 3 * r <= n;
+  if (d.fast_ortho) {
+    choose_split_tiles(6 * r / 64, (m / 256) * (r / 256), d.chunk, &d.split_ap6, &d.kchunk_ap6);
+    choose_split_tiles(3 * r / 64, (m / 256) * (r / 256), d.chunk, &d.split_ap3, &d.kchunk_ap3);
+    choose_split_tiles(3 * m / 64, (r / 256) * (r / 256), d.chunk, &d.split_e, &d.kchunk_e);
+    const size_t pa = static_cast<size_t>(d.split_ap6 > d.split_ap3 ? d.split_ap6 : d.split_ap3) * mr * 4;
+    const size_t pe = static_cast<size_t>(d.split_e) * rr * 4;
+    if (pa > part) part = pa;
+    if (pe > part) part = pe;
+  }
   if (d.stream_sweeps) {
     // one 128-row workgroup per CU over the chunk's members, at least 128 k
     // (eight 16-deep stages) per slice
@@ -181,6 +183,10 @@ bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* p) {
     d.off_blo = o;   o = align_up(o + mn2);
     d.off_bhit = o;  o = align_up(o + mn2);
     d.off_blot = o;  o = align_up(o + mn2);
+  } else if (d.fast_ortho) {
+    // the three m x r and r x r piece sets of the orthonormalisation products
+    d.off_bhi = o;   o = align_up(o + 3 * mr * 2);
+    d.off_blo = o;   o = align_up(o + 3 * rr * 2);
   }
   if (d.fast_sweeps || d.stream_sweeps) {
     d.off_qhit = o;  o = align_up(o + nr * 2);

@@ -53,19 +53,21 @@ struct DionPlan {
   // (((i / 32) * r / 16 + k / 16) * 64 + i % 32 + 32 * (k / 8 % 2)) * 8 + k % 8)
   bool frag_p;
   size_t off_pf;
-  // Sweeps on the 256 x 256 kernel (m, n, r multiples of 256, bf16 weights):
+  // Sweeps on the 256 x 256 kernel (m, n, r multiples of 256, r >= 768, bf16 weights):
   // bf16x2 pieces of B = M + G (m x n) and B^T, of Q^T (r x n) and of P^T (r x m),
   // and split-K factors in k tiles of the three-segment reductions.
   bool fast_sweeps;
   int split_fl, kchunk_fl, split_fr, kchunk_fr;
-  // Streaming sweeps (r = 64, 128 or 256, m and n multiples of 64, bf16
+  // Streaming sweeps (r = 64, 128, 256 or 512, m and n multiples of 64, bf16
   // weights): split-K factors of sweep 1 (over n) and sweep 2 (over m), with
   // the transposed bf16 pieces of Q and P in off_qhit.. off_plot.
   bool stream_sweeps;
   int split_sl, kchunk_sl, split_sr, kchunk_sr;
   size_t off_bhi, off_blo, off_bhit, off_blot, off_qhit, off_qlot, off_phit, off_plot;
-  // Orthonormalisation products on the 256 x 256 kernel (with fast_sweeps and
-  // 3 r <= n): bf16 pieces in the B-piece buffers, free between the sweeps.
+  // Orthonormalisation products on the 256 x 256 kernel (with fast_sweeps, or
+  // with the streaming sweeps at r = 512 and m a multiple of 256; and 3 r <= n):
+  // bf16 pieces in the B-piece buffers, free between the sweeps, or (streaming)
+  // in off_bhi (three m x r sets) and off_blo (three r x r sets).
   int fast_ortho;
   int split_ap6, kchunk_ap6;  // P1 = P~ T1, six segments of r
   int split_ap3, kchunk_ap3;  // P = P1 T2, three segments of r

@@ -97,23 +97,26 @@ static void check_dion(int64_t m, int64_t n, int r, int batch) {
   // every split-K partial set that goes through the shared partial buffer
   size_t part = std::max({(size_t)p.split_left * mr * 4, (size_t)p.split_right * nr * 4,
                           (size_t)p.split_gram * rr * 8, (size_t)p.split_gram2 * rr * 4});
+  const bool stream = (r == 64 || r == 128 || r == 256 || r == 512) && m % 64 == 0 && n % 64 == 0;
+  EXPECT(p.stream_sweeps == stream, "stream sweeps flag on %lld x %lld r %d", (long long)m,
+         (long long)n, r);
+  EXPECT(p.fast_sweeps == (!stream && m % 256 == 0 && n % 256 == 0 && r % 256 == 0 && r >= 512),
+         "fast sweeps flag on %lld x %lld r %d", (long long)m, (long long)n, r);
+  EXPECT(!!p.fast_ortho == ((p.fast_sweeps || (stream && r == 512 && m % 256 == 0)) && 3 * r <= n),
+         "fast orthonormalisation flag on %lld x %lld r %d", (long long)m, (long long)n, r);
   if (p.fast_sweeps) {
-    EXPECT(m % 256 == 0 && n % 256 == 0 && r % 256 == 0 && r >= 512, "fast sweeps on %lld x %lld r %d",
-           (long long)m, (long long)n, r);
     check_split("fast left", 3 * n / 64, p.split_fl, p.kchunk_fl, 1, m, n, r);
     check_split("fast right", 3 * m / 64, p.split_fr, p.kchunk_fr, 1, m, n, r);
     part = std::max({part, (size_t)p.split_fl * mr * 4, (size_t)p.split_fr * nr * 4});
-    if (p.fast_ortho) {
-      check_split("ap6", 6 * r / 64, p.split_ap6, p.kchunk_ap6, 1, m, n, r);
-      check_split("ap3", 3 * r / 64, p.split_ap3, p.kchunk_ap3, 1, m, n, r);
-      check_split("e", 3 * m / 64, p.split_e, p.kchunk_e, 1, m, n, r);
-      part = std::max({part, (size_t)std::max(p.split_ap6, p.split_ap3) * mr * 4,
-                       (size_t)p.split_e * rr * 4});
-    }
+  }
+  if (p.fast_ortho) {
+    check_split("ap6", 6 * r / 64, p.split_ap6, p.kchunk_ap6, 1, m, n, r);
+    check_split("ap3", 3 * r / 64, p.split_ap3, p.kchunk_ap3, 1, m, n, r);
+    check_split("e", 3 * m / 64, p.split_e, p.kchunk_e, 1, m, n, r);
+    part = std::max({part, (size_t)std::max(p.split_ap6, p.split_ap3) * mr * 4,
+                     (size_t)p.split_e * rr * 4});
   }
   if (p.stream_sweeps) {
-    EXPECT((r == 64 || r == 128 || r == 256) && m % 64 == 0 && n % 64 == 0,
-           "stream sweeps on %lld x %lld r %d", (long long)m, (long long)n, r);
     check_split("stream left", n, p.split_sl, p.kchunk_sl, 16, m, n, r);
     check_split("stream right", m, p.split_sr, p.kchunk_sr, 16, m, n, r);
     part = std::max({part, (size_t)p.split_sl * mr * 4, (size_t)p.split_sr * nr * 4});
@@ -128,10 +131,14 @@ static void check_dion(int64_t m, int64_t n, int r, int batch) {
       {"qb", p.off_qb, (size_t)n * p.rpb * 2},
       {"pf", p.off_pf, p.frag_p ? mr * 2 : 0}};
   EXPECT(p.frag_p == ((r == 256 || r == 512) && m % 128 == 0), "fragment-order P flag");
-  if (p.fast_sweeps)
+  if (p.fast_sweeps) {
     for (auto pr : {std::make_pair("bhi", p.off_bhi), std::make_pair("blo", p.off_blo),
                     std::make_pair("bhit", p.off_bhit), std::make_pair("blot", p.off_blot)})
       rs.push_back({pr.first, pr.second, (size_t)m * n * 2});
+  } else if (p.fast_ortho) {
+    rs.push_back({"ortho a pieces", p.off_bhi, 3 * mr * 2});
+    rs.push_back({"ortho b pieces", p.off_blo, 3 * rr * 2});
+  }
   if (p.fast_sweeps || p.stream_sweeps) {
     rs.push_back({"qhit", p.off_qhit, nr * 2});
     rs.push_back({"qlot", p.off_qlot, nr * 2});

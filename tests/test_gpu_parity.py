@@ -128,13 +128,16 @@ DION_SHAPES = [(96, 80, 16), (300, 200, 37), (513, 257, 64), (128, 1000, 128), (
                # two-accumulator kernel (1152 rows: not 256-divisible)
                (384, 352, 256), (640, 1056, 512), (768, 1024, 512), (1152, 2048, 1024)]
 
-# bf16: the streaming sweeps (r = 64, 128, 256 with both sides multiples of 64),
-# with a last row tile of 64 rows, and r = m = n.  (fp32 weights take the
-# generic sweeps; on the last two shapes their P~ is conditioned badly enough
-# that fp32-accurate products land at 1.1e-4 and 1.7e-4 against the fp64
-# oracle, above the fp32 bar.)
+# bf16: the streaming sweeps (r = 64, 128, 256, 512 with both sides multiples
+# of 64), with a last row tile of 64 rows, and r = m = n; at r = 512 with the
+# orthonormalisation products on the 256 x 256 kernel (m a multiple of 256,
+# 3 r <= n: the first reduce writes P~'s pieces, the last one P's transposed
+# pieces k-blocked) and without them (576 rows).  (fp32 weights take the
+# generic sweeps; on (256, 256, 256) and (1024, 512, 256) their P~ is
+# conditioned badly enough that fp32-accurate products land at 1.1e-4 and
+# 1.7e-4 against the fp64 oracle, above the fp32 bar.)
 STREAM_SHAPES = [(384, 320, 64), (320, 448, 128), (576, 768, 256), (256, 256, 256),
-                 (1024, 512, 256)]
+                 (1024, 512, 256), (512, 1536, 512), (1024, 2048, 512), (576, 1024, 512)]
 
 
 @pytest.mark.parametrize("shape", STREAM_SHAPES)
