@@ -123,11 +123,13 @@ hipError_t dion_update_bf16(const DionUpdateArgs& a, int members, hipStream_t s)
   // r = 512 with P in fragment order: the streaming kernel
   if (a.rank == 512 && a.has_pf && dion_update_stream_ok(a, members))
     return launch_dion_update_stream(a, members, s);
-  // From r = 512 on, the products weigh enough that the 256 x 256 pair is the
-  // fastest (12-layer GPT groups at r = 512: 15.7 ms per step against 16.5 with
-  // the streaming kernel); at r = 256 the step is bound by its 14 mn bytes and
-  // the streaming kernel (memory terms loaded under the products, 16-byte
-  // accesses) is; the two-accumulator 256 x 128 kernel takes every other case.
+  // From r = 768 on (and at r = 512 without the fragment-order P) the products
+  // weigh enough that the 256 x 256 pair is the fastest (12-layer GPT groups at
+  // r = 512: 15.7 ms per step against 16.5 with the streaming kernel reading P
+  // row by row; 15.1 against 15.4 once it read the fragment-order copy); at
+  // r = 256 the step is bound by its 14 mn bytes and the streaming kernel
+  // (memory terms loaded under the products, 16-byte accesses) is; the
+  // two-accumulator 256 x 128 kernel takes every other case.
   if (a.rank >= 512 && fast_ok(a.M, a.N, a.rank, a.pb, a.rb) && a.qb.vec && a.qb.ld % 8 == 0 &&
       rows16(a.m, members, 4) && rows16(a.g, members, 2) && rows16(a.x, members, 2)) {
     // two launches of the 256 x 256 kernel: momentum, then weight

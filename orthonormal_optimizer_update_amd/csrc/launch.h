@@ -186,7 +186,7 @@ struct DionRightArgs {
 };
 hipError_t launch_dion_right(const DionRightArgs& a, bool bf16, int members, hipStream_t s);
 
-// Dion sweeps for bf16 weights at r = 64, 128 or 256 (kernels_sweep.hip):
+// Dion sweeps for bf16 weights at r = 64, 128, 256 or 512 (kernels_sweep.hip):
 // trans = false: out = (M + G) F^T, out rows = rows of M (sweep 1, F = Q^T);
 // trans = true:  out = (M + G)^T F^T, out rows = columns of M (sweep 2, F = P^T).
 // F is given as two bf16 pieces (hi, lo), r x K k-blocked as split_t writes
