@@ -214,6 +214,44 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     ca.mat_stride = static_cast<int64_t>(mb / 8); ca.vec_stride = static_cast<int64_t>(mb / 8);
     ca.r = r; ca.status = status;
     float* tt = reinterpret_cast<float*>(base + pl.off_tt);
+    // P ends up in tP (off_p): tPt, or tP1 when the fp64 pass writes it
+    MatArg tP = tPt;
+    size_t off_p = pl.off_pt;
+    if (pl.ortho64) {
+      // T1^T in fp64 into the scaled-Gram region (free once the chain is
+      // done), then P = P~ T1 in one pass of fp64 products into tP1, with the
+      // bf16 copy the update reads
+      double* ttd = reinterpret_cast<double*>(base + pl.off_s);
+      ORTHO_TRY(launch_cholesky_inverse(ca, nullptr, 0, nb, s, ttd, static_cast<int64_t>(mb / 8)));
+      Apply64Args a64{};
+      a64.pt = tPt; a64.t = ttd; a64.t_member_stride = static_cast<int64_t>(mb / 8);
+      a64.out = tP1; a64.out_bf16 = tPb; a64.has_bf16 = bf; a64.m = mi; a64.r = r;
+      ORTHO_TRY(launch_apply64(a64, nb, s));
+      tP = tP1;
+      off_p = pl.off_p1;
+      // the fragment-order copy (streaming update) and the transposed pieces
+      // (sweep 2: k-blocked for the streaming kernel, ld m for the 256 x 256
+      // one); every path that reads them has m and r multiples of 64
+      const bool need_frag = bf && pl.frag_p;
+      const bool need_t = stream_sw || fast_sw;
+      if (need_frag || need_t) {
+        RedPiecesArgs rd{};
+        rd.part = reinterpret_cast<const float*>(base + pl.off_p1);
+        rd.part_member_stride = static_cast<int64_t>(mb / 4);
+        rd.slice = m * r; rd.splits = 1; rd.rows = mi; rd.cols = r;
+        if (need_t) {
+          rd.tpiece[0] = ws_table(base, mb, pl.off_phit, nb, m, r, mi, 2, 16);
+          rd.tpiece[1] = ws_table(base, mb, pl.off_plot, nb, m, r, mi, 2, 16);
+          rd.has_t = 1;
+          rd.t_blocked = stream_sw;
+        }
+        if (need_frag) {
+          rd.frag = ws_table(base, mb, pl.off_pf, nb, r, mi, r, 2, 16);
+          rd.has_frag = 1;
+        }
+        ORTHO_TRY(launch_reduce_pieces(rd, nb, s));
+      }
+    } else {
     ORTHO_TRY(launch_cholesky_inverse(ca, tt, static_cast<int64_t>(mb / 4), nb, s));
     if (fast_or) {
       // The same three products on the 256 x 256 kernel over bf16 pieces
@@ -300,6 +338,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     }
     ORTHO_TRY(launch_apply_t(aa, false, nb, s));
     }
+    }
 
     // Sweep 2: R = (M + G)^T P, then Q' = column-normalised R.
     int split_r = pl.split_right;
@@ -309,7 +348,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       const MatArg tBloT = ws_table(base, mb, pl.off_blot, nb, m, ni, mi, 2, 16);
       const MatArg tPhiT = ws_table(base, mb, pl.off_phit, nb, m, r, mi, 2, 16);
       const MatArg tPloT = ws_table(base, mb, pl.off_plot, nb, m, r, mi, 2, 16);
-      if (!pl.fast_ortho) {  // else the last orthonormalisation reduce wrote them
+      if (!pl.fast_ortho && !pl.ortho64) {  // else the last orthonormalisation reduce wrote them
         SplitTArgs pa{};
         pa.src = tPt; pa.hit = tPhiT; pa.lot = tPloT; pa.rows = mi; pa.cols = r;
         ORTHO_TRY(launch_split_t(pa, nb, s));
@@ -333,7 +372,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       split_r = pl.split_sr;
     } else {
       DionRightArgs rb{};
-      rb.m = tM; rb.g = tG; rb.p = tPt; rb.out = tPart;
+      rb.m = tM; rb.g = tG; rb.p = tP; rb.out = tPart;
       rb.split_stride = n * r;
       rb.M = mi; rb.N = ni; rb.r = r;
       rb.splits = pl.split_right; rb.kchunk = pl.kchunk_right; rb.small = pl.small_right;
@@ -353,7 +392,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     ORTHO_TRY(launch_colnorm(cn, nb, s));
 
     if (P_out)
-      ORTHO_TRY(hipMemcpy2DAsync(P_out->data, P_out->ld * 4, base + pl.off_pt, rp * 4, r * 4, m,
+      ORTHO_TRY(hipMemcpy2DAsync(P_out->data, P_out->ld * 4, base + off_p, rp * 4, r * 4, m,
                                  hipMemcpyDeviceToDevice, s));
     if (R_out)
       ORTHO_TRY(hipMemcpy2DAsync(R_out->data, R_out->ld * 4, base + pl.off_r, rp * 4, r * 4, n,
@@ -361,7 +400,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
 
     // Sweep 3: error feedback into M and the weight update into X.
     DionUpdateArgs ua{};
-    ua.p = tPt; ua.r = tR; ua.q = tQ; ua.m = tM; ua.g = tG; ua.x = tX;
+    ua.p = tP; ua.r = tR; ua.q = tQ; ua.m = tM; ua.g = tG; ua.x = tX;
     ua.pb = tPb; ua.rb = tRb; ua.qb = tQb;
     // the fragment-order P, written by the last orthonormalisation product or
     // its reduce

@@ -1564,20 +1564,27 @@ __global__ __launch_bounds__(256) void chol_update_kernel(CholArgs a, int kb) {
 // the right factor of P1 = P_tilde T with T = D L^{-T} upper triangular.
 // Diagonal tiles of X are L_jj^{-1}; a tile below the diagonal is formed as
 // X_jk = L_jj^{-1} Y_jk from the Y block the factorisation left there.
-__global__ __launch_bounds__(256) void make_t_kernel(CholArgs a, float* tt, int64_t tt_stride) {
+// T1^T = (D L^-T)^T, lower triangular r x r (ld r, zeros above the diagonal):
+// into tt as fp32 and / or into ttd as fp64 (either may be null).
+__global__ __launch_bounds__(256) void make_t_kernel(CholArgs a, float* tt, int64_t tt_stride,
+                                                     double* ttd, int64_t ttd_stride) {
   __shared__ double sT[2][64][kCP];
   const int member = blockIdx.z;
   const double* X = a.x + member * a.mat_stride;
   const double* d = a.d + member * a.vec_stride;
-  float* out = tt + member * tt_stride;
+  float* out = tt ? tt + member * tt_stride : nullptr;
+  double* outd = ttd ? ttd + member * ttd_stride : nullptr;
   const int r = a.r;
   const int jb = blockIdx.y, kb = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (kb >= jb) {
     for (int q = 0; q < 16; ++q) {
       const int j = jb * 64 + q * 4 + wave, k = kb * 64 + lane;
-      if (j < r && k < r)
-        out[(int64_t)j * r + k] = (kb == jb && k <= j) ? static_cast<float>(X[(int64_t)j * r + k] * d[k]) : 0.f;
+      if (j < r && k < r) {
+        const double v = (kb == jb && k <= j) ? X[(int64_t)j * r + k] * d[k] : 0.0;
+        if (out) out[(int64_t)j * r + k] = static_cast<float>(v);
+        if (outd) outd[(int64_t)j * r + k] = v;
+      }
     }
     return;
   }
@@ -1598,7 +1605,104 @@ __global__ __launch_bounds__(256) void make_t_kernel(CholArgs a, float* tt, int6
       for (int e = 0; e < 4; ++e) {
         const int j = jb * 64 + wa * 32 + i * 16 + (lane >> 4) + 4 * e;
         const int k = kb * 64 + wb * 32 + jj * 16 + (lane & 15);
-        if (j < r && k < r) out[(int64_t)j * r + k] = static_cast<float>(acc[i][jj][e] * d[k]);
+        if (j < r && k < r) {
+          const double v = acc[i][jj][e] * d[k];
+          if (out) out[(int64_t)j * r + k] = static_cast<float>(v);
+          if (outd) outd[(int64_t)j * r + k] = v;
+        }
+      }
+}
+
+// P = P~ T1 with fp64 products, T1 given as T1^T (lower triangular, fp64, ld r):
+// P[i][j] = sum over k <= j of P~[i][k] T1^T[j][k].  With T1 from the fp64
+// Cholesky of the fp64 Gram and the products in fp64, the columns of P are
+// orthonormal to about cond(P~)^2 2^-53 before the final rounding to fp32, so
+// no correction pass follows.  64 x 64 output tiles, four waves of 32 x 32
+// (2 x 2 fp64 16x16x4 products), k in tiles of 32 up to the tile's last
+// column (T1 is upper triangular); both operands staged in LDS k-major as
+// fp64 (P~ widened on the way), the next k tile loaded into registers while
+// this one's products run.  Tiles of the last column block first: they carry
+// the longest k range.  grid (tiles_i * tiles_j, members).
+__global__ __launch_bounds__(256) void apply64_kernel(Apply64Args a) {
+  __shared__ double sa[2][32][66];
+  __shared__ double sb[2][32][66];
+  const int member = blockIdx.y;
+  const float* P = static_cast<const float*>(a.pt.p[member]);
+  const double* T = a.t + member * a.t_member_stride;
+  const int m = a.m, r = a.r;
+  const int tiles_i = (m + 63) / 64, tiles_j = (r + 63) / 64;
+  const int jt = tiles_j - 1 - static_cast<int>(blockIdx.x) / tiles_i;
+  const int it = static_cast<int>(blockIdx.x) % tiles_i;
+  const int i0 = it * 64, j0 = jt * 64;
+  const int kend = min(r, j0 + 64);
+  const int nk = (kend + 31) / 32;
+  const int64_t ldp = a.pt.ld;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wa = wave >> 1, wb = wave & 1;
+  // thread: elements e = tid + 256 q of each 64 x 32 operand tile, row e / 32,
+  // k e % 32 (a row's 32 k contiguous in global memory)
+  float va[8];
+  double vb[8];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int e = threadIdx.x + q * 256;
+      const int row = e >> 5, kk = e & 31, k = k0 + kk;
+      const bool okk = k < kend;
+      va[q] = (okk && i0 + row < m) ? P[(int64_t)(i0 + row) * ldp + k] : 0.f;
+      vb[q] = (okk && j0 + row < r) ? T[(int64_t)(j0 + row) * r + k] : 0.0;
+    }
+  };
+  auto store = [&](int st) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int e = threadIdx.x + q * 256;
+      sa[st][e & 31][e >> 5] = static_cast<double>(va[q]);
+      sb[st][e & 31][e >> 5] = vb[q];
+    }
+  };
+  doublex4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = doublex4{0.0, 0.0, 0.0, 0.0};
+  load(0);
+  store(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    __syncthreads();
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) load((kt + 1) * 32);
+#pragma unroll
+    for (int kk = 0; kk < 32; kk += 4) {
+      double af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) af[i] = sa[cur][kk + (lane >> 4)][wa * 32 + i * 16 + (lane & 15)];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bf[j] = sb[cur][kk + (lane >> 4)][wb * 32 + j * 16 + (lane & 15)];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) store(cur ^ 1);
+  }
+  float* out = static_cast<float*>(const_cast<void*>(a.out.p[member]));
+  uint16_t* ob = a.has_bf16 ? static_cast<uint16_t*>(const_cast<void*>(a.out_bf16.p[member])) : nullptr;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = i0 + wa * 32 + i * 16 + (lane >> 4) + 4 * e;
+        const int col = j0 + wb * 32 + j * 16 + (lane & 15);
+        if (row < m && col < r) {
+          const float v = static_cast<float>(acc[i][j][e]);
+          out[(int64_t)row * a.out.ld + col] = v;
+          if (ob) ob[(int64_t)row * a.out_bf16.ld + col] = to_bf16_bits(v);
+        }
       }
 }
 
@@ -1779,7 +1883,7 @@ hipError_t launch_gram64(const Gram64Args& a, int splits, int members, hipStream
 
 // Cholesky of the scaled Gram, its inverse, and T^T, for every member.
 hipError_t launch_cholesky_inverse(const CholArgs& a, float* tt, int64_t tt_stride, int members,
-                                   hipStream_t s) {
+                                   hipStream_t s, double* ttd, int64_t ttd_stride) {
   const int r = a.r, nblk = cdiv(r, 64);
   hipLaunchKernelGGL(chol_prep_kernel, dim3(cdiv(r, 16), cdiv(r, 16), members), dim3(256), 0, s, a);
   // Block 0 is factored on its own; block kb + 1 is factored by the update
@@ -1790,7 +1894,15 @@ hipError_t launch_cholesky_inverse(const CholArgs& a, float* tt, int64_t tt_stri
     const int nupd = T * (T + 1) / 2 + T * (kb + 1);
     hipLaunchKernelGGL(chol_update_kernel, dim3(nupd, members), dim3(256), 0, s, a, kb);
   }
-  hipLaunchKernelGGL(make_t_kernel, dim3(nblk, nblk, members), dim3(256), 0, s, a, tt, tt_stride);
+  hipLaunchKernelGGL(make_t_kernel, dim3(nblk, nblk, members), dim3(256), 0, s, a, tt, tt_stride,
+                     ttd, ttd_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_apply64(const Apply64Args& a, int members, hipStream_t s) {
+  if (a.m < 1 || a.r < 1 || a.t == nullptr) return hipErrorInvalidValue;
+  const int tiles = cdiv(a.m, 64) * cdiv(a.r, 64);
+  hipLaunchKernelGGL(apply64_kernel, dim3(tiles, members), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

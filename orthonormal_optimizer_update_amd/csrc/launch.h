@@ -157,8 +157,22 @@ hipError_t launch_ns_init(const NsInitArgs& a, int members, bool bf16, hipStream
 hipError_t launch_ns_store(const NsInitArgs& a, const MatArg& out, int members, bool bf16,
                            hipStream_t s);
 hipError_t launch_gram64(const Gram64Args& a, int splits, int members, hipStream_t s);
+// P = P~ T1 with fp64 products (apply64_kernel): t holds T1^T, r x r fp64,
+// lower triangular (ld r), as make_t writes it into ttd.
+struct Apply64Args {
+  MatArg pt;                  // fp32 m x r
+  const double* t;            // member 0's T1^T
+  int64_t t_member_stride;
+  MatArg out;                 // fp32 m x r (must not alias pt)
+  MatArg out_bf16;            // optional bf16 copy (has_bf16)
+  int has_bf16;
+  int m, r;
+};
+hipError_t launch_apply64(const Apply64Args& a, int members, hipStream_t s);
+
+// T1^T into tt (fp32) and / or ttd (fp64, when not null).
 hipError_t launch_cholesky_inverse(const CholArgs& a, float* tt, int64_t tt_stride, int members,
-                                   hipStream_t s);
+                                   hipStream_t s, double* ttd = nullptr, int64_t ttd_stride = 0);
 
 // --- GEMM-family sweeps (kernels_gemm.hip) ---------------------------------
 

@@ -133,7 +133,9 @@ bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* p) {
   // sweeps, their pieces live in the B-piece buffers (three m x r and r x r
   // sets fit when 3 r <= n); with the streaming sweeps at r = 512, in regions
   // of their own.
-  d.fast_ortho = (d.fast_sweeps || (d.stream_sweeps && r == 512 && m % 256 == 0)) && 3 * r <= n;
+  d.ortho64 = r <= kOrtho64MaxRank;
+  d.fast_ortho = !d.ortho64 && (d.fast_sweeps || (d.stream_sweeps && r == 512 && m % 256 == 0)) &&
+                 3 * r <= n;
   if (d.fast_ortho) {
     choose_split_tiles(6 * r / 64, (m / 256) * (r / 256), d.chunk, &d.split_ap6, &d.kchunk_ap6);
     choose_split_tiles(3 * r / 64, (m / 256) * (r / 256), d.chunk, &d.split_ap3, &d.kchunk_ap3);

@@ -11,6 +11,8 @@ namespace ortho {
 
 constexpr int kMaxMembersPerLaunch = 32;  // must match kMaxBatch in common.h
 constexpr size_t kWsAlign = 256;
+// Largest rank whose orthonormalisation takes one fp64 pass (apply64).
+constexpr int kOrtho64MaxRank = 2048;
 
 // P1^T P1 of the correction pass runs on 64 x 64 tiles below this rank (a
 // 256 x 256 result is only 4 tiles of 128); the plan sizes its split for them.
@@ -64,6 +66,10 @@ struct DionPlan {
   bool stream_sweeps;
   int split_sl, kchunk_sl, split_sr, kchunk_sr;
   size_t off_bhi, off_blo, off_bhit, off_blot, off_qhit, off_qlot, off_phit, off_plot;
+  // P = P~ T1 in one pass of fp64 products (apply64), T1^T in fp64 in the
+  // scaled-Gram region and P in off_p1, for r <= kOrtho64MaxRank; above it the
+  // two passes over bf16 pieces (first-order correction) below.
+  bool ortho64;
   // Orthonormalisation products on the 256 x 256 kernel (with fast_sweeps, or
   // with the streaming sweeps at r = 512 and m a multiple of 256; and 3 r <= n):
   // bf16 pieces in the B-piece buffers, free between the sweeps, or (streaming)

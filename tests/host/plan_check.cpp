@@ -102,7 +102,9 @@ static void check_dion(int64_t m, int64_t n, int r, int batch) {
          (long long)n, r);
   EXPECT(p.fast_sweeps == (!stream && m % 256 == 0 && n % 256 == 0 && r % 256 == 0 && r >= 512),
          "fast sweeps flag on %lld x %lld r %d", (long long)m, (long long)n, r);
-  EXPECT(!!p.fast_ortho == ((p.fast_sweeps || (stream && r == 512 && m % 256 == 0)) && 3 * r <= n),
+  EXPECT(p.ortho64 == (r <= kOrtho64MaxRank), "fp64 orthonormalisation flag for r %d", r);
+  EXPECT(!!p.fast_ortho == (!p.ortho64 && (p.fast_sweeps || (stream && r == 512 && m % 256 == 0)) &&
+                            3 * r <= n),
          "fast orthonormalisation flag on %lld x %lld r %d", (long long)m, (long long)n, r);
   if (p.fast_sweeps) {
     check_split("fast left", 3 * n / 64, p.split_fl, p.kchunk_fl, 1, m, n, r);
