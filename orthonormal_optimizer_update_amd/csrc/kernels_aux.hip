@@ -1,5 +1,7 @@
 // Reductions, normalisations and the small dense r x r linear algebra of the
 // Dion orthonormalisation, for gfx950.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -1640,25 +1642,31 @@ __global__ __launch_bounds__(256) void apply64_kernel(Apply64Args a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wa = wave >> 1, wb = wave & 1;
   // thread: elements e = tid + 256 q of each 64 x 32 operand tile, row e / 32,
-  // k e % 32 (a row's 32 k contiguous in global memory)
-  float va[8];
-  double vb[8];
-  auto load = [&](int k0) {
+  // k e % 32 (a row's 32 k contiguous in global memory).  Loads are
+  // branch-free (addresses clamped into the operands, out-of-range values
+  // selected to zero) and run two k tiles ahead, into alternating register sets.
+  float va[2][8];
+  double vb[2][8];
+  auto load = [&](auto buf_c, int k0) {
+    constexpr int buf = decltype(buf_c)::value;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int e = threadIdx.x + q * 256;
-      const int row = e >> 5, kk = e & 31, k = k0 + kk;
-      const bool okk = k < kend;
-      va[q] = (okk && i0 + row < m) ? P[(int64_t)(i0 + row) * ldp + k] : 0.f;
-      vb[q] = (okk && j0 + row < r) ? T[(int64_t)(j0 + row) * r + k] : 0.0;
+      const int row = e >> 5, k = k0 + (e & 31);
+      const int kc = min(k, kend - 1);
+      const float x = P[(int64_t)min(i0 + row, m - 1) * ldp + kc];
+      const double y = T[(int64_t)min(j0 + row, r - 1) * r + kc];
+      va[buf][q] = (k < kend && i0 + row < m) ? x : 0.f;
+      vb[buf][q] = (k < kend && j0 + row < r) ? y : 0.0;
     }
   };
-  auto store = [&](int st) {
+  auto store = [&](int st, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int e = threadIdx.x + q * 256;
-      sa[st][e & 31][e >> 5] = static_cast<double>(va[q]);
-      sb[st][e & 31][e >> 5] = vb[q];
+      sa[st][e & 31][e >> 5] = static_cast<double>(va[buf][q]);
+      sb[st][e & 31][e >> 5] = vb[buf][q];
     }
   };
   doublex4 acc[2][2];
@@ -1666,27 +1674,41 @@ __global__ __launch_bounds__(256) void apply64_kernel(Apply64Args a) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = doublex4{0.0, 0.0, 0.0, 0.0};
-  load(0);
-  store(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    __syncthreads();
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  load(B0{}, 0);
+  if (nk > 1) load(B1{}, 32);
+  store(0, B0{});
+  // k tile kt from LDS stage kt & 1; on entry its registers (set kt & 1) are
+  // in LDS, and set (kt + 1) & 1 holds tile kt + 1 (or is in flight)
+  auto step = [&](int kt, auto set_c) {
+    constexpr int SET = decltype(set_c)::value;
     const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) load((kt + 1) * 32);
+    __syncthreads();
+    if (kt + 2 < nk) load(set_c, (kt + 2) * 32);
+    // fragments of the next 4-deep k step read while this step's products run
+    double af[2][2], bf[2][2];
+    auto frags = [&](int buf, int kk) {
 #pragma unroll
-    for (int kk = 0; kk < 32; kk += 4) {
-      double af[2], bf[2];
+      for (int i = 0; i < 2; ++i) af[buf][i] = sa[cur][kk + (lane >> 4)][wa * 32 + i * 16 + (lane & 15)];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = sa[cur][kk + (lane >> 4)][wa * 32 + i * 16 + (lane & 15)];
+      for (int j = 0; j < 2; ++j) bf[buf][j] = sb[cur][kk + (lane >> 4)][wb * 32 + j * 16 + (lane & 15)];
+    };
+    frags(0, 0);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bf[j] = sb[cur][kk + (lane >> 4)][wb * 32 + j * 16 + (lane & 15)];
+    for (int ks = 0; ks < 8; ++ks) {
+      if (ks + 1 < 8) frags((ks + 1) & 1, (ks + 1) * 4);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[i], bf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[ks & 1][i], bf[ks & 1][j], acc[i][j], 0, 0, 0);
     }
-    if (more) store(cur ^ 1);
+    if (kt + 1 < nk) store(cur ^ 1, std::integral_constant<int, SET ^ 1>{});
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, B0{});
+    if (kt + 1 < nk) step(kt + 1, B1{});
   }
   float* out = static_cast<float*>(const_cast<void*>(a.out.p[member]));
   uint16_t* ob = a.has_bf16 ? static_cast<uint16_t*>(const_cast<void*>(a.out_bf16.p[member])) : nullptr;
