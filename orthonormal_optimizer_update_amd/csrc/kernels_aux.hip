@@ -748,6 +748,10 @@ __global__ __launch_bounds__(256) void ns_linear_kernel(NsPolyArgs a) {
 // lane l is row l/16 + 4*e, column l%16 of the 16 x 16 tile (rows interleave
 // across the four result registers, unlike the fp32-result instructions).
 // ---------------------------------------------------------------------------
+// FULL: r a multiple of 64 and every k slice a whole number of 32-row tiles,
+// so no load needs a bounds check (the checked loads' selects let the compiler
+// sink each load into a branch of its own and wait for it there).
+template <bool FULL>
 __global__ __launch_bounds__(256) void gram64_kernel(Gram64Args a) {
   __shared__ double sa[2][32][66];
   __shared__ double sb[2][32][66];
@@ -768,26 +772,40 @@ __global__ __launch_bounds__(256) void gram64_kernel(Gram64Args a) {
   const int nk = kend > kbeg ? (kend - kbeg + 31) / 32 : 0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wa = wave >> 1, wb = wave & 1;
-  // each thread moves 8 elements of each 32 x 64 operand tile
-  float va[8], vb[8];
-  auto load = [&](int k0) {
+  // each thread moves 8 elements of each 32 x 64 operand tile.  Loads are
+  // branch-free (addresses clamped into P, out-of-range values selected to
+  // zero) and run two k tiles ahead, into alternating register sets.
+  float va[2][8], vb[2][8];
+  auto load = [&](auto buf_c, int k0) {
+    constexpr int buf = decltype(buf_c)::value;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int e = threadIdx.x + q * 256;
       const int kr = e >> 6, cc = e & 63;
       const int gk = k0 + kr;
-      const bool ok = gk < kend;
-      const float* row = P + (int64_t)gk * a.p.ld;
-      va[q] = (ok && a0 + cc < r) ? row[a0 + cc] : 0.f;
-      if (!diag) vb[q] = (ok && b0 + cc < r) ? row[b0 + cc] : 0.f;
+      if constexpr (FULL) {
+        const float* row = P + (int64_t)gk * a.p.ld;
+        va[buf][q] = row[a0 + cc];
+        vb[buf][q] = row[b0 + cc];
+      } else {
+        const bool ok = gk < kend;
+        const float* row = P + (int64_t)min(gk, kend - 1) * a.p.ld;
+        const float x = row[min(a0 + cc, r - 1)];
+        va[buf][q] = (ok && a0 + cc < r) ? x : 0.f;
+        if (!diag) {
+          const float y = row[min(b0 + cc, r - 1)];
+          vb[buf][q] = (ok && b0 + cc < r) ? y : 0.f;
+        }
+      }
     }
   };
-  auto store = [&](int st) {
+  auto store = [&](int st, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int e = threadIdx.x + q * 256;
-      sa[st][e >> 6][e & 63] = static_cast<double>(va[q]);
-      if (!diag) sb[st][e >> 6][e & 63] = static_cast<double>(vb[q]);
+      sa[st][e >> 6][e & 63] = static_cast<double>(va[buf][q]);
+      if (FULL || !diag) sb[st][e >> 6][e & 63] = static_cast<double>(vb[buf][q]);
     }
   };
   doublex4 acc[2][2];
@@ -795,31 +813,45 @@ __global__ __launch_bounds__(256) void gram64_kernel(Gram64Args a) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = doublex4{0.0, 0.0, 0.0, 0.0};
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
   if (nk > 0) {
-    load(kbeg);
-    store(0);
+    load(B0{}, kbeg);
+    if (nk > 1) load(B1{}, kbeg + 32);
+    store(0, B0{});
   }
-  for (int kt = 0; kt < nk; ++kt) {
-    __syncthreads();
+  // k tile kt from LDS stage kt & 1; register set kt & 1 is free on entry and
+  // set (kt + 1) & 1 holds tile kt + 1 (or has it in flight)
+  auto step = [&](int kt, auto set_c) {
+    constexpr int SET = decltype(set_c)::value;
     const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) load(kbeg + (kt + 1) * 32);
+    __syncthreads();
+    if (kt + 2 < nk) load(set_c, kbeg + (kt + 2) * 32);
     double (*A)[66] = sa[cur];
     double (*B)[66] = diag ? sa[cur] : sb[cur];
+    // fragments of the next 4-deep k step read while this step's products run
+    double af[2][2], bf[2][2];
+    auto frags = [&](int buf, int kk) {
 #pragma unroll
-    for (int kk = 0; kk < 32; kk += 4) {
-      double af[2], bf[2];
+      for (int i = 0; i < 2; ++i) af[buf][i] = A[kk + (lane >> 4)][wa * 32 + i * 16 + (lane & 15)];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = A[kk + (lane >> 4)][wa * 32 + i * 16 + (lane & 15)];
+      for (int j = 0; j < 2; ++j) bf[buf][j] = B[kk + (lane >> 4)][wb * 32 + j * 16 + (lane & 15)];
+    };
+    frags(0, 0);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bf[j] = B[kk + (lane >> 4)][wb * 32 + j * 16 + (lane & 15)];
+    for (int ks = 0; ks < 8; ++ks) {
+      if (ks + 1 < 8) frags((ks + 1) & 1, (ks + 1) * 4);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[i], bf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[ks & 1][i], bf[ks & 1][j], acc[i][j], 0, 0, 0);
     }
-    if (more) store(cur ^ 1);
+    if (kt + 1 < nk) store(cur ^ 1, std::integral_constant<int, SET ^ 1>{});
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, B0{});
+    if (kt + 1 < nk) step(kt + 1, B1{});
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -1899,7 +1931,10 @@ hipError_t launch_gram64(const Gram64Args& a, int splits, int members, hipStream
   }
   const int tb = cdiv(a.r, 64);
   dim3 grid(tb * (tb + 1) / 2, splits, members);
-  hipLaunchKernelGGL(gram64_kernel, grid, dim3(256), 0, s, a);
+  // every tile and k slice whole: m and the slice length multiples of 32
+  const bool full = a.r % 64 == 0 && a.kchunk % 32 == 0 && a.m % 32 == 0;
+  if (full) hipLaunchKernelGGL(gram64_kernel<true>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(gram64_kernel<false>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
