@@ -138,8 +138,28 @@ struct LdRow {
         ld(a.ld), ld2(a2.ld), rows(a.rows), vec(a.vec && (!ADD || a2.vec)) {}
 
   // Without ADD, rows past the end load nothing: every column index is then
-  // past the zero limit.
+  // past the zero limit.  A tile wholly inside the source (a uniform test)
+  // takes plain vector loads: with the per-lane choice between the vector and
+  // the element-wise path, both ran under exec masks and each vector load
+  // waited for every load before it.
   __device__ __forceinline__ void load(int row0, int k0, int kend) {
+    if (vec && row0 + ROWS <= rows && k0 + BK <= kend) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int idx = threadIdx.x + c * NT;
+        const int r = idx / CPR, kc = (idx % CPR) * 4;
+        const SRC_T* src = p + (int64_t)(row0 + r) * ld + k0 + kc;
+        if constexpr (ADD) {
+          const float4 mv = raw_to_f4(*reinterpret_cast<const typename Raw4<SRC_T>::type*>(src));
+          const float4 g = raw_to_f4(*reinterpret_cast<const typename Raw4<SRC2_T>::type*>(
+              p2 + (int64_t)(row0 + r) * ld2 + k0 + kc));
+          vs[c] = make_float4(mv.x + g.x, mv.y + g.y, mv.z + g.z, mv.w + g.w);
+        } else {
+          v[c] = *reinterpret_cast<const typename Raw4<SRC_T>::type*>(src);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int idx = threadIdx.x + c * NT;
@@ -241,8 +261,30 @@ struct LdCol {
         ld(a.ld), ld2(a2.ld), rows(a.rows), vec(a.vec && (!ADD || a2.vec)) {}
 
   // Without ADD, source rows past kend load nothing: every column index is
-  // then past the zero limit.
+  // then past the zero limit.  A tile wholly inside the source takes plain
+  // vector loads (as in LdRow).
   __device__ __forceinline__ void load(int row0, int k0, int kend) {
+    if (vec && row0 + ROWS <= rows && k0 + BK <= kend) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int idx = threadIdx.x + c * NT;
+        const int jc = (idx % JC) * 4, kc = (idx / JC) * 4;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int64_t gk = k0 + kc + t;
+          const SRC_T* src = p + gk * ld + row0 + jc;
+          if constexpr (ADD) {
+            const float4 mv = raw_to_f4(*reinterpret_cast<const typename Raw4<SRC_T>::type*>(src));
+            const float4 g = raw_to_f4(
+                *reinterpret_cast<const typename Raw4<SRC2_T>::type*>(p2 + gk * ld2 + row0 + jc));
+            vs[c][t] = make_float4(mv.x + g.x, mv.y + g.y, mv.z + g.z, mv.w + g.w);
+          } else {
+            v[c][t] = *reinterpret_cast<const typename Raw4<SRC_T>::type*>(src);
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int idx = threadIdx.x + c * NT;
