@@ -98,6 +98,18 @@ __device__ __forceinline__ float4 load4<uint16_t>(const uint16_t* row, int c, in
   return make_float4(t[0], t[1], t[2], t[3]);
 }
 
+// Four consecutive elements as stored (fp32: float4, bf16 bits: uint2), and
+// their fp32 values.
+template <typename T> struct Raw4;
+template <> struct Raw4<float> { typedef float4 type; };
+template <> struct Raw4<uint16_t> { typedef uint2 type; };
+
+__device__ __forceinline__ float4 raw_to_f4(const float4& v) { return v; }
+__device__ __forceinline__ float4 raw_to_f4(const uint2& u) {
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+
 __device__ __forceinline__ float f4_get(const float4& v, int j) {
   return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
 }

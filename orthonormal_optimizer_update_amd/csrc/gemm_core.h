@@ -83,17 +83,14 @@ __device__ __forceinline__ void put4(bf16* s, int pstride, float a, float b, flo
   }
 }
 
-// Four consecutive elements as loaded, before any conversion: fp32 as a
-// float4, bf16 as the raw 8 bytes.  Loaders of one source keep this form until
-// store(), with rows outside the matrix masked by a zero limit rather than a
+// Four consecutive elements as loaded, before any conversion (Raw4: fp32 as
+// a float4, bf16 as the raw 8 bytes).  Loaders of one source keep this form
+// until store(), with rows outside the matrix masked by a zero limit rather than a
 // branch (measured: the triangular and correction applies of the
 // orthonormalisation 29 -> 24 us and 28 -> 22 us at 4096 x 256).  Loaders that
 // add two sources (M + G) add at load time: deferring that add to store()
 // measured slower (Dion sweeps at 4096 x 4096, r = 256: 81 -> 101 us and
 // 78 -> 89 us).
-template <typename T> struct Raw4;
-template <> struct Raw4<float> { typedef float4 type; };
-template <> struct Raw4<uint16_t> { typedef uint2 type; };
 
 template <typename T>
 __device__ __forceinline__ typename Raw4<T>::type load_raw4(const T* row, int c, int limit, bool vec);
@@ -110,11 +107,6 @@ __device__ __forceinline__ uint2 load_raw4<uint16_t>(const uint16_t* row, int c,
   return make_uint2(t[0] | (uint32_t(t[1]) << 16), t[2] | (uint32_t(t[3]) << 16));
 }
 
-__device__ __forceinline__ float4 raw_to_f4(const float4& v) { return v; }
-__device__ __forceinline__ float4 raw_to_f4(const uint2& u) {
-  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
-}
 
 // Row-major source, k contiguous: element (i, k) = S[i*ld + k].  The source
 // is SRC_T (float or bf16 bits); with ADD = true the element is
