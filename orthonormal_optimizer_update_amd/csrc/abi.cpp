@@ -197,14 +197,9 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       ORTHO_TRY(launch_reduce_splits(ra, nb, s));
     }
 
-    // Orthonormalisation of P_tilde (Q-factor of its thin QR, diag(R) > 0).
-    // Pass 1: fp64 Gram, column-scaled fp64 Cholesky and triangular inverse,
-    // P1 = P_tilde T1 with bf16x6 products (T1 = D L^-T, upper triangular).
-    Gram64Args ga{};
-    ga.p = tPt; ga.part = part_d; ga.part_member_stride = static_cast<int64_t>(mb / 8);
-    ga.slice = static_cast<int64_t>(r) * r; ga.m = mi; ga.r = r; ga.kchunk = pl.kchunk_gram;
-    ga.big = pl.gram_big;
-    ORTHO_TRY(launch_gram64(ga, pl.split_gram, nb, s));
+    // Orthonormalisation of P_tilde (Q-factor of its thin QR, diag(R) > 0):
+    // fp64 Gram, column-scaled fp64 Cholesky and triangular inverse, then
+    // P = P_tilde T1 (T1 = D L^-T, upper triangular).
     CholArgs ca{};
     ca.part = part_d; ca.part_member_stride = static_cast<int64_t>(mb / 8);
     ca.slice = static_cast<int64_t>(r) * r; ca.splits = pl.split_gram;
@@ -217,16 +212,30 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     // P ends up in tP (off_p): tPt, or tP1 when the fp64 pass writes it
     MatArg tP = tPt;
     size_t off_p = pl.off_pt;
-    if (pl.ortho64) {
-      // T1^T in fp64 into the scaled-Gram region (free once the chain is
-      // done), then P = P~ T1 in one pass of fp64 products into tP1, with the
-      // bf16 copy the update reads
-      double* ttd = reinterpret_cast<double*>(base + pl.off_s);
-      ORTHO_TRY(launch_cholesky_inverse(ca, nullptr, 0, nb, s, ttd, static_cast<int64_t>(mb / 8)));
-      Apply64Args a64{};
-      a64.pt = tPt; a64.t = ttd; a64.t_member_stride = static_cast<int64_t>(mb / 8);
-      a64.out = tP1; a64.out_bf16 = tPb; a64.has_bf16 = bf; a64.m = mi; a64.r = r;
-      ORTHO_TRY(launch_apply64(a64, nb, s));
+    if (!pl.small_ortho) {
+      Gram64Args ga{};
+      ga.p = tPt; ga.part = part_d; ga.part_member_stride = static_cast<int64_t>(mb / 8);
+      ga.slice = static_cast<int64_t>(r) * r; ga.m = mi; ga.r = r; ga.kchunk = pl.kchunk_gram;
+      ga.big = pl.gram_big;
+      ORTHO_TRY(launch_gram64(ga, pl.split_gram, nb, s));
+    }
+    if (pl.small_ortho || pl.ortho64) {
+      if (pl.small_ortho) {
+        // r <= 64 and a short P~: the whole chain in one workgroup per member
+        SmallOrthoArgs so{};
+        so.pt = tPt; so.out = tP1; so.out_bf16 = tPb; so.has_bf16 = bf; so.m = mi; so.ca = ca;
+        ORTHO_TRY(launch_small_ortho(so, nb, s));
+      } else {
+        // T1^T in fp64 into the scaled-Gram region (free once the chain is
+        // done), then P = P~ T1 in one pass of fp64 products into tP1, with
+        // the bf16 copy the update reads
+        double* ttd = reinterpret_cast<double*>(base + pl.off_s);
+        ORTHO_TRY(launch_cholesky_inverse(ca, nullptr, 0, nb, s, ttd, static_cast<int64_t>(mb / 8)));
+        Apply64Args a64{};
+        a64.pt = tPt; a64.t = ttd; a64.t_member_stride = static_cast<int64_t>(mb / 8);
+        a64.out = tP1; a64.out_bf16 = tPb; a64.has_bf16 = bf; a64.m = mi; a64.r = r;
+        ORTHO_TRY(launch_apply64(a64, nb, s));
+      }
       tP = tP1;
       off_p = pl.off_p1;
       // the fragment-order copy (streaming update) and the transposed pieces

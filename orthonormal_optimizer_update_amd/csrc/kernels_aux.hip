@@ -1335,6 +1335,174 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(CholArgs a, int kb) {
   chol_diag_factor(a, kb, blockIdx.x, LY, dinv);
 }
 
+// The whole orthonormalisation of a rank of at most 64 in one workgroup per
+// member, for short P~ (m <= 256; the small-problem chain of separate launches
+// is latency, not work): P~ is read once into LDS (fp32, every load in flight
+// together), then the fp64 Gram W = P~^T P~ (2 x 2 waves of 32 x 32 fp64
+// 16x16x4 products, operands widened as they are read), the column scaling
+// d = diag(W)^-1/2, the 64 x 64 Cholesky and inverse in LDS
+// (chol_diag_factor), T1^T = L^-1 D in place, and P = P~ T1 in fp64 (the
+// products of a wave stop at its last column: T1 is upper triangular).  Same
+// steps, in the same precisions, as the multi-launch chain with the fp64
+// apply.  grid (members).
+constexpr int kSoPitch = 68;   // floats per LDS row of P~: 16 consecutive rows at one k on distinct banks
+__global__ __launch_bounds__(256) void small_ortho_kernel(SmallOrthoArgs a) {
+  __shared__ double LY[2][64][kCP];
+  __shared__ float sp[256 * kSoPitch];
+  __shared__ double dinv[64], dsc[64];
+  const int member = blockIdx.x;
+  const float* P = static_cast<const float*>(a.pt.p[member]);
+  const int64_t ldp = a.pt.ld;
+  const int m = a.m, r = a.ca.r;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int wa = wave >> 1, wb = wave & 1;
+  double (*L)[kCP] = LY[0];
+  double (*Y)[kCP] = LY[1];
+
+  // 0. P~ (m x r, zero-padded to 64 columns and to a multiple of 16 rows) into
+  // LDS, every load of a thread issued before any store: float4 loads when the
+  // rows allow them (a uniform test), else element-wise in passes of 64 rows
+  const int mp = (m + 15) & ~15;
+  if (a.pt.vec && (r & 3) == 0 && (ldp & 3) == 0) {
+    float4 v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = threadIdx.x + q * 256;
+      const int i = e >> 4, c4 = (e & 15) * 4;
+      const float4 x = *reinterpret_cast<const float4*>(P + (int64_t)min(i, m - 1) * ldp + min(c4, r - 4));
+      v[q] = (i < m && c4 < r) ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = threadIdx.x + q * 256;
+      const int i = e >> 4, c4 = (e & 15) * 4;
+      if (i < mp) *reinterpret_cast<float4*>(sp + i * kSoPitch + c4) = v[q];
+    }
+  } else {
+    for (int r0 = 0; r0 < mp; r0 += 64) {
+      float v[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int e = threadIdx.x + q * 256;
+        const int i = r0 + (e >> 6), c = e & 63;
+        const float x = P[(int64_t)min(i, m - 1) * ldp + min(c, r - 1)];
+        v[q] = (i < m && c < r) ? x : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int e = threadIdx.x + q * 256;
+        const int i = r0 + (e >> 6);
+        if (i < mp) sp[i * kSoPitch + (e & 63)] = v[q];
+      }
+    }
+  }
+  __syncthreads();
+
+  // 1. W = P~^T P~, the 10 lower 16 x 16 blocks: each wave over a quarter of
+  // the rows of P~ (fragments of the next 4-deep k step read under the current
+  // products), then the four partial sums added into L in wave order
+  {
+    constexpr int kBI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+    constexpr int kBJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+    doublex4 w[10];
+#pragma unroll
+    for (int b = 0; b < 10; ++b) w[b] = doublex4{0.0, 0.0, 0.0, 0.0};
+    const int quarter = mp / 4;   // a multiple of 4
+    const int kb0 = wave * quarter;
+    double f[2][4];
+    auto frags = [&](int buf, int kk) {
+      const float* row = sp + (kb0 + kk + (lane >> 4)) * kSoPitch + (lane & 15);
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) f[buf][bi] = static_cast<double>(row[bi * 16]);
+    };
+    if (quarter > 0) frags(0, 0);
+    for (int kk = 0; kk < quarter; kk += 8) {
+      if (kk + 4 < quarter) frags(1, kk + 4);
+#pragma unroll
+      for (int b = 0; b < 10; ++b)
+        w[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(f[0][kBI[b]], f[0][kBJ[b]], w[b], 0, 0, 0);
+      if (kk + 4 >= quarter) break;
+      if (kk + 8 < quarter) frags(0, kk + 8);
+#pragma unroll
+      for (int b = 0; b < 10; ++b)
+        w[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(f[1][kBI[b]], f[1][kBJ[b]], w[b], 0, 0, 0);
+    }
+    for (int src = 0; src < 4; ++src) {
+      if (wave == src) {
+#pragma unroll
+        for (int b = 0; b < 10; ++b)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            double& dst = L[kBI[b] * 16 + (lane >> 4) + 4 * e][kBJ[b] * 16 + (lane & 15)];
+            dst = src == 0 ? w[b][e] : dst + w[b][e];
+          }
+      }
+      __syncthreads();
+    }
+  }
+  // 2. d_i = W_ii^-1/2 (1 for a zero column or padding); L = the scaled lower
+  // triangle with identity padding, Y = I (as chol_prep and chol_diag_load)
+  if (threadIdx.x < 64) {
+    const int t = threadIdx.x;
+    const double w = L[t][t];
+    dsc[t] = (t < r && w > 0.0) ? 1.0 / sqrt(w) : 1.0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int gi = q * 4 + wave, gj = lane;
+    const double id = gi == gj ? 1.0 : 0.0;
+    L[gi][gj] = (gi < r && gj <= gi) ? L[gi][gj] * dsc[gi] * dsc[gj] : id;
+    Y[gi][gj] = id;
+  }
+  __syncthreads();
+  // 3. L and Y = L^-1 in LDS
+  chol_diag_factor(a.ca, 0, member, LY, dinv);
+  __syncthreads();
+  // 4. T1^T[j][k] = Y[j][k] d_k
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int gi = q * 4 + wave, gj = lane;
+    Y[gi][gj] *= dsc[gj];
+  }
+  __syncthreads();
+  // 5. P = P~ T1 over 64-row tiles of the resident P~: wave w owns rows
+  // 16 w .. + 15 of each tile and all four 16-column blocks; block jb needs
+  // k < 16 (jb + 1) (T1 is upper triangular), 40 products per tile
+  float* out = static_cast<float*>(const_cast<void*>(a.out.p[member]));
+  uint16_t* ob = a.has_bf16 ? static_cast<uint16_t*>(const_cast<void*>(a.out_bf16.p[member])) : nullptr;
+  for (int i0 = 0; i0 < m; i0 += 64) {
+    doublex4 acc4[4];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) acc4[jb] = doublex4{0.0, 0.0, 0.0, 0.0};
+    const float* arow = sp + min(i0 + wave * 16 + (lane & 15), mp - 1) * kSoPitch + (lane >> 4);
+#pragma unroll
+    for (int k0 = 0; k0 < 64; k0 += 4) {
+      const double af = static_cast<double>(arow[k0]);
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        if (k0 < 16 * (jb + 1)) {
+          const double bf = Y[jb * 16 + (lane & 15)][k0 + (lane >> 4)];
+          acc4[jb] = __builtin_amdgcn_mfma_f64_16x16x4f64(af, bf, acc4[jb], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = i0 + wave * 16 + (lane >> 4) + 4 * e;
+        const int col = jb * 16 + (lane & 15);
+        if (row < m && col < r) {
+          const float x = static_cast<float>(acc4[jb][e]);
+          out[(int64_t)row * a.out.ld + col] = x;
+          if (ob) ob[(int64_t)row * a.out_bf16.ld + col] = to_bf16_bits(x);
+        }
+      }
+  }
+}
+
 // 64 x 64 fp64 tiles of row-major r x r matrices through LDS (pitch kCP),
 // four waves of 32 x 32 on v_mfma_f64_16x16x4f64.  Element e of acc[i][j] in
 // lane l is row wa * 32 + i * 16 + l / 16 + 4 e, column wb * 32 + j * 16 +
@@ -1953,6 +2121,12 @@ hipError_t launch_cholesky_inverse(const CholArgs& a, float* tt, int64_t tt_stri
   }
   hipLaunchKernelGGL(make_t_kernel, dim3(nblk, nblk, members), dim3(256), 0, s, a, tt, tt_stride,
                      ttd, ttd_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_small_ortho(const SmallOrthoArgs& a, int members, hipStream_t s) {
+  if (a.ca.r < 1 || a.ca.r > 64 || a.m < 1 || a.m > 256) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(small_ortho_kernel, dim3(members), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -170,6 +170,20 @@ struct Apply64Args {
 };
 hipError_t launch_apply64(const Apply64Args& a, int members, hipStream_t s);
 
+// The whole orthonormalisation (fp64 Gram, scaled Cholesky and inverse,
+// P = P~ T1 in fp64) in one workgroup per member, for r <= 64 and a short P~
+// (small_ortho_kernel).  ca supplies r, the status word and the s / x
+// scratch that the diagonal factorisation writes; out must not alias pt.
+struct SmallOrthoArgs {
+  MatArg pt;                  // fp32 m x r
+  MatArg out;                 // fp32 m x r
+  MatArg out_bf16;            // optional bf16 copy (has_bf16)
+  int has_bf16;
+  int m;
+  CholArgs ca;
+};
+hipError_t launch_small_ortho(const SmallOrthoArgs& a, int members, hipStream_t s);
+
 // T1^T into tt (fp32) and / or ttd (fp64, when not null).
 hipError_t launch_cholesky_inverse(const CholArgs& a, float* tt, int64_t tt_stride, int members,
                                    hipStream_t s, double* ttd = nullptr, int64_t ttd_stride = 0);

@@ -134,6 +134,7 @@ bool plan_dion(int64_t m, int64_t n, int32_t r, int32_t batch, DionPlan* p) {
   // sets fit when 3 r <= n); with the streaming sweeps at r = 512, in regions
   // of their own.
   d.ortho64 = r <= kOrtho64MaxRank;
+  d.small_ortho = r <= 64 && m <= kSmallOrthoMaxRows;
   d.fast_ortho = !d.ortho64 && (d.fast_sweeps || (d.stream_sweeps && r == 512 && m % 256 == 0)) &&
                  3 * r <= n;
   if (d.fast_ortho) {

@@ -13,6 +13,8 @@ constexpr int kMaxMembersPerLaunch = 32;  // must match kMaxBatch in common.h
 constexpr size_t kWsAlign = 256;
 // Largest rank whose orthonormalisation takes one fp64 pass (apply64).
 constexpr int kOrtho64MaxRank = 2048;
+// Longest P~ whose whole orthonormalisation runs in one workgroup (r <= 64).
+constexpr int kSmallOrthoMaxRows = 256;
 
 // P1^T P1 of the correction pass runs on 64 x 64 tiles below this rank (a
 // 256 x 256 result is only 4 tiles of 128); the plan sizes its split for them.
@@ -70,6 +72,9 @@ struct DionPlan {
   // scaled-Gram region and P in off_p1, for r <= kOrtho64MaxRank; above it the
   // two passes over bf16 pieces (first-order correction) below.
   bool ortho64;
+  // r <= 64 and m <= kSmallOrthoMaxRows: Gram, Cholesky and the fp64 apply in
+  // one workgroup per member (small_ortho_kernel).
+  bool small_ortho;
   // Orthonormalisation products on the 256 x 256 kernel (with fast_sweeps, or
   // with the streaming sweeps at r = 512 and m a multiple of 256; and 3 r <= n):
   // bf16 pieces in the B-piece buffers, free between the sweeps, or (streaming)

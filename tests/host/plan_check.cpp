@@ -103,6 +103,8 @@ static void check_dion(int64_t m, int64_t n, int r, int batch) {
   EXPECT(p.fast_sweeps == (!stream && m % 256 == 0 && n % 256 == 0 && r % 256 == 0 && r >= 512),
          "fast sweeps flag on %lld x %lld r %d", (long long)m, (long long)n, r);
   EXPECT(p.ortho64 == (r <= kOrtho64MaxRank), "fp64 orthonormalisation flag for r %d", r);
+  EXPECT(p.small_ortho == (r <= 64 && m <= kSmallOrthoMaxRows), "one-workgroup orthonormalisation flag (m %lld r %d)",
+         (long long)m, r);
   EXPECT(!!p.fast_ortho == (!p.ortho64 && (p.fast_sweeps || (stream && r == 512 && m % 256 == 0)) &&
                             3 * r <= n),
          "fast orthonormalisation flag on %lld x %lld r %d", (long long)m, (long long)n, r);
