@@ -1,0 +1,304 @@
+// Symmetric bf16 products C = A B^T with C symmetric (the Newton-Schulz Gram
+// X X^T and polynomial b A + c A A, A symmetric), on gfx950, spread so that
+// one 256-row tile grid of side T fills T^2 workgroups of about equal work:
+//
+// - each tile (tm, tn) above the diagonal is computed as two 256 x 128 column
+//   halves, each by its own workgroup (four waves of 128 x 64: 4 x 2
+//   v_mfma_f32_32x32x16_bf16 accumulators), and stored with its mirror;
+// - each diagonal tile computes only its 36 upper 32 x 32 blocks: wave w owns
+//   block rows w and 7 - w (8 - w and w + 1 blocks: nine per wave), and the
+//   blocks above the diagonal are stored with their mirror.
+// T (T - 1) half tiles and T diagonal tiles make T^2 workgroups: 256 at
+// 4096 x 4096, one per CU, where the 256 x 256 kernel ran the T (T + 1) / 2
+// upper tiles on 136 CUs.  A half tile carries half a tile's products, a
+// diagonal tile 9/16 of them.
+//
+// Operand tiles (256 x 64 of A, 128 x 64 of B; a diagonal tile's B is its A)
+// go straight from global memory into LDS with global_load_lds_dwordx4 in the
+// same swizzled layout as the 256 x 256 kernel, three stages deep; the
+// fragments of the next 16-deep k step are read while the current step's
+// products run.  After the loop, the policy's memory term (kFastPre == 1: a
+// bf16 source S, symmetric like the result) is added as S[col][row .. row + 3]
+// (one 8-byte read per lane), mirrors are stored straight from the
+// accumulators (four consecutive rows of one column are contiguous in the
+// mirror), and the direct blocks pass through a per-wave LDS transposition so
+// that each store instruction covers eight whole 32-column row segments.
+//
+// Requirements (checked by the launcher): M = N, a multiple of 256; K a
+// multiple of 64; 16-byte aligned rows; the operand-row conditions of the
+// 256 x 256 kernel (fast_ok); one split.
+#pragma once
+
+#include <type_traits>
+
+#include "gemm_fast.h"
+
+namespace ortho {
+
+namespace symk {
+
+constexpr int BK = 64;
+constexpr int A_BYTES = 256 * BK * 2;    // 32 KB
+constexpr int B_BYTES = 128 * BK * 2;    // 16 KB
+constexpr int STAGE = A_BYTES + B_BYTES;
+constexpr int NSTAGE = 3;
+constexpr int kTp = 36;                  // floats per row of a wave's 32 x 32 staging block
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// The policy's memory term (kFastPre == 1) for NB accumulator blocks at rows
+// r0[b], columns c0[b]: S[row0 + t][col] read as S[col][row0 + t] (S
+// symmetric), every load of the wave issued before any is added.
+template <class Epi, int NB>
+__device__ __forceinline__ void blocks_pre(const Epi& epi, floatx16 (&acc)[NB], const int (&r0)[NB],
+                                           const int (&c0)[NB], int lane) {
+  if constexpr (Epi::kFastPre == 1) {
+    const uint16_t* src = static_cast<const uint16_t*>(epi.fast_pre_src());
+    const int64_t ld = epi.fast_pre_ld();
+    const float sc = epi.fast_pre_scale();
+    uint2 u[NB][4];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int row0 = r0[b] + g * 8 + (lane >> 5) * 4, col = c0[b] + (lane & 31);
+        u[b][g] = *reinterpret_cast<const uint2*>(src + (int64_t)col * ld + row0);
+      }
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        acc[b][g * 4 + 0] += sc * __uint_as_float(u[b][g].x << 16);
+        acc[b][g * 4 + 1] += sc * __uint_as_float(u[b][g].x & 0xffff0000u);
+        acc[b][g * 4 + 2] += sc * __uint_as_float(u[b][g].y << 16);
+        acc[b][g * 4 + 3] += sc * __uint_as_float(u[b][g].y & 0xffff0000u);
+      }
+  }
+}
+
+// The mirror and the direct store of one 32 x 32 accumulator block at rows
+// r0, columns c0 (r0 < c0 unless the block is on the diagonal).  st: this
+// wave's staging block in LDS.
+template <class Epi>
+__device__ __forceinline__ void block_out(Epi& epi, const floatx16& acc, int r0, int c0, bool mirror,
+                                          float* st, int lane) {
+  if (mirror) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int row0 = r0 + g * 8 + (lane >> 5) * 4, col = c0 + (lane & 31);
+      const floatx4 v = {acc[g * 4 + 0], acc[g * 4 + 1], acc[g * 4 + 2], acc[g * 4 + 3]};
+      epi.fast_store_t4(col, row0, v);
+    }
+  }
+  // direct: transpose through LDS (the wave's own 32 x kTp floats; LDS
+  // instructions of a wave run in order, so no barrier is needed)
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      st[(g * 8 + (lane >> 5) * 4 + t) * kTp + (lane & 31)] = acc[g * 4 + t];
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int rl = (lane >> 3) + 8 * q, cl = (lane & 7) * 4;
+    const floatx4 v = *reinterpret_cast<const floatx4*>(st + rl * kTp + cl);
+    epi.fast_store4(r0 + rl, c0 + cl, v);
+  }
+}
+
+}  // namespace symk
+
+template <class Epi>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_sym(GemmParams<typename Epi::Args> p) {
+  using namespace fast;
+  static_assert(Epi::kSegs == 1 && Epi::kFastSym && Epi::kFastPre2 == 0, "symmetric single-segment policies");
+  __shared__ __attribute__((aligned(1024))) char smem[symk::NSTAGE * symk::STAGE];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // Workgroup -> tile.  Each XCD (workgroup id mod 8) takes a contiguous run
+  // of the ordered list; the list walks tile rows, each row's diagonal tile
+  // first, then the two halves of each tile to its right, so a run shares A
+  // row blocks in its XCD's L2.
+  const int T = p.tiles_n;
+  const int nwg = gridDim.x;
+  int t = blockIdx.x;
+  if ((nwg & 7) == 0) t = (t & 7) * (nwg >> 3) + (t >> 3);
+  int tm = 0, rem = t;
+  while (rem >= 1 + 2 * (T - 1 - tm)) {
+    rem -= 1 + 2 * (T - 1 - tm);
+    ++tm;
+  }
+  const bool diag = rem == 0;
+  const int tn = diag ? tm : tm + 1 + (rem - 1) / 2;
+  const int half = diag ? 0 : (rem - 1) & 1;
+  const int bi = blockIdx.y;
+  const int m0 = tm * 256;
+  const int n0 = tn * 256 + half * 128;
+
+  const uint16_t* A = static_cast<const uint16_t*>(p.a.p[bi]);
+  const uint16_t* B = static_cast<const uint16_t*>(p.b0.p[bi]);
+  const int64_t lda = p.a.ld, ldb = p.b0.ld;
+  const int nk = p.K / symk::BK;
+  Epi epi(p.e, bi, 0);
+  const unsigned lds0 = lds_addr(smem);
+
+  // copy instruction q of wave w: A rows (8 w + q) * 8 .. + 7 (q < 8), B rows
+  // (4 w + q) * 8 .. + 7 (q < 4); lane = 8 * (row within the group) + stored
+  // chunk position, the fetched chunk swizzled as in the 256 x 256 kernel
+  const int sub = lane >> 3, pos = lane & 7;
+  unsigned offa[8], offb[4];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int row = (wave * 8 + q) * 8 + sub;
+    offa[q] = static_cast<unsigned>((row * lda + swz(row, pos) * 8) * 2);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = (wave * 4 + q) * 8 + sub;
+    offb[q] = static_cast<unsigned>((row * ldb + swz(row, pos) * 8) * 2);
+  }
+  auto issue = [&](int kt, int st) {
+    const char* ba = uniform_ptr(reinterpret_cast<const char*>(A + (int64_t)m0 * lda + kt * symk::BK));
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dma16(offa[q], ba, lds0 + st * symk::STAGE + (wave * 8 + q) * 1024);
+    if (!diag) {
+      const char* bb = uniform_ptr(reinterpret_cast<const char*>(B + (int64_t)n0 * ldb + kt * symk::BK));
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        dma16(offb[q], bb, lds0 + st * symk::STAGE + symk::A_BYTES + (wave * 4 + q) * 1024);
+    }
+  };
+  // wait for tile kt's copies (those of tile kt + 1, if issued, stay in flight)
+  auto ready = [&](int kt) {
+    asm volatile("" ::: "memory");
+    if (kt + 1 < nk) {
+      if (diag) symk::wait_vm<8>();
+      else symk::wait_vm<12>();
+    } else {
+      symk::wait_vm<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  const int frow = lane & 31, fchunk = lane >> 5;
+  float* stage_out = reinterpret_cast<float*>(smem) + wave * 32 * symk::kTp;
+
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+
+  if (!diag) {
+    // ---- half tile: wave (wm, wn) rows wm * 128 .. + 127, columns wn * 64 .. + 63
+    const int wm = wave >> 1, wn = wave & 1;
+    floatx16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    for (int kt = 0; kt < nk; ++kt) {
+      ready(kt);
+      if (kt + 2 < nk) issue(kt + 2, (kt + 2) % symk::NSTAGE);
+      const char* ta = smem + (kt % symk::NSTAGE) * symk::STAGE;
+      const char* tb = ta + symk::A_BYTES;
+      bf16x8 fa[2][4], fb[2][2];
+      auto rd = [&](int buf, int kk) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[buf][i] = read_frag(ta, wm * 128 + i * 32 + frow, kk * 2 + fchunk);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fb[buf][j] = read_frag(tb, wn * 64 + j * 32 + frow, kk * 2 + fchunk);
+      };
+      rd(0, 0);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        if (kk < 3) rd((kk + 1) & 1, kk + 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
+      }
+    }
+    __syncthreads();   // every wave is done with the operand stages
+    floatx16 blk[8];
+    int r0[8], c0[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        blk[i * 2 + j] = acc[i][j];
+        r0[i * 2 + j] = m0 + wm * 128 + i * 32;
+        c0[i * 2 + j] = n0 + wn * 64 + j * 32;
+      }
+    symk::blocks_pre(epi, blk, r0, c0, lane);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) symk::block_out(epi, blk[b], r0[b], c0[b], true, stage_out, lane);
+    return;
+  }
+
+  // ---- diagonal tile: wave W owns block rows W and 7 - W of the upper blocks
+  auto diag_wave = [&](auto w_c) {
+    constexpr int W = decltype(w_c)::value;
+    constexpr int NF = 8 - W;          // fragments of block rows W .. 7
+    constexpr int N0 = 8 - W;          // blocks (W, W .. 7)
+    constexpr int N1 = W + 1;          // blocks (7 - W, 7 - W .. 7)
+    floatx16 acc[N0 + N1];
+#pragma unroll
+    for (int b = 0; b < N0 + N1; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
+    for (int kt = 0; kt < nk; ++kt) {
+      ready(kt);
+      if (kt + 2 < nk) issue(kt + 2, (kt + 2) % symk::NSTAGE);
+      const char* ta = smem + (kt % symk::NSTAGE) * symk::STAGE;
+      bf16x8 f[2][NF];
+      auto rd = [&](int buf, int kk) {
+#pragma unroll
+        for (int b = 0; b < NF; ++b) f[buf][b] = read_frag(ta, (W + b) * 32 + frow, kk * 2 + fchunk);
+      };
+      rd(0, 0);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        if (kk < 3) rd((kk + 1) & 1, kk + 1);
+#pragma unroll
+        for (int b = 0; b < N0; ++b)
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[kk & 1][0], f[kk & 1][b], acc[b], 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < N1; ++b)
+          acc[N0 + b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[kk & 1][7 - 2 * W], f[kk & 1][7 - 2 * W + b],
+                                                               acc[N0 + b], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+    int r0[N0 + N1], c0[N0 + N1];
+#pragma unroll
+    for (int b = 0; b < N0; ++b) {
+      r0[b] = m0 + W * 32;
+      c0[b] = m0 + (W + b) * 32;
+    }
+#pragma unroll
+    for (int b = 0; b < N1; ++b) {
+      r0[N0 + b] = m0 + (7 - W) * 32;
+      c0[N0 + b] = m0 + (7 - W + b) * 32;
+    }
+    symk::blocks_pre(epi, acc, r0, c0, lane);
+#pragma unroll
+    for (int b = 0; b < N0; ++b) symk::block_out(epi, acc[b], r0[b], c0[b], b > 0, stage_out, lane);
+#pragma unroll
+    for (int b = 0; b < N1; ++b)
+      symk::block_out(epi, acc[N0 + b], r0[N0 + b], c0[N0 + b], b > 0, stage_out, lane);
+  };
+  switch (wave) {
+    case 0: diag_wave(std::integral_constant<int, 0>{}); break;
+    case 1: diag_wave(std::integral_constant<int, 1>{}); break;
+    case 2: diag_wave(std::integral_constant<int, 2>{}); break;
+    default: diag_wave(std::integral_constant<int, 3>{}); break;
+  }
+}
+
+}  // namespace ortho

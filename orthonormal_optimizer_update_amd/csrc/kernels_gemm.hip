@@ -3,6 +3,7 @@
 #include "epilogues.h"
 #include "gemm_core.h"
 #include "gemm_fast.h"
+#include "gemm_sym.h"
 #include "launch.h"
 #include "plan.h"
 
@@ -189,6 +190,18 @@ hipError_t run_fast(GemmParams<typename Epi::Args>& p, int members, hipStream_t 
   return hipGetLastError();
 }
 
+// Symmetric products (Gram, polynomial) on the 256 x 256 grid's T^2
+// equal-work workgroups (gemm_sym.h): M = N, the conditions of fast_ok.
+template <class Epi>
+hipError_t run_sym(GemmParams<typename Epi::Args>& p, int members, hipStream_t s) {
+  if (p.M != p.N || p.M % 256 != 0 || p.K % 64 != 0) return hipErrorInvalidValue;
+  p.tiles_n = p.M / 256;
+  p.splits = 1;
+  dim3 grid(p.tiles_n * p.tiles_n, members);
+  hipLaunchKernelGGL((gemm_bf16_sym<Epi>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 // Newton-Schulz products whose 256 x 256 grid (upper tiles for the symmetric
 // ones) would give fewer than 128 workgroups over a launch's members run on
 // the 128 x 128 kernel instead: four times the workgroups (full tiles, so the
@@ -213,10 +226,7 @@ hipError_t ns_gram_t(const NsGramArgs& a, int members, hipStream_t s) {
   p.splits = 1; p.kchunk = 0; p.tri = 0;
   if (ns_few_fast_tiles(a.M, a.M, members, true))
     return run<CfgNsMid, NsRow<CfgNsMid>, NsRow<CfgNsMid>, EpiNSGram>(p, members, s);
-  if (fast_ok(p.M, p.N, p.K, p.a, p.b0)) {
-    p.sym = 1;  // X X^T: upper tiles, mirrored
-    return run_fast<EpiNSGram>(p, members, s);
-  }
+  if (fast_ok(p.M, p.N, p.K, p.a, p.b0)) return run_sym<EpiNSGram>(p, members, s);  // X X^T
   return run<Cfg, NsRow<Cfg>, NsRow<Cfg>, EpiNSGram>(p, members, s);
 }
 
@@ -231,10 +241,8 @@ hipError_t ns_poly_t(const NsPolyArgs& a, int members, hipStream_t s) {
   p.splits = 1; p.kchunk = 0; p.tri = 0;
   if (ns_few_fast_tiles(a.M, a.M, members, true))
     return run<CfgNsMid, NsRow<CfgNsMid>, NsRow<CfgNsMid>, EpiNSPoly>(p, members, s);
-  if (fast_ok(p.M, p.N, p.K, p.a, p.b0)) {
-    p.sym = 1;  // b A + c A A is symmetric with A: upper tiles, mirrored
-    return run_fast<EpiNSPoly>(p, members, s);
-  }
+  // b A + c A A is symmetric with A
+  if (fast_ok(p.M, p.N, p.K, p.a, p.b0)) return run_sym<EpiNSPoly>(p, members, s);
   return run<Cfg, NsRow<Cfg>, NsRow<Cfg>, EpiNSPoly>(p, members, s);
 }
 
