@@ -42,7 +42,7 @@ PEAK_HBM_GBS = 8000.0
 # passes over `bench.py --counter-sample`, each scaled by the same counter's
 # reading for a 256 MiB elementwise copy (fetch factor 2.0, write factor 1.0).
 # Set to None whenever the kernel changes, until the passes are taken again.
-TRAFFIC_BYTES_PER_LAUNCH = 2.801e8
+TRAFFIC_BYTES_PER_LAUNCH = 2.844e8
 
 
 def parse():
@@ -392,8 +392,8 @@ def main():
     # right factor and workspace; the gradient is only read), so each runs on
     # its own stream (default priority), forked from the main stream and joined
     # back to it every step: the idle CUs of one path's narrow launches (the
-    # Cholesky chain, the symmetric Newton-Schulz products on 136 of 256 CUs)
-    # take the other paths' work.
+    # Cholesky chain, the small orthonormalisation products) take the other
+    # paths' work.
     main = torch.cuda.current_stream()
     side = {nm: torch.cuda.Stream() for nm in names}
 
@@ -464,11 +464,11 @@ def main():
                         "TFLOP/s": tfs, "mfma_frac": tfs / PEAK_BF16_TFLOPS,
                         "model_bytes": nbytes, "model_flops": fl}
 
-    # Dominant kernel: the Newton-Schulz MFMA GEMM (three launches per
+    # Dominant kernel: the Newton-Schulz MFMA products (three launches per
     # iteration).  Work per iteration is counted densely, 4 m m n + 2 m^3 (Gram,
-    # polynomial, apply).  The Gram and the polynomial are symmetric and the
-    # kernel computes only their tiles on and above the diagonal, so the
-    # products it executes are reported beside the dense rate.  Its average
+    # polynomial, apply).  The Gram and the polynomial are symmetric and their
+    # kernel computes only the blocks on and above the diagonal, so the
+    # products executed are reported beside the dense rate.  The average
     # launch time is
     # (time of 6 iterations - time of 1 iteration) / 15, on the same stream:
     # both runs launch the same normalisation kernels, and both keep the GPU
@@ -487,14 +487,18 @@ def main():
     gemm_ms = (t6.ms - t1.ms) / reps / 15.0
     flops = (4.0 * m * m * n + 2.0 * m ** 3) / 3.0  # dense count, mean per launch
     achieved = flops / (gemm_ms * 1e-3) / 1e12
+    # products computed by the Gram and the polynomial (gemm_bf16_sym): the
+    # T (T - 1) upper 256 x 128 half tiles whole, and 36 of the 64 32 x 32
+    # blocks of each of the T diagonal tiles, out of T^2 tiles
     tiles = m // 256
-    sym_frac = (tiles * (tiles + 1) // 2) / float(tiles * tiles)  # tiles computed, Gram and polynomial
+    sym_frac = (tiles * (tiles - 1) * 0.5 + tiles * 36.0 / 64.0) / float(tiles * tiles)
     executed = (2.0 * m * m * n * sym_frac + 2.0 * m ** 3 * sym_frac + 2.0 * m * m * n) / 3.0
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": TRAFFIC_BYTES_PER_LAUNCH,
-                "kernel": "gemm_bf16_256 (Newton-Schulz products X X^T, b A + c A^2, a X + Bp X; "
-                          "bf16 MFMA 32x32x16, 256x256 tiles, direct-to-LDS operand copies; the two "
-                          "symmetric products on their upper tiles only)",
+                "kernel": "Newton-Schulz products: X X^T and b A + c A^2 on gemm_bf16_sym (the upper "
+                          "256x256 tiles as 256x128 halves and the diagonal tiles' upper 32x32 "
+                          "blocks, one workgroup per CU), a X + Bp X on gemm_bf16_256; bf16 MFMA "
+                          "32x32x16, direct-to-LDS operand copies",
                 "avg_launch_ms": gemm_ms, "flops_per_launch": flops,
                 "executed_flops_per_launch": executed,
                 "executed_tflops": executed / (gemm_ms * 1e-3) / 1e12}
