@@ -15,9 +15,12 @@
 //
 // Operand tiles (256 x 64 of A, 128 x 64 of B; a diagonal tile's B is its A)
 // go straight from global memory into LDS with global_load_lds_dwordx4 in the
-// same swizzled layout as the 256 x 256 kernel, three stages deep; the
-// fragments of the next 16-deep k step are read while the current step's
-// products run.  After the loop, the policy's memory term (kFastPre == 1: a
+// same swizzled layout as the 256 x 256 kernel, three stages deep.  The issue
+// order inside a k tile is fixed with scheduling fences: every slot of a
+// 16-deep k step holds one product and at most one fragment read for the next
+// step (left to itself the compiler sinks each read to just before its first
+// product and waits on it there), and a tile's copies are spread over four k
+// steps rather than issued in one burst.  After the loop, the policy's memory term (kFastPre == 1: a
 // bf16 source S, symmetric like the result) is added as S[col][row .. row + 3]
 // (one 8-byte read per lane), mirrors are stored straight from the
 // accumulators (four consecutive rows of one column are contiguous in the
@@ -25,7 +28,7 @@
 // that each store instruction covers eight whole 32-column row segments.
 //
 // Requirements (checked by the launcher): M = N, a multiple of 256; K a
-// multiple of 64; 16-byte aligned rows; the operand-row conditions of the
+// positive multiple of 64; 16-byte aligned rows; the operand-row conditions of the
 // 256 x 256 kernel (fast_ok); one split.
 #pragma once
 
@@ -161,26 +164,56 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_sym(GemmParams<typename Epi:
     const int row = (wave * 4 + q) * 8 + sub;
     offb[q] = static_cast<unsigned>((row * ldb + swz(row, pos) * 8) * 2);
   }
-  auto issue = [&](int kt, int st) {
-    const char* ba = uniform_ptr(reinterpret_cast<const char*>(A + (int64_t)m0 * lda + kt * symk::BK));
-#pragma unroll
-    for (int q = 0; q < 8; ++q) dma16(offa[q], ba, lds0 + st * symk::STAGE + (wave * 8 + q) * 1024);
-    if (!diag) {
-      const char* bb = uniform_ptr(reinterpret_cast<const char*>(B + (int64_t)n0 * ldb + kt * symk::BK));
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        dma16(offb[q], bb, lds0 + st * symk::STAGE + symk::A_BYTES + (wave * 4 + q) * 1024);
-    }
+  auto base_a = [&](int kt) {
+    return uniform_ptr(reinterpret_cast<const char*>(A + (int64_t)m0 * lda + kt * symk::BK));
   };
-  // wait for tile kt's copies (those of tile kt + 1, if issued, stay in flight)
-  auto ready = [&](int kt) {
-    asm volatile("" ::: "memory");
-    if (kt + 1 < nk) {
-      if (diag) symk::wait_vm<8>();
-      else symk::wait_vm<12>();
-    } else {
-      symk::wait_vm<0>();
+  auto base_b = [&](int kt) {
+    return uniform_ptr(reinterpret_cast<const char*>(B + (int64_t)n0 * ldb + kt * symk::BK));
+  };
+  auto dma_a = [&](int q, const char* ba, int st) {
+    dma16(offa[q], ba, lds0 + st * symk::STAGE + (wave * 8 + q) * 1024);
+  };
+  auto dma_b = [&](int q, const char* bb, int st) {
+    dma16(offb[q], bb, lds0 + st * symk::STAGE + symk::A_BYTES + (wave * 4 + q) * 1024);
+  };
+  // copy c of a tile: c < 8 the A rows of dma_a(c), else the B rows of dma_b(c - 8)
+  auto dma_c = [&](int c, const char* ba, const char* bb, int st) {
+    if (c < 8) dma_a(c, ba, st);
+    else dma_b(c - 8, bb, st);
+  };
+  // Stage of tile k: k mod 3.  Tile k + 3's copies are spread over the four
+  // k steps that follow the barrier at which every wave is done with tile k
+  // (E of them in tile k's last step, the rest in the first three steps of
+  // tile k + 1), so that the copy instructions of the four waves never queue
+  // up at once.  Before the loop: tiles 0 and 1 whole and tile 2's first E
+  // copies, then wait for tile 0.  At every later wait each wave has exactly
+  // one tile's copies (8 or 12) in flight.  A tile index past the last
+  // reloads the last tile into a stage nobody reads.
+  const int ncp = diag ? 8 : 12;          // copies per tile and wave
+  const int ecp = diag ? 2 : 4;           // of them in the last k step
+  {
+#pragma unroll
+    for (int k = 0; k < symk::NSTAGE; ++k) {
+      const int kl = min(k, nk - 1);
+      const char* ba = base_a(kl);
+      const char* bb = base_b(kl);
+      const int nc = k + 1 < symk::NSTAGE ? ncp : ecp;
+#pragma unroll
+      for (int c = 0; c < 12; ++c)
+        if (c < nc) dma_c(c, ba, bb, k);
     }
+    asm volatile("" ::: "memory");
+    if (diag) symk::wait_vm<10>();
+    else symk::wait_vm<16>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+  // end of a tile's first three k steps: this wave's fragment reads and tile
+  // kt + 1's copies done (tile kt + 2's in flight), then every wave's
+  auto tile_barrier = [&]() {
+    asm volatile("" ::: "memory");
+    if (diag) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
@@ -188,11 +221,14 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_sym(GemmParams<typename Epi:
   const int frow = lane & 31, fchunk = lane >> 5;
   float* stage_out = reinterpret_cast<float*>(smem) + wave * 32 * symk::kTp;
 
-  issue(0, 0);
-  if (nk > 1) issue(1, 1);
-
   if (!diag) {
-    // ---- half tile: wave (wm, wn) rows wm * 128 .. + 127, columns wn * 64 .. + 63
+    // ---- half tile: wave (wm, wn) rows wm * 128 .. + 127, columns wn * 64 .. + 63.
+    // Issue order fixed by scheduling fences: each of the 8 slots of a
+    // 16-deep k step holds one product and (slots 0 .. 5) one fragment read
+    // for the next step, in the order the next step consumes them (a0 b0 b1
+    // a1 a2 a3); slots 0, 3, 6 of the first three steps carry copies 4 .. 11
+    // of tile kt + 2, slots 0 .. 3 of the fourth step copies 0 .. 3 of tile
+    // kt + 3, and the fourth step reads the first step of tile kt + 1.
     const int wm = wave >> 1, wn = wave & 1;
     floatx16 acc[4][2];
 #pragma unroll
@@ -201,29 +237,55 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_sym(GemmParams<typename Epi:
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-    for (int kt = 0; kt < nk; ++kt) {
-      ready(kt);
-      if (kt + 2 < nk) issue(kt + 2, (kt + 2) % symk::NSTAGE);
-      const char* ta = smem + (kt % symk::NSTAGE) * symk::STAGE;
+    bf16x8 fa[2][4], fb[2][2];
+    auto rd = [&](int buf, int q, const char* ta, int kk) {
       const char* tb = ta + symk::A_BYTES;
-      bf16x8 fa[2][4], fb[2][2];
-      auto rd = [&](int buf, int kk) {
+      const int c = kk * 2 + fchunk;
+      if (q == 0) fa[buf][0] = read_frag(ta, wm * 128 + frow, c);
+      if (q == 1) fb[buf][0] = read_frag(tb, wn * 64 + frow, c);
+      if (q == 2) fb[buf][1] = read_frag(tb, wn * 64 + 32 + frow, c);
+      if (q >= 3) fa[buf][q - 2] = read_frag(ta, wm * 128 + (q - 2) * 32 + frow, c);
+    };
+    auto mma = [&](int buf, int q) {
+      const int i = q >> 1, j = q & 1;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+    };
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fa[buf][i] = read_frag(ta, wm * 128 + i * 32 + frow, kk * 2 + fchunk);
+    for (int q = 0; q < 6; ++q) rd(0, q, smem, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    int cur = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* ta = smem + cur * symk::STAGE;
+      const int nxt = cur == symk::NSTAGE - 1 ? 0 : cur + 1;
+      const int prv = nxt == symk::NSTAGE - 1 ? 0 : nxt + 1;   // tile kt + 2's stage
+      const int k2 = min(kt + 2, nk - 1);
+      const char* ba2 = base_a(k2);
+      const char* bb2 = base_b(k2);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) fb[buf][j] = read_frag(tb, wn * 64 + j * 32 + frow, kk * 2 + fchunk);
-      };
-      rd(0, 0);
+      for (int kk = 0; kk < 3; ++kk) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        if (kk < 3) rd((kk + 1) & 1, kk + 1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
+        for (int q = 0; q < 8; ++q) {
+          if (q < 6) rd((kk + 1) & 1, q, ta, kk + 1);
+          if (q % 3 == 0 && 4 + 3 * kk + q / 3 < 12) dma_c(4 + 3 * kk + q / 3, ba2, bb2, prv);
+          mma(kk & 1, q);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
+      tile_barrier();
+      const int k3 = min(kt + 3, nk - 1);
+      const char* ba3 = base_a(k3);
+      const char* bb3 = base_b(k3);
+      const char* na = smem + nxt * symk::STAGE;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (q < 6) rd(0, q, na, 0);
+        if (q < 4) dma_c(q, ba3, bb3, cur);
+        mma(1, q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      cur = nxt;
     }
+    symk::wait_vm<0>();   // the reloads past the last tile land before the LDS is reused
     __syncthreads();   // every wave is done with the operand stages
     floatx16 blk[8];
     int r0[8], c0[8];
@@ -252,28 +314,53 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_sym(GemmParams<typename Epi:
     for (int b = 0; b < N0 + N1; ++b)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
+    // the same slot order as the half tiles: nine products per step, slots
+    // 0 .. NF - 1 read the next step's fragments (row W + q); slots 0 and 4
+    // of the first three steps carry copies 2 .. 7 of tile kt + 2, those of
+    // the fourth step copies 0 and 1 of tile kt + 3
+    bf16x8 f[2][NF];
+    auto rd = [&](int buf, int q, const char* ta, int kk) {
+      f[buf][q] = read_frag(ta, (W + q) * 32 + frow, kk * 2 + fchunk);
+    };
+    auto mma = [&](int buf, int b) {
+      if (b < N0)
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[buf][0], f[buf][b], acc[b], 0, 0, 0);
+      else
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[buf][7 - 2 * W], f[buf][7 - 2 * W + b - N0],
+                                                         acc[b], 0, 0, 0);
+    };
+#pragma unroll
+    for (int q = 0; q < NF; ++q) rd(0, q, smem, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    int cur = 0;
     for (int kt = 0; kt < nk; ++kt) {
-      ready(kt);
-      if (kt + 2 < nk) issue(kt + 2, (kt + 2) % symk::NSTAGE);
-      const char* ta = smem + (kt % symk::NSTAGE) * symk::STAGE;
-      bf16x8 f[2][NF];
-      auto rd = [&](int buf, int kk) {
+      const char* ta = smem + cur * symk::STAGE;
+      const int nxt = cur == symk::NSTAGE - 1 ? 0 : cur + 1;
+      const int prv = nxt == symk::NSTAGE - 1 ? 0 : nxt + 1;   // tile kt + 2's stage
+      const char* ba2 = base_a(min(kt + 2, nk - 1));
 #pragma unroll
-        for (int b = 0; b < NF; ++b) f[buf][b] = read_frag(ta, (W + b) * 32 + frow, kk * 2 + fchunk);
-      };
-      rd(0, 0);
+      for (int kk = 0; kk < 3; ++kk) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        if (kk < 3) rd((kk + 1) & 1, kk + 1);
-#pragma unroll
-        for (int b = 0; b < N0; ++b)
-          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[kk & 1][0], f[kk & 1][b], acc[b], 0, 0, 0);
-#pragma unroll
-        for (int b = 0; b < N1; ++b)
-          acc[N0 + b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[kk & 1][7 - 2 * W], f[kk & 1][7 - 2 * W + b],
-                                                               acc[N0 + b], 0, 0, 0);
+        for (int q = 0; q < N0 + N1; ++q) {
+          if (q < NF) rd((kk + 1) & 1, q, ta, kk + 1);
+          if (q % 4 == 0 && q < 8) dma_a(2 + 2 * kk + q / 4, ba2, prv);
+          mma(kk & 1, q);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
+      tile_barrier();
+      const char* ba3 = base_a(min(kt + 3, nk - 1));
+      const char* na = smem + nxt * symk::STAGE;
+#pragma unroll
+      for (int q = 0; q < N0 + N1; ++q) {
+        if (q < NF) rd(0, q, na, 0);
+        if (q % 4 == 0 && q < 8) dma_a(q / 4, ba3, cur);
+        mma(1, q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      cur = nxt;
     }
+    symk::wait_vm<0>();
     __syncthreads();
     int r0[N0 + N1], c0[N0 + N1];
 #pragma unroll

@@ -194,7 +194,7 @@ hipError_t run_fast(GemmParams<typename Epi::Args>& p, int members, hipStream_t 
 // equal-work workgroups (gemm_sym.h): M = N, the conditions of fast_ok.
 template <class Epi>
 hipError_t run_sym(GemmParams<typename Epi::Args>& p, int members, hipStream_t s) {
-  if (p.M != p.N || p.M % 256 != 0 || p.K % 64 != 0) return hipErrorInvalidValue;
+  if (p.M != p.N || p.M % 256 != 0 || p.K % 64 != 0 || p.K < 64) return hipErrorInvalidValue;
   p.tiles_n = p.M / 256;
   p.splits = 1;
   dim3 grid(p.tiles_n * p.tiles_n, members);
@@ -226,7 +226,7 @@ hipError_t ns_gram_t(const NsGramArgs& a, int members, hipStream_t s) {
   p.splits = 1; p.kchunk = 0; p.tri = 0;
   if (ns_few_fast_tiles(a.M, a.M, members, true))
     return run<CfgNsMid, NsRow<CfgNsMid>, NsRow<CfgNsMid>, EpiNSGram>(p, members, s);
-  if (fast_ok(p.M, p.N, p.K, p.a, p.b0)) return run_sym<EpiNSGram>(p, members, s);  // X X^T
+  if (fast_ok(p.M, p.N, p.K, p.a, p.b0) && p.K >= 64) return run_sym<EpiNSGram>(p, members, s);  // X X^T
   return run<Cfg, NsRow<Cfg>, NsRow<Cfg>, EpiNSGram>(p, members, s);
 }
 
@@ -242,7 +242,7 @@ hipError_t ns_poly_t(const NsPolyArgs& a, int members, hipStream_t s) {
   if (ns_few_fast_tiles(a.M, a.M, members, true))
     return run<CfgNsMid, NsRow<CfgNsMid>, NsRow<CfgNsMid>, EpiNSPoly>(p, members, s);
   // b A + c A A is symmetric with A
-  if (fast_ok(p.M, p.N, p.K, p.a, p.b0)) return run_sym<EpiNSPoly>(p, members, s);
+  if (fast_ok(p.M, p.N, p.K, p.a, p.b0) && p.K >= 64) return run_sym<EpiNSPoly>(p, members, s);
   return run<Cfg, NsRow<Cfg>, NsRow<Cfg>, EpiNSPoly>(p, members, s);
 }
 
