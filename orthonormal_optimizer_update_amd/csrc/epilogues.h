@@ -6,6 +6,8 @@
 // can all be in flight at once, so the epilogue itself only stores.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace ortho {
@@ -21,7 +23,11 @@ namespace ortho {
 //                 (fast_pre2_src(), fast_pre2_ld(), fast_pre2_scale()).
 //   fast_store4   receives four consecutive columns of one row of the result.
 //   kFastT / fast_store_t4  receive four consecutive rows of one column
-//                 (transposed outputs), straight from the accumulators.
+//                 (transposed outputs), straight from the accumulators; a
+//                 kFastT policy also names, through fast_t_rows(ld), a
+//                 16-byte-aligned bf16 destination that the kernel fills with
+//                 whole row pieces of the transposed tile instead (null: use
+//                 fast_store_t4, or nothing when fast_t_any() is false).
 //   kFastSym      the result is symmetric: with GemmParams::sym the kernel
 //                 computes the tiles on and above the diagonal only and hands
 //                 each off-diagonal tile to fast_store_t4 as well (its mirror).
@@ -296,6 +302,22 @@ struct EpiNSApply {
   __device__ const void* fast_pre2_src() const { return nullptr; }
   __device__ int64_t fast_pre2_ld() const { return 0; }
   __device__ float fast_pre2_scale() const { return 0.f; }
+  // The transposed bf16 destination when whole 16-byte pieces of its rows
+  // may be stored (X^T, or the caller's transposed bf16 output on the last
+  // iteration), else null; fast_t_any: whether there is a transposed output.
+  __device__ uint16_t* fast_t_rows(int64_t& ld) const {
+    uint16_t* d = nullptr;
+    if (!last) {
+      d = xbt;
+      ld = ldbt;
+    } else if (out_t && std::is_same<OUT_T, uint16_t>::value) {
+      d = reinterpret_cast<uint16_t*>(out);
+      ld = ldo;
+    }
+    if (d == nullptr || reinterpret_cast<uintptr_t>(d) % 16 != 0 || ld % 8 != 0) return nullptr;
+    return d;
+  }
+  __device__ bool fast_t_any() const { return last ? out_t : xbt != nullptr; }
   // rows row0..row0+3 of column col: consecutive elements of one row of X^T
   __device__ __forceinline__ void fast_store_t4(int col, int row0, floatx4 v) {
     if (last) {

@@ -37,6 +37,10 @@ namespace fast {
 
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int TILE_BYTES = BM * BK * 2;  // 32 KB per operand per stage
+// row of the transposed bf16 tile staged in LDS: 256 elements + 8 of padding
+// (528 bytes: 16-byte aligned, and the 32 columns written by one instruction
+// fall two to a bank pair)
+constexpr int kTRow = 264;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -142,7 +146,11 @@ __device__ __forceinline__ void fast_preload(floatx16 (&acc)[4][4], const void* 
 template <class Epi>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_256(GemmParams<typename Epi::Args> p) {
   using namespace fast;
-  __shared__ __attribute__((aligned(1024))) char smem_fast[2 * 2 * TILE_BYTES];
+  // (policies with a transposed output also stage that tile, 256 x kTRow
+  // bf16, in the same memory after the loop)
+  constexpr int kLds = Epi::kFastT ? (256 * kTRow * 2 > 4 * TILE_BYTES ? 256 * kTRow * 2 : 4 * TILE_BYTES)
+                                   : 4 * TILE_BYTES;
+  __shared__ __attribute__((aligned(1024))) char smem_fast[kLds];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -324,10 +332,46 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_256(GemmParams<typename Epi:
     fast_preload<true, true>(acc, epi.fast_pre2_src(), epi.fast_pre2_ld(), epi.fast_pre2_scale(),
                              m0, n0, smem_fast, wave, lane);
 
+  // A transposed bf16 output with a 16-byte-aligned destination goes through
+  // LDS: each lane writes its four consecutive rows of one column as 8 bytes
+  // of one row of the transposed tile, then every half-wave stores one whole
+  // 512-byte row piece (the per-lane stores below write 8 bytes at 32
+  // addresses 8 KB apart per instruction, and took 13 us of a 4096^2 apply).
+  bool t_done = false;
+  if constexpr (Epi::kFastT) {
+    int64_t tld = 0;
+    uint16_t* tdst = epi.fast_t_rows(tld);
+    if (tdst != nullptr) {
+      uint16_t* tt = reinterpret_cast<uint16_t*>(smem_fast);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int r0 = wm * 128 + i * 32 + g * 8 + (lane >> 5) * 4;
+            const int c = wn * 128 + j * 32 + (lane & 31);
+            const floatx4 v = {acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
+                               acc[i][j][g * 4 + 3]};
+            *reinterpret_cast<uint2*>(tt + c * kTRow + r0) = pack_bf16x4(v);
+          }
+      __syncthreads();
+#pragma unroll 8
+      for (int q = 0; q < 32; ++q) {
+        const int c = wave * 64 + q * 2 + (lane >> 5);
+        const uint4 v = *reinterpret_cast<const uint4*>(tt + c * kTRow + (lane & 31) * 8);
+        *reinterpret_cast<uint4*>(tdst + (int64_t)(n0 + c) * tld + m0 + (lane & 31) * 8) = v;
+      }
+      __syncthreads();
+      t_done = true;
+    } else if (!epi.fast_t_any()) {
+      t_done = true;
+    }
+  }
   // Transposed outputs straight from the accumulators (four consecutive rows
   // of one column per lane): a transposed copy, or the mirror tile (tn, tm)
   // of a symmetric result.
-  if (Epi::kFastT || (Epi::kFastSym && p.sym && tm != tn)) {
+  if (!t_done && (Epi::kFastT || (Epi::kFastSym && p.sym && tm != tn))) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
