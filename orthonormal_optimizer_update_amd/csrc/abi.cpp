@@ -142,6 +142,20 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       }
     }
 
+    // The split-K reduce of P~ into tPt, or, when the one-workgroup
+    // orthonormalisation follows, left to that kernel (it sums the slices as
+    // it loads P~, in the same order).
+    RedArgs pt_red{};
+    bool pt_red_pending = false;
+    auto reduce_pt = [&](const RedArgs& ra) -> hipError_t {
+      if (pl.small_ortho && small_ortho_reduce_ok(ra)) {
+        pt_red = ra;
+        pt_red_pending = true;
+        return hipSuccess;
+      }
+      return launch_reduce_splits(ra, nb, s);
+    };
+
     // Streaming sweeps (bf16 weights, r = 64, 128, 256 or 512): the pieces of
     // Q^T, then one pass over M and G into split-K slices.
     SweepArgs sw{};
@@ -177,7 +191,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
         ra.part = part_f; ra.part_member_stride = static_cast<int64_t>(mb / 4);
         ra.slice = m * r; ra.splits = pl.split_sl; ra.rows = mi; ra.cols = r;
         ra.out = tPt; ra.colsq = nullptr; ra.colsq_member_stride = 0;
-        ORTHO_TRY(launch_reduce_splits(ra, nb, s));
+        ORTHO_TRY(reduce_pt(ra));
       }
     }
 
@@ -194,7 +208,7 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       ra.part = part_f; ra.part_member_stride = static_cast<int64_t>(mb / 4);
       ra.slice = m * r; ra.splits = pl.split_left; ra.rows = mi; ra.cols = r;
       ra.out = tPt; ra.colsq = nullptr; ra.colsq_member_stride = 0;
-      ORTHO_TRY(launch_reduce_splits(ra, nb, s));
+      ORTHO_TRY(reduce_pt(ra));
     }
 
     // Orthonormalisation of P_tilde (Q-factor of its thin QR, diag(R) > 0):
@@ -224,6 +238,11 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
         // r <= 64 and a short P~: the whole chain in one workgroup per member
         SmallOrthoArgs so{};
         so.pt = tPt; so.out = tP1; so.out_bf16 = tPb; so.has_bf16 = bf; so.m = mi; so.ca = ca;
+        if (pt_red_pending) {   // sweep 1's split-K slices, summed by the kernel
+          so.part = pt_red.part; so.part_member_stride = pt_red.part_member_stride;
+          so.slice = pt_red.slice; so.splits = pt_red.splits;
+          pt_red_pending = false;
+        }
         ORTHO_TRY(launch_small_ortho(so, nb, s));
       } else {
         // T1^T in fp64 into the scaled-Gram region (free once the chain is
@@ -393,12 +412,11 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     rr.out = tR;
     rr.colsq = reinterpret_cast<float*>(base + pl.off_colsq);
     rr.colsq_member_stride = static_cast<int64_t>(mb / 4);
-    ORTHO_TRY(launch_reduce_splits(rr, nb, s));
     ColnormArgs cn{};
     cn.r = tR; cn.q = tQ; cn.colsq = rr.colsq; cn.colsq_member_stride = rr.colsq_member_stride;
     cn.nrb = pl.nrb; cn.rows = ni; cn.cols = r; cn.status = status;
     cn.rb = tRb; cn.qb = tQb; cn.c1 = 1.0f - mu; cn.c2 = lr * scale; cn.has_bf16 = bf;
-    ORTHO_TRY(launch_colnorm(cn, nb, s));
+    ORTHO_TRY(launch_reduce_colnorm(rr, cn, nb, s));
 
     if (P_out)
       ORTHO_TRY(hipMemcpy2DAsync(P_out->data, P_out->ld * 4, base + off_p, rp * 4, r * 4, m,

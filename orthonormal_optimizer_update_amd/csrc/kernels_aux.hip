@@ -361,6 +361,96 @@ __global__ __launch_bounds__(256) void colnorm_kernel(ColnormArgs a) {
   }
 }
 
+// The split-K reduce of a short R (rows <= kFusedColnormRows) fused with its
+// column normalisation: one workgroup of 1024 threads per 64 columns per
+// member; thread (rg, cq) holds four columns of rows rg, rg + 64, ... (at most
+// 16).  Every slice load of a thread is issued before the sums are used; each
+// row's slices are added in slice order (the bits reduce_splits_vec_kernel
+// stores).  R is written, the squares go into per-thread column sums, the 64
+// row groups are added in order and 1/|R[:, j]| formed as in
+// colnorm_inv_kernel (zero column: 0 and ORTHO_DEV_ZERO_COLUMN; NaN
+// propagates); then Q' = R diag(inv) and the bf16 operands from the rows
+// still in registers, as colnorm_kernel.  cols % 4 == 0 and 16-byte aligned
+// slices (the launcher checks); RPT = rows per thread, rows <= 64 RPT (a
+// compile-time count: the loads of every row are unconditional, at clamped
+// addresses, so that they are all in flight before the first add).
+// grid (ceil(cols / 64), members).
+template <int RPT>
+__global__ __launch_bounds__(1024) void reduce_colnorm_kernel(RedArgs a, ColnormArgs cn) {
+  constexpr int kRowsPerThread = RPT;
+  __shared__ float red[64][65];
+  __shared__ float inv[64];
+  const int bi = blockIdx.y;
+  const float* part = a.part + bi * a.part_member_stride;
+  float* out = static_cast<float*>(const_cast<void*>(a.out.p[bi]));
+  const int cq = threadIdx.x & 15, rg = threadIdx.x >> 4;
+  const int c = blockIdx.x * 64 + cq * 4;
+  const bool act = c < a.cols;
+  const int cl = min(c, a.cols - 4);   // clamped: every load stays inside a row
+  floatx4 v[kRowsPerThread];
+#pragma unroll
+  for (int j = 0; j < kRowsPerThread; ++j) v[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < a.splits; ++k) {
+    const float* src = part + k * a.slice + cl;
+#pragma unroll
+    for (int j = 0; j < kRowsPerThread; ++j)
+      v[j] += *reinterpret_cast<const floatx4*>(src + (int64_t)min(rg + 64 * j, a.rows - 1) * a.cols);
+  }
+  floatx4 sq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kRowsPerThread; ++j) {
+    const int row = rg + 64 * j;
+    if (act && row < a.rows) {
+      *reinterpret_cast<floatx4*>(out + (int64_t)row * a.out.ld + c) = v[j];
+      sq += v[j] * v[j];
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) red[rg][cq * 4 + t] = sq[t];
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int cc = blockIdx.x * 64 + threadIdx.x;
+    float w = 0.f;
+    if (cc < a.cols) {
+      float t = 0.f;
+      for (int g = 0; g < 64; ++g) t += red[g][threadIdx.x];
+      if (t > 0.f) {
+        w = 1.0f / sqrtf(t);
+      } else if (!(t != t)) {
+        w = 0.f;
+        if (cn.status) atomicOr(cn.status, 2);
+      } else {
+        w = t;
+      }
+    }
+    inv[threadIdx.x] = w;
+  }
+  __syncthreads();
+  if (!act) return;
+  float* q = static_cast<float*>(const_cast<void*>(cn.q.p[bi]));
+  uint16_t* rb = cn.has_bf16 ? static_cast<uint16_t*>(const_cast<void*>(cn.rb.p[bi])) : nullptr;
+  uint16_t* qb = cn.has_bf16 ? static_cast<uint16_t*>(const_cast<void*>(cn.qb.p[bi])) : nullptr;
+  const floatx4 iv = {inv[cq * 4 + 0], inv[cq * 4 + 1], inv[cq * 4 + 2], inv[cq * 4 + 3]};
+#pragma unroll
+  for (int j = 0; j < kRowsPerThread; ++j) {
+    const int row = rg + 64 * j;
+    if (row >= a.rows) break;
+    const floatx4 qv = v[j] * iv;
+    float* qrow = q + (int64_t)row * cn.q.ld;
+    if (cn.q.vec) {
+      *reinterpret_cast<floatx4*>(qrow + c) = qv;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) qrow[c + t] = qv[t];
+    }
+    if (rb) {
+      const floatx4 rs = cn.c1 * v[j], qs = cn.c2 * qv;
+      *reinterpret_cast<uint2*>(rb + (int64_t)row * cn.rb.ld + c) = pack_bf16x4(rs);
+      *reinterpret_cast<uint2*>(qb + (int64_t)row * cn.qb.ld + c) = pack_bf16x4(qs);
+    }
+  }
+}
+
 // Newton-Schulz polynomial for a Gram side of M = 64 or 128 rows, fused with the
 // reduction of the split Gram.  One workgroup per member: A = the sum of the
 // k-split partials in slice order, rounded to bf16 into LDS (the value the
@@ -1362,9 +1452,35 @@ __global__ __launch_bounds__(256) void small_ortho_kernel(SmallOrthoArgs a) {
 
   // 0. P~ (m x r, zero-padded to 64 columns and to a multiple of 16 rows) into
   // LDS, every load of a thread issued before any store: float4 loads when the
-  // rows allow them (a uniform test), else element-wise in passes of 64 rows
+  // rows allow them (a uniform test), else element-wise in passes of 64 rows;
+  // or, with split-K slices, their sum in slice order (16-byte aligned)
   const int mp = (m + 15) & ~15;
-  if (a.pt.vec && (r & 3) == 0 && (ldp & 3) == 0) {
+  if (a.splits > 0) {
+    const float* part = a.part + member * a.part_member_stride;
+    float4 v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < a.splits; ++k) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int e = threadIdx.x + q * 256;
+        const int i = e >> 4, c4 = (e & 15) * 4;
+        // unconditional load and add (rows and columns past the end are
+        // clamped here and zeroed at the store): a conditional add would let
+        // the compiler move the load under the condition and wait on each
+        const float4 x = *reinterpret_cast<const float4*>(part + k * a.slice + (int64_t)min(i, m - 1) * r +
+                                                          min(c4, r - 4));
+        v[q].x += x.x; v[q].y += x.y; v[q].z += x.z; v[q].w += x.w;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = threadIdx.x + q * 256;
+      const int i = e >> 4, c4 = (e & 15) * 4;
+      const float4 z = (i < m && c4 < r) ? v[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i < mp) *reinterpret_cast<float4*>(sp + i * kSoPitch + c4) = z;
+    }
+  } else if (a.pt.vec && (r & 3) == 0 && (ldp & 3) == 0) {
     float4 v[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
@@ -2027,6 +2143,31 @@ hipError_t launch_split_t(const SplitTArgs& a, int members, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_reduce_colnorm(const RedArgs& a, const ColnormArgs& cn, int members, hipStream_t s) {
+  const bool fused = a.rows <= kFusedColnormRows && a.cols % 4 == 0 && a.slice % 4 == 0 &&
+                     a.part_member_stride % 4 == 0 && a.out.vec &&
+                     (reinterpret_cast<uintptr_t>(a.part) & 15) == 0 && cn.rows == a.rows &&
+                     cn.cols == a.cols && (!cn.has_bf16 || (cn.rb.vec && cn.qb.vec));
+  if (!fused) {
+    const hipError_t e = launch_reduce_splits(a, members, s);
+    if (e != hipSuccess) return e;
+    return launch_colnorm(cn, members, s);
+  }
+  const dim3 grid(cdiv(a.cols, 64), members);
+  const int rpt = cdiv(a.rows, 64);
+  if (rpt <= 1) hipLaunchKernelGGL(reduce_colnorm_kernel<1>, grid, dim3(1024), 0, s, a, cn);
+  else if (rpt <= 2) hipLaunchKernelGGL(reduce_colnorm_kernel<2>, grid, dim3(1024), 0, s, a, cn);
+  else if (rpt <= 4) hipLaunchKernelGGL(reduce_colnorm_kernel<4>, grid, dim3(1024), 0, s, a, cn);
+  else if (rpt <= 8) hipLaunchKernelGGL(reduce_colnorm_kernel<8>, grid, dim3(1024), 0, s, a, cn);
+  else hipLaunchKernelGGL(reduce_colnorm_kernel<kFusedColnormRows / 64>, grid, dim3(1024), 0, s, a, cn);
+  return hipGetLastError();
+}
+
+bool small_ortho_reduce_ok(const RedArgs& a) {
+  return a.splits > 0 && a.cols % 4 == 0 && a.slice % 4 == 0 && a.part_member_stride % 4 == 0 &&
+         (reinterpret_cast<uintptr_t>(a.part) & 15) == 0;
+}
+
 hipError_t launch_colnorm(const ColnormArgs& a, int members, hipStream_t s) {
   hipLaunchKernelGGL(colnorm_inv_kernel, dim3(cdiv(a.cols, 64), members), dim3(256), 0, s, a);
   const hipError_t e = hipGetLastError();
@@ -2126,6 +2267,9 @@ hipError_t launch_cholesky_inverse(const CholArgs& a, float* tt, int64_t tt_stri
 
 hipError_t launch_small_ortho(const SmallOrthoArgs& a, int members, hipStream_t s) {
   if (a.ca.r < 1 || a.ca.r > 64 || a.m < 1 || a.m > 256) return hipErrorInvalidValue;
+  if (a.splits > 0 && (a.ca.r % 4 != 0 || a.slice % 4 != 0 || a.part_member_stride % 4 != 0 ||
+                       (reinterpret_cast<uintptr_t>(a.part) & 15) != 0))
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(small_ortho_kernel, dim3(members), dim3(256), 0, s, a);
   return hipGetLastError();
 }

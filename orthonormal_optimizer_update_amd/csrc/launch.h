@@ -150,6 +150,14 @@ hipError_t launch_reduce_pieces(const RedPiecesArgs& a, int members, hipStream_t
 
 hipError_t launch_reduce_splits(const RedArgs& a, int members, hipStream_t s);
 hipError_t launch_colnorm(const ColnormArgs& a, int members, hipStream_t s);
+// The split-K reduce of R followed by the column normalisation (a.out is cn.r):
+// one launch (reduce_colnorm_kernel) when R is short (rows <= kFusedColnormRows)
+// and the reduce's vector path applies, else the two launches above.
+constexpr int kFusedColnormRows = 1024;
+hipError_t launch_reduce_colnorm(const RedArgs& a, const ColnormArgs& cn, int members, hipStream_t s);
+// Whether small_ortho_kernel can sum P~'s split-K slices itself (see
+// SmallOrthoArgs::splits): 16-byte alignment of the slices and their rows.
+bool small_ortho_reduce_ok(const RedArgs& a);
 hipError_t launch_sumsq(const SumsqArgs& a, int nblocks, int members, bool bf16, hipStream_t s);
 hipError_t launch_ns_scale(const float* partial, int64_t partial_stride, int nparts, float* scale,
                            int64_t scale_stride, float eps, int members, hipStream_t s);
@@ -175,12 +183,18 @@ hipError_t launch_apply64(const Apply64Args& a, int members, hipStream_t s);
 // (small_ortho_kernel).  ca supplies r, the status word and the s / x
 // scratch that the diagonal factorisation writes; out must not alias pt.
 struct SmallOrthoArgs {
-  MatArg pt;                  // fp32 m x r
+  MatArg pt;                  // fp32 m x r (read when splits == 0)
   MatArg out;                 // fp32 m x r
   MatArg out_bf16;            // optional bf16 copy (has_bf16)
   int has_bf16;
   int m;
   CholArgs ca;
+  // splits > 0: P~ is instead the sum, in slice order, of `splits` split-K
+  // slices at part (ld r, slice stride `slice`, member stride
+  // part_member_stride), as reduce_splits_vec_kernel would store it
+  const float* part;
+  int64_t part_member_stride, slice;
+  int splits;
 };
 hipError_t launch_small_ortho(const SmallOrthoArgs& a, int members, hipStream_t s);
 
