@@ -361,10 +361,10 @@ __global__ __launch_bounds__(256) void colnorm_kernel(ColnormArgs a) {
   }
 }
 
-// The split-K reduce of a short R (rows <= kFusedColnormRows) fused with its
+// The split-K reduce of a short R (rows <= kFusedColnormRows = 512) fused with its
 // column normalisation: one workgroup of 1024 threads per 64 columns per
 // member; thread (rg, cq) holds four columns of rows rg, rg + 64, ... (at most
-// 16).  Every slice load of a thread is issued before the sums are used; each
+// 8).  Every slice load of a thread is issued before the sums are used; each
 // row's slices are added in slice order (the bits reduce_splits_vec_kernel
 // stores).  R is written, the squares go into per-thread column sums, the 64
 // row groups are added in order and 1/|R[:, j]| formed as in
@@ -2144,7 +2144,11 @@ hipError_t launch_split_t(const SplitTArgs& a, int members, hipStream_t s) {
 }
 
 hipError_t launch_reduce_colnorm(const RedArgs& a, const ColnormArgs& cn, int members, hipStream_t s) {
-  const bool fused = a.rows <= kFusedColnormRows && a.cols % 4 == 0 && a.slice % 4 == 0 &&
+  // one workgroup per 64 columns reads all of its slices: only while that is a
+  // few loads per thread (at 1024 x 64 with 16 slices it took 40 us longer
+  // than the three launches)
+  const bool fused = a.rows <= kFusedColnormRows && cdiv(a.rows, 64) * a.splits <= 16 &&
+                     a.cols % 4 == 0 && a.slice % 4 == 0 &&
                      a.part_member_stride % 4 == 0 && a.out.vec &&
                      (reinterpret_cast<uintptr_t>(a.part) & 15) == 0 && cn.rows == a.rows &&
                      cn.cols == a.cols && (!cn.has_bf16 || (cn.rb.vec && cn.qb.vec));
@@ -2158,7 +2162,6 @@ hipError_t launch_reduce_colnorm(const RedArgs& a, const ColnormArgs& cn, int me
   if (rpt <= 1) hipLaunchKernelGGL(reduce_colnorm_kernel<1>, grid, dim3(1024), 0, s, a, cn);
   else if (rpt <= 2) hipLaunchKernelGGL(reduce_colnorm_kernel<2>, grid, dim3(1024), 0, s, a, cn);
   else if (rpt <= 4) hipLaunchKernelGGL(reduce_colnorm_kernel<4>, grid, dim3(1024), 0, s, a, cn);
-  else if (rpt <= 8) hipLaunchKernelGGL(reduce_colnorm_kernel<8>, grid, dim3(1024), 0, s, a, cn);
   else hipLaunchKernelGGL(reduce_colnorm_kernel<kFusedColnormRows / 64>, grid, dim3(1024), 0, s, a, cn);
   return hipGetLastError();
 }

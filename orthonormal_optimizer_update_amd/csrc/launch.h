@@ -151,9 +151,10 @@ hipError_t launch_reduce_pieces(const RedPiecesArgs& a, int members, hipStream_t
 hipError_t launch_reduce_splits(const RedArgs& a, int members, hipStream_t s);
 hipError_t launch_colnorm(const ColnormArgs& a, int members, hipStream_t s);
 // The split-K reduce of R followed by the column normalisation (a.out is cn.r):
-// one launch (reduce_colnorm_kernel) when R is short (rows <= kFusedColnormRows)
-// and the reduce's vector path applies, else the two launches above.
-constexpr int kFusedColnormRows = 1024;
+// one launch (reduce_colnorm_kernel) when R is short (rows <= kFusedColnormRows,
+// at most 16 slice loads per thread) and the reduce's vector path applies, else
+// the launches above.
+constexpr int kFusedColnormRows = 512;
 hipError_t launch_reduce_colnorm(const RedArgs& a, const ColnormArgs& cn, int members, hipStream_t s);
 // Whether small_ortho_kernel can sum P~'s split-K slices itself (see
 // SmallOrthoArgs::splits): 16-byte alignment of the slices and their rows.
