@@ -108,6 +108,17 @@ def test_ns_wide_2048x8192_deterministic():
     assert np.array_equal(got, again)
 
 
+def test_ns_tall_4096x2048():
+    """A tall 4096 x 2048 matrix: the iteration runs on the transpose (Gram side
+    2048, the 256 x 256 products) and the last apply writes the bf16 output
+    transposed, through the LDS-staged row pieces of the transposed tile."""
+    G = synth.gradient(13, 4096, 2048, 1, "bf16")
+    note("ns 4096x2048 tall")
+    got = gpu_ns(G, "bf16")
+    assert got.shape == (4096, 2048)
+    assert rel(got, oracle.newton_schulz(G)) <= TOL["bf16"]
+
+
 def test_ns_square_4096_deterministic():
     """Two runs of the 4096 x 4096 iteration give the same bits."""
     G = synth.gradient(12, 4096, 4096, 1, "bf16")
