@@ -164,7 +164,9 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       sw.m = tM; sw.g = user_table(G, b0, nb, 16);
       sw.f[0] = ws_table(base, mb, pl.off_qhit, nb, n, r, ni, 2, 16);
       sw.f[1] = ws_table(base, mb, pl.off_qlot, nb, n, r, ni, 2, 16);
-      sw.out = part_f; sw.out_member_stride = static_cast<int64_t>(mb / 4);
+      // one k slice: the sweep writes P~ itself (ld r), no reduce follows
+      sw.out = pl.split_sl == 1 ? reinterpret_cast<float*>(base + pl.off_pt) : part_f;
+      sw.out_member_stride = static_cast<int64_t>(mb / 4);
       sw.split_stride = m * r;
       sw.rows = mi; sw.K = ni; sw.r = r; sw.kchunk = pl.kchunk_sl; sw.M_rows = mi;
       stream_sw = dion_sweep_ok(sw, nb);
@@ -176,7 +178,9 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       qa.src = tQ; qa.hit = sw.f[0]; qa.lot = sw.f[1]; qa.rows = ni; qa.cols = r; qa.blocked = 1;
       ORTHO_TRY(launch_split_t(qa, nb, s));
       ORTHO_TRY(launch_dion_sweep(sw, false, nb, s));
-      if (fast_or) {
+      if (pl.split_sl == 1 && !fast_or) {
+        // P~ is already in tPt
+      } else if (fast_or) {
         // the reduce also writes the bf16x3 pieces of P_tilde for P1 = P~ T1
         RedPiecesArgs ra{};
         ra.part = part_f; ra.part_member_stride = static_cast<int64_t>(mb / 4);
@@ -395,6 +399,8 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
       sr.f[1] = ws_table(base, mb, pl.off_plot, nb, m, r, mi, 2, 16);
       sr.split_stride = n * r;
       sr.rows = ni; sr.K = mi; sr.kchunk = pl.kchunk_sr;
+      // one k slice: the sweep writes R itself (ld r), the reduce only sums squares
+      sr.out = pl.split_sr == 1 ? reinterpret_cast<float*>(base + pl.off_r) : part_f;
       // (the pieces were written by the last orthonormalisation product)
       ORTHO_TRY(launch_dion_sweep(sr, true, nb, s));
       split_r = pl.split_sr;
@@ -410,6 +416,10 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
     rr.part = part_f; rr.part_member_stride = static_cast<int64_t>(mb / 4);
     rr.slice = n * r; rr.splits = split_r; rr.rows = ni; rr.cols = r;
     rr.out = tR;
+    if (stream_sw && split_r == 1) {
+      rr.part = reinterpret_cast<const float*>(base + pl.off_r);
+      rr.no_store = 1;
+    }
     rr.colsq = reinterpret_cast<float*>(base + pl.off_colsq);
     rr.colsq_member_stride = static_cast<int64_t>(mb / 4);
     ColnormArgs cn{};

@@ -28,7 +28,7 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(RedArgs a) {
       if (r >= a.rows) break;
       float s = 0.f;
       for (int k = 0; k < a.splits; ++k) s += part[k * a.slice + (int64_t)r * a.cols + c];
-      out[(int64_t)r * a.out.ld + c] = s;
+      if (!a.no_store) out[(int64_t)r * a.out.ld + c] = s;
       sq += s * s;
     }
   }
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void reduce_splits_vec_kernel(RedArgs a) {
       floatx4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
       for (int k = 0; k < a.splits; ++k) s += *reinterpret_cast<const floatx4*>(src + k * a.slice);
-      *reinterpret_cast<floatx4*>(out + (int64_t)r * a.out.ld + c) = s;
+      if (!a.no_store) *reinterpret_cast<floatx4*>(out + (int64_t)r * a.out.ld + c) = s;
       if (a.has_bf16) {
         uint16_t* ob = static_cast<uint16_t*>(const_cast<void*>(a.out_bf16.p[bi]));
         const uint16_t h[4] = {to_bf16_bits(s[0]), to_bf16_bits(s[1]), to_bf16_bits(s[2]),
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(1024) void reduce_colnorm_kernel(RedArgs a, Colnorm
   for (int j = 0; j < kRowsPerThread; ++j) {
     const int row = rg + 64 * j;
     if (act && row < a.rows) {
-      *reinterpret_cast<floatx4*>(out + (int64_t)row * a.out.ld + c) = v[j];
+      if (!a.no_store) *reinterpret_cast<floatx4*>(out + (int64_t)row * a.out.ld + c) = v[j];
       sq += v[j] * v[j];
     }
   }

@@ -18,6 +18,7 @@ struct RedArgs {
   int has_bf16;
   float* colsq;               // optional per-64-row-block column sums of squares
   int64_t colsq_member_stride;
+  int no_store;               // splits == 1 and part is out's memory: column sums only
 };
 
 struct ColnormArgs {
