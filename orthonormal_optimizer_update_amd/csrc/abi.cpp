@@ -257,15 +257,28 @@ ortho_status run_dion(int32_t batch, const ortho_mat* X, const ortho_mat* G, con
         Apply64Args a64{};
         a64.pt = tPt; a64.t = ttd; a64.t_member_stride = static_cast<int64_t>(mb / 8);
         a64.out = tP1; a64.out_bf16 = tPb; a64.has_bf16 = bf; a64.m = mi; a64.r = r;
+        // the fragment-order copy and sweep 2's transposed pieces from the same
+        // tiles (every path that reads them has m and r multiples of 64)
+        if (bf && pl.frag_p) {
+          a64.frag = ws_table(base, mb, pl.off_pf, nb, r, mi, r, 2, 16);
+          a64.has_frag = 1;
+        }
+        if (stream_sw || fast_sw) {
+          a64.tpiece[0] = ws_table(base, mb, pl.off_phit, nb, m, r, mi, 2, 16);
+          a64.tpiece[1] = ws_table(base, mb, pl.off_plot, nb, m, r, mi, 2, 16);
+          a64.has_t = 1;
+          a64.t_blocked = stream_sw;
+        }
         ORTHO_TRY(launch_apply64(a64, nb, s));
       }
       tP = tP1;
       off_p = pl.off_p1;
-      // the fragment-order copy (streaming update) and the transposed pieces
-      // (sweep 2: k-blocked for the streaming kernel, ld m for the 256 x 256
-      // one); every path that reads them has m and r multiples of 64
-      const bool need_frag = bf && pl.frag_p;
-      const bool need_t = stream_sw || fast_sw;
+      // after the one-workgroup path: the fragment-order copy (streaming
+      // update) and the transposed pieces (sweep 2: k-blocked for the
+      // streaming kernel, ld m for the 256 x 256 one); every path that reads
+      // them has m and r multiples of 64
+      const bool need_frag = pl.small_ortho && bf && pl.frag_p;
+      const bool need_t = pl.small_ortho && (stream_sw || fast_sw);
       if (need_frag || need_t) {
         RedPiecesArgs rd{};
         rd.part = reinterpret_cast<const float*>(base + pl.off_p1);

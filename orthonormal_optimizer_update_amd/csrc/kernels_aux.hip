@@ -2028,20 +2028,87 @@ __global__ __launch_bounds__(256) void apply64_kernel(Apply64Args a) {
   }
   float* out = static_cast<float*>(const_cast<void*>(a.out.p[member]));
   uint16_t* ob = a.has_bf16 ? static_cast<uint16_t*>(const_cast<void*>(a.out_bf16.p[member])) : nullptr;
+  if (i0 + 64 > m || j0 + 64 > r || !a.out.vec || (ob && !a.out_bf16.vec)) {
+    // a ragged tile (or rows without 16-byte alignment): element by element
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = i0 + wa * 32 + i * 16 + (lane >> 4) + 4 * e;
+          const int col = j0 + wb * 32 + j * 16 + (lane & 15);
+          if (row < m && col < r) {
+            const float v = static_cast<float>(acc[i][j][e]);
+            out[(int64_t)row * a.out.ld + col] = v;
+            if (ob) ob[(int64_t)row * a.out_bf16.ld + col] = to_bf16_bits(v);
+          }
+        }
+    return;
+  }
+  // A whole tile goes through LDS (the operand stages, free now) as fp32, so
+  // that each thread stores four consecutive columns of four rows: P, its bf16
+  // copy, and (has_frag, has_t) the layouts the update and sweep 2 read, which
+  // a separate pass over P would otherwise write (reduce_pieces_kernel).
+  __syncthreads();   // every wave is done with sa and sb
+  float (*tile)[68] = reinterpret_cast<float (*)[68]>(&sa[0][0][0]);
+  uint16_t (*th)[68] = reinterpret_cast<uint16_t (*)[68]>(&sb[0][0][0]);
+  uint16_t (*tl)[68] = th + 64;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
+      for (int e = 0; e < 4; ++e)
+        tile[wa * 32 + i * 16 + (lane >> 4) + 4 * e][wb * 32 + j * 16 + (lane & 15)] =
+            static_cast<float>(acc[i][j][e]);
+  __syncthreads();
+  const int cl = (threadIdx.x & 15) * 4;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int rl = (threadIdx.x >> 4) + 16 * q;
+    const int64_t row = i0 + rl;
+    const floatx4 v = *reinterpret_cast<const floatx4*>(&tile[rl][cl]);
+    *reinterpret_cast<floatx4*>(out + row * a.out.ld + j0 + cl) = v;
+    const uint16_t h[4] = {to_bf16_bits(v[0]), to_bf16_bits(v[1]), to_bf16_bits(v[2]), to_bf16_bits(v[3])};
+    if (ob) *reinterpret_cast<uint2*>(ob + row * a.out_bf16.ld + j0 + cl) = pack4(h);
+    if (a.has_frag) {
+      // element (row, k): (((row / 32) * r / 16 + k / 16) * 64 + row % 32 +
+      // 32 * (k / 8 % 2)) * 8 + k % 8; k = j0 + cl .. + 3 share one 8-group
+      const int k = j0 + cl;
+      const int64_t o = (((row >> 5) * (r >> 4) + (k >> 4)) * 64 + (row & 31) + 32 * ((k >> 3) & 1)) * 8 + (k & 7);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(const_cast<void*>(a.frag.p[member])) + o) = pack4(h);
+    }
+    if (a.has_t) {
+#pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = i0 + wa * 32 + i * 16 + (lane >> 4) + 4 * e;
-        const int col = j0 + wb * 32 + j * 16 + (lane & 15);
-        if (row < m && col < r) {
-          const float v = static_cast<float>(acc[i][j][e]);
-          out[(int64_t)row * a.out.ld + col] = v;
-          if (ob) ob[(int64_t)row * a.out_bf16.ld + col] = to_bf16_bits(v);
-        }
+        bf16 bh, bl;
+        split_bf16(v[e], bh, bl);
+        th[cl + e][rl] = __builtin_bit_cast(uint16_t, bh);
+        tl[cl + e][rl] = __builtin_bit_cast(uint16_t, bl);
       }
+    }
+  }
+  if (!a.has_t) return;   // uniform over the grid
+  __syncthreads();
+  uint16_t* hit = static_cast<uint16_t*>(const_cast<void*>(a.tpiece[0].p[member]));
+  uint16_t* lot = static_cast<uint16_t*>(const_cast<void*>(a.tpiece[1].p[member]));
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int j = (threadIdx.x >> 4) + 16 * q;   // row of the transposed tile
+    const int i4 = (threadIdx.x & 15) * 4;
+    uint16_t hh[4], ll[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hh[e] = th[j][i4 + e];
+      ll[e] = tl[j][i4 + e];
+    }
+    const int64_t ot = a.t_blocked
+        ? (int64_t)((i0 + i4) >> 4) * r * 16 + (int64_t)(j0 + j) * 16 + ((i0 + i4) & 15)
+        : (int64_t)(j0 + j) * a.tpiece[0].ld + i0 + i4;
+    *reinterpret_cast<uint2*>(hit + ot) = pack4(hh);
+    *reinterpret_cast<uint2*>(lot + ot) = pack4(ll);
+  }
 }
 
 // First-order correction of a nearly orthonormal basis P1: with
@@ -2279,6 +2346,10 @@ hipError_t launch_small_ortho(const SmallOrthoArgs& a, int members, hipStream_t 
 
 hipError_t launch_apply64(const Apply64Args& a, int members, hipStream_t s) {
   if (a.m < 1 || a.r < 1 || a.t == nullptr) return hipErrorInvalidValue;
+  // the extra layouts come from whole 64 x 64 tiles, 16-byte aligned rows
+  if ((a.has_frag || a.has_t) && (a.m % 64 != 0 || a.r % 64 != 0 || !a.out.vec ||
+                                  (a.has_bf16 && !a.out_bf16.vec)))
+    return hipErrorInvalidValue;
   const int tiles = cdiv(a.m, 64) * cdiv(a.r, 64);
   hipLaunchKernelGGL(apply64_kernel, dim3(tiles, members), dim3(256), 0, s, a);
   return hipGetLastError();

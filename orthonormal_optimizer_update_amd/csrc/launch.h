@@ -177,6 +177,13 @@ struct Apply64Args {
   MatArg out_bf16;            // optional bf16 copy (has_bf16)
   int has_bf16;
   int m, r;
+  // optional further copies of P (m and r multiples of 64), in the layouts of
+  // reduce_pieces_kernel: bf16 in MFMA fragment order (has_frag) and the
+  // transposed hi / lo pieces (has_t; k-blocked when t_blocked)
+  MatArg frag;
+  int has_frag;
+  MatArg tpiece[2];
+  int has_t, t_blocked;
 };
 hipError_t launch_apply64(const Apply64Args& a, int members, hipStream_t s);
 
