@@ -67,33 +67,9 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
-// wait until at most `later` stages of PER copies each are outstanding
-template <int PER>
-__device__ __forceinline__ void wait_later(int later) {
-  switch (later) {
-    case 0: wait_vm<0>(); break;
-    case 1: wait_vm<PER>(); break;
-    case 2: wait_vm<2 * PER>(); break;
-    case 3: wait_vm<3 * PER>(); break;
-    case 4: wait_vm<4 * PER>(); break;
-    case 5: wait_vm<5 * PER>(); break;
-    default: wait_vm<6 * PER>(); break;
-  }
-}
-
-__device__ __forceinline__ float2 bf16x2_to_f32(uint32_t u) {
-  return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
-}
-
-// 8 fp32 values as two bf16 pieces (x = hi + lo + O(2^-16 |x|)).
-__device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const bf16 h = to_bf16(x[t]);
-    hi[t] = h;
-    lo[t] = to_bf16(x[t] - static_cast<float>(h));
-  }
-}
+// s_waitcnt lgkmcnt(0) as the compiler's own wait instruction (vmcnt and
+// expcnt at their maxima), which its wait insertion takes into account
+__device__ __forceinline__ void lds_reads_done() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
 }  // namespace
 
@@ -201,11 +177,19 @@ __global__ __launch_bounds__(512, 1) void dion_sweep_kernel(SweepArgs a) {
       dma16(off[u], uniform_ptr(base), lds0 + buf * L::kStageBytes + c * 1024);
     }
   };
-  // wait until at most `later` stages of this wave's copies are outstanding
+  // wait until at most `later` stages of this wave's copies are outstanding:
+  // the steady state (kStages - 3 later stages in flight) has its own
+  // immediate count, any other case waits for all copies (vector memory
+  // loads complete in order, so a smaller count is always safe)
   auto wait_stages = [&](int later) {
-    static_assert(kStages <= 8 && 6 * L::kMaxPerWave < 64, "wait cases cover up to six later stages");
-    if (ncopy == L::kLo) wait_later<L::kLo>(later);
-    else wait_later<L::kMaxPerWave>(later);
+    constexpr int kSteady = kStages > 3 ? kStages - 3 : 0;
+    static_assert(kSteady * L::kMaxPerWave < 64, "vmcnt range");
+    if (later >= kSteady) {
+      if (ncopy == L::kLo) wait_vm<kSteady * L::kLo>();
+      else wait_vm<kSteady * L::kMaxPerWave>();
+    } else {
+      wait_vm<0>();
+    }
   };
 
   // wave (rb, ch): output rows rb * 32 .. + 31, columns ch * R / 2 .. + R / 2 - 1
@@ -235,35 +219,52 @@ __global__ __launch_bounds__(512, 1) void dion_sweep_kernel(SweepArgs a) {
       fb[buf][j][pc] = *reinterpret_cast<const bf16x8*>(sp + pc * L::kPieceBytes + o);
     }
   };
-  // the A fragment of stage st into fa[buf]: B = M + G split into hi and lo
-  auto read_a = [&](int st, int buf) {
+  // The A fragment of a stage (output row rl, k = half*8 .. + 7 of the
+  // stage) in two phases: the raw M and G values from LDS, then B = M + G in
+  // fp32 split into bf16 hi and lo, in four parts of two k each, so the
+  // conversions can sit between the products of the previous stage instead
+  // of waiting on the LDS reads ahead of them.
+  float rm[8];
+  uint32_t rg[8];   // G's bf16 bits: two k per word (sweep 1), one per word (sweep 2)
+  auto load_a = [&](int st) {
     const char* sb = smem + (st % kStages) * L::kStageBytes;
     const float* sm = reinterpret_cast<const float*>(sb);
     const uint16_t* sg = reinterpret_cast<const uint16_t*>(sb + kMBytes);
-    // output row rl, k = half*8 .. + 7 of the stage
-    float x[8];
     if (!TRANS) {
       const floatx4 m0 = *reinterpret_cast<const floatx4*>(sm + rl * 16 + (((2 * half) ^ ((rl >> 2) & 3)) * 4));
       const floatx4 m1 = *reinterpret_cast<const floatx4*>(sm + rl * 16 + (((2 * half + 1) ^ ((rl >> 2) & 3)) * 4));
       const uint4 g = *reinterpret_cast<const uint4*>(sg + rl * 16 + ((half ^ ((rl >> 3) & 1)) * 8));
-      const float2 g0 = bf16x2_to_f32(g.x), g1 = bf16x2_to_f32(g.y), g2 = bf16x2_to_f32(g.z),
-                   g3 = bf16x2_to_f32(g.w);
-      x[0] = m0[0] + g0.x; x[1] = m0[1] + g0.y; x[2] = m0[2] + g1.x; x[3] = m0[3] + g1.y;
-      x[4] = m1[0] + g2.x; x[5] = m1[1] + g2.y; x[6] = m1[2] + g3.x; x[7] = m1[3] + g3.y;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) { rm[t] = m0[t]; rm[4 + t] = m1[t]; }
+      rg[0] = g.x; rg[1] = g.y; rg[2] = g.z; rg[3] = g.w;   // two k per word
     } else {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const int kr = half * 8 + t;
-        x[t] = sm[kr * 128 + rl] + bf16_bits_to_f32(sg[kr * 128 + rl]);
+        rm[t] = sm[kr * 128 + rl];
+        rg[t] = sg[kr * 128 + rl];
       }
     }
-    split8(x, fa[buf][0], fa[buf][1]);
   };
-  auto read_frags = [&](int st, auto buf_c) {
-    constexpr int buf = decltype(buf_c)::value;
-    read_a(st, buf);
-    read_factor(st, buf, 0);
-    read_factor(st, buf, 1);
+  // part p (k = 2p, 2p + 1) of the split of the loaded values into fa[buf]
+  auto convert_a = [&](int p, int buf) {
+#pragma unroll
+    for (int t = 2 * p; t < 2 * p + 2; ++t) {
+      const uint32_t gb = TRANS ? (rg[t] << 16)
+                                : ((t & 1) ? (rg[t >> 1] & 0xffff0000u) : (rg[t >> 1] << 16));
+      const float x = rm[t] + __uint_as_float(gb);
+      const bf16 h = to_bf16(x);
+      fa[buf][0][t] = h;
+      fa[buf][1][t] = to_bf16(x - static_cast<float>(h));
+    }
+    // pin the part here: without this the compiler sinks the arithmetic to
+    // its first use, past the next barrier, where nothing hides it
+    asm volatile("" : "+v"(fa[buf][0]), "+v"(fa[buf][1]));
+  };
+  auto read_a = [&](int st, int buf) {
+    load_a(st);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) convert_a(p, buf);
   };
   // wait until this wave's copies of stage `st` are done (at most the stages
   // issued after it still outstanding), then the barrier makes every wave's
@@ -281,18 +282,25 @@ __global__ __launch_bounds__(512, 1) void dion_sweep_kernel(SweepArgs a) {
     if (st < nst) issue(st);
   int issued_last = min(kStages - 2, nst - 1);
   ready(0, issued_last);
-  if constexpr (R == 512) {
-    read_a(0, 0);
-    read_factor(0, 0, 0);
-    read_factor(0, 0, 1);
-  } else {
-    read_frags(0, std::integral_constant<int, 0>{});
-  }
+  read_a(0, 0);
+  read_factor(0, 0, 0);
+  read_factor(0, 0, 1);
 
+  // MFMA q of a step's t products after which part p of the next stage's A
+  // conversion runs: the last parts as late as possible, two products apart,
+  // none before the middle, so the raw reads have landed
+  auto conv_slot = [](int p, int t) {
+    const int q = t - 1 - 2 * (3 - p);
+    return q > t / 2 ? q : t / 2;
+  };
   // one stage whose fragments are in buffer CUR (a compile-time index, so the
-  // fragments stay in registers); the next stage's go to buffer CUR ^ 1
+  // fragments stay in registers); the next stage's raw A values and factor
+  // fragments are read ahead of the products and its A fragment is built
+  // into buffer CUR ^ 1 between them.  Past the last stage the reads hit a
+  // stale buffer and the values go unused.
   auto step = [&](auto cur_c, int st) {
     constexpr int CUR = decltype(cur_c)::value;
+    constexpr int T = 3 * NB;
     if (st + 1 < nst) {
       // stage st + 1 in LDS; after this barrier every wave has read stage st's
       // fragments (previous step), so the buffer of stage st - 1 is free
@@ -301,18 +309,27 @@ __global__ __launch_bounds__(512, 1) void dion_sweep_kernel(SweepArgs a) {
         issue(st + kStages - 1);
         issued_last = st + kStages - 1;
       }
-      read_frags(st + 1, std::integral_constant<int, CUR ^ 1>{});
     }
+    // the previous step's reads are long done; saying so here keeps the
+    // compiler from counting them behind this step's 24 reads (past the
+    // 15 the LDS counter holds) and waiting on those before the products
+    lds_reads_done();
+    load_a(st + 1);
+    read_factor(st + 1, CUR ^ 1, 0);
+    read_factor(st + 1, CUR ^ 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
     // each product kind over all accumulators before the next kind
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
-      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[CUR][0], fb[CUR][j][0], acc[j], 0, 0, 0);
+    for (int q = 0; q < T; ++q) {
+      const int kind = q / NB, j = q % NB;
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[CUR][kind == 2 ? 1 : 0],
+                                                       fb[CUR][j][kind == 1 ? 1 : 0], acc[j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
-      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[CUR][0], fb[CUR][j][1], acc[j], 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[CUR][1], fb[CUR][j][0], acc[j], 0, 0, 0);
+      for (int p = 0; p < 4; ++p)
+        if (conv_slot(p, T) == q) convert_a(p, CUR ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   // r = 512: fa[CUR] and fb[0] hold stage st on entry
   auto step512 = [&](auto cur_c, int st) {
@@ -328,17 +345,21 @@ __global__ __launch_bounds__(512, 1) void dion_sweep_kernel(SweepArgs a) {
         issue(st + kStages - 1);
         issued_last = st + kStages - 1;
       }
-      read_a(st + 1, CUR ^ 1);
+      lds_reads_done();
       read_factor(st + 1, 0, 1);
     }
+    load_a(st + 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
-      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[CUR][0], fb[0][j][0], acc[j], 0, 0, 0);
+    for (int q = 0; q < 2 * NB; ++q) {
+      const int j = q % NB;
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[CUR][q < NB ? 0 : 1], fb[0][j][0], acc[j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
-      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[CUR][1], fb[0][j][0], acc[j], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+      for (int p = 0; p < 4; ++p)
+        if (conv_slot(p, 2 * NB) == q) convert_a(p, CUR ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (more) read_factor(st + 1, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
