@@ -112,6 +112,52 @@ __device__ __forceinline__ void block_out(Epi& epi, const floatx16& acc, int r0,
   }
 }
 
+struct SymTile {
+  int tm, tn, half;
+};
+
+// Unit u of the ordered walk over the upper triangle of a t x t tile grid:
+// tile rows in order, each row's diagonal tile (one unit) first, then the two
+// 256 x 128 halves of each tile to its right.
+__host__ __device__ inline SymTile sym_walk(int t, int u) {
+  int tm = 0;
+  while (u >= 1 + 2 * (t - 1 - tm)) {
+    u -= 1 + 2 * (t - 1 - tm);
+    ++tm;
+  }
+  if (u == 0) return SymTile{tm, tm, 0};
+  return SymTile{tm, tm + 1 + (u - 1) / 2, (u - 1) & 1};
+}
+
+// Workgroup b of the nwg = T^2 units of a T x T tile grid (T diagonal tiles,
+// T (T - 1) halves).  Workgroups are dealt to the 8 XCDs round robin (XCD
+// b mod 8, in the order b / 8), and both operands of these products are row
+// blocks of one matrix, so an XCD's L2 fetches the union of the row blocks
+// its tiles touch.  With T = 4 s, the grid splits into 4 x 4 blocks of s x s
+// tiles: XCDs 0..5 each take one of the six blocks above the diagonal (2 s^2
+// units, 2 s distinct row blocks) and XCDs 6 and 7 two of the four diagonal
+// blocks each (s^2 units and s row blocks apiece): 16 s row blocks fetched
+// in all, against about twice that for runs of the row-ordered walk.  Any
+// other T takes, per XCD, a contiguous run of the walk.
+__host__ __device__ inline SymTile sym_tile(int t, int nwg, int b) {
+  if (nwg == t * t && t % 4 == 0) {
+    const int s = t / 4, x = b & 7, l = b >> 3;
+    if (x < 6) {
+      // off-diagonal block (bi, bj) of the 4 x 4 block grid, tiles in row order
+      const int bi = x < 3 ? 0 : (x < 5 ? 1 : 2);
+      const int bj = x < 3 ? x + 1 : (x < 5 ? x - 1 : 3);
+      const int i = l / (2 * s), rem = l - i * 2 * s;
+      return SymTile{bi * s + i, bj * s + rem / 2, rem & 1};
+    }
+    // diagonal blocks 2 (x - 6) and 2 (x - 6) + 1, s^2 units each
+    const int d = 2 * (x - 6) + (l >= s * s ? 1 : 0);
+    const SymTile w = sym_walk(s, l % (s * s));
+    return SymTile{d * s + w.tm, d * s + w.tn, w.half};
+  }
+  const int u = (nwg & 7) == 0 ? (b & 7) * (nwg >> 3) + (b >> 3) : b;
+  return sym_walk(t, u);
+}
+
 }  // namespace symk
 
 template <class Epi>
@@ -122,22 +168,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_sym(GemmParams<typename Epi:
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  // Workgroup -> tile.  Each XCD (workgroup id mod 8) takes a contiguous run
-  // of the ordered list; the list walks tile rows, each row's diagonal tile
-  // first, then the two halves of each tile to its right, so a run shares A
-  // row blocks in its XCD's L2.
-  const int T = p.tiles_n;
-  const int nwg = gridDim.x;
-  int t = blockIdx.x;
-  if ((nwg & 7) == 0) t = (t & 7) * (nwg >> 3) + (t >> 3);
-  int tm = 0, rem = t;
-  while (rem >= 1 + 2 * (T - 1 - tm)) {
-    rem -= 1 + 2 * (T - 1 - tm);
-    ++tm;
-  }
-  const bool diag = rem == 0;
-  const int tn = diag ? tm : tm + 1 + (rem - 1) / 2;
-  const int half = diag ? 0 : (rem - 1) & 1;
+  // Workgroup -> tile (symk::sym_tile): the tiles of one XCD share operand
+  // row blocks in its L2.
+  const symk::SymTile tile = symk::sym_tile(p.tiles_n, gridDim.x, blockIdx.x);
+  const int tm = tile.tm, tn = tile.tn, half = tile.half;
+  const bool diag = tm == tn;
   const int bi = blockIdx.y;
   const int m0 = tm * 256;
   const int n0 = tn * 256 + half * 128;
