@@ -42,7 +42,7 @@ PEAK_HBM_GBS = 8000.0
 # passes over `bench.py --counter-sample`, each scaled by the same counter's
 # reading for a 256 MiB elementwise copy (fetch factor 2.0, write factor 1.0).
 # Set to None whenever the kernel changes, until the passes are taken again.
-TRAFFIC_BYTES_PER_LAUNCH = 2.836e8
+TRAFFIC_BYTES_PER_LAUNCH = 2.412e8
 
 
 def parse():

@@ -1446,7 +1446,6 @@ __global__ __launch_bounds__(256) void small_ortho_kernel(SmallOrthoArgs a) {
   const int m = a.m, r = a.ca.r;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int wa = wave >> 1, wb = wave & 1;
   double (*L)[kCP] = LY[0];
   double (*Y)[kCP] = LY[1];
 
