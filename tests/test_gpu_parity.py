@@ -119,6 +119,20 @@ def test_ns_tall_4096x2048():
     assert rel(got, oracle.newton_schulz(G)) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("members,side", [(5, 1792), (4, 2048)])
+def test_ns_symmetric_tile_maps(members, side):
+    """The symmetric Gram and polynomial kernels' two workgroup-to-tile maps,
+    on batched groups large enough to take that kernel: 5 x 1792^2 (a 7 x 7
+    tile grid, not a multiple of four: each XCD a run of the row-ordered walk)
+    and 4 x 2048^2 (8 x 8: the XCD block partition with 2 x 2-tile blocks)."""
+    Gs = [synth.gradient(15, side, side, 1, "bf16", index=i) for i in range(members)]
+    note(f"ns batched {members} x {side}^2 symmetric tile maps")
+    outs = api.newton_schulz_batched([to_dev(g, "bf16") for g in Gs], steps=5)
+    torch.cuda.synchronize()
+    for i in range(members):
+        assert rel(to_host(outs[i]), oracle.newton_schulz(Gs[i])) <= TOL["bf16"], i
+
+
 def test_ns_square_4096_deterministic():
     """Two runs of the 4096 x 4096 iteration give the same bits."""
     G = synth.gradient(12, 4096, 4096, 1, "bf16")
