@@ -285,18 +285,30 @@ def workload_table(torch, api, synth, calls=10, only=None):
             for Xs, Gs, Ms, Qs, ws in groups:
                 api.dion_step_batched(Xs, Gs, Ms, Qs, wl["mu"], wl["lr"], ws=ws)
         ms = timed(gpt_step)
-        # The same step with each shape group's call on a stream of its own
-        # (separate workspaces, no shared state): one group's latency-bound
+        # The same step with each shape group's calls on streams of their own
+        # (separate workspaces, no shared state): one call's latency-bound
         # phases (the Cholesky chains, the small launches) run beside another
-        # group's products.
+        # call's products.
         main = torch.cuda.current_stream()
-        side = [torch.cuda.Stream() for _ in groups]
+        # a group of more than 32 matrices splits into calls of at most 32 (the
+        # library's launch chunk), each on its own stream, with its own workspace
+        chunks = []
+        for Xs, Gs, Ms, Qs, ws in groups:
+            if len(Xs) <= 32:
+                chunks.append((Xs, Gs, Ms, Qs, ws))
+                continue
+            m, n, r = Xs[0].size(0), Xs[0].size(1), Qs[0].size(1)
+            for c0 in range(0, len(Xs), 32):
+                sl = slice(c0, c0 + 32)
+                chunks.append((Xs[sl], Gs[sl], Ms[sl], Qs[sl],
+                              api.workspace(api.dion_workspace_size(m, n, r, len(Xs[sl])), dev)))
+        side = [torch.cuda.Stream() for _ in chunks]
 
         def gpt_step_streams():
             fork = torch.cuda.Event()
             fork.record(main)
             done = []
-            for st, (Xs, Gs, Ms, Qs, ws) in zip(side, groups):
+            for st, (Xs, Gs, Ms, Qs, ws) in zip(side, chunks):
                 st.wait_event(fork)
                 with torch.cuda.stream(st):
                     api.dion_step_batched(Xs, Gs, Ms, Qs, wl["mu"], wl["lr"], ws=ws)
@@ -311,7 +323,7 @@ def workload_table(torch, api, synth, calls=10, only=None):
                            "GB/s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
                            "TFLOP/s": flops / (ms * 1e-3) / 1e12,
                            "dion_r_quarter_group_streams_ms": ms_streams,
-                           "group_streams": len(groups)}
+                           "group_streams": len(chunks)}
         del groups
         torch.cuda.empty_cache()
 
